@@ -1,0 +1,55 @@
+"""The seeded input generators: determinism and the structure each workload promises."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+
+def test_deterministic_and_seed_sensitive():
+    a, b = W.tiny_fp32(), W.tiny_fp32()
+    assert torch.equal(a.k_pool, b.k_pool) and torch.equal(a.q, b.q)
+    c = W.tiny_fp32(seed=77)
+    assert not torch.equal(a.k_pool, c.k_pool)
+
+
+def test_tiny_planted_keys():
+    w = W.tiny_fp32()
+    assert w.k_pool.shape == (64, 2, 16, 64) and w.dtype == "f32"
+    for g, (p, s) in enumerate(zip(w.extra["planted_pages"], w.extra["planted_slots"])):
+        for j in range(2):
+            key = w.k_pool[p, j, s].double()
+            q = w.q[0, j * 4 + g].double()
+            assert abs(key.norm().item() - 24.0) < 1e-4
+            assert torch.nn.functional.cosine_similarity(key, q, dim=0).item() > 0.99999
+
+
+def test_ragged_batch_structure():
+    w = W.ragged_batch()
+    lens = w.seq_lens.numpy()
+    assert w.B == 16 and lens.min() >= 4096 and lens.max() <= 16384
+    used = np.concatenate([w.page_table[b, :w.n_pages(b)].numpy() for b in range(w.B)])
+    assert np.array_equal(np.sort(used), np.arange(w.num_phys_pages))  # a permutation of the pool
+    assert not np.array_equal(used, np.arange(w.num_phys_pages))
+    assert w.k == 32
+
+
+@pytest.mark.slow
+def test_qwen_needles_align_with_group_query():
+    w = W.qwen4b_128k()
+    assert w.k_pool.shape == (4096, 8, 32, 128) and w.k == 128
+    q = w.q.double()[0]
+    for j in range(8):
+        u = q[j * 4:(j + 1) * 4].sum(0)
+        for p in w.extra["needle_pages"]:
+            m = w.k_pool[p, j].double().mean(0)
+            cos = torch.nn.functional.cosine_similarity(m, u, dim=0).item()
+            assert abs(cos - 0.9) < 0.01
+
+
+def test_speculative_queries_are_correlated():
+    w = W.speculative_rope(steps=8)
+    qs = w.extra["q_steps"].double()
+    cos = torch.nn.functional.cosine_similarity(qs[1:], qs[:-1], dim=-1)
+    assert 0.75 < cos.mean().item() < 0.92
+    assert torch.equal(w.q, w.extra["q_steps"][0])

@@ -1,0 +1,315 @@
+"""Seeded synthetic inputs for the sparse-page decode workloads.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the benchmark. It holds
+random draws, shapes and the layout of the paged KV pool only: none of the arithmetic of the
+method itself (no page summary, no score, no selection, no attention, no rotary rotation).
+
+The shapes follow the pages' workloads:
+  * a paged KV cache with fixed-size token pages and grouped-query heads ("Key-Value (KV) Cache"
+    wiki page, the PagedAttention and GQA entries);
+  * Llama-3.1-8B / Qwen-3-4B shaped long-context decode (the KV Packet review, section 3, names
+    both models);
+  * strongly correlated queries of adjacent decode steps (FreeKV summary, section 2.1: cosine of
+    about 0.84 or more between neighbouring steps' queries).
+
+Every tensor is a CPU torch tensor; callers move it to the device. bf16 values are produced by
+round-to-nearest-even of fp32/fp64 draws (torch's conversion).
+
+Seeds: workload ``i`` (1-based) draws from ``numpy.random.Generator(PCG64(1000 + i))`` unless a
+seed is given, in a fixed order: q, K, V, structure (plants / needles / outliers), page table.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "make",
+    "tiny_fp32",
+    "llama8b_32k",
+    "ragged_batch",
+    "qwen4b_128k",
+    "speculative_rope",
+    "custom",
+]
+
+
+@dataclass
+class Workload:
+    """One decode problem over a paged GQA KV cache.
+
+    Pool layout: ``k_pool``/``v_pool`` are ``[num_phys_pages][Hkv][P][D]``; ``page_table[b][n]``
+    is the physical page holding logical page ``n`` of sequence ``b``; ``seq_lens[b]`` is the
+    number of valid tokens. Entries of ``page_table`` at or beyond ``ceil(L_b / P)`` are 0 and
+    never read.
+    """
+
+    name: str
+    dtype: str  # "f32" or "bf16"
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    P: int
+    k: int  # pages selected per (sequence, KV head)
+    seq_lens: torch.Tensor  # int32 [B]
+    page_table: torch.Tensor  # int32 [B][max_pages]
+    k_pool: torch.Tensor  # [Npp][Hkv][P][D]
+    v_pool: torch.Tensor  # [Npp][Hkv][P][D]
+    q: torch.Tensor  # [B][Hq][D] (first decode step)
+    extra: Dict[str, object] = field(default_factory=dict)
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def num_phys_pages(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.page_table.shape[1])
+
+    def n_pages(self, b: int) -> int:
+        return -(-int(self.seq_lens[b]) // self.P)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _to(x: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t if dtype == "f32" else t.to(torch.bfloat16)
+
+
+def _normal(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.standard_normal(size=shape, dtype=np.float64)
+
+
+def _identity_table(B: int, n_pages: int) -> torch.Tensor:
+    return torch.arange(B * n_pages, dtype=torch.int32).reshape(B, n_pages)
+
+
+def _outlier_channels(rng: np.random.Generator, Hkv: int, D: int, n: int = 4) -> np.ndarray:
+    return np.stack([rng.choice(D, size=n, replace=False) for _ in range(Hkv)])
+
+
+def _apply_outliers(keys: np.ndarray, chans: np.ndarray, scale: float = 8.0) -> None:
+    # keys: [Npp][Hkv][P][D]; channels chans[j] of KV head j are scaled in place
+    for j in range(chans.shape[0]):
+        keys[:, j, :, chans[j]] *= scale
+
+
+def tiny_fp32(seed: int = 1001) -> Workload:
+    """1 sequence, 8 query / 2 KV heads, D 64, 1024 tokens, P 16 (64 pages), k 16, fp32.
+
+    q, K, V ~ N(0,1); four planted tokens in four distinct pages. At planted token g (g = 0..3)
+    the key of KV head j is 3*sqrt(D) * q[j*G + g] / |q[j*G + g]|, so every query head of a group
+    has one strongly matching token and selection is not trivial.
+    """
+    B, Hq, Hkv, D, L, P, k = 1, 8, 2, 64, 1024, 16, 16
+    G = Hq // Hkv
+    rng = _rng(seed)
+    q = _normal(rng, (B, Hq, D)).astype(np.float32).astype(np.float64)
+    npg = L // P
+    K = _normal(rng, (npg, Hkv, P, D))
+    V = _normal(rng, (npg, Hkv, P, D))
+    pages = rng.choice(npg, size=G, replace=False)
+    slots = rng.integers(0, P, size=G)
+    for g in range(G):
+        for j in range(Hkv):
+            qh = q[0, j * G + g]
+            K[pages[g], j, slots[g]] = 3.0 * np.sqrt(D) * qh / np.linalg.norm(qh)
+    return Workload(
+        "tiny_fp32", "f32", B, Hq, Hkv, D, P, k,
+        seq_lens=torch.tensor([L], dtype=torch.int32),
+        page_table=_identity_table(B, npg),
+        k_pool=_to(K, "f32"), v_pool=_to(V, "f32"), q=_to(q, "f32"),
+        extra={"planted_pages": pages.tolist(), "planted_slots": slots.tolist()},
+    )
+
+
+def llama8b_32k(seed: int = 1002, context: int = 32768, budget_tokens: int = 2048) -> Workload:
+    """Llama-3.1-8B-shaped decode step: B 1, 32 / 8 heads, D 128, bf16, P 32, top-k = budget / P.
+
+    q, V ~ N(0,1); K ~ N(0,1) with 4 outlier channels per KV head scaled by 8.
+    """
+    B, Hq, Hkv, D, P = 1, 32, 8, 128, 32
+    rng = _rng(seed)
+    q = _normal(rng, (B, Hq, D))
+    npg = -(-context // P)
+    K = _normal(rng, (npg, Hkv, P, D))
+    V = _normal(rng, (npg, Hkv, P, D))
+    chans = _outlier_channels(rng, Hkv, D)
+    _apply_outliers(K, chans)
+    return Workload(
+        "llama8b_32k", "bf16", B, Hq, Hkv, D, P, budget_tokens // P,
+        seq_lens=torch.tensor([context], dtype=torch.int32),
+        page_table=_identity_table(B, npg),
+        k_pool=_to(K, "bf16"), v_pool=_to(V, "bf16"), q=_to(q, "bf16"),
+        extra={"outlier_channels": chans.tolist()},
+    )
+
+
+def ragged_batch(seed: int = 1003, B: int = 16, lo: int = 4096, hi: int = 16384,
+                 budget_tokens: int = 1024) -> Workload:
+    """Batch of 16 sequences with lengths uniform in [4096, 16384], shared paged pool.
+
+    32 / 8 heads, D 128, bf16, P 32, k = 1024 / 32 = 32. q, V ~ N(0,1); K as in the 32K case
+    (4 outlier channels per KV head, x8). One random permutation of the pool's pages is laid out
+    over all (sequence, logical page) pairs in order, so every sequence's table is permuted.
+    """
+    Hq, Hkv, D, P = 32, 8, 128, 32
+    rng = _rng(seed)
+    q = _normal(rng, (B, Hq, D))
+    lens = rng.integers(lo, hi + 1, size=B)
+    npgs = [-(-int(L) // P) for L in lens]
+    Npp = int(sum(npgs))
+    K = _normal(rng, (Npp, Hkv, P, D))
+    V = _normal(rng, (Npp, Hkv, P, D))
+    chans = _outlier_channels(rng, Hkv, D)
+    _apply_outliers(K, chans)
+    perm = rng.permutation(Npp)
+    maxp = max(npgs)
+    table = np.zeros((B, maxp), dtype=np.int32)
+    off = 0
+    for b, n in enumerate(npgs):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    return Workload(
+        "ragged_batch", "bf16", B, Hq, Hkv, D, P, budget_tokens // P,
+        seq_lens=torch.tensor(lens, dtype=torch.int32),
+        page_table=torch.from_numpy(table),
+        k_pool=_to(K, "bf16"), v_pool=_to(V, "bf16"), q=_to(q, "bf16"),
+        extra={"outlier_channels": chans.tolist()},
+    )
+
+
+def qwen4b_128k(seed: int = 1004, context: int = 131072, budget_tokens: int = 4096,
+                n_needles: int = 16, cosine: float = 0.9) -> Workload:
+    """Qwen-3-4B-shaped long context: B 1, 32 / 8 heads, D 128, bf16, P 32, k = 4096 / 32 = 128.
+
+    q, K, V ~ N(0,1), plus 16 needle pages (distinct logical pages, shared by all KV heads). In a
+    needle page of KV head j the 32 keys are (noise - its token mean) + m_j with
+    m_j = sqrt(D) * (c * u + sqrt(1 - c^2) * w): u is the unit vector along the sum of the group's
+    (bf16) queries, w a random unit vector orthogonal to u, c = 0.9. The needle page's mean key
+    therefore has cosine c with the group's query direction (before bf16 rounding).
+    """
+    B, Hq, Hkv, D, P = 1, 32, 8, 128, 32
+    G = Hq // Hkv
+    rng = _rng(seed)
+    q = torch.from_numpy(_normal(rng, (B, Hq, D)).astype(np.float32)).to(torch.bfloat16)
+    qd = q.to(torch.float64).numpy()
+    npg = -(-context // P)
+    K = _normal(rng, (npg, Hkv, P, D))
+    V = _normal(rng, (npg, Hkv, P, D))
+    needles = np.sort(rng.choice(npg, size=n_needles, replace=False))
+    for j in range(Hkv):
+        u = qd[0, j * G:(j + 1) * G].sum(axis=0)
+        u /= np.linalg.norm(u)
+        for p in needles:
+            w = _normal(rng, (D,))
+            w -= (w @ u) * u
+            w /= np.linalg.norm(w)
+            m = np.sqrt(D) * (cosine * u + np.sqrt(1.0 - cosine * cosine) * w)
+            noise = K[p, j]
+            K[p, j] = noise - noise.mean(axis=0, keepdims=True) + m
+    return Workload(
+        "qwen4b_128k", "bf16", B, Hq, Hkv, D, P, budget_tokens // P,
+        seq_lens=torch.tensor([context], dtype=torch.int32),
+        page_table=_identity_table(B, npg),
+        k_pool=_to(K, "bf16"), v_pool=_to(V, "bf16"), q=q,
+        extra={"needle_pages": needles.tolist()},
+    )
+
+
+def speculative_rope(seed: int = 1005, steps: int = 64, rho: float = 0.85, tau: float = 0.8,
+                     context: int = 32768, block_tokens: int = 4096,
+                     theta: float = 500000.0) -> Workload:
+    """32K Llama-shaped cache built from precomputed blocks, plus a run of correlated queries.
+
+    Shapes as the 32K case (B 1, 32 / 8 heads, D 128, bf16, P 32, k 64). Queries follow
+    q_t = rho * q_{t-1} + sqrt(1 - rho^2) * eps_t per head (fp32, on unrounded values; the bf16
+    copy of each step is the input). ``k_pool`` holds the RAW (un-rotated) keys, N(0,1) with 4
+    outlier channels per KV head (x8); the rotary encoding of each 4096-token block at positions
+    0..4095 and its re-positioning to offset 4096 * block are steps of the method, done by each
+    side. ``extra['q_steps']`` is bf16 [steps][B][Hq][D].
+    """
+    B, Hq, Hkv, D, P = 1, 32, 8, 128, 32
+    rng = _rng(seed)
+    q0 = _normal(rng, (B, Hq, D)).astype(np.float32)
+    npg = -(-context // P)
+    K = _normal(rng, (npg, Hkv, P, D))
+    V = _normal(rng, (npg, Hkv, P, D))
+    chans = _outlier_channels(rng, Hkv, D)
+    _apply_outliers(K, chans)
+    qs = [q0]
+    a = np.float32(rho)
+    c = np.float32(np.sqrt(1.0 - rho * rho))
+    for _ in range(1, steps):
+        eps = _normal(rng, (B, Hq, D)).astype(np.float32)
+        qs.append((a * qs[-1] + c * eps).astype(np.float32))
+    q_steps = torch.from_numpy(np.stack(qs)).to(torch.bfloat16)
+    return Workload(
+        "speculative_rope", "bf16", B, Hq, Hkv, D, P, 2048 // P,
+        seq_lens=torch.tensor([context], dtype=torch.int32),
+        page_table=_identity_table(B, npg),
+        k_pool=_to(K, "bf16"), v_pool=_to(V, "bf16"), q=q_steps[0].clone(),
+        extra={"q_steps": q_steps, "rho": rho, "tau": tau, "theta": theta,
+               "block_tokens": block_tokens, "outlier_channels": chans.tolist()},
+    )
+
+
+def custom(seed: int, B: int, Hq: int, Hkv: int, D: int, P: int, k: int, lens, dtype: str = "bf16",
+           permute: bool = True, spare_pages: int = 0) -> Workload:
+    """Small seeded case with arbitrary shapes (for edge-case tests): q, K, V ~ N(0,1).
+
+    ``lens`` gives each sequence's token count (0 allowed). With ``permute`` the pool's pages are
+    shuffled over the (sequence, logical page) pairs; ``spare_pages`` adds unreferenced pages.
+    """
+    rng = _rng(seed)
+    lens = np.asarray(lens, dtype=np.int64)
+    q = _normal(rng, (B, Hq, D))
+    npgs = [-(-int(L) // P) for L in lens]
+    Npp = int(sum(npgs)) + spare_pages
+    Npp = max(Npp, 1)
+    K = _normal(rng, (Npp, Hkv, P, D))
+    V = _normal(rng, (Npp, Hkv, P, D))
+    perm = rng.permutation(Npp) if permute else np.arange(Npp)
+    maxp = max(max(npgs), 1)
+    table = np.zeros((B, maxp), dtype=np.int32)
+    off = 0
+    for b, n in enumerate(npgs):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    return Workload(
+        f"custom_{seed}", dtype, B, Hq, Hkv, D, P, k,
+        seq_lens=torch.tensor(lens, dtype=torch.int32),
+        page_table=torch.from_numpy(table),
+        k_pool=_to(K, dtype), v_pool=_to(V, dtype), q=_to(q, dtype),
+    )
+
+
+WORKLOADS = {
+    "tiny_fp32": tiny_fp32,
+    "llama8b_32k": llama8b_32k,
+    "ragged_batch": ragged_batch,
+    "qwen4b_128k": qwen4b_128k,
+    "speculative_rope": speculative_rope,
+}
+
+
+def make(name: str, seed: Optional[int] = None) -> Workload:
+    fn = WORKLOADS[name]
+    return fn() if seed is None else fn(seed=seed)
