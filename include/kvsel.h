@@ -1,0 +1,188 @@
+/*
+ * kvsel — query-aware sparse-page decode attention over a paged GQA KV cache, for AMD Instinct
+ * MI355X (gfx950). C ABI of libkvsel.so.
+ *
+ * The operations follow these pages (cited by title and section):
+ *  [FreeKV]   "FreeKV: Boosting KV Cache Retrieval for Efficient LLM Inference" (Korean summary),
+ *             technical summary section 1 (keep the whole KV cache, use only the part a step
+ *             needs) and section 2.1 (choose KV pages per KV head with the current query; reuse
+ *             the previous step's pages; correct a KV head when its group-mean query similarity
+ *             is below tau).
+ *  [KV wiki]  "Key-Value (KV) Cache" wiki page: paged storage (PagedAttention entry), grouped-query
+ *             heads (Graph entry), decode bound by memory bandwidth (bottleneck entry).
+ *  [KV Packet] "[Paper review] KV Packet: Recomputation-Free Context-Independent KV Caching for
+ *             LLMs", section 1: RoPE re-aligns precomputed KV states to new positions.
+ * Where the pages leave a step open, the header states the rule this library implements.
+ *
+ * Conventions shared by every call
+ *  - Shapes: B sequences, Hq query heads, Hkv KV heads (G = Hq / Hkv; query head h reads KV head
+ *    h / G), head dim D in {64, 128}, page size P in {16, 32}, G in {1, 2, 4, 8}.
+ *  - Element type (kvsel_paged_kv.dtype): KVSEL_F32 (float) or KVSEL_BF16 (bfloat16 bits in
+ *    uint16). K, V, q, summaries and attention outputs all use it.
+ *  - Pool: k_pool and v_pool are [num_phys_pages][Hkv][P][D], row-major. Physical page p, KV
+ *    head j, slot s starts at element ((p * Hkv + j) * P + s) * D.
+ *  - page_table is int32 [B][max_pages_per_seq]: logical page n of sequence b lives in physical
+ *    page page_table[b][n]. seq_lens is int32 [B]; sequence b has N_b = ceil(seq_lens[b] / P)
+ *    logical pages, and slot s of logical page n is valid iff n * P + s < seq_lens[b]. Table
+ *    entries at or past N_b and invalid slots are never read (they may hold anything).
+ *  - All pointers in the descriptors and arguments are DEVICE pointers unless marked host, and
+ *    must stay valid until the work enqueued on `stream` completes. The caller owns every buffer;
+ *    the library allocates, frees and retains no memory.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues work and returns
+ *    without synchronizing; outputs are ready when the stream reaches that point.
+ *  - Errors: arguments are validated on the host BEFORE anything is enqueued, so a failing call
+ *    has no effect. Device-side contents (page ids in range, seq_lens <= max_pages_per_seq * P,
+ *    selected ids < N_b) are the caller's contract and are not checked.
+ */
+#ifndef KVSEL_H
+#define KVSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVSEL_ABI_VERSION 1
+
+typedef int32_t kvsel_status;
+#define KVSEL_OK 0
+#define KVSEL_ERR_INVALID_ARGUMENT 1 /* NULL required pointer, size < 1, Hq % Hkv != 0, ...  */
+#define KVSEL_ERR_UNSUPPORTED 2      /* D, P, G or dtype without a kernel                    */
+#define KVSEL_ERR_WORKSPACE 3        /* workspace NULL or smaller than kvsel_workspace_bytes */
+#define KVSEL_ERR_DEVICE 4           /* current device is not gfx950, or no device           */
+#define KVSEL_ERR_LAUNCH 5           /* the HIP runtime rejected a launch                    */
+
+#define KVSEL_F32 0
+#define KVSEL_BF16 1
+
+/* Workspace kinds for kvsel_workspace_bytes. */
+#define KVSEL_OP_SCORE_TOPK 1
+#define KVSEL_OP_ATTENTION 2
+
+/* Host struct describing one paged KV cache (device pointers inside). */
+typedef struct kvsel_paged_kv {
+  int32_t dtype;             /* KVSEL_F32 or KVSEL_BF16                              */
+  int32_t batch;             /* B                                                    */
+  int32_t num_q_heads;       /* Hq                                                   */
+  int32_t num_kv_heads;      /* Hkv                                                  */
+  int32_t head_dim;          /* D                                                    */
+  int32_t page_size;         /* P                                                    */
+  int32_t num_phys_pages;    /* pages in the pool                                    */
+  int32_t max_pages_per_seq; /* row length of page_table                             */
+  const void* k_pool;        /* [num_phys_pages][Hkv][P][D]                          */
+  const void* v_pool;        /* [num_phys_pages][Hkv][P][D] (may be NULL where unused) */
+  const int32_t* page_table; /* [B][max_pages_per_seq]                               */
+  const int32_t* seq_lens;   /* [B]                                                  */
+} kvsel_paged_kv;
+
+/* Host struct: rotary re-positioning of keys ([KV Packet] section 1). Rotate-half convention:
+ * channel pair (i, i + D/2) with c = cos[row][i], s = sin[row][i] becomes
+ * (x_i*c - x_{i+D/2}*s, x_{i+D/2}*c + x_i*s), each product and sum rounded to fp32 separately
+ * (no fused multiply-add), then rounded to the element type (round-to-nearest-even).
+ * Slot s of physical page p uses table row page_row[p] + row_step * s; page_row[p] < 0 leaves
+ * the page as it is. row_step 1 encodes per-token positions; row_step 0 shifts a whole page. */
+typedef struct kvsel_rope {
+  const float* cos;        /* [n_rows][D/2] fp32                                       */
+  const float* sin;        /* [n_rows][D/2] fp32                                       */
+  const int32_t* page_row; /* [num_phys_pages]; every used row must be < n_rows         */
+  int32_t n_rows;
+  int32_t row_step;        /* 0 or 1                                                    */
+} kvsel_rope;
+
+/* Host struct: speculative reuse with correction ([FreeKV] section 2.1). For every (b, j):
+ * C = mean over the G query heads of KV head j of cos(q[b][h], q_prev[b][h]), computed in fp64;
+ * corrected = first_step || C < tau (strict); the list used for attention is the fresh
+ * selection of this call when corrected, else prev_idx / prev_cnt (the previous step's fresh
+ * selection). */
+typedef struct kvsel_reuse {
+  const void* q_prev;       /* [B][Hq][D] element type: previous step's query           */
+  const int32_t* prev_idx;  /* [B][Hkv][k]                                              */
+  const int32_t* prev_cnt;  /* [B][Hkv]                                                 */
+  double tau;
+  int32_t first_step;       /* non-zero: always use the fresh selection                */
+  int32_t* used_idx;        /* out [B][Hkv][k]                                          */
+  int32_t* used_cnt;        /* out [B][Hkv]                                             */
+  uint8_t* corrected;       /* out [B][Hkv], 1 = fresh selection used                   */
+  double* similarity;       /* out [B][Hkv], may be NULL                                */
+} kvsel_reuse;
+
+/* ABI version (KVSEL_ABI_VERSION of the build). */
+int32_t kvsel_abi_version(void);
+
+/* Static string naming a status code; never NULL. */
+const char* kvsel_status_str(kvsel_status status);
+
+/* Bytes of device workspace `op` needs for this cache descriptor, top-k size k and (for
+ * KVSEL_OP_ATTENTION) pages_per_split (0 = the library's choice). Returns 0 for invalid input.
+ * Pure host arithmetic: touches no device. */
+size_t kvsel_workspace_bytes(const kvsel_paged_kv* kv, int32_t k, int32_t op,
+                             int32_t pages_per_split);
+
+/* Page-summary build. For every logical page n < N_b of every sequence b and every KV head j,
+ * writes summ[p][j][0][:] = channel-wise minimum and summ[p][j][1][:] = channel-wise maximum of
+ * the valid slots' keys, p = page_table[b][n]. summ is [num_phys_pages][Hkv][2][D] in the element
+ * type; rows of pages no sequence references are left untouched. A physical page referenced by
+ * two (b, n) pairs must hold the same number of valid slots in both.
+ * tail_only != 0 rebuilds only each sequence's last logical page (the page a decode step appends
+ * to). rope != NULL applies the rotary rotation to each key before the reduction (bit-identical
+ * to rotating the pool first with kvsel_rope_shift).
+ * [FreeKV] section 2.1 chooses KV pages with the query; the min/max page summary is this
+ * library's rule for it (the pages do not define one). */
+kvsel_status kvsel_build_summaries(const kvsel_paged_kv* kv, const kvsel_rope* rope,
+                                   int32_t tail_only, void* summ, void* stream);
+
+/* Query-aware page scoring and top-k selection, per (sequence, KV head).
+ * score[b][j][n] = fp32 rounding of the fp64 sum over the G query heads g of KV head j and the D
+ * channels d of (q[b][jG+g][d] >= 0 ? q*hi : q*lo) with lo/hi from summ of page page_table[b][n]
+ * (an upper bound of sum_g q_g . k over the page's keys). Products are exact in fp64 and the sum
+ * is accumulated in fp64.
+ * sel_idx[b][j][0..cnt) (int32 [B][Hkv][k]) receives the min(k, N_b) logical pages with the
+ * largest scores, ties to the lower page index, listed in ascending page order; the rest of the
+ * row is -1. sel_cnt[b][j] (int32 [B][Hkv]) receives the count.
+ * scores (fp32 [B][Hkv][max_pages_per_seq], may be NULL) receives the scores of n < N_b.
+ * reuse (may be NULL) adds the speculative-reuse decision described at kvsel_reuse, evaluated on
+ * this call's fresh selection.
+ * ws / ws_bytes: device workspace of kvsel_workspace_bytes(kv, k, KVSEL_OP_SCORE_TOPK, 0) bytes.
+ * [FreeKV] sections 1 and 2.1. */
+kvsel_status kvsel_score_topk(const kvsel_paged_kv* kv, const void* summ, const void* q,
+                              int32_t k, int32_t* sel_idx, int32_t* sel_cnt, float* scores,
+                              const kvsel_reuse* reuse, void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse paged decode attention over the selected pages.
+ * For every sequence b and query head h (KV head j = h / G), over the valid slots t of the
+ * logical pages sel_idx[b][j][0..sel_cnt[b][j]):
+ *   z_t = scale * q[b][h] . k_t,  out[b][h] = sum_t softmax(z)_t v_t,  lse[b][h] = log sum exp z
+ * with fp32 arithmetic (K/V read in the element type). out is [B][Hq][D] in the element type;
+ * lse is fp32 [B][Hq] and may be NULL. A (b, h) with nothing selected gets out = 0 and
+ * lse = -inf. The work is split over groups of pages_per_split consecutive selected pages
+ * (0 = the library's choice) and the splits are merged by log-sum-exp.
+ * rope != NULL rotates each key on the fly (bit-identical to a pool rotated by kvsel_rope_shift).
+ * ws / ws_bytes: kvsel_workspace_bytes(kv, k, KVSEL_OP_ATTENTION, pages_per_split) bytes.
+ * [FreeKV] section 2.1 (attention over the retrieved pages), [KV wiki] (decode attention, GQA). */
+kvsel_status kvsel_sparse_decode_attn(const kvsel_paged_kv* kv, const kvsel_rope* rope,
+                                      const void* q, const int32_t* sel_idx,
+                                      const int32_t* sel_cnt, int32_t k, float scale,
+                                      int32_t pages_per_split, void* out, float* lse, void* ws,
+                                      size_t ws_bytes, void* stream);
+
+/* Rotary table: cos[r][i], sin[r][i] (fp32 [n_rows][D/2]) of the angle
+ * (first_position + r) * theta^(-2i/D), evaluated in fp64 and rounded to fp32.
+ * [KV Packet] section 1 (RoPE encodes position by rotation). */
+kvsel_status kvsel_rope_table(double theta, int32_t head_dim, int32_t first_position,
+                              int32_t n_rows, float* cos, float* sin, void* stream);
+
+/* Materialized rotary re-positioning: writes the rotated keys of every physical page with
+ * page_row[p] >= 0 into k_out ([num_phys_pages][Hkv][P][D], element type) and copies the other
+ * pages unchanged. k_out may equal kv->k_pool (in place; unrotated pages are then skipped).
+ * Only kv->dtype, num_kv_heads, head_dim, page_size, num_phys_pages and k_pool are used.
+ * [KV Packet] section 1. */
+kvsel_status kvsel_rope_shift(const kvsel_paged_kv* kv, const kvsel_rope* rope, void* k_out,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSEL_H */

@@ -15,8 +15,11 @@ __all__ = ["kv_cache_bytes", "selected_kv_bytes", "summary_bytes"]
 
 
 def __getattr__(name):
-    # The binding is loaded lazily so that CPU-only users (tests of the accounting) need no GPU.
-    from . import kvsel as _k
+    # The binding is imported lazily so that CPU-only users (the accounting) need no HIP runtime.
+    if name.startswith("__") or name in ("kvsel", "build", "accounting"):
+        raise AttributeError(name)
+    import importlib
+    _k = importlib.import_module(__name__ + ".kvsel")
     if hasattr(_k, name):
         return getattr(_k, name)
     raise AttributeError(name)

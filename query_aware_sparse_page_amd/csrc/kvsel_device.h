@@ -1,0 +1,169 @@
+// Device helpers shared by the kvsel kernels (gfx950, wave64).
+//
+// Element types: float, or bf16 stored as uint16 bits (bf16_t). Every K/V/summary row is read
+// as 16-byte vectors: a lane holds VEC = 16 / sizeof(element) consecutive channels of one row,
+// LPR = D / VEC lanes cover a row, and one wave-wide load covers RPW = 64 / LPR rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvsel {
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct elem_traits;
+template <>
+struct elem_traits<float> {
+  static constexpr int VEC = 4;
+};
+template <>
+struct elem_traits<bf16_t> {
+  static constexpr int VEC = 8;
+};
+
+template <typename T, int D>
+struct row_map {
+  static constexpr int VEC = elem_traits<T>::VEC;
+  static constexpr int LPR = D / VEC;   // lanes per row
+  static constexpr int RPW = 64 / LPR;  // rows per wave-wide load
+  static_assert(D % VEC == 0 && 64 % LPR == 0, "row does not tile a wave");
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Round an fp32 value to the element type and widen it back.
+template <typename T>
+__device__ __forceinline__ float round_to_elem(float x);
+template <>
+__device__ __forceinline__ float round_to_elem<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float round_to_elem<bf16_t>(float x) {
+  return bf16_to_f32(f32_to_bf16_bits(x));
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Unpack one 16-byte vector into VEC floats.
+template <typename T>
+__device__ __forceinline__ void unpack(const uint4& v, float* f);
+template <>
+__device__ __forceinline__ void unpack<float>(const uint4& v, float* f) {
+  f[0] = __uint_as_float(v.x);
+  f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z);
+  f[3] = __uint_as_float(v.w);
+}
+template <>
+__device__ __forceinline__ void unpack<bf16_t>(const uint4& v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// Pack VEC floats (already representable in T) into one 16-byte vector.
+template <typename T>
+__device__ __forceinline__ uint4 pack(const float* f);
+template <>
+__device__ __forceinline__ uint4 pack<float>(const float* f) {
+  return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                    __float_as_uint(f[3]));
+}
+template <>
+__device__ __forceinline__ uint4 pack<bf16_t>(const float* f) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = f32_to_bf16_bits(f[2 * i]) | (f32_to_bf16_bits(f[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Load one element of type T (scalar) as float.
+template <typename T>
+__device__ __forceinline__ float load_elem(const T* p, size_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_elem<bf16_t>(const bf16_t* p, size_t i) {
+  return bf16_to_f32(p[i].bits);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_elem(T* p, size_t i, float x);
+template <>
+__device__ __forceinline__ void store_elem<float>(float* p, size_t i, float x) { p[i] = x; }
+template <>
+__device__ __forceinline__ void store_elem<bf16_t>(bf16_t* p, size_t i, float x) {
+  p[i].bits = (uint16_t)f32_to_bf16_bits(x);
+}
+
+// ------------------------------------------------------------------------------------------
+// Rotary rotation of one lane's slice of a key row (rotate-half pairs (i, i + D/2)).
+//
+// The lane holds channels [c0, c0 + VEC) of a row in `x`; its partner lane (lane ^ (LPR / 2))
+// holds the paired channels. Every product and every sum is rounded to fp32 on its own (FP
+// contraction off), and the result is rounded to the element type, so the kernels that rotate
+// on the fly (summaries, attention) and the one that materializes (rope shift) agree bit for
+// bit. `row` < 0 means: leave the slice unchanged. Must be called by all lanes of the wave.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float rot_mul(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+__device__ __forceinline__ float rot_sub(float a, float b) {
+#pragma clang fp contract(off)
+  return a - b;
+}
+__device__ __forceinline__ float rot_add(float a, float b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void rope_rotate_slice(float* x, int c0, int row, const float* __restrict__ cos_t,
+                                                  const float* __restrict__ sin_t) {
+  constexpr int VEC = row_map<T, D>::VEC;
+  constexpr int LPR = row_map<T, D>::LPR;
+  constexpr int HALF = D / 2;
+  float partner[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) partner[e] = __shfl_xor(x[e], LPR / 2);
+  if (row < 0) return;
+  const bool first = c0 < HALF;
+  const int i0 = first ? c0 : c0 - HALF;
+  const float* cr = cos_t + (size_t)row * HALF + i0;
+  const float* sr = sin_t + (size_t)row * HALF + i0;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    const float c = cr[e], s = sr[e];
+    float y;
+    if (first)
+      y = rot_sub(rot_mul(x[e], c), rot_mul(partner[e], s));  // x_i c - x_{i+D/2} s
+    else
+      y = rot_add(rot_mul(x[e], c), rot_mul(partner[e], s));  // x_{i+D/2} c + x_i s
+    x[e] = round_to_elem<T>(y);
+  }
+}
+
+// Orderable key of an fp32 score: unsigned order == float order; -0 and +0 map together.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace kvsel

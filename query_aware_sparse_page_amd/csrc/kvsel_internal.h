@@ -1,0 +1,62 @@
+// Internal launch interface between the C ABI layer (kvsel_abi.hip) and the kernel files.
+// Arguments reaching these launchers have been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvsel {
+
+// Flattened, validated copy of a kvsel_paged_kv descriptor.
+struct LaunchKV {
+  int dtype;  // 0 = f32, 1 = bf16
+  int B, Hq, Hkv, G, D, P, log2P, Npp, maxp;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+};
+
+// Rotary table arguments passed to kernels by value; page_row == nullptr means "no rotation".
+struct RopeArgs {
+  const float* cos;
+  const float* sin;
+  const int32_t* page_row;
+  int row_step;
+};
+
+struct ReuseArgs {
+  const void* q_prev;  // nullptr: no reuse decision
+  const int32_t* prev_idx;
+  const int32_t* prev_cnt;
+  double tau;
+  int first_step;
+  int32_t* used_idx;
+  int32_t* used_cnt;
+  uint8_t* corrected;
+  double* similarity;
+};
+
+hipError_t launch_summaries(const LaunchKV& kv, const RopeArgs& rope, int tail_only, void* summ,
+                            hipStream_t stream);
+
+hipError_t launch_score_topk(const LaunchKV& kv, const void* summ, const void* q, int k,
+                             int32_t* sel_idx, int32_t* sel_cnt, float* scores,
+                             const ReuseArgs& reuse, hipStream_t stream);
+
+// Workspace of the attention for a given split size (bytes).
+size_t attention_workspace(const LaunchKV& kv, int k, int pages_per_split);
+int attention_pages_per_split(const LaunchKV& kv, int k, int requested);
+
+hipError_t launch_attention(const LaunchKV& kv, const RopeArgs& rope, const void* q,
+                            const int32_t* sel_idx, const int32_t* sel_cnt, int k, float scale,
+                            int pages_per_split, void* out, float* lse, void* ws,
+                            hipStream_t stream);
+
+hipError_t launch_rope_table(double theta, int D, int first_position, int n_rows, float* cos,
+                             float* sin, hipStream_t stream);
+
+hipError_t launch_rope_shift(const LaunchKV& kv, const RopeArgs& rope, void* k_out,
+                             hipStream_t stream);
+
+}  // namespace kvsel

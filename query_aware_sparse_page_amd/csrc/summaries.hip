@@ -1,0 +1,115 @@
+// Page-summary build: channel-wise min / max of the valid keys of each (page, KV head).
+//
+// One wave reduces one (physical page, KV head) tile of P x D keys: each lane loads 16-byte
+// slices of rows (coalesced: LPR lanes cover one row, so one wave-wide load reads RPW whole
+// rows), keeps a running min / max per channel, then the RPW row groups are folded with
+// cross-lane exchanges and the first row group writes the lo and hi rows (16 bytes per lane).
+// Min / max are exact, so the result does not depend on the reduction order.
+#include "kvsel_device.h"
+#include "kvsel_internal.h"
+
+namespace kvsel {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_pool,
+                                                        const int32_t* __restrict__ page_table,
+                                                        const int32_t* __restrict__ seq_lens, int B,
+                                                        int Hkv, int P, int maxp, int tail_only,
+                                                        RopeArgs rope, T* __restrict__ summ) {
+  using M = row_map<T, D>;
+  constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
+  constexpr int MAX_LOADS = 32 / RPW;  // P <= 32
+
+  const int lane = threadIdx.x & 63;
+  const long unit = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  int b, n, j;
+  if (tail_only) {
+    if (unit >= (long)B * Hkv) return;
+    b = (int)(unit / Hkv);
+    j = (int)(unit % Hkv);
+    const int L = seq_lens[b];
+    if (L <= 0) return;
+    n = (L - 1) / P;
+  } else {
+    if (unit >= (long)B * maxp * Hkv) return;
+    b = (int)(unit / ((long)maxp * Hkv));
+    const int rem = (int)(unit % ((long)maxp * Hkv));
+    n = rem / Hkv;
+    j = rem % Hkv;
+    if (n * P >= seq_lens[b]) return;
+  }
+  const int L = seq_lens[b];
+  const int p = page_table[(size_t)b * maxp + n];
+  const int valid = min(P, L - n * P);
+  const int rg = lane / LPR;
+  const int c0 = (lane % LPR) * VEC;
+
+  const T* tile = k_pool + ((size_t)p * Hkv + j) * P * D;
+  uint4 raw[MAX_LOADS];
+#pragma unroll
+  for (int i = 0; i < MAX_LOADS; ++i) {
+    const int s = rg + i * RPW;
+    raw[i] = (s < valid) ? load16(tile + (size_t)s * D + c0) : make_uint4(0, 0, 0, 0);
+  }
+
+  float lo[VEC], hi[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    lo[e] = __int_as_float(0x7f800000);   // +inf
+    hi[e] = __int_as_float(0xff800000);   // -inf
+  }
+  const int prow = rope.page_row ? rope.page_row[p] : -1;
+#pragma unroll
+  for (int i = 0; i < MAX_LOADS; ++i) {
+    const int s = rg + i * RPW;
+    if (i * RPW >= P) break;
+    float x[VEC];
+    unpack<T>(raw[i], x);
+    if (rope.page_row)  // all lanes take part in the partner exchange
+      rope_rotate_slice<T, D>(x, c0, prow < 0 ? -1 : prow + rope.row_step * s, rope.cos, rope.sin);
+    if (s < valid) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        lo[e] = fminf(lo[e], x[e]);
+        hi[e] = fmaxf(hi[e], x[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = LPR; m < 64; m <<= 1) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      lo[e] = fminf(lo[e], __shfl_xor(lo[e], m));
+      hi[e] = fmaxf(hi[e], __shfl_xor(hi[e], m));
+    }
+  }
+  if (rg == 0) {
+    T* out = summ + ((size_t)p * Hkv + j) * 2 * D;
+    store16(out + c0, pack<T>(lo));
+    store16(out + D + c0, pack<T>(hi));
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_summaries_t(const LaunchKV& kv, const RopeArgs& rope, int tail_only,
+                                     void* summ, hipStream_t stream) {
+  const long units = tail_only ? (long)kv.B * kv.Hkv : (long)kv.B * kv.maxp * kv.Hkv;
+  const long blocks = (units + 3) / 4;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((summaries_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const T*)kv.k_pool, kv.page_table, kv.seq_lens, kv.B, kv.Hkv, kv.P, kv.maxp,
+                     tail_only, rope, (T*)summ);
+  return hipGetLastError();
+}
+
+hipError_t launch_summaries(const LaunchKV& kv, const RopeArgs& rope, int tail_only, void* summ,
+                            hipStream_t stream) {
+  if (kv.dtype == 0) {
+    if (kv.D == 64) return launch_summaries_t<float, 64>(kv, rope, tail_only, summ, stream);
+    return launch_summaries_t<float, 128>(kv, rope, tail_only, summ, stream);
+  }
+  if (kv.D == 64) return launch_summaries_t<bf16_t, 64>(kv, rope, tail_only, summ, stream);
+  return launch_summaries_t<bf16_t, 128>(kv, rope, tail_only, summ, stream);
+}
+
+}  // namespace kvsel

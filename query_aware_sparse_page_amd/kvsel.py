@@ -1,0 +1,314 @@
+"""ctypes binding of libkvsel.so (the C ABI in include/kvsel.h).
+
+Argument marshalling only: these wrappers check devices / dtypes / contiguity, allocate outputs
+and workspaces with torch when the caller does not pass them, and hand raw device pointers plus
+torch's current HIP stream to the library. Every step of the computation runs in the library's
+HIP kernels; there is no fallback path. A missing library raises ``KvselError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvsel.so")
+
+KVSEL_F32 = 0
+KVSEL_BF16 = 1
+KVSEL_OP_SCORE_TOPK = 1
+KVSEL_OP_ATTENTION = 2
+
+c_i32 = ctypes.c_int32
+c_vp = ctypes.c_void_p
+
+
+class KvselError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class PagedKVDesc(ctypes.Structure):
+    _fields_ = [
+        ("dtype", c_i32), ("batch", c_i32), ("num_q_heads", c_i32), ("num_kv_heads", c_i32),
+        ("head_dim", c_i32), ("page_size", c_i32), ("num_phys_pages", c_i32),
+        ("max_pages_per_seq", c_i32), ("k_pool", c_vp), ("v_pool", c_vp), ("page_table", c_vp),
+        ("seq_lens", c_vp),
+    ]
+
+
+class RopeDesc(ctypes.Structure):
+    _fields_ = [("cos", c_vp), ("sin", c_vp), ("page_row", c_vp), ("n_rows", c_i32),
+                ("row_step", c_i32)]
+
+
+class ReuseDesc(ctypes.Structure):
+    _fields_ = [
+        ("q_prev", c_vp), ("prev_idx", c_vp), ("prev_cnt", c_vp), ("tau", ctypes.c_double),
+        ("first_step", c_i32), ("used_idx", c_vp), ("used_cnt", c_vp), ("corrected", c_vp),
+        ("similarity", c_vp),
+    ]
+
+
+EXPORTS = {
+    "kvsel_abi_version": (c_i32, []),
+    "kvsel_status_str": (ctypes.c_char_p, [c_i32]),
+    "kvsel_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PagedKVDesc), c_i32, c_i32, c_i32]),
+    "kvsel_build_summaries": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_i32,
+                                      c_vp, c_vp]),
+    "kvsel_score_topk": (c_i32, [ctypes.POINTER(PagedKVDesc), c_vp, c_vp, c_i32, c_vp, c_vp, c_vp,
+                                 ctypes.POINTER(ReuseDesc), c_vp, ctypes.c_size_t, c_vp]),
+    "kvsel_sparse_decode_attn": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp,
+                                         c_vp, c_vp, c_i32, ctypes.c_float, c_i32, c_vp, c_vp, c_vp,
+                                         ctypes.c_size_t, c_vp]),
+    "kvsel_rope_table": (c_i32, [ctypes.c_double, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
+    "kvsel_rope_shift": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp, c_vp]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvsel.so (once) and declare its signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise KvselError(-1, f"{LIB_PATH} is not built; run "
+                                 "`python -m query_aware_sparse_page_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().kvsel_status_str(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise KvselError(status, status_str(status))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _elem_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return KVSEL_F32
+    if dtype == torch.bfloat16:
+        return KVSEL_BF16
+    raise ValueError(f"unsupported element type {dtype}")
+
+
+@dataclass
+class PagedKV:
+    """Device tensors of one paged KV cache: pools [Npp][Hkv][P][D], page_table int32
+    [B][max_pages], seq_lens int32 [B]."""
+
+    k_pool: torch.Tensor
+    v_pool: Optional[torch.Tensor]
+    page_table: torch.Tensor
+    seq_lens: torch.Tensor
+    num_q_heads: int
+
+    def desc(self) -> PagedKVDesc:
+        _dev(self.k_pool, "k_pool")
+        if self.v_pool is not None:
+            _dev(self.v_pool, "v_pool", self.k_pool.dtype)
+        _dev(self.page_table, "page_table", torch.int32)
+        _dev(self.seq_lens, "seq_lens", torch.int32)
+        Npp, Hkv, P, D = self.k_pool.shape
+        B, maxp = self.page_table.shape
+        return PagedKVDesc(_elem_code(self.k_pool.dtype), B, self.num_q_heads, Hkv, D, P, Npp, maxp,
+                           self.k_pool.data_ptr(),
+                           self.v_pool.data_ptr() if self.v_pool is not None else None,
+                           self.page_table.data_ptr(), self.seq_lens.data_ptr())
+
+    @property
+    def batch(self) -> int:
+        return int(self.page_table.shape[0])
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k_pool.shape[1])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.k_pool.shape[3])
+
+    @property
+    def device(self) -> torch.device:
+        return self.k_pool.device
+
+
+@dataclass
+class Rope:
+    """Rotary table (fp32 [n_rows][D/2] cos and sin) and per-physical-page row (int32 [Npp])."""
+
+    cos: torch.Tensor
+    sin: torch.Tensor
+    page_row: torch.Tensor
+    row_step: int = 0
+
+    def desc(self) -> RopeDesc:
+        _dev(self.cos, "cos", torch.float32)
+        _dev(self.sin, "sin", torch.float32)
+        _dev(self.page_row, "page_row", torch.int32)
+        return RopeDesc(self.cos.data_ptr(), self.sin.data_ptr(), self.page_row.data_ptr(),
+                        int(self.cos.shape[0]), int(self.row_step))
+
+
+def _rope_ptr(rope: Optional[Rope]):
+    return None if rope is None else ctypes.byref(rope.desc())
+
+
+def workspace_bytes(kv: PagedKV, k: int, op: int, pages_per_split: int = 0) -> int:
+    return int(lib().kvsel_workspace_bytes(ctypes.byref(kv.desc()), k, op, pages_per_split))
+
+
+def _workspace(kv: PagedKV, k: int, op: int, pps: int, ws: Optional[torch.Tensor]):
+    need = workspace_bytes(kv, k, op, pps)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=kv.device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def build_summaries(kv: PagedKV, rope: Optional[Rope] = None, tail_only: bool = False,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-page channel-wise key min/max: returns summ [Npp][Hkv][2][D] (pool element type)."""
+    d = kv.desc()
+    Npp, Hkv, _, D = kv.k_pool.shape
+    if out is None:
+        out = torch.empty((Npp, Hkv, 2, D), dtype=kv.k_pool.dtype, device=kv.device)
+    _dev(out, "summ", kv.k_pool.dtype)
+    _check(lib().kvsel_build_summaries(ctypes.byref(d), _rope_ptr(rope), int(bool(tail_only)),
+                                       _ptr(out), _stream(kv.device)))
+    return out
+
+
+@dataclass
+class Reuse:
+    """Inputs of the speculative-reuse decision (previous query and previous fresh selection)."""
+
+    q_prev: torch.Tensor
+    prev_idx: torch.Tensor
+    prev_cnt: torch.Tensor
+    tau: float
+    first_step: bool = False
+
+
+def score_topk(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, *,
+               scores: Optional[torch.Tensor] = None, reuse: Optional[Reuse] = None,
+               sel_idx: Optional[torch.Tensor] = None, sel_cnt: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None):
+    """Page scores + top-k. Returns (sel_idx [B][Hkv][k], sel_cnt [B][Hkv]) and, with ``reuse``,
+    additionally (used_idx, used_cnt, corrected uint8, similarity fp64)."""
+    d = kv.desc()
+    B, Hkv = kv.batch, kv.num_kv_heads
+    dev = kv.device
+    _dev(summ, "summ", kv.k_pool.dtype)
+    _dev(q, "q", kv.k_pool.dtype)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+    if sel_cnt is None:
+        sel_cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    if scores is not None:
+        _dev(scores, "scores", torch.float32)
+    rd = None
+    extra = ()
+    if reuse is not None:
+        used_idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+        used_cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+        corrected = torch.empty((B, Hkv), dtype=torch.uint8, device=dev)
+        sim = torch.empty((B, Hkv), dtype=torch.float64, device=dev)
+        _dev(reuse.q_prev, "q_prev", kv.k_pool.dtype)
+        _dev(reuse.prev_idx, "prev_idx", torch.int32)
+        _dev(reuse.prev_cnt, "prev_cnt", torch.int32)
+        rd = ReuseDesc(reuse.q_prev.data_ptr(), reuse.prev_idx.data_ptr(), reuse.prev_cnt.data_ptr(),
+                       float(reuse.tau), int(bool(reuse.first_step)), used_idx.data_ptr(),
+                       used_cnt.data_ptr(), corrected.data_ptr(), sim.data_ptr())
+        extra = (used_idx, used_cnt, corrected, sim)
+    ws, ws_bytes = (None, 0)
+    if scores is None:
+        ws, ws_bytes = _workspace(kv, k, KVSEL_OP_SCORE_TOPK, 0, workspace)
+    _check(lib().kvsel_score_topk(ctypes.byref(d), _ptr(summ), _ptr(q), k, _ptr(sel_idx),
+                                  _ptr(sel_cnt), _ptr(scores),
+                                  None if rd is None else ctypes.byref(rd), _ptr(ws), ws_bytes,
+                                  _stream(dev)))
+    return (sel_idx, sel_cnt) + extra
+
+
+def default_scale(head_dim: int) -> float:
+    """1/sqrt(D) rounded to fp32 (the softmax scale both the library and its callers use)."""
+    return float(torch.tensor(1.0 / math.sqrt(head_dim), dtype=torch.float32))
+
+
+def sparse_decode_attn(kv: PagedKV, q: torch.Tensor, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
+                       k: Optional[int] = None, *, scale: Optional[float] = None,
+                       pages_per_split: int = 0, rope: Optional[Rope] = None,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                       want_lse: bool = True, workspace: Optional[torch.Tensor] = None
+                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Decode attention over the selected pages. Returns (out [B][Hq][D], lse fp32 [B][Hq])."""
+    d = kv.desc()
+    dev = kv.device
+    _dev(q, "q", kv.k_pool.dtype)
+    _dev(sel_idx, "sel_idx", torch.int32)
+    _dev(sel_cnt, "sel_cnt", torch.int32)
+    k = int(sel_idx.shape[-1]) if k is None else k
+    if scale is None:
+        scale = default_scale(kv.head_dim)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    ws, ws_bytes = _workspace(kv, k, KVSEL_OP_ATTENTION, pages_per_split, workspace)
+    _check(lib().kvsel_sparse_decode_attn(ctypes.byref(d), _rope_ptr(rope), _ptr(q), _ptr(sel_idx),
+                                          _ptr(sel_cnt), k, scale, pages_per_split, _ptr(out),
+                                          _ptr(lse), _ptr(ws), ws_bytes, _stream(dev)))
+    return out, lse
+
+
+def rope_table(theta: float, head_dim: int, first_position: int, n_rows: int,
+               device: torch.device) -> Tuple[torch.Tensor, torch.Tensor]:
+    """cos/sin fp32 [n_rows][D/2] of (first_position + r) * theta^(-2i/D), built on the device."""
+    cos = torch.empty((n_rows, head_dim // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    _check(lib().kvsel_rope_table(float(theta), head_dim, first_position, n_rows, _ptr(cos),
+                                  _ptr(sin), _stream(torch.device(device))))
+    return cos, sin
+
+
+def rope_shift(kv: PagedKV, rope: Rope, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Materialized rotation of the key pool (out may be kv.k_pool for in place)."""
+    d = kv.desc()
+    if out is None:
+        out = torch.empty_like(kv.k_pool)
+    _dev(out, "k_out", kv.k_pool.dtype)
+    _check(lib().kvsel_rope_shift(ctypes.byref(d), ctypes.byref(rope.desc()), _ptr(out),
+                                  _stream(kv.device)))
+    return out

@@ -1,0 +1,118 @@
+"""C ABI on the CPU: the library loads, exports every symbol include/kvsel.h declares, and its
+host-side validation returns the documented status codes before touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvsel.h")
+
+
+@pytest.fixture(scope="module")
+def K():
+    from query_aware_sparse_page_amd import kvsel as K
+    if not os.path.exists(K.LIB_PATH):
+        from query_aware_sparse_page_amd.build import build
+        build()
+    K.lib()
+    return K
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvsel_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ["kvsel_build_summaries", "kvsel_score_topk", "kvsel_sparse_decode_attn",
+              "kvsel_rope_shift"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(K):
+    lib = K.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(K.EXPORTS)
+
+
+def test_version_and_status_strings(K):
+    lib = K.lib()
+    assert lib.kvsel_abi_version() == 1
+    for code, tag in [(0, "KVSEL_OK"), (1, "INVALID_ARGUMENT"), (2, "UNSUPPORTED"),
+                      (3, "WORKSPACE"), (4, "DEVICE"), (5, "LAUNCH"), (99, "UNKNOWN")]:
+        assert tag in lib.kvsel_status_str(code).decode()
+
+
+def _desc(K, **kw):
+    base = dict(dtype=K.KVSEL_BF16, batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                page_size=32, num_phys_pages=1024, max_pages_per_seq=1024,
+                k_pool=0x1000, v_pool=0x2000, page_table=0x3000, seq_lens=0x4000)
+    base.update(kw)
+    return K.PagedKVDesc(*[base[f] for f, _ in K.PagedKVDesc._fields_])
+
+
+def test_workspace_sizes(K):
+    lib = K.lib()
+    d = _desc(K)
+    ws = lib.kvsel_workspace_bytes(ctypes.byref(d), 64, K.KVSEL_OP_SCORE_TOPK, 0)
+    assert ws == 1 * 8 * 1024 * 4
+    # 64 pages in splits of 2 -> 32 partials per (b, KV head, query head of the group)
+    parts = 1 * 8 * 32 * 4
+    acc = parts * 128 * 4
+    assert lib.kvsel_workspace_bytes(ctypes.byref(d), 64, K.KVSEL_OP_ATTENTION, 2) == \
+        ((acc + 255) // 256) * 256 + parts * 8
+    # one split needs no workspace
+    assert lib.kvsel_workspace_bytes(ctypes.byref(d), 2, K.KVSEL_OP_ATTENTION, 2) == 0
+    assert lib.kvsel_workspace_bytes(None, 64, K.KVSEL_OP_SCORE_TOPK, 0) == 0
+    assert lib.kvsel_workspace_bytes(ctypes.byref(d), 0, K.KVSEL_OP_SCORE_TOPK, 0) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_q_heads", 30, 1),          # Hq % Hkv != 0
+    ("batch", 0, 1),
+    ("k_pool", None, 1),
+    ("head_dim", 96, 2),
+    ("page_size", 64, 2),
+    ("num_q_heads", 8 * 16, 2),      # G = 16
+    ("dtype", 7, 2),
+])
+def test_descriptor_validation(K, field, value, status):
+    lib = K.lib()
+    d = _desc(K, **{field: value})
+    st = lib.kvsel_build_summaries(ctypes.byref(d), None, 0, ctypes.c_void_p(0x5000), None)
+    assert st == status
+
+
+def test_call_argument_validation(K):
+    lib = K.lib()
+    d = _desc(K)
+    p = ctypes.c_void_p(0x5000)
+    assert lib.kvsel_build_summaries(None, None, 0, p, None) == 1
+    assert lib.kvsel_build_summaries(ctypes.byref(d), None, 0, None, None) == 1
+    # score/top-k: k < 1, NULL outputs, missing workspace when no score buffer is given
+    assert lib.kvsel_score_topk(ctypes.byref(d), p, p, 0, p, p, p, None, None, 0, None) == 1
+    assert lib.kvsel_score_topk(ctypes.byref(d), p, p, 64, None, p, p, None, None, 0, None) == 1
+    assert lib.kvsel_score_topk(ctypes.byref(d), p, p, 64, p, p, None, None, None, 0, None) == 3
+    assert lib.kvsel_score_topk(ctypes.byref(d), p, p, 64, p, p, None, None, p, 16, None) == 3
+    bad_reuse = K.ReuseDesc(None, 1, 1, 0.8, 0, 1, 1, 1, None)
+    assert lib.kvsel_score_topk(ctypes.byref(d), p, p, 64, p, p, p, ctypes.byref(bad_reuse), None,
+                                0, None) == 1
+    # attention: missing V pool, bad split request, workspace too small
+    dv = _desc(K, v_pool=None)
+    assert lib.kvsel_sparse_decode_attn(ctypes.byref(dv), None, p, p, p, 64, 0.1, 0, p, None, p,
+                                        1 << 30, None) == 1
+    assert lib.kvsel_sparse_decode_attn(ctypes.byref(d), None, p, p, p, 64, 0.1, -1, p, None, p,
+                                        1 << 30, None) == 1
+    assert lib.kvsel_sparse_decode_attn(ctypes.byref(d), None, p, p, p, 64, 0.1, 2, p, None, p,
+                                        100, None) == 3
+    # rope descriptors
+    bad_rope = K.RopeDesc(0x10, 0x20, 0x30, 4, 2)
+    assert lib.kvsel_rope_shift(ctypes.byref(d), ctypes.byref(bad_rope), p, None) == 1
+    assert lib.kvsel_rope_shift(ctypes.byref(d), None, p, None) == 1
+    assert lib.kvsel_rope_table(500000.0, 127, 0, 4, p, p, None) == 1
+    assert lib.kvsel_rope_table(-1.0, 128, 0, 4, p, p, None) == 1

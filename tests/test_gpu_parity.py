@@ -1,0 +1,173 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, element by element.
+
+Full-size workloads (the 32K Llama-shaped step, the ragged batch of 16, the 128K Qwen-shaped
+context, the tiny fp32 case) run in the launch configuration the benchmark times (default split)
+and are compared on every output; small seeded cases cover the edge cases (empty and one-token
+sequences, partial pages, k >= pages, every supported G / D / P / dtype, split sizes).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_common import (assert_attention_close, assert_scores_close, assert_selection_equal,
+                        assert_summaries_equal, kv_of, oracle_path, referenced_pages, say,
+                        scale_of)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from query_aware_sparse_page_amd import kvsel as K
+    K.lib()  # raises if libkvsel.so is missing: no fallback
+    return K
+
+
+def run_gpu_path(K, w, pps=0, scores=True):
+    say(f"path {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} P={w.P} k={w.k} dtype={w.dtype} pps={pps}")
+    kv = kv_of(K, w)
+    q = w.q.cuda()
+    summ = K.build_summaries(kv)
+    sc = torch.full((w.B, w.Hkv, w.max_pages), float("nan"), device="cuda") if scores else None
+    sel, cnt = K.score_topk(kv, summ, q, w.k, scores=sc)
+    out, lse = K.sparse_decode_attn(kv, q, sel, cnt, w.k, pages_per_split=pps)
+    torch.cuda.synchronize()
+    return dict(kv=kv, q=q, summ=summ, scores=sc, sel=sel, cnt=cnt, out=out, lse=lse)
+
+
+FULL = ["tiny_fp32", "llama8b_32k", "ragged_batch", "qwen4b_128k"]
+_cache = {}
+
+
+def full_case(name):
+    if name not in _cache:
+        w = W.make(name)
+        _cache.clear()  # keep one full-size workload in host memory at a time
+        _cache[name] = (w, oracle_path(w, scale_of(w.D)))
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload_parity(K, name):
+    w, ref = full_case(name)
+    g = run_gpu_path(K, w)
+    assert_summaries_equal(g["summ"], ref["summ"], referenced_pages(w))
+    n_exact, n = assert_scores_close(g["scores"], ref["scores"], w, exact=(w.dtype == "bf16"))
+    say(f"{name}: scores exact {n_exact}/{n}; min k-boundary margin {ref['margins'].min()} ulp")
+    assert_selection_equal(g["sel"], g["cnt"], ref["sel"], ref["cnt"], ref["margins"])
+    err = assert_attention_close(g["out"], g["lse"], ref["out"], ref["lse"], w.dtype)
+    say(f"{name}: attention max abs err {err:.3g}")
+
+
+def test_structure_is_found(K):
+    # planted tokens (tiny) and needle pages (128K) end up in every KV head's selection
+    w = W.tiny_fp32()
+    g = run_gpu_path(K, w)
+    s = g["sel"].cpu().numpy()
+    for j in range(w.Hkv):
+        assert set(w.extra["planted_pages"]) <= set(s[0, j].tolist())
+
+
+@pytest.mark.parametrize("case", [
+    dict(seed=101, B=3, Hq=8, Hkv=2, D=64, P=16, k=3, lens=[0, 1, 47], dtype="bf16"),
+    dict(seed=102, B=2, Hq=8, Hkv=8, D=128, P=32, k=4, lens=[200, 31], dtype="bf16"),     # G=1
+    dict(seed=103, B=2, Hq=16, Hkv=2, D=128, P=16, k=5, lens=[33, 170], dtype="bf16"),    # G=8
+    dict(seed=104, B=2, Hq=4, Hkv=2, D=64, P=32, k=8, lens=[96, 65], dtype="bf16"),       # k >= N
+    dict(seed=105, B=2, Hq=8, Hkv=4, D=128, P=32, k=3, lens=[300, 64], dtype="f32"),      # G=2
+    dict(seed=106, B=3, Hq=8, Hkv=2, D=64, P=16, k=4, lens=[16, 100, 257], dtype="f32"),
+    dict(seed=107, B=1, Hq=32, Hkv=8, D=128, P=32, k=64, lens=[32768 - 5], dtype="bf16"),  # ragged tail
+])
+def test_edge_case_parity(K, case):
+    w = W.custom(case["seed"], case["B"], case["Hq"], case["Hkv"], case["D"], case["P"], case["k"],
+                 case["lens"], case["dtype"], spare_pages=3)
+    # poison every slot no sequence may read: padding of partial pages and unreferenced pages
+    used = set(referenced_pages(w))
+    for p in range(w.num_phys_pages):
+        if p not in used:
+            w.k_pool[p] = float("nan")
+            w.v_pool[p] = float("nan")
+    for b in range(w.B):
+        L = int(w.seq_lens[b])
+        if L % w.P:
+            p = int(w.page_table[b, L // w.P])
+            w.k_pool[p, :, L % w.P:] = float("nan")
+            w.v_pool[p, :, L % w.P:] = float("nan")
+    ref = oracle_path(w, scale_of(w.D))
+    for pps in (0, 1, 4):
+        g = run_gpu_path(K, w, pps=pps)
+        assert_summaries_equal(g["summ"], ref["summ"], sorted(used))
+        assert_scores_close(g["scores"], ref["scores"], w, exact=(w.dtype == "bf16"))
+        assert_selection_equal(g["sel"], g["cnt"], ref["sel"], ref["cnt"], ref["margins"])
+        assert_attention_close(g["out"], g["lse"], ref["out"], ref["lse"], w.dtype)
+        # empty sequences give zeros and -inf
+        for b in range(w.B):
+            if int(w.seq_lens[b]) == 0:
+                assert (g["out"][b].float() == 0).all() and torch.isinf(g["lse"][b]).all()
+
+
+def test_all_pages_equals_dense_attention(K):
+    w = W.custom(111, B=2, Hq=8, Hkv=2, D=128, P=32, k=40, lens=[1200, 777], dtype="bf16")
+    ref = oracle_path(w, scale_of(w.D))
+    assert (ref["cnt"] == np.array([[38, 38], [25, 25]])).all()  # k >= N: everything selected
+    g = run_gpu_path(K, w)
+    K_ = w.k_pool.double().numpy()
+    V_ = w.v_pool.double().numpy()
+    for b in range(w.B):
+        L = int(w.seq_lens[b])
+        pages = range(w.n_pages(b))
+        keys = np.stack([O.gather_tokens(K_, w.page_table, L, b, j, pages, w.P) for j in range(w.Hkv)])
+        vals = np.stack([O.gather_tokens(V_, w.page_table, L, b, j, pages, w.P) for j in range(w.Hkv)])
+        dense, dlse = O.dense_decode_attention(w.q[b:b + 1], keys[None], vals[None], scale_of(w.D))
+        assert np.abs(g["out"][b].float().cpu().numpy() - dense[0]).max() <= 2e-2
+        assert np.abs(g["lse"][b].cpu().numpy() - dlse[0]).max() <= 1e-3
+
+
+def test_weights_sum_to_one(K):
+    w = W.custom(121, B=2, Hq=8, Hkv=2, D=128, P=32, k=8, lens=[4000, 513], dtype="bf16")
+    w.v_pool.fill_(1.0)
+    g = run_gpu_path(K, w, pps=2)
+    assert (g["out"].float() == 1.0).all()
+
+
+def test_split_invariance_and_determinism(K):
+    w = W.custom(131, B=2, Hq=32, Hkv=8, D=128, P=32, k=16, lens=[5000, 3333], dtype="f32")
+    outs = [run_gpu_path(K, w, pps=pps)["out"].cpu() for pps in (1, 2, 4, 8)]
+    for o in outs[1:]:
+        assert (o - outs[0]).abs().max().item() <= 1e-6
+    again = run_gpu_path(K, w, pps=2)["out"].cpu()
+    assert torch.equal(again, outs[1])
+
+
+def test_page_table_permutation_invariance(K):
+    a = W.custom(141, B=2, Hq=8, Hkv=2, D=128, P=32, k=6, lens=[900, 400], dtype="bf16",
+                 permute=False)
+    b = W.custom(141, B=2, Hq=8, Hkv=2, D=128, P=32, k=6, lens=[900, 400], dtype="bf16",
+                 permute=False)
+    rng = np.random.Generator(np.random.PCG64(3))
+    perm = rng.permutation(a.num_phys_pages)
+    inv = np.argsort(perm)
+    b.k_pool = a.k_pool[torch.from_numpy(perm)].contiguous()
+    b.v_pool = a.v_pool[torch.from_numpy(perm)].contiguous()
+    b.page_table = torch.from_numpy(inv[a.page_table.numpy()].astype(np.int32))
+    ga, gb = run_gpu_path(K, a), run_gpu_path(K, b)
+    assert torch.equal(ga["sel"], gb["sel"])
+    assert torch.equal(ga["out"], gb["out"])
+
+
+def test_tail_only_summary_refresh(K):
+    w = W.custom(151, B=3, Hq=8, Hkv=2, D=128, P=32, k=4, lens=[100, 64, 1], dtype="bf16")
+    say("tail-only summaries")
+    kv = kv_of(K, w)
+    full = K.build_summaries(kv)
+    tail = full.clone()
+    # change the keys of each sequence's last page, refresh only the tails
+    for b in range(w.B):
+        p = int(w.page_table[b, w.n_pages(b) - 1])
+        kv.k_pool[p] = kv.k_pool[p] * 2 + 1
+    K.build_summaries(kv, tail_only=True, out=tail)
+    torch.cuda.synchronize()
+    ref = O.page_summaries(kv.k_pool.cpu(), w.page_table, w.seq_lens, w.P)
+    assert_summaries_equal(tail, ref, referenced_pages(w))
