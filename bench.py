@@ -1,0 +1,254 @@
+"""Benchmark of the sparse-page decode step on one MI355X.
+
+One step = the decode-time path of one layer for one batch: refresh the summary of each
+sequence's tail page, score every page and select the top-k per (sequence, KV head), and run
+the sparse paged decode attention (split-K + merge) over the selected pages. Inputs are resident
+in HBM before the timed region. The step is timed over R copies of the cache at distinct HBM
+addresses, used in turn like the layers of a model, so the Infinity Cache cannot serve a step
+from the previous visit; the R steps are captured once in a HIP graph and replayed.
+
+Prints ONE JSON line: µs/step of the whole path (the headline value), the roofline of the
+dominant kernel (the attention split kernel; its duration measured with HIP events on the
+launch stream), the 128K-context secondary numbers, and the CPU oracle timed on a bounded sample
+of the same workload as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps 400] [--warmup 40] [--workload llama8b_32k]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+from query_aware_sparse_page_amd import kvsel as K  # noqa: E402
+from query_aware_sparse_page_amd.accounting import selected_kv_bytes, summary_bytes  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "sparse decode-attn µs/step and achieved HBM GB/s (% of peak) at 32K/128K ctx"
+
+
+class Layer:
+    """One copy of the cache (its own HBM addresses) with preallocated outputs/workspaces."""
+
+    def __init__(self, w, dev, k_pool, v_pool):
+        self.kv = K.PagedKV(k_pool, v_pool, w.page_table.to(dev), w.seq_lens.to(dev), w.Hq)
+        self.q = w.q.to(dev)
+        self.k = w.k
+        self.summ = K.build_summaries(self.kv)
+        self.sel = torch.empty((w.B, w.Hkv, w.k), dtype=torch.int32, device=dev)
+        self.cnt = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+        self.ws_score = K.new_workspace(self.kv, w.k, K.KVSEL_OP_SCORE_TOPK)
+        self.ws_attn = K.new_workspace(self.kv, w.k, K.KVSEL_OP_ATTENTION)
+
+    def select(self):
+        K.score_topk(self.kv, self.summ, self.q, self.k, refresh_tail=True, sel_idx=self.sel,
+                     sel_cnt=self.cnt, workspace=self.ws_score)
+
+    def attend(self):
+        K.sparse_decode_attn(self.kv, self.q, self.sel, self.cnt, self.k, out=self.out,
+                             lse=self.lse, workspace=self.ws_attn)
+
+    def step(self):
+        self.select()
+        self.attend()
+
+
+def make_layers(w, dev, n):
+    k0 = w.k_pool.to(dev)
+    v0 = K.device_v_layout(w.v_pool.to(dev))
+    layers = [Layer(w, dev, k0, v0)]
+    for _ in range(n - 1):
+        layers.append(Layer(w, dev, k0.clone(), v0.clone()))
+    torch.cuda.synchronize()
+    return layers
+
+
+def time_graph(layers, steps, warmup):
+    """µs per step of the whole path, replaying a graph of one step per layer."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for lay in layers:  # eager warm-up before capture
+            lay.step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for lay in layers:
+            lay.step()
+    reps_w = max(1, warmup // len(layers))
+    reps = max(1, steps // len(layers))
+    for _ in range(reps_w):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    n = reps * len(layers)
+    return e0.elapsed_time(e1) * 1000.0 / n, n
+
+
+def time_kernel(layers, fn, launches):
+    """Average GPU duration (µs) of the launches of ``fn(layer)``, each bracketed by HIP events
+    recorded on the launch stream. A GPU-side spin queued first keeps the device busy while the
+    host enqueues, so each event pair brackets GPU work only."""
+    for lay in layers:
+        lay.select()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    torch.cuda._sleep(int(2.0e8))  # ~0.1 s of GPU spin
+    for i in range(launches):
+        lay = layers[i % len(layers)]
+        starts[i].record()
+        fn(lay)
+        ends[i].record()
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) * 1000.0 for a, b in zip(starts, ends)])
+    return float(d.mean()), float(np.median(d)), d
+
+
+def attention_bytes(w, lay):
+    sel = lay.sel.cpu().numpy()
+    cnt = lay.cnt.cpu().numpy()
+    esize = 4 if w.dtype == "f32" else 2
+    return selected_kv_bytes(w.seq_lens.tolist(), sel, cnt, w.Hkv, w.P, w.D, esize)
+
+
+def measure(name, dev, steps, warmup, n_layers):
+    w = W.make(name)
+    layers = make_layers(w, dev, n_layers)
+    us_step, n = time_graph(layers, steps, warmup)
+    attn_mean, attn_med, _ = time_kernel(layers, Layer.attend, max(64, min(steps, 512)))
+    sel_mean, _, _ = time_kernel(layers, Layer.select, max(64, min(steps, 512)))
+    abytes = attention_bytes(w, layers[0])
+    esize = 4 if w.dtype == "f32" else 2
+    sbytes = summary_bytes(w.seq_lens.tolist(), w.Hkv, w.P, w.D, esize)
+    return dict(w=w, layers=layers, us_step=us_step, steps=n, attn_us=attn_mean,
+                attn_us_median=attn_med, select_us=sel_mean, attn_bytes=abytes,
+                summary_bytes=sbytes)
+
+
+def cpu_baseline(w, lay, budget_s=12.0):
+    """The oracle's decode step (tail summary + scores + top-k + attention) on the host, for a
+    bounded number of repetitions of the same workload; also checks the GPU's step output."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+
+    scale = K.default_scale(w.D)
+    summ = O.page_summaries(w.k_pool, w.page_table, w.seq_lens, w.P)  # prefill, untimed
+    times = []
+    with threadpool_limits(limits=1):
+        t_end = time.perf_counter() + budget_s
+        while True:
+            t0 = time.perf_counter()
+            for b in range(w.B):  # decode-time refresh of each tail page's summary
+                L = int(w.seq_lens[b])
+                n = (L - 1) // w.P
+                p = int(w.page_table[b, n])
+                toks = O.as_f64(w.k_pool[p, :, :L - n * w.P])
+                summ[p, :, 0] = toks.min(axis=1)
+                summ[p, :, 1] = toks.max(axis=1)
+            sel, cnt, out, lse = O.decode_step(w.q, summ, w.k_pool, w.v_pool, w.page_table,
+                                               w.seq_lens, w.P, w.k, scale)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() > t_end or len(times) >= 50:
+                break
+    ok_sel = bool(np.array_equal(lay.sel.cpu().numpy(), sel) and
+                  np.array_equal(lay.cnt.cpu().numpy(), cnt))
+    err = float(np.abs(lay.out.float().cpu().numpy() - out).max())
+    return dict(value=float(np.median(times)) * 1e6, unit="us/step", cores=1, kind="oracle",
+                sample=f"{len(times)} full decode steps of the same workload (B={w.B}, "
+                       f"ctx={int(w.seq_lens.max())}), fp64 NumPy, 1 thread",
+                parity=dict(selection_bit_exact=ok_sel, attention_max_abs_err=err))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="llama8b_32k")
+    ap.add_argument("--layers", type=int, default=8, help="cache copies rotated like layers")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    K.lib()
+
+    m = measure(args.workload, dev, args.steps, args.warmup, args.layers)
+    w = m["w"]
+    achieved = m["attn_bytes"] / (m["attn_us"] * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(m["us_step"], 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": m["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(m["us_step"] / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+            "head_dim": w.D, "context": int(w.seq_lens.max()), "page_size": w.P,
+            "topk_pages": w.k, "layers_rotated": args.layers,
+            "step": "tail-page summary refresh + page scores + top-k + sparse attention",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "attn_kernel (kvsel_sparse_decode_attn: split-K + fused merge, one launch)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes": m["attn_bytes"],
+            "avg_us": round(m["attn_us"], 3),
+            "median_us": round(m["attn_us_median"], 3),
+        },
+        "select_us": round(m["select_us"], 3),
+    }
+    keep = m["layers"][0]  # its last step's outputs are checked against the CPU oracle
+    del m["layers"]
+    torch.cuda.empty_cache()
+    if not args.no_secondary and args.workload != "qwen4b_128k":
+        s = measure("qwen4b_128k", dev, args.steps, args.warmup, max(2, args.layers // 2))
+        sach = s["attn_bytes"] / (s["attn_us"] * 1e-6) / 1e9
+        result["secondary"] = {"qwen4b_128k": {
+            "us_per_step": round(s["us_step"], 3), "attn_us": round(s["attn_us"], 3),
+            "attn_GBps": round(sach, 1), "attn_frac": round(sach / HBM_PEAK_GBPS, 4),
+            "select_us": round(s["select_us"], 3), "attn_bytes": s["attn_bytes"]}}
+        del s
+        torch.cuda.empty_cache()
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, keep)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -19,8 +19,11 @@
  *    h / G), head dim D in {64, 128}, page size P in {16, 32}, G in {1, 2, 4, 8}.
  *  - Element type (kvsel_paged_kv.dtype): KVSEL_F32 (float) or KVSEL_BF16 (bfloat16 bits in
  *    uint16). K, V, q, summaries and attention outputs all use it.
- *  - Pool: k_pool and v_pool are [num_phys_pages][Hkv][P][D], row-major. Physical page p, KV
- *    head j, slot s starts at element ((p * Hkv + j) * P + s) * D.
+ *  - Pools: k_pool is [num_phys_pages][Hkv][P][D] (token-major pages: key of physical page p,
+ *    KV head j, slot s starts at element ((p * Hkv + j) * P + s) * D). v_pool is
+ *    [num_phys_pages][Hkv][D][P] (channel-major pages: channel d of the values of page p, head j
+ *    is the run of P slots starting at ((p * Hkv + j) * D + d) * P), so that the probability x
+ *    value contraction over a page's tokens reads consecutive tokens.
  *  - page_table is int32 [B][max_pages_per_seq]: logical page n of sequence b lives in physical
  *    page page_table[b][n]. seq_lens is int32 [B]; sequence b has N_b = ceil(seq_lens[b] / P)
  *    logical pages, and slot s of logical page n is valid iff n * P + s < seq_lens[b]. Table
@@ -61,6 +64,9 @@ typedef int32_t kvsel_status;
 #define KVSEL_OP_SCORE_TOPK 1
 #define KVSEL_OP_ATTENTION 2
 
+/* Flags of kvsel_score_topk. */
+#define KVSEL_SCORE_REFRESH_TAIL 1 /* rebuild each sequence's last-page summary first */
+
 /* Host struct describing one paged KV cache (device pointers inside). */
 typedef struct kvsel_paged_kv {
   int32_t dtype;             /* KVSEL_F32 or KVSEL_BF16                              */
@@ -72,7 +78,7 @@ typedef struct kvsel_paged_kv {
   int32_t num_phys_pages;    /* pages in the pool                                    */
   int32_t max_pages_per_seq; /* row length of page_table                             */
   const void* k_pool;        /* [num_phys_pages][Hkv][P][D]                          */
-  const void* v_pool;        /* [num_phys_pages][Hkv][P][D] (may be NULL where unused) */
+  const void* v_pool;        /* [num_phys_pages][Hkv][D][P] (may be NULL where unused) */
   const int32_t* page_table; /* [B][max_pages_per_seq]                               */
   const int32_t* seq_lens;   /* [B]                                                  */
 } kvsel_paged_kv;
@@ -116,7 +122,9 @@ const char* kvsel_status_str(kvsel_status status);
 
 /* Bytes of device workspace `op` needs for this cache descriptor, top-k size k and (for
  * KVSEL_OP_ATTENTION) pages_per_split (0 = the library's choice). Returns 0 for invalid input.
- * Pure host arithmetic: touches no device. */
+ * Pure host arithmetic: touches no device.
+ * A workspace may be reused by later calls on the same stream; two calls in flight at once must
+ * not share one. */
 size_t kvsel_workspace_bytes(const kvsel_paged_kv* kv, int32_t k, int32_t op,
                              int32_t pages_per_split);
 
@@ -133,7 +141,7 @@ size_t kvsel_workspace_bytes(const kvsel_paged_kv* kv, int32_t k, int32_t op,
 kvsel_status kvsel_build_summaries(const kvsel_paged_kv* kv, const kvsel_rope* rope,
                                    int32_t tail_only, void* summ, void* stream);
 
-/* Query-aware page scoring and top-k selection, per (sequence, KV head).
+/* Query-aware page scoring and top-k selection, per (sequence, KV head), in one launch.
  * score[b][j][n] = fp32 rounding of the fp64 sum over the G query heads g of KV head j and the D
  * channels d of (q[b][jG+g][d] >= 0 ? q*hi : q*lo) with lo/hi from summ of page page_table[b][n]
  * (an upper bound of sum_g q_g . k over the page's keys). Products are exact in fp64 and the sum
@@ -144,11 +152,17 @@ kvsel_status kvsel_build_summaries(const kvsel_paged_kv* kv, const kvsel_rope* r
  * scores (fp32 [B][Hkv][max_pages_per_seq], may be NULL) receives the scores of n < N_b.
  * reuse (may be NULL) adds the speculative-reuse decision described at kvsel_reuse, evaluated on
  * this call's fresh selection.
- * ws / ws_bytes: device workspace of kvsel_workspace_bytes(kv, k, KVSEL_OP_SCORE_TOPK, 0) bytes.
+ * flags: KVSEL_SCORE_REFRESH_TAIL first rebuilds summ for each sequence's last logical page from
+ * the key pool (rotated by `rope` when non-NULL), exactly as kvsel_build_summaries with
+ * tail_only would, and scores that page from the fresh values (the decode-append step).
+ * Without the flag summ is only read and rope is ignored.
+ * ws / ws_bytes: with scores == NULL, a device workspace of at least
+ * kvsel_workspace_bytes(kv, k, KVSEL_OP_SCORE_TOPK, 0) bytes holds the scores; otherwise unused.
  * [FreeKV] sections 1 and 2.1. */
-kvsel_status kvsel_score_topk(const kvsel_paged_kv* kv, const void* summ, const void* q,
-                              int32_t k, int32_t* sel_idx, int32_t* sel_cnt, float* scores,
-                              const kvsel_reuse* reuse, void* ws, size_t ws_bytes, void* stream);
+kvsel_status kvsel_score_topk(const kvsel_paged_kv* kv, const kvsel_rope* rope, void* summ,
+                              const void* q, int32_t k, int32_t flags, int32_t* sel_idx,
+                              int32_t* sel_cnt, float* scores, const kvsel_reuse* reuse, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /* Sparse paged decode attention over the selected pages.
  * For every sequence b and query head h (KV head j = h / G), over the valid slots t of the
@@ -157,9 +171,11 @@ kvsel_status kvsel_score_topk(const kvsel_paged_kv* kv, const void* summ, const 
  * with fp32 arithmetic (K/V read in the element type). out is [B][Hq][D] in the element type;
  * lse is fp32 [B][Hq] and may be NULL. A (b, h) with nothing selected gets out = 0 and
  * lse = -inf. The work is split over groups of pages_per_split consecutive selected pages
- * (0 = the library's choice) and the splits are merged by log-sum-exp.
+ * (0 = the library's choice; a request is rounded to a supported size, and raised so that a list
+ * has at most 256 splits) and the splits are merged by log-sum-exp in a second launch.
  * rope != NULL rotates each key on the fly (bit-identical to a pool rotated by kvsel_rope_shift).
- * ws / ws_bytes: kvsel_workspace_bytes(kv, k, KVSEL_OP_ATTENTION, pages_per_split) bytes.
+ * ws / ws_bytes: workspace of kvsel_workspace_bytes(kv, k, KVSEL_OP_ATTENTION, pages_per_split)
+ * bytes for the split partials (0 bytes, and ws may be NULL, when there is a single split).
  * [FreeKV] section 2.1 (attention over the retrieved pages), [KV wiki] (decode attention, GQA). */
 kvsel_status kvsel_sparse_decode_attn(const kvsel_paged_kv* kv, const kvsel_rope* rope,
                                       const void* q, const int32_t* sel_idx,
@@ -168,7 +184,9 @@ kvsel_status kvsel_sparse_decode_attn(const kvsel_paged_kv* kv, const kvsel_rope
                                       size_t ws_bytes, void* stream);
 
 /* Rotary table: cos[r][i], sin[r][i] (fp32 [n_rows][D/2]) of the angle
- * (first_position + r) * theta^(-2i/D), evaluated in fp64 and rounded to fp32.
+ * (first_position + r) * theta^(-2i/D), evaluated in fp64 and rounded to fp32. head_dim is even
+ * and <= 128. The D/2 frequencies theta^(-2i/D) are evaluated once on the host with the C
+ * library's pow; angles and their cos / sin are evaluated on the device.
  * [KV Packet] section 1 (RoPE encodes position by rotation). */
 kvsel_status kvsel_rope_table(double theta, int32_t head_dim, int32_t first_position,
                               int32_t n_rows, float* cos, float* sin, void* stream);
@@ -176,7 +194,8 @@ kvsel_status kvsel_rope_table(double theta, int32_t head_dim, int32_t first_posi
 /* Materialized rotary re-positioning: writes the rotated keys of every physical page with
  * page_row[p] >= 0 into k_out ([num_phys_pages][Hkv][P][D], element type) and copies the other
  * pages unchanged. k_out may equal kv->k_pool (in place; unrotated pages are then skipped).
- * Only kv->dtype, num_kv_heads, head_dim, page_size, num_phys_pages and k_pool are used.
+ * Only the pool fields of kv (dtype, num_kv_heads, head_dim, page_size, num_phys_pages,
+ * k_pool) are read, but kv must still pass the descriptor checks.
  * [KV Packet] section 1. */
 kvsel_status kvsel_rope_shift(const kvsel_paged_kv* kv, const kvsel_rope* rope, void* k_out,
                               void* stream);

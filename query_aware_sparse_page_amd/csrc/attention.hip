@@ -1,17 +1,32 @@
-// Sparse paged decode attention (split-K over the selected pages) and the log-sum-exp merge.
+// Sparse paged decode attention on the matrix cores: split-K over the selected pages, then a
+// log-sum-exp merge of the splits in a second launch.
 //
-// attn_split_kernel: one 256-thread block per (split, KV head, sequence). A split is pps
-// consecutive entries of the selection list (pps * P rows); each of the 4 waves owns CPW chunks
-// of RPW rows. All K and V loads of the block are issued before any arithmetic (16-byte
-// coalesced slices, LPR lanes per row), so a block has its whole 2 * pps * P * D-element tile in
-// flight at once. The whole GQA group (G query heads) is served from one read of K and V.
-// Per wave: z = scale * q.k folded over the LPR lanes of a row, a wave-wide max, p = exp(z - m),
-// l = sum p, acc = sum p * v folded over the row groups. The 4 waves are then merged through LDS
-// and the block writes one (m, l, acc[D]) partial per query head -- or, with a single split,
-// the normalized output directly.
+// Work unit: a "tile" of TT token slots (TT = 32 for bf16, 16 for fp32) taken in order from the
+// concatenated selected pages of one list (= sequence, KV head). Grid: one block per
+// (split, list), list varying fastest, so that all splits of a list are placed on one XCD by the
+// round-robin block placement when the number of lists is a multiple of 8. A block has WAVES
+// waves; each wave owns TPW consecutive tiles, issues every K and V load of its tiles first,
+// then runs the contractions on MFMA with the GQA group of query heads as the M dimension
+// (rows >= G are zero and ignored):
 //
-// attn_merge_kernel: one block per (query head, sequence); thread d combines the partials of
-// channel d: M = max m_s, out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
+//  bf16 (v_mfma_f32_16x16x32_bf16; lane l: r16 = l % 16, q4 = l / 16):
+//   S^T = K q^T per 16-token half h: A = K rows (16 tokens x 32 channels), B = q^T (32 channels x
+//   16 heads). Row r of half h is token 8*(r/4) + 4h + r%4 of the tile, so after both halves
+//   lane l holds the scores of head r16 for the 8 consecutive tokens 8*q4 .. 8*q4+7 -- exactly
+//   the A operand of O = P V (16 heads x 32 tokens), with no data movement between lanes.
+//   B = V (32 tokens x 16 channels) wants 8 consecutive tokens of one channel per lane: V pages
+//   are stored channel-major ([D][P]), so that is one 16-byte load.
+//  fp32 (v_mfma_f32_16x16x4f32): the same shape with 4-deep steps; step s of q K^T takes channel
+//   (D/4)*q4 + s (a lane's 16-byte K loads cover its channels), step s of P V takes token
+//   4*q4 + s (a lane's 16-byte V load covers its tokens).
+//
+// Softmax: per wave a two-pass max / exp over its tiles (the max needs 2 cross-lane steps),
+// l accumulated per lane, O accumulated in the MFMA accumulators; the waves of a block merge
+// through LDS. One split: the block writes out / lse directly. Otherwise it writes its
+// (acc[G][D], m, l) partial and attn_merge_kernel (one block per list) combines the partials in
+// split order: M = max m_s, out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
+// Invalid token slots (past a sequence's end, or past the list's count) load as zeros and get
+// probability 0, so poisoned padding never reaches the accumulators.
 #include <math.h>
 
 #include "kvsel_device.h"
@@ -19,218 +34,528 @@
 
 namespace kvsel {
 
-template <typename T, int D, int G, int CPW>
-__global__ __launch_bounds__(256) void attn_split_kernel(
-    const T* __restrict__ k_pool, const T* __restrict__ v_pool,
-    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
-    const T* __restrict__ q, const int32_t* __restrict__ sel_idx,
-    const int32_t* __restrict__ sel_cnt, int Hkv, int P, int log2P, int maxp, int k, int pps,
-    int nsplit, float scale, RopeArgs rope, float* __restrict__ part_acc,
-    float2* __restrict__ part_ml, T* __restrict__ out, float* __restrict__ lse) {
-  using M = row_map<T, D>;
-  constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int ATT_MAX_SPLITS = 256;
+constexpr int MERGE_THREADS = 256;
+
+struct AttnArgs {
+  const void* k_pool;
+  const void* v_pool;   // channel-major pages: [Npp][Hkv][D][P]
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const void* q;
+  const int32_t* sel_idx;
+  const int32_t* sel_cnt;
+  int Hkv, P, log2P, maxp, k, pps, nsplit, nlists;
+  float scale;
+  RopeArgs rope;
+  float* part_acc;   // [nlists][nsplit][G][D]
+  float2* part_ml;   // [nlists][nsplit][G]
+  void* out;
+  float* lse;
+};
+
+// Wave-uniform page lookup of the NPT pages a tile of TT token slots touches (NPT = 2 when a
+// 32-slot tile spans two 16-slot pages). The addresses follow the selection id and page-table
+// entry as read (an id out of range is clamped to a valid entry), and the list count only
+// decides validity, so the dependent chain is id -> page table -> K / V with every id load in one
+// round and every page-table load in the next.
+template <int P, int TT, int TPW>
+struct TilePages {
+  static constexpr int NPT = TT > P ? TT / P : 1;
+  int page[TPW][NPT];   // physical page to address (always a valid page)
+  int valid[TPW][NPT];  // valid slots of that page; 0 when the slot range is not in the list
+};
+
+template <int P, int TT, int TPW>
+__device__ __forceinline__ void lookup_tiles(const AttnArgs& a, int list, int b, int split,
+                                             int first_tile, TilePages<P, TT, TPW>& tp) {
+  constexpr int NPT = TilePages<P, TT, TPW>::NPT;
+  int n[TPW][NPT];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int sp = split * a.pps + ((first_tile + t) * TT) / P + u;
+      n[t][u] = sp < a.k ? __builtin_amdgcn_readfirstlane(a.sel_idx[(size_t)list * a.k + sp]) : -1;
+    }
+  const int cnt = __builtin_amdgcn_readfirstlane(min(a.sel_cnt[list], a.k));
+  const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int nn = n[t][u];
+      const bool in_range = nn >= 0 && nn < a.maxp;
+      tp.page[t][u] =
+          __builtin_amdgcn_readfirstlane(a.page_table[(size_t)b * a.maxp + (in_range ? nn : 0)]);
+      const int sp = split * a.pps + ((first_tile + t) * TT) / P + u;
+      tp.valid[t][u] = (in_range && sp < cnt) ? min(P, L - nn * P) : 0;
+    }
+}
+
+// Rotate-half rotation of one channel pair held by the same lane (bits identical to
+// rope_rotate_slice).
+template <typename T>
+__device__ __forceinline__ void rope_pair(float& x1, float& x2, float c, float s) {
+  const float y1 = rot_sub(rot_mul(x1, c), rot_mul(x2, s));
+  const float y2 = rot_add(rot_mul(x2, c), rot_mul(x1, s));
+  x1 = round_to_elem<T>(y1);
+  x2 = round_to_elem<T>(y2);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+  bf16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float* f) { return pack<bf16_t>(f); }
+
+// Zero the bf16 elements e of v whose bit e of `keep` is clear (invalid token slots).
+__device__ __forceinline__ uint4 mask_bf16x8(const uint4& v, int keep) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] &= ((keep >> (2 * i)) & 1 ? 0x0000ffffu : 0u) | ((keep >> (2 * i + 1)) & 1 ? 0xffff0000u : 0u);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Zero the fp32 elements e of v whose bit e of `keep` is clear.
+__device__ __forceinline__ uint4 mask_f32x4(const uint4& v, int keep) {
+  return make_uint4((keep & 1) ? v.x : 0u, (keep & 2) ? v.y : 0u, (keep & 4) ? v.z : 0u,
+                    (keep & 8) ? v.w : 0u);
+}
+
+constexpr int ATT_MAX_G = 8;
+
+// Block-level merge of the waves' (m, l, O) and the write of the block's result.
+template <typename T, int D, int WAVES>
+__device__ __forceinline__ void finish_block(const AttnArgs& a, int G, int list, int split, int b,
+                                             int j, float (*s_m)[ATT_MAX_G],
+                                             float (*s_l)[ATT_MAX_G],
+                                             float (*s_o)[ATT_MAX_G][D]) {
   const float NEG_INF = __int_as_float(0xff800000);
-
-  const int split = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int rg = lane / LPR, c0 = (lane % LPR) * VEC;
-  const size_t list = (size_t)b * Hkv + j;
-  const int cnt = min(sel_cnt[list], k);
-  const int L = seq_lens[b];
-  const int Hq = Hkv * G;
-
-  // ---- issue every K / V load of this wave first ----
-  uint4 kraw[CPW], vraw[CPW];
-  bool valid[CPW];
-  int rrow[CPW];
-#pragma unroll
-  for (int i = 0; i < CPW; ++i) {
-    const int r0 = (w * CPW + i) * RPW;  // first row of the chunk (wave-uniform)
-    const int sp = split * pps + (r0 >> log2P);
-    const int s = (r0 & (P - 1)) + rg;
-    bool ok = false;
-    size_t off = 0;
-    rrow[i] = -1;
-    if (sp < cnt) {
-      const int n = sel_idx[list * k + sp];
-      const int p = n >= 0 && n < maxp ? page_table[(size_t)b * maxp + n] : 0;
-      ok = n >= 0 && n < maxp && n * P + s < L;
-      off = (((size_t)p * Hkv + j) * P + s) * D + c0;
-      if (rope.page_row) {
-        const int pr = rope.page_row[p];
-        rrow[i] = pr < 0 ? -1 : pr + rope.row_step * s;
-      }
-    }
-    kraw[i] = ok ? load16(k_pool + off) : make_uint4(0, 0, 0, 0);
-    vraw[i] = ok ? load16(v_pool + off) : make_uint4(0, 0, 0, 0);
-    valid[i] = ok;
-  }
-
-  float qf[G][VEC];
-#pragma unroll
-  for (int g = 0; g < G; ++g) unpack<T>(load16(q + ((size_t)b * Hq + j * G + g) * D + c0), qf[g]);
-
-  // ---- scores of this wave's rows ----
-  float z[CPW][G];
-#pragma unroll
-  for (int i = 0; i < CPW; ++i) {
-    float kf[VEC];
-    unpack<T>(kraw[i], kf);
-    if (rope.page_row) rope_rotate_slice<T, D>(kf, c0, rrow[i], rope.cos, rope.sin);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float s = 0.0f;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) s = fmaf(qf[g][e], kf[e], s);
-#pragma unroll
-      for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m);
-      z[i][g] = valid[i] ? s * scale : NEG_INF;
-    }
-  }
-  float mx[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float m = z[0][g];
-#pragma unroll
-    for (int i = 1; i < CPW; ++i) m = fmaxf(m, z[i][g]);
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-    mx[g] = m;
-  }
-  float l[G], acc[G][VEC];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    l[g] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[g][e] = 0.0f;
-  }
-#pragma unroll
-  for (int i = 0; i < CPW; ++i) {
-    float vf[VEC];
-    unpack<T>(vraw[i], vf);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float pz = valid[i] ? __expf(z[i][g] - mx[g]) : 0.0f;
-      l[g] += pz;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[g][e] = fmaf(pz, vf[e], acc[g][e]);
-    }
-  }
-#pragma unroll
-  for (int o = LPR; o < 64; o <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      l[g] += __shfl_xor(l[g], o);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[g][e] += __shfl_xor(acc[g][e], o);
-    }
-  }
-
-  // ---- merge the 4 waves ----
-  __shared__ float s_m[4][G], s_l[4][G];
-  __shared__ float s_acc[4][G][D];
-  if (rg == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) s_acc[w][g][c0 + e] = acc[g][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      s_m[w][g] = mx[g];
-      s_l[w][g] = l[g];
-    }
-  }
+  const int Hq = a.Hkv * G;
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * D; idx += WAVES * 64) {
     const int g = idx / D, d = idx % D;
     float Mx = s_m[0][g];
 #pragma unroll
-    for (int v = 1; v < 4; ++v) Mx = fmaxf(Mx, s_m[v][g]);
+    for (int v = 1; v < WAVES; ++v) Mx = fmaxf(Mx, s_m[v][g]);
     float Ls = 0.0f, A = 0.0f;
     if (Mx != NEG_INF) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
+      for (int v = 0; v < WAVES; ++v) {
         if (s_m[v][g] != NEG_INF) {
           const float f = __expf(s_m[v][g] - Mx);
           Ls = fmaf(s_l[v][g], f, Ls);
-          A = fmaf(s_acc[v][g][d], f, A);
+          A = fmaf(s_o[v][g][d], f, A);
         }
       }
     }
-    if (nsplit == 1) {
+    if (a.nsplit == 1) {
       const size_t o = ((size_t)b * Hq + j * G + g) * D + d;
-      store_elem<T>(out, o, Mx == NEG_INF ? 0.0f : A / Ls);
-      if (d == 0 && lse) lse[(size_t)b * Hq + j * G + g] = Mx == NEG_INF ? NEG_INF : Mx + logf(Ls);
+      store_elem<T>((T*)a.out, o, Mx == NEG_INF ? 0.0f : A / Ls);
+      if (d == 0 && a.lse)
+        a.lse[(size_t)b * Hq + j * G + g] = Mx == NEG_INF ? NEG_INF : Mx + logf(Ls);
     } else {
-      const size_t ps = (list * nsplit + split) * G + g;
-      part_acc[ps * D + d] = A;
-      if (d == 0) part_ml[ps] = make_float2(Mx, Ls);
+      const size_t ps = ((size_t)list * a.nsplit + split) * G + g;
+      a.part_acc[ps * D + d] = A;
+      if (d == 0) a.part_ml[ps] = make_float2(Mx, Ls);
     }
   }
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part_acc,
-                                                         const float2* __restrict__ part_ml,
-                                                         int Hkv, int G, int nsplit,
-                                                         T* __restrict__ out, float* __restrict__ lse) {
+// ------------------------------------------------------------------------------------------
+// bf16
+// ------------------------------------------------------------------------------------------
+template <int D, int P, int WAVES, int TPW, bool ROPE>
+__global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a, int G) {
+  constexpr int TT = 32;       // tokens per tile
+  constexpr int CB = D / 32;   // 32-channel blocks of q K^T
+  constexpr int VB = D / 16;   // 16-channel blocks of P V
+  using TP = TilePages<P, TT, TPW>;
   const float NEG_INF = __int_as_float(0xff800000);
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int j = h / G, g = h % G;
-  const size_t list = (size_t)b * Hkv + j;
-  const int Hq = Hkv * G;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float Mx = NEG_INF;
-    for (int s = 0; s < nsplit; ++s) Mx = fmaxf(Mx, part_ml[(list * nsplit + s) * G + g].x);
-    const size_t o = ((size_t)b * Hq + h) * D + d;
-    if (Mx == NEG_INF) {
-      store_elem<T>(out, o, 0.0f);
-      if (d == 0 && lse) lse[(size_t)b * Hq + h] = NEG_INF;
-      continue;
-    }
-    float Ls = 0.0f, A = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-      const size_t ps = (list * nsplit + s) * G + g;
-      const float2 ml = part_ml[ps];
-      if (ml.x != NEG_INF) {
-        const float f = __expf(ml.x - Mx);
-        Ls = fmaf(ml.y, f, Ls);
-        A = fmaf(part_acc[ps * D + d], f, A);
+  const int list = blockIdx.x % a.nlists, split = blockIdx.x / a.nlists;
+  const int b = list / a.Hkv, j = list % a.Hkv;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int Hq = a.Hkv * G;
+  const bf16_t* kp = (const bf16_t*)a.k_pool;
+  const bf16_t* vp = (const bf16_t*)a.v_pool;
+
+  // q^T operand (independent of the selection): q[head r16][32 cb + 8 q4 .. +8], zero rows >= G
+  // (loads below are unconditional, from clamped valid addresses, and masked where used: a
+  // conditional load makes the compiler wait for it before issuing the next one)
+  uint4 qraw[CB];
+  {
+    const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)b * Hq + j * G + min(r16, G - 1)) * D + 8 * q4;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) qraw[cb] = load16(qrow + 32 * cb);
+  }
+
+  TP tp;
+  lookup_tiles<P, TT, TPW>(a, list, b, split, w * TPW, tp);
+
+  // ---- every K / V load of this wave's tiles ----
+  uint4 kraw[TPW][2][CB], vraw[TPW][VB];
+  int vmask[TPW];  // bit e set: token 8*q4 + e of the tile is valid
+  int krow[TPW][2];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int x = 8 * (r16 / 4) + 4 * h + (r16 % 4);  // token of row r16 in half h
+      const int u = x / P, slot = x % P;
+      const int pg = tp.page[t][u];
+      // an invalid token's row of S^T is masked to -inf below (rows of an MFMA are
+      // independent), so its K needs no zeroing
+      const bf16_t* row = kp + (((size_t)pg * a.Hkv + j) * P + slot) * D + 8 * q4;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) kraw[t][h][cb] = load16(row + 32 * cb);
+      if (ROPE) {
+        const int pr = a.rope.page_row[pg];
+        krow[t][h] = pr < 0 ? -1 : pr + a.rope.row_step * slot;
       }
     }
-    store_elem<T>(out, o, A / Ls);
-    if (d == 0 && lse) lse[(size_t)b * Hq + h] = Mx + logf(Ls);
+    const int xv = 8 * q4;  // first of the lane's 8 value tokens
+    const int u = xv / P, slot = xv % P;
+    const int pg = tp.page[t][u];
+    int m = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m |= (slot + e < tp.valid[t][u]) ? (1 << e) : 0;
+    vmask[t] = m;
+    const bf16_t* vt = vp + ((size_t)pg * a.Hkv + j) * D * P + slot + (size_t)r16 * P;
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = load16(vt + (size_t)(16 * vb) * P);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use
+
+  // ---- S^T = K q^T ----
+  f32x4_t s[TPW][2];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (ROPE) {
+        // rotate-half pairs (c, c + D/2) sit in blocks cb and cb + CB/2 of the same lane
+        const int row = krow[t][h];
+        if (row >= 0) {
+#pragma unroll
+          for (int cb = 0; cb < CB / 2; ++cb) {
+            float x1[8], x2[8];
+            unpack<bf16_t>(kraw[t][h][cb], x1);
+            unpack<bf16_t>(kraw[t][h][cb + CB / 2], x2);
+            const float* cr = a.rope.cos + (size_t)row * (D / 2) + 32 * cb + 8 * q4;
+            const float* sr = a.rope.sin + (size_t)row * (D / 2) + 32 * cb + 8 * q4;  // row >= 0 here
+            float cv[8], sv[8];
+            unpack<float>(load16(cr), cv);
+            unpack<float>(load16(cr + 4), cv + 4);
+            unpack<float>(load16(sr), sv);
+            unpack<float>(load16(sr + 4), sv + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rope_pair<bf16_t>(x1[e], x2[e], cv[e], sv[e]);
+            kraw[t][h][cb] = pack_bf16x8(x1);
+            kraw[t][h][cb + CB / 2] = pack_bf16x8(x2);
+          }
+        }
+      }
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kraw[t][h][cb]), as_bf16x8(qraw[cb]),
+                                                      acc, 0, 0, 0);
+      s[t][h] = acc;
+    }
+  }
+
+  // ---- softmax over the wave's tokens (head r16; tokens 8*q4 + 4h + i of each tile) ----
+  float z[TPW][8];
+  float m = NEG_INF;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = s[t][e >> 2][e & 3] * a.scale;
+      z[t][e] = ((vmask[t] >> e) & 1) && r16 < G ? v : NEG_INF;
+      m = fmaxf(m, z[t][e]);
+    }
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  float l = 0.0f;
+  f32x4_t o[VB];
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb) o[vb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // P enters the MFMA as bf16: normalize by the sum of the rounded values, so the weights
+      // applied to V sum to one exactly
+      p[e] = z[t][e] == NEG_INF ? 0.0f : round_to_elem<bf16_t>(__expf(z[t][e] - m));
+      l += p[e];
+    }
+    const bf16x8_t pa = as_bf16x8(pack_bf16x8(p));
+    const bool partial = vmask[t] != 0xff;  // zero invalid slots (0 * NaN poison is NaN)
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) {
+      const uint4 vv = partial ? mask_bf16x8(vraw[t][vb], vmask[t]) : vraw[t][vb];
+      o[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(vv), o[vb], 0, 0, 0);
+    }
+  }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+
+  // ---- merge the block's waves through LDS ----
+  __shared__ float s_m[WAVES][ATT_MAX_G], s_l[WAVES][ATT_MAX_G];
+  __shared__ float s_o[WAVES][ATT_MAX_G][D];
+  if (q4 == 0 && r16 < G) {
+    s_m[w][r16] = m;
+    s_l[w][r16] = l;
+  }
+  if (4 * q4 < G) {  // lanes holding rows (heads) 4*q4 .. 4*q4+3
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_o[w][4 * q4 + i][16 * vb + r16] = o[vb][i];
+  }
+  finish_block<bf16_t, D, WAVES>(a, G, list, split, b, j, s_m, s_l, s_o);
+}
+
+// ------------------------------------------------------------------------------------------
+// fp32
+// ------------------------------------------------------------------------------------------
+template <int D, int P, int WAVES, int TPW, bool ROPE>
+__global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(AttnArgs a, int G) {
+  constexpr int TT = 16;       // tokens per tile
+  constexpr int KC = D / 4;    // channels per lane in q K^T (4 lane groups)
+  constexpr int KL = KC / 4;   // 16-byte loads per lane per token
+  constexpr int VB = D / 16;   // 16-channel blocks of P V
+  using TP = TilePages<P, TT, TPW>;
+  const float NEG_INF = __int_as_float(0xff800000);
+  const int list = blockIdx.x % a.nlists, split = blockIdx.x / a.nlists;
+  const int b = list / a.Hkv, j = list % a.Hkv;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int Hq = a.Hkv * G;
+  const float* kp = (const float*)a.k_pool;
+  const float* vp = (const float*)a.v_pool;
+
+  float qv[KC];
+  {
+    // unconditional loads from clamped addresses, masked where used (see the bf16 kernel)
+    const float* qrow = (const float*)a.q + ((size_t)b * Hq + j * G + min(r16, G - 1)) * D + KC * q4;
+#pragma unroll
+    for (int u = 0; u < KL; ++u) unpack<float>(load16(qrow + 4 * u), qv + 4 * u);
+    if (r16 >= G) {
+#pragma unroll
+      for (int c = 0; c < KC; ++c) qv[c] = 0.0f;
+    }
+  }
+  TP tp;
+  lookup_tiles<P, TT, TPW>(a, list, b, split, w * TPW, tp);
+
+  uint4 kraw[TPW][KL], vraw[TPW][VB];
+  int vmask[TPW];
+  int krow[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int tile = w * TPW + t;
+    const int base = (tile * TT) % P;  // first slot of the tile within its page
+    const int pg = tp.page[t][0];
+    const int slot = base + r16;
+    const float* row = kp + (((size_t)pg * a.Hkv + j) * P + slot) * D + KC * q4;
+#pragma unroll
+    for (int u = 0; u < KL; ++u) kraw[t][u] = load16(row + 4 * u);
+    if (ROPE) {
+      const int pr = a.rope.page_row[pg];
+      krow[t] = pr < 0 ? -1 : pr + a.rope.row_step * slot;
+    }
+    const int vslot = base + 4 * q4;
+    int mk = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mk |= (vslot + e < tp.valid[t][0]) ? (1 << e) : 0;
+    vmask[t] = mk;
+    const float* vt = vp + ((size_t)pg * a.Hkv + j) * D * P + vslot + (size_t)r16 * P;
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = load16(vt + (size_t)(16 * vb) * P);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use
+
+  f32x4_t s[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    float kv[KC];
+#pragma unroll
+    for (int u = 0; u < KL; ++u) unpack<float>(kraw[t][u], kv + 4 * u);
+    if (ROPE) {
+      // rotate-half partner of channel c (lane group q4) is in lane group q4 ^ 2; every lane
+      // group of token r16 computed the same table row
+      const int row = krow[t];
+      float pv[KC];
+#pragma unroll
+      for (int e = 0; e < KC; ++e) pv[e] = __shfl_xor(kv[e], 32);
+      if (row >= 0) {
+        const bool first = q4 < 2;
+        const int i0 = first ? KC * q4 : KC * q4 - D / 2;
+        const float* cr = a.rope.cos + (size_t)row * (D / 2) + i0;
+        const float* sr = a.rope.sin + (size_t)row * (D / 2) + i0;
+#pragma unroll
+        for (int e = 0; e < KC; ++e) {
+          float x1 = first ? kv[e] : pv[e], x2 = first ? pv[e] : kv[e];
+          rope_pair<float>(x1, x2, cr[e], sr[e]);
+          kv[e] = first ? x1 : x2;
+        }
+      }
+    }
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[c], qv[c], acc, 0, 0, 0);
+    s[t] = acc;
+  }
+  float z[TPW][4];
+  float m = NEG_INF;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = s[t][i] * a.scale;
+      z[t][i] = ((vmask[t] >> i) & 1) && r16 < G ? v : NEG_INF;
+      m = fmaxf(m, z[t][i]);
+    }
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  float l = 0.0f;
+  f32x4_t o[VB];
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb) o[vb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = z[t][i] == NEG_INF ? 0.0f : __expf(z[t][i] - m);
+      l += p[i];
+    }
+    const bool partial = vmask[t] != 0xf;
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) {
+      float vv[4];
+      unpack<float>(partial ? mask_f32x4(vraw[t][vb], vmask[t]) : vraw[t][vb], vv);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        o[vb] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[st], vv[st], o[vb], 0, 0, 0);
+    }
+  }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+
+  __shared__ float s_m[WAVES][ATT_MAX_G], s_l[WAVES][ATT_MAX_G];
+  __shared__ float s_o[WAVES][ATT_MAX_G][D];
+  if (q4 == 0 && r16 < G) {
+    s_m[w][r16] = m;
+    s_l[w][r16] = l;
+  }
+  if (4 * q4 < G) {
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_o[w][4 * q4 + i][16 * vb + r16] = o[vb][i];
+  }
+  finish_block<float, D, WAVES>(a, G, list, split, b, j, s_m, s_l, s_o);
+}
+
+// ------------------------------------------------------------------------------------------
+// merge: one block per list, every partial load of a thread issued together
+// ------------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(MERGE_THREADS) void attn_merge_kernel(AttnArgs a, int G) {
+  const float NEG_INF = __int_as_float(0xff800000);
+  const int list = blockIdx.x;
+  const int b = list / a.Hkv, j = list % a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int Hq = a.Hkv * G;
+  const int ns = a.nsplit;
+  __shared__ float s_w[ATT_MAX_SPLITS][ATT_MAX_G];
+  __shared__ float s_M[ATT_MAX_G], s_L[ATT_MAX_G];
+  const float2* ml = a.part_ml + (size_t)list * ns * G;
+  for (int g = w; g < G; g += MERGE_THREADS / 64) {
+    float mx = NEG_INF;
+    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, ml[s * G + g].x);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float ls = 0.0f;
+    for (int s = lane; s < ns; s += 64) {
+      const float2 v = ml[s * G + g];
+      const float f = (mx == NEG_INF || v.x == NEG_INF) ? 0.0f : __expf(v.x - mx);
+      s_w[s][g] = f;
+      ls = fmaf(v.y, f, ls);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) ls += __shfl_xor(ls, o);
+    if (lane == 0) {
+      s_M[g] = mx;
+      s_L[g] = ls;
+    }
+  }
+  __syncthreads();
+  const float* pa = a.part_acc + (size_t)list * ns * G * D;
+  for (int idx = tid; idx < G * D; idx += MERGE_THREADS) {
+    const int g = idx / D, d = idx % D;
+    float A = 0.0f;
+    int s = 0;
+    for (; s + 8 <= ns; s += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pa[((size_t)(s + u) * G + g) * D + d];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) A = fmaf(v[u], s_w[s + u][g], A);
+    }
+    for (; s < ns; ++s) A = fmaf(pa[((size_t)s * G + g) * D + d], s_w[s][g], A);
+    const size_t o = ((size_t)b * Hq + j * G + g) * D + d;
+    const bool empty = s_M[g] == NEG_INF;
+    store_elem<T>((T*)a.out, o, empty ? 0.0f : A / s_L[g]);
+    if (d == 0 && a.lse) a.lse[(size_t)b * Hq + j * G + g] = empty ? NEG_INF : s_M[g] + logf(s_L[g]);
   }
 }
 
-// ---- host side ----
+// ------------------------------------------------------------------------------------------
+// host side
+// ------------------------------------------------------------------------------------------
 
-static int rows_per_wave_load(const LaunchKV& kv) {
-  const int vec = kv.dtype == 0 ? 4 : 8;
-  return 64 / (kv.D / vec);
-}
-
-// Chunks per wave for a split of pps pages, or 0 when that split size has no kernel.
-static int chunks_per_wave(const LaunchKV& kv, int pps) {
+// Tiles per split for a request of pps pages; 0 when the split size has no kernel. A split is
+// WAVES * TPW tiles with (WAVES, TPW) in {(1,1), (2,1), (4,1), (4,2)}.
+static int tiles_for(const LaunchKV& kv, int pps) {
+  const int tt = kv.dtype == 0 ? 16 : 32;
   const int rows = pps * kv.P;
-  const int per = 4 * rows_per_wave_load(kv);
-  if (rows % per) return 0;
-  const int cpw = rows / per;
-  return (cpw == 1 || cpw == 2 || cpw == 4 || cpw == 8) ? cpw : 0;
+  if (rows % tt) return 0;
+  const int tiles = rows / tt;
+  return (tiles == 1 || tiles == 2 || tiles == 4 || tiles == 8) ? tiles : 0;
 }
 
 int attention_pages_per_split(const LaunchKV& kv, int k, int requested) {
-  (void)k;
-  int want = requested > 0 ? requested : 2;
+  const int want = requested > 0 ? requested : 2;
+  int pps = 0;
   // largest supported split not above the request, else the smallest supported one
-  for (int p = want; p >= 1; --p)
-    if (chunks_per_wave(kv, p)) return p;
-  for (int p = want + 1; p <= 64; ++p)
-    if (chunks_per_wave(kv, p)) return p;
-  return 0;
+  for (int p = want; p >= 1 && !pps; --p)
+    if (tiles_for(kv, p)) pps = p;
+  for (int p = want + 1; p <= 64 && !pps; ++p)
+    if (tiles_for(kv, p)) pps = p;
+  // at most ATT_MAX_SPLITS splits per list
+  while (pps && (k + pps - 1) / pps > ATT_MAX_SPLITS) {
+    int next = 0;
+    for (int p = pps + 1; p <= 64 && !next; ++p)
+      if (tiles_for(kv, p)) next = p;
+    pps = next;
+  }
+  return pps;
 }
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t attention_workspace(const LaunchKV& kv, int k, int pages_per_split) {
   const int pps = attention_pages_per_split(kv, k, pages_per_split);
@@ -238,61 +563,41 @@ size_t attention_workspace(const LaunchKV& kv, int k, int pages_per_split) {
   const size_t nsplit = (size_t)((k + pps - 1) / pps);
   if (nsplit <= 1) return 0;
   const size_t parts = (size_t)kv.B * kv.Hkv * nsplit * kv.G;
-  const size_t acc_bytes = parts * kv.D * sizeof(float);
-  return ((acc_bytes + 255) & ~(size_t)255) + parts * sizeof(float2);
+  return align256(parts * kv.D * sizeof(float)) + parts * sizeof(float2);
 }
 
-template <typename T, int D, int G, int CPW>
-static void launch_split(const LaunchKV& kv, const RopeArgs& rope, const void* q,
-                         const int32_t* sel_idx, const int32_t* sel_cnt, int k, float scale,
-                         int pps, int nsplit, float* part_acc, float2* part_ml, void* out,
-                         float* lse, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_split_kernel<T, D, G, CPW>),
-                     dim3((unsigned)nsplit, (unsigned)kv.Hkv, (unsigned)kv.B), dim3(256), 0, stream,
-                     (const T*)kv.k_pool, (const T*)kv.v_pool, kv.page_table, kv.seq_lens,
-                     (const T*)q, sel_idx, sel_cnt, kv.Hkv, kv.P, kv.log2P, kv.maxp, k, pps, nsplit,
-                     scale, rope, part_acc, part_ml, (T*)out, lse);
-}
-
-template <typename T, int D, int G>
-static void launch_split_cpw(int cpw, const LaunchKV& kv, const RopeArgs& rope, const void* q,
-                             const int32_t* sel_idx, const int32_t* sel_cnt, int k, float scale,
-                             int pps, int nsplit, float* part_acc, float2* part_ml, void* out,
-                             float* lse, hipStream_t stream) {
-  switch (cpw) {
-    case 1: launch_split<T, D, G, 1>(kv, rope, q, sel_idx, sel_cnt, k, scale, pps, nsplit, part_acc, part_ml, out, lse, stream); break;
-    case 2: launch_split<T, D, G, 2>(kv, rope, q, sel_idx, sel_cnt, k, scale, pps, nsplit, part_acc, part_ml, out, lse, stream); break;
-    case 4: launch_split<T, D, G, 4>(kv, rope, q, sel_idx, sel_cnt, k, scale, pps, nsplit, part_acc, part_ml, out, lse, stream); break;
-    default: launch_split<T, D, G, 8>(kv, rope, q, sel_idx, sel_cnt, k, scale, pps, nsplit, part_acc, part_ml, out, lse, stream); break;
+template <typename T, int D, int P, int WAVES, int TPW>
+static void launch_split(const AttnArgs& a, int G, bool rope, hipStream_t stream) {
+  const dim3 grid((unsigned)((long)a.nlists * a.nsplit));
+  const dim3 block(WAVES * 64);
+  if constexpr (sizeof(T) == 2) {
+    if (rope) hipLaunchKernelGGL((attn_bf16_kernel<D, P, WAVES, TPW, true>), grid, block, 0, stream, a, G);
+    else hipLaunchKernelGGL((attn_bf16_kernel<D, P, WAVES, TPW, false>), grid, block, 0, stream, a, G);
+  } else {
+    if (rope) hipLaunchKernelGGL((attn_f32_kernel<D, P, WAVES, TPW, true>), grid, block, 0, stream, a, G);
+    else hipLaunchKernelGGL((attn_f32_kernel<D, P, WAVES, TPW, false>), grid, block, 0, stream, a, G);
   }
+}
+
+template <typename T, int D, int P>
+static hipError_t launch_tiles(int tiles, const AttnArgs& a, int G, bool rope, hipStream_t stream) {
+  switch (tiles) {
+    case 1: launch_split<T, D, P, 1, 1>(a, G, rope, stream); break;
+    case 2: launch_split<T, D, P, 2, 1>(a, G, rope, stream); break;
+    case 4: launch_split<T, D, P, 4, 1>(a, G, rope, stream); break;
+    default: launch_split<T, D, P, 4, 2>(a, G, rope, stream); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3((unsigned)a.nlists), dim3(MERGE_THREADS), 0,
+                     stream, a, G);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_attention_t(const LaunchKV& kv, const RopeArgs& rope, const void* q,
-                                     const int32_t* sel_idx, const int32_t* sel_cnt, int k,
-                                     float scale, int pps, void* out, float* lse, void* ws,
-                                     hipStream_t stream) {
-  const int nsplit = (k + pps - 1) / pps;
-  const int cpw = chunks_per_wave(kv, pps);
-  float* part_acc = nullptr;
-  float2* part_ml = nullptr;
-  if (nsplit > 1) {
-    const size_t parts = (size_t)kv.B * kv.Hkv * nsplit * kv.G;
-    part_acc = (float*)ws;
-    part_ml = (float2*)((char*)ws + (((parts * kv.D * sizeof(float)) + 255) & ~(size_t)255));
-  }
-  switch (kv.G) {
-    case 1: launch_split_cpw<T, D, 1>(cpw, kv, rope, q, sel_idx, sel_cnt, k, scale, pps, nsplit, part_acc, part_ml, out, lse, stream); break;
-    case 2: launch_split_cpw<T, D, 2>(cpw, kv, rope, q, sel_idx, sel_cnt, k, scale, pps, nsplit, part_acc, part_ml, out, lse, stream); break;
-    case 4: launch_split_cpw<T, D, 4>(cpw, kv, rope, q, sel_idx, sel_cnt, k, scale, pps, nsplit, part_acc, part_ml, out, lse, stream); break;
-    default: launch_split_cpw<T, D, 8>(cpw, kv, rope, q, sel_idx, sel_cnt, k, scale, pps, nsplit, part_acc, part_ml, out, lse, stream); break;
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nsplit == 1) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3((unsigned)kv.Hq, (unsigned)kv.B),
-                     dim3(D < 128 ? D : 128), 0, stream, part_acc, part_ml, kv.Hkv, kv.G, nsplit,
-                     (T*)out, lse);
-  return hipGetLastError();
+static hipError_t launch_p(int P, int tiles, const AttnArgs& a, int G, bool rope, hipStream_t stream) {
+  if (P == 16) return launch_tiles<T, D, 16>(tiles, a, G, rope, stream);
+  return launch_tiles<T, D, 32>(tiles, a, G, rope, stream);
 }
 
 hipError_t launch_attention(const LaunchKV& kv, const RopeArgs& rope, const void* q,
@@ -300,14 +605,41 @@ hipError_t launch_attention(const LaunchKV& kv, const RopeArgs& rope, const void
                             int pages_per_split, void* out, float* lse, void* ws,
                             hipStream_t stream) {
   const int pps = attention_pages_per_split(kv, k, pages_per_split);
-  if (kv.dtype == 0) {
-    if (kv.D == 64)
-      return launch_attention_t<float, 64>(kv, rope, q, sel_idx, sel_cnt, k, scale, pps, out, lse, ws, stream);
-    return launch_attention_t<float, 128>(kv, rope, q, sel_idx, sel_cnt, k, scale, pps, out, lse, ws, stream);
+  AttnArgs a;
+  a.k_pool = kv.k_pool;
+  a.v_pool = kv.v_pool;
+  a.page_table = kv.page_table;
+  a.seq_lens = kv.seq_lens;
+  a.q = q;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.Hkv = kv.Hkv;
+  a.P = kv.P;
+  a.log2P = kv.log2P;
+  a.maxp = kv.maxp;
+  a.k = k;
+  a.pps = pps;
+  a.nsplit = (k + pps - 1) / pps;
+  a.nlists = kv.B * kv.Hkv;
+  a.scale = scale;
+  a.rope = rope;
+  a.part_acc = nullptr;
+  a.part_ml = nullptr;
+  if (a.nsplit > 1) {
+    const size_t parts = (size_t)a.nlists * a.nsplit * kv.G;
+    a.part_acc = (float*)ws;
+    a.part_ml = (float2*)((char*)ws + align256(parts * kv.D * sizeof(float)));
   }
-  if (kv.D == 64)
-    return launch_attention_t<bf16_t, 64>(kv, rope, q, sel_idx, sel_cnt, k, scale, pps, out, lse, ws, stream);
-  return launch_attention_t<bf16_t, 128>(kv, rope, q, sel_idx, sel_cnt, k, scale, pps, out, lse, ws, stream);
+  a.out = out;
+  a.lse = lse;
+  const int tiles = tiles_for(kv, pps);
+  const bool r = rope.page_row != nullptr;
+  if (kv.dtype == 0) {
+    if (kv.D == 64) return launch_p<float, 64>(kv.P, tiles, a, kv.G, r, stream);
+    return launch_p<float, 128>(kv.P, tiles, a, kv.G, r, stream);
+  }
+  if (kv.D == 64) return launch_p<bf16_t, 64>(kv.P, tiles, a, kv.G, r, stream);
+  return launch_p<bf16_t, 128>(kv.P, tiles, a, kv.G, r, stream);
 }
 
 }  // namespace kvsel

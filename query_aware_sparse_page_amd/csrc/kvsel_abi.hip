@@ -81,8 +81,11 @@ kvsel_status flatten_rope(const kvsel_rope* rope, RopeArgs* out) {
   return KVSEL_OK;
 }
 
-size_t score_workspace(const LaunchKV& kv) {
-  return (size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float);
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Room for the scores when the caller does not provide a score buffer.
+size_t score_workspace(const LaunchKV& kv, bool with_scores) {
+  return with_scores ? align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float)) : 0;
 }
 
 kvsel_status launch_status(hipError_t e) { return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_LAUNCH; }
@@ -109,7 +112,7 @@ size_t kvsel_workspace_bytes(const kvsel_paged_kv* kv, int32_t k, int32_t op,
                              int32_t pages_per_split) {
   LaunchKV f;
   if (k < 1 || flatten(kv, 0, &f) != KVSEL_OK) return 0;
-  if (op == KVSEL_OP_SCORE_TOPK) return score_workspace(f);
+  if (op == KVSEL_OP_SCORE_TOPK) return score_workspace(f, true);
   if (op == KVSEL_OP_ATTENTION) return attention_workspace(f, k, pages_per_split);
   return 0;
 }
@@ -126,13 +129,17 @@ kvsel_status kvsel_build_summaries(const kvsel_paged_kv* kv, const kvsel_rope* r
   return launch_status(launch_summaries(f, r, tail_only ? 1 : 0, summ, (hipStream_t)stream));
 }
 
-kvsel_status kvsel_score_topk(const kvsel_paged_kv* kv, const void* summ, const void* q,
-                              int32_t k, int32_t* sel_idx, int32_t* sel_cnt, float* scores,
-                              const kvsel_reuse* reuse, void* ws, size_t ws_bytes, void* stream) {
+kvsel_status kvsel_score_topk(const kvsel_paged_kv* kv, const kvsel_rope* rope, void* summ,
+                              const void* q, int32_t k, int32_t flags, int32_t* sel_idx,
+                              int32_t* sel_cnt, float* scores, const kvsel_reuse* reuse, void* ws,
+                              size_t ws_bytes, void* stream) {
   LaunchKV f;
+  RopeArgs r;
   kvsel_status st = flatten(kv, 2, &f);
   if (st != KVSEL_OK) return st;
   if (!summ || !q || !sel_idx || !sel_cnt || k < 1) return KVSEL_ERR_INVALID_ARGUMENT;
+  if (flags & ~KVSEL_SCORE_REFRESH_TAIL) return KVSEL_ERR_INVALID_ARGUMENT;
+  if ((st = flatten_rope(rope, &r)) != KVSEL_OK) return st;
   ReuseArgs ra;
   memset(&ra, 0, sizeof(ra));
   if (reuse) {
@@ -150,12 +157,12 @@ kvsel_status kvsel_score_topk(const kvsel_paged_kv* kv, const void* summ, const 
     ra.similarity = reuse->similarity;
   }
   if (!scores) {
-    if (!ws || ws_bytes < score_workspace(f)) return KVSEL_ERR_WORKSPACE;
+    if (!ws || ws_bytes < score_workspace(f, true)) return KVSEL_ERR_WORKSPACE;
     scores = (float*)ws;
   }
   if ((st = check_device()) != KVSEL_OK) return st;
-  return launch_status(
-      launch_score_topk(f, summ, q, k, sel_idx, sel_cnt, scores, ra, (hipStream_t)stream));
+  return launch_status(launch_score_topk(f, r, summ, q, k, flags, sel_idx, sel_cnt, scores, ra,
+                                         (hipStream_t)stream));
 }
 
 kvsel_status kvsel_sparse_decode_attn(const kvsel_paged_kv* kv, const kvsel_rope* rope,
@@ -180,7 +187,8 @@ kvsel_status kvsel_sparse_decode_attn(const kvsel_paged_kv* kv, const kvsel_rope
 
 kvsel_status kvsel_rope_table(double theta, int32_t head_dim, int32_t first_position,
                               int32_t n_rows, float* cos_t, float* sin_t, void* stream) {
-  if (!cos_t || !sin_t || n_rows < 1 || head_dim < 2 || (head_dim & 1) || !(theta > 0.0))
+  if (!cos_t || !sin_t || n_rows < 1 || head_dim < 2 || head_dim > 128 || (head_dim & 1) ||
+      !(theta > 0.0))
     return KVSEL_ERR_INVALID_ARGUMENT;
   kvsel_status st = check_device();
   if (st != KVSEL_OK) return st;

@@ -25,6 +25,11 @@ struct RopeArgs {
   int row_step;
 };
 
+// Per-pair inverse rotary frequencies theta^(-2i/D), i < D/2 <= 64 (kernel argument by value).
+struct InvFreq {
+  double v[64];
+};
+
 struct ReuseArgs {
   const void* q_prev;  // nullptr: no reuse decision
   const int32_t* prev_idx;
@@ -40,8 +45,11 @@ struct ReuseArgs {
 hipError_t launch_summaries(const LaunchKV& kv, const RopeArgs& rope, int tail_only, void* summ,
                             hipStream_t stream);
 
-hipError_t launch_score_topk(const LaunchKV& kv, const void* summ, const void* q, int k,
-                             int32_t* sel_idx, int32_t* sel_cnt, float* scores,
+// Blocks of the selection kernel per list (each block scores one chunk of pages).
+int select_blocks_per_list(const LaunchKV& kv);
+
+hipError_t launch_score_topk(const LaunchKV& kv, const RopeArgs& rope, void* summ, const void* q,
+                             int k, int flags, int32_t* sel_idx, int32_t* sel_cnt, float* scores,
                              const ReuseArgs& reuse, hipStream_t stream);
 
 // Workspace of the attention for a given split size (bytes).

@@ -1,7 +1,9 @@
 // Rotary re-positioning of keys: the cos/sin table and the materialized rotation.
 //
-// rope_table_kernel: one thread per (row, pair i): angle = (first + row) * theta^(-2i/D) in fp64,
-// cos / sin in fp64, each rounded once to fp32.
+// rope_table_kernel: one thread per (row, pair i): angle = (first + row) * inv_freq[i] in fp64,
+// cos / sin in fp64, each rounded once to fp32. The D/2 inverse frequencies theta^(-2i/D) depend
+// on theta and D only; the host evaluates them once per call with the C library's pow and passes
+// them by value, so every device angle is the exact fp64 product of the position and that value.
 //
 // rope_shift_kernel: one wave per (physical page, KV head); rows are read and written as 16-byte
 // slices and rotated by rope_rotate_slice (the routine the summary and attention kernels use
@@ -13,15 +15,14 @@
 
 namespace kvsel {
 
-__global__ __launch_bounds__(256) void rope_table_kernel(double theta, int D, int first, int n_rows,
-                                                         float* __restrict__ cos_t,
+__global__ __launch_bounds__(256) void rope_table_kernel(InvFreq inv_freq, int D, int first,
+                                                         int n_rows, float* __restrict__ cos_t,
                                                          float* __restrict__ sin_t) {
   const int half = D / 2;
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long)n_rows * half) return;
   const int r = (int)(idx / half), i = (int)(idx % half);
-  const double inv = pow(theta, -(2.0 * i) / D);
-  const double a = (double)(first + r) * inv;
+  const double a = (double)(first + r) * inv_freq.v[i];
   cos_t[idx] = (float)cos(a);
   sin_t[idx] = (float)sin(a);
 }
@@ -52,8 +53,10 @@ hipError_t launch_rope_table(double theta, int D, int first_position, int n_rows
                              float* sin_t, hipStream_t stream) {
   const long total = (long)n_rows * (D / 2);
   if (total == 0) return hipSuccess;
+  InvFreq inv;
+  for (int i = 0; i < D / 2; ++i) inv.v[i] = pow(theta, -(2.0 * i) / D);
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                     theta, D, first_position, n_rows, cos_t, sin_t);
+                     inv, D, first_position, n_rows, cos_t, sin_t);
   return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ KVSEL_F32 = 0
 KVSEL_BF16 = 1
 KVSEL_OP_SCORE_TOPK = 1
 KVSEL_OP_ATTENTION = 2
+KVSEL_SCORE_REFRESH_TAIL = 1
 
 c_i32 = ctypes.c_int32
 c_vp = ctypes.c_void_p
@@ -61,8 +62,9 @@ EXPORTS = {
     "kvsel_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PagedKVDesc), c_i32, c_i32, c_i32]),
     "kvsel_build_summaries": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_i32,
                                       c_vp, c_vp]),
-    "kvsel_score_topk": (c_i32, [ctypes.POINTER(PagedKVDesc), c_vp, c_vp, c_i32, c_vp, c_vp, c_vp,
-                                 ctypes.POINTER(ReuseDesc), c_vp, ctypes.c_size_t, c_vp]),
+    "kvsel_score_topk": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp, c_vp,
+                                 c_i32, c_i32, c_vp, c_vp, c_vp, ctypes.POINTER(ReuseDesc), c_vp,
+                                 ctypes.c_size_t, c_vp]),
     "kvsel_sparse_decode_attn": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp,
                                          c_vp, c_vp, c_i32, ctypes.c_float, c_i32, c_vp, c_vp, c_vp,
                                          ctypes.c_size_t, c_vp]),
@@ -124,9 +126,16 @@ def _elem_code(dtype: torch.dtype) -> int:
     raise ValueError(f"unsupported element type {dtype}")
 
 
+def device_v_layout(v_pool: torch.Tensor) -> torch.Tensor:
+    """Values in the library's page layout: [Npp][Hkv][P][D] (token-major) -> [Npp][Hkv][D][P]
+    (channel-major pages)."""
+    return v_pool.transpose(-1, -2).contiguous()
+
+
 @dataclass
 class PagedKV:
-    """Device tensors of one paged KV cache: pools [Npp][Hkv][P][D], page_table int32
+    """Device tensors of one paged KV cache: k_pool [Npp][Hkv][P][D] (token-major pages),
+    v_pool [Npp][Hkv][D][P] (channel-major pages, see ``device_v_layout``), page_table int32
     [B][max_pages], seq_lens int32 [B]."""
 
     k_pool: torch.Tensor
@@ -139,6 +148,10 @@ class PagedKV:
         _dev(self.k_pool, "k_pool")
         if self.v_pool is not None:
             _dev(self.v_pool, "v_pool", self.k_pool.dtype)
+            Npp, Hkv, P, D = self.k_pool.shape
+            if tuple(self.v_pool.shape) != (Npp, Hkv, D, P):
+                raise ValueError(f"v_pool must be [Npp][Hkv][D][P] = {(Npp, Hkv, D, P)}, got "
+                                 f"{tuple(self.v_pool.shape)}")
         _dev(self.page_table, "page_table", torch.int32)
         _dev(self.seq_lens, "seq_lens", torch.int32)
         Npp, Hkv, P, D = self.k_pool.shape
@@ -190,10 +203,16 @@ def workspace_bytes(kv: PagedKV, k: int, op: int, pages_per_split: int = 0) -> i
     return int(lib().kvsel_workspace_bytes(ctypes.byref(kv.desc()), k, op, pages_per_split))
 
 
+def new_workspace(kv: PagedKV, k: int, op: int, pages_per_split: int = 0) -> torch.Tensor:
+    """A zero-filled workspace for ``op`` (the library leaves its counters zero after each
+    call, so the buffer can be reused by later calls on the same stream)."""
+    need = workspace_bytes(kv, k, op, pages_per_split)
+    return torch.zeros(max(need, 1), dtype=torch.uint8, device=kv.device)
+
+
 def _workspace(kv: PagedKV, k: int, op: int, pps: int, ws: Optional[torch.Tensor]):
-    need = workspace_bytes(kv, k, op, pps)
     if ws is None:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=kv.device)
+        ws = new_workspace(kv, k, op, pps)
     return ws, ws.numel() * ws.element_size()
 
 
@@ -222,11 +241,13 @@ class Reuse:
 
 
 def score_topk(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, *,
+               refresh_tail: bool = False, rope: Optional[Rope] = None,
                scores: Optional[torch.Tensor] = None, reuse: Optional[Reuse] = None,
                sel_idx: Optional[torch.Tensor] = None, sel_cnt: Optional[torch.Tensor] = None,
                workspace: Optional[torch.Tensor] = None):
-    """Page scores + top-k. Returns (sel_idx [B][Hkv][k], sel_cnt [B][Hkv]) and, with ``reuse``,
-    additionally (used_idx, used_cnt, corrected uint8, similarity fp64)."""
+    """Page scores + top-k (one launch). Returns (sel_idx [B][Hkv][k], sel_cnt [B][Hkv]) and,
+    with ``reuse``, additionally (used_idx, used_cnt, corrected uint8, similarity fp64).
+    ``refresh_tail`` first rebuilds each sequence's last-page summary in ``summ``."""
     d = kv.desc()
     B, Hkv = kv.batch, kv.num_kv_heads
     dev = kv.device
@@ -252,11 +273,10 @@ def score_topk(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, *,
                        float(reuse.tau), int(bool(reuse.first_step)), used_idx.data_ptr(),
                        used_cnt.data_ptr(), corrected.data_ptr(), sim.data_ptr())
         extra = (used_idx, used_cnt, corrected, sim)
-    ws, ws_bytes = (None, 0)
-    if scores is None:
-        ws, ws_bytes = _workspace(kv, k, KVSEL_OP_SCORE_TOPK, 0, workspace)
-    _check(lib().kvsel_score_topk(ctypes.byref(d), _ptr(summ), _ptr(q), k, _ptr(sel_idx),
-                                  _ptr(sel_cnt), _ptr(scores),
+    ws, ws_bytes = _workspace(kv, k, KVSEL_OP_SCORE_TOPK, 0, workspace)
+    flags = KVSEL_SCORE_REFRESH_TAIL if refresh_tail else 0
+    _check(lib().kvsel_score_topk(ctypes.byref(d), _rope_ptr(rope), _ptr(summ), _ptr(q), k, flags,
+                                  _ptr(sel_idx), _ptr(sel_cnt), _ptr(scores),
                                   None if rd is None else ctypes.byref(rd), _ptr(ws), ws_bytes,
                                   _stream(dev)))
     return (sel_idx, sel_cnt) + extra

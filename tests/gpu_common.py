@@ -19,7 +19,7 @@ def say(*a):
 
 
 def kv_of(K, w, dev="cuda"):
-    return K.PagedKV(w.k_pool.to(dev), w.v_pool.to(dev), w.page_table.to(dev),
+    return K.PagedKV(w.k_pool.to(dev), K.device_v_layout(w.v_pool.to(dev)), w.page_table.to(dev),
                      w.seq_lens.to(dev), w.Hq)
 
 

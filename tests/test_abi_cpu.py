@@ -60,7 +60,7 @@ def test_workspace_sizes(K):
     lib = K.lib()
     d = _desc(K)
     ws = lib.kvsel_workspace_bytes(ctypes.byref(d), 64, K.KVSEL_OP_SCORE_TOPK, 0)
-    assert ws == 1 * 8 * 1024 * 4
+    assert ws == 1 * 8 * 1024 * 4  # room for the scores
     # 64 pages in splits of 2 -> 32 partials per (b, KV head, query head of the group)
     parts = 1 * 8 * 32 * 4
     acc = parts * 128 * 4
@@ -94,14 +94,19 @@ def test_call_argument_validation(K):
     p = ctypes.c_void_p(0x5000)
     assert lib.kvsel_build_summaries(None, None, 0, p, None) == 1
     assert lib.kvsel_build_summaries(ctypes.byref(d), None, 0, None, None) == 1
-    # score/top-k: k < 1, NULL outputs, missing workspace when no score buffer is given
-    assert lib.kvsel_score_topk(ctypes.byref(d), p, p, 0, p, p, p, None, None, 0, None) == 1
-    assert lib.kvsel_score_topk(ctypes.byref(d), p, p, 64, None, p, p, None, None, 0, None) == 1
-    assert lib.kvsel_score_topk(ctypes.byref(d), p, p, 64, p, p, None, None, None, 0, None) == 3
-    assert lib.kvsel_score_topk(ctypes.byref(d), p, p, 64, p, p, None, None, p, 16, None) == 3
+    # score/top-k: k < 1, NULL outputs, unknown flags, missing or short workspace
+    st = lib.kvsel_score_topk
+    assert st(ctypes.byref(d), None, p, p, 0, 0, p, p, p, None, p, 1 << 20, None) == 1
+    assert st(ctypes.byref(d), None, p, p, 64, 0, None, p, p, None, p, 1 << 20, None) == 1
+    assert st(ctypes.byref(d), None, p, p, 64, 4, p, p, p, None, p, 1 << 20, None) == 1
+    assert st(ctypes.byref(d), None, p, p, 64, 0, p, p, None, None, None, 0, None) == 3
+    assert st(ctypes.byref(d), None, p, p, 64, 0, p, p, None, None, p, 1024, None) == 3
     bad_reuse = K.ReuseDesc(None, 1, 1, 0.8, 0, 1, 1, 1, None)
-    assert lib.kvsel_score_topk(ctypes.byref(d), p, p, 64, p, p, p, ctypes.byref(bad_reuse), None,
-                                0, None) == 1
+    assert st(ctypes.byref(d), None, p, p, 64, 0, p, p, p, ctypes.byref(bad_reuse), p, 1 << 20,
+              None) == 1
+    bad_rope = K.RopeDesc(0x10, None, 0x30, 4, 0)
+    assert st(ctypes.byref(d), ctypes.byref(bad_rope), p, p, 64, 1, p, p, p, None, p, 1 << 20,
+              None) == 1
     # attention: missing V pool, bad split request, workspace too small
     dv = _desc(K, v_pool=None)
     assert lib.kvsel_sparse_decode_attn(ctypes.byref(dv), None, p, p, p, 64, 0.1, 0, p, None, p,

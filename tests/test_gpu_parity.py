@@ -171,3 +171,43 @@ def test_tail_only_summary_refresh(K):
     torch.cuda.synchronize()
     ref = O.page_summaries(kv.k_pool.cpu(), w.page_table, w.seq_lens, w.P)
     assert_summaries_equal(tail, ref, referenced_pages(w))
+
+
+def test_fused_tail_refresh_in_selection(K):
+    # a decode step appends to each tail page; the selection call rebuilds those summaries first
+    w = W.custom(161, B=3, Hq=32, Hkv=8, D=128, P=32, k=6, lens=[700, 64, 33], dtype="bf16")
+    say("score_topk with tail refresh")
+    kv = kv_of(K, w)
+    summ = K.build_summaries(kv)
+    for b in range(w.B):
+        p = int(w.page_table[b, w.n_pages(b) - 1])
+        kv.k_pool[p] = kv.k_pool[p] * 3 - 1
+    sc = torch.full((w.B, w.Hkv, w.max_pages), float("nan"), device="cuda")
+    sel, cnt = K.score_topk(kv, summ, w.q.cuda(), w.k, refresh_tail=True, scores=sc)
+    torch.cuda.synchronize()
+    kpool = kv.k_pool.cpu()
+    ref_summ = O.page_summaries(kpool, w.page_table, w.seq_lens, w.P)
+    assert_summaries_equal(summ, ref_summ, referenced_pages(w))
+    ref_sc = O.page_scores(w.q, ref_summ, w.page_table, w.seq_lens, w.P)
+    ref_sel, ref_cnt = O.top_pages(ref_sc, w.seq_lens, w.P, w.k)
+    assert_scores_close(sc, ref_sc, w, exact=True)
+    assert_selection_equal(sel, cnt, ref_sel, ref_cnt)
+
+
+def test_workspace_reuse_across_calls(K):
+    # one workspace serves consecutive calls on a stream
+    w = W.custom(171, B=2, Hq=32, Hkv=8, D=128, P=32, k=16, lens=[3000, 2100], dtype="bf16")
+    say("workspace reuse")
+    kv = kv_of(K, w)
+    summ = K.build_summaries(kv)
+    ws_s = K.new_workspace(kv, w.k, K.KVSEL_OP_SCORE_TOPK)
+    ws_a = K.new_workspace(kv, w.k, K.KVSEL_OP_ATTENTION, 2)
+    gen = torch.Generator().manual_seed(5)
+    for it in range(4):
+        q = torch.randn(w.q.shape, generator=gen).to(torch.bfloat16).cuda()
+        sel, cnt = K.score_topk(kv, summ, q, w.k, workspace=ws_s)
+        out, lse = K.sparse_decode_attn(kv, q, sel, cnt, w.k, pages_per_split=2, workspace=ws_a)
+        sel2, cnt2 = K.score_topk(kv, summ, q, w.k)
+        out2, lse2 = K.sparse_decode_attn(kv, q, sel2, cnt2, w.k, pages_per_split=2)
+        torch.cuda.synchronize()
+        assert torch.equal(sel, sel2) and torch.equal(out, out2) and torch.equal(lse, lse2)

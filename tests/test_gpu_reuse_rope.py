@@ -39,7 +39,9 @@ def test_rope_table_matches_oracle(K):
     oc, os_ = O.rope_table(500000.0, 128, 0, 32768)
     same = table_agreement(gc, gs, oc, os_)
     say(f"rope table: {int(same.sum())}/{same.size} entries bit-identical")
-    assert same.mean() > 0.999
+    # both sides round the same fp64 angle's cos/sin; two libms can differ only when the value
+    # sits within an fp64 ulp of an fp32 rounding boundary
+    assert same.size - int(same.sum()) <= 4
 
 
 @pytest.mark.parametrize("dtype,D,P,row_step,in_place", [
@@ -93,13 +95,28 @@ def spec(K):
     o_enc = O.rope_rotate(w.k_pool, oc, os_, enc_row, 1, "bf16")
     o_abs = O.rope_rotate(torch.from_numpy(o_enc).to(torch.bfloat16), oc, os_, shift_row, 0, "bf16")
     return dict(w=w, kv_enc=kv_enc, shift=shift, absk=absk, o_enc=o_enc, o_abs=o_abs,
-                table_same=bool(same.all()), enc_gpu=enc)
+                table_same=bool(same.all()), same=same, enc_row=enc_row, shift_row=shift_row,
+                enc_gpu=enc)
 
 
 def test_speculative_rope_blocks_match_oracle(spec):
-    assert spec["table_same"], "tables differ: bit-exact key comparison does not apply"
-    np.testing.assert_array_equal(spec["enc_gpu"].float().cpu().numpy(), spec["o_enc"])
-    np.testing.assert_array_equal(spec["absk"].float().cpu().numpy(), spec["o_abs"])
+    w = spec["w"]
+    g_enc = spec["enc_gpu"].float().cpu().numpy()
+    g_abs = spec["absk"].float().cpu().numpy()
+    if spec["table_same"]:
+        np.testing.assert_array_equal(g_enc, spec["o_enc"])
+        np.testing.assert_array_equal(g_abs, spec["o_abs"])
+        return
+    # bit-exact wherever every table entry a value depends on agrees; 1 bf16 ulp elsewhere
+    same = spec["same"]
+    half = w.D // 2
+    enc_rows = spec["enc_row"][:, None] + np.arange(w.P)[None, :]
+    ok_enc = same[enc_rows]  # [Npp][P][half]
+    ok_abs = ok_enc & same[spec["shift_row"]][:, None, :]
+    for got, ref, ok in ((g_enc, spec["o_enc"], ok_enc), (g_abs, spec["o_abs"], ok_abs)):
+        m = np.broadcast_to(np.concatenate([ok, ok], axis=-1)[:, None], got.shape)
+        assert np.array_equal(got[m], ref[m])
+        assert (np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-30).all()
 
 
 def test_fused_rope_is_bit_identical_to_materialized(K, spec):
@@ -120,14 +137,16 @@ def test_fused_rope_is_bit_identical_to_materialized(K, spec):
 
 def test_speculative_decode_loop_matches_oracle(K, spec):
     w = spec["w"]
-    assert spec["table_same"]
     tau = w.extra["tau"]
     qs = w.extra["q_steps"]
-    kv = K.PagedKV(spec["absk"], spec["kv_enc"].v_pool, spec["kv_enc"].page_table,
+    o_pool = torch.from_numpy(spec["o_abs"]).to(torch.bfloat16)
+    # identical tables: the GPU's own rotated keys (end to end); otherwise the oracle's keys, so
+    # the selection / reuse / attention comparison stays bit-exact
+    keys = spec["absk"] if spec["table_same"] else o_pool.cuda()
+    kv = K.PagedKV(keys, spec["kv_enc"].v_pool, spec["kv_enc"].page_table,
                    spec["kv_enc"].seq_lens, w.Hq)
     say("speculative loop: summaries")
     summ = K.build_summaries(kv)
-    o_pool = torch.from_numpy(spec["o_abs"]).to(torch.bfloat16)
     o_summ = O.page_summaries(o_pool, w.page_table, w.seq_lens, w.P)
     torch.cuda.synchronize()
     assert_summaries_equal(summ, o_summ, referenced_pages(w))
