@@ -56,9 +56,11 @@ class Layer:
         K.score_topk(self.kv, self.summ, self.q, self.k, refresh_tail=True, sel_idx=self.sel,
                      sel_cnt=self.cnt, workspace=self.ws_score)
 
+    pps = 0  # pages per split: 0 = the library's choice
+
     def attend(self):
         K.sparse_decode_attn(self.kv, self.q, self.sel, self.cnt, self.k, out=self.out,
-                             lse=self.lse, workspace=self.ws_attn)
+                             lse=self.lse, pages_per_split=self.pps, workspace=self.ws_attn)
 
     def step(self):
         self.select()
@@ -104,24 +106,31 @@ def time_graph(layers, steps, warmup):
     return e0.elapsed_time(e1) * 1000.0 / n, n
 
 
+def _event_pairs(layers, fn, launches):
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    torch.cuda._sleep(int(2.0e8))  # ~0.1 s of GPU spin: the host enqueues everything meanwhile
+    for i in range(launches):
+        starts[i].record()
+        if fn is not None:
+            fn(layers[i % len(layers)])
+        ends[i].record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) * 1000.0 for a, b in zip(starts, ends)])
+
+
 def time_kernel(layers, fn, launches):
     """Average GPU duration (µs) of the launches of ``fn(layer)``, each bracketed by HIP events
     recorded on the launch stream. A GPU-side spin queued first keeps the device busy while the
-    host enqueues, so each event pair brackets GPU work only."""
+    host enqueues, so each event pair brackets GPU work only; the average duration of an empty
+    event pair, measured the same way, is subtracted."""
     for lay in layers:
         lay.select()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
-    torch.cuda._sleep(int(2.0e8))  # ~0.1 s of GPU spin
-    for i in range(launches):
-        lay = layers[i % len(layers)]
-        starts[i].record()
-        fn(lay)
-        ends[i].record()
-    torch.cuda.synchronize()
-    d = np.array([a.elapsed_time(b) * 1000.0 for a, b in zip(starts, ends)])
-    return float(d.mean()), float(np.median(d)), d
+    d = _event_pairs(layers, fn, launches)
+    empty = _event_pairs(layers, None, launches)
+    ov = float(empty.mean())
+    return float(d.mean()) - ov, float(np.median(d)) - ov, ov
 
 
 def attention_bytes(w, lay):
@@ -135,14 +144,45 @@ def measure(name, dev, steps, warmup, n_layers):
     w = W.make(name)
     layers = make_layers(w, dev, n_layers)
     us_step, n = time_graph(layers, steps, warmup)
-    attn_mean, attn_med, _ = time_kernel(layers, Layer.attend, max(64, min(steps, 512)))
+    attn_mean, attn_med, ev_ov = time_kernel(layers, Layer.attend, max(64, min(steps, 512)))
     sel_mean, _, _ = time_kernel(layers, Layer.select, max(64, min(steps, 512)))
     abytes = attention_bytes(w, layers[0])
     esize = 4 if w.dtype == "f32" else 2
     sbytes = summary_bytes(w.seq_lens.tolist(), w.Hkv, w.P, w.D, esize)
     return dict(w=w, layers=layers, us_step=us_step, steps=n, attn_us=attn_mean,
                 attn_us_median=attn_med, select_us=sel_mean, attn_bytes=abytes,
-                summary_bytes=sbytes)
+                summary_bytes=sbytes, event_overhead_us=ev_ov)
+
+
+def recorded_traffic():
+    """Attention HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current attention source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attention_llama8b_32k_counters.md")
+    src = os.path.join(ROOT, "query_aware_sparse_page_amd", "csrc", "attention.hip")
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    vals = dict(line.split("=", 1) for line in text.splitlines() if "=" in line and " " not in line)
+    if vals.get("attention_source_sha256_16") != sha:
+        return None
+    return int(float(vals["attention_traffic_bytes_per_launch"]))
+
+
+def sweep_pps(name, dev, n_layers, launches=256):
+    """Attention call time for each split size (pages per split)."""
+    w = W.make(name)
+    layers = make_layers(w, dev, n_layers)
+    out = {}
+    for pps in (1, 2, 4, 8):
+        for lay in layers:
+            lay.pps = pps
+            lay.ws_attn = K.new_workspace(lay.kv, w.k, K.KVSEL_OP_ATTENTION, pps)
+        t, med, _ = time_kernel(layers, Layer.attend, launches)
+        out[pps] = round(t, 3)
+    print(json.dumps({"sweep_pps": name, "attn_us_by_pages_per_split": out}), flush=True)
 
 
 def cpu_baseline(w, lay, budget_s=12.0):
@@ -179,6 +219,25 @@ def cpu_baseline(w, lay, budget_s=12.0):
                 parity=dict(selection_bit_exact=ok_sel, attention_max_abs_err=err))
 
 
+def counter_pass(name, dev, n_layers):
+    """Eager steps over the rotated layers, then a plain device copy of exactly 64 MiB: its
+    FETCH_SIZE / WRITE_SIZE per dispatch calibrate the counters against known bytes."""
+    w = W.make(name)
+    layers = make_layers(w, dev, n_layers)
+    for _ in range(2):
+        for lay in layers:
+            lay.step()
+    torch.cuda.synchronize()
+    src = torch.empty(64 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_pass": name, "layers": n_layers, "steps": 2 * n_layers,
+                      "calibration_copy_bytes": 64 << 20}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +247,11 @@ def main():
     ap.add_argument("--layers", type=int, default=8, help="cache copies rotated like layers")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--sweep-pps", action="store_true",
+                    help="time the attention call for each split size and exit")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="only run a few eager steps plus a 64 MiB calibration copy (for rocprofv3 "
+                         "--pmc FETCH_SIZE / WRITE_SIZE runs) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -196,6 +260,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     K.lib()
+    if args.counter_pass:
+        counter_pass(args.workload, dev, args.layers)
+        return
+    if args.sweep_pps:
+        for name in (args.workload, "qwen4b_128k", "ragged_batch"):
+            sweep_pps(name, dev, 4)
+            torch.cuda.empty_cache()
+        return
 
     m = measure(args.workload, dev, args.steps, args.warmup, args.layers)
     w = m["w"]
@@ -221,15 +293,16 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_kernel (kvsel_sparse_decode_attn: split-K + fused merge, one launch)",
+            "kernel": "kvsel_sparse_decode_attn: attn_bf16_kernel (split-K) + attn_merge_kernel",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic() if w.name == "llama8b_32k" else None,
             "algorithmic_bytes": m["attn_bytes"],
             "avg_us": round(m["attn_us"], 3),
             "median_us": round(m["attn_us_median"], 3),
+            "event_pair_overhead_us": round(m["event_overhead_us"], 3),
         },
         "select_us": round(m["select_us"], 3),
     }

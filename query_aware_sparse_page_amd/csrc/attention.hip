@@ -38,7 +38,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int ATT_MAX_SPLITS = 256;
-constexpr int MERGE_THREADS = 256;
 
 struct AttnArgs {
   const void* k_pool;
@@ -48,7 +47,7 @@ struct AttnArgs {
   const void* q;
   const int32_t* sel_idx;
   const int32_t* sel_cnt;
-  int Hkv, P, log2P, maxp, k, pps, nsplit, nlists;
+  int Hkv, P, log2P, maxp, Npp, k, pps, nsplit, nlists;
   float scale;
   RopeArgs rope;
   float* part_acc;   // [nlists][nsplit][G][D]
@@ -89,8 +88,9 @@ __device__ __forceinline__ void lookup_tiles(const AttnArgs& a, int list, int b,
     for (int u = 0; u < NPT; ++u) {
       const int nn = n[t][u];
       const bool in_range = nn >= 0 && nn < a.maxp;
-      tp.page[t][u] =
-          __builtin_amdgcn_readfirstlane(a.page_table[(size_t)b * a.maxp + (in_range ? nn : 0)]);
+      // an entry outside the list may hold anything: clamp it into the pool before addressing
+      const int pg = __builtin_amdgcn_readfirstlane(a.page_table[(size_t)b * a.maxp + (in_range ? nn : 0)]);
+      tp.page[t][u] = min(max(pg, 0), a.Npp - 1);
       const int sp = split * a.pps + ((first_tile + t) * TT) / P + u;
       tp.valid[t][u] = (in_range && sp < cnt) ? min(P, L - nn * P) : 0;
     }
@@ -283,8 +283,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a, int G
       z[t][e] = ((vmask[t] >> e) & 1) && r16 < G ? v : NEG_INF;
       m = fmaxf(m, z[t][e]);
     }
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
+  m = fmaxf(m, xor16_f32(m));
+  m = fmaxf(m, xor32_f32(m));
   float l = 0.0f;
   f32x4_t o[VB];
 #pragma unroll
@@ -307,8 +307,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a, int G
       o[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(vv), o[vb], 0, 0, 0);
     }
   }
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l += xor16_f32(l);
+  l += xor32_f32(l);
 
   // ---- merge the block's waves through LDS ----
   __shared__ float s_m[WAVES][ATT_MAX_G], s_l[WAVES][ATT_MAX_G];
@@ -427,8 +427,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(AttnArgs a, int G)
       z[t][i] = ((vmask[t] >> i) & 1) && r16 < G ? v : NEG_INF;
       m = fmaxf(m, z[t][i]);
     }
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
+  m = fmaxf(m, xor16_f32(m));
+  m = fmaxf(m, xor32_f32(m));
   float l = 0.0f;
   f32x4_t o[VB];
 #pragma unroll
@@ -451,8 +451,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(AttnArgs a, int G)
         o[vb] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[st], vv[st], o[vb], 0, 0, 0);
     }
   }
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l += xor16_f32(l);
+  l += xor32_f32(l);
 
   __shared__ float s_m[WAVES][ATT_MAX_G], s_l[WAVES][ATT_MAX_G];
   __shared__ float s_o[WAVES][ATT_MAX_G][D];
@@ -470,57 +470,58 @@ __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(AttnArgs a, int G)
 }
 
 // ------------------------------------------------------------------------------------------
-// merge: one block per list, every partial load of a thread issued together
+// merge: one block per (list, query head of the group), one thread per channel. The partial
+// accumulators of up to MERGE_CHUNK splits and every (m, l) pair are loaded in one round, so the
+// merge costs one memory round trip for up to MERGE_CHUNK splits.
 // ------------------------------------------------------------------------------------------
+constexpr int MERGE_CHUNK = 32;
+
 template <typename T, int D>
-__global__ __launch_bounds__(MERGE_THREADS) void attn_merge_kernel(AttnArgs a, int G) {
+__global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int G) {
   const float NEG_INF = __int_as_float(0xff800000);
-  const int list = blockIdx.x;
+  const int list = blockIdx.x / G, g = blockIdx.x % G;
   const int b = list / a.Hkv, j = list % a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int d = threadIdx.x;
   const int Hq = a.Hkv * G;
   const int ns = a.nsplit;
-  __shared__ float s_w[ATT_MAX_SPLITS][ATT_MAX_G];
-  __shared__ float s_M[ATT_MAX_G], s_L[ATT_MAX_G];
-  const float2* ml = a.part_ml + (size_t)list * ns * G;
-  for (int g = w; g < G; g += MERGE_THREADS / 64) {
-    float mx = NEG_INF;
-    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, ml[s * G + g].x);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    float ls = 0.0f;
-    for (int s = lane; s < ns; s += 64) {
-      const float2 v = ml[s * G + g];
-      const float f = (mx == NEG_INF || v.x == NEG_INF) ? 0.0f : __expf(v.x - mx);
-      s_w[s][g] = f;
-      ls = fmaf(v.y, f, ls);
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) ls += __shfl_xor(ls, o);
-    if (lane == 0) {
-      s_M[g] = mx;
-      s_L[g] = ls;
-    }
+  __shared__ float s_m[ATT_MAX_SPLITS], s_l[ATT_MAX_SPLITS];
+  const float2* ml = a.part_ml + (size_t)list * ns * G + g;
+  const float* pa = a.part_acc + ((size_t)list * ns * G + g) * D + d;
+  for (int s = d; s < ns; s += D) {
+    const float2 v = ml[(size_t)s * G];
+    s_m[s] = v.x;
+    s_l[s] = v.y;
   }
+  float v[MERGE_CHUNK];
+#pragma unroll
+  for (int u = 0; u < MERGE_CHUNK; ++u) v[u] = u < ns ? pa[(size_t)u * G * D] : 0.0f;
   __syncthreads();
-  const float* pa = a.part_acc + (size_t)list * ns * G * D;
-  for (int idx = tid; idx < G * D; idx += MERGE_THREADS) {
-    const int g = idx / D, d = idx % D;
-    float A = 0.0f;
-    int s = 0;
-    for (; s + 8 <= ns; s += 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = pa[((size_t)(s + u) * G + g) * D + d];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) A = fmaf(v[u], s_w[s + u][g], A);
-    }
-    for (; s < ns; ++s) A = fmaf(pa[((size_t)s * G + g) * D + d], s_w[s][g], A);
-    const size_t o = ((size_t)b * Hq + j * G + g) * D + d;
-    const bool empty = s_M[g] == NEG_INF;
-    store_elem<T>((T*)a.out, o, empty ? 0.0f : A / s_L[g]);
-    if (d == 0 && a.lse) a.lse[(size_t)b * Hq + j * G + g] = empty ? NEG_INF : s_M[g] + logf(s_L[g]);
+  float M = NEG_INF;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, s_m[s]);
+  const size_t o = ((size_t)b * Hq + j * G + g) * D + d;
+  if (M == NEG_INF) {
+    store_elem<T>((T*)a.out, o, 0.0f);
+    if (d == 0 && a.lse) a.lse[(size_t)b * Hq + j * G + g] = NEG_INF;
+    return;
   }
+  float L = 0.0f, A = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += MERGE_CHUNK) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int u = 0; u < MERGE_CHUNK; ++u) v[u] = s0 + u < ns ? pa[(size_t)(s0 + u) * G * D] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < MERGE_CHUNK; ++u) {
+      const int s = s0 + u;
+      if (s < ns && s_m[s] != NEG_INF) {
+        const float f = __expf(s_m[s] - M);
+        L = fmaf(s_l[s], f, L);
+        A = fmaf(v[u], f, A);
+      }
+    }
+  }
+  store_elem<T>((T*)a.out, o, A / L);
+  if (d == 0 && a.lse) a.lse[(size_t)b * Hq + j * G + g] = M + logf(L);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -538,7 +539,8 @@ static int tiles_for(const LaunchKV& kv, int pps) {
 }
 
 int attention_pages_per_split(const LaunchKV& kv, int k, int requested) {
-  const int want = requested > 0 ? requested : 2;
+  // default 4 pages per split: measured best at 32K, 128K and the ragged batch of 16
+  const int want = requested > 0 ? requested : 4;
   int pps = 0;
   // largest supported split not above the request, else the smallest supported one
   for (int p = want; p >= 1 && !pps; --p)
@@ -589,8 +591,8 @@ static hipError_t launch_tiles(int tiles, const AttnArgs& a, int G, bool rope, h
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3((unsigned)a.nlists), dim3(MERGE_THREADS), 0,
-                     stream, a, G);
+  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3((unsigned)(a.nlists * G)), dim3(D), 0, stream,
+                     a, G);
   return hipGetLastError();
 }
 
@@ -617,6 +619,7 @@ hipError_t launch_attention(const LaunchKV& kv, const RopeArgs& rope, const void
   a.P = kv.P;
   a.log2P = kv.log2P;
   a.maxp = kv.maxp;
+  a.Npp = kv.Npp;
   a.k = k;
   a.pps = pps;
   a.nsplit = (k + pps - 1) / pps;

@@ -160,6 +160,88 @@ __device__ __forceinline__ void rope_rotate_slice(float* x, int c0, int row, con
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Cross-lane primitives on DPP and the gfx950 permlane swaps (no LDS round trip).
+// ------------------------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, BANK_MASK, false);
+}
+
+// DPP controls: quad permutations, mirrors, row shifts and row broadcasts.
+constexpr int DPP_QUAD_XOR1 = 0xb1;    // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4e;    // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
+constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+
+// Inclusive wave-wide scan (lane 0 first) of an associative op with identity `id`.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, uint32_t id, Op op) {
+  v = op(v, dpp_u32<DPP_ROW_SHR1>(id, v));
+  v = op(v, dpp_u32<DPP_ROW_SHR2>(id, v));
+  v = op(v, dpp_u32<DPP_ROW_SHR4, 0xf, 0xe>(id, v));
+  v = op(v, dpp_u32<DPP_ROW_SHR8, 0xf, 0xc>(id, v));
+  v = op(v, dpp_u32<DPP_ROW_BCAST15, 0xa>(id, v));
+  v = op(v, dpp_u32<DPP_ROW_BCAST31, 0xc>(id, v));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_scan_add(uint32_t v) {
+  return wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = wave_scan(v, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Value of lane ^ 16 and lane ^ 32 (gfx950 permlane swaps).
+__device__ __forceinline__ uint32_t xor16_u32(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return ((threadIdx.x >> 4) & 1) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t xor32_u32(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ float xor16_f32(float v) { return __uint_as_float(xor16_u32(__float_as_uint(v))); }
+__device__ __forceinline__ float xor32_f32(float v) { return __uint_as_float(xor32_u32(__float_as_uint(v))); }
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint32_t lo = dpp_u32<CTRL>(0u, (uint32_t)u), hi = dpp_u32<CTRL>(0u, (uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double xor16_f64(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  return __longlong_as_double((long long)(((uint64_t)xor16_u32((uint32_t)(u >> 32)) << 32) |
+                                          xor16_u32((uint32_t)u)));
+}
+__device__ __forceinline__ double xor32_f64(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  return __longlong_as_double((long long)(((uint64_t)xor32_u32((uint32_t)(u >> 32)) << 32) |
+                                          xor32_u32((uint32_t)u)));
+}
+
+// Sum over aligned segments of SEG lanes (SEG in {4, 8, 16, 32, 64}); every lane of a segment
+// gets the segment's sum (butterflies: quad xor 1, quad xor 2, half-row mirror, row mirror,
+// then lane ^ 16 and lane ^ 32).
+template <int SEG>
+__device__ __forceinline__ double seg_sum_f64(double x) {
+  x += dpp_f64<DPP_QUAD_XOR1>(x);
+  x += dpp_f64<DPP_QUAD_XOR2>(x);
+  if (SEG >= 8) x += dpp_f64<DPP_ROW_HALF_MIRROR>(x);
+  if (SEG >= 16) x += dpp_f64<DPP_ROW_MIRROR>(x);
+  if (SEG >= 32) x += xor16_f64(x);
+  if (SEG >= 64) x += xor32_f64(x);
+  return x;
+}
+
 // Orderable key of an fp32 score: unsigned order == float order; -0 and +0 map together.
 __device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);

@@ -9,10 +9,11 @@
 // writes it, and scores it from the fresh values.
 //
 // topk_kernel: one block per list. An exact radix select over orderable 32-bit score keys
-// (4 passes of 8-bit digits, most significant first) finds the k-th largest key T; pages with
-// key > T are taken, pages with key == T are taken in ascending page order until k are chosen
-// (ties go to the lower index), and a ballot-based block prefix sum writes them in ascending
-// order. The same block evaluates the speculative-reuse decision.
+// (8-bit digits, most significant first, starting below the bits all keys share, stopping once
+// the boundary bucket is exactly what is still needed) finds the boundary; pages above it are
+// taken and pages in the boundary bucket are taken in ascending page order (ties go to the lower
+// index); a block scan gives each chosen page its slot in the ascending output. Its first wave
+// evaluates the speculative-reuse decision.
 //
 // The two kernels are separate launches on purpose: a "last block of the list does the top-k"
 // fusion needs a device-scope release / acquire per block, which on this GPU writes back and
@@ -32,7 +33,7 @@ struct SelectArgs {
   const void* q;
   const int32_t* page_table;
   const int32_t* seq_lens;
-  int Hkv, P, maxp, k, nlists, nchunks, refresh_tail;
+  int Hkv, P, maxp, Npp, k, nlists, nchunks, refresh_tail;
   RopeArgs rope;
   float* scores;
   int32_t* sel_idx;
@@ -42,11 +43,9 @@ struct SelectArgs {
 
 struct TopkSmem {
   uint32_t keys[SEL_LDS_KEYS];
-  uint32_t hist[256];
-  uint32_t wave_cnt[2][SEL_WAVES];
-  uint32_t prefix, remaining;
-  double cosv[8];
-  int corr;
+  uint32_t hist[SEL_WAVES][256];
+  uint32_t wave_a[SEL_WAVES], wave_b[SEL_WAVES];
+  uint32_t prefix, need, count;
 };
 
 // Min / max of the valid rows of one (page, KV head) tile, computed by one wave. On return the
@@ -96,10 +95,41 @@ __device__ __forceinline__ void tile_minmax(const T* tile, int valid, int P, int
   }
 }
 
+// Exclusive scan over the block of two counters (wave scans on DPP, one barrier for the wave
+// totals); also returns nothing else: the block totals are not needed.
+__device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, uint32_t& a_ex,
+                                                      uint32_t& b_ex, TopkSmem& sm) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t ia = wave_scan_add(a), ib = wave_scan_add(b);
+  if (lane == 63) {
+    sm.wave_a[w] = ia;
+    sm.wave_b[w] = ib;
+  }
+  __syncthreads();
+  uint32_t ba = 0, bb = 0;
+#pragma unroll
+  for (int v = 0; v < SEL_WAVES; ++v)
+    if (v < w) {
+      ba += sm.wave_a[v];
+      bb += sm.wave_b[v];
+    }
+  a_ex = ba + ia - a;
+  b_ex = bb + ib - b;
+}
+
 // Exact top-k of the N scores of one list, by the whole block; writes out[0..k) ascending
 // (padded with -1) and, when `used` is non-null, the same list there too.
+//
+// Radix select over orderable keys, most significant digit first, starting below the bits all
+// keys share (block min / max) and stopping as soon as the bucket holding the k-th largest key
+// holds exactly the number of keys still needed. Keys are loaded in batches of independent
+// loads; histograms are per wave (no LDS atomic contention across waves); every scan and
+// reduction runs on DPP. The chosen set is {keys in buckets above the boundary bucket} plus the
+// first `need` keys of the boundary bucket in index order (ties to the lower page index); one
+// block scan over per-thread contiguous index chunks gives every chosen page its output slot.
 __device__ void block_topk(const float* __restrict__ sc, int N, int k, int32_t* __restrict__ out,
                            int32_t* __restrict__ used, TopkSmem& sm) {
+  constexpr int BATCH = 8;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (N <= k) {
     for (int i = tid; i < k; i += SEL_THREADS) {
@@ -110,84 +140,99 @@ __device__ void block_topk(const float* __restrict__ sc, int N, int k, int32_t* 
     return;
   }
   const bool cached = N <= SEL_LDS_KEYS;
-  if (cached)
-    for (int i = tid; i < N; i += SEL_THREADS) sm.keys[i] = score_key(sc[i]);
-  if (tid == 0) {
-    sm.prefix = 0;
-    sm.remaining = (uint32_t)k;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int base = tid; base < N; base += SEL_THREADS * BATCH) {
+    float v[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) v[u] = sc[min(base + u * SEL_THREADS, N - 1)];  // clamped
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int i = base + u * SEL_THREADS;
+      if (i < N) {
+        const uint32_t key = score_key(v[u]);
+        if (cached) sm.keys[i] = key;
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+      }
+    }
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  for (int i = tid; i < SEL_WAVES * 256; i += SEL_THREADS) (&sm.hist[0][0])[i] = 0;
+  if (lane == 0) {
+    sm.wave_a[w] = kmin;
+    sm.wave_b[w] = kmax;
   }
   __syncthreads();
-  uint32_t prefix = 0, mask = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += SEL_THREADS) sm.hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < N; i += SEL_THREADS) {
-      const uint32_t u = cached ? sm.keys[i] : score_key(sc[i]);
-      if ((u & mask) == prefix) atomicAdd(&sm.hist[(u >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (w == 0) {
-      uint32_t h[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) h[t] = sm.hist[4 * lane + t];
-      const uint32_t own = h[0] + h[1] + h[2] + h[3];
-      uint32_t suf = own;  // inclusive suffix sum over lanes >= lane
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_down(suf, o);
-        if (lane + o < 64) suf += t;
-      }
-      const uint32_t rem = sm.remaining;
-      uint32_t cum = suf - own;  // elements in the bins above this lane's four
-#pragma unroll
-      for (int t = 3; t >= 0; --t) {
-        const uint32_t after = cum + h[t];
-        if (cum < rem && after >= rem) {
-          sm.prefix = prefix | ((uint32_t)(4 * lane + t) << shift);
-          sm.remaining = rem - cum;
-        }
-        cum = after;
-      }
-    }
-    __syncthreads();
-    prefix = sm.prefix;
-    mask |= 0xffu << shift;
+  for (int v = 0; v < SEL_WAVES; ++v) {
+    kmin = min(kmin, sm.wave_a[v]);
+    kmax = max(kmax, sm.wave_b[v]);
   }
-  const uint32_t T_key = prefix;
-  const uint32_t need_eq = sm.remaining;
-  const unsigned long long lt_mask = (1ull << lane) - 1ull;
-  uint32_t base_eq = 0, base_sel = 0;
-  for (int t0 = 0; t0 < N; t0 += SEL_THREADS) {
-    const int i = t0 + tid;
-    const uint32_t u = i < N ? (cached ? sm.keys[i] : score_key(sc[i])) : 0u;
-    const bool gt = i < N && u > T_key;
-    const bool eq = i < N && u == T_key;
-    const unsigned long long eqm = __ballot(eq);
-    if (lane == 0) sm.wave_cnt[0][w] = (uint32_t)__popcll(eqm);
-    __syncthreads();
-    uint32_t eq_before = base_eq + (uint32_t)__popcll(eqm & lt_mask), eq_tot = 0;
+  uint32_t prefix = kmax, mask = 0xffffffffu, need = (uint32_t)k;
+  if (kmin != kmax) {
+    const int top_bit = 31 - __clz((int)(kmin ^ kmax));
+    mask = top_bit == 31 ? 0u : ~((2u << top_bit) - 1u);
+    prefix = kmax & mask;
+    for (int top = top_bit; top >= 0; top -= 8) {
+      const int shift = top >= 7 ? top - 7 : 0;
+      const uint32_t dmask = (2u << (top - shift)) - 1u;
+      for (int i = tid; i < N; i += SEL_THREADS) {
+        const uint32_t u = cached ? sm.keys[i] : score_key(sc[i]);
+        if ((u & mask) == prefix) atomicAdd(&sm.hist[w][(u >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      // thread t owns bin 255 - t (largest first); its total over the per-wave histograms
+      const int bin = 255 - tid;
+      uint32_t tot = 0;
 #pragma unroll
-    for (int v = 0; v < SEL_WAVES; ++v) {
-      if (v < w) eq_before += sm.wave_cnt[0][v];
-      eq_tot += sm.wave_cnt[0][v];
-    }
-    const bool sel = gt || (eq && eq_before < need_eq);
-    const unsigned long long selm = __ballot(sel);
-    if (lane == 0) sm.wave_cnt[1][w] = (uint32_t)__popcll(selm);
-    __syncthreads();
-    uint32_t pos = base_sel + (uint32_t)__popcll(selm & lt_mask), sel_tot = 0;
+      for (int v = 0; v < SEL_WAVES; ++v) {
+        tot += sm.hist[v][bin];
+        sm.hist[v][bin] = 0;  // ready for the next pass (read only by this thread)
+      }
+      const uint32_t incl = wave_scan_add(tot);
+      if (lane == 63) sm.wave_a[w] = incl;
+      __syncthreads();
+      uint32_t above = incl - tot;  // keys in larger bins
 #pragma unroll
-    for (int v = 0; v < SEL_WAVES; ++v) {
-      if (v < w) pos += sm.wave_cnt[1][v];
-      sel_tot += sm.wave_cnt[1][v];
+      for (int v = 0; v < SEL_WAVES; ++v)
+        if (v < w) above += sm.wave_a[v];
+      if (tot > 0 && above < need && above + tot >= need) {
+        sm.prefix = prefix | ((uint32_t)bin << shift);
+        sm.need = need - above;
+        sm.count = tot;
+      }
+      __syncthreads();
+      prefix = sm.prefix;
+      need = sm.need;
+      mask |= dmask << shift;
+      if (sm.count == need) break;  // the whole boundary bucket is taken
     }
-    if (sel && pos < (uint32_t)k) {
-      out[pos] = i;
-      if (used) used[pos] = i;
+  }
+  // ---- compaction: thread t owns indices [t*C, t*C + C) ----
+  const int C = (N + SEL_THREADS - 1) / SEL_THREADS;
+  const int i0 = tid * C, i1 = min(N, i0 + C);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t u = (cached ? sm.keys[i] : score_key(sc[i])) & mask;
+    n_gt += u > prefix;
+    n_eq += u == prefix;
+  }
+  uint32_t gt_ex, eq_ex;
+  block_exclusive_scan2(n_gt, n_eq, gt_ex, eq_ex, sm);
+  uint32_t pos = gt_ex + min(eq_ex, need);
+  uint32_t eq_seen = eq_ex;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t u = (cached ? sm.keys[i] : score_key(sc[i])) & mask;
+    const bool sel = u > prefix || (u == prefix && eq_seen < need);
+    eq_seen += u == prefix;
+    if (sel) {
+      if (pos < (uint32_t)k) {
+        out[pos] = i;
+        if (used) used[pos] = i;
+      }
+      ++pos;
     }
-    base_eq += eq_tot;
-    base_sel += sel_tot;
-    __syncthreads();
   }
 }
 
@@ -202,7 +247,7 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   const int list = blockIdx.x % a.nlists;
   const int chunk = blockIdx.x / a.nlists;
   const int b = list / a.Hkv, j = list % a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = a.P;
   const int L = a.seq_lens[b];
   const int N = L > 0 ? (L + P - 1) / P : 0;
@@ -210,20 +255,31 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   const int Hq = a.Hkv * G;
   const T* q = (const T*)a.q;
   const int c0 = (lane % LPR) * VEC;
+  const int n = n0 + w * PPW + lane / LPR;
+  const bool active = n < N;
 
-  // ---- decode-time refresh of the tail page's summary ----
+  // ---- loads first (unconditional, clamped addresses): q slice, page id, summary rows ----
+  uint4 qraw[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) qraw[g] = load16(q + ((size_t)b * Hq + j * G + g) * D + c0);
+  // inactive lanes read entry 0 (any value) and clamp it into the pool: an address, never used
+  const int p = min(max(a.page_table[(size_t)b * a.maxp + (active ? n : 0)], 0), a.Npp - 1);
+  const T* srow = (const T*)a.summ + ((size_t)p * a.Hkv + j) * 2 * D + c0;
+  const uint4 lo_raw = load16(srow), hi_raw = load16(srow + D);
+
+  // ---- decode-time refresh of the tail page's summary (overlaps the loads above) ----
   const bool has_tail = a.refresh_tail && N > 0 && N - 1 >= n0 && N - 1 < n0 + PPB;
   if (has_tail) {
     if (w == 0) {
-      const int n = N - 1;
-      const int p = a.page_table[(size_t)b * a.maxp + n];
-      const int valid = L - n * P;
-      const int prow = a.rope.page_row ? a.rope.page_row[p] : -1;
+      const int nt = N - 1;
+      const int pt = a.page_table[(size_t)b * a.maxp + nt];
+      const int valid = L - nt * P;
+      const int prow = a.rope.page_row ? a.rope.page_row[pt] : -1;
       float lo[VEC], hi[VEC];
-      tile_minmax<T, D>((const T*)a.k_pool + ((size_t)p * a.Hkv + j) * P * D, valid, P, lane, prow,
+      tile_minmax<T, D>((const T*)a.k_pool + ((size_t)pt * a.Hkv + j) * P * D, valid, P, lane, prow,
                         a.rope, lo, hi);
       if (lane < LPR) {
-        T* out = (T*)a.summ + ((size_t)p * a.Hkv + j) * 2 * D;
+        T* out = (T*)a.summ + ((size_t)pt * a.Hkv + j) * 2 * D;
         store16(out + c0, pack<T>(lo));
         store16(out + D + c0, pack<T>(hi));
 #pragma unroll
@@ -237,55 +293,44 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   }
 
   // ---- scores of this block's pages ----
-  {
-    const int n = n0 + w * PPW + lane / LPR;
-    const bool active = n < N;
-    double qd[G][VEC];
+  double qd[G][VEC];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float f[VEC];
-      unpack<T>(load16(q + ((size_t)b * Hq + j * G + g) * D + c0), f);
+  for (int g = 0; g < G; ++g) {
+    float f[VEC];
+    unpack<T>(qraw[g], f);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) qd[g][e] = (double)f[e];
-    }
-    float lo[VEC], hi[VEC];
-    if (active && has_tail && n == N - 1) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        lo[e] = s_tail[0][c0 + e];
-        hi[e] = s_tail[1][c0 + e];
-      }
-    } else if (active) {
-      const int p = a.page_table[(size_t)b * a.maxp + n];
-      const T* s = (const T*)a.summ + ((size_t)p * a.Hkv + j) * 2 * D;
-      unpack<T>(load16(s + c0), lo);
-      unpack<T>(load16(s + D + c0), hi);
-    } else {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) lo[e] = hi[e] = 0.0f;
-    }
-    double acc = 0.0;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const double x = (double)(qd[g][e] >= 0.0 ? hi[e] : lo[e]);
-        acc = fma(qd[g][e], x, acc);
-      }
-    }
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m);
-    if (active && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
+    for (int e = 0; e < VEC; ++e) qd[g][e] = (double)f[e];
   }
-
+  float lo[VEC], hi[VEC];
+  unpack<T>(lo_raw, lo);
+  unpack<T>(hi_raw, hi);
+  if (has_tail && n == N - 1) {  // the stale rows loaded above are replaced by the fresh ones
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      lo[e] = s_tail[0][c0 + e];
+      hi[e] = s_tail[1][c0 + e];
+    }
+  }
+  double acc = 0.0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const double x = (double)(qd[g][e] >= 0.0 ? hi[e] : lo[e]);
+      acc = fma(qd[g][e], x, acc);
+    }
+  }
+  acc = seg_sum_f64<LPR>(acc);
+  if (active && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
 }
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(SelectArgs a) {
   __shared__ TopkSmem sm;
+  __shared__ int s_corr;
   const int list = blockIdx.x;
   const int b = list / a.Hkv, j = list % a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = a.P;
   const int L = a.seq_lens[b];
   const int N = L > 0 ? (L + P - 1) / P : 0;
@@ -295,41 +340,35 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(SelectArgs a) {
   int corrected = 1;
   const bool reuse_on = a.reuse.q_prev != nullptr;
   if (reuse_on) {
-    if (w < G) {
-      // mean over the group of cos(q, q_prev) in fp64
-      double dot = 0.0, na = 0.0, nb = 0.0;
-      for (int g = w; g < G; g += SEL_WAVES) {
+    if (w == 0) {
+      // mean over the group of cos(q, q_prev), fp64
+      double csum = 0.0;
+      for (int g = 0; g < G; ++g) {
         const int h = j * G + g;
         const T* x = q + ((size_t)b * Hq + h) * D;
         const T* y = (const T*)a.reuse.q_prev + ((size_t)b * Hq + h) * D;
-        dot = na = nb = 0.0;
+        double dot = 0.0, na = 0.0, nb = 0.0;
         for (int d = lane; d < D; d += 64) {
           const double xv = (double)load_elem<T>(x, d), yv = (double)load_elem<T>(y, d);
           dot = fma(xv, yv, dot);
           na = fma(xv, xv, na);
           nb = fma(yv, yv, nb);
         }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-          dot += __shfl_xor(dot, m);
-          na += __shfl_xor(na, m);
-          nb += __shfl_xor(nb, m);
-        }
-        if (lane == 0) sm.cosv[g] = dot / (sqrt(na) * sqrt(nb));
+        dot = seg_sum_f64<64>(dot);
+        na = seg_sum_f64<64>(na);
+        nb = seg_sum_f64<64>(nb);
+        csum += dot / (sqrt(na) * sqrt(nb));
+      }
+      const double C = csum / G;
+      const int corr = (a.reuse.first_step || C < a.reuse.tau) ? 1 : 0;
+      if (lane == 0) {
+        s_corr = corr;
+        a.reuse.corrected[list] = (uint8_t)corr;
+        if (a.reuse.similarity) a.reuse.similarity[list] = C;
       }
     }
     __syncthreads();
-    if (tid == 0) {
-      double csum = 0.0;
-      for (int g = 0; g < G; ++g) csum += sm.cosv[g];
-      const double C = csum / G;
-      const int corr = (a.reuse.first_step || C < a.reuse.tau) ? 1 : 0;
-      sm.corr = corr;
-      a.reuse.corrected[list] = (uint8_t)corr;
-      if (a.reuse.similarity) a.reuse.similarity[list] = C;
-    }
-    __syncthreads();
-    corrected = sm.corr;
+    corrected = s_corr;
   }
   int32_t* used = (reuse_on && corrected) ? a.reuse.used_idx + (size_t)list * a.k : nullptr;
   block_topk(a.scores + (size_t)list * a.maxp, N, a.k, a.sel_idx + (size_t)list * a.k, used, sm);
@@ -391,6 +430,7 @@ hipError_t launch_score_topk(const LaunchKV& kv, const RopeArgs& rope, void* sum
   a.Hkv = kv.Hkv;
   a.P = kv.P;
   a.maxp = kv.maxp;
+  a.Npp = kv.Npp;
   a.k = k;
   a.nlists = kv.B * kv.Hkv;
   a.nchunks = select_blocks_per_list(kv);

@@ -211,3 +211,26 @@ def test_workspace_reuse_across_calls(K):
         out2, lse2 = K.sparse_decode_attn(kv, q, sel2, cnt2, w.k, pages_per_split=2)
         torch.cuda.synchronize()
         assert torch.equal(sel, sel2) and torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("case", ["five_patterns", "all_equal", "uncached_9000_pages"])
+def test_topk_ties_and_long_lists(K, case):
+    if case == "uncached_9000_pages":
+        w = W.custom(181, B=1, Hq=2, Hkv=1, D=64, P=16, k=300, lens=[16 * 9000 - 3], dtype="bf16")
+    else:
+        w = W.custom(182, B=2, Hq=4, Hkv=2, D=64, P=16, k=17, lens=[16 * 200, 16 * 50 - 7],
+                     dtype="bf16", permute=False)
+        npat = 5 if case == "five_patterns" else 1
+        for p in range(w.num_phys_pages):
+            w.k_pool[p] = w.k_pool[p % npat]  # exact copies: scores tie exactly
+    say(f"top-k stress {case}: N={[w.n_pages(b) for b in range(w.B)]} k={w.k}")
+    kv = kv_of(K, w)
+    summ = K.build_summaries(kv)
+    sc = torch.full((w.B, w.Hkv, w.max_pages), float("nan"), device="cuda")
+    sel, cnt = K.score_topk(kv, summ, w.q.cuda(), w.k, scores=sc)
+    torch.cuda.synchronize()
+    ref_summ = O.page_summaries(w.k_pool, w.page_table, w.seq_lens, w.P)
+    ref_sc = O.page_scores(w.q, ref_summ, w.page_table, w.seq_lens, w.P)
+    ref_sel, ref_cnt = O.top_pages(ref_sc, w.seq_lens, w.P, w.k)
+    assert_scores_close(sc, ref_sc, w, exact=True)
+    assert_selection_equal(sel, cnt, ref_sel, ref_cnt)
