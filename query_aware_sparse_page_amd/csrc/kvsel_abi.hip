@@ -156,13 +156,14 @@ kvsel_status kvsel_score_topk(const kvsel_paged_kv* kv, const kvsel_rope* rope, 
     ra.corrected = reuse->corrected;
     ra.similarity = reuse->similarity;
   }
+  const bool requested = scores != nullptr;
   if (!scores) {
     if (!ws || ws_bytes < score_workspace(f, true)) return KVSEL_ERR_WORKSPACE;
     scores = (float*)ws;
   }
   if ((st = check_device()) != KVSEL_OK) return st;
-  return launch_status(launch_score_topk(f, r, summ, q, k, flags, sel_idx, sel_cnt, scores, ra,
-                                         (hipStream_t)stream));
+  return launch_status(launch_score_topk(f, r, summ, q, k, flags, sel_idx, sel_cnt, scores,
+                                         requested, ra, (hipStream_t)stream));
 }
 
 kvsel_status kvsel_sparse_decode_attn(const kvsel_paged_kv* kv, const kvsel_rope* rope,

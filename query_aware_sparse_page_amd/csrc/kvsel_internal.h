@@ -48,9 +48,11 @@ hipError_t launch_summaries(const LaunchKV& kv, const RopeArgs& rope, int tail_o
 // Blocks of the selection kernel per list (each block scores one chunk of pages).
 int select_blocks_per_list(const LaunchKV& kv);
 
+// scores_requested: the caller asked for the scores (else `scores` is workspace and the one-launch
+// path may skip writing it).
 hipError_t launch_score_topk(const LaunchKV& kv, const RopeArgs& rope, void* summ, const void* q,
                              int k, int flags, int32_t* sel_idx, int32_t* sel_cnt, float* scores,
-                             const ReuseArgs& reuse, hipStream_t stream);
+                             bool scores_requested, const ReuseArgs& reuse, hipStream_t stream);
 
 // Workspace of the attention for a given split size (bytes).
 size_t attention_workspace(const LaunchKV& kv, int k, int pages_per_split);

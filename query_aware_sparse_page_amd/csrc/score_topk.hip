@@ -33,7 +33,7 @@ struct SelectArgs {
   const void* q;
   const int32_t* page_table;
   const int32_t* seq_lens;
-  int Hkv, P, maxp, Npp, k, nlists, nchunks, refresh_tail;
+  int Hkv, P, maxp, Npp, k, nlists, nchunks, refresh_tail, write_scores;
   RopeArgs rope;
   float* scores;
   int32_t* sel_idx;
@@ -41,10 +41,13 @@ struct SelectArgs {
   ReuseArgs reuse;
 };
 
+template <int NT>
 struct TopkSmem {
+  static constexpr int NW = NT / 64;
   uint32_t keys[SEL_LDS_KEYS];
-  uint32_t hist[SEL_WAVES][256];
-  uint32_t wave_a[SEL_WAVES], wave_b[SEL_WAVES];
+  uint32_t hist[NW][256];
+  uint32_t wave_a[NW], wave_b[NW];      // scan totals
+  uint32_t wave_min[NW], wave_max[NW];  // key range (own slots: read with no barrier after)
   uint32_t prefix, need, count;
 };
 
@@ -97,8 +100,9 @@ __device__ __forceinline__ void tile_minmax(const T* tile, int valid, int P, int
 
 // Exclusive scan over the block of two counters (wave scans on DPP, one barrier for the wave
 // totals); also returns nothing else: the block totals are not needed.
+template <int NT>
 __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, uint32_t& a_ex,
-                                                      uint32_t& b_ex, TopkSmem& sm) {
+                                                      uint32_t& b_ex, TopkSmem<NT>& sm) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint32_t ia = wave_scan_add(a), ib = wave_scan_add(b);
   if (lane == 63) {
@@ -108,7 +112,7 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, ui
   __syncthreads();
   uint32_t ba = 0, bb = 0;
 #pragma unroll
-  for (int v = 0; v < SEL_WAVES; ++v)
+  for (int v = 0; v < NT / 64; ++v)
     if (v < w) {
       ba += sm.wave_a[v];
       bb += sm.wave_b[v];
@@ -127,27 +131,37 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, ui
 // reduction runs on DPP. The chosen set is {keys in buckets above the boundary bucket} plus the
 // first `need` keys of the boundary bucket in index order (ties to the lower page index); one
 // block scan over per-thread contiguous index chunks gives every chosen page its output slot.
+// KEYS_IN_LDS: the caller already stored the N (<= SEL_LDS_KEYS) keys in sm.keys and `sc` is
+// not read.
+template <int NT, bool KEYS_IN_LDS>
 __device__ void block_topk(const float* __restrict__ sc, int N, int k, int32_t* __restrict__ out,
-                           int32_t* __restrict__ used, TopkSmem& sm) {
+                           int32_t* __restrict__ used, TopkSmem<NT>& sm) {
   constexpr int BATCH = 8;
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (N <= k) {
-    for (int i = tid; i < k; i += SEL_THREADS) {
+    for (int i = tid; i < k; i += NT) {
       const int v = i < N ? i : -1;
       out[i] = v;
       if (used) used[i] = v;
     }
     return;
   }
-  const bool cached = N <= SEL_LDS_KEYS;
+  const bool cached = KEYS_IN_LDS || N <= SEL_LDS_KEYS;
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for (int base = tid; base < N; base += SEL_THREADS * BATCH) {
+  if (KEYS_IN_LDS) {
+    for (int i = tid; i < N; i += NT) {
+      kmin = min(kmin, sm.keys[i]);
+      kmax = max(kmax, sm.keys[i]);
+    }
+  } else
+  for (int base = tid; base < N; base += NT * BATCH) {
     float v[BATCH];
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) v[u] = sc[min(base + u * SEL_THREADS, N - 1)];  // clamped
+    for (int u = 0; u < BATCH; ++u) v[u] = sc[min(base + u * NT, N - 1)];  // clamped
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const int i = base + u * SEL_THREADS;
+      const int i = base + u * NT;
       if (i < N) {
         const uint32_t key = score_key(v[u]);
         if (cached) sm.keys[i] = key;
@@ -158,16 +172,16 @@ __device__ void block_topk(const float* __restrict__ sc, int N, int k, int32_t* 
   }
   kmin = wave_min_u32(kmin);
   kmax = wave_max_u32(kmax);
-  for (int i = tid; i < SEL_WAVES * 256; i += SEL_THREADS) (&sm.hist[0][0])[i] = 0;
+  for (int i = tid; i < NW * 256; i += NT) (&sm.hist[0][0])[i] = 0;
   if (lane == 0) {
-    sm.wave_a[w] = kmin;
-    sm.wave_b[w] = kmax;
+    sm.wave_min[w] = kmin;
+    sm.wave_max[w] = kmax;
   }
   __syncthreads();
 #pragma unroll
-  for (int v = 0; v < SEL_WAVES; ++v) {
-    kmin = min(kmin, sm.wave_a[v]);
-    kmax = max(kmax, sm.wave_b[v]);
+  for (int v = 0; v < NW; ++v) {
+    kmin = min(kmin, sm.wave_min[v]);
+    kmax = max(kmax, sm.wave_max[v]);
   }
   uint32_t prefix = kmax, mask = 0xffffffffu, need = (uint32_t)k;
   if (kmin != kmax) {
@@ -177,25 +191,27 @@ __device__ void block_topk(const float* __restrict__ sc, int N, int k, int32_t* 
     for (int top = top_bit; top >= 0; top -= 8) {
       const int shift = top >= 7 ? top - 7 : 0;
       const uint32_t dmask = (2u << (top - shift)) - 1u;
-      for (int i = tid; i < N; i += SEL_THREADS) {
+      for (int i = tid; i < N; i += NT) {
         const uint32_t u = cached ? sm.keys[i] : score_key(sc[i]);
         if ((u & mask) == prefix) atomicAdd(&sm.hist[w][(u >> shift) & dmask], 1u);
       }
       __syncthreads();
-      // thread t owns bin 255 - t (largest first); its total over the per-wave histograms
+      // thread t < 256 owns bin 255 - t (largest first); its total over the per-wave histograms
       const int bin = 255 - tid;
       uint32_t tot = 0;
+      if (tid < 256) {
 #pragma unroll
-      for (int v = 0; v < SEL_WAVES; ++v) {
-        tot += sm.hist[v][bin];
-        sm.hist[v][bin] = 0;  // ready for the next pass (read only by this thread)
+        for (int v = 0; v < NW; ++v) {
+          tot += sm.hist[v][bin];
+          sm.hist[v][bin] = 0;  // ready for the next pass (read only by this thread)
+        }
       }
       const uint32_t incl = wave_scan_add(tot);
       if (lane == 63) sm.wave_a[w] = incl;
       __syncthreads();
       uint32_t above = incl - tot;  // keys in larger bins
 #pragma unroll
-      for (int v = 0; v < SEL_WAVES; ++v)
+      for (int v = 0; v < NW; ++v)
         if (v < w) above += sm.wave_a[v];
       if (tot > 0 && above < need && above + tot >= need) {
         sm.prefix = prefix | ((uint32_t)bin << shift);
@@ -210,7 +226,7 @@ __device__ void block_topk(const float* __restrict__ sc, int N, int k, int32_t* 
     }
   }
   // ---- compaction: thread t owns indices [t*C, t*C + C) ----
-  const int C = (N + SEL_THREADS - 1) / SEL_THREADS;
+  const int C = (N + NT - 1) / NT;
   const int i0 = tid * C, i1 = min(N, i0 + C);
   uint32_t n_gt = 0, n_eq = 0;
   for (int i = i0; i < i1; ++i) {
@@ -250,7 +266,7 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = a.P;
   const int L = a.seq_lens[b];
-  const int N = L > 0 ? (L + P - 1) / P : 0;
+  const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;  // never past the table row
   const int n0 = chunk * PPB;
   const int Hq = a.Hkv * G;
   const T* q = (const T*)a.q;
@@ -324,65 +340,180 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   if (active && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
 }
 
+// Speculative-reuse decision of one list, by the block's first wave: mean over the group of
+// cos(q, q_prev) in fp64; corrected = first step or C < tau. Every thread gets the decision.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(SEL_THREADS) void topk_kernel(SelectArgs a) {
-  __shared__ TopkSmem sm;
-  __shared__ int s_corr;
-  const int list = blockIdx.x;
-  const int b = list / a.Hkv, j = list % a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int P = a.P;
-  const int L = a.seq_lens[b];
-  const int N = L > 0 ? (L + P - 1) / P : 0;
+__device__ int reuse_decision(const SelectArgs& a, int list, int b, int j, int* s_corr) {
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Hq = a.Hkv * G;
-  const T* q = (const T*)a.q;
-
-  int corrected = 1;
-  const bool reuse_on = a.reuse.q_prev != nullptr;
-  if (reuse_on) {
-    if (w == 0) {
-      // mean over the group of cos(q, q_prev), fp64
-      double csum = 0.0;
-      for (int g = 0; g < G; ++g) {
-        const int h = j * G + g;
-        const T* x = q + ((size_t)b * Hq + h) * D;
-        const T* y = (const T*)a.reuse.q_prev + ((size_t)b * Hq + h) * D;
-        double dot = 0.0, na = 0.0, nb = 0.0;
-        for (int d = lane; d < D; d += 64) {
-          const double xv = (double)load_elem<T>(x, d), yv = (double)load_elem<T>(y, d);
-          dot = fma(xv, yv, dot);
-          na = fma(xv, xv, na);
-          nb = fma(yv, yv, nb);
-        }
-        dot = seg_sum_f64<64>(dot);
-        na = seg_sum_f64<64>(na);
-        nb = seg_sum_f64<64>(nb);
-        csum += dot / (sqrt(na) * sqrt(nb));
+  if (w == 0) {
+    double csum = 0.0;
+    for (int g = 0; g < G; ++g) {
+      const int h = j * G + g;
+      const T* x = (const T*)a.q + ((size_t)b * Hq + h) * D;
+      const T* y = (const T*)a.reuse.q_prev + ((size_t)b * Hq + h) * D;
+      double dot = 0.0, na = 0.0, nb = 0.0;
+      for (int d = lane; d < D; d += 64) {
+        const double xv = (double)load_elem<T>(x, d), yv = (double)load_elem<T>(y, d);
+        dot = fma(xv, yv, dot);
+        na = fma(xv, xv, na);
+        nb = fma(yv, yv, nb);
       }
-      const double C = csum / G;
-      const int corr = (a.reuse.first_step || C < a.reuse.tau) ? 1 : 0;
-      if (lane == 0) {
-        s_corr = corr;
-        a.reuse.corrected[list] = (uint8_t)corr;
-        if (a.reuse.similarity) a.reuse.similarity[list] = C;
-      }
+      dot = seg_sum_f64<64>(dot);
+      na = seg_sum_f64<64>(na);
+      nb = seg_sum_f64<64>(nb);
+      csum += dot / (sqrt(na) * sqrt(nb));
     }
-    __syncthreads();
-    corrected = s_corr;
+    const double C = csum / G;
+    const int corr = (a.reuse.first_step || C < a.reuse.tau) ? 1 : 0;
+    if (lane == 0) {
+      *s_corr = corr;
+      a.reuse.corrected[list] = (uint8_t)corr;
+      if (a.reuse.similarity) a.reuse.similarity[list] = C;
+    }
   }
+  __syncthreads();
+  return *s_corr;
+}
+
+// Selection outputs of one list once its keys are known (shared by both launch structures).
+template <int NT, bool KEYS_IN_LDS>
+__device__ void select_outputs(const SelectArgs& a, int list, int N, int corrected, bool reuse_on,
+                               TopkSmem<NT>& sm) {
+  const int tid = threadIdx.x;
   int32_t* used = (reuse_on && corrected) ? a.reuse.used_idx + (size_t)list * a.k : nullptr;
-  block_topk(a.scores + (size_t)list * a.maxp, N, a.k, a.sel_idx + (size_t)list * a.k, used, sm);
+  block_topk<NT, KEYS_IN_LDS>(a.scores + (size_t)list * a.maxp, N, a.k,
+                              a.sel_idx + (size_t)list * a.k, used, sm);
   const int cnt = N < a.k ? N : a.k;
   if (tid == 0) a.sel_cnt[list] = cnt;
   if (reuse_on) {
     if (corrected) {
       if (tid == 0) a.reuse.used_cnt[list] = cnt;
     } else {
-      for (int i = tid; i < a.k; i += SEL_THREADS)
+      for (int i = tid; i < a.k; i += NT)
         a.reuse.used_idx[(size_t)list * a.k + i] = a.reuse.prev_idx[(size_t)list * a.k + i];
       if (tid == 0) a.reuse.used_cnt[list] = a.reuse.prev_cnt[list];
     }
   }
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(SEL_THREADS) void topk_kernel(SelectArgs a) {
+  __shared__ TopkSmem<SEL_THREADS> sm;
+  __shared__ int s_corr;
+  const int list = blockIdx.x;
+  const int b = list / a.Hkv, j = list % a.Hkv;
+  const int L = a.seq_lens[b];
+  const int N = L > 0 ? min((L + a.P - 1) / a.P, a.maxp) : 0;
+  const bool reuse_on = a.reuse.q_prev != nullptr;
+  const int corrected = reuse_on ? reuse_decision<T, D, G>(a, list, b, j, &s_corr) : 1;
+  select_outputs<SEL_THREADS, false>(a, list, N, corrected, reuse_on, sm);
+}
+
+// ------------------------------------------------------------------------------------------
+// One launch for lists of at most FUSED_MAX_PAGES pages: one 1024-thread block per list scores
+// every page (keys straight into LDS) and then selects, so no score ever goes through memory
+// and no second launch is needed. The block first stages the list's page-table row in LDS (one
+// round of loads), then issues the summary loads in batches of UNROLL pages per lane. Wave 0
+// refreshes the tail page (when asked) and scores it from registers while the other waves score
+// the rest.
+// ------------------------------------------------------------------------------------------
+constexpr int FUSED_THREADS = 1024;
+constexpr int FUSED_MAX_PAGES = 2048;
+constexpr int FUSED_MIN_LISTS = 64;
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs a) {
+  using M = row_map<T, D>;
+  constexpr int VEC = M::VEC, LPR = M::LPR;
+  constexpr int PPW = 64 / LPR;                     // pages per wave per iteration
+  constexpr int PPI = (FUSED_THREADS / 64) * PPW;   // pages per block iteration
+  constexpr int UNROLL = G >= 4 ? 4 : 8;  // summary loads in flight per lane
+  __shared__ TopkSmem<FUSED_THREADS> sm;
+  __shared__ int s_pt[FUSED_MAX_PAGES];
+  __shared__ int s_corr;
+  const int list = blockIdx.x;
+  const int b = list / a.Hkv, j = list % a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = a.P;
+  const int L = a.seq_lens[b];
+  const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;  // never past the table row
+  const int Hq = a.Hkv * G;
+  const int c0 = (lane % LPR) * VEC;
+  const bool refresh = a.refresh_tail && N > 0;
+  const int n_end = refresh ? N - 1 : N;  // pages scored from stored summaries
+
+  for (int n = tid; n < n_end; n += FUSED_THREADS)
+    s_pt[n] = min(max(a.page_table[(size_t)b * a.maxp + n], 0), a.Npp - 1);
+  uint4 qraw[G];  // packed query slices (half the registers of unpacked bf16)
+#pragma unroll
+  for (int g = 0; g < G; ++g) qraw[g] = load16((const T*)a.q + ((size_t)b * Hq + j * G + g) * D + c0);
+
+  // ---- wave 0: decode-time refresh of the tail page, scored from registers ----
+  if (refresh && w == 0) {
+    const int nt = N - 1;
+    const int pt = min(max(a.page_table[(size_t)b * a.maxp + nt], 0), a.Npp - 1);
+    const int prow = a.rope.page_row ? a.rope.page_row[pt] : -1;
+    float lo[VEC], hi[VEC];
+    tile_minmax<T, D>((const T*)a.k_pool + ((size_t)pt * a.Hkv + j) * P * D, L - nt * P, P, lane,
+                      prow, a.rope, lo, hi);
+    if (lane < LPR) {
+      T* out = (T*)a.summ + ((size_t)pt * a.Hkv + j) * 2 * D;
+      store16(out + c0, pack<T>(lo));
+      store16(out + D + c0, pack<T>(hi));
+    }
+    double acc = 0.0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float qf[VEC];
+      unpack<T>(qraw[g], qf);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc = fma((double)qf[e], (double)(qf[e] >= 0.0f ? hi[e] : lo[e]), acc);
+    }
+    acc = seg_sum_f64<LPR>(acc);
+    if (lane == 0) {
+      sm.keys[nt] = score_key((float)acc);
+      if (a.write_scores) a.scores[(size_t)list * a.maxp + nt] = (float)acc;
+    }
+  }
+  __syncthreads();  // page-table row staged
+
+  // ---- every other page ----
+  for (int it0 = 0; it0 * PPI < n_end; it0 += UNROLL) {
+    uint4 lo_raw[UNROLL], hi_raw[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int n = (it0 + u) * PPI + w * PPW + lane / LPR;
+      const int p = s_pt[min(n, n_end - 1)];
+      const T* srow = (const T*)a.summ + ((size_t)p * a.Hkv + j) * 2 * D + c0;
+      lo_raw[u] = load16(srow);
+      hi_raw[u] = load16(srow + D);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int n = (it0 + u) * PPI + w * PPW + lane / LPR;
+      float lo[VEC], hi[VEC];
+      unpack<T>(lo_raw[u], lo);
+      unpack<T>(hi_raw[u], hi);
+      double acc = 0.0;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float qf[VEC];
+        unpack<T>(qraw[g], qf);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc = fma((double)qf[e], (double)(qf[e] >= 0.0f ? hi[e] : lo[e]), acc);
+      }
+      acc = seg_sum_f64<LPR>(acc);
+      if (n < n_end && (lane % LPR) == 0) {
+        sm.keys[n] = score_key((float)acc);
+        if (a.write_scores) a.scores[(size_t)list * a.maxp + n] = (float)acc;
+      }
+    }
+  }
+  __syncthreads();
+  const bool reuse_on = a.reuse.q_prev != nullptr;
+  const int corrected = reuse_on ? reuse_decision<T, D, G>(a, list, b, j, &s_corr) : 1;
+  select_outputs<FUSED_THREADS, true>(a, list, N, corrected, reuse_on, sm);
 }
 
 template <typename T, int D>
@@ -400,6 +531,17 @@ int select_blocks_per_list(const LaunchKV& kv) {
 
 template <typename T, int D, int G>
 static hipError_t launch_select_t(const SelectArgs& a, hipStream_t stream) {
+  // One block per list reads a whole list's summaries through one CU, so the one-launch form
+  // pays only when there are enough lists to spread over the chip (measured on the bf16 path:
+  // 8 lists of 1024 pages take 24.7 us in one launch against 10.2 us in two; 128 lists of up
+  // to 1024 pages take 15.8 us against 18.6 us).
+  if constexpr (G <= 4) {  // larger groups would spill at 1024 threads
+    if (a.nlists >= FUSED_MIN_LISTS && a.maxp <= FUSED_MAX_PAGES) {
+      hipLaunchKernelGGL((select_fused_kernel<T, D, G>), dim3((unsigned)a.nlists), dim3(FUSED_THREADS),
+                         0, stream, a);
+      return hipGetLastError();
+    }
+  }
   const long blocks = (long)a.nlists * a.nchunks;
   hipLaunchKernelGGL((score_kernel<T, D, G>), dim3((unsigned)blocks), dim3(SEL_THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
@@ -420,7 +562,7 @@ static hipError_t launch_select_g(int G, const SelectArgs& a, hipStream_t stream
 
 hipError_t launch_score_topk(const LaunchKV& kv, const RopeArgs& rope, void* summ, const void* q,
                              int k, int flags, int32_t* sel_idx, int32_t* sel_cnt, float* scores,
-                             const ReuseArgs& reuse, hipStream_t stream) {
+                             bool scores_requested, const ReuseArgs& reuse, hipStream_t stream) {
   SelectArgs a;
   a.k_pool = kv.k_pool;
   a.summ = summ;
@@ -437,6 +579,7 @@ hipError_t launch_score_topk(const LaunchKV& kv, const RopeArgs& rope, void* sum
   a.refresh_tail = (flags & 1) ? 1 : 0;
   a.rope = rope;
   a.scores = scores;
+  a.write_scores = scores_requested ? 1 : 0;
   a.sel_idx = sel_idx;
   a.sel_cnt = sel_cnt;
   a.reuse = reuse;

@@ -245,7 +245,7 @@ def score_topk(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, *,
                scores: Optional[torch.Tensor] = None, reuse: Optional[Reuse] = None,
                sel_idx: Optional[torch.Tensor] = None, sel_cnt: Optional[torch.Tensor] = None,
                workspace: Optional[torch.Tensor] = None):
-    """Page scores + top-k (one launch). Returns (sel_idx [B][Hkv][k], sel_cnt [B][Hkv]) and,
+    """Page scores + top-k. Returns (sel_idx [B][Hkv][k], sel_cnt [B][Hkv]) and,
     with ``reuse``, additionally (used_idx, used_cnt, corrected uint8, similarity fp64).
     ``refresh_tail`` first rebuilds each sequence's last-page summary in ``summ``."""
     d = kv.desc()

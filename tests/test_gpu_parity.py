@@ -234,3 +234,67 @@ def test_topk_ties_and_long_lists(K, case):
     ref_sel, ref_cnt = O.top_pages(ref_sc, w.seq_lens, w.P, w.k)
     assert_scores_close(sc, ref_sc, w, exact=True)
     assert_selection_equal(sel, cnt, ref_sel, ref_cnt)
+
+
+LAUNCH_LENS = [60807, 1280, 5, 1, 33, 4096, 20000, 31999, 777, 64, 65, 50000, 12345, 2, 32, 8000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_selection_launch_structures_agree(K, dtype):
+    # with at least 64 lists of at most 2048 table entries, one block per list scores and selects
+    # in one launch; a wider page table (same sequences, unused extra columns) takes the
+    # two-launch path. Both must give the same scores, selection and reuse decision, with and
+    # without the tail refresh and with and without a scores output.
+    w = W.custom(191, B=16, Hq=16, Hkv=4, D=128, P=32, k=24, lens=LAUNCH_LENS, dtype=dtype)
+    say(f"one-launch vs two-launch selection, {dtype}, N={[w.n_pages(b) for b in range(w.B)]}")
+    assert w.B * w.Hkv >= 64 and w.max_pages <= 2048
+    kv = kv_of(K, w)
+    wide_pt = torch.cat([w.page_table, torch.zeros(w.B, 2100 - w.max_pages, dtype=torch.int32)], 1)
+    kv_wide = K.PagedKV(kv.k_pool, kv.v_pool, wide_pt.cuda(), kv.seq_lens, w.Hq)
+    q = w.q.cuda()
+    summ = K.build_summaries(kv)
+    ref_summ = O.page_summaries(w.k_pool, w.page_table, w.seq_lens, w.P)
+    ref_sc = O.page_scores(w.q, ref_summ, w.page_table, w.seq_lens, w.P)
+    ref_sel, ref_cnt = O.top_pages(ref_sc, w.seq_lens, w.P, w.k)
+    margins = O.selection_margin_ulps(ref_sc, w.seq_lens, w.P, w.k)
+    for refresh in (False, True):
+        sc_a = torch.full((w.B, w.Hkv, w.max_pages), float("nan"), device="cuda")
+        sc_b = torch.full((w.B, w.Hkv, 2100), float("nan"), device="cuda")
+        sel_a, cnt_a = K.score_topk(kv, summ, q, w.k, refresh_tail=refresh, scores=sc_a)
+        sel_b, cnt_b = K.score_topk(kv_wide, summ, q, w.k, refresh_tail=refresh, scores=sc_b)
+        sel_c, cnt_c = K.score_topk(kv, summ, q, w.k, refresh_tail=refresh)
+        torch.cuda.synchronize()
+        assert torch.equal(sel_a, sel_b) and torch.equal(cnt_a, cnt_b)
+        assert torch.equal(sel_a, sel_c) and torch.equal(cnt_a, cnt_c)
+        for b in range(w.B):
+            N = w.n_pages(b)
+            assert torch.equal(sc_a[b, :, :N], sc_b[b, :, :N])
+        assert_scores_close(sc_a, ref_sc, w, exact=(dtype == "bf16"))
+        assert_selection_equal(sel_a, cnt_a, ref_sel, ref_cnt, margins)
+
+    # reuse decision: half the sequences keep a query close to the previous one
+    gen = torch.Generator().manual_seed(192)
+    q_prev = w.q.clone().float()
+    q_prev[: w.B // 2] += 0.05 * torch.randn(q_prev[: w.B // 2].shape, generator=gen)
+    q_prev[w.B // 2:] = torch.randn(q_prev[w.B // 2:].shape, generator=gen)
+    q_prev = q_prev.to(w.q.dtype).cuda()
+    prev_idx = torch.randint(0, 5, (w.B, w.Hkv, w.k), generator=gen, dtype=torch.int32).cuda()
+    prev_cnt = torch.full((w.B, w.Hkv), 3, dtype=torch.int32).cuda()
+    res = []
+    for kvx in (kv, kv_wide):
+        res.append(K.score_topk(kvx, summ, q, w.k,
+                                reuse=K.Reuse(q_prev, prev_idx, prev_cnt, 0.8, first_step=False)))
+    torch.cuda.synchronize()
+    for x, y in zip(res[0], res[1]):
+        assert torch.equal(x, y)
+    sel, cnt, used, used_cnt, corrected, sim = res[0]
+    ref_sim = O.query_similarity(w.q, q_prev.cpu(), w.Hkv)
+    assert corrected.cpu().numpy().sum() not in (0, corrected.numel())  # both outcomes occur
+    np.testing.assert_allclose(sim.cpu().numpy(), ref_sim, rtol=0, atol=1e-12)
+    for b in range(w.B):
+        for j in range(w.Hkv):
+            exp_c = int(ref_sim[b, j] < 0.8)
+            assert int(corrected[b, j]) == exp_c
+            src, src_cnt = (sel, cnt) if exp_c else (prev_idx, prev_cnt)
+            assert int(used_cnt[b, j]) == int(src_cnt[b, j])
+            assert torch.equal(used[b, j], src[b, j])
