@@ -141,7 +141,7 @@ size_t kvsel_workspace_bytes(const kvsel_paged_kv* kv, int32_t k, int32_t op,
 kvsel_status kvsel_build_summaries(const kvsel_paged_kv* kv, const kvsel_rope* rope,
                                    int32_t tail_only, void* summ, void* stream);
 
-/* Query-aware page scoring and top-k selection, per (sequence, KV head), in one launch.
+/* Query-aware page scoring and top-k selection, per (sequence, KV head).
  * score[b][j][n] = fp32 rounding of the fp64 sum over the G query heads g of KV head j and the D
  * channels d of (q[b][jG+g][d] >= 0 ? q*hi : q*lo) with lo/hi from summ of page page_table[b][n]
  * (an upper bound of sum_g q_g . k over the page's keys). Products are exact in fp64 and the sum

@@ -487,14 +487,22 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int G) {
   __shared__ float s_m[ATT_MAX_SPLITS], s_l[ATT_MAX_SPLITS];
   const float2* ml = a.part_ml + (size_t)list * ns * G + g;
   const float* pa = a.part_acc + ((size_t)list * ns * G + g) * D + d;
-  for (int s = d; s < ns; s += D) {
-    const float2 v = ml[(size_t)s * G];
-    s_m[s] = v.x;
-    s_l[s] = v.y;
-  }
+  // one round of unconditional loads with clamped indices (a conditional load would make the
+  // compiler wait for each one before the next)
+  const float2 mv = ml[(size_t)min(d, ns - 1) * G];
   float v[MERGE_CHUNK];
 #pragma unroll
-  for (int u = 0; u < MERGE_CHUNK; ++u) v[u] = u < ns ? pa[(size_t)u * G * D] : 0.0f;
+  for (int u = 0; u < MERGE_CHUNK; ++u) v[u] = pa[(size_t)min(u, ns - 1) * G * D];
+  __builtin_amdgcn_sched_barrier(0);
+  if (d < ns) {
+    s_m[d] = mv.x;
+    s_l[d] = mv.y;
+  }
+  for (int s = d + D; s < ns; s += D) {  // more splits than threads
+    const float2 x = ml[(size_t)s * G];
+    s_m[s] = x.x;
+    s_l[s] = x.y;
+  }
   __syncthreads();
   float M = NEG_INF;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, s_m[s]);
@@ -508,7 +516,7 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int G) {
   for (int s0 = 0; s0 < ns; s0 += MERGE_CHUNK) {
     if (s0 > 0) {
 #pragma unroll
-      for (int u = 0; u < MERGE_CHUNK; ++u) v[u] = s0 + u < ns ? pa[(size_t)(s0 + u) * G * D] : 0.0f;
+      for (int u = 0; u < MERGE_CHUNK; ++u) v[u] = pa[(size_t)min(s0 + u, ns - 1) * G * D];
     }
 #pragma unroll
     for (int u = 0; u < MERGE_CHUNK; ++u) {

@@ -26,6 +26,7 @@ namespace kvsel {
 constexpr int SEL_THREADS = 256;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
 constexpr int SEL_LDS_KEYS = 8192;
+constexpr int TOPK_BATCH = 8;  // independent score loads in flight per thread
 
 struct SelectArgs {
   const void* k_pool;
@@ -122,7 +123,9 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, ui
 }
 
 // Exact top-k of the N scores of one list, by the whole block; writes out[0..k) ascending
-// (padded with -1) and, when `used` is non-null, the same list there too.
+// (padded with -1) and, when `used` is non-null, the same list there too. `first` holds the
+// caller's loads of sc[min(tid + u * NT, row - 1)] for u < TOPK_BATCH (issued before the
+// sequence length is known, so they overlap its load).
 //
 // Radix select over orderable keys, most significant digit first, starting below the bits all
 // keys share (block min / max) and stopping as soon as the bucket holding the k-th largest key
@@ -134,9 +137,9 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, ui
 // KEYS_IN_LDS: the caller already stored the N (<= SEL_LDS_KEYS) keys in sm.keys and `sc` is
 // not read.
 template <int NT, bool KEYS_IN_LDS>
-__device__ void block_topk(const float* __restrict__ sc, int N, int k, int32_t* __restrict__ out,
-                           int32_t* __restrict__ used, TopkSmem<NT>& sm) {
-  constexpr int BATCH = 8;
+__device__ void block_topk(const float* __restrict__ sc, const float* first, int N, int k,
+                           int32_t* __restrict__ out, int32_t* __restrict__ used, TopkSmem<NT>& sm) {
+  constexpr int BATCH = TOPK_BATCH;
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (N <= k) {
@@ -154,11 +157,15 @@ __device__ void block_topk(const float* __restrict__ sc, int N, int k, int32_t* 
       kmin = min(kmin, sm.keys[i]);
       kmax = max(kmax, sm.keys[i]);
     }
-  } else
-  for (int base = tid; base < N; base += NT * BATCH) {
+  } else {
     float v[BATCH];
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) v[u] = sc[min(base + u * NT, N - 1)];  // clamped
+    for (int u = 0; u < BATCH; ++u) v[u] = first[u];
+    for (int base = tid; base < N; base += NT * BATCH) {
+      if (base != tid) {
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) v[u] = sc[min(base + u * NT, N - 1)];  // clamped
+      }
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int i = base + u * NT;
@@ -168,6 +175,7 @@ __device__ void block_topk(const float* __restrict__ sc, int N, int k, int32_t* 
         kmin = min(kmin, key);
         kmax = max(kmax, key);
       }
+    }
     }
   }
   kmin = wave_min_u32(kmin);
@@ -265,23 +273,30 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   const int b = list / a.Hkv, j = list % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = a.P;
-  const int L = a.seq_lens[b];
-  const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;  // never past the table row
   const int n0 = chunk * PPB;
   const int Hq = a.Hkv * G;
   const T* q = (const T*)a.q;
   const int c0 = (lane % LPR) * VEC;
   const int n = n0 + w * PPW + lane / LPR;
-  const bool active = n < N;
 
-  // ---- loads first (unconditional, clamped addresses): q slice, page id, summary rows ----
+  // ---- loads first (unconditional, clamped addresses): q slice, page id, summary rows; the
+  // sequence length is read after they are issued, so its latency overlaps theirs ----
   uint4 qraw[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) qraw[g] = load16(q + ((size_t)b * Hq + j * G + g) * D + c0);
-  // inactive lanes read entry 0 (any value) and clamp it into the pool: an address, never used
-  const int p = min(max(a.page_table[(size_t)b * a.maxp + (active ? n : 0)], 0), a.Npp - 1);
-  const T* srow = (const T*)a.summ + ((size_t)p * a.Hkv + j) * 2 * D + c0;
+  // the table index depends on the row width only, so this load does not wait for seq_lens;
+  // entries past the sequence may hold anything and are clamped into the pool (never used)
+  const int pt_raw = a.page_table[(size_t)b * a.maxp + min(n, a.maxp - 1)];
+  const T* summ = (const T*)a.summ;
+  const size_t row_off = (size_t)j * 2 * D + c0, page_stride = (size_t)a.Hkv * 2 * D;
+  __builtin_amdgcn_sched_barrier(0);
+  const int L = a.seq_lens[b];
+  __builtin_amdgcn_sched_barrier(0);
+  const int p = min(max(pt_raw, 0), a.Npp - 1);
+  const T* srow = summ + (size_t)p * page_stride + row_off;
   const uint4 lo_raw = load16(srow), hi_raw = load16(srow + D);
+  const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;  // never past the table row
+  const bool active = n < N;
 
   // ---- decode-time refresh of the tail page's summary (overlaps the loads above) ----
   const bool has_tail = a.refresh_tail && N > 0 && N - 1 >= n0 && N - 1 < n0 + PPB;
@@ -378,11 +393,11 @@ __device__ int reuse_decision(const SelectArgs& a, int list, int b, int j, int* 
 
 // Selection outputs of one list once its keys are known (shared by both launch structures).
 template <int NT, bool KEYS_IN_LDS>
-__device__ void select_outputs(const SelectArgs& a, int list, int N, int corrected, bool reuse_on,
-                               TopkSmem<NT>& sm) {
+__device__ void select_outputs(const SelectArgs& a, const float* first, int list, int N,
+                               int corrected, bool reuse_on, TopkSmem<NT>& sm) {
   const int tid = threadIdx.x;
   int32_t* used = (reuse_on && corrected) ? a.reuse.used_idx + (size_t)list * a.k : nullptr;
-  block_topk<NT, KEYS_IN_LDS>(a.scores + (size_t)list * a.maxp, N, a.k,
+  block_topk<NT, KEYS_IN_LDS>(a.scores + (size_t)list * a.maxp, first, N, a.k,
                               a.sel_idx + (size_t)list * a.k, used, sm);
   const int cnt = N < a.k ? N : a.k;
   if (tid == 0) a.sel_cnt[list] = cnt;
@@ -403,11 +418,15 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(SelectArgs a) {
   __shared__ int s_corr;
   const int list = blockIdx.x;
   const int b = list / a.Hkv, j = list % a.Hkv;
+  const float* sc = a.scores + (size_t)list * a.maxp;
+  float first[TOPK_BATCH];
+#pragma unroll
+  for (int u = 0; u < TOPK_BATCH; ++u) first[u] = sc[min((int)threadIdx.x + u * SEL_THREADS, a.maxp - 1)];
   const int L = a.seq_lens[b];
   const int N = L > 0 ? min((L + a.P - 1) / a.P, a.maxp) : 0;
   const bool reuse_on = a.reuse.q_prev != nullptr;
   const int corrected = reuse_on ? reuse_decision<T, D, G>(a, list, b, j, &s_corr) : 1;
-  select_outputs<SEL_THREADS, false>(a, list, N, corrected, reuse_on, sm);
+  select_outputs<SEL_THREADS, false>(a, first, list, N, corrected, reuse_on, sm);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -513,7 +532,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
   __syncthreads();
   const bool reuse_on = a.reuse.q_prev != nullptr;
   const int corrected = reuse_on ? reuse_decision<T, D, G>(a, list, b, j, &s_corr) : 1;
-  select_outputs<FUSED_THREADS, true>(a, list, N, corrected, reuse_on, sm);
+  select_outputs<FUSED_THREADS, true>(a, nullptr, list, N, corrected, reuse_on, sm);
 }
 
 template <typename T, int D>

@@ -298,3 +298,32 @@ def test_selection_launch_structures_agree(K, dtype):
             src, src_cnt = (sel, cnt) if exp_c else (prev_idx, prev_cnt)
             assert int(used_cnt[b, j]) == int(src_cnt[b, j])
             assert torch.equal(used[b, j], src[b, j])
+
+
+@pytest.mark.parametrize("case", [
+    # 256 splits of one page, G = 8: more (split, group row) pairs than threads, several load rounds
+    dict(seed=201, B=2, Hq=16, Hkv=2, D=128, P=32, k=256, lens=[32 * 300 + 9, 32 * 256],
+         dtype="bf16", pps=1),
+    dict(seed=202, B=2, Hq=16, Hkv=2, D=64, P=16, k=256, lens=[16 * 260, 16 * 100 + 3],
+         dtype="f32", pps=1),
+    # lists whose counts differ: empty splits at the end of the short list
+    dict(seed=203, B=3, Hq=8, Hkv=2, D=128, P=32, k=40, lens=[32 * 50, 32 * 7 + 1, 0],
+         dtype="bf16", pps=2),
+])
+def test_many_splits_merge_parity(K, case):
+    w = W.custom(case["seed"], case["B"], case["Hq"], case["Hkv"], case["D"], case["P"], case["k"],
+                 case["lens"], case["dtype"])
+    ref = oracle_path(w, scale_of(w.D))
+    ws = None
+    for rep in range(3):  # the same workspace three times
+        say(f"many splits {case['seed']} rep {rep}")
+        kv = kv_of(K, w)
+        summ = K.build_summaries(kv)
+        sel, cnt = K.score_topk(kv, summ, w.q.cuda(), w.k)
+        if ws is None:
+            ws = K.new_workspace(kv, w.k, K.KVSEL_OP_ATTENTION, case["pps"])
+        out, lse = K.sparse_decode_attn(kv, w.q.cuda(), sel, cnt, w.k,
+                                        pages_per_split=case["pps"], workspace=ws)
+        torch.cuda.synchronize()
+        assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["margins"])
+        assert_attention_close(out, lse, ref["out"], ref["lse"], w.dtype)
