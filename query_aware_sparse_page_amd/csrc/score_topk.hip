@@ -45,12 +45,37 @@ struct SelectArgs {
 template <int NT>
 struct TopkSmem {
   static constexpr int NW = NT / 64;
+  static constexpr int HC = NW < 4 ? NW : 4;  // histogram copies: wave w counts into copy w % HC
   uint32_t keys[SEL_LDS_KEYS];
-  uint32_t hist[NW][256];
+  // three rotating sets of HC 256-bin histograms, as 64 uint4 (lane l reads bins 4l .. 4l+3)
+  uint4 hist[3][HC][64];
   uint32_t wave_a[NW], wave_b[NW];      // scan totals
   uint32_t wave_min[NW], wave_max[NW];  // key range (own slots: read with no barrier after)
-  uint32_t prefix, need, count;
 };
+
+// Boundary bin of one radix pass, found by every wave on its own from the histogram totals
+// (t = bins 4l .. 4l+3 of lane l): the bin b with above(b) < need <= above(b) + count(b), where
+// above(b) counts the keys in larger bins. Returns the digit; need becomes need - above(b) and
+// count the bin's total. The result is wave-uniform and identical in every wave.
+__device__ __forceinline__ uint32_t boundary_bin(uint4 t, uint32_t& need, uint32_t& count) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t incl = wave_scan_add(t.x + t.y + t.z + t.w);
+  // keys above bins 4l+3, 4l+2, 4l+1, 4l (higher lanes hold the larger bins)
+  const uint32_t a3 = __builtin_amdgcn_readlane(incl, 63) - incl;
+  const uint32_t a2 = a3 + t.w, a1 = a2 + t.z, a0 = a1 + t.y;
+  const bool h3 = a3 < need && need <= a2;
+  const bool h2 = a2 < need && need <= a1;
+  const bool h1 = a1 < need && need <= a0;
+  const bool h0 = a0 < need && need <= a0 + t.x;
+  const uint32_t sel = h3 ? 3u : h2 ? 2u : h1 ? 1u : 0u;
+  const uint32_t above = h3 ? a3 : h2 ? a2 : h1 ? a1 : a0;
+  const uint32_t cnt = h3 ? t.w : h2 ? t.z : h1 ? t.y : t.x;
+  const int src = __builtin_ctzll(__ballot(h0 || h1 || h2 || h3));  // exactly one lane
+  const uint32_t packed = __builtin_amdgcn_readlane((4u * lane + sel) | (above << 8), src);
+  count = __builtin_amdgcn_readlane(cnt, src);
+  need -= packed >> 8;
+  return packed & 255u;
+}
 
 // Min / max of the valid rows of one (page, KV head) tile, computed by one wave. On return the
 // lanes of row group 0 hold lo / hi of channels [c0, c0 + VEC).
@@ -134,9 +159,9 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, ui
 // reduction runs on DPP. The chosen set is {keys in buckets above the boundary bucket} plus the
 // first `need` keys of the boundary bucket in index order (ties to the lower page index); one
 // block scan over per-thread contiguous index chunks gives every chosen page its output slot.
-// KEYS_IN_LDS: the caller already stored the N (<= SEL_LDS_KEYS) keys in sm.keys and `sc` is
-// not read.
-template <int NT, bool KEYS_IN_LDS>
+// This form reads the scores from memory (keeping them in LDS when they fit); lists whose keys
+// fit in registers take block_topk_regs.
+template <int NT>
 __device__ void block_topk(const float* __restrict__ sc, const float* first, int N, int k,
                            int32_t* __restrict__ out, int32_t* __restrict__ used, TopkSmem<NT>& sm) {
   constexpr int BATCH = TOPK_BATCH;
@@ -150,14 +175,9 @@ __device__ void block_topk(const float* __restrict__ sc, const float* first, int
     }
     return;
   }
-  const bool cached = KEYS_IN_LDS || N <= SEL_LDS_KEYS;
+  const bool cached = N <= SEL_LDS_KEYS;
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  if (KEYS_IN_LDS) {
-    for (int i = tid; i < N; i += NT) {
-      kmin = min(kmin, sm.keys[i]);
-      kmax = max(kmax, sm.keys[i]);
-    }
-  } else {
+  {
     float v[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) v[u] = first[u];
@@ -178,9 +198,10 @@ __device__ void block_topk(const float* __restrict__ sc, const float* first, int
     }
     }
   }
+  constexpr int HC = TopkSmem<NT>::HC;
   kmin = wave_min_u32(kmin);
   kmax = wave_max_u32(kmax);
-  for (int i = tid; i < NW * 256; i += NT) (&sm.hist[0][0])[i] = 0;
+  for (int i = tid; i < HC * 64; i += NT) (&sm.hist[0][0][0])[i] = make_uint4(0, 0, 0, 0);
   if (lane == 0) {
     sm.wave_min[w] = kmin;
     sm.wave_max[w] = kmax;
@@ -196,41 +217,34 @@ __device__ void block_topk(const float* __restrict__ sc, const float* first, int
     const int top_bit = 31 - __clz((int)(kmin ^ kmax));
     mask = top_bit == 31 ? 0u : ~((2u << top_bit) - 1u);
     prefix = kmax & mask;
-    for (int top = top_bit; top >= 0; top -= 8) {
+    // One barrier per pass: the counts go into set p % 3; after the barrier every wave reads the
+    // totals and finds the boundary itself. Set (p + 1) % 3 is cleared before the barrier; its
+    // last readers (pass p - 2) all passed the previous barrier.
+    for (int top = top_bit, pass = 0; top >= 0; top -= 8, ++pass) {
+      const int cur = pass % 3, nxt = (pass + 1) % 3;
       const int shift = top >= 7 ? top - 7 : 0;
       const uint32_t dmask = (2u << (top - shift)) - 1u;
+      for (int i = tid; i < HC * 64; i += NT) (&sm.hist[nxt][0][0])[i] = make_uint4(0, 0, 0, 0);
+      uint32_t* h = (uint32_t*)&sm.hist[cur][w % HC][0];
       for (int i = tid; i < N; i += NT) {
         const uint32_t u = cached ? sm.keys[i] : score_key(sc[i]);
-        if ((u & mask) == prefix) atomicAdd(&sm.hist[w][(u >> shift) & dmask], 1u);
+        if ((u & mask) == prefix) atomicAdd(&h[(u >> shift) & dmask], 1u);
       }
       __syncthreads();
-      // thread t < 256 owns bin 255 - t (largest first); its total over the per-wave histograms
-      const int bin = 255 - tid;
-      uint32_t tot = 0;
-      if (tid < 256) {
+      uint4 t = sm.hist[cur][0][lane];
 #pragma unroll
-        for (int v = 0; v < NW; ++v) {
-          tot += sm.hist[v][bin];
-          sm.hist[v][bin] = 0;  // ready for the next pass (read only by this thread)
-        }
+      for (int c = 1; c < HC; ++c) {
+        const uint4 x = sm.hist[cur][c][lane];
+        t.x += x.x;
+        t.y += x.y;
+        t.z += x.z;
+        t.w += x.w;
       }
-      const uint32_t incl = wave_scan_add(tot);
-      if (lane == 63) sm.wave_a[w] = incl;
-      __syncthreads();
-      uint32_t above = incl - tot;  // keys in larger bins
-#pragma unroll
-      for (int v = 0; v < NW; ++v)
-        if (v < w) above += sm.wave_a[v];
-      if (tot > 0 && above < need && above + tot >= need) {
-        sm.prefix = prefix | ((uint32_t)bin << shift);
-        sm.need = need - above;
-        sm.count = tot;
-      }
-      __syncthreads();
-      prefix = sm.prefix;
-      need = sm.need;
+      uint32_t count;
+      const uint32_t digit = boundary_bin(t, need, count);
+      prefix |= digit << shift;
       mask |= dmask << shift;
-      if (sm.count == need) break;  // the whole boundary bucket is taken
+      if (count == need) break;  // the whole boundary bucket is taken
     }
   }
   // ---- compaction: thread t owns indices [t*C, t*C + C) ----
@@ -355,6 +369,109 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   if (active && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
 }
 
+// The same selection with the keys in registers: thread t holds the keys of indices
+// t*C .. t*C + C - 1 (indices >= N are ignored). A radix pass is then one predicated LDS atomic
+// per key, one barrier, and the boundary search.
+template <int NT, int C>
+__device__ void block_topk_regs(const uint32_t (&key)[C], int N, int k, int32_t* __restrict__ out,
+                                int32_t* __restrict__ used, TopkSmem<NT>& sm) {
+  constexpr int NW = NT / 64;
+  constexpr int HC = TopkSmem<NT>::HC;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (N <= k) {
+    for (int i = tid; i < k; i += NT) {
+      const int v = i < N ? i : -1;
+      out[i] = v;
+      if (used) used[i] = v;
+    }
+    return;
+  }
+  const int i0 = tid * C;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int u = 0; u < C; ++u) {
+    if (i0 + u < N) {
+      kmin = min(kmin, key[u]);
+      kmax = max(kmax, key[u]);
+    }
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  for (int i = tid; i < HC * 64; i += NT) (&sm.hist[0][0][0])[i] = make_uint4(0, 0, 0, 0);
+  if (lane == 0) {
+    sm.wave_min[w] = kmin;
+    sm.wave_max[w] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    kmin = min(kmin, sm.wave_min[v]);
+    kmax = max(kmax, sm.wave_max[v]);
+  }
+  uint32_t prefix = kmax, mask = 0xffffffffu, need = (uint32_t)k;
+  if (kmin != kmax) {
+    const int top_bit = 31 - __clz((int)(kmin ^ kmax));
+    mask = top_bit == 31 ? 0u : ~((2u << top_bit) - 1u);
+    prefix = kmax & mask;
+    // rotating histogram sets as in block_topk: one barrier per pass
+    for (int top = top_bit, pass = 0; top >= 0; top -= 8, ++pass) {
+      const int cur = pass % 3, nxt = (pass + 1) % 3;
+      const int shift = top >= 7 ? top - 7 : 0;
+      const uint32_t dmask = (2u << (top - shift)) - 1u;
+      for (int i = tid; i < HC * 64; i += NT) (&sm.hist[nxt][0][0])[i] = make_uint4(0, 0, 0, 0);
+      uint32_t* h = (uint32_t*)&sm.hist[cur][w % HC][0];
+#pragma unroll
+      for (int u = 0; u < C; ++u) {
+        if (i0 + u < N && (key[u] & mask) == prefix) atomicAdd(&h[(key[u] >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      uint4 t = sm.hist[cur][0][lane];
+#pragma unroll
+      for (int c = 1; c < HC; ++c) {
+        const uint4 x = sm.hist[cur][c][lane];
+        t.x += x.x;
+        t.y += x.y;
+        t.z += x.z;
+        t.w += x.w;
+      }
+      uint32_t count;
+      const uint32_t digit = boundary_bin(t, need, count);
+      prefix |= digit << shift;
+      mask |= dmask << shift;
+      if (count == need) break;  // the whole boundary bucket is taken
+    }
+  }
+  // ---- compaction over the thread's contiguous indices ----
+  uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int u = 0; u < C; ++u) {
+    const uint32_t m = key[u] & mask;
+    const bool ok = i0 + u < N;
+    n_gt += ok && m > prefix;
+    n_eq += ok && m == prefix;
+  }
+  uint32_t gt_ex, eq_ex;
+  block_exclusive_scan2(n_gt, n_eq, gt_ex, eq_ex, sm);
+  uint32_t pos = gt_ex + min(eq_ex, need);
+  uint32_t eq_seen = eq_ex;
+#pragma unroll
+  for (int u = 0; u < C; ++u) {
+    const int i = i0 + u;
+    const uint32_t m = key[u] & mask;
+    if (i < N) {
+      const bool sel = m > prefix || (m == prefix && eq_seen < need);
+      eq_seen += m == prefix;
+      if (sel) {
+        if (pos < (uint32_t)k) {
+          out[pos] = i;
+          if (used) used[pos] = i;
+        }
+        ++pos;
+      }
+    }
+  }
+}
+
 // Speculative-reuse decision of one list, by the block's first wave: mean over the group of
 // cos(q, q_prev) in fp64; corrected = first step or C < tau. Every thread gets the decision.
 template <typename T, int D, int G>
@@ -392,13 +509,13 @@ __device__ int reuse_decision(const SelectArgs& a, int list, int b, int j, int* 
 }
 
 // Selection outputs of one list once its keys are known (shared by both launch structures).
-template <int NT, bool KEYS_IN_LDS>
-__device__ void select_outputs(const SelectArgs& a, const float* first, int list, int N,
-                               int corrected, bool reuse_on, TopkSmem<NT>& sm) {
+// topk(out, used) runs the block's selection.
+template <int NT, class TopK>
+__device__ void select_outputs(const SelectArgs& a, int list, int N, int corrected, bool reuse_on,
+                               TopK topk) {
   const int tid = threadIdx.x;
   int32_t* used = (reuse_on && corrected) ? a.reuse.used_idx + (size_t)list * a.k : nullptr;
-  block_topk<NT, KEYS_IN_LDS>(a.scores + (size_t)list * a.maxp, first, N, a.k,
-                              a.sel_idx + (size_t)list * a.k, used, sm);
+  topk(a.sel_idx + (size_t)list * a.k, used);
   const int cnt = N < a.k ? N : a.k;
   if (tid == 0) a.sel_cnt[list] = cnt;
   if (reuse_on) {
@@ -412,21 +529,54 @@ __device__ void select_outputs(const SelectArgs& a, const float* first, int list
   }
 }
 
+// Top-k of one list with C keys per thread in registers (C * SEL_THREADS >= row width). The score
+// loads depend on the row width only, so they go out before the sequence length is known.
+template <typename T, int D, int G, int C>
+__device__ void topk_regs(const SelectArgs& a, int list, int b, int j, TopkSmem<SEL_THREADS>& sm,
+                          int* s_corr) {
+  const int tid = threadIdx.x;
+  const float* sc = a.scores + (size_t)list * a.maxp;
+  float v[C];
+#pragma unroll
+  for (int u = 0; u < C; ++u) v[u] = sc[min(tid * C + u, a.maxp - 1)];
+  const int L = a.seq_lens[b];
+  const int N = L > 0 ? min((L + a.P - 1) / a.P, a.maxp) : 0;
+  const bool reuse_on = a.reuse.q_prev != nullptr;
+  const int corrected = reuse_on ? reuse_decision<T, D, G>(a, list, b, j, s_corr) : 1;
+  uint32_t key[C];
+#pragma unroll
+  for (int u = 0; u < C; ++u) key[u] = score_key(v[u]);
+  select_outputs<SEL_THREADS>(a, list, N, corrected, reuse_on, [&](int32_t* out, int32_t* used) {
+    block_topk_regs<SEL_THREADS, C>(key, N, a.k, out, used, sm);
+  });
+}
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(SelectArgs a) {
   __shared__ TopkSmem<SEL_THREADS> sm;
   __shared__ int s_corr;
+  const int tid = threadIdx.x;
   const int list = blockIdx.x;
   const int b = list / a.Hkv, j = list % a.Hkv;
+  const int cpt = (a.maxp + SEL_THREADS - 1) / SEL_THREADS;  // keys per thread
+  if (cpt <= 1) return topk_regs<T, D, G, 1>(a, list, b, j, sm, &s_corr);
+  if (cpt <= 2) return topk_regs<T, D, G, 2>(a, list, b, j, sm, &s_corr);
+  if (cpt <= 4) return topk_regs<T, D, G, 4>(a, list, b, j, sm, &s_corr);
+  if (cpt <= 8) return topk_regs<T, D, G, 8>(a, list, b, j, sm, &s_corr);
+  if (cpt <= 16) return topk_regs<T, D, G, 16>(a, list, b, j, sm, &s_corr);
+  if (cpt <= 32) return topk_regs<T, D, G, 32>(a, list, b, j, sm, &s_corr);
+  // wider rows: scores re-read from memory by block_topk
   const float* sc = a.scores + (size_t)list * a.maxp;
   float first[TOPK_BATCH];
 #pragma unroll
-  for (int u = 0; u < TOPK_BATCH; ++u) first[u] = sc[min((int)threadIdx.x + u * SEL_THREADS, a.maxp - 1)];
+  for (int u = 0; u < TOPK_BATCH; ++u) first[u] = sc[min(tid + u * SEL_THREADS, a.maxp - 1)];
   const int L = a.seq_lens[b];
   const int N = L > 0 ? min((L + a.P - 1) / a.P, a.maxp) : 0;
   const bool reuse_on = a.reuse.q_prev != nullptr;
   const int corrected = reuse_on ? reuse_decision<T, D, G>(a, list, b, j, &s_corr) : 1;
-  select_outputs<SEL_THREADS, false>(a, first, list, N, corrected, reuse_on, sm);
+  select_outputs<SEL_THREADS>(a, list, N, corrected, reuse_on, [&](int32_t* out, int32_t* used) {
+    block_topk<SEL_THREADS>(sc, first, N, a.k, out, used, sm);
+  });
 }
 
 // ------------------------------------------------------------------------------------------
@@ -532,7 +682,18 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
   __syncthreads();
   const bool reuse_on = a.reuse.q_prev != nullptr;
   const int corrected = reuse_on ? reuse_decision<T, D, G>(a, list, b, j, &s_corr) : 1;
-  select_outputs<FUSED_THREADS, true>(a, nullptr, list, N, corrected, reuse_on, sm);
+  static_assert(FUSED_MAX_PAGES == 2 * FUSED_THREADS, "one or two keys per thread");
+  if (N <= FUSED_THREADS) {
+    uint32_t key[1] = {sm.keys[tid]};
+    select_outputs<FUSED_THREADS>(a, list, N, corrected, reuse_on, [&](int32_t* out, int32_t* used) {
+      block_topk_regs<FUSED_THREADS, 1>(key, N, a.k, out, used, sm);
+    });
+  } else {
+    uint32_t key[2] = {sm.keys[2 * tid], sm.keys[2 * tid + 1]};
+    select_outputs<FUSED_THREADS>(a, list, N, corrected, reuse_on, [&](int32_t* out, int32_t* used) {
+      block_topk_regs<FUSED_THREADS, 2>(key, N, a.k, out, used, sm);
+    });
+  }
 }
 
 template <typename T, int D>
