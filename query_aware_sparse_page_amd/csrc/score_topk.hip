@@ -77,10 +77,12 @@ __device__ __forceinline__ uint32_t boundary_bin(uint4 t, uint32_t& need, uint32
   return packed & 255u;
 }
 
-// Min / max of the valid rows of one (page, KV head) tile, computed by one wave. On return the
-// lanes of row group 0 hold lo / hi of channels [c0, c0 + VEC).
+// Min / max of the valid rows (1 <= valid) of one (page, KV head) tile of physical page pt,
+// computed by one wave. On return every lane holds lo / hi of its channels [c0, c0 + VEC). The
+// row loads are unconditional (rows past `valid` re-read the last valid row and are ignored), so
+// they all go out at once; the page's rotary row is read after them.
 template <typename T, int D>
-__device__ __forceinline__ void tile_minmax(const T* tile, int valid, int P, int lane, int prow,
+__device__ __forceinline__ void tile_minmax(const T* tile, int valid, int P, int lane, int pt,
                                             const RopeArgs& rope, float* lo, float* hi) {
   using M = row_map<T, D>;
   constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
@@ -91,8 +93,9 @@ __device__ __forceinline__ void tile_minmax(const T* tile, int valid, int P, int
 #pragma unroll
   for (int i = 0; i < MAX_LOADS; ++i) {
     const int s = rg + i * RPW;
-    raw[i] = (s < valid) ? load16(tile + (size_t)s * D + c0) : make_uint4(0, 0, 0, 0);
+    raw[i] = load16(tile + (size_t)min(s, valid - 1) * D + c0);
   }
+  const int prow = rope.page_row ? rope.page_row[pt] : -1;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     lo[e] = __int_as_float(0x7f800000);
@@ -280,7 +283,6 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   constexpr int VEC = M::VEC, LPR = M::LPR;
   constexpr int PPW = 64 / LPR;          // pages per wave
   constexpr int PPB = SEL_WAVES * PPW;   // pages per block
-  __shared__ float s_tail[2][D];
 
   const int list = blockIdx.x % a.nlists;
   const int chunk = blockIdx.x / a.nlists;
@@ -312,29 +314,35 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;  // never past the table row
   const bool active = n < N;
 
-  // ---- decode-time refresh of the tail page's summary (overlaps the loads above) ----
-  const bool has_tail = a.refresh_tail && N > 0 && N - 1 >= n0 && N - 1 < n0 + PPB;
-  if (has_tail) {
-    if (w == 0) {
-      const int nt = N - 1;
-      const int pt = a.page_table[(size_t)b * a.maxp + nt];
-      const int valid = L - nt * P;
-      const int prow = a.rope.page_row ? a.rope.page_row[pt] : -1;
-      float lo[VEC], hi[VEC];
-      tile_minmax<T, D>((const T*)a.k_pool + ((size_t)pt * a.Hkv + j) * P * D, valid, P, lane, prow,
-                        a.rope, lo, hi);
-      if (lane < LPR) {
-        T* out = (T*)a.summ + ((size_t)pt * a.Hkv + j) * 2 * D;
-        store16(out + c0, pack<T>(lo));
-        store16(out + D + c0, pack<T>(hi));
+  // ---- decode-time refresh of the tail page's summary, by the wave that scores that page: the
+  // page id is already in its lanes, so the key tile loads go out one hop after the page table,
+  // alongside the summary loads, and no other wave waits ----
+  float lo[VEC], hi[VEC];
+  const int nt = N - 1;
+  const int wn0 = n0 + w * PPW;  // first page of this wave
+  if (a.refresh_tail && N > 0 && nt >= wn0 && nt < wn0 + PPW) {  // wave-uniform
+    const int rg = nt - wn0;                                   // the tail page's row group
+    const int pt = __builtin_amdgcn_readlane(p, rg * LPR);
+    float flo[VEC], fhi[VEC];
+    tile_minmax<T, D>((const T*)a.k_pool + ((size_t)pt * a.Hkv + j) * P * D, L - nt * P, P, lane,
+                      pt, a.rope, flo, fhi);
+    if (lane < LPR) {
+      T* out = (T*)a.summ + ((size_t)pt * a.Hkv + j) * 2 * D;
+      store16(out + c0, pack<T>(flo));
+      store16(out + D + c0, pack<T>(fhi));
+    }
+    unpack<T>(lo_raw, lo);
+    unpack<T>(hi_raw, hi);
+    if (lane / LPR == rg) {  // the stale rows loaded above are replaced by the fresh ones
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          s_tail[0][c0 + e] = lo[e];
-          s_tail[1][c0 + e] = hi[e];
-        }
+      for (int e = 0; e < VEC; ++e) {
+        lo[e] = flo[e];
+        hi[e] = fhi[e];
       }
     }
-    __syncthreads();
+  } else {
+    unpack<T>(lo_raw, lo);
+    unpack<T>(hi_raw, hi);
   }
 
   // ---- scores of this block's pages ----
@@ -345,16 +353,6 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
     unpack<T>(qraw[g], f);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) qd[g][e] = (double)f[e];
-  }
-  float lo[VEC], hi[VEC];
-  unpack<T>(lo_raw, lo);
-  unpack<T>(hi_raw, hi);
-  if (has_tail && n == N - 1) {  // the stale rows loaded above are replaced by the fresh ones
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      lo[e] = s_tail[0][c0 + e];
-      hi[e] = s_tail[1][c0 + e];
-    }
   }
   double acc = 0.0;
 #pragma unroll
@@ -622,10 +620,9 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
   if (refresh && w == 0) {
     const int nt = N - 1;
     const int pt = min(max(a.page_table[(size_t)b * a.maxp + nt], 0), a.Npp - 1);
-    const int prow = a.rope.page_row ? a.rope.page_row[pt] : -1;
     float lo[VEC], hi[VEC];
     tile_minmax<T, D>((const T*)a.k_pool + ((size_t)pt * a.Hkv + j) * P * D, L - nt * P, P, lane,
-                      prow, a.rope, lo, hi);
+                      pt, a.rope, lo, hi);
     if (lane < LPR) {
       T* out = (T*)a.summ + ((size_t)pt * a.Hkv + j) * 2 * D;
       store16(out + c0, pack<T>(lo));

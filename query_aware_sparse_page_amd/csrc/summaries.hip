@@ -49,7 +49,9 @@ __global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_
 #pragma unroll
   for (int i = 0; i < MAX_LOADS; ++i) {
     const int s = rg + i * RPW;
-    raw[i] = (s < valid) ? load16(tile + (size_t)s * D + c0) : make_uint4(0, 0, 0, 0);
+    // unconditional (rows past `valid` >= 1 re-read the last valid row and are ignored below),
+    // so every load goes out before the first wait
+    raw[i] = load16(tile + (size_t)min(s, valid - 1) * D + c0);
   }
 
   float lo[VEC], hi[VEC];
