@@ -52,10 +52,14 @@ extern "C" {
 typedef int32_t kvsel_status;
 #define KVSEL_OK 0
 #define KVSEL_ERR_INVALID_ARGUMENT 1 /* NULL required pointer, size < 1, Hq % Hkv != 0, ...  */
-#define KVSEL_ERR_UNSUPPORTED 2      /* D, P, G or dtype without a kernel                    */
+#define KVSEL_ERR_UNSUPPORTED 2      /* D, P, G, dtype or size without a kernel               */
 #define KVSEL_ERR_WORKSPACE 3        /* workspace NULL or smaller than kvsel_workspace_bytes */
 #define KVSEL_ERR_DEVICE 4           /* current device is not gfx950, or no device           */
 #define KVSEL_ERR_LAUNCH 5           /* the HIP runtime rejected a launch                    */
+
+/* Largest supported batch and page-table width (launch-grid limits). */
+#define KVSEL_MAX_BATCH 65535
+#define KVSEL_MAX_PAGES_PER_SEQ 1048576
 
 #define KVSEL_F32 0
 #define KVSEL_BF16 1

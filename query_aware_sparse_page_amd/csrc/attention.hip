@@ -3,8 +3,9 @@
 //
 // Work unit: a "tile" of TT token slots (TT = 32 for bf16, 16 for fp32) taken in order from the
 // concatenated selected pages of one list (= sequence, KV head). Grid: one block per
-// (split, list), list varying fastest, so that all splits of a list are placed on one XCD by the
-// round-robin block placement when the number of lists is a multiple of 8. A block has WAVES
+// (KV head, sequence, split) in a 3-D grid, KV head varying fastest, so that all splits of a list
+// are placed on one XCD by the round-robin block placement when the number of lists is a multiple
+// of 8, and no block index needs an integer division. A block has WAVES
 // waves; each wave owns TPW consecutive tiles, issues every K and V load of its tiles first,
 // then runs the contractions on MFMA with the GQA group of query heads as the M dimension
 // (rows >= G are zero and ignored):
@@ -179,8 +180,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a, int G
   constexpr int VB = D / 16;   // 16-channel blocks of P V
   using TP = TilePages<P, TT, TPW>;
   const float NEG_INF = __int_as_float(0xff800000);
-  const int list = blockIdx.x % a.nlists, split = blockIdx.x / a.nlists;
-  const int b = list / a.Hkv, j = list % a.Hkv;
+  const int j = blockIdx.x, b = blockIdx.y, split = blockIdx.z;  // grid (Hkv, B, splits)
+  const int list = b * a.Hkv + j;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q4 = lane >> 4;
   const int Hq = a.Hkv * G;
@@ -337,8 +338,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(AttnArgs a, int G)
   constexpr int VB = D / 16;   // 16-channel blocks of P V
   using TP = TilePages<P, TT, TPW>;
   const float NEG_INF = __int_as_float(0xff800000);
-  const int list = blockIdx.x % a.nlists, split = blockIdx.x / a.nlists;
-  const int b = list / a.Hkv, j = list % a.Hkv;
+  const int j = blockIdx.x, b = blockIdx.y, split = blockIdx.z;  // grid (Hkv, B, splits)
+  const int list = b * a.Hkv + j;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q4 = lane >> 4;
   const int Hq = a.Hkv * G;
@@ -479,20 +480,22 @@ constexpr int MERGE_CHUNK = 32;
 template <typename T, int D>
 __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int G) {
   const float NEG_INF = __int_as_float(0xff800000);
-  const int list = blockIdx.x / G, g = blockIdx.x % G;
-  const int b = list / a.Hkv, j = list % a.Hkv;
+  const int g = blockIdx.x, j = blockIdx.y, b = blockIdx.z;  // grid (G, Hkv, B)
+  const int list = b * a.Hkv + j;
   const int d = threadIdx.x;
   const int Hq = a.Hkv * G;
   const int ns = a.nsplit;
   __shared__ float s_m[ATT_MAX_SPLITS], s_l[ATT_MAX_SPLITS];
   const float2* ml = a.part_ml + (size_t)list * ns * G + g;
-  const float* pa = a.part_acc + ((size_t)list * ns * G + g) * D + d;
+  const float* pa = a.part_acc + ((size_t)list * ns * G + g) * D;  // block-uniform base
+  const int GD = G * D;
   // one round of unconditional loads with clamped indices (a conditional load would make the
-  // compiler wait for each one before the next)
-  const float2 mv = ml[(size_t)min(d, ns - 1) * G];
+  // compiler wait for each one before the next); each split's row address is block-uniform, so
+  // a load is a scalar base plus this thread's channel offset
+  const float2 mv = ml[min(d, ns - 1) * G];
   float v[MERGE_CHUNK];
 #pragma unroll
-  for (int u = 0; u < MERGE_CHUNK; ++u) v[u] = pa[(size_t)min(u, ns - 1) * G * D];
+  for (int u = 0; u < MERGE_CHUNK; ++u) v[u] = (pa + min(u, ns - 1) * GD)[d];
   __builtin_amdgcn_sched_barrier(0);
   if (d < ns) {
     s_m[d] = mv.x;
@@ -516,7 +519,7 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int G) {
   for (int s0 = 0; s0 < ns; s0 += MERGE_CHUNK) {
     if (s0 > 0) {
 #pragma unroll
-      for (int u = 0; u < MERGE_CHUNK; ++u) v[u] = pa[(size_t)min(s0 + u, ns - 1) * G * D];
+      for (int u = 0; u < MERGE_CHUNK; ++u) v[u] = (pa + min(s0 + u, ns - 1) * GD)[d];
     }
 #pragma unroll
     for (int u = 0; u < MERGE_CHUNK; ++u) {
@@ -578,7 +581,7 @@ size_t attention_workspace(const LaunchKV& kv, int k, int pages_per_split) {
 
 template <typename T, int D, int P, int WAVES, int TPW>
 static void launch_split(const AttnArgs& a, int G, bool rope, hipStream_t stream) {
-  const dim3 grid((unsigned)((long)a.nlists * a.nsplit));
+  const dim3 grid(a.Hkv, a.nlists / a.Hkv, a.nsplit);
   const dim3 block(WAVES * 64);
   if constexpr (sizeof(T) == 2) {
     if (rope) hipLaunchKernelGGL((attn_bf16_kernel<D, P, WAVES, TPW, true>), grid, block, 0, stream, a, G);
@@ -599,7 +602,7 @@ static hipError_t launch_tiles(int tiles, const AttnArgs& a, int G, bool rope, h
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3((unsigned)(a.nlists * G)), dim3(D), 0, stream,
+  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(G, a.Hkv, a.nlists / a.Hkv), dim3(D), 0, stream,
                      a, G);
   return hipGetLastError();
 }

@@ -49,6 +49,9 @@ kvsel_status flatten(const kvsel_paged_kv* kv, int need, LaunchKV* out) {
   if (kv->head_dim != 64 && kv->head_dim != 128) return KVSEL_ERR_UNSUPPORTED;
   if (kv->page_size != 16 && kv->page_size != 32) return KVSEL_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVSEL_ERR_UNSUPPORTED;
+  // grid limits: sequences and page-range chunks index the second and third grid dimensions
+  if (kv->batch > KVSEL_MAX_BATCH || kv->max_pages_per_seq > KVSEL_MAX_PAGES_PER_SEQ)
+    return KVSEL_ERR_UNSUPPORTED;
   out->dtype = kv->dtype == KVSEL_F32 ? 0 : 1;
   out->B = kv->batch;
   out->Hq = kv->num_q_heads;

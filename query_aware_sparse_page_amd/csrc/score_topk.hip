@@ -284,9 +284,9 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   constexpr int PPW = 64 / LPR;          // pages per wave
   constexpr int PPB = SEL_WAVES * PPW;   // pages per block
 
-  const int list = blockIdx.x % a.nlists;
-  const int chunk = blockIdx.x / a.nlists;
-  const int b = list / a.Hkv, j = list % a.Hkv;
+  // grid (Hkv, B, chunks): the indices need no division; KV heads vary fastest
+  const int j = blockIdx.x, b = blockIdx.y, chunk = blockIdx.z;
+  const int list = b * a.Hkv + j;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = a.P;
   const int n0 = chunk * PPB;
@@ -554,8 +554,8 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(SelectArgs a) {
   __shared__ TopkSmem<SEL_THREADS> sm;
   __shared__ int s_corr;
   const int tid = threadIdx.x;
-  const int list = blockIdx.x;
-  const int b = list / a.Hkv, j = list % a.Hkv;
+  const int j = blockIdx.x, b = blockIdx.y;  // grid (Hkv, B)
+  const int list = b * a.Hkv + j;
   const int cpt = (a.maxp + SEL_THREADS - 1) / SEL_THREADS;  // keys per thread
   if (cpt <= 1) return topk_regs<T, D, G, 1>(a, list, b, j, sm, &s_corr);
   if (cpt <= 2) return topk_regs<T, D, G, 2>(a, list, b, j, sm, &s_corr);
@@ -599,8 +599,8 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
   __shared__ TopkSmem<FUSED_THREADS> sm;
   __shared__ int s_pt[FUSED_MAX_PAGES];
   __shared__ int s_corr;
-  const int list = blockIdx.x;
-  const int b = list / a.Hkv, j = list % a.Hkv;
+  const int j = blockIdx.x, b = blockIdx.y;  // grid (Hkv, B)
+  const int list = b * a.Hkv + j;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = a.P;
   const int L = a.seq_lens[b];
@@ -714,16 +714,17 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t stream) {
   // to 1024 pages take 15.8 us against 18.6 us).
   if constexpr (G <= 4) {  // larger groups would spill at 1024 threads
     if (a.nlists >= FUSED_MIN_LISTS && a.maxp <= FUSED_MAX_PAGES) {
-      hipLaunchKernelGGL((select_fused_kernel<T, D, G>), dim3((unsigned)a.nlists), dim3(FUSED_THREADS),
-                         0, stream, a);
+      hipLaunchKernelGGL((select_fused_kernel<T, D, G>), dim3(a.Hkv, a.nlists / a.Hkv),
+                         dim3(FUSED_THREADS), 0, stream, a);
       return hipGetLastError();
     }
   }
-  const long blocks = (long)a.nlists * a.nchunks;
-  hipLaunchKernelGGL((score_kernel<T, D, G>), dim3((unsigned)blocks), dim3(SEL_THREADS), 0, stream, a);
+  hipLaunchKernelGGL((score_kernel<T, D, G>), dim3(a.Hkv, a.nlists / a.Hkv, a.nchunks), dim3(SEL_THREADS),
+                     0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((topk_kernel<T, D, G>), dim3((unsigned)a.nlists), dim3(SEL_THREADS), 0, stream, a);
+  hipLaunchKernelGGL((topk_kernel<T, D, G>), dim3(a.Hkv, a.nlists / a.Hkv), dim3(SEL_THREADS), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -80,6 +80,8 @@ def test_workspace_sizes(K):
     ("page_size", 64, 2),
     ("num_q_heads", 8 * 16, 2),      # G = 16
     ("dtype", 7, 2),
+    ("batch", 65536, 2),             # beyond the launch-grid limits
+    ("max_pages_per_seq", (1 << 20) + 1, 2),
 ])
 def test_descriptor_validation(K, field, value, status):
     lib = K.lib()
