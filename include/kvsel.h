@@ -67,6 +67,7 @@ typedef int32_t kvsel_status;
 /* Workspace kinds for kvsel_workspace_bytes. */
 #define KVSEL_OP_SCORE_TOPK 1
 #define KVSEL_OP_ATTENTION 2
+#define KVSEL_OP_SELECT_ATTEND 3
 
 /* Flags of kvsel_score_topk. */
 #define KVSEL_SCORE_REFRESH_TAIL 1 /* rebuild each sequence's last-page summary first */
@@ -186,6 +187,22 @@ kvsel_status kvsel_sparse_decode_attn(const kvsel_paged_kv* kv, const kvsel_rope
                                       const int32_t* sel_cnt, int32_t k, float scale,
                                       int32_t pages_per_split, void* out, float* lse, void* ws,
                                       size_t ws_bytes, void* stream);
+
+/* Selection and attention in one call: the outputs of kvsel_score_topk (without reuse, scores
+ * kept in the workspace) followed by kvsel_sparse_decode_attn with the library's default split,
+ * bit for bit. The top-k is re-derived inside the attention launch by every block of a list from
+ * the page scores (each block keeps the pages of its own split), so the K / V reads follow one
+ * memory round trip after the scores instead of the selection-ids -> page-table chain, and no
+ * separate top-k launch runs. Rotary gathers, page tables wider than 8192 entries (4096 for
+ * bf16 with P 16) and k above 1024 run the two calls' launches instead; the outputs are the
+ * same either way.
+ * sel_idx / sel_cnt: as kvsel_score_topk. out / lse: as kvsel_sparse_decode_attn. flags: as
+ * kvsel_score_topk. ws / ws_bytes: kvsel_workspace_bytes(kv, k, KVSEL_OP_SELECT_ATTEND, 0).
+ * [FreeKV] sections 1 and 2.1. */
+kvsel_status kvsel_select_attend(const kvsel_paged_kv* kv, const kvsel_rope* rope, void* summ,
+                                 const void* q, int32_t k, int32_t flags, float scale,
+                                 int32_t* sel_idx, int32_t* sel_cnt, void* out, float* lse,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /* Rotary table: cos[r][i], sin[r][i] (fp32 [n_rows][D/2]) of the angle
  * (first_position + r) * theta^(-2i/D), evaluated in fp64 and rounded to fp32. head_dim is even

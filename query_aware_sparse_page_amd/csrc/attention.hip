@@ -32,6 +32,7 @@
 
 #include "kvsel_device.h"
 #include "kvsel_internal.h"
+#include "kvsel_topk.h"
 
 namespace kvsel {
 
@@ -55,7 +56,13 @@ struct AttnArgs {
   float2* part_ml;   // [nlists][nsplit][G]
   void* out;
   float* lse;
+  // fused selection only: the scores, and the selection outputs written by split 0
+  const float* scores;  // [nlists][maxp]
+  int32_t* sel_out;     // [nlists][k]
+  int32_t* cnt_out;     // [nlists]
 };
+
+constexpr int ATT_MAX_PPS = 16;  // pages per split of the fused-selection launches
 
 // Wave-uniform page lookup of the NPT pages a tile of TT token slots touches (NPT = 2 when a
 // 32-slot tile spans two 16-slot pages). The addresses follow the selection id and page-table
@@ -94,6 +101,71 @@ __device__ __forceinline__ void lookup_tiles(const AttnArgs& a, int list, int b,
       tp.page[t][u] = min(max(pg, 0), a.Npp - 1);
       const int sp = split * a.pps + ((first_tile + t) * TT) / P + u;
       tp.valid[t][u] = (in_range && sp < cnt) ? min(P, L - nn * P) : 0;
+    }
+}
+
+// Fused selection (kvsel_select_attend): every block of a list re-derives the list's top-k from
+// the page scores with the block-wide radix select and keeps the pages of its own split. The
+// scores and the page-table row are loaded together, so the K / V loads follow one memory round
+// trip and the select, instead of the selection ids -> page table -> K / V chain. The block of
+// split 0 also writes the selection outputs.
+template <int NT>
+struct SplitSelectSmem {
+  RadixSmem<NT> r;
+  int page[ATT_MAX_PPS];   // physical page at each of the split's positions
+  int valid[ATT_MAX_PPS];  // its valid slots (0: nothing selected at that position)
+};
+
+template <int P, int TT, int TPW, int NT, int C>
+__device__ __forceinline__ void select_tiles(const AttnArgs& a, int list, int b, int split,
+                                             int first_tile, TilePages<P, TT, TPW>& tp,
+                                             SplitSelectSmem<NT>& ss) {
+  constexpr int NPT = TilePages<P, TT, TPW>::NPT;
+  const int tid = threadIdx.x;
+  const float* sc = a.scores + (size_t)list * a.maxp;
+  const int32_t* row = a.page_table + (size_t)b * a.maxp;
+  float v[C];
+  int pt[C];
+#pragma unroll
+  for (int u = 0; u < C; ++u) {  // indices from the row width only: no wait for seq_lens
+    const int i = min(tid * C + u, a.maxp - 1);
+    v[u] = sc[i];
+    pt[u] = row[i];
+  }
+  const int L = a.seq_lens[b];
+  const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;
+  if (tid < a.pps) {
+    ss.page[tid] = 0;
+    ss.valid[tid] = 0;
+  }
+  uint32_t key[C];
+#pragma unroll
+  for (int u = 0; u < C; ++u) key[u] = score_key(v[u]);
+  __syncthreads();  // positions cleared before any is filled
+  const int first = split * a.pps;
+  const bool writer = split == 0 && a.sel_out != nullptr;
+  int32_t* out = a.sel_out + (size_t)list * a.k;
+  block_topk_regs<NT, C>(key, N, a.k, ss.r, [&](int pos, int i, int u) {
+    if (writer) out[pos] = i;
+    const int sp = pos - first;
+    if (sp >= 0 && sp < a.pps) {
+      ss.page[sp] = min(max(pt[u], 0), a.Npp - 1);  // any table value stays inside the pool
+      ss.valid[sp] = min(P, L - i * P);
+    }
+  });
+  if (writer) {
+    const int cnt = min(N, a.k);
+    for (int i = cnt + tid; i < a.k; i += NT) out[i] = -1;
+    if (tid == 0) a.cnt_out[list] = cnt;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int sp = ((first_tile + t) * TT) / P + u;
+      tp.page[t][u] = __builtin_amdgcn_readfirstlane(ss.page[sp]);
+      tp.valid[t][u] = __builtin_amdgcn_readfirstlane(ss.valid[sp]);
     }
 }
 
@@ -173,7 +245,8 @@ __device__ __forceinline__ void finish_block(const AttnArgs& a, int G, int list,
 // ------------------------------------------------------------------------------------------
 // bf16
 // ------------------------------------------------------------------------------------------
-template <int D, int P, int WAVES, int TPW, bool ROPE>
+// SEL_C > 0: fused selection with SEL_C score keys per thread (select_tiles).
+template <int D, int P, int WAVES, int TPW, bool ROPE, int SEL_C = 0>
 __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a, int G) {
   constexpr int TT = 32;       // tokens per tile
   constexpr int CB = D / 32;   // 32-channel blocks of q K^T
@@ -199,7 +272,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a, int G
   }
 
   TP tp;
-  lookup_tiles<P, TT, TPW>(a, list, b, split, w * TPW, tp);
+  if constexpr (SEL_C > 0) {
+    __shared__ SplitSelectSmem<WAVES * 64> ss;
+    select_tiles<P, TT, TPW, WAVES * 64, SEL_C>(a, list, b, split, w * TPW, tp, ss);
+  } else {
+    lookup_tiles<P, TT, TPW>(a, list, b, split, w * TPW, tp);
+  }
 
   // ---- every K / V load of this wave's tiles ----
   uint4 kraw[TPW][2][CB], vraw[TPW][VB];
@@ -330,7 +408,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a, int G
 // ------------------------------------------------------------------------------------------
 // fp32
 // ------------------------------------------------------------------------------------------
-template <int D, int P, int WAVES, int TPW, bool ROPE>
+template <int D, int P, int WAVES, int TPW, bool ROPE, int SEL_C = 0>
 __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(AttnArgs a, int G) {
   constexpr int TT = 16;       // tokens per tile
   constexpr int KC = D / 4;    // channels per lane in q K^T (4 lane groups)
@@ -358,7 +436,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(AttnArgs a, int G)
     }
   }
   TP tp;
-  lookup_tiles<P, TT, TPW>(a, list, b, split, w * TPW, tp);
+  if constexpr (SEL_C > 0) {
+    __shared__ SplitSelectSmem<WAVES * 64> ss;
+    select_tiles<P, TT, TPW, WAVES * 64, SEL_C>(a, list, b, split, w * TPW, tp, ss);
+  } else {
+    lookup_tiles<P, TT, TPW>(a, list, b, split, w * TPW, tp);
+  }
 
   uint4 kraw[TPW][KL], vraw[TPW][VB];
   int vmask[TPW];
@@ -613,11 +696,9 @@ static hipError_t launch_p(int P, int tiles, const AttnArgs& a, int G, bool rope
   return launch_tiles<T, D, 32>(tiles, a, G, rope, stream);
 }
 
-hipError_t launch_attention(const LaunchKV& kv, const RopeArgs& rope, const void* q,
-                            const int32_t* sel_idx, const int32_t* sel_cnt, int k, float scale,
-                            int pages_per_split, void* out, float* lse, void* ws,
-                            hipStream_t stream) {
-  const int pps = attention_pages_per_split(kv, k, pages_per_split);
+static AttnArgs attn_args(const LaunchKV& kv, const RopeArgs& rope, const void* q,
+                          const int32_t* sel_idx, const int32_t* sel_cnt, int k, float scale,
+                          int pps, void* out, float* lse, void* ws) {
   AttnArgs a;
   a.k_pool = kv.k_pool;
   a.v_pool = kv.v_pool;
@@ -646,6 +727,18 @@ hipError_t launch_attention(const LaunchKV& kv, const RopeArgs& rope, const void
   }
   a.out = out;
   a.lse = lse;
+  a.scores = nullptr;
+  a.sel_out = nullptr;
+  a.cnt_out = nullptr;
+  return a;
+}
+
+hipError_t launch_attention(const LaunchKV& kv, const RopeArgs& rope, const void* q,
+                            const int32_t* sel_idx, const int32_t* sel_cnt, int k, float scale,
+                            int pages_per_split, void* out, float* lse, void* ws,
+                            hipStream_t stream) {
+  const int pps = attention_pages_per_split(kv, k, pages_per_split);
+  const AttnArgs a = attn_args(kv, rope, q, sel_idx, sel_cnt, k, scale, pps, out, lse, ws);
   const int tiles = tiles_for(kv, pps);
   const bool r = rope.page_row != nullptr;
   if (kv.dtype == 0) {
@@ -654,6 +747,95 @@ hipError_t launch_attention(const LaunchKV& kv, const RopeArgs& rope, const void
   }
   if (kv.D == 64) return launch_p<bf16_t, 64>(kv.P, tiles, a, kv.G, r, stream);
   return launch_p<bf16_t, 128>(kv.P, tiles, a, kv.G, r, stream);
+}
+
+// ------------------------------------------------------------------------------------------
+// kvsel_select_attend: scores (score kernel), then the attention launch with the selection
+// fused in (select_tiles), then the merge. The fused launch uses the default split of
+// FUSED_PPS pages, whose block shape depends only on the dtype and page size:
+//   bf16, P 32: 4 waves x 1 tile   bf16, P 16: 2 waves x 1 tile
+//   fp32, P 32: 4 waves x 2 tiles  fp32, P 16: 4 waves x 1 tile
+// Other cases (a rotary gather, a table too wide for the register-resident select, a k that
+// needs larger splits) run the two separate calls' launches instead.
+// ------------------------------------------------------------------------------------------
+constexpr int FUSED_PPS = 4;
+
+template <typename T, int P>
+struct FusedShape {
+  static constexpr int WAVES = (sizeof(T) == 2 && P == 16) ? 2 : 4;
+  static constexpr int TPW = (sizeof(T) == 4 && P == 32) ? 2 : 1;
+};
+
+static int fused_keys_per_thread(const LaunchKV& kv) {
+  const int nt = (kv.dtype == 1 && kv.P == 16) ? 128 : 256;
+  const int c = (kv.maxp + nt - 1) / nt;
+  return c <= 1 ? 1 : c <= 4 ? 4 : c <= 16 ? 16 : c <= 32 ? 32 : 0;
+}
+
+bool select_attend_fused(const LaunchKV& kv, const RopeArgs& rope, int k) {
+  return rope.page_row == nullptr && fused_keys_per_thread(kv) > 0 &&
+         attention_pages_per_split(kv, k, 0) == FUSED_PPS;
+}
+
+template <typename T, int D, int P, int C>
+static void launch_fused_c(const AttnArgs& a, int G, hipStream_t stream) {
+  using S = FusedShape<T, P>;
+  const dim3 grid(a.Hkv, a.nlists / a.Hkv, a.nsplit);
+  const dim3 block(S::WAVES * 64);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, P, S::WAVES, S::TPW, false, C>), grid, block, 0, stream, a, G);
+  else
+    hipLaunchKernelGGL((attn_f32_kernel<D, P, S::WAVES, S::TPW, false, C>), grid, block, 0, stream, a, G);
+}
+
+template <typename T, int D, int P>
+static hipError_t launch_fused(int c, const AttnArgs& a, int G, hipStream_t stream) {
+  switch (c) {
+    case 1: launch_fused_c<T, D, P, 1>(a, G, stream); break;
+    case 4: launch_fused_c<T, D, P, 4>(a, G, stream); break;
+    case 16: launch_fused_c<T, D, P, 16>(a, G, stream); break;
+    default: launch_fused_c<T, D, P, 32>(a, G, stream); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(G, a.Hkv, a.nlists / a.Hkv), dim3(D), 0, stream,
+                     a, G);
+  return hipGetLastError();
+}
+
+size_t select_attend_workspace(const LaunchKV& kv, int k) {
+  return align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float)) + attention_workspace(kv, k, 0);
+}
+
+hipError_t launch_select_attend(const LaunchKV& kv, const RopeArgs& rope, void* summ,
+                                const void* q, int k, int flags, float scale, int32_t* sel_idx,
+                                int32_t* sel_cnt, void* out, float* lse, void* ws,
+                                hipStream_t stream) {
+  float* scores = (float*)ws;
+  void* attn_ws = (char*)ws + align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float));
+  if (!select_attend_fused(kv, rope, k)) {
+    hipError_t e = launch_score_topk(kv, rope, summ, q, k, flags, sel_idx, sel_cnt, scores, false,
+                                     ReuseArgs{}, stream);
+    if (e != hipSuccess) return e;
+    return launch_attention(kv, rope, q, sel_idx, sel_cnt, k, scale, 0, out, lse, attn_ws, stream);
+  }
+  hipError_t e = launch_scores(kv, rope, summ, q, flags, scores, stream);
+  if (e != hipSuccess) return e;
+  AttnArgs a = attn_args(kv, rope, q, nullptr, nullptr, k, scale, FUSED_PPS, out, lse, attn_ws);
+  a.scores = scores;
+  a.sel_out = sel_idx;
+  a.cnt_out = sel_cnt;
+  const int c = fused_keys_per_thread(kv);
+  if (kv.dtype == 0) {
+    if (kv.D == 64) return kv.P == 16 ? launch_fused<float, 64, 16>(c, a, kv.G, stream)
+                                      : launch_fused<float, 64, 32>(c, a, kv.G, stream);
+    return kv.P == 16 ? launch_fused<float, 128, 16>(c, a, kv.G, stream)
+                      : launch_fused<float, 128, 32>(c, a, kv.G, stream);
+  }
+  if (kv.D == 64) return kv.P == 16 ? launch_fused<bf16_t, 64, 16>(c, a, kv.G, stream)
+                                    : launch_fused<bf16_t, 64, 32>(c, a, kv.G, stream);
+  return kv.P == 16 ? launch_fused<bf16_t, 128, 16>(c, a, kv.G, stream)
+                    : launch_fused<bf16_t, 128, 32>(c, a, kv.G, stream);
 }
 
 }  // namespace kvsel

@@ -117,6 +117,7 @@ size_t kvsel_workspace_bytes(const kvsel_paged_kv* kv, int32_t k, int32_t op,
   if (k < 1 || flatten(kv, 0, &f) != KVSEL_OK) return 0;
   if (op == KVSEL_OP_SCORE_TOPK) return score_workspace(f, true);
   if (op == KVSEL_OP_ATTENTION) return attention_workspace(f, k, pages_per_split);
+  if (op == KVSEL_OP_SELECT_ATTEND) return select_attend_workspace(f, k);
   return 0;
 }
 
@@ -187,6 +188,24 @@ kvsel_status kvsel_sparse_decode_attn(const kvsel_paged_kv* kv, const kvsel_rope
   if ((st = check_device()) != KVSEL_OK) return st;
   return launch_status(launch_attention(f, r, q, sel_idx, sel_cnt, k, scale, pages_per_split, out,
                                         lse, ws, (hipStream_t)stream));
+}
+
+kvsel_status kvsel_select_attend(const kvsel_paged_kv* kv, const kvsel_rope* rope, void* summ,
+                                 const void* q, int32_t k, int32_t flags, float scale,
+                                 int32_t* sel_idx, int32_t* sel_cnt, void* out, float* lse,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  LaunchKV f;
+  RopeArgs r;
+  kvsel_status st = flatten(kv, 3, &f);
+  if (st != KVSEL_OK) return st;
+  if (!summ || !q || !sel_idx || !sel_cnt || !out || k < 1) return KVSEL_ERR_INVALID_ARGUMENT;
+  if (flags & ~KVSEL_SCORE_REFRESH_TAIL) return KVSEL_ERR_INVALID_ARGUMENT;
+  if ((st = flatten_rope(rope, &r)) != KVSEL_OK) return st;
+  if (attention_pages_per_split(f, k, 0) <= 0) return KVSEL_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < select_attend_workspace(f, k)) return KVSEL_ERR_WORKSPACE;
+  if ((st = check_device()) != KVSEL_OK) return st;
+  return launch_status(launch_select_attend(f, r, summ, q, k, flags, scale, sel_idx, sel_cnt, out,
+                                            lse, ws, (hipStream_t)stream));
 }
 
 kvsel_status kvsel_rope_table(double theta, int32_t head_dim, int32_t first_position,

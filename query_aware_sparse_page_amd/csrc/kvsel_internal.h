@@ -54,6 +54,19 @@ hipError_t launch_score_topk(const LaunchKV& kv, const RopeArgs& rope, void* sum
                              int k, int flags, int32_t* sel_idx, int32_t* sel_cnt, float* scores,
                              bool scores_requested, const ReuseArgs& reuse, hipStream_t stream);
 
+// Scores only (score kernel, with the optional tail refresh), into scores [B][Hkv][maxp].
+hipError_t launch_scores(const LaunchKV& kv, const RopeArgs& rope, void* summ, const void* q,
+                         int flags, float* scores, hipStream_t stream);
+
+// Selection + attention in one call: scores, then the attention launch with the selection fused
+// in (when select_attend_fused), then the merge. Workspace: select_attend_workspace bytes.
+bool select_attend_fused(const LaunchKV& kv, const RopeArgs& rope, int k);
+size_t select_attend_workspace(const LaunchKV& kv, int k);
+hipError_t launch_select_attend(const LaunchKV& kv, const RopeArgs& rope, void* summ,
+                                const void* q, int k, int flags, float scale, int32_t* sel_idx,
+                                int32_t* sel_cnt, void* out, float* lse, void* ws,
+                                hipStream_t stream);
+
 // Workspace of the attention for a given split size (bytes).
 size_t attention_workspace(const LaunchKV& kv, int k, int pages_per_split);
 int attention_pages_per_split(const LaunchKV& kv, int k, int requested);

@@ -20,6 +20,7 @@
 // invalidates the XCD's L2 and measured slower than the second launch.
 #include "kvsel_device.h"
 #include "kvsel_internal.h"
+#include "kvsel_topk.h"
 
 namespace kvsel {
 
@@ -35,6 +36,7 @@ struct SelectArgs {
   const int32_t* page_table;
   const int32_t* seq_lens;
   int Hkv, P, maxp, Npp, k, nlists, nchunks, refresh_tail, write_scores;
+  int scores_only;  // launch the score kernel alone (the fused selection + attention call)
   RopeArgs rope;
   float* scores;
   int32_t* sel_idx;
@@ -42,40 +44,11 @@ struct SelectArgs {
   ReuseArgs reuse;
 };
 
+// Radix-select state plus an LDS copy of the keys (block_topk, which reads scores from memory).
 template <int NT>
-struct TopkSmem {
-  static constexpr int NW = NT / 64;
-  static constexpr int HC = NW < 4 ? NW : 4;  // histogram copies: wave w counts into copy w % HC
+struct TopkSmem : RadixSmem<NT> {
   uint32_t keys[SEL_LDS_KEYS];
-  // three rotating sets of HC 256-bin histograms, as 64 uint4 (lane l reads bins 4l .. 4l+3)
-  uint4 hist[3][HC][64];
-  uint32_t wave_a[NW], wave_b[NW];      // scan totals
-  uint32_t wave_min[NW], wave_max[NW];  // key range (own slots: read with no barrier after)
 };
-
-// Boundary bin of one radix pass, found by every wave on its own from the histogram totals
-// (t = bins 4l .. 4l+3 of lane l): the bin b with above(b) < need <= above(b) + count(b), where
-// above(b) counts the keys in larger bins. Returns the digit; need becomes need - above(b) and
-// count the bin's total. The result is wave-uniform and identical in every wave.
-__device__ __forceinline__ uint32_t boundary_bin(uint4 t, uint32_t& need, uint32_t& count) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t incl = wave_scan_add(t.x + t.y + t.z + t.w);
-  // keys above bins 4l+3, 4l+2, 4l+1, 4l (higher lanes hold the larger bins)
-  const uint32_t a3 = __builtin_amdgcn_readlane(incl, 63) - incl;
-  const uint32_t a2 = a3 + t.w, a1 = a2 + t.z, a0 = a1 + t.y;
-  const bool h3 = a3 < need && need <= a2;
-  const bool h2 = a2 < need && need <= a1;
-  const bool h1 = a1 < need && need <= a0;
-  const bool h0 = a0 < need && need <= a0 + t.x;
-  const uint32_t sel = h3 ? 3u : h2 ? 2u : h1 ? 1u : 0u;
-  const uint32_t above = h3 ? a3 : h2 ? a2 : h1 ? a1 : a0;
-  const uint32_t cnt = h3 ? t.w : h2 ? t.z : h1 ? t.y : t.x;
-  const int src = __builtin_ctzll(__ballot(h0 || h1 || h2 || h3));  // exactly one lane
-  const uint32_t packed = __builtin_amdgcn_readlane((4u * lane + sel) | (above << 8), src);
-  count = __builtin_amdgcn_readlane(cnt, src);
-  need -= packed >> 8;
-  return packed & 255u;
-}
 
 // Min / max of the valid rows (1 <= valid) of one (page, KV head) tile of physical page pt,
 // computed by one wave. On return every lane holds lo / hi of its channels [c0, c0 + VEC). The
@@ -125,29 +98,6 @@ __device__ __forceinline__ void tile_minmax(const T* tile, int valid, int P, int
       hi[e] = fmaxf(hi[e], __shfl_xor(hi[e], m));
     }
   }
-}
-
-// Exclusive scan over the block of two counters (wave scans on DPP, one barrier for the wave
-// totals); also returns nothing else: the block totals are not needed.
-template <int NT>
-__device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, uint32_t& a_ex,
-                                                      uint32_t& b_ex, TopkSmem<NT>& sm) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint32_t ia = wave_scan_add(a), ib = wave_scan_add(b);
-  if (lane == 63) {
-    sm.wave_a[w] = ia;
-    sm.wave_b[w] = ib;
-  }
-  __syncthreads();
-  uint32_t ba = 0, bb = 0;
-#pragma unroll
-  for (int v = 0; v < NT / 64; ++v)
-    if (v < w) {
-      ba += sm.wave_a[v];
-      bb += sm.wave_b[v];
-    }
-  a_ex = ba + ia - a;
-  b_ex = bb + ib - b;
 }
 
 // Exact top-k of the N scores of one list, by the whole block; writes out[0..k) ascending
@@ -367,106 +317,17 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   if (active && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
 }
 
-// The same selection with the keys in registers: thread t holds the keys of indices
-// t*C .. t*C + C - 1 (indices >= N are ignored). A radix pass is then one predicated LDS atomic
-// per key, one barrier, and the boundary search.
+// block_topk_regs writing the ascending list to out (and used, when non-null), padded with -1.
 template <int NT, int C>
-__device__ void block_topk_regs(const uint32_t (&key)[C], int N, int k, int32_t* __restrict__ out,
-                                int32_t* __restrict__ used, TopkSmem<NT>& sm) {
-  constexpr int NW = NT / 64;
-  constexpr int HC = TopkSmem<NT>::HC;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (N <= k) {
-    for (int i = tid; i < k; i += NT) {
-      const int v = i < N ? i : -1;
-      out[i] = v;
-      if (used) used[i] = v;
-    }
-    return;
-  }
-  const int i0 = tid * C;
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-  for (int u = 0; u < C; ++u) {
-    if (i0 + u < N) {
-      kmin = min(kmin, key[u]);
-      kmax = max(kmax, key[u]);
-    }
-  }
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
-  for (int i = tid; i < HC * 64; i += NT) (&sm.hist[0][0][0])[i] = make_uint4(0, 0, 0, 0);
-  if (lane == 0) {
-    sm.wave_min[w] = kmin;
-    sm.wave_max[w] = kmax;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    kmin = min(kmin, sm.wave_min[v]);
-    kmax = max(kmax, sm.wave_max[v]);
-  }
-  uint32_t prefix = kmax, mask = 0xffffffffu, need = (uint32_t)k;
-  if (kmin != kmax) {
-    const int top_bit = 31 - __clz((int)(kmin ^ kmax));
-    mask = top_bit == 31 ? 0u : ~((2u << top_bit) - 1u);
-    prefix = kmax & mask;
-    // rotating histogram sets as in block_topk: one barrier per pass
-    for (int top = top_bit, pass = 0; top >= 0; top -= 8, ++pass) {
-      const int cur = pass % 3, nxt = (pass + 1) % 3;
-      const int shift = top >= 7 ? top - 7 : 0;
-      const uint32_t dmask = (2u << (top - shift)) - 1u;
-      for (int i = tid; i < HC * 64; i += NT) (&sm.hist[nxt][0][0])[i] = make_uint4(0, 0, 0, 0);
-      uint32_t* h = (uint32_t*)&sm.hist[cur][w % HC][0];
-#pragma unroll
-      for (int u = 0; u < C; ++u) {
-        if (i0 + u < N && (key[u] & mask) == prefix) atomicAdd(&h[(key[u] >> shift) & dmask], 1u);
-      }
-      __syncthreads();
-      uint4 t = sm.hist[cur][0][lane];
-#pragma unroll
-      for (int c = 1; c < HC; ++c) {
-        const uint4 x = sm.hist[cur][c][lane];
-        t.x += x.x;
-        t.y += x.y;
-        t.z += x.z;
-        t.w += x.w;
-      }
-      uint32_t count;
-      const uint32_t digit = boundary_bin(t, need, count);
-      prefix |= digit << shift;
-      mask |= dmask << shift;
-      if (count == need) break;  // the whole boundary bucket is taken
-    }
-  }
-  // ---- compaction over the thread's contiguous indices ----
-  uint32_t n_gt = 0, n_eq = 0;
-#pragma unroll
-  for (int u = 0; u < C; ++u) {
-    const uint32_t m = key[u] & mask;
-    const bool ok = i0 + u < N;
-    n_gt += ok && m > prefix;
-    n_eq += ok && m == prefix;
-  }
-  uint32_t gt_ex, eq_ex;
-  block_exclusive_scan2(n_gt, n_eq, gt_ex, eq_ex, sm);
-  uint32_t pos = gt_ex + min(eq_ex, need);
-  uint32_t eq_seen = eq_ex;
-#pragma unroll
-  for (int u = 0; u < C; ++u) {
-    const int i = i0 + u;
-    const uint32_t m = key[u] & mask;
-    if (i < N) {
-      const bool sel = m > prefix || (m == prefix && eq_seen < need);
-      eq_seen += m == prefix;
-      if (sel) {
-        if (pos < (uint32_t)k) {
-          out[pos] = i;
-          if (used) used[pos] = i;
-        }
-        ++pos;
-      }
-    }
+__device__ void topk_to_list(const uint32_t (&key)[C], int N, int k, int32_t* __restrict__ out,
+                             int32_t* __restrict__ used, RadixSmem<NT>& sm) {
+  block_topk_regs<NT, C>(key, N, k, sm, [&](int pos, int i, int) {
+    out[pos] = i;
+    if (used) used[pos] = i;
+  });
+  for (int i = max(N, 0) + threadIdx.x; i < k; i += NT) {
+    out[i] = -1;
+    if (used) used[i] = -1;
   }
 }
 
@@ -545,7 +406,7 @@ __device__ void topk_regs(const SelectArgs& a, int list, int b, int j, TopkSmem<
 #pragma unroll
   for (int u = 0; u < C; ++u) key[u] = score_key(v[u]);
   select_outputs<SEL_THREADS>(a, list, N, corrected, reuse_on, [&](int32_t* out, int32_t* used) {
-    block_topk_regs<SEL_THREADS, C>(key, N, a.k, out, used, sm);
+    topk_to_list<SEL_THREADS, C>(key, N, a.k, out, used, sm);
   });
 }
 
@@ -683,12 +544,12 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
   if (N <= FUSED_THREADS) {
     uint32_t key[1] = {sm.keys[tid]};
     select_outputs<FUSED_THREADS>(a, list, N, corrected, reuse_on, [&](int32_t* out, int32_t* used) {
-      block_topk_regs<FUSED_THREADS, 1>(key, N, a.k, out, used, sm);
+      topk_to_list<FUSED_THREADS, 1>(key, N, a.k, out, used, sm);
     });
   } else {
     uint32_t key[2] = {sm.keys[2 * tid], sm.keys[2 * tid + 1]};
     select_outputs<FUSED_THREADS>(a, list, N, corrected, reuse_on, [&](int32_t* out, int32_t* used) {
-      block_topk_regs<FUSED_THREADS, 2>(key, N, a.k, out, used, sm);
+      topk_to_list<FUSED_THREADS, 2>(key, N, a.k, out, used, sm);
     });
   }
 }
@@ -713,7 +574,7 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t stream) {
   // 8 lists of 1024 pages take 24.7 us in one launch against 10.2 us in two; 128 lists of up
   // to 1024 pages take 15.8 us against 18.6 us).
   if constexpr (G <= 4) {  // larger groups would spill at 1024 threads
-    if (a.nlists >= FUSED_MIN_LISTS && a.maxp <= FUSED_MAX_PAGES) {
+    if (!a.scores_only && a.nlists >= FUSED_MIN_LISTS && a.maxp <= FUSED_MAX_PAGES) {
       hipLaunchKernelGGL((select_fused_kernel<T, D, G>), dim3(a.Hkv, a.nlists / a.Hkv),
                          dim3(FUSED_THREADS), 0, stream, a);
       return hipGetLastError();
@@ -723,6 +584,7 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t stream) {
                      0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.scores_only) return hipSuccess;
   hipLaunchKernelGGL((topk_kernel<T, D, G>), dim3(a.Hkv, a.nlists / a.Hkv), dim3(SEL_THREADS), 0,
                      stream, a);
   return hipGetLastError();
@@ -738,9 +600,18 @@ static hipError_t launch_select_g(int G, const SelectArgs& a, hipStream_t stream
   }
 }
 
-hipError_t launch_score_topk(const LaunchKV& kv, const RopeArgs& rope, void* summ, const void* q,
-                             int k, int flags, int32_t* sel_idx, int32_t* sel_cnt, float* scores,
-                             bool scores_requested, const ReuseArgs& reuse, hipStream_t stream) {
+static hipError_t launch_select(const SelectArgs& a, const LaunchKV& kv, hipStream_t stream) {
+  if (kv.dtype == 0) {
+    if (kv.D == 64) return launch_select_g<float, 64>(kv.G, a, stream);
+    return launch_select_g<float, 128>(kv.G, a, stream);
+  }
+  if (kv.D == 64) return launch_select_g<bf16_t, 64>(kv.G, a, stream);
+  return launch_select_g<bf16_t, 128>(kv.G, a, stream);
+}
+
+static SelectArgs select_args(const LaunchKV& kv, const RopeArgs& rope, void* summ, const void* q,
+                              int k, int flags, int32_t* sel_idx, int32_t* sel_cnt, float* scores,
+                              bool scores_requested, const ReuseArgs& reuse) {
   SelectArgs a;
   a.k_pool = kv.k_pool;
   a.summ = summ;
@@ -761,12 +632,24 @@ hipError_t launch_score_topk(const LaunchKV& kv, const RopeArgs& rope, void* sum
   a.sel_idx = sel_idx;
   a.sel_cnt = sel_cnt;
   a.reuse = reuse;
-  if (kv.dtype == 0) {
-    if (kv.D == 64) return launch_select_g<float, 64>(kv.G, a, stream);
-    return launch_select_g<float, 128>(kv.G, a, stream);
-  }
-  if (kv.D == 64) return launch_select_g<bf16_t, 64>(kv.G, a, stream);
-  return launch_select_g<bf16_t, 128>(kv.G, a, stream);
+  a.scores_only = 0;
+  return a;
+}
+
+hipError_t launch_score_topk(const LaunchKV& kv, const RopeArgs& rope, void* summ, const void* q,
+                             int k, int flags, int32_t* sel_idx, int32_t* sel_cnt, float* scores,
+                             bool scores_requested, const ReuseArgs& reuse, hipStream_t stream) {
+  return launch_select(select_args(kv, rope, summ, q, k, flags, sel_idx, sel_cnt, scores,
+                                   scores_requested, reuse),
+                       kv, stream);
+}
+
+hipError_t launch_scores(const LaunchKV& kv, const RopeArgs& rope, void* summ, const void* q,
+                         int flags, float* scores, hipStream_t stream) {
+  SelectArgs a = select_args(kv, rope, summ, q, 1, flags, nullptr, nullptr, scores, true,
+                             ReuseArgs{});
+  a.scores_only = 1;
+  return launch_select(a, kv, stream);
 }
 
 }  // namespace kvsel

@@ -22,6 +22,7 @@ KVSEL_F32 = 0
 KVSEL_BF16 = 1
 KVSEL_OP_SCORE_TOPK = 1
 KVSEL_OP_ATTENTION = 2
+KVSEL_OP_SELECT_ATTEND = 3
 KVSEL_SCORE_REFRESH_TAIL = 1
 
 c_i32 = ctypes.c_int32
@@ -68,6 +69,9 @@ EXPORTS = {
     "kvsel_sparse_decode_attn": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp,
                                          c_vp, c_vp, c_i32, ctypes.c_float, c_i32, c_vp, c_vp, c_vp,
                                          ctypes.c_size_t, c_vp]),
+    "kvsel_select_attend": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp, c_vp,
+                                    c_i32, c_i32, ctypes.c_float, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                    ctypes.c_size_t, c_vp]),
     "kvsel_rope_table": (c_i32, [ctypes.c_double, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "kvsel_rope_shift": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp, c_vp]),
 }
@@ -311,6 +315,38 @@ def sparse_decode_attn(kv: PagedKV, q: torch.Tensor, sel_idx: torch.Tensor, sel_
                                           _ptr(sel_cnt), k, scale, pages_per_split, _ptr(out),
                                           _ptr(lse), _ptr(ws), ws_bytes, _stream(dev)))
     return out, lse
+
+
+
+def select_attend(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, *,
+                  refresh_tail: bool = False, rope: Optional[Rope] = None,
+                  scale: Optional[float] = None, sel_idx: Optional[torch.Tensor] = None,
+                  sel_cnt: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                  workspace: Optional[torch.Tensor] = None):
+    """score_topk + sparse_decode_attn (default split) in one call, with the top-k fused into the
+    attention launch. Returns (sel_idx, sel_cnt, out, lse)."""
+    d = kv.desc()
+    B, Hkv = kv.batch, kv.num_kv_heads
+    dev = kv.device
+    _dev(summ, "summ", kv.k_pool.dtype)
+    _dev(q, "q", kv.k_pool.dtype)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+    if sel_cnt is None:
+        sel_cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    if scale is None:
+        scale = default_scale(kv.head_dim)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    ws, ws_bytes = _workspace(kv, k, KVSEL_OP_SELECT_ATTEND, 0, workspace)
+    flags = KVSEL_SCORE_REFRESH_TAIL if refresh_tail else 0
+    _check(lib().kvsel_select_attend(ctypes.byref(d), _rope_ptr(rope), _ptr(summ), _ptr(q), k, flags,
+                                     scale, _ptr(sel_idx), _ptr(sel_cnt), _ptr(out), _ptr(lse),
+                                     _ptr(ws), ws_bytes, _stream(dev)))
+    return sel_idx, sel_cnt, out, lse
 
 
 def rope_table(theta: float, head_dim: int, first_position: int, n_rows: int,
