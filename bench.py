@@ -5,14 +5,19 @@ sequence's tail page, score every page and select the top-k per (sequence, KV he
 the sparse paged decode attention (split-K + merge) over the selected pages -- one
 kvsel_select_attend call (scores, then the attention launch with the top-k fused in, then the
 merge); the same step as two calls (kvsel_score_topk + kvsel_sparse_decode_attn) is reported
-beside it. Inputs are resident in HBM before the timed region. The step is timed over R copies of the cache at distinct HBM
-addresses, used in turn like the layers of a model, so the Infinity Cache cannot serve a step
-from the previous visit; the R steps are captured once in a HIP graph and replayed.
+beside it. Inputs are resident in HBM before the timed region.
+
+The step is timed over R copies of the cache at distinct HBM addresses (default 48), used in
+turn like the layers of a model: the selected K/V of all copies (48 x 8 MiB at 32K) exceeds the
+256 MB Infinity Cache, so a copy's pages have been evicted by the time it is visited again (the
+situation of a real decode, where every layer runs between two visits of one layer's cache).
+The R steps are captured once in a HIP graph and replayed.
 
 Prints ONE JSON line: µs/step of the whole path (the headline value), the roofline of the
-dominant kernel (the attention split kernel; its duration measured with HIP events on the
-launch stream), the 128K-context secondary numbers, and the CPU oracle timed on a bounded sample
-of the same workload as a baseline.
+dominant kernel (the attention call: its time per call from a graph of back-to-back calls between
+two HIP events on the replay stream), a plain gather of the same K/V tiles for context, the
+128K-context secondary numbers, and the CPU oracle timed on a bounded sample of the same workload
+as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps 400] [--warmup 40] [--workload llama8b_32k]
 """
@@ -65,6 +70,10 @@ class Layer:
         K.sparse_decode_attn(self.kv, self.q, self.sel, self.cnt, self.k, out=self.out,
                              lse=self.lse, pages_per_split=self.pps, workspace=self.ws_attn)
 
+    def probe(self):
+        """Plain gather of the K/V tiles the selection names (measurement context)."""
+        K.gather_probe(self.probe_addr, self.probe_chunk, self.probe_sink)
+
     def step(self):
         """The decode step as one kvsel_select_attend call (top-k fused into the attention)."""
         K.select_attend(self.kv, self.summ, self.q, self.k, refresh_tail=True, sel_idx=self.sel,
@@ -115,31 +124,36 @@ def time_graph(layers, steps, warmup, step=Layer.step):
     return e0.elapsed_time(e1) * 1000.0 / n, n
 
 
-def _event_pairs(layers, fn, launches):
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
-    torch.cuda._sleep(int(2.0e8))  # ~0.1 s of GPU spin: the host enqueues everything meanwhile
-    for i in range(launches):
-        starts[i].record()
-        if fn is not None:
-            fn(layers[i % len(layers)])
-        ends[i].record()
-    torch.cuda.synchronize()
-    return np.array([a.elapsed_time(b) * 1000.0 for a, b in zip(starts, ends)])
-
-
-def time_kernel(layers, fn, launches):
-    """Average GPU duration (µs) of the launches of ``fn(layer)``, each bracketed by HIP events
-    recorded on the launch stream. A GPU-side spin queued first keeps the device busy while the
-    host enqueues, so each event pair brackets GPU work only; the average duration of an empty
-    event pair, measured the same way, is subtracted."""
+def time_calls(layers, fn, launches):
+    """Average GPU time (µs) of one ``fn(layer)`` call: ``launches`` calls, rotating over the
+    layers, are captured in a HIP graph and replayed back to back between two HIP events on the
+    replay stream; the time per call includes the call's own launch gaps, so it equals the sum
+    of its kernels' durations in a rocprofv3 kernel trace of the same run."""
     for lay in layers:
         lay.select()
     torch.cuda.synchronize()
-    d = _event_pairs(layers, fn, launches)
-    empty = _event_pairs(layers, None, launches)
-    ov = float(empty.mean())
-    return float(d.mean()) - ov, float(np.median(d)) - ov, ov
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(len(layers)):  # eager warm-up before capture
+            fn(layers[i])
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(launches):
+            fn(layers[i % len(layers)])
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / (reps * launches)
 
 
 def attention_bytes(w, lay):
@@ -154,14 +168,21 @@ def measure(name, dev, steps, warmup, n_layers):
     layers = make_layers(w, dev, n_layers)
     us_step, n = time_graph(layers, steps, warmup)
     us_two, _ = time_graph(layers, steps, warmup, Layer.step_two_calls)
-    attn_mean, attn_med, ev_ov = time_kernel(layers, Layer.attend, max(64, min(steps, 512)))
-    sel_mean, _, _ = time_kernel(layers, Layer.select, max(64, min(steps, 512)))
-    abytes = attention_bytes(w, layers[0])
+    n_calls = max(len(layers), min(steps, 512) // len(layers) * len(layers))
+    attn_mean = time_calls(layers, Layer.attend, n_calls)
+    sel_mean = time_calls(layers, Layer.select, n_calls)
     esize = 4 if w.dtype == "f32" else 2
+    for lay in layers:  # the tiles each layer's selection names, at that layer's addresses
+        lay.probe_addr = K.tile_addresses(lay.kv, lay.sel, lay.cnt, w.page_table)
+        lay.probe_chunk = w.P * w.D * esize
+        lay.probe_sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    probe_us = time_calls(layers, Layer.probe, n_calls)
+    probe_bytes = int(layers[0].probe_addr.numel()) * w.P * w.D * esize
+    abytes = attention_bytes(w, layers[0])
     sbytes = summary_bytes(w.seq_lens.tolist(), w.Hkv, w.P, w.D, esize)
     return dict(w=w, layers=layers, us_step=us_step, us_two_calls=us_two, steps=n, attn_us=attn_mean,
-                attn_us_median=attn_med, select_us=sel_mean, attn_bytes=abytes,
-                summary_bytes=sbytes, event_overhead_us=ev_ov)
+                select_us=sel_mean, attn_bytes=abytes, summary_bytes=sbytes, probe_us=probe_us,
+                probe_bytes=probe_bytes, calls_timed=n_calls)
 
 
 def recorded_traffic():
@@ -190,8 +211,7 @@ def sweep_pps(name, dev, n_layers, launches=256):
         for lay in layers:
             lay.pps = pps
             lay.ws_attn = K.new_workspace(lay.kv, w.k, K.KVSEL_OP_ATTENTION, pps)
-        t, med, _ = time_kernel(layers, Layer.attend, launches)
-        out[pps] = round(t, 3)
+        out[pps] = round(time_calls(layers, Layer.attend, launches), 3)
     print(json.dumps({"sweep_pps": name, "attn_us_by_pages_per_split": out}), flush=True)
 
 
@@ -254,7 +274,9 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="llama8b_32k")
-    ap.add_argument("--layers", type=int, default=8, help="cache copies rotated like layers")
+    ap.add_argument("--layers", type=int, default=48,
+                    help="cache copies rotated like layers (48 x 8 MiB of selected K/V exceeds the "
+                         "256 MB Infinity Cache, so every call reads HBM)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep-pps", action="store_true",
@@ -275,7 +297,7 @@ def main():
         return
     if args.sweep_pps:
         for name in (args.workload, "qwen4b_128k", "ragged_batch"):
-            sweep_pps(name, dev, 4)
+            sweep_pps(name, dev, args.layers // 2)
             torch.cuda.empty_cache()
         return
 
@@ -312,8 +334,10 @@ def main():
             "traffic": recorded_traffic() if w.name == "llama8b_32k" else None,
             "algorithmic_bytes": m["attn_bytes"],
             "avg_us": round(m["attn_us"], 3),
-            "median_us": round(m["attn_us_median"], 3),
-            "event_pair_overhead_us": round(m["event_overhead_us"], 3),
+            "calls_timed": m["calls_timed"],
+            # the same K/V tiles moved by a plain gather (no index chain, math or merge)
+            "gather_probe": {"bytes": m["probe_bytes"], "avg_us": round(m["probe_us"], 3),
+                             "GBps": round(m["probe_bytes"] / (m["probe_us"] * 1e-6) / 1e9, 1)},
         },
         "select_us": round(m["select_us"], 3),
         "two_call_us_per_step": round(m["us_two_calls"], 3),

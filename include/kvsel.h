@@ -221,6 +221,19 @@ kvsel_status kvsel_rope_table(double theta, int32_t head_dim, int32_t first_posi
 kvsel_status kvsel_rope_shift(const kvsel_paged_kv* kv, const kvsel_rope* rope, void* k_out,
                               void* stream);
 
+/* ---- measurement ---- */
+
+/* Read-bandwidth probe: gathers n_chunks chunks of chunk_bytes bytes (1, 2, 4, 8, 16 or 32 KiB;
+ * each chunk 16-byte aligned) whose device addresses are in chunk_addr (device array, uint64
+ * [n_chunks]), one wave per chunk with every load issued before the first use, and folds the
+ * data into *sink (device, one word; written only in the practically impossible case that the
+ * fold equals a fixed constant). Given the K and V tiles an attention call reads, it times the
+ * same bytes moved with no index chain, arithmetic or merge: context for the attention
+ * kernel's bandwidth, not part of the decode path.
+ * [KV wiki] (decode speed is set by memory bandwidth). */
+kvsel_status kvsel_gather_probe(const uint64_t* chunk_addr, int32_t n_chunks, int32_t chunk_bytes,
+                                uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

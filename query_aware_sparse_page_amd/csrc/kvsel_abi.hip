@@ -208,6 +208,16 @@ kvsel_status kvsel_select_attend(const kvsel_paged_kv* kv, const kvsel_rope* rop
                                             lse, ws, (hipStream_t)stream));
 }
 
+kvsel_status kvsel_gather_probe(const uint64_t* chunk_addr, int32_t n_chunks, int32_t chunk_bytes,
+                                uint32_t* sink, void* stream) {
+  if (!chunk_addr || !sink || n_chunks < 1 || n_chunks > (1 << 26)) return KVSEL_ERR_INVALID_ARGUMENT;
+  const int kib = chunk_bytes / 1024;
+  if (chunk_bytes % 1024 || kib < 1 || kib > 32 || (kib & (kib - 1))) return KVSEL_ERR_INVALID_ARGUMENT;
+  kvsel_status st = check_device();
+  if (st != KVSEL_OK) return st;
+  return launch_status(launch_gather_probe(chunk_addr, n_chunks, kib, sink, (hipStream_t)stream));
+}
+
 kvsel_status kvsel_rope_table(double theta, int32_t head_dim, int32_t first_position,
                               int32_t n_rows, float* cos_t, float* sin_t, void* stream) {
   if (!cos_t || !sin_t || n_rows < 1 || head_dim < 2 || head_dim > 128 || (head_dim & 1) ||

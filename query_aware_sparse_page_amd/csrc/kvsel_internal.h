@@ -76,6 +76,10 @@ hipError_t launch_attention(const LaunchKV& kv, const RopeArgs& rope, const void
                             int pages_per_split, void* out, float* lse, void* ws,
                             hipStream_t stream);
 
+// Gather probe: n_chunks chunks of chunk_kib KiB (1..32, a power of two) at device addresses.
+hipError_t launch_gather_probe(const uint64_t* addr, int n_chunks, int chunk_kib, uint32_t* sink,
+                               hipStream_t stream);
+
 hipError_t launch_rope_table(double theta, int D, int first_position, int n_rows, float* cos,
                              float* sin, hipStream_t stream);
 

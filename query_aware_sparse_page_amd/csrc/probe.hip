@@ -1,0 +1,42 @@
+// Read-bandwidth probe: the plain gather of a list of chunks, for measurement context.
+//
+// One wave per chunk; each lane issues all its 16-byte loads of the chunk before using any of
+// them, then the data is xor-folded into one word so the loads cannot be dropped. Fed with the
+// K and V tiles a sparse attention call reads, it gives the time of moving exactly those bytes
+// with no index chain, no arithmetic and no merge: the floor the attention kernel is compared
+// against.
+#include "kvsel_internal.h"
+
+namespace kvsel {
+
+template <int LPL>  // 16-byte loads per lane: chunk = LPL KiB
+__global__ __launch_bounds__(256) void gather_probe_kernel(const uint64_t* __restrict__ addr,
+                                                           int n_chunks, uint32_t* sink) {
+  const int lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (c >= n_chunks) return;  // whole waves only
+  const uint4* p = reinterpret_cast<const uint4*>(addr[c]) + lane;
+  uint4 v[LPL];
+#pragma unroll
+  for (int i = 0; i < LPL; ++i) v[i] = p[i * 64];
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i < LPL; ++i) x ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  if (x == 0x9e3779b9u) sink[0] = x;  // practically never: keeps the loads live
+}
+
+hipError_t launch_gather_probe(const uint64_t* addr, int n_chunks, int chunk_kib, uint32_t* sink,
+                               hipStream_t stream) {
+  const dim3 grid((unsigned)((n_chunks + 3) / 4)), block(256);
+  switch (chunk_kib) {
+    case 1: hipLaunchKernelGGL(gather_probe_kernel<1>, grid, block, 0, stream, addr, n_chunks, sink); break;
+    case 2: hipLaunchKernelGGL(gather_probe_kernel<2>, grid, block, 0, stream, addr, n_chunks, sink); break;
+    case 4: hipLaunchKernelGGL(gather_probe_kernel<4>, grid, block, 0, stream, addr, n_chunks, sink); break;
+    case 8: hipLaunchKernelGGL(gather_probe_kernel<8>, grid, block, 0, stream, addr, n_chunks, sink); break;
+    case 16: hipLaunchKernelGGL(gather_probe_kernel<16>, grid, block, 0, stream, addr, n_chunks, sink); break;
+    default: hipLaunchKernelGGL(gather_probe_kernel<32>, grid, block, 0, stream, addr, n_chunks, sink); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

@@ -72,6 +72,7 @@ EXPORTS = {
     "kvsel_select_attend": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp, c_vp,
                                     c_i32, c_i32, ctypes.c_float, c_vp, c_vp, c_vp, c_vp, c_vp,
                                     ctypes.c_size_t, c_vp]),
+    "kvsel_gather_probe": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp]),
     "kvsel_rope_table": (c_i32, [ctypes.c_double, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "kvsel_rope_shift": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp, c_vp]),
 }
@@ -368,3 +369,35 @@ def rope_shift(kv: PagedKV, rope: Rope, out: Optional[torch.Tensor] = None) -> t
     _check(lib().kvsel_rope_shift(ctypes.byref(d), ctypes.byref(rope.desc()), _ptr(out),
                                   _stream(kv.device)))
     return out
+
+
+def gather_probe(chunk_addr: torch.Tensor, chunk_bytes: int, sink: Optional[torch.Tensor] = None):
+    """Read-bandwidth probe over device chunks (``chunk_addr``: int64 device addresses)."""
+    _dev(chunk_addr, "chunk_addr", torch.int64)
+    dev = chunk_addr.device
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    _check(lib().kvsel_gather_probe(_ptr(chunk_addr), int(chunk_addr.numel()), int(chunk_bytes),
+                                    _ptr(sink), _stream(dev)))
+    return sink
+
+
+def tile_addresses(kv: PagedKV, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
+                   page_table: torch.Tensor) -> torch.Tensor:
+    """Device addresses of the K and V (page, KV head) tiles the selection names (host-side
+    bookkeeping for gather_probe; ``page_table`` on the host)."""
+    sel = sel_idx.cpu()
+    cnt = sel_cnt.cpu()
+    esize = kv.k_pool.element_size()
+    tile = kv.k_pool.shape[2] * kv.head_dim * esize  # P * D elements
+    kb, vb = kv.k_pool.data_ptr(), kv.v_pool.data_ptr()
+    addrs = []
+    for b in range(sel.shape[0]):
+        for j in range(sel.shape[1]):
+            for n in sel[b, j, :int(cnt[b, j])].tolist():
+                p = int(page_table[b, n])
+                off = (p * kv.num_kv_heads + j) * tile
+                addrs.append(kb + off)
+                addrs.append(vb + off)
+    return torch.tensor(addrs, dtype=torch.int64).to(kv.device)
+

@@ -123,3 +123,13 @@ def test_call_argument_validation(K):
     assert lib.kvsel_rope_shift(ctypes.byref(d), None, p, None) == 1
     assert lib.kvsel_rope_table(500000.0, 127, 0, 4, p, p, None) == 1
     assert lib.kvsel_rope_table(-1.0, 128, 0, 4, p, p, None) == 1
+
+
+def test_gather_probe_validation(K):
+    lib = K.lib()
+    p = ctypes.c_void_p(0x5000)
+    assert lib.kvsel_gather_probe(None, 4, 8192, p, None) == 1
+    assert lib.kvsel_gather_probe(p, 4, 8192, None, None) == 1
+    assert lib.kvsel_gather_probe(p, 0, 8192, p, None) == 1
+    for bad in (0, 512, 3072, 65536, 8193):
+        assert lib.kvsel_gather_probe(p, 4, bad, p, None) == 1
