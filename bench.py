@@ -256,7 +256,9 @@ def counter_pass(name, dev, n_layers):
     layers = make_layers(w, dev, n_layers)
     for _ in range(2):
         for lay in layers:
-            lay.step()
+            lay.step()  # kvsel_select_attend
+        for lay in layers:
+            lay.step_two_calls()  # kvsel_score_topk + kvsel_sparse_decode_attn
     torch.cuda.synchronize()
     src = torch.empty(64 << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
@@ -264,7 +266,7 @@ def counter_pass(name, dev, n_layers):
     for _ in range(4):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"counter_pass": name, "layers": n_layers, "steps": 2 * n_layers,
+    print(json.dumps({"counter_pass": name, "layers": n_layers, "steps_per_form": 2 * n_layers,
                       "calibration_copy_bytes": 64 << 20}), flush=True)
 
 
