@@ -215,6 +215,84 @@ def sweep_pps(name, dev, n_layers, launches=256):
     print(json.dumps({"sweep_pps": name, "attn_us_by_pages_per_split": out}), flush=True)
 
 
+def speculative(dev, reps=3):
+    """The speculative workload: a 32K cache built from eight rotary-encoded 4096-token blocks,
+    re-positioned on the fly (fused rotary gather), then 64 decode steps with AR(1) queries where
+    step t attends over step t-1's pages unless the group-mean query similarity is below tau.
+    The 64 steps (score_topk with reuse + attention over the used pages) are one HIP graph;
+    reports µs per step (warm: the same cache every step) and the quality statistics."""
+    w = W.speculative_rope()
+    bt = w.extra["block_tokens"]
+    blocks = bt // w.P
+    npg = w.num_phys_pages
+    cos, sin = K.rope_table(w.extra["theta"], w.D, 0, 8 * bt, dev)
+    kv_raw = K.PagedKV(w.k_pool.to(dev), K.device_v_layout(w.v_pool.to(dev)),
+                       w.page_table.to(dev), w.seq_lens.to(dev), w.Hq)
+    enc_row = torch.from_numpy(((np.arange(npg) % blocks) * w.P).astype(np.int32)).to(dev)
+    shift_row = torch.from_numpy(((np.arange(npg) // blocks) * bt).astype(np.int32)).to(dev)
+    enc = K.rope_shift(kv_raw, K.Rope(cos, sin, enc_row, 1))  # the precomputed blocks
+    kv = K.PagedKV(enc, kv_raw.v_pool, kv_raw.page_table, kv_raw.seq_lens, w.Hq)
+    shift = K.Rope(cos, sin, shift_row, 0)
+    summ = K.build_summaries(kv, rope=shift)
+    qs = w.extra["q_steps"].to(dev)
+    T, tau = qs.shape[0], w.extra["tau"]
+    B, Hkv, k = w.B, w.Hkv, w.k
+    sel = torch.zeros((T, B, Hkv, k), dtype=torch.int32, device=dev)
+    cnt = torch.zeros((T, B, Hkv), dtype=torch.int32, device=dev)
+    out = torch.empty((T,) + tuple(w.q.shape), dtype=qs.dtype, device=dev)
+    lse = torch.empty((T, B, w.Hq), dtype=torch.float32, device=dev)
+    ws_s = K.new_workspace(kv, k, K.KVSEL_OP_SCORE_TOPK)
+    ws_a = K.new_workspace(kv, k, K.KVSEL_OP_ATTENTION)
+    res = []
+
+    def loop():
+        res.clear()
+        for t in range(T):
+            r = K.score_topk(kv, summ, qs[t], k, sel_idx=sel[t], sel_cnt=cnt[t], workspace=ws_s,
+                             reuse=K.Reuse(qs[t - 1] if t else qs[t], sel[t - 1] if t else sel[t],
+                                           cnt[t - 1] if t else cnt[t], tau, first_step=(t == 0)))
+            res.append(r)
+            K.sparse_decode_attn(kv, qs[t], r[2], r[3], k, rope=shift, out=out[t], lse=lse[t],
+                                 workspace=ws_a)
+
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        loop()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        loop()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / (reps * T)
+    corrected = torch.stack([r[4] for r in res]).cpu().numpy()   # [T][B][Hkv]
+    used = torch.stack([r[2] for r in res]).cpu().numpy()
+    ucnt = torch.stack([r[3] for r in res]).cpu().numpy()
+    fresh, fcnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    overlap = []
+    for t in range(1, T):
+        for b in range(B):
+            for j in range(Hkv):
+                u = set(used[t, b, j, :ucnt[t, b, j]].tolist())
+                f = set(fresh[t, b, j, :fcnt[t, b, j]].tolist())
+                overlap.append(len(u & f) / k)
+    return {"us_per_step": round(us, 3), "steps": T, "tau": tau, "rho": w.extra["rho"],
+            "correction_rate": round(float(corrected[1:].mean()), 4),
+            "corrections": int(corrected[1:].sum()), "decisions": int(corrected[1:].size),
+            "mean_overlap_used_fresh": round(float(np.mean(overlap)), 4),
+            "step": "score + top-k + reuse decision, then attention over the used pages with "
+                    "the rotary re-positioning fused into the key gather (warm: one cache)"}
+
+
 def cpu_baseline(w, lay, budget_s=12.0):
     """The oracle's decode step (tail summary + scores + top-k + attention) on the host, for a
     bounded number of repetitions of the same workload; also checks the GPU's step output."""
@@ -243,7 +321,17 @@ def cpu_baseline(w, lay, budget_s=12.0):
     ok_sel = bool(np.array_equal(lay.sel.cpu().numpy(), sel) and
                   np.array_equal(lay.cnt.cpu().numpy(), cnt))
     err = float(np.abs(lay.out.float().cpu().numpy() - out).max())
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    host = dict(affinity=len(os.sched_getaffinity(0)), cpu_count=os.cpu_count(), model=model)
     return dict(value=float(np.median(times)) * 1e6, unit="us/step", cores=1, kind="oracle",
+                host=host,
                 sample=f"{len(times)} full decode steps of the same workload (B={w.B}, "
                        f"ctx={int(w.seq_lens.max())}), fp64 NumPy, 1 thread",
                 parity=dict(selection_bit_exact=ok_sel, attention_max_abs_err=err))
@@ -356,6 +444,9 @@ def main():
             "attn_GBps": round(sach, 1), "attn_frac": round(sach / HBM_PEAK_GBPS, 4),
             "select_us": round(s["select_us"], 3), "attn_bytes": s["attn_bytes"]}}
         del s
+        torch.cuda.empty_cache()
+    if not args.no_secondary:
+        result.setdefault("secondary", {})["speculative_rope_64_steps"] = speculative(dev)
         torch.cuda.empty_cache()
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, keep)
