@@ -221,6 +221,23 @@ kvsel_status kvsel_rope_table(double theta, int32_t head_dim, int32_t first_posi
 kvsel_status kvsel_rope_shift(const kvsel_paged_kv* kv, const kvsel_rope* rope, void* k_out,
                               void* stream);
 
+/* Device-side check of the contents every other entry point takes on trust (the host cannot
+ * read device memory before enqueuing): ORs into *flags (device uint32, sticky: bits are set,
+ * never cleared by the library)
+ *   KVSEL_CHECK_SEQ_LEN   if some seq_lens[b] < 0 or > max_pages_per_seq * page_size;
+ *   KVSEL_CHECK_PAGE_ID   if some page_table[b][n], n < N_b, is outside [0, num_phys_pages);
+ *   KVSEL_CHECK_SELECTION (only when sel_idx != NULL; sel_cnt and k then required) if some
+ *     sel_cnt[b][j] is outside [0, min(k, N_b)] or the first sel_cnt[b][j] entries of
+ *     sel_idx[b][j] are not strictly ascending page ids in [0, N_b).
+ * Reads stay inside the arrays the descriptor sizes whatever their contents, so it is safe to
+ * run on the inputs it is meant to reject. One launch of one block per sequence; for debugging
+ * and input validation, not for the decode path. */
+#define KVSEL_CHECK_SEQ_LEN 1u
+#define KVSEL_CHECK_PAGE_ID 2u
+#define KVSEL_CHECK_SELECTION 4u
+kvsel_status kvsel_check_inputs(const kvsel_paged_kv* kv, const int32_t* sel_idx,
+                                const int32_t* sel_cnt, int32_t k, uint32_t* flags, void* stream);
+
 /* ---- measurement ---- */
 
 /* Read-bandwidth probe: gathers n_chunks chunks of chunk_bytes bytes (1, 2, 4, 8, 16 or 32 KiB;

@@ -208,6 +208,16 @@ kvsel_status kvsel_select_attend(const kvsel_paged_kv* kv, const kvsel_rope* rop
                                             lse, ws, (hipStream_t)stream));
 }
 
+kvsel_status kvsel_check_inputs(const kvsel_paged_kv* kv, const int32_t* sel_idx,
+                                const int32_t* sel_cnt, int32_t k, uint32_t* flags, void* stream) {
+  LaunchKV f;
+  kvsel_status st = flatten(kv, 2, &f);
+  if (st != KVSEL_OK) return st;
+  if (!flags || (sel_idx && (!sel_cnt || k < 1))) return KVSEL_ERR_INVALID_ARGUMENT;
+  if ((st = check_device()) != KVSEL_OK) return st;
+  return launch_status(launch_check_inputs(f, sel_idx, sel_cnt, k, flags, (hipStream_t)stream));
+}
+
 kvsel_status kvsel_gather_probe(const uint64_t* chunk_addr, int32_t n_chunks, int32_t chunk_bytes,
                                 uint32_t* sink, void* stream) {
   if (!chunk_addr || !sink || n_chunks < 1 || n_chunks > (1 << 26)) return KVSEL_ERR_INVALID_ARGUMENT;

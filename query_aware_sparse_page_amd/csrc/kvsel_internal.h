@@ -76,6 +76,10 @@ hipError_t launch_attention(const LaunchKV& kv, const RopeArgs& rope, const void
                             int pages_per_split, void* out, float* lse, void* ws,
                             hipStream_t stream);
 
+// Device-side contract check; ORs KVSEL_CHECK_* bits into *flags.
+hipError_t launch_check_inputs(const LaunchKV& kv, const int32_t* sel_idx, const int32_t* sel_cnt,
+                               int k, uint32_t* flags, hipStream_t stream);
+
 // Gather probe: n_chunks chunks of chunk_kib KiB (1..32, a power of two) at device addresses.
 hipError_t launch_gather_probe(const uint64_t* addr, int n_chunks, int chunk_kib, uint32_t* sink,
                                hipStream_t stream);

@@ -24,6 +24,9 @@ KVSEL_OP_SCORE_TOPK = 1
 KVSEL_OP_ATTENTION = 2
 KVSEL_OP_SELECT_ATTEND = 3
 KVSEL_SCORE_REFRESH_TAIL = 1
+KVSEL_CHECK_SEQ_LEN = 1
+KVSEL_CHECK_PAGE_ID = 2
+KVSEL_CHECK_SELECTION = 4
 
 c_i32 = ctypes.c_int32
 c_vp = ctypes.c_void_p
@@ -72,6 +75,7 @@ EXPORTS = {
     "kvsel_select_attend": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp, c_vp,
                                     c_i32, c_i32, ctypes.c_float, c_vp, c_vp, c_vp, c_vp, c_vp,
                                     ctypes.c_size_t, c_vp]),
+    "kvsel_check_inputs": (c_i32, [ctypes.POINTER(PagedKVDesc), c_vp, c_vp, c_i32, c_vp, c_vp]),
     "kvsel_gather_probe": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp]),
     "kvsel_rope_table": (c_i32, [ctypes.c_double, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "kvsel_rope_shift": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp, c_vp]),
@@ -400,4 +404,21 @@ def tile_addresses(kv: PagedKV, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
                 addrs.append(kb + off)
                 addrs.append(vb + off)
     return torch.tensor(addrs, dtype=torch.int64).to(kv.device)
+
+
+def check_inputs(kv: PagedKV, sel_idx: Optional[torch.Tensor] = None,
+                 sel_cnt: Optional[torch.Tensor] = None, k: Optional[int] = None,
+                 flags: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Device-side contract check; returns the (sticky) int32 flag word (KVSEL_CHECK_* bits)."""
+    d = kv.desc()
+    dev = kv.device
+    if flags is None:
+        flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    if sel_idx is not None:
+        _dev(sel_idx, "sel_idx", torch.int32)
+        _dev(sel_cnt, "sel_cnt", torch.int32)
+        k = int(sel_idx.shape[-1]) if k is None else k
+    _check(lib().kvsel_check_inputs(ctypes.byref(d), _ptr(sel_idx), _ptr(sel_cnt),
+                                    0 if k is None else int(k), _ptr(flags), _stream(dev)))
+    return flags
 

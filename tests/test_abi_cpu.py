@@ -133,3 +133,14 @@ def test_gather_probe_validation(K):
     assert lib.kvsel_gather_probe(p, 0, 8192, p, None) == 1
     for bad in (0, 512, 3072, 65536, 8193):
         assert lib.kvsel_gather_probe(p, 4, bad, p, None) == 1
+
+
+def test_check_inputs_validation(K):
+    lib = K.lib()
+    d = _desc(K)
+    p = ctypes.c_void_p(0x5000)
+    assert lib.kvsel_check_inputs(ctypes.byref(d), None, None, 0, None, None) == 1   # no flags
+    assert lib.kvsel_check_inputs(ctypes.byref(d), p, None, 64, p, None) == 1        # no counts
+    assert lib.kvsel_check_inputs(ctypes.byref(d), p, p, 0, p, None) == 1            # k < 1
+    dn = _desc(K, page_table=None)
+    assert lib.kvsel_check_inputs(ctypes.byref(dn), None, None, 0, p, None) == 1
