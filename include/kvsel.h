@@ -134,10 +134,10 @@ size_t kvsel_workspace_bytes(const kvsel_paged_kv* kv, int32_t k, int32_t op,
                              int32_t pages_per_split);
 
 /* Page-summary build. For every logical page n < N_b of every sequence b and every KV head j,
- * writes summ[p][j][0][:] = channel-wise minimum and summ[p][j][1][:] = channel-wise maximum of
- * the valid slots' keys, p = page_table[b][n]. summ is [num_phys_pages][Hkv][2][D] in the element
- * type; rows of pages no sequence references are left untouched. A physical page referenced by
- * two (b, n) pairs must hold the same number of valid slots in both.
+ * writes summ[b][j][n][0][:] = channel-wise minimum and summ[b][j][n][1][:] = channel-wise
+ * maximum of the valid slots' keys of physical page page_table[b][n]. summ is
+ * [B][Hkv][max_pages_per_seq][2][D] in the element type (sequence-major: scoring reads a list's
+ * summaries as one contiguous run, without the page table); entries n >= N_b are left untouched.
  * tail_only != 0 rebuilds only each sequence's last logical page (the page a decode step appends
  * to). rope != NULL applies the rotary rotation to each key before the reduction (bit-identical
  * to rotating the pool first with kvsel_rope_shift).
@@ -148,7 +148,7 @@ kvsel_status kvsel_build_summaries(const kvsel_paged_kv* kv, const kvsel_rope* r
 
 /* Query-aware page scoring and top-k selection, per (sequence, KV head).
  * score[b][j][n] = fp32 rounding of the fp64 sum over the G query heads g of KV head j and the D
- * channels d of (q[b][jG+g][d] >= 0 ? q*hi : q*lo) with lo/hi from summ of page page_table[b][n]
+ * channels d of (q[b][jG+g][d] >= 0 ? q*hi : q*lo) with lo/hi = summ[b][j][n]
  * (an upper bound of sum_g q_g . k over the page's keys). Products are exact in fp64 and the sum
  * is accumulated in fp64.
  * sel_idx[b][j][0..cnt) (int32 [B][Hkv][k]) receives the min(k, N_b) logical pages with the

@@ -2,7 +2,7 @@
 //
 // score_kernel: one block per (page chunk, list), list = (sequence, KV head) varying fastest.
 // Each block scores 4 * PPW pages: LPR lanes read a page's lo and hi rows as 16-byte slices
-// (coalesced), multiply by the group's query slice in fp64 (a bf16 x bf16 or fp32 x fp32 product
+// (the summaries are sequence-major, so a block reads one contiguous run), multiply by the group's query slice in fp64 (a bf16 x bf16 or fp32 x fp32 product
 // is exact in fp64), take q*hi for q >= 0 and q*lo otherwise, and fold the LPR lanes; one
 // fp64 -> fp32 rounding per score. With the tail refresh on, the block holding a sequence's last
 // page first rebuilds that page's summary from the key pool (the page a decode step appends to),
@@ -245,22 +245,20 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   const int c0 = (lane % LPR) * VEC;
   const int n = n0 + w * PPW + lane / LPR;
 
-  // ---- loads first (unconditional, clamped addresses): q slice, page id, summary rows; the
-  // sequence length is read after they are issued, so its latency overlaps theirs ----
+  // ---- loads first (unconditional, clamped addresses), all in one round: q slice, summary
+  // rows (sequence-major, so no page-table hop), the page id (used only for the tail refresh)
+  // and the sequence length ----
   uint4 qraw[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) qraw[g] = load16(q + ((size_t)b * Hq + j * G + g) * D + c0);
-  // the table index depends on the row width only, so this load does not wait for seq_lens;
+  const int nc = min(n, a.maxp - 1);  // from the row width only: no wait for seq_lens
+  const T* srow = (const T*)a.summ + ((size_t)list * a.maxp + nc) * 2 * D + c0;
+  const uint4 lo_raw = load16(srow), hi_raw = load16(srow + D);
   // entries past the sequence may hold anything and are clamped into the pool (never used)
-  const int pt_raw = a.page_table[(size_t)b * a.maxp + min(n, a.maxp - 1)];
-  const T* summ = (const T*)a.summ;
-  const size_t row_off = (size_t)j * 2 * D + c0, page_stride = (size_t)a.Hkv * 2 * D;
+  const int pt_raw = a.page_table[(size_t)b * a.maxp + nc];
   __builtin_amdgcn_sched_barrier(0);
   const int L = a.seq_lens[b];
-  __builtin_amdgcn_sched_barrier(0);
   const int p = min(max(pt_raw, 0), a.Npp - 1);
-  const T* srow = summ + (size_t)p * page_stride + row_off;
-  const uint4 lo_raw = load16(srow), hi_raw = load16(srow + D);
   const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;  // never past the table row
   const bool active = n < N;
 
@@ -277,7 +275,7 @@ __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
     tile_minmax<T, D>((const T*)a.k_pool + ((size_t)pt * a.Hkv + j) * P * D, L - nt * P, P, lane,
                       pt, a.rope, flo, fhi);
     if (lane < LPR) {
-      T* out = (T*)a.summ + ((size_t)pt * a.Hkv + j) * 2 * D;
+      T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;
       store16(out + c0, pack<T>(flo));
       store16(out + D + c0, pack<T>(fhi));
     }
@@ -441,8 +439,8 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(SelectArgs a) {
 // ------------------------------------------------------------------------------------------
 // One launch for lists of at most FUSED_MAX_PAGES pages: one 1024-thread block per list scores
 // every page (keys straight into LDS) and then selects, so no score ever goes through memory
-// and no second launch is needed. The block first stages the list's page-table row in LDS (one
-// round of loads), then issues the summary loads in batches of UNROLL pages per lane. Wave 0
+// and no second launch is needed. The summary loads (sequence-major rows) go out in batches of
+// UNROLL pages per lane. Wave 0
 // refreshes the tail page (when asked) and scores it from registers while the other waves score
 // the rest.
 // ------------------------------------------------------------------------------------------
@@ -458,7 +456,6 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
   constexpr int PPI = (FUSED_THREADS / 64) * PPW;   // pages per block iteration
   constexpr int UNROLL = G >= 4 ? 4 : 8;  // summary loads in flight per lane
   __shared__ TopkSmem<FUSED_THREADS> sm;
-  __shared__ int s_pt[FUSED_MAX_PAGES];
   __shared__ int s_corr;
   const int j = blockIdx.x, b = blockIdx.y;  // grid (Hkv, B)
   const int list = b * a.Hkv + j;
@@ -471,8 +468,6 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
   const bool refresh = a.refresh_tail && N > 0;
   const int n_end = refresh ? N - 1 : N;  // pages scored from stored summaries
 
-  for (int n = tid; n < n_end; n += FUSED_THREADS)
-    s_pt[n] = min(max(a.page_table[(size_t)b * a.maxp + n], 0), a.Npp - 1);
   uint4 qraw[G];  // packed query slices (half the registers of unpacked bf16)
 #pragma unroll
   for (int g = 0; g < G; ++g) qraw[g] = load16((const T*)a.q + ((size_t)b * Hq + j * G + g) * D + c0);
@@ -485,7 +480,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
     tile_minmax<T, D>((const T*)a.k_pool + ((size_t)pt * a.Hkv + j) * P * D, L - nt * P, P, lane,
                       pt, a.rope, lo, hi);
     if (lane < LPR) {
-      T* out = (T*)a.summ + ((size_t)pt * a.Hkv + j) * 2 * D;
+      T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;
       store16(out + c0, pack<T>(lo));
       store16(out + D + c0, pack<T>(hi));
     }
@@ -503,7 +498,6 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
       if (a.write_scores) a.scores[(size_t)list * a.maxp + nt] = (float)acc;
     }
   }
-  __syncthreads();  // page-table row staged
 
   // ---- every other page ----
   for (int it0 = 0; it0 * PPI < n_end; it0 += UNROLL) {
@@ -511,8 +505,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int n = (it0 + u) * PPI + w * PPW + lane / LPR;
-      const int p = s_pt[min(n, n_end - 1)];
-      const T* srow = (const T*)a.summ + ((size_t)p * a.Hkv + j) * 2 * D + c0;
+      const T* srow = (const T*)a.summ + ((size_t)list * a.maxp + min(n, n_end - 1)) * 2 * D + c0;
       lo_raw[u] = load16(srow);
       hi_raw[u] = load16(srow + D);
     }

@@ -1,6 +1,8 @@
-// Page-summary build: channel-wise min / max of the valid keys of each (page, KV head).
+// Page-summary build: channel-wise min / max of the valid keys of each (logical page, KV head),
+// stored sequence-major, summ[b][j][n][lo | hi][D], so that scoring reads each list's summaries
+// as one contiguous run with no page-table hop.
 //
-// One wave reduces one (physical page, KV head) tile of P x D keys: each lane loads 16-byte
+// One wave reduces one (page, KV head) tile of P x D keys: each lane loads 16-byte
 // slices of rows (coalesced: LPR lanes cover one row, so one wave-wide load reads RPW whole
 // rows), keeps a running min / max per channel, then the RPW row groups are folded with
 // cross-lane exchanges and the first row group writes the lo and hi rows (16 bytes per lane).
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_
     }
   }
   if (rg == 0) {
-    T* out = summ + ((size_t)p * Hkv + j) * 2 * D;
+    T* out = summ + (((size_t)b * Hkv + j) * maxp + n) * 2 * D;
     store16(out + c0, pack<T>(lo));
     store16(out + D + c0, pack<T>(hi));
   }

@@ -127,6 +127,13 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
     return t
 
 
+def _check_summ(kv: "PagedKV", summ: torch.Tensor) -> None:
+    _dev(summ, "summ", kv.k_pool.dtype)
+    shape = (kv.batch, kv.num_kv_heads, int(kv.page_table.shape[1]), 2, kv.head_dim)
+    if tuple(summ.shape) != shape:
+        raise ValueError(f"summ must be {shape} (sequence-major), got {tuple(summ.shape)}")
+
+
 def _elem_code(dtype: torch.dtype) -> int:
     if dtype == torch.float32:
         return KVSEL_F32
@@ -227,12 +234,16 @@ def _workspace(kv: PagedKV, k: int, op: int, pps: int, ws: Optional[torch.Tensor
 
 def build_summaries(kv: PagedKV, rope: Optional[Rope] = None, tail_only: bool = False,
                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Per-page channel-wise key min/max: returns summ [Npp][Hkv][2][D] (pool element type)."""
+    """Per-page channel-wise key min/max, sequence-major: returns summ [B][Hkv][max_pages][2][D]
+    (pool element type); summ[b][j][n] summarizes logical page n of sequence b."""
     d = kv.desc()
-    Npp, Hkv, _, D = kv.k_pool.shape
+    _, Hkv, _, D = kv.k_pool.shape
+    shape = (kv.batch, Hkv, int(kv.page_table.shape[1]), 2, D)
     if out is None:
-        out = torch.empty((Npp, Hkv, 2, D), dtype=kv.k_pool.dtype, device=kv.device)
+        out = torch.empty(shape, dtype=kv.k_pool.dtype, device=kv.device)
     _dev(out, "summ", kv.k_pool.dtype)
+    if tuple(out.shape) != shape:
+        raise ValueError(f"summ must be {shape}, got {tuple(out.shape)}")
     _check(lib().kvsel_build_summaries(ctypes.byref(d), _rope_ptr(rope), int(bool(tail_only)),
                                        _ptr(out), _stream(kv.device)))
     return out
@@ -260,7 +271,7 @@ def score_topk(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, *,
     d = kv.desc()
     B, Hkv = kv.batch, kv.num_kv_heads
     dev = kv.device
-    _dev(summ, "summ", kv.k_pool.dtype)
+    _check_summ(kv, summ)
     _dev(q, "q", kv.k_pool.dtype)
     if sel_idx is None:
         sel_idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
@@ -334,7 +345,7 @@ def select_attend(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, *,
     d = kv.desc()
     B, Hkv = kv.batch, kv.num_kv_heads
     dev = kv.device
-    _dev(summ, "summ", kv.k_pool.dtype)
+    _check_summ(kv, summ)
     _dev(q, "q", kv.k_pool.dtype)
     if sel_idx is None:
         sel_idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)

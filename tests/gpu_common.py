@@ -34,12 +34,22 @@ def referenced_pages(w):
     return sorted(set(out))
 
 
-def assert_summaries_equal(gpu_summ, ref_summ, pages):
-    g = gpu_summ.float().cpu().numpy()[pages]
-    r = ref_summ[pages]
-    assert np.isfinite(r).all()
-    bad = np.argwhere(g != r)  # by value: -0 == +0
-    assert bad.size == 0, f"{len(bad)} summary values differ, first {bad[:3].tolist()}"
+def assert_summaries_equal(gpu_summ, ref_summ, w):
+    """gpu_summ is sequence-major [B][Hkv][max_pages][2][D]; ref_summ is the oracle's per physical
+    page [Npp][Hkv][2][D]: logical page n of sequence b must equal physical page page_table[b][n]."""
+    g = gpu_summ.float().cpu().numpy()
+    n_bad = 0
+    first = None
+    for b in range(w.B):
+        N = w.n_pages(b)
+        pages = w.page_table[b, :N].numpy()
+        r = ref_summ[pages].transpose(1, 0, 2, 3)  # [Hkv][N][2][D]
+        assert np.isfinite(r).all()
+        bad = np.argwhere(g[b, :, :N] != r)  # by value: -0 == +0
+        n_bad += len(bad)
+        if len(bad) and first is None:
+            first = (b, bad[:3].tolist())
+    assert n_bad == 0, f"{n_bad} summary values differ, first {first}"
 
 
 def orderable32(x):

@@ -54,7 +54,7 @@ def full_case(name):
 def test_full_workload_parity(K, name):
     w, ref = full_case(name)
     g = run_gpu_path(K, w)
-    assert_summaries_equal(g["summ"], ref["summ"], referenced_pages(w))
+    assert_summaries_equal(g["summ"], ref["summ"], w)
     n_exact, n = assert_scores_close(g["scores"], ref["scores"], w, exact=(w.dtype == "bf16"))
     say(f"{name}: scores exact {n_exact}/{n}; min k-boundary margin {ref['margins'].min()} ulp")
     assert_selection_equal(g["sel"], g["cnt"], ref["sel"], ref["cnt"], ref["margins"])
@@ -98,7 +98,7 @@ def test_edge_case_parity(K, case):
     ref = oracle_path(w, scale_of(w.D))
     for pps in (0, 1, 4):
         g = run_gpu_path(K, w, pps=pps)
-        assert_summaries_equal(g["summ"], ref["summ"], sorted(used))
+        assert_summaries_equal(g["summ"], ref["summ"], w)
         assert_scores_close(g["scores"], ref["scores"], w, exact=(w.dtype == "bf16"))
         assert_selection_equal(g["sel"], g["cnt"], ref["sel"], ref["cnt"], ref["margins"])
         assert_attention_close(g["out"], g["lse"], ref["out"], ref["lse"], w.dtype)
@@ -170,7 +170,7 @@ def test_tail_only_summary_refresh(K):
     K.build_summaries(kv, tail_only=True, out=tail)
     torch.cuda.synchronize()
     ref = O.page_summaries(kv.k_pool.cpu(), w.page_table, w.seq_lens, w.P)
-    assert_summaries_equal(tail, ref, referenced_pages(w))
+    assert_summaries_equal(tail, ref, w)
 
 
 def test_fused_tail_refresh_in_selection(K):
@@ -187,7 +187,7 @@ def test_fused_tail_refresh_in_selection(K):
     torch.cuda.synchronize()
     kpool = kv.k_pool.cpu()
     ref_summ = O.page_summaries(kpool, w.page_table, w.seq_lens, w.P)
-    assert_summaries_equal(summ, ref_summ, referenced_pages(w))
+    assert_summaries_equal(summ, ref_summ, w)
     ref_sc = O.page_scores(w.q, ref_summ, w.page_table, w.seq_lens, w.P)
     ref_sel, ref_cnt = O.top_pages(ref_sc, w.seq_lens, w.P, w.k)
     assert_scores_close(sc, ref_sc, w, exact=True)
@@ -253,6 +253,9 @@ def test_selection_launch_structures_agree(K, dtype):
     kv_wide = K.PagedKV(kv.k_pool, kv.v_pool, wide_pt.cuda(), kv.seq_lens, w.Hq)
     q = w.q.cuda()
     summ = K.build_summaries(kv)
+    summ_wide = K.build_summaries(kv_wide)  # sequence-major: one row per table entry
+    for b in range(w.B):  # entries past a sequence's pages are never written
+        assert torch.equal(summ[b, :, :w.n_pages(b)], summ_wide[b, :, :w.n_pages(b)])
     ref_summ = O.page_summaries(w.k_pool, w.page_table, w.seq_lens, w.P)
     ref_sc = O.page_scores(w.q, ref_summ, w.page_table, w.seq_lens, w.P)
     ref_sel, ref_cnt = O.top_pages(ref_sc, w.seq_lens, w.P, w.k)
@@ -261,7 +264,7 @@ def test_selection_launch_structures_agree(K, dtype):
         sc_a = torch.full((w.B, w.Hkv, w.max_pages), float("nan"), device="cuda")
         sc_b = torch.full((w.B, w.Hkv, 2100), float("nan"), device="cuda")
         sel_a, cnt_a = K.score_topk(kv, summ, q, w.k, refresh_tail=refresh, scores=sc_a)
-        sel_b, cnt_b = K.score_topk(kv_wide, summ, q, w.k, refresh_tail=refresh, scores=sc_b)
+        sel_b, cnt_b = K.score_topk(kv_wide, summ_wide, q, w.k, refresh_tail=refresh, scores=sc_b)
         sel_c, cnt_c = K.score_topk(kv, summ, q, w.k, refresh_tail=refresh)
         torch.cuda.synchronize()
         assert torch.equal(sel_a, sel_b) and torch.equal(cnt_a, cnt_b)
@@ -281,8 +284,8 @@ def test_selection_launch_structures_agree(K, dtype):
     prev_idx = torch.randint(0, 5, (w.B, w.Hkv, w.k), generator=gen, dtype=torch.int32).cuda()
     prev_cnt = torch.full((w.B, w.Hkv), 3, dtype=torch.int32).cuda()
     res = []
-    for kvx in (kv, kv_wide):
-        res.append(K.score_topk(kvx, summ, q, w.k,
+    for kvx, sx in ((kv, summ), (kv_wide, summ_wide)):
+        res.append(K.score_topk(kvx, sx, q, w.k,
                                 reuse=K.Reuse(q_prev, prev_idx, prev_cnt, 0.8, first_step=False)))
     torch.cuda.synchronize()
     for x, y in zip(res[0], res[1]):

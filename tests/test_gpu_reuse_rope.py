@@ -149,7 +149,7 @@ def test_speculative_decode_loop_matches_oracle(K, spec):
     summ = K.build_summaries(kv)
     o_summ = O.page_summaries(o_pool, w.page_table, w.seq_lens, w.P)
     torch.cuda.synchronize()
-    assert_summaries_equal(summ, o_summ, referenced_pages(w))
+    assert_summaries_equal(summ, o_summ, w)
     scale = scale_of(w.D)
     prev = (torch.zeros((w.B, w.Hkv, w.k), dtype=torch.int32, device="cuda"),
             torch.zeros((w.B, w.Hkv), dtype=torch.int32, device="cuda"))

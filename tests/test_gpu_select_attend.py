@@ -106,7 +106,8 @@ def test_tail_refresh_and_workspace_reuse(K):
         sep = separate_calls(K, kv, summ_b, q, w.k, refresh_tail=True)
         torch.cuda.synchronize()
         assert_same(fused, sep)
-        assert torch.equal(summ_a, summ_b)
+        for b in range(w.B):  # entries past a sequence's pages are never written
+            assert torch.equal(summ_a[b, :, :w.n_pages(b)], summ_b[b, :, :w.n_pages(b)])
     ref_summ = O.page_summaries(kv.k_pool.cpu(), w.page_table, w.seq_lens, w.P)
     sc = O.page_scores(w.q, ref_summ, w.page_table, w.seq_lens, w.P)
     ref_sel, ref_cnt = O.top_pages(sc, w.seq_lens, w.P, w.k)
