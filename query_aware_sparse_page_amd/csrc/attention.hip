@@ -563,7 +563,9 @@ constexpr int MERGE_CHUNK = 32;
 template <typename T, int D>
 __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int G) {
   const float NEG_INF = __int_as_float(0xff800000);
-  const int g = blockIdx.x, j = blockIdx.y, b = blockIdx.z;  // grid (G, Hkv, B)
+  // grid (Hkv, G, B): KV heads vary fastest, as in the attention grid, so a list's merge blocks
+  // are dispatched to the XCD that ran its splits (round-robin placement)
+  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int list = b * a.Hkv + j;
   const int d = threadIdx.x;
   const int Hq = a.Hkv * G;
@@ -685,7 +687,7 @@ static hipError_t launch_tiles(int tiles, const AttnArgs& a, int G, bool rope, h
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(G, a.Hkv, a.nlists / a.Hkv), dim3(D), 0, stream,
+  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(a.Hkv, G, a.nlists / a.Hkv), dim3(D), 0, stream,
                      a, G);
   return hipGetLastError();
 }
@@ -798,7 +800,7 @@ static hipError_t launch_fused(int c, const AttnArgs& a, int G, hipStream_t stre
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(G, a.Hkv, a.nlists / a.Hkv), dim3(D), 0, stream,
+  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(a.Hkv, G, a.nlists / a.Hkv), dim3(D), 0, stream,
                      a, G);
   return hipGetLastError();
 }
