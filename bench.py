@@ -219,8 +219,8 @@ def speculative(dev, reps=3):
     """The speculative workload: a 32K cache built from eight rotary-encoded 4096-token blocks,
     re-positioned on the fly (fused rotary gather), then 64 decode steps with AR(1) queries where
     step t attends over step t-1's pages unless the group-mean query similarity is below tau.
-    The 64 steps (score_topk with reuse + attention over the used pages) are one HIP graph;
-    reports µs per step (warm: the same cache every step) and the quality statistics."""
+    The 64 steps are one HIP graph, as overlapped speculative steps and as serial calls; reports
+    µs per step of both (warm: the same cache every step) and the quality statistics."""
     w = W.speculative_rope()
     bt = w.extra["block_tokens"]
     blocks = bt // w.P
@@ -245,7 +245,7 @@ def speculative(dev, reps=3):
     ws_a = K.new_workspace(kv, k, K.KVSEL_OP_ATTENTION)
     res = []
 
-    def loop():
+    def loop_serial():
         res.clear()
         for t in range(T):
             r = K.score_topk(kv, summ, qs[t], k, sel_idx=sel[t], sel_cnt=cnt[t], workspace=ws_s,
@@ -255,25 +255,43 @@ def speculative(dev, reps=3):
             K.sparse_decode_attn(kv, qs[t], r[2], r[3], k, rope=shift, out=out[t], lse=lse[t],
                                  workspace=ws_a)
 
-    st = torch.cuda.Stream()
-    st.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(st):
-        loop()
-    torch.cuda.current_stream().wait_stream(st)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        loop()
-    g.replay()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+    def loop_overlapped():
+        res.clear()
+        for t in range(T):
+            r = K.speculative_step(kv, summ, qs[t], k,
+                                   K.Reuse(qs[t - 1] if t else qs[t], sel[t - 1] if t else sel[t],
+                                           cnt[t - 1] if t else cnt[t], tau, first_step=(t == 0)),
+                                   rope=shift, sel_idx=sel[t], sel_cnt=cnt[t], out=out[t],
+                                   lse=lse[t], workspace=ws_f)
+            res.append(r)
+
+    def timed(loop):
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            loop()
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            loop()
         g.replay()
-    e1.record()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / (reps * T)
+
+    ws_f = K.new_workspace(kv, k, K.KVSEL_OP_SPECULATIVE_STEP)
+    us_serial = timed(loop_serial)
+    out_serial = out.clone()
+    us = timed(loop_overlapped)
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1000.0 / (reps * T)
+    same = bool(torch.equal(out, out_serial))
     corrected = torch.stack([r[4] for r in res]).cpu().numpy()   # [T][B][Hkv]
     used = torch.stack([r[2] for r in res]).cpu().numpy()
     ucnt = torch.stack([r[3] for r in res]).cpu().numpy()
@@ -285,12 +303,16 @@ def speculative(dev, reps=3):
                 u = set(used[t, b, j, :ucnt[t, b, j]].tolist())
                 f = set(fresh[t, b, j, :fcnt[t, b, j]].tolist())
                 overlap.append(len(u & f) / k)
-    return {"us_per_step": round(us, 3), "steps": T, "tau": tau, "rho": w.extra["rho"],
+    return {"us_per_step": round(us, 3), "serial_us_per_step": round(us_serial, 3),
+            "overlapped_equals_serial": same, "steps": T, "tau": tau, "rho": w.extra["rho"],
             "correction_rate": round(float(corrected[1:].mean()), 4),
             "corrections": int(corrected[1:].sum()), "decisions": int(corrected[1:].size),
             "mean_overlap_used_fresh": round(float(np.mean(overlap)), 4),
-            "step": "score + top-k + reuse decision, then attention over the used pages with "
-                    "the rotary re-positioning fused into the key gather (warm: one cache)"}
+            "step": "kvsel_speculative_step: attention over the previous step's pages on a side "
+                    "stream while the main stream scores, selects and decides; corrected lists "
+                    "attended again; rotary re-positioning fused into the key gather (warm: one "
+                    "cache). serial_us_per_step: kvsel_score_topk with reuse, then "
+                    "kvsel_sparse_decode_attn over the used pages"}
 
 
 def cpu_baseline(w, lay, budget_s=12.0):

@@ -68,6 +68,7 @@ typedef int32_t kvsel_status;
 #define KVSEL_OP_SCORE_TOPK 1
 #define KVSEL_OP_ATTENTION 2
 #define KVSEL_OP_SELECT_ATTEND 3
+#define KVSEL_OP_SPECULATIVE_STEP 4
 
 /* Flags of kvsel_score_topk. */
 #define KVSEL_SCORE_REFRESH_TAIL 1 /* rebuild each sequence's last-page summary first */
@@ -220,6 +221,28 @@ kvsel_status kvsel_rope_table(double theta, int32_t head_dim, int32_t first_posi
  * [KV Packet] section 1. */
 kvsel_status kvsel_rope_shift(const kvsel_paged_kv* kv, const kvsel_rope* rope, void* k_out,
                               void* stream);
+
+/* Speculative decode step: the outputs of kvsel_score_topk with `reuse` (required) followed by
+ * kvsel_sparse_decode_attn over the used pages (reuse->used_idx / used_cnt) with the library's
+ * default split, bit for bit, with the attention over the previous step's pages
+ * (reuse->prev_idx / prev_cnt) overlapped with the selection: it is enqueued on side_stream
+ * after fork_event is recorded on `stream`, while `stream` scores, selects and decides; then
+ * `stream` waits on join_event (recorded on side_stream), attends again over the fresh pages of
+ * the lists the decision corrected, and merges. With reuse->first_step every list is corrected
+ * and the step runs serially on `stream` (the events and side stream are not used). Capturable
+ * in a HIP graph when both streams take part in the capture.
+ * side_stream: a stream other than `stream` (hipStream_t, non-NULL). fork_event / join_event:
+ * hipEvent_t handles owned by the caller (timing may be disabled). sel_idx / sel_cnt must not
+ * alias prev_idx / prev_cnt. ws / ws_bytes: kvsel_workspace_bytes(kv, k,
+ * KVSEL_OP_SPECULATIVE_STEP, 0). Other arguments as kvsel_score_topk and kvsel_sparse_decode_attn.
+ * [FreeKV] section 2.1 (speculative retrieval: attention at step i over the pages chosen at step
+ * i-1, overlapped with the selection; fine-grained correction when the group-mean similarity is
+ * below tau). */
+kvsel_status kvsel_speculative_step(const kvsel_paged_kv* kv, const kvsel_rope* rope, void* summ,
+                                    const void* q, int32_t k, int32_t flags, float scale,
+                                    const kvsel_reuse* reuse, int32_t* sel_idx, int32_t* sel_cnt,
+                                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream,
+                                    void* side_stream, void* fork_event, void* join_event);
 
 /* Device-side check of the contents every other entry point takes on trust (the host cannot
  * read device memory before enqueuing): ORs into *flags (device uint32, sticky: bits are set,

@@ -60,6 +60,8 @@ struct AttnArgs {
   const float* scores;  // [nlists][maxp]
   int32_t* sel_out;     // [nlists][k]
   int32_t* cnt_out;     // [nlists]
+  // speculative step only: lists with only_lists[list] == 0 do nothing (nullable: all lists)
+  const uint8_t* only_lists;
 };
 
 constexpr int ATT_MAX_PPS = 16;  // pages per split of the fused-selection launches
@@ -255,6 +257,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a, int G
   const float NEG_INF = __int_as_float(0xff800000);
   const int j = blockIdx.x, b = blockIdx.y, split = blockIdx.z;  // grid (Hkv, B, splits)
   const int list = b * a.Hkv + j;
+  if (a.only_lists && !a.only_lists[list]) return;  // whole block: before any barrier
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q4 = lane >> 4;
   const int Hq = a.Hkv * G;
@@ -418,6 +421,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(AttnArgs a, int G)
   const float NEG_INF = __int_as_float(0xff800000);
   const int j = blockIdx.x, b = blockIdx.y, split = blockIdx.z;  // grid (Hkv, B, splits)
   const int list = b * a.Hkv + j;
+  if (a.only_lists && !a.only_lists[list]) return;  // whole block: before any barrier
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q4 = lane >> 4;
   const int Hq = a.Hkv * G;
@@ -677,25 +681,42 @@ static void launch_split(const AttnArgs& a, int G, bool rope, hipStream_t stream
   }
 }
 
+// parts: 1 = the split launch, 2 = the merge launch (when there is more than one split)
 template <typename T, int D, int P>
-static hipError_t launch_tiles(int tiles, const AttnArgs& a, int G, bool rope, hipStream_t stream) {
-  switch (tiles) {
-    case 1: launch_split<T, D, P, 1, 1>(a, G, rope, stream); break;
-    case 2: launch_split<T, D, P, 2, 1>(a, G, rope, stream); break;
-    case 4: launch_split<T, D, P, 4, 1>(a, G, rope, stream); break;
-    default: launch_split<T, D, P, 4, 2>(a, G, rope, stream); break;
+static hipError_t launch_tiles(int tiles, const AttnArgs& a, int G, bool rope, int parts,
+                               hipStream_t stream) {
+  if (parts & 1) {
+    switch (tiles) {
+      case 1: launch_split<T, D, P, 1, 1>(a, G, rope, stream); break;
+      case 2: launch_split<T, D, P, 2, 1>(a, G, rope, stream); break;
+      case 4: launch_split<T, D, P, 4, 1>(a, G, rope, stream); break;
+      default: launch_split<T, D, P, 4, 2>(a, G, rope, stream); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit == 1) return e;
+  if (!(parts & 2) || a.nsplit == 1) return hipSuccess;
   hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(a.Hkv, G, a.nlists / a.Hkv), dim3(D), 0, stream,
                      a, G);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_p(int P, int tiles, const AttnArgs& a, int G, bool rope, hipStream_t stream) {
-  if (P == 16) return launch_tiles<T, D, 16>(tiles, a, G, rope, stream);
-  return launch_tiles<T, D, 32>(tiles, a, G, rope, stream);
+static hipError_t launch_p(int P, int tiles, const AttnArgs& a, int G, bool rope, int parts,
+                           hipStream_t stream) {
+  if (P == 16) return launch_tiles<T, D, 16>(tiles, a, G, rope, parts, stream);
+  return launch_tiles<T, D, 32>(tiles, a, G, rope, parts, stream);
+}
+
+static hipError_t launch_parts(const LaunchKV& kv, const AttnArgs& a, bool rope, int parts,
+                               hipStream_t stream) {
+  const int tiles = tiles_for(kv, a.pps);
+  if (kv.dtype == 0) {
+    if (kv.D == 64) return launch_p<float, 64>(kv.P, tiles, a, kv.G, rope, parts, stream);
+    return launch_p<float, 128>(kv.P, tiles, a, kv.G, rope, parts, stream);
+  }
+  if (kv.D == 64) return launch_p<bf16_t, 64>(kv.P, tiles, a, kv.G, rope, parts, stream);
+  return launch_p<bf16_t, 128>(kv.P, tiles, a, kv.G, rope, parts, stream);
 }
 
 static AttnArgs attn_args(const LaunchKV& kv, const RopeArgs& rope, const void* q,
@@ -732,6 +753,7 @@ static AttnArgs attn_args(const LaunchKV& kv, const RopeArgs& rope, const void* 
   a.scores = nullptr;
   a.sel_out = nullptr;
   a.cnt_out = nullptr;
+  a.only_lists = nullptr;
   return a;
 }
 
@@ -741,14 +763,54 @@ hipError_t launch_attention(const LaunchKV& kv, const RopeArgs& rope, const void
                             hipStream_t stream) {
   const int pps = attention_pages_per_split(kv, k, pages_per_split);
   const AttnArgs a = attn_args(kv, rope, q, sel_idx, sel_cnt, k, scale, pps, out, lse, ws);
-  const int tiles = tiles_for(kv, pps);
+  return launch_parts(kv, a, rope.page_row != nullptr, 3, stream);
+}
+
+// ------------------------------------------------------------------------------------------
+// Speculative decode step ([FreeKV] section 2.1: step t attends over step t-1's pages unless the
+// group-mean query similarity falls below tau). The attention over the previous pages does not
+// depend on this step's selection, so it runs on a side stream while the main stream scores,
+// selects and decides; after the join, the lists the decision corrected are attended again over
+// their fresh pages (the split launch with a list mask: the other lists' blocks exit at once),
+// overwriting their partials, and one merge finishes every list. The outputs are those of
+// kvsel_score_topk with reuse followed by kvsel_sparse_decode_attn over the used pages, bit for
+// bit: every list's partials come from the same split kernel over the same pages.
+// ------------------------------------------------------------------------------------------
+hipError_t launch_speculative_step(const LaunchKV& kv, const RopeArgs& rope, void* summ,
+                                   const void* q, int k, int flags, float scale,
+                                   const ReuseArgs& reuse, int32_t* sel_idx, int32_t* sel_cnt,
+                                   void* out, float* lse, void* ws, hipStream_t stream,
+                                   hipStream_t side, hipEvent_t fork, hipEvent_t join) {
+  float* scores = (float*)ws;
+  void* attn_ws = (char*)ws + align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float));
+  const int pps = attention_pages_per_split(kv, k, 0);
   const bool r = rope.page_row != nullptr;
-  if (kv.dtype == 0) {
-    if (kv.D == 64) return launch_p<float, 64>(kv.P, tiles, a, kv.G, r, stream);
-    return launch_p<float, 128>(kv.P, tiles, a, kv.G, r, stream);
+  if (reuse.first_step) {  // every list is corrected: the plain serial step
+    hipError_t e = launch_score_topk(kv, rope, summ, q, k, flags, sel_idx, sel_cnt, scores, false,
+                                     reuse, stream);
+    if (e != hipSuccess) return e;
+    return launch_attention(kv, rope, q, reuse.used_idx, reuse.used_cnt, k, scale, 0, out, lse,
+                            attn_ws, stream);
   }
-  if (kv.D == 64) return launch_p<bf16_t, 64>(kv.P, tiles, a, kv.G, r, stream);
-  return launch_p<bf16_t, 128>(kv.P, tiles, a, kv.G, r, stream);
+  hipError_t e = hipEventRecord(fork, stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
+  if (e != hipSuccess) return e;
+  // side stream: the previous step's pages (split launch only)
+  const AttnArgs spec =
+      attn_args(kv, rope, q, reuse.prev_idx, reuse.prev_cnt, k, scale, pps, out, lse, attn_ws);
+  if ((e = launch_parts(kv, spec, r, 1, side)) != hipSuccess) return e;
+  // main stream: scores, top-k, reuse decision
+  e = launch_score_topk(kv, rope, summ, q, k, flags, sel_idx, sel_cnt, scores, false, reuse,
+                        stream);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(join, side);
+  if (e == hipSuccess) e = hipStreamWaitEvent(stream, join, 0);
+  if (e != hipSuccess) return e;
+  // corrected lists again over their fresh pages, then the merge of every list
+  AttnArgs fix =
+      attn_args(kv, rope, q, reuse.used_idx, reuse.used_cnt, k, scale, pps, out, lse, attn_ws);
+  fix.only_lists = reuse.corrected;
+  return launch_parts(kv, fix, r, 3, stream);
 }
 
 // ------------------------------------------------------------------------------------------

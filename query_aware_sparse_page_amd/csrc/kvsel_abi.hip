@@ -117,7 +117,8 @@ size_t kvsel_workspace_bytes(const kvsel_paged_kv* kv, int32_t k, int32_t op,
   if (k < 1 || flatten(kv, 0, &f) != KVSEL_OK) return 0;
   if (op == KVSEL_OP_SCORE_TOPK) return score_workspace(f, true);
   if (op == KVSEL_OP_ATTENTION) return attention_workspace(f, k, pages_per_split);
-  if (op == KVSEL_OP_SELECT_ATTEND) return select_attend_workspace(f, k);
+  if (op == KVSEL_OP_SELECT_ATTEND || op == KVSEL_OP_SPECULATIVE_STEP)
+    return select_attend_workspace(f, k);
   return 0;
 }
 
@@ -206,6 +207,43 @@ kvsel_status kvsel_select_attend(const kvsel_paged_kv* kv, const kvsel_rope* rop
   if ((st = check_device()) != KVSEL_OK) return st;
   return launch_status(launch_select_attend(f, r, summ, q, k, flags, scale, sel_idx, sel_cnt, out,
                                             lse, ws, (hipStream_t)stream));
+}
+
+kvsel_status kvsel_speculative_step(const kvsel_paged_kv* kv, const kvsel_rope* rope, void* summ,
+                                    const void* q, int32_t k, int32_t flags, float scale,
+                                    const kvsel_reuse* reuse, int32_t* sel_idx, int32_t* sel_cnt,
+                                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream,
+                                    void* side_stream, void* fork_event, void* join_event) {
+  LaunchKV f;
+  RopeArgs r;
+  kvsel_status st = flatten(kv, 3, &f);
+  if (st != KVSEL_OK) return st;
+  if (!summ || !q || !sel_idx || !sel_cnt || !out || k < 1 || !reuse) return KVSEL_ERR_INVALID_ARGUMENT;
+  if (!reuse->q_prev || !reuse->prev_idx || !reuse->prev_cnt || !reuse->used_idx ||
+      !reuse->used_cnt || !reuse->corrected)
+    return KVSEL_ERR_INVALID_ARGUMENT;
+  if (!side_stream || side_stream == stream || !fork_event || !join_event)
+    return KVSEL_ERR_INVALID_ARGUMENT;
+  if (flags & ~KVSEL_SCORE_REFRESH_TAIL) return KVSEL_ERR_INVALID_ARGUMENT;
+  if ((st = flatten_rope(rope, &r)) != KVSEL_OK) return st;
+  if (attention_pages_per_split(f, k, 0) <= 0) return KVSEL_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < select_attend_workspace(f, k)) return KVSEL_ERR_WORKSPACE;
+  ReuseArgs ra;
+  memset(&ra, 0, sizeof(ra));
+  ra.q_prev = reuse->q_prev;
+  ra.prev_idx = reuse->prev_idx;
+  ra.prev_cnt = reuse->prev_cnt;
+  ra.tau = reuse->tau;
+  ra.first_step = reuse->first_step;
+  ra.used_idx = reuse->used_idx;
+  ra.used_cnt = reuse->used_cnt;
+  ra.corrected = reuse->corrected;
+  ra.similarity = reuse->similarity;
+  if ((st = check_device()) != KVSEL_OK) return st;
+  return launch_status(launch_speculative_step(f, r, summ, q, k, flags, scale, ra, sel_idx,
+                                               sel_cnt, out, lse, ws, (hipStream_t)stream,
+                                               (hipStream_t)side_stream, (hipEvent_t)fork_event,
+                                               (hipEvent_t)join_event));
 }
 
 kvsel_status kvsel_check_inputs(const kvsel_paged_kv* kv, const int32_t* sel_idx,
