@@ -219,7 +219,7 @@ def speculative(dev, reps=3):
     """The speculative workload: a 32K cache built from eight rotary-encoded 4096-token blocks,
     re-positioned on the fly (fused rotary gather), then 64 decode steps with AR(1) queries where
     step t attends over step t-1's pages unless the group-mean query similarity is below tau.
-    The 64 steps are one HIP graph, as overlapped speculative steps and as serial calls; reports
+    The 64 steps are one HIP graph, as speculative steps and as serial calls; reports
     µs per step of both (warm: the same cache every step) and the quality statistics."""
     w = W.speculative_rope()
     bt = w.extra["block_tokens"]
@@ -308,10 +308,11 @@ def speculative(dev, reps=3):
             "correction_rate": round(float(corrected[1:].mean()), 4),
             "corrections": int(corrected[1:].sum()), "decisions": int(corrected[1:].size),
             "mean_overlap_used_fresh": round(float(np.mean(overlap)), 4),
-            "step": "kvsel_speculative_step: attention over the previous step's pages on a side "
-                    "stream while the main stream scores, selects and decides; corrected lists "
-                    "attended again; rotary re-positioning fused into the key gather (warm: one "
-                    "cache). serial_us_per_step: kvsel_score_topk with reuse, then "
+            "step": "kvsel_speculative_step: attention over the previous step's pages in the "
+                    "same launch as the page scoring and the reuse decision, then the fused "
+                    "selection (corrected lists attended again over their fresh pages) and the "
+                    "merge; rotary re-positioning fused into the key gather (warm: one cache). "
+                    "serial_us_per_step: kvsel_score_topk with reuse, then "
                     "kvsel_sparse_decode_attn over the used pages"}
 
 

@@ -194,9 +194,8 @@ kvsel_status kvsel_sparse_decode_attn(const kvsel_paged_kv* kv, const kvsel_rope
  * bit for bit. The top-k is re-derived inside the attention launch by every block of a list from
  * the page scores (each block keeps the pages of its own split), so the K / V reads follow one
  * memory round trip after the scores instead of the selection-ids -> page-table chain, and no
- * separate top-k launch runs. Rotary gathers, page tables wider than 8192 entries (4096 for
- * bf16 with P 16) and k above 1024 run the two calls' launches instead; the outputs are the
- * same either way.
+ * separate top-k launch runs. Page tables wider than 8192 entries (4096 for bf16 with P 16) and
+ * k above 1024 run the two calls' launches instead; the outputs are the same either way.
  * sel_idx / sel_cnt: as kvsel_score_topk. out / lse: as kvsel_sparse_decode_attn. flags: as
  * kvsel_score_topk. ws / ws_bytes: kvsel_workspace_bytes(kv, k, KVSEL_OP_SELECT_ATTEND, 0).
  * [FreeKV] sections 1 and 2.1. */
@@ -224,25 +223,24 @@ kvsel_status kvsel_rope_shift(const kvsel_paged_kv* kv, const kvsel_rope* rope, 
 
 /* Speculative decode step: the outputs of kvsel_score_topk with `reuse` (required) followed by
  * kvsel_sparse_decode_attn over the used pages (reuse->used_idx / used_cnt) with the library's
- * default split, bit for bit, with the attention over the previous step's pages
- * (reuse->prev_idx / prev_cnt) overlapped with the selection: it is enqueued on side_stream
- * after fork_event is recorded on `stream`, while `stream` scores, selects and decides; then
- * `stream` waits on join_event (recorded on side_stream), attends again over the fresh pages of
- * the lists the decision corrected, and merges. With reuse->first_step every list is corrected
- * and the step runs serially on `stream` (the events and side stream are not used). Capturable
- * in a HIP graph when both streams take part in the capture.
- * side_stream: a stream other than `stream` (hipStream_t, non-NULL). fork_event / join_event:
- * hipEvent_t handles owned by the caller (timing may be disabled). sel_idx / sel_cnt must not
- * alias prev_idx / prev_cnt. ws / ws_bytes: kvsel_workspace_bytes(kv, k,
- * KVSEL_OP_SPECULATIVE_STEP, 0). Other arguments as kvsel_score_topk and kvsel_sparse_decode_attn.
+ * default split, bit for bit. The attention over the previous step's pages (reuse->prev_idx /
+ * prev_cnt), which does not depend on this step's selection, runs in the same launch as the page
+ * scoring and the reuse decision; the next launch selects, and re-attends only the lists the
+ * decision corrected, over their fresh pages; a last launch merges the splits. With
+ * reuse->first_step every list is corrected and no attention runs over the previous pages.
+ * Cases the fused selection of kvsel_select_attend does not cover run the two calls serially,
+ * with the same outputs. One stream; capturable in a HIP graph.
+ * sel_idx / sel_cnt and reuse->used_idx / used_cnt must not alias reuse->prev_idx / prev_cnt.
+ * ws / ws_bytes: kvsel_workspace_bytes(kv, k, KVSEL_OP_SPECULATIVE_STEP, 0). Other arguments as
+ * kvsel_score_topk and kvsel_sparse_decode_attn.
  * [FreeKV] section 2.1 (speculative retrieval: attention at step i over the pages chosen at step
  * i-1, overlapped with the selection; fine-grained correction when the group-mean similarity is
  * below tau). */
 kvsel_status kvsel_speculative_step(const kvsel_paged_kv* kv, const kvsel_rope* rope, void* summ,
                                     const void* q, int32_t k, int32_t flags, float scale,
                                     const kvsel_reuse* reuse, int32_t* sel_idx, int32_t* sel_cnt,
-                                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream,
-                                    void* side_stream, void* fork_event, void* join_event);
+                                    void* out, float* lse, void* ws, size_t ws_bytes,
+                                    void* stream);
 
 /* Device-side check of the contents every other entry point takes on trust (the host cannot
  * read device memory before enqueuing): ORs into *flags (device uint32, sticky: bits are set,

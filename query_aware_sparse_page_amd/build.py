@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvsel.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["summaries.hip", "score_topk.hip", "attention.hip", "rope.hip", "probe.hip", "check.hip", "kvsel_abi.hip"]
+SOURCES = ["summaries.hip", "score_topk.hip", "attention.hip", "select_attend.hip", "speculative.hip",
+           "rope.hip", "probe.hip", "check.hip", "kvsel_abi.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -1,560 +1,20 @@
-// Sparse paged decode attention on the matrix cores: split-K over the selected pages, then a
-// log-sum-exp merge of the splits in a second launch.
-//
-// Work unit: a "tile" of TT token slots (TT = 32 for bf16, 16 for fp32) taken in order from the
-// concatenated selected pages of one list (= sequence, KV head). Grid: one block per
-// (KV head, sequence, split) in a 3-D grid, KV head varying fastest, so that all splits of a list
-// are placed on one XCD by the round-robin block placement when the number of lists is a multiple
-// of 8, and no block index needs an integer division. A block has WAVES
-// waves; each wave owns TPW consecutive tiles, issues every K and V load of its tiles first,
-// then runs the contractions on MFMA with the GQA group of query heads as the M dimension
-// (rows >= G are zero and ignored):
-//
-//  bf16 (v_mfma_f32_16x16x32_bf16; lane l: r16 = l % 16, q4 = l / 16):
-//   S^T = K q^T per 16-token half h: A = K rows (16 tokens x 32 channels), B = q^T (32 channels x
-//   16 heads). Row r of half h is token 8*(r/4) + 4h + r%4 of the tile, so after both halves
-//   lane l holds the scores of head r16 for the 8 consecutive tokens 8*q4 .. 8*q4+7 -- exactly
-//   the A operand of O = P V (16 heads x 32 tokens), with no data movement between lanes.
-//   B = V (32 tokens x 16 channels) wants 8 consecutive tokens of one channel per lane: V pages
-//   are stored channel-major ([D][P]), so that is one 16-byte load.
-//  fp32 (v_mfma_f32_16x16x4f32): the same shape with 4-deep steps; step s of q K^T takes channel
-//   (D/4)*q4 + s (a lane's 16-byte K loads cover its channels), step s of P V takes token
-//   4*q4 + s (a lane's 16-byte V load covers its tokens).
-//
-// Softmax: per wave a two-pass max / exp over its tiles (the max needs 2 cross-lane steps),
-// l accumulated per lane, O accumulated in the MFMA accumulators; the waves of a block merge
-// through LDS. One split: the block writes out / lse directly. Otherwise it writes its
-// (acc[G][D], m, l) partial and attn_merge_kernel (one block per list) combines the partials in
-// split order: M = max m_s, out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
-// Invalid token slots (past a sequence's end, or past the list's count) load as zeros and get
-// probability 0, so poisoned padding never reaches the accumulators.
-#include <math.h>
-
-#include "kvsel_device.h"
-#include "kvsel_internal.h"
-#include "kvsel_topk.h"
+// Sparse paged decode attention: the split launch over the selected pages (one block per
+// (KV head, sequence, split), body attn_bf16_block / attn_f32_block) and the log-sum-exp merge
+// of the splits in a second launch. The kernel design (tiles, MFMA layouts, softmax, partials)
+// is described in kvsel_attn.h.
+#include "kvsel_attn.h"
 
 namespace kvsel {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int ATT_MAX_SPLITS = 256;
-
-struct AttnArgs {
-  const void* k_pool;
-  const void* v_pool;   // channel-major pages: [Npp][Hkv][D][P]
-  const int32_t* page_table;
-  const int32_t* seq_lens;
-  const void* q;
-  const int32_t* sel_idx;
-  const int32_t* sel_cnt;
-  int Hkv, P, log2P, maxp, Npp, k, pps, nsplit, nlists;
-  float scale;
-  RopeArgs rope;
-  float* part_acc;   // [nlists][nsplit][G][D]
-  float2* part_ml;   // [nlists][nsplit][G]
-  void* out;
-  float* lse;
-  // fused selection only: the scores, and the selection outputs written by split 0
-  const float* scores;  // [nlists][maxp]
-  int32_t* sel_out;     // [nlists][k]
-  int32_t* cnt_out;     // [nlists]
-  // speculative step only: lists with only_lists[list] == 0 do nothing (nullable: all lists)
-  const uint8_t* only_lists;
-};
-
-constexpr int ATT_MAX_PPS = 16;  // pages per split of the fused-selection launches
-
-// Wave-uniform page lookup of the NPT pages a tile of TT token slots touches (NPT = 2 when a
-// 32-slot tile spans two 16-slot pages). The addresses follow the selection id and page-table
-// entry as read (an id out of range is clamped to a valid entry), and the list count only
-// decides validity, so the dependent chain is id -> page table -> K / V with every id load in one
-// round and every page-table load in the next.
-template <int P, int TT, int TPW>
-struct TilePages {
-  static constexpr int NPT = TT > P ? TT / P : 1;
-  int page[TPW][NPT];   // physical page to address (always a valid page)
-  int valid[TPW][NPT];  // valid slots of that page; 0 when the slot range is not in the list
-};
-
-template <int P, int TT, int TPW>
-__device__ __forceinline__ void lookup_tiles(const AttnArgs& a, int list, int b, int split,
-                                             int first_tile, TilePages<P, TT, TPW>& tp) {
-  constexpr int NPT = TilePages<P, TT, TPW>::NPT;
-  int n[TPW][NPT];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int u = 0; u < NPT; ++u) {
-      const int sp = split * a.pps + ((first_tile + t) * TT) / P + u;
-      n[t][u] = sp < a.k ? __builtin_amdgcn_readfirstlane(a.sel_idx[(size_t)list * a.k + sp]) : -1;
-    }
-  const int cnt = __builtin_amdgcn_readfirstlane(min(a.sel_cnt[list], a.k));
-  const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int u = 0; u < NPT; ++u) {
-      const int nn = n[t][u];
-      const bool in_range = nn >= 0 && nn < a.maxp;
-      // an entry outside the list may hold anything: clamp it into the pool before addressing
-      const int pg = __builtin_amdgcn_readfirstlane(a.page_table[(size_t)b * a.maxp + (in_range ? nn : 0)]);
-      tp.page[t][u] = min(max(pg, 0), a.Npp - 1);
-      const int sp = split * a.pps + ((first_tile + t) * TT) / P + u;
-      tp.valid[t][u] = (in_range && sp < cnt) ? min(P, L - nn * P) : 0;
-    }
-}
-
-// Fused selection (kvsel_select_attend): every block of a list re-derives the list's top-k from
-// the page scores with the block-wide radix select and keeps the pages of its own split. The
-// scores and the page-table row are loaded together, so the K / V loads follow one memory round
-// trip and the select, instead of the selection ids -> page table -> K / V chain. The block of
-// split 0 also writes the selection outputs.
-template <int NT>
-struct SplitSelectSmem {
-  RadixSmem<NT> r;
-  int page[ATT_MAX_PPS];   // physical page at each of the split's positions
-  int valid[ATT_MAX_PPS];  // its valid slots (0: nothing selected at that position)
-};
-
-template <int P, int TT, int TPW, int NT, int C>
-__device__ __forceinline__ void select_tiles(const AttnArgs& a, int list, int b, int split,
-                                             int first_tile, TilePages<P, TT, TPW>& tp,
-                                             SplitSelectSmem<NT>& ss) {
-  constexpr int NPT = TilePages<P, TT, TPW>::NPT;
-  const int tid = threadIdx.x;
-  const float* sc = a.scores + (size_t)list * a.maxp;
-  const int32_t* row = a.page_table + (size_t)b * a.maxp;
-  float v[C];
-  int pt[C];
-#pragma unroll
-  for (int u = 0; u < C; ++u) {  // indices from the row width only: no wait for seq_lens
-    const int i = min(tid * C + u, a.maxp - 1);
-    v[u] = sc[i];
-    pt[u] = row[i];
-  }
-  const int L = a.seq_lens[b];
-  const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;
-  if (tid < a.pps) {
-    ss.page[tid] = 0;
-    ss.valid[tid] = 0;
-  }
-  uint32_t key[C];
-#pragma unroll
-  for (int u = 0; u < C; ++u) key[u] = score_key(v[u]);
-  __syncthreads();  // positions cleared before any is filled
-  const int first = split * a.pps;
-  const bool writer = split == 0 && a.sel_out != nullptr;
-  int32_t* out = a.sel_out + (size_t)list * a.k;
-  block_topk_regs<NT, C>(key, N, a.k, ss.r, [&](int pos, int i, int u) {
-    if (writer) out[pos] = i;
-    const int sp = pos - first;
-    if (sp >= 0 && sp < a.pps) {
-      ss.page[sp] = min(max(pt[u], 0), a.Npp - 1);  // any table value stays inside the pool
-      ss.valid[sp] = min(P, L - i * P);
-    }
-  });
-  if (writer) {
-    const int cnt = min(N, a.k);
-    for (int i = cnt + tid; i < a.k; i += NT) out[i] = -1;
-    if (tid == 0) a.cnt_out[list] = cnt;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int u = 0; u < NPT; ++u) {
-      const int sp = ((first_tile + t) * TT) / P + u;
-      tp.page[t][u] = __builtin_amdgcn_readfirstlane(ss.page[sp]);
-      tp.valid[t][u] = __builtin_amdgcn_readfirstlane(ss.valid[sp]);
-    }
-}
-
-// Rotate-half rotation of one channel pair held by the same lane (bits identical to
-// rope_rotate_slice).
-template <typename T>
-__device__ __forceinline__ void rope_pair(float& x1, float& x2, float c, float s) {
-  const float y1 = rot_sub(rot_mul(x1, c), rot_mul(x2, s));
-  const float y2 = rot_add(rot_mul(x2, c), rot_mul(x1, s));
-  x1 = round_to_elem<T>(y1);
-  x2 = round_to_elem<T>(y2);
-}
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
-  bf16x8_t r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
-}
-
-__device__ __forceinline__ uint4 pack_bf16x8(const float* f) { return pack<bf16_t>(f); }
-
-// Zero the bf16 elements e of v whose bit e of `keep` is clear (invalid token slots).
-__device__ __forceinline__ uint4 mask_bf16x8(const uint4& v, int keep) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] &= ((keep >> (2 * i)) & 1 ? 0x0000ffffu : 0u) | ((keep >> (2 * i + 1)) & 1 ? 0xffff0000u : 0u);
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-// Zero the fp32 elements e of v whose bit e of `keep` is clear.
-__device__ __forceinline__ uint4 mask_f32x4(const uint4& v, int keep) {
-  return make_uint4((keep & 1) ? v.x : 0u, (keep & 2) ? v.y : 0u, (keep & 4) ? v.z : 0u,
-                    (keep & 8) ? v.w : 0u);
-}
-
-constexpr int ATT_MAX_G = 8;
-
-// Block-level merge of the waves' (m, l, O) and the write of the block's result.
-template <typename T, int D, int WAVES>
-__device__ __forceinline__ void finish_block(const AttnArgs& a, int G, int list, int split, int b,
-                                             int j, float (*s_m)[ATT_MAX_G],
-                                             float (*s_l)[ATT_MAX_G],
-                                             float (*s_o)[ATT_MAX_G][D]) {
-  const float NEG_INF = __int_as_float(0xff800000);
-  const int Hq = a.Hkv * G;
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += WAVES * 64) {
-    const int g = idx / D, d = idx % D;
-    float Mx = s_m[0][g];
-#pragma unroll
-    for (int v = 1; v < WAVES; ++v) Mx = fmaxf(Mx, s_m[v][g]);
-    float Ls = 0.0f, A = 0.0f;
-    if (Mx != NEG_INF) {
-#pragma unroll
-      for (int v = 0; v < WAVES; ++v) {
-        if (s_m[v][g] != NEG_INF) {
-          const float f = __expf(s_m[v][g] - Mx);
-          Ls = fmaf(s_l[v][g], f, Ls);
-          A = fmaf(s_o[v][g][d], f, A);
-        }
-      }
-    }
-    if (a.nsplit == 1) {
-      const size_t o = ((size_t)b * Hq + j * G + g) * D + d;
-      store_elem<T>((T*)a.out, o, Mx == NEG_INF ? 0.0f : A / Ls);
-      if (d == 0 && a.lse)
-        a.lse[(size_t)b * Hq + j * G + g] = Mx == NEG_INF ? NEG_INF : Mx + logf(Ls);
-    } else {
-      const size_t ps = ((size_t)list * a.nsplit + split) * G + g;
-      a.part_acc[ps * D + d] = A;
-      if (d == 0) a.part_ml[ps] = make_float2(Mx, Ls);
-    }
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// bf16
-// ------------------------------------------------------------------------------------------
-// SEL_C > 0: fused selection with SEL_C score keys per thread (select_tiles).
-template <int D, int P, int WAVES, int TPW, bool ROPE, int SEL_C = 0>
+template <int D, int P, int WAVES, int TPW, bool ROPE>
 __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a, int G) {
-  constexpr int TT = 32;       // tokens per tile
-  constexpr int CB = D / 32;   // 32-channel blocks of q K^T
-  constexpr int VB = D / 16;   // 16-channel blocks of P V
-  using TP = TilePages<P, TT, TPW>;
-  const float NEG_INF = __int_as_float(0xff800000);
-  const int j = blockIdx.x, b = blockIdx.y, split = blockIdx.z;  // grid (Hkv, B, splits)
-  const int list = b * a.Hkv + j;
-  if (a.only_lists && !a.only_lists[list]) return;  // whole block: before any barrier
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r16 = lane & 15, q4 = lane >> 4;
-  const int Hq = a.Hkv * G;
-  const bf16_t* kp = (const bf16_t*)a.k_pool;
-  const bf16_t* vp = (const bf16_t*)a.v_pool;
-
-  // q^T operand (independent of the selection): q[head r16][32 cb + 8 q4 .. +8], zero rows >= G
-  // (loads below are unconditional, from clamped valid addresses, and masked where used: a
-  // conditional load makes the compiler wait for it before issuing the next one)
-  uint4 qraw[CB];
-  {
-    const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)b * Hq + j * G + min(r16, G - 1)) * D + 8 * q4;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) qraw[cb] = load16(qrow + 32 * cb);
-  }
-
-  TP tp;
-  if constexpr (SEL_C > 0) {
-    __shared__ SplitSelectSmem<WAVES * 64> ss;
-    select_tiles<P, TT, TPW, WAVES * 64, SEL_C>(a, list, b, split, w * TPW, tp, ss);
-  } else {
-    lookup_tiles<P, TT, TPW>(a, list, b, split, w * TPW, tp);
-  }
-
-  // ---- every K / V load of this wave's tiles ----
-  uint4 kraw[TPW][2][CB], vraw[TPW][VB];
-  int vmask[TPW];  // bit e set: token 8*q4 + e of the tile is valid
-  int krow[TPW][2];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int x = 8 * (r16 / 4) + 4 * h + (r16 % 4);  // token of row r16 in half h
-      const int u = x / P, slot = x % P;
-      const int pg = tp.page[t][u];
-      // an invalid token's row of S^T is masked to -inf below (rows of an MFMA are
-      // independent), so its K needs no zeroing
-      const bf16_t* row = kp + (((size_t)pg * a.Hkv + j) * P + slot) * D + 8 * q4;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) kraw[t][h][cb] = load16(row + 32 * cb);
-      if (ROPE) {
-        const int pr = a.rope.page_row[pg];
-        krow[t][h] = pr < 0 ? -1 : pr + a.rope.row_step * slot;
-      }
-    }
-    const int xv = 8 * q4;  // first of the lane's 8 value tokens
-    const int u = xv / P, slot = xv % P;
-    const int pg = tp.page[t][u];
-    int m = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) m |= (slot + e < tp.valid[t][u]) ? (1 << e) : 0;
-    vmask[t] = m;
-    const bf16_t* vt = vp + ((size_t)pg * a.Hkv + j) * D * P + slot + (size_t)r16 * P;
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = load16(vt + (size_t)(16 * vb) * P);
-  }
-  __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use
-
-  // ---- S^T = K q^T ----
-  f32x4_t s[TPW][2];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (ROPE) {
-        // rotate-half pairs (c, c + D/2) sit in blocks cb and cb + CB/2 of the same lane
-        const int row = krow[t][h];
-        if (row >= 0) {
-#pragma unroll
-          for (int cb = 0; cb < CB / 2; ++cb) {
-            float x1[8], x2[8];
-            unpack<bf16_t>(kraw[t][h][cb], x1);
-            unpack<bf16_t>(kraw[t][h][cb + CB / 2], x2);
-            const float* cr = a.rope.cos + (size_t)row * (D / 2) + 32 * cb + 8 * q4;
-            const float* sr = a.rope.sin + (size_t)row * (D / 2) + 32 * cb + 8 * q4;  // row >= 0 here
-            float cv[8], sv[8];
-            unpack<float>(load16(cr), cv);
-            unpack<float>(load16(cr + 4), cv + 4);
-            unpack<float>(load16(sr), sv);
-            unpack<float>(load16(sr + 4), sv + 4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) rope_pair<bf16_t>(x1[e], x2[e], cv[e], sv[e]);
-            kraw[t][h][cb] = pack_bf16x8(x1);
-            kraw[t][h][cb + CB / 2] = pack_bf16x8(x2);
-          }
-        }
-      }
-      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kraw[t][h][cb]), as_bf16x8(qraw[cb]),
-                                                      acc, 0, 0, 0);
-      s[t][h] = acc;
-    }
-  }
-
-  // ---- softmax over the wave's tokens (head r16; tokens 8*q4 + 4h + i of each tile) ----
-  float z[TPW][8];
-  float m = NEG_INF;
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = s[t][e >> 2][e & 3] * a.scale;
-      z[t][e] = ((vmask[t] >> e) & 1) && r16 < G ? v : NEG_INF;
-      m = fmaxf(m, z[t][e]);
-    }
-  m = fmaxf(m, xor16_f32(m));
-  m = fmaxf(m, xor32_f32(m));
-  float l = 0.0f;
-  f32x4_t o[VB];
-#pragma unroll
-  for (int vb = 0; vb < VB; ++vb) o[vb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    float p[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // P enters the MFMA as bf16: normalize by the sum of the rounded values, so the weights
-      // applied to V sum to one exactly
-      p[e] = z[t][e] == NEG_INF ? 0.0f : round_to_elem<bf16_t>(__expf(z[t][e] - m));
-      l += p[e];
-    }
-    const bf16x8_t pa = as_bf16x8(pack_bf16x8(p));
-    const bool partial = vmask[t] != 0xff;  // zero invalid slots (0 * NaN poison is NaN)
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb) {
-      const uint4 vv = partial ? mask_bf16x8(vraw[t][vb], vmask[t]) : vraw[t][vb];
-      o[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(vv), o[vb], 0, 0, 0);
-    }
-  }
-  l += xor16_f32(l);
-  l += xor32_f32(l);
-
-  // ---- merge the block's waves through LDS ----
-  __shared__ float s_m[WAVES][ATT_MAX_G], s_l[WAVES][ATT_MAX_G];
-  __shared__ float s_o[WAVES][ATT_MAX_G][D];
-  if (q4 == 0 && r16 < G) {
-    s_m[w][r16] = m;
-    s_l[w][r16] = l;
-  }
-  if (4 * q4 < G) {  // lanes holding rows (heads) 4*q4 .. 4*q4+3
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_o[w][4 * q4 + i][16 * vb + r16] = o[vb][i];
-  }
-  finish_block<bf16_t, D, WAVES>(a, G, list, split, b, j, s_m, s_l, s_o);
+  // grid (Hkv, B, splits)
+  attn_bf16_block<D, P, WAVES, TPW, ROPE>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// ------------------------------------------------------------------------------------------
-// fp32
-// ------------------------------------------------------------------------------------------
-template <int D, int P, int WAVES, int TPW, bool ROPE, int SEL_C = 0>
+template <int D, int P, int WAVES, int TPW, bool ROPE>
 __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(AttnArgs a, int G) {
-  constexpr int TT = 16;       // tokens per tile
-  constexpr int KC = D / 4;    // channels per lane in q K^T (4 lane groups)
-  constexpr int KL = KC / 4;   // 16-byte loads per lane per token
-  constexpr int VB = D / 16;   // 16-channel blocks of P V
-  using TP = TilePages<P, TT, TPW>;
-  const float NEG_INF = __int_as_float(0xff800000);
-  const int j = blockIdx.x, b = blockIdx.y, split = blockIdx.z;  // grid (Hkv, B, splits)
-  const int list = b * a.Hkv + j;
-  if (a.only_lists && !a.only_lists[list]) return;  // whole block: before any barrier
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r16 = lane & 15, q4 = lane >> 4;
-  const int Hq = a.Hkv * G;
-  const float* kp = (const float*)a.k_pool;
-  const float* vp = (const float*)a.v_pool;
-
-  float qv[KC];
-  {
-    // unconditional loads from clamped addresses, masked where used (see the bf16 kernel)
-    const float* qrow = (const float*)a.q + ((size_t)b * Hq + j * G + min(r16, G - 1)) * D + KC * q4;
-#pragma unroll
-    for (int u = 0; u < KL; ++u) unpack<float>(load16(qrow + 4 * u), qv + 4 * u);
-    if (r16 >= G) {
-#pragma unroll
-      for (int c = 0; c < KC; ++c) qv[c] = 0.0f;
-    }
-  }
-  TP tp;
-  if constexpr (SEL_C > 0) {
-    __shared__ SplitSelectSmem<WAVES * 64> ss;
-    select_tiles<P, TT, TPW, WAVES * 64, SEL_C>(a, list, b, split, w * TPW, tp, ss);
-  } else {
-    lookup_tiles<P, TT, TPW>(a, list, b, split, w * TPW, tp);
-  }
-
-  uint4 kraw[TPW][KL], vraw[TPW][VB];
-  int vmask[TPW];
-  int krow[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int tile = w * TPW + t;
-    const int base = (tile * TT) % P;  // first slot of the tile within its page
-    const int pg = tp.page[t][0];
-    const int slot = base + r16;
-    const float* row = kp + (((size_t)pg * a.Hkv + j) * P + slot) * D + KC * q4;
-#pragma unroll
-    for (int u = 0; u < KL; ++u) kraw[t][u] = load16(row + 4 * u);
-    if (ROPE) {
-      const int pr = a.rope.page_row[pg];
-      krow[t] = pr < 0 ? -1 : pr + a.rope.row_step * slot;
-    }
-    const int vslot = base + 4 * q4;
-    int mk = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) mk |= (vslot + e < tp.valid[t][0]) ? (1 << e) : 0;
-    vmask[t] = mk;
-    const float* vt = vp + ((size_t)pg * a.Hkv + j) * D * P + vslot + (size_t)r16 * P;
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = load16(vt + (size_t)(16 * vb) * P);
-  }
-  __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use
-
-  f32x4_t s[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    float kv[KC];
-#pragma unroll
-    for (int u = 0; u < KL; ++u) unpack<float>(kraw[t][u], kv + 4 * u);
-    if (ROPE) {
-      // rotate-half partner of channel c (lane group q4) is in lane group q4 ^ 2; every lane
-      // group of token r16 computed the same table row
-      const int row = krow[t];
-      float pv[KC];
-#pragma unroll
-      for (int e = 0; e < KC; ++e) pv[e] = __shfl_xor(kv[e], 32);
-      if (row >= 0) {
-        const bool first = q4 < 2;
-        const int i0 = first ? KC * q4 : KC * q4 - D / 2;
-        const float* cr = a.rope.cos + (size_t)row * (D / 2) + i0;
-        const float* sr = a.rope.sin + (size_t)row * (D / 2) + i0;
-#pragma unroll
-        for (int e = 0; e < KC; ++e) {
-          float x1 = first ? kv[e] : pv[e], x2 = first ? pv[e] : kv[e];
-          rope_pair<float>(x1, x2, cr[e], sr[e]);
-          kv[e] = first ? x1 : x2;
-        }
-      }
-    }
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int c = 0; c < KC; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[c], qv[c], acc, 0, 0, 0);
-    s[t] = acc;
-  }
-  float z[TPW][4];
-  float m = NEG_INF;
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float v = s[t][i] * a.scale;
-      z[t][i] = ((vmask[t] >> i) & 1) && r16 < G ? v : NEG_INF;
-      m = fmaxf(m, z[t][i]);
-    }
-  m = fmaxf(m, xor16_f32(m));
-  m = fmaxf(m, xor32_f32(m));
-  float l = 0.0f;
-  f32x4_t o[VB];
-#pragma unroll
-  for (int vb = 0; vb < VB; ++vb) o[vb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = z[t][i] == NEG_INF ? 0.0f : __expf(z[t][i] - m);
-      l += p[i];
-    }
-    const bool partial = vmask[t] != 0xf;
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb) {
-      float vv[4];
-      unpack<float>(partial ? mask_f32x4(vraw[t][vb], vmask[t]) : vraw[t][vb], vv);
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        o[vb] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[st], vv[st], o[vb], 0, 0, 0);
-    }
-  }
-  l += xor16_f32(l);
-  l += xor32_f32(l);
-
-  __shared__ float s_m[WAVES][ATT_MAX_G], s_l[WAVES][ATT_MAX_G];
-  __shared__ float s_o[WAVES][ATT_MAX_G][D];
-  if (q4 == 0 && r16 < G) {
-    s_m[w][r16] = m;
-    s_l[w][r16] = l;
-  }
-  if (4 * q4 < G) {
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_o[w][4 * q4 + i][16 * vb + r16] = o[vb][i];
-  }
-  finish_block<float, D, WAVES>(a, G, list, split, b, j, s_m, s_l, s_o);
+  attn_f32_block<D, P, WAVES, TPW, ROPE>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -657,8 +117,6 @@ int attention_pages_per_split(const LaunchKV& kv, int k, int requested) {
   return pps;
 }
 
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 size_t attention_workspace(const LaunchKV& kv, int k, int pages_per_split) {
   const int pps = attention_pages_per_split(kv, k, pages_per_split);
   if (pps <= 0) return 0;
@@ -719,9 +177,9 @@ static hipError_t launch_parts(const LaunchKV& kv, const AttnArgs& a, bool rope,
   return launch_p<bf16_t, 128>(kv.P, tiles, a, kv.G, rope, parts, stream);
 }
 
-static AttnArgs attn_args(const LaunchKV& kv, const RopeArgs& rope, const void* q,
-                          const int32_t* sel_idx, const int32_t* sel_cnt, int k, float scale,
-                          int pps, void* out, float* lse, void* ws) {
+AttnArgs attn_args(const LaunchKV& kv, const RopeArgs& rope, const void* q, const int32_t* sel_idx,
+                   const int32_t* sel_cnt, int k, float scale, int pps, void* out, float* lse,
+                   void* ws) {
   AttnArgs a;
   a.k_pool = kv.k_pool;
   a.v_pool = kv.v_pool;
@@ -753,7 +211,7 @@ static AttnArgs attn_args(const LaunchKV& kv, const RopeArgs& rope, const void* 
   a.scores = nullptr;
   a.sel_out = nullptr;
   a.cnt_out = nullptr;
-  a.only_lists = nullptr;
+  a.reuse = ReuseArgs{};
   return a;
 }
 
@@ -766,140 +224,8 @@ hipError_t launch_attention(const LaunchKV& kv, const RopeArgs& rope, const void
   return launch_parts(kv, a, rope.page_row != nullptr, 3, stream);
 }
 
-// ------------------------------------------------------------------------------------------
-// Speculative decode step ([FreeKV] section 2.1: step t attends over step t-1's pages unless the
-// group-mean query similarity falls below tau). The attention over the previous pages does not
-// depend on this step's selection, so it runs on a side stream while the main stream scores,
-// selects and decides; after the join, the lists the decision corrected are attended again over
-// their fresh pages (the split launch with a list mask: the other lists' blocks exit at once),
-// overwriting their partials, and one merge finishes every list. The outputs are those of
-// kvsel_score_topk with reuse followed by kvsel_sparse_decode_attn over the used pages, bit for
-// bit: every list's partials come from the same split kernel over the same pages.
-// ------------------------------------------------------------------------------------------
-hipError_t launch_speculative_step(const LaunchKV& kv, const RopeArgs& rope, void* summ,
-                                   const void* q, int k, int flags, float scale,
-                                   const ReuseArgs& reuse, int32_t* sel_idx, int32_t* sel_cnt,
-                                   void* out, float* lse, void* ws, hipStream_t stream,
-                                   hipStream_t side, hipEvent_t fork, hipEvent_t join) {
-  float* scores = (float*)ws;
-  void* attn_ws = (char*)ws + align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float));
-  const int pps = attention_pages_per_split(kv, k, 0);
-  const bool r = rope.page_row != nullptr;
-  if (reuse.first_step) {  // every list is corrected: the plain serial step
-    hipError_t e = launch_score_topk(kv, rope, summ, q, k, flags, sel_idx, sel_cnt, scores, false,
-                                     reuse, stream);
-    if (e != hipSuccess) return e;
-    return launch_attention(kv, rope, q, reuse.used_idx, reuse.used_cnt, k, scale, 0, out, lse,
-                            attn_ws, stream);
-  }
-  hipError_t e = hipEventRecord(fork, stream);
-  if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
-  if (e != hipSuccess) return e;
-  // side stream: the previous step's pages (split launch only)
-  const AttnArgs spec =
-      attn_args(kv, rope, q, reuse.prev_idx, reuse.prev_cnt, k, scale, pps, out, lse, attn_ws);
-  if ((e = launch_parts(kv, spec, r, 1, side)) != hipSuccess) return e;
-  // main stream: scores, top-k, reuse decision
-  e = launch_score_topk(kv, rope, summ, q, k, flags, sel_idx, sel_cnt, scores, false, reuse,
-                        stream);
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(join, side);
-  if (e == hipSuccess) e = hipStreamWaitEvent(stream, join, 0);
-  if (e != hipSuccess) return e;
-  // corrected lists again over their fresh pages, then the merge of every list
-  AttnArgs fix =
-      attn_args(kv, rope, q, reuse.used_idx, reuse.used_cnt, k, scale, pps, out, lse, attn_ws);
-  fix.only_lists = reuse.corrected;
-  return launch_parts(kv, fix, r, 3, stream);
-}
-
-// ------------------------------------------------------------------------------------------
-// kvsel_select_attend: scores (score kernel), then the attention launch with the selection
-// fused in (select_tiles), then the merge. The fused launch uses the default split of
-// FUSED_PPS pages, whose block shape depends only on the dtype and page size:
-//   bf16, P 32: 4 waves x 1 tile   bf16, P 16: 2 waves x 1 tile
-//   fp32, P 32: 4 waves x 2 tiles  fp32, P 16: 4 waves x 1 tile
-// Other cases (a rotary gather, a table too wide for the register-resident select, a k that
-// needs larger splits) run the two separate calls' launches instead.
-// ------------------------------------------------------------------------------------------
-constexpr int FUSED_PPS = 4;
-
-template <typename T, int P>
-struct FusedShape {
-  static constexpr int WAVES = (sizeof(T) == 2 && P == 16) ? 2 : 4;
-  static constexpr int TPW = (sizeof(T) == 4 && P == 32) ? 2 : 1;
-};
-
-static int fused_keys_per_thread(const LaunchKV& kv) {
-  const int nt = (kv.dtype == 1 && kv.P == 16) ? 128 : 256;
-  const int c = (kv.maxp + nt - 1) / nt;
-  return c <= 1 ? 1 : c <= 4 ? 4 : c <= 16 ? 16 : c <= 32 ? 32 : 0;
-}
-
-bool select_attend_fused(const LaunchKV& kv, const RopeArgs& rope, int k) {
-  return rope.page_row == nullptr && fused_keys_per_thread(kv) > 0 &&
-         attention_pages_per_split(kv, k, 0) == FUSED_PPS;
-}
-
-template <typename T, int D, int P, int C>
-static void launch_fused_c(const AttnArgs& a, int G, hipStream_t stream) {
-  using S = FusedShape<T, P>;
-  const dim3 grid(a.Hkv, a.nlists / a.Hkv, a.nsplit);
-  const dim3 block(S::WAVES * 64);
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, P, S::WAVES, S::TPW, false, C>), grid, block, 0, stream, a, G);
-  else
-    hipLaunchKernelGGL((attn_f32_kernel<D, P, S::WAVES, S::TPW, false, C>), grid, block, 0, stream, a, G);
-}
-
-template <typename T, int D, int P>
-static hipError_t launch_fused(int c, const AttnArgs& a, int G, hipStream_t stream) {
-  switch (c) {
-    case 1: launch_fused_c<T, D, P, 1>(a, G, stream); break;
-    case 4: launch_fused_c<T, D, P, 4>(a, G, stream); break;
-    case 16: launch_fused_c<T, D, P, 16>(a, G, stream); break;
-    default: launch_fused_c<T, D, P, 32>(a, G, stream); break;
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(a.Hkv, G, a.nlists / a.Hkv), dim3(D), 0, stream,
-                     a, G);
-  return hipGetLastError();
-}
-
-size_t select_attend_workspace(const LaunchKV& kv, int k) {
-  return align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float)) + attention_workspace(kv, k, 0);
-}
-
-hipError_t launch_select_attend(const LaunchKV& kv, const RopeArgs& rope, void* summ,
-                                const void* q, int k, int flags, float scale, int32_t* sel_idx,
-                                int32_t* sel_cnt, void* out, float* lse, void* ws,
-                                hipStream_t stream) {
-  float* scores = (float*)ws;
-  void* attn_ws = (char*)ws + align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float));
-  if (!select_attend_fused(kv, rope, k)) {
-    hipError_t e = launch_score_topk(kv, rope, summ, q, k, flags, sel_idx, sel_cnt, scores, false,
-                                     ReuseArgs{}, stream);
-    if (e != hipSuccess) return e;
-    return launch_attention(kv, rope, q, sel_idx, sel_cnt, k, scale, 0, out, lse, attn_ws, stream);
-  }
-  hipError_t e = launch_scores(kv, rope, summ, q, flags, scores, stream);
-  if (e != hipSuccess) return e;
-  AttnArgs a = attn_args(kv, rope, q, nullptr, nullptr, k, scale, FUSED_PPS, out, lse, attn_ws);
-  a.scores = scores;
-  a.sel_out = sel_idx;
-  a.cnt_out = sel_cnt;
-  const int c = fused_keys_per_thread(kv);
-  if (kv.dtype == 0) {
-    if (kv.D == 64) return kv.P == 16 ? launch_fused<float, 64, 16>(c, a, kv.G, stream)
-                                      : launch_fused<float, 64, 32>(c, a, kv.G, stream);
-    return kv.P == 16 ? launch_fused<float, 128, 16>(c, a, kv.G, stream)
-                      : launch_fused<float, 128, 32>(c, a, kv.G, stream);
-  }
-  if (kv.D == 64) return kv.P == 16 ? launch_fused<bf16_t, 64, 16>(c, a, kv.G, stream)
-                                    : launch_fused<bf16_t, 64, 32>(c, a, kv.G, stream);
-  return kv.P == 16 ? launch_fused<bf16_t, 128, 16>(c, a, kv.G, stream)
-                    : launch_fused<bf16_t, 128, 32>(c, a, kv.G, stream);
+hipError_t launch_merge(const LaunchKV& kv, const AttnArgs& a, hipStream_t stream) {
+  return launch_parts(kv, a, false, 2, stream);
 }
 
 }  // namespace kvsel

@@ -212,8 +212,7 @@ kvsel_status kvsel_select_attend(const kvsel_paged_kv* kv, const kvsel_rope* rop
 kvsel_status kvsel_speculative_step(const kvsel_paged_kv* kv, const kvsel_rope* rope, void* summ,
                                     const void* q, int32_t k, int32_t flags, float scale,
                                     const kvsel_reuse* reuse, int32_t* sel_idx, int32_t* sel_cnt,
-                                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream,
-                                    void* side_stream, void* fork_event, void* join_event) {
+                                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   LaunchKV f;
   RopeArgs r;
   kvsel_status st = flatten(kv, 3, &f);
@@ -221,8 +220,6 @@ kvsel_status kvsel_speculative_step(const kvsel_paged_kv* kv, const kvsel_rope* 
   if (!summ || !q || !sel_idx || !sel_cnt || !out || k < 1 || !reuse) return KVSEL_ERR_INVALID_ARGUMENT;
   if (!reuse->q_prev || !reuse->prev_idx || !reuse->prev_cnt || !reuse->used_idx ||
       !reuse->used_cnt || !reuse->corrected)
-    return KVSEL_ERR_INVALID_ARGUMENT;
-  if (!side_stream || side_stream == stream || !fork_event || !join_event)
     return KVSEL_ERR_INVALID_ARGUMENT;
   if (flags & ~KVSEL_SCORE_REFRESH_TAIL) return KVSEL_ERR_INVALID_ARGUMENT;
   if ((st = flatten_rope(rope, &r)) != KVSEL_OK) return st;
@@ -241,9 +238,7 @@ kvsel_status kvsel_speculative_step(const kvsel_paged_kv* kv, const kvsel_rope* 
   ra.similarity = reuse->similarity;
   if ((st = check_device()) != KVSEL_OK) return st;
   return launch_status(launch_speculative_step(f, r, summ, q, k, flags, scale, ra, sel_idx,
-                                               sel_cnt, out, lse, ws, (hipStream_t)stream,
-                                               (hipStream_t)side_stream, (hipEvent_t)fork_event,
-                                               (hipEvent_t)join_event));
+                                               sel_cnt, out, lse, ws, (hipStream_t)stream));
 }
 
 kvsel_status kvsel_check_inputs(const kvsel_paged_kv* kv, const int32_t* sel_idx,

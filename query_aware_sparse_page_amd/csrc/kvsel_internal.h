@@ -67,13 +67,13 @@ hipError_t launch_select_attend(const LaunchKV& kv, const RopeArgs& rope, void* 
                                 int32_t* sel_cnt, void* out, float* lse, void* ws,
                                 hipStream_t stream);
 
-// The speculative step: attention over the previous pages on `side` while `stream` selects; the
-// corrected lists are attended again after the join. Workspace: select_attend_workspace bytes.
+// The speculative step: scoring, the reuse decision and the attention over the previous pages
+// in one launch, then the fused selection (corrected lists attended again) and the merge.
+// Workspace: select_attend_workspace bytes.
 hipError_t launch_speculative_step(const LaunchKV& kv, const RopeArgs& rope, void* summ,
                                    const void* q, int k, int flags, float scale,
                                    const ReuseArgs& reuse, int32_t* sel_idx, int32_t* sel_cnt,
-                                   void* out, float* lse, void* ws, hipStream_t stream,
-                                   hipStream_t side, hipEvent_t fork, hipEvent_t join);
+                                   void* out, float* lse, void* ws, hipStream_t stream);
 
 // Workspace of the attention for a given split size (bytes).
 size_t attention_workspace(const LaunchKV& kv, int k, int pages_per_split);

@@ -1,0 +1,202 @@
+// Page scoring shared by the selection kernels (score_topk.hip) and the speculative-step launch
+// that co-schedules scoring with attention (speculative.hip): the selection arguments, the
+// min / max of one key tile (the tail refresh), the score of a chunk of pages by one block, and
+// the group-mean query similarity of the speculative-reuse decision.
+#pragma once
+
+#include "kvsel_device.h"
+#include "kvsel_internal.h"
+
+namespace kvsel {
+
+struct SelectArgs {
+  const void* k_pool;
+  void* summ;
+  const void* q;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int Hkv, P, maxp, Npp, k, nlists, nchunks, refresh_tail, write_scores;
+  int scores_only;  // launch the score kernel alone (the fused selection + attention call)
+  RopeArgs rope;
+  float* scores;
+  int32_t* sel_idx;
+  int32_t* sel_cnt;
+  ReuseArgs reuse;
+};
+
+// Min / max of the valid rows (1 <= valid) of one (page, KV head) tile of physical page pt,
+// computed by one wave. On return every lane holds lo / hi of its channels [c0, c0 + VEC). The
+// row loads are unconditional (rows past `valid` re-read the last valid row and are ignored), so
+// they all go out at once; the page's rotary row is read after them.
+template <typename T, int D>
+__device__ __forceinline__ void tile_minmax(const T* tile, int valid, int P, int lane, int pt,
+                                            const RopeArgs& rope, float* lo, float* hi) {
+  using M = row_map<T, D>;
+  constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
+  constexpr int MAX_LOADS = 32 / RPW;
+  const int rg = lane / LPR;
+  const int c0 = (lane % LPR) * VEC;
+  uint4 raw[MAX_LOADS];
+#pragma unroll
+  for (int i = 0; i < MAX_LOADS; ++i) {
+    const int s = rg + i * RPW;
+    raw[i] = load16(tile + (size_t)min(s, valid - 1) * D + c0);
+  }
+  const int prow = rope.page_row ? rope.page_row[pt] : -1;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    lo[e] = __int_as_float(0x7f800000);
+    hi[e] = __int_as_float(0xff800000);
+  }
+#pragma unroll
+  for (int i = 0; i < MAX_LOADS; ++i) {
+    const int s = rg + i * RPW;
+    if (i * RPW >= P) break;
+    float x[VEC];
+    unpack<T>(raw[i], x);
+    if (rope.page_row)
+      rope_rotate_slice<T, D>(x, c0, prow < 0 ? -1 : prow + rope.row_step * s, rope.cos, rope.sin);
+    if (s < valid) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        lo[e] = fminf(lo[e], x[e]);
+        hi[e] = fmaxf(hi[e], x[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = LPR; m < 64; m <<= 1) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      lo[e] = fminf(lo[e], __shfl_xor(lo[e], m));
+      hi[e] = fmaxf(hi[e], __shfl_xor(hi[e], m));
+    }
+  }
+}
+
+// Scores of chunk `chunk` (WAVES * 64 / LPR consecutive pages) of list (sequence b, KV head j),
+// by one block of WAVES waves: LPR lanes read a page's lo and hi rows as 16-byte slices
+// (sequence-major summaries: one contiguous run per block), multiply by the group's query slice
+// in fp64 (a bf16 x bf16 or fp32 x fp32 product is exact in fp64), take q*hi for q >= 0 and
+// q*lo otherwise, and fold the LPR lanes; one fp64 -> fp32 rounding per score. With the tail
+// refresh on, the wave holding the sequence's last page first rebuilds that page's summary from
+// the key pool, writes it, and scores it from the fresh values.
+template <typename T, int D, int G, int WAVES>
+__device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, int chunk) {
+  using M = row_map<T, D>;
+  constexpr int VEC = M::VEC, LPR = M::LPR;
+  constexpr int PPW = 64 / LPR;          // pages per wave
+  constexpr int PPB = WAVES * PPW;       // pages per block
+
+  const int list = b * a.Hkv + j;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = a.P;
+  const int n0 = chunk * PPB;
+  const int Hq = a.Hkv * G;
+  const T* q = (const T*)a.q;
+  const int c0 = (lane % LPR) * VEC;
+  const int n = n0 + w * PPW + lane / LPR;
+
+  // ---- loads first (unconditional, clamped addresses), all in one round: q slice, summary
+  // rows (sequence-major, so no page-table hop), the page id (used only for the tail refresh)
+  // and the sequence length ----
+  uint4 qraw[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) qraw[g] = load16(q + ((size_t)b * Hq + j * G + g) * D + c0);
+  const int nc = min(n, a.maxp - 1);  // from the row width only: no wait for seq_lens
+  const T* srow = (const T*)a.summ + ((size_t)list * a.maxp + nc) * 2 * D + c0;
+  const uint4 lo_raw = load16(srow), hi_raw = load16(srow + D);
+  // entries past the sequence may hold anything and are clamped into the pool (never used)
+  const int pt_raw = a.page_table[(size_t)b * a.maxp + nc];
+  __builtin_amdgcn_sched_barrier(0);
+  const int L = a.seq_lens[b];
+  const int p = min(max(pt_raw, 0), a.Npp - 1);
+  const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;  // never past the table row
+  const bool active = n < N;
+
+  // ---- decode-time refresh of the tail page's summary, by the wave that scores that page: the
+  // page id is already in its lanes, so the key tile loads go out one hop after the page table,
+  // alongside the summary loads, and no other wave waits ----
+  float lo[VEC], hi[VEC];
+  const int nt = N - 1;
+  const int wn0 = n0 + w * PPW;  // first page of this wave
+  if (a.refresh_tail && N > 0 && nt >= wn0 && nt < wn0 + PPW) {  // wave-uniform
+    const int rg = nt - wn0;                                   // the tail page's row group
+    const int pt = __builtin_amdgcn_readlane(p, rg * LPR);
+    float flo[VEC], fhi[VEC];
+    tile_minmax<T, D>((const T*)a.k_pool + ((size_t)pt * a.Hkv + j) * P * D, L - nt * P, P, lane,
+                      pt, a.rope, flo, fhi);
+    if (lane < LPR) {
+      T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;
+      store16(out + c0, pack<T>(flo));
+      store16(out + D + c0, pack<T>(fhi));
+    }
+    unpack<T>(lo_raw, lo);
+    unpack<T>(hi_raw, hi);
+    if (lane / LPR == rg) {  // the stale rows loaded above are replaced by the fresh ones
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        lo[e] = flo[e];
+        hi[e] = fhi[e];
+      }
+    }
+  } else {
+    unpack<T>(lo_raw, lo);
+    unpack<T>(hi_raw, hi);
+  }
+
+  // ---- scores of this block's pages ----
+  double qd[G][VEC];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float f[VEC];
+    unpack<T>(qraw[g], f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) qd[g][e] = (double)f[e];
+  }
+  double acc = 0.0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const double x = (double)(qd[g][e] >= 0.0 ? hi[e] : lo[e]);
+      acc = fma(qd[g][e], x, acc);
+    }
+  }
+  acc = seg_sum_f64<LPR>(acc);
+  if (active && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
+}
+
+// Group-mean cosine similarity of this step's and the previous step's queries for KV head j of
+// sequence b, by one wave, in fp64: for each of the G heads, dot / (|q| |q_prev|) with the
+// channel sums taken lane-strided and folded across the wave; then the mean over the group.
+// Every lane returns the same value, and every caller gets the same bits.
+template <typename T, int D>
+__device__ __forceinline__ double group_cosine(const T* q, const T* q_prev, int Hkv, int G, int b,
+                                               int j) {
+  const int lane = threadIdx.x & 63;
+  const int Hq = Hkv * G;
+  double csum = 0.0;
+  for (int g = 0; g < G; ++g) {
+    const size_t row = ((size_t)b * Hq + j * G + g) * D;
+    double dot = 0.0, na = 0.0, nb = 0.0;
+    for (int d = lane; d < D; d += 64) {
+      const double xv = (double)load_elem<T>(q + row, d), yv = (double)load_elem<T>(q_prev + row, d);
+      dot = fma(xv, yv, dot);
+      na = fma(xv, xv, na);
+      nb = fma(yv, yv, nb);
+    }
+    dot = seg_sum_f64<64>(dot);
+    na = seg_sum_f64<64>(na);
+    nb = seg_sum_f64<64>(nb);
+    csum += dot / (sqrt(na) * sqrt(nb));
+  }
+  return csum / G;
+}
+
+// Host: the selection arguments of one call (score_topk.hip).
+SelectArgs select_args(const LaunchKV& kv, const RopeArgs& rope, void* summ, const void* q, int k,
+                       int flags, int32_t* sel_idx, int32_t* sel_cnt, float* scores,
+                       bool scores_requested, const ReuseArgs& reuse);
+
+}  // namespace kvsel

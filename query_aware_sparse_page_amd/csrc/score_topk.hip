@@ -1,12 +1,7 @@
 // Query-aware page scoring, top-k page selection and the speculative-reuse decision.
 //
-// score_kernel: one block per (page chunk, list), list = (sequence, KV head) varying fastest.
-// Each block scores 4 * PPW pages: LPR lanes read a page's lo and hi rows as 16-byte slices
-// (the summaries are sequence-major, so a block reads one contiguous run), multiply by the group's query slice in fp64 (a bf16 x bf16 or fp32 x fp32 product
-// is exact in fp64), take q*hi for q >= 0 and q*lo otherwise, and fold the LPR lanes; one
-// fp64 -> fp32 rounding per score. With the tail refresh on, the block holding a sequence's last
-// page first rebuilds that page's summary from the key pool (the page a decode step appends to),
-// writes it, and scores it from the fresh values.
+// score_kernel: one block per (page chunk, list), list = (sequence, KV head) varying fastest;
+// each block scores 4 * PPW pages (score_block: summary loads, fp64 products, tail refresh).
 //
 // topk_kernel: one block per list. An exact radix select over orderable 32-bit score keys
 // (8-bit digits, most significant first, starting below the bits all keys share, stopping once
@@ -20,6 +15,7 @@
 // invalidates the XCD's L2 and measured slower than the second launch.
 #include "kvsel_device.h"
 #include "kvsel_internal.h"
+#include "kvsel_score.h"
 #include "kvsel_topk.h"
 
 namespace kvsel {
@@ -29,76 +25,11 @@ constexpr int SEL_WAVES = SEL_THREADS / 64;
 constexpr int SEL_LDS_KEYS = 8192;
 constexpr int TOPK_BATCH = 8;  // independent score loads in flight per thread
 
-struct SelectArgs {
-  const void* k_pool;
-  void* summ;
-  const void* q;
-  const int32_t* page_table;
-  const int32_t* seq_lens;
-  int Hkv, P, maxp, Npp, k, nlists, nchunks, refresh_tail, write_scores;
-  int scores_only;  // launch the score kernel alone (the fused selection + attention call)
-  RopeArgs rope;
-  float* scores;
-  int32_t* sel_idx;
-  int32_t* sel_cnt;
-  ReuseArgs reuse;
-};
-
 // Radix-select state plus an LDS copy of the keys (block_topk, which reads scores from memory).
 template <int NT>
 struct TopkSmem : RadixSmem<NT> {
   uint32_t keys[SEL_LDS_KEYS];
 };
-
-// Min / max of the valid rows (1 <= valid) of one (page, KV head) tile of physical page pt,
-// computed by one wave. On return every lane holds lo / hi of its channels [c0, c0 + VEC). The
-// row loads are unconditional (rows past `valid` re-read the last valid row and are ignored), so
-// they all go out at once; the page's rotary row is read after them.
-template <typename T, int D>
-__device__ __forceinline__ void tile_minmax(const T* tile, int valid, int P, int lane, int pt,
-                                            const RopeArgs& rope, float* lo, float* hi) {
-  using M = row_map<T, D>;
-  constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
-  constexpr int MAX_LOADS = 32 / RPW;
-  const int rg = lane / LPR;
-  const int c0 = (lane % LPR) * VEC;
-  uint4 raw[MAX_LOADS];
-#pragma unroll
-  for (int i = 0; i < MAX_LOADS; ++i) {
-    const int s = rg + i * RPW;
-    raw[i] = load16(tile + (size_t)min(s, valid - 1) * D + c0);
-  }
-  const int prow = rope.page_row ? rope.page_row[pt] : -1;
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    lo[e] = __int_as_float(0x7f800000);
-    hi[e] = __int_as_float(0xff800000);
-  }
-#pragma unroll
-  for (int i = 0; i < MAX_LOADS; ++i) {
-    const int s = rg + i * RPW;
-    if (i * RPW >= P) break;
-    float x[VEC];
-    unpack<T>(raw[i], x);
-    if (rope.page_row)
-      rope_rotate_slice<T, D>(x, c0, prow < 0 ? -1 : prow + rope.row_step * s, rope.cos, rope.sin);
-    if (s < valid) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        lo[e] = fminf(lo[e], x[e]);
-        hi[e] = fmaxf(hi[e], x[e]);
-      }
-    }
-  }
-#pragma unroll
-  for (int m = LPR; m < 64; m <<= 1) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      lo[e] = fminf(lo[e], __shfl_xor(lo[e], m));
-      hi[e] = fmaxf(hi[e], __shfl_xor(hi[e], m));
-    }
-  }
-}
 
 // Exact top-k of the N scores of one list, by the whole block; writes out[0..k) ascending
 // (padded with -1) and, when `used` is non-null, the same list there too. `first` holds the
@@ -229,90 +160,8 @@ __device__ void block_topk(const float* __restrict__ sc, const float* first, int
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
-  using M = row_map<T, D>;
-  constexpr int VEC = M::VEC, LPR = M::LPR;
-  constexpr int PPW = 64 / LPR;          // pages per wave
-  constexpr int PPB = SEL_WAVES * PPW;   // pages per block
-
   // grid (Hkv, B, chunks): the indices need no division; KV heads vary fastest
-  const int j = blockIdx.x, b = blockIdx.y, chunk = blockIdx.z;
-  const int list = b * a.Hkv + j;
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int P = a.P;
-  const int n0 = chunk * PPB;
-  const int Hq = a.Hkv * G;
-  const T* q = (const T*)a.q;
-  const int c0 = (lane % LPR) * VEC;
-  const int n = n0 + w * PPW + lane / LPR;
-
-  // ---- loads first (unconditional, clamped addresses), all in one round: q slice, summary
-  // rows (sequence-major, so no page-table hop), the page id (used only for the tail refresh)
-  // and the sequence length ----
-  uint4 qraw[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) qraw[g] = load16(q + ((size_t)b * Hq + j * G + g) * D + c0);
-  const int nc = min(n, a.maxp - 1);  // from the row width only: no wait for seq_lens
-  const T* srow = (const T*)a.summ + ((size_t)list * a.maxp + nc) * 2 * D + c0;
-  const uint4 lo_raw = load16(srow), hi_raw = load16(srow + D);
-  // entries past the sequence may hold anything and are clamped into the pool (never used)
-  const int pt_raw = a.page_table[(size_t)b * a.maxp + nc];
-  __builtin_amdgcn_sched_barrier(0);
-  const int L = a.seq_lens[b];
-  const int p = min(max(pt_raw, 0), a.Npp - 1);
-  const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;  // never past the table row
-  const bool active = n < N;
-
-  // ---- decode-time refresh of the tail page's summary, by the wave that scores that page: the
-  // page id is already in its lanes, so the key tile loads go out one hop after the page table,
-  // alongside the summary loads, and no other wave waits ----
-  float lo[VEC], hi[VEC];
-  const int nt = N - 1;
-  const int wn0 = n0 + w * PPW;  // first page of this wave
-  if (a.refresh_tail && N > 0 && nt >= wn0 && nt < wn0 + PPW) {  // wave-uniform
-    const int rg = nt - wn0;                                   // the tail page's row group
-    const int pt = __builtin_amdgcn_readlane(p, rg * LPR);
-    float flo[VEC], fhi[VEC];
-    tile_minmax<T, D>((const T*)a.k_pool + ((size_t)pt * a.Hkv + j) * P * D, L - nt * P, P, lane,
-                      pt, a.rope, flo, fhi);
-    if (lane < LPR) {
-      T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;
-      store16(out + c0, pack<T>(flo));
-      store16(out + D + c0, pack<T>(fhi));
-    }
-    unpack<T>(lo_raw, lo);
-    unpack<T>(hi_raw, hi);
-    if (lane / LPR == rg) {  // the stale rows loaded above are replaced by the fresh ones
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        lo[e] = flo[e];
-        hi[e] = fhi[e];
-      }
-    }
-  } else {
-    unpack<T>(lo_raw, lo);
-    unpack<T>(hi_raw, hi);
-  }
-
-  // ---- scores of this block's pages ----
-  double qd[G][VEC];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float f[VEC];
-    unpack<T>(qraw[g], f);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) qd[g][e] = (double)f[e];
-  }
-  double acc = 0.0;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const double x = (double)(qd[g][e] >= 0.0 ? hi[e] : lo[e]);
-      acc = fma(qd[g][e], x, acc);
-    }
-  }
-  acc = seg_sum_f64<LPR>(acc);
-  if (active && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
+  score_block<T, D, G, SEL_WAVES>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // block_topk_regs writing the ascending list to out (and used, when non-null), padded with -1.
@@ -329,31 +178,14 @@ __device__ void topk_to_list(const uint32_t (&key)[C], int N, int k, int32_t* __
   }
 }
 
-// Speculative-reuse decision of one list, by the block's first wave: mean over the group of
-// cos(q, q_prev) in fp64; corrected = first step or C < tau. Every thread gets the decision.
+// Speculative-reuse decision of one list, by the block's first wave: the group-mean cosine
+// similarity C of this step's and the previous step's queries; corrected = first step or C < tau.
+// Every thread gets the decision.
 template <typename T, int D, int G>
 __device__ int reuse_decision(const SelectArgs& a, int list, int b, int j, int* s_corr) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int Hq = a.Hkv * G;
   if (w == 0) {
-    double csum = 0.0;
-    for (int g = 0; g < G; ++g) {
-      const int h = j * G + g;
-      const T* x = (const T*)a.q + ((size_t)b * Hq + h) * D;
-      const T* y = (const T*)a.reuse.q_prev + ((size_t)b * Hq + h) * D;
-      double dot = 0.0, na = 0.0, nb = 0.0;
-      for (int d = lane; d < D; d += 64) {
-        const double xv = (double)load_elem<T>(x, d), yv = (double)load_elem<T>(y, d);
-        dot = fma(xv, yv, dot);
-        na = fma(xv, xv, na);
-        nb = fma(yv, yv, nb);
-      }
-      dot = seg_sum_f64<64>(dot);
-      na = seg_sum_f64<64>(na);
-      nb = seg_sum_f64<64>(nb);
-      csum += dot / (sqrt(na) * sqrt(nb));
-    }
-    const double C = csum / G;
+    const double C = group_cosine<T, D>((const T*)a.q, (const T*)a.reuse.q_prev, a.Hkv, G, b, j);
     const int corr = (a.reuse.first_step || C < a.reuse.tau) ? 1 : 0;
     if (lane == 0) {
       *s_corr = corr;
@@ -602,9 +434,9 @@ static hipError_t launch_select(const SelectArgs& a, const LaunchKV& kv, hipStre
   return launch_select_g<bf16_t, 128>(kv.G, a, stream);
 }
 
-static SelectArgs select_args(const LaunchKV& kv, const RopeArgs& rope, void* summ, const void* q,
-                              int k, int flags, int32_t* sel_idx, int32_t* sel_cnt, float* scores,
-                              bool scores_requested, const ReuseArgs& reuse) {
+SelectArgs select_args(const LaunchKV& kv, const RopeArgs& rope, void* summ, const void* q, int k,
+                       int flags, int32_t* sel_idx, int32_t* sel_cnt, float* scores,
+                       bool scores_requested, const ReuseArgs& reuse) {
   SelectArgs a;
   a.k_pool = kv.k_pool;
   a.summ = summ;

@@ -1,0 +1,104 @@
+// kvsel_select_attend: the scores (score kernel), then the attention launch with the selection
+// fused in (select_tiles: every block re-derives its list's top-k from the scores and keeps the
+// pages of its own split), then the merge. The fused launch uses the default split of FUSED_PPS
+// pages (block shapes in kvsel_attn.h). Other cases (a table too wide for the register-resident
+// select, a k that needs larger splits) run the two separate calls' launches instead.
+#include "kvsel_attn.h"
+
+namespace kvsel {
+
+template <int D, int P, int WAVES, int TPW, bool ROPE, int C>
+__global__ __launch_bounds__(WAVES * 64) void fused_bf16_kernel(AttnArgs a, int G) {
+  // grid (Hkv, B, splits)
+  attn_bf16_block<D, P, WAVES, TPW, ROPE, C>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+template <int D, int P, int WAVES, int TPW, bool ROPE, int C>
+__global__ __launch_bounds__(WAVES * 64) void fused_f32_kernel(AttnArgs a, int G) {
+  attn_f32_block<D, P, WAVES, TPW, ROPE, C>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Score keys per thread of the fused select (the block holds the whole table row in registers).
+static int fused_keys_per_thread(const LaunchKV& kv) {
+  const int nt = (kv.dtype == 1 && kv.P == 16) ? 128 : 256;
+  const int c = (kv.maxp + nt - 1) / nt;
+  return c <= 1 ? 1 : c <= 4 ? 4 : c <= 16 ? 16 : c <= 32 ? 32 : 0;
+}
+
+bool select_attend_fused(const LaunchKV& kv, const RopeArgs&, int k) {
+  return fused_keys_per_thread(kv) > 0 && attention_pages_per_split(kv, k, 0) == FUSED_PPS;
+}
+
+template <typename T, int D, int P, bool ROPE, int C>
+static void launch_fused_c(const AttnArgs& a, int G, hipStream_t stream) {
+  using S = FusedShape<T, P>;
+  const dim3 grid(a.Hkv, a.nlists / a.Hkv, a.nsplit);
+  const dim3 block(S::WAVES * 64);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((fused_bf16_kernel<D, P, S::WAVES, S::TPW, ROPE, C>), grid, block, 0, stream, a, G);
+  else
+    hipLaunchKernelGGL((fused_f32_kernel<D, P, S::WAVES, S::TPW, ROPE, C>), grid, block, 0, stream, a, G);
+}
+
+template <typename T, int D, int P, bool ROPE>
+static void launch_fused_r(int c, const AttnArgs& a, int G, hipStream_t stream) {
+  switch (c) {
+    case 1: launch_fused_c<T, D, P, ROPE, 1>(a, G, stream); break;
+    case 4: launch_fused_c<T, D, P, ROPE, 4>(a, G, stream); break;
+    case 16: launch_fused_c<T, D, P, ROPE, 16>(a, G, stream); break;
+    default: launch_fused_c<T, D, P, ROPE, 32>(a, G, stream); break;
+  }
+}
+
+template <typename T, int D>
+static void launch_fused_p(int P, int c, const AttnArgs& a, int G, bool rope, hipStream_t stream) {
+  if (P == 16) {
+    if (rope) launch_fused_r<T, D, 16, true>(c, a, G, stream);
+    else launch_fused_r<T, D, 16, false>(c, a, G, stream);
+  } else {
+    if (rope) launch_fused_r<T, D, 32, true>(c, a, G, stream);
+    else launch_fused_r<T, D, 32, false>(c, a, G, stream);
+  }
+}
+
+hipError_t launch_fused_select(const LaunchKV& kv, const AttnArgs& a, bool rope,
+                               hipStream_t stream) {
+  const int c = fused_keys_per_thread(kv);
+  if (kv.dtype == 0) {
+    if (kv.D == 64) launch_fused_p<float, 64>(kv.P, c, a, kv.G, rope, stream);
+    else launch_fused_p<float, 128>(kv.P, c, a, kv.G, rope, stream);
+  } else {
+    if (kv.D == 64) launch_fused_p<bf16_t, 64>(kv.P, c, a, kv.G, rope, stream);
+    else launch_fused_p<bf16_t, 128>(kv.P, c, a, kv.G, rope, stream);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_merge(kv, a, stream);
+}
+
+size_t select_attend_workspace(const LaunchKV& kv, int k) {
+  return align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float)) + attention_workspace(kv, k, 0);
+}
+
+hipError_t launch_select_attend(const LaunchKV& kv, const RopeArgs& rope, void* summ,
+                                const void* q, int k, int flags, float scale, int32_t* sel_idx,
+                                int32_t* sel_cnt, void* out, float* lse, void* ws,
+                                hipStream_t stream) {
+  float* scores = (float*)ws;
+  void* attn_ws = (char*)ws + align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float));
+  if (!select_attend_fused(kv, rope, k)) {
+    hipError_t e = launch_score_topk(kv, rope, summ, q, k, flags, sel_idx, sel_cnt, scores, false,
+                                     ReuseArgs{}, stream);
+    if (e != hipSuccess) return e;
+    return launch_attention(kv, rope, q, sel_idx, sel_cnt, k, scale, 0, out, lse, attn_ws, stream);
+  }
+  hipError_t e = launch_scores(kv, rope, summ, q, flags, scores, stream);
+  if (e != hipSuccess) return e;
+  AttnArgs a = attn_args(kv, rope, q, nullptr, nullptr, k, scale, FUSED_PPS, out, lse, attn_ws);
+  a.scores = scores;
+  a.sel_out = sel_idx;
+  a.cnt_out = sel_cnt;
+  return launch_fused_select(kv, a, rope.page_row != nullptr, stream);
+}
+
+}  // namespace kvsel

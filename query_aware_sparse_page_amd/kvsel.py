@@ -79,7 +79,7 @@ EXPORTS = {
     "kvsel_speculative_step": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp,
                                        c_vp, c_i32, c_i32, ctypes.c_float,
                                        ctypes.POINTER(ReuseDesc), c_vp, c_vp, c_vp, c_vp, c_vp,
-                                       ctypes.c_size_t, c_vp, c_vp, c_vp, c_vp]),
+                                       ctypes.c_size_t, c_vp]),
     "kvsel_check_inputs": (c_i32, [ctypes.POINTER(PagedKVDesc), c_vp, c_vp, c_i32, c_vp, c_vp]),
     "kvsel_gather_probe": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp]),
     "kvsel_rope_table": (c_i32, [ctypes.c_double, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
@@ -439,34 +439,16 @@ def check_inputs(kv: PagedKV, sel_idx: Optional[torch.Tensor] = None,
     return flags
 
 
-_side = {}
-
-
-def _side_objects(dev: torch.device):
-    """A side stream and two events per device for the speculative step (the events are
-    recorded once so that their handles exist before any graph capture)."""
-    key = dev.index if dev.index is not None else torch.cuda.current_device()
-    if key not in _side:
-        with torch.cuda.device(key):
-            side = torch.cuda.Stream()
-            fork, join = torch.cuda.Event(), torch.cuda.Event()
-            fork.record()
-            join.record()
-            torch.cuda.synchronize()
-        _side[key] = (side, fork, join)
-    return _side[key]
-
 
 def speculative_step(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, reuse: Reuse, *,
                      refresh_tail: bool = False, rope: Optional[Rope] = None,
                      scale: Optional[float] = None, sel_idx: Optional[torch.Tensor] = None,
                      sel_cnt: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                      lse: Optional[torch.Tensor] = None, want_lse: bool = True,
-                     workspace: Optional[torch.Tensor] = None,
-                     side_stream: Optional[torch.cuda.Stream] = None):
-    """score_topk with reuse + sparse_decode_attn over the used pages, with the attention over
-    the previous pages overlapped with the selection on a side stream. Returns (sel_idx,
-    sel_cnt, used_idx, used_cnt, corrected, similarity, out, lse)."""
+                     workspace: Optional[torch.Tensor] = None):
+    """score_topk with reuse + sparse_decode_attn over the used pages in one call, the attention
+    over the previous step's pages sharing a launch with the scoring. Returns (sel_idx, sel_cnt,
+    used_idx, used_cnt, corrected, similarity, out, lse)."""
     d = kv.desc()
     B, Hkv = kv.batch, kv.num_kv_heads
     dev = kv.device
@@ -492,15 +474,11 @@ def speculative_step(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, r
     rd = ReuseDesc(reuse.q_prev.data_ptr(), reuse.prev_idx.data_ptr(), reuse.prev_cnt.data_ptr(),
                    float(reuse.tau), int(bool(reuse.first_step)), used_idx.data_ptr(),
                    used_cnt.data_ptr(), corrected.data_ptr(), sim.data_ptr())
-    side, fork, join = _side_objects(dev)
-    if side_stream is not None:
-        side = side_stream
     ws, ws_bytes = _workspace(kv, k, KVSEL_OP_SPECULATIVE_STEP, 0, workspace)
     flags = KVSEL_SCORE_REFRESH_TAIL if refresh_tail else 0
     _check(lib().kvsel_speculative_step(ctypes.byref(d), _rope_ptr(rope), _ptr(summ), _ptr(q), k,
                                         flags, scale, ctypes.byref(rd), _ptr(sel_idx),
                                         _ptr(sel_cnt), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
-                                        _stream(dev), side.cuda_stream, fork.cuda_event,
-                                        join.cuda_event))
+                                        _stream(dev)))
     return sel_idx, sel_cnt, used_idx, used_cnt, corrected, sim, out, lse
 

@@ -1,6 +1,7 @@
-"""kvsel_speculative_step (attention over the previous pages overlapped with the selection on a
-side stream, corrected lists attended again) against the serial calls, bit for bit, and the
-oracle; eager and captured in a HIP graph."""
+"""kvsel_speculative_step (attention over the previous pages in the scoring launch, corrected
+lists attended again by the fused selection) against the serial calls, bit for bit, and the
+oracle; every block shape of the co-scheduled launch, the rotary gather, the serial fallback, and
+capture in a HIP graph."""
 import numpy as np
 import pytest
 import torch
@@ -20,19 +21,20 @@ def K():
     return K
 
 
-def setup_case(K, k, seed=601, dtype="bf16"):
-    w = W.custom(seed, B=4, Hq=32, Hkv=8, D=128, P=32, k=k, lens=[4000, 3000, 2017, 5000],
-                 dtype=dtype)
+def setup_case(K, k, seed=601, dtype="bf16", Hq=32, Hkv=8, D=128, P=32,
+               lens=(4000, 3000, 2017, 5000), rope=None):
+    w = W.custom(seed, B=len(lens), Hq=Hq, Hkv=Hkv, D=D, P=P, k=k, lens=list(lens), dtype=dtype)
     kv = kv_of(K, w)
-    summ = K.build_summaries(kv)
+    summ = K.build_summaries(kv, rope=rope)
     gen = torch.Generator().manual_seed(seed)
     q = w.q.clone().float()
     q_prev = q.clone()
-    # KV heads 0..3 of every sequence keep a close previous query, 4..7 a fresh one
-    G = w.Hq // w.Hkv
-    close = q[:, : 4 * G] + 0.05 * torch.randn(q[:, : 4 * G].shape, generator=gen)
-    q_prev[:, : 4 * G] = close
-    q_prev[:, 4 * G:] = torch.randn(q_prev[:, 4 * G:].shape, generator=gen)
+    # the first half of the KV heads of every sequence keep a close previous query, the rest get
+    # a fresh one
+    G = Hq // Hkv
+    h = (Hkv // 2) * G
+    q_prev[:, :h] = q[:, :h] + 0.05 * torch.randn(q[:, :h].shape, generator=gen)
+    q_prev[:, h:] = torch.randn(q_prev[:, h:].shape, generator=gen)
     q = q.to(w.q.dtype).cuda()
     q_prev = q_prev.to(w.q.dtype).cuda()
     prev_idx, prev_cnt = K.score_topk(kv, summ, q_prev, k)  # the previous step's fresh pages
@@ -40,9 +42,9 @@ def setup_case(K, k, seed=601, dtype="bf16"):
     return w, kv, summ, q, q_prev, prev_idx, prev_cnt
 
 
-def serial(K, kv, summ, q, k, reuse):
+def serial(K, kv, summ, q, k, reuse, rope=None):
     sel, cnt, used, ucnt, corr, sim = K.score_topk(kv, summ, q, k, reuse=reuse)
-    out, lse = K.sparse_decode_attn(kv, q, used, ucnt, k)
+    out, lse = K.sparse_decode_attn(kv, q, used, ucnt, k, rope=rope)
     return sel, cnt, used, ucnt, corr, sim, out, lse
 
 
@@ -54,27 +56,81 @@ def assert_same(a, b):
         assert torch.equal(x, y), f"{n} differs between the speculative step and the serial calls"
 
 
-@pytest.mark.parametrize("k", [16, 4])  # 4 splits (merge) and a single split (direct writes)
-def test_speculative_step_matches_serial(K, k):
-    w, kv, summ, q, q_prev, prev_idx, prev_cnt = setup_case(K, k)
+def check_both_outcomes(K, kv, summ, q, q_prev, prev_idx, prev_cnt, k, rope=None):
+    Hkv = kv.num_kv_heads
     for first in (False, True):
-        say(f"speculative step k={k} first_step={first}")
         reuse = K.Reuse(q_prev, prev_idx, prev_cnt, 0.8, first_step=first)
-        spec = K.speculative_step(kv, summ, q, k, reuse)
-        ref = serial(K, kv, summ, q, k, reuse)
+        spec = K.speculative_step(kv, summ, q, k, reuse, rope=rope)
+        ref = serial(K, kv, summ, q, k, reuse, rope=rope)
         torch.cuda.synchronize()
         assert_same(spec, ref)
         corr = spec[4].cpu().numpy()
         if first:
             assert corr.all()
-        else:
-            assert corr[:, 4:].all() and not corr[:, :4].any()  # both outcomes occur
+        else:  # both outcomes occur
+            assert corr[:, Hkv // 2:].all() and not corr[:, :Hkv // 2].any()
+    return spec
+
+
+# (dtype, P, D, Hq, Hkv, k): every block shape of the co-scheduled launch (bf16 P 32: 4 waves;
+# bf16 P 16: 2 waves; fp32 P 32: 4 waves x 2 tiles; fp32 P 16), group sizes 1..8, one split
+# (direct writes, no merge) and many
+SHAPES = [
+    ("bf16", 32, 128, 32, 8, 16),
+    ("bf16", 32, 128, 32, 8, 4),
+    ("bf16", 16, 64, 64, 8, 12),
+    ("f32", 32, 128, 16, 8, 16),
+    ("f32", 16, 64, 8, 8, 9),
+    ("bf16", 32, 64, 8, 4, 40),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_speculative_step_matches_serial(K, shape):
+    dtype, P, D, Hq, Hkv, k = shape
+    say(f"speculative step {shape}")
+    w, kv, summ, q, q_prev, prev_idx, prev_cnt = setup_case(K, k, dtype=dtype, Hq=Hq, Hkv=Hkv,
+                                                              D=D, P=P)
+    spec = check_both_outcomes(K, kv, summ, q, q_prev, prev_idx, prev_cnt, k)
     # the used pages' attention against the oracle
     out, lse = spec[6], spec[7]
     o_out, o_lse = O.sparse_decode_attention(q.cpu(), w.k_pool, w.v_pool, w.page_table, w.seq_lens,
                                              spec[2].cpu().numpy(), spec[3].cpu().numpy(), w.P,
                                              scale_of(w.D))
-    assert_attention_close(out, lse, o_out, o_lse, "bf16")
+    assert_attention_close(out, lse, o_out, o_lse, dtype)
+
+
+def test_speculative_step_empty_and_short_sequences(K):
+    k = 16
+    say("speculative step: empty, one-page and short sequences")
+    w, kv, summ, q, q_prev, prev_idx, prev_cnt = setup_case(K, k, seed=605,
+                                                              lens=(0, 31, 4000, 33, 512))
+    spec = check_both_outcomes(K, kv, summ, q, q_prev, prev_idx, prev_cnt, k)
+    assert int(spec[1][0].max()) == 0 and int(spec[3][0].max()) == 0
+    assert bool((spec[7][0] == float("-inf")).all()) and not bool(spec[6][0].float().any())
+
+
+def test_speculative_step_rotary_gather(K):
+    k = 16
+    n_rows = 4
+    lens = (4000, 3000, 2017, 5000)
+    n_phys = sum(-(-L // 32) for L in lens)
+    cos, sin = K.rope_table(500000.0, 128, 4096, n_rows, torch.device("cuda"))
+    page_row = torch.full((n_phys,), -1, dtype=torch.int32)
+    page_row[: n_phys // 2] = torch.arange(n_phys // 2, dtype=torch.int32) % n_rows
+    rope = K.Rope(cos, sin, page_row.cuda(), row_step=0)
+    say("speculative step with the rotary gather")
+    w, kv, summ, q, q_prev, prev_idx, prev_cnt = setup_case(K, k, seed=603, lens=lens, rope=rope)
+    check_both_outcomes(K, kv, summ, q, q_prev, prev_idx, prev_cnt, k, rope=rope)
+
+
+def test_speculative_step_serial_fallback(K):
+    # k above 1024 needs splits larger than the fused selection's: the two calls run serially
+    k = 1100
+    say("speculative step fallback: k = 1100")
+    w, kv, summ, q, q_prev, prev_idx, prev_cnt = setup_case(K, k, seed=604, Hq=8, Hkv=2, D=64,
+                                                              P=16, lens=(16 * 1500,))
+    check_both_outcomes(K, kv, summ, q, q_prev, prev_idx, prev_cnt, k)
 
 
 def test_speculative_step_in_a_graph(K):
@@ -87,7 +143,7 @@ def test_speculative_step_in_a_graph(K):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        K.speculative_step(kv, summ, q, k, reuse)  # warm-up (creates the side objects)
+        K.speculative_step(kv, summ, q, k, reuse)  # warm-up
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()

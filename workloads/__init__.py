@@ -89,6 +89,8 @@ def _rng(seed: int) -> np.random.Generator:
 
 
 def _to(x: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"element type {dtype!r}: expected 'f32' or 'bf16'")
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
     return t if dtype == "f32" else t.to(torch.bfloat16)
 
