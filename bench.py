@@ -163,6 +163,11 @@ def attention_bytes(w, lay):
     return selected_kv_bytes(w.seq_lens.tolist(), sel, cnt, w.Hkv, w.P, w.D, esize)
 
 
+def progress(msg):
+    """One line per finished phase, on stderr (stdout carries only the result line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def measure(name, dev, steps, warmup, n_layers):
     w = W.make(name)
     layers = make_layers(w, dev, n_layers)
@@ -185,15 +190,27 @@ def measure(name, dev, steps, warmup, n_layers):
                 probe_bytes=probe_bytes, calls_timed=n_calls)
 
 
+# The sources the attention call's kernels are compiled from: a change to any of them makes the
+# committed counter summary stale.
+ATTENTION_SOURCES = ("attention.hip", "kvsel_attn.h", "kvsel_device.h", "kvsel_topk.h")
+
+
+def attention_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in ATTENTION_SOURCES:
+        with open(os.path.join(ROOT, "query_aware_sparse_page_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def recorded_traffic():
     """Attention HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current attention source (else None)."""
-    import hashlib
+    taken on the current attention sources (else None)."""
     path = os.path.join(ROOT, "profiles", "attention_llama8b_32k_counters.md")
-    src = os.path.join(ROOT, "query_aware_sparse_page_amd", "csrc", "attention.hip")
     try:
         text = open(path).read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        sha = attention_source_hash()
     except OSError:
         return None
     vals = dict(line.split("=", 1) for line in text.splitlines() if "=" in line and " " not in line)
@@ -378,7 +395,8 @@ def counter_pass(name, dev, n_layers):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"counter_pass": name, "layers": n_layers, "steps_per_form": 2 * n_layers,
-                      "calibration_copy_bytes": 64 << 20}), flush=True)
+                      "calibration_copy_bytes": 64 << 20,
+                      "attention_source_sha256_16": attention_source_hash()}), flush=True)
 
 
 def main():
@@ -458,21 +476,31 @@ def main():
     keep = m["layers"][0]  # its last step's outputs are checked against the CPU oracle
     del m["layers"]
     torch.cuda.empty_cache()
-    if not args.no_secondary and args.workload != "qwen4b_128k":
-        s = measure("qwen4b_128k", dev, args.steps, args.warmup, max(2, args.layers // 2))
+    progress(f"{w.name}: step {result['value']} us, attention call {m['attn_us']:.3f} us")
+    # the 128K case of the metric, and the batched case whose 64 MiB per step is where bandwidth
+    # rather than latency sets the time
+    for name, n_layers in (("qwen4b_128k", max(2, args.layers // 2)),
+                           ("ragged_batch", max(2, args.layers // 4))):
+        if args.no_secondary or name == args.workload:
+            continue
+        s = measure(name, dev, args.steps, args.warmup, n_layers)
         sach = s["attn_bytes"] / (s["attn_us"] * 1e-6) / 1e9
-        result["secondary"] = {"qwen4b_128k": {
+        result.setdefault("secondary", {})[name] = {
             "us_per_step": round(s["us_step"], 3),
             "two_call_us_per_step": round(s["us_two_calls"], 3), "attn_us": round(s["attn_us"], 3),
             "attn_GBps": round(sach, 1), "attn_frac": round(sach / HBM_PEAK_GBPS, 4),
-            "select_us": round(s["select_us"], 3), "attn_bytes": s["attn_bytes"]}}
+            "select_us": round(s["select_us"], 3), "attn_bytes": s["attn_bytes"],
+            "layers_rotated": n_layers}
+        progress(f"{name}: step {s['us_step']:.3f} us, attention call {s['attn_us']:.3f} us")
         del s
         torch.cuda.empty_cache()
     if not args.no_secondary:
         result.setdefault("secondary", {})["speculative_rope_64_steps"] = speculative(dev)
+        progress("speculative workload done")
         torch.cuda.empty_cache()
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, keep)
+        progress("cpu baseline done")
     print(json.dumps(result), flush=True)
 
 

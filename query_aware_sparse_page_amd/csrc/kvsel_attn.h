@@ -79,8 +79,17 @@ constexpr int ATT_MAX_PPS = 16;  // pages per split of the fused-selection launc
 template <int P, int TT, int TPW>
 struct TilePages {
   static constexpr int NPT = TT > P ? TT / P : 1;
+  static_assert(NPT <= 2, "a tile spans at most two pages");
   int page[TPW][NPT];   // physical page to address (always a valid page)
   int valid[TPW][NPT];  // valid slots of that page; 0 when the slot range is not in the list
+  // Entry u (lane-dependent, 0 or 1) of tile t, by arithmetic: a register array indexed by a
+  // per-lane value (which a select of two entries can be folded into) lands in private memory.
+  __device__ __forceinline__ int page_of(int t, int u) const {
+    return NPT == 1 ? page[t][0] : page[t][0] + u * (page[t][NPT - 1] - page[t][0]);
+  }
+  __device__ __forceinline__ int valid_of(int t, int u) const {
+    return NPT == 1 ? valid[t][0] : valid[t][0] + u * (valid[t][NPT - 1] - valid[t][0]);
+  }
 };
 
 template <int P, int TT, int TPW>
@@ -324,7 +333,7 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
     for (int h = 0; h < 2; ++h) {
       const int x = 8 * (r16 / 4) + 4 * h + (r16 % 4);  // token of row r16 in half h
       const int u = x / P, slot = x % P;
-      const int pg = tp.page[t][u];
+      const int pg = tp.page_of(t, u);
       // an invalid token's row of S^T is masked to -inf below (rows of an MFMA are
       // independent), so its K needs no zeroing
       const bf16_t* row = kp + (((size_t)pg * a.Hkv + j) * P + slot) * D + 8 * q4;
@@ -337,10 +346,10 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
     }
     const int xv = 8 * q4;  // first of the lane's 8 value tokens
     const int u = xv / P, slot = xv % P;
-    const int pg = tp.page[t][u];
+    const int pg = tp.page_of(t, u);
     int m = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m |= (slot + e < tp.valid[t][u]) ? (1 << e) : 0;
+    for (int e = 0; e < 8; ++e) m |= (slot + e < tp.valid_of(t, u)) ? (1 << e) : 0;
     vmask[t] = m;
     const bf16_t* vt = vp + ((size_t)pg * a.Hkv + j) * D * P + slot + (size_t)r16 * P;
 #pragma unroll
