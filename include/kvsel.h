@@ -194,8 +194,10 @@ kvsel_status kvsel_sparse_decode_attn(const kvsel_paged_kv* kv, const kvsel_rope
  * bit for bit. The top-k is re-derived inside the attention launch by every block of a list from
  * the page scores (each block keeps the pages of its own split), so the K / V reads follow one
  * memory round trip after the scores instead of the selection-ids -> page-table chain, and no
- * separate top-k launch runs. Page tables wider than 8192 entries (4096 for bf16 with P 16) and
- * k above 1024 run the two calls' launches instead; the outputs are the same either way.
+ * separate top-k launch runs. The fused form is taken where it measured faster than the
+ * separate launches: fewer than 64 (sequence, KV head) lists, tables of at most 1024 entries
+ * (512 for bf16 with P 16) and k up to 1024; other cases run the two calls' launches inside this
+ * call. The outputs are the same either way.
  * sel_idx / sel_cnt: as kvsel_score_topk. out / lse: as kvsel_sparse_decode_attn. flags: as
  * kvsel_score_topk. ws / ws_bytes: kvsel_workspace_bytes(kv, k, KVSEL_OP_SELECT_ATTEND, 0).
  * [FreeKV] sections 1 and 2.1. */
@@ -228,8 +230,8 @@ kvsel_status kvsel_rope_shift(const kvsel_paged_kv* kv, const kvsel_rope* rope, 
  * scoring and the reuse decision; the next launch selects, and re-attends only the lists the
  * decision corrected, over their fresh pages; a last launch merges the splits. With
  * reuse->first_step every list is corrected and no attention runs over the previous pages.
- * Cases the fused selection of kvsel_select_attend does not cover run the two calls serially,
- * with the same outputs. One stream; capturable in a HIP graph.
+ * Page tables wider than 8192 entries (4096 for bf16 with P 16) and k above 1024 run the two
+ * calls serially instead, with the same outputs. One stream; capturable in a HIP graph.
  * sel_idx / sel_cnt and reuse->used_idx / used_cnt must not alias reuse->prev_idx / prev_cnt.
  * ws / ws_bytes: kvsel_workspace_bytes(kv, k, KVSEL_OP_SPECULATIVE_STEP, 0). Other arguments as
  * kvsel_score_topk and kvsel_sparse_decode_attn.

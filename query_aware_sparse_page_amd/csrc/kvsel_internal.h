@@ -58,8 +58,15 @@ hipError_t launch_score_topk(const LaunchKV& kv, const RopeArgs& rope, void* sum
 hipError_t launch_scores(const LaunchKV& kv, const RopeArgs& rope, void* summ, const void* q,
                          int flags, float* scores, hipStream_t stream);
 
+// Lists from which the selection runs as one launch (one block per list scores and selects;
+// score_topk.hip) instead of the score and top-k launches.
+constexpr int SELECT_ONE_LAUNCH_MIN_LISTS = 64;
+
 // Selection + attention in one call: scores, then the attention launch with the selection fused
 // in (when select_attend_fused), then the merge. Workspace: select_attend_workspace bytes.
+// fused_select_supported: the fused launch exists for this shape (register-resident select of
+// the table row, the default split); select_attend_fused: kvsel_select_attend also takes it.
+bool fused_select_supported(const LaunchKV& kv, int k);
 bool select_attend_fused(const LaunchKV& kv, const RopeArgs& rope, int k);
 size_t select_attend_workspace(const LaunchKV& kv, int k);
 hipError_t launch_select_attend(const LaunchKV& kv, const RopeArgs& rope, void* summ,

@@ -278,7 +278,6 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(SelectArgs a) {
 // ------------------------------------------------------------------------------------------
 constexpr int FUSED_THREADS = 1024;
 constexpr int FUSED_MAX_PAGES = 2048;
-constexpr int FUSED_MIN_LISTS = 64;
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs a) {
@@ -399,7 +398,7 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t stream) {
   // 8 lists of 1024 pages take 24.7 us in one launch against 10.2 us in two; 128 lists of up
   // to 1024 pages take 15.8 us against 18.6 us).
   if constexpr (G <= 4) {  // larger groups would spill at 1024 threads
-    if (!a.scores_only && a.nlists >= FUSED_MIN_LISTS && a.maxp <= FUSED_MAX_PAGES) {
+    if (!a.scores_only && a.nlists >= SELECT_ONE_LAUNCH_MIN_LISTS && a.maxp <= FUSED_MAX_PAGES) {
       hipLaunchKernelGGL((select_fused_kernel<T, D, G>), dim3(a.Hkv, a.nlists / a.Hkv),
                          dim3(FUSED_THREADS), 0, stream, a);
       return hipGetLastError();

@@ -1,8 +1,8 @@
 // kvsel_select_attend: the scores (score kernel), then the attention launch with the selection
 // fused in (select_tiles: every block re-derives its list's top-k from the scores and keeps the
 // pages of its own split), then the merge. The fused launch uses the default split of FUSED_PPS
-// pages (block shapes in kvsel_attn.h). Other cases (a table too wide for the register-resident
-// select, a k that needs larger splits) run the two separate calls' launches instead.
+// pages (block shapes in kvsel_attn.h). Other cases (many lists, a wide table, a k that needs
+// larger splits; select_attend_fused) run the two separate calls' launches instead.
 #include "kvsel_attn.h"
 
 namespace kvsel {
@@ -25,8 +25,18 @@ static int fused_keys_per_thread(const LaunchKV& kv) {
   return c <= 1 ? 1 : c <= 4 ? 4 : c <= 16 ? 16 : c <= 32 ? 32 : 0;
 }
 
-bool select_attend_fused(const LaunchKV& kv, const RopeArgs&, int k) {
+bool fused_select_supported(const LaunchKV& kv, int k) {
   return fused_keys_per_thread(kv) > 0 && attention_pages_per_split(kv, k, 0) == FUSED_PPS;
+}
+
+// Every block of a list repeats the list's select, so the fused form pays where that select is
+// cheap and the blocks are few: at most 4 keys per thread (tables of <= 1024 pages; 512 for bf16
+// with P 16) and fewer lists than the one-launch selection takes. Measured with cold caches:
+// 8 lists of 1024 pages 18.8 us against 20.2 us for the separate launches; 8 lists of 4096 pages
+// 30.6 against 30.5; 128 lists of <= 512 pages 37.5 against 36.5.
+bool select_attend_fused(const LaunchKV& kv, const RopeArgs&, int k) {
+  return fused_select_supported(kv, k) && fused_keys_per_thread(kv) <= 4 &&
+         kv.B * kv.Hkv < SELECT_ONE_LAUNCH_MIN_LISTS;
 }
 
 template <typename T, int D, int P, bool ROPE, int C>

@@ -83,7 +83,7 @@ hipError_t launch_speculative_step(const LaunchKV& kv, const RopeArgs& rope, voi
                                    void* out, float* lse, void* ws, hipStream_t stream) {
   float* scores = (float*)ws;
   void* attn_ws = (char*)ws + align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float));
-  if (!select_attend_fused(kv, rope, k)) {  // the two calls, serially
+  if (!fused_select_supported(kv, k)) {  // the two calls, serially
     hipError_t e = launch_score_topk(kv, rope, summ, q, k, flags, sel_idx, sel_cnt, scores, false,
                                      reuse, stream);
     if (e != hipSuccess) return e;

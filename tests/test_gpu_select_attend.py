@@ -115,7 +115,8 @@ def test_tail_refresh_and_workspace_reuse(K):
 
 
 def test_fallback_paths_match(K):
-    # a rotary gather and k above 1024 take the separate launches inside the same call
+    # k above 1024 needs splits larger than the fused launch's, and a 1500-page table is wider
+    # than the fused form is taken for: the separate launches run inside the same call
     w = W.custom(331, B=1, Hq=8, Hkv=2, D=64, P=16, k=1100, lens=[16 * 1500], dtype="bf16")
     say("select_attend fallback: k = 1100")
     kv = kv_of(K, w)
@@ -125,15 +126,30 @@ def test_fallback_paths_match(K):
     sep = separate_calls(K, kv, summ, q, w.k)
     torch.cuda.synchronize()
     assert_same(fused, sep)
-    n_rows = 4
-    cos, sin = K.rope_table(500000.0, w.D, 4096, n_rows, torch.device("cuda"))
-    page_row = torch.full((w.num_phys_pages,), -1, dtype=torch.int32)
-    page_row[: w.num_phys_pages // 2] = torch.arange(w.num_phys_pages // 2, dtype=torch.int32) % n_rows
-    rope = K.Rope(cos, sin, page_row.cuda(), row_step=0)
-    say("select_attend fallback: rotary gather")
-    summ_r = K.build_summaries(kv, rope=rope)
-    fused = K.select_attend(kv, summ_r, q, 64, rope=rope)
-    sel, cnt = K.score_topk(kv, summ_r, q, 64)
-    out, lse = K.sparse_decode_attn(kv, q, sel, cnt, 64, rope=rope)
+    say("select_attend fallback: 1500-page table, k = 64")
+    fused = K.select_attend(kv, summ, q, 64)
+    sep = separate_calls(K, kv, summ, q, 64)
     torch.cuda.synchronize()
-    assert_same(fused, (sel, cnt, out, lse))
+    assert_same(fused, sep)
+
+
+def test_rotary_gather_fused(K):
+    # the fused launch with the rotary gather, bf16 P 16 (2-wave blocks) and fp32 P 32
+    for seed, dtype, P, D, lens in ((332, "bf16", 16, 64, [16 * 300, 16 * 200 + 5]),
+                                    (333, "f32", 32, 128, [32 * 250 + 7, 32 * 90])):
+        w = W.custom(seed, B=2, Hq=8, Hkv=2, D=D, P=P, k=24, lens=lens, dtype=dtype)
+        kv = kv_of(K, w)
+        q = w.q.cuda()
+        n_rows = 4
+        cos, sin = K.rope_table(500000.0, w.D, 4096, n_rows, torch.device("cuda"))
+        page_row = torch.full((w.num_phys_pages,), -1, dtype=torch.int32)
+        half = w.num_phys_pages // 2
+        page_row[:half] = torch.arange(half, dtype=torch.int32) % n_rows
+        rope = K.Rope(cos, sin, page_row.cuda(), row_step=0)
+        say(f"select_attend with the rotary gather ({dtype}, P {P})")
+        summ_r = K.build_summaries(kv, rope=rope)
+        fused = K.select_attend(kv, summ_r, q, w.k, rope=rope)
+        sel, cnt = K.score_topk(kv, summ_r, q, w.k)
+        out, lse = K.sparse_decode_attn(kv, q, sel, cnt, w.k, rope=rope)
+        torch.cuda.synchronize()
+        assert_same(fused, (sel, cnt, out, lse))

@@ -133,6 +133,16 @@ def test_speculative_step_serial_fallback(K):
     check_both_outcomes(K, kv, summ, q, q_prev, prev_idx, prev_cnt, k)
 
 
+def test_speculative_step_wide_table(K):
+    # 2100 pages: 16 score keys per thread in the fused select (a form kvsel_select_attend does
+    # not take), with the previous pages attended in the shared launch
+    k = 32
+    say("speculative step: 2100-page table")
+    w, kv, summ, q, q_prev, prev_idx, prev_cnt = setup_case(K, k, seed=606, Hq=16, Hkv=4,
+                                                              lens=(32 * 2100 - 9, 32 * 700))
+    check_both_outcomes(K, kv, summ, q, q_prev, prev_idx, prev_cnt, k)
+
+
 def test_speculative_step_in_a_graph(K):
     k = 16
     w, kv, summ, q, q_prev, prev_idx, prev_cnt = setup_case(K, k, seed=602)
