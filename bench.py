@@ -47,8 +47,8 @@ METRIC = "sparse decode-attn µs/step and achieved HBM GB/s (% of peak) at 32K/1
 class Layer:
     """One copy of the cache (its own HBM addresses) with preallocated outputs/workspaces."""
 
-    def __init__(self, w, dev, k_pool, v_pool):
-        self.kv = K.PagedKV(k_pool, v_pool, w.page_table.to(dev), w.seq_lens.to(dev), w.Hq)
+    def __init__(self, w, dev, k_pool, v_pool, page_table, seq_lens):
+        self.kv = K.PagedKV(k_pool, v_pool, page_table, seq_lens, w.Hq)
         self.q = w.q.to(dev)
         self.k = w.k
         self.summ = K.build_summaries(self.kv)
@@ -86,11 +86,15 @@ class Layer:
 
 
 def make_layers(w, dev, n):
+    """n copies of the cache at distinct HBM addresses, used in turn like a model's layers: each
+    has its own K / V pools, summaries, query and outputs; the page table and sequence lengths
+    are shared by all, as a serving engine's block table is shared by every layer."""
     k0 = w.k_pool.to(dev)
     v0 = K.device_v_layout(w.v_pool.to(dev))
-    layers = [Layer(w, dev, k0, v0)]
+    table, lens = w.page_table.to(dev), w.seq_lens.to(dev)
+    layers = [Layer(w, dev, k0, v0, table, lens)]
     for _ in range(n - 1):
-        layers.append(Layer(w, dev, k0.clone(), v0.clone()))
+        layers.append(Layer(w, dev, k0.clone(), v0.clone(), table, lens))
     torch.cuda.synchronize()
     return layers
 

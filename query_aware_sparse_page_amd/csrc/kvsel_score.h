@@ -97,17 +97,19 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
   const int c0 = (lane % LPR) * VEC;
   const int n = n0 + w * PPW + lane / LPR;
 
-  // ---- loads first (unconditional, clamped addresses), all in one round: q slice, summary
-  // rows (sequence-major, so no page-table hop), the page id (used only for the tail refresh)
-  // and the sequence length ----
+  // ---- loads first (unconditional, clamped addresses), all in one round: the page id (used
+  // only for the tail refresh), q slice, summary rows (sequence-major, so no page-table hop) and
+  // the sequence length ----
+  const int nc = min(n, a.maxp - 1);  // from the row width only: no wait for seq_lens
+  // the page id first: the wave that refreshes the tail page waits for it alone (loads complete
+  // in issue order) and sends its key-tile loads while the summary rows are still in flight
+  // (entries past the sequence may hold anything and are clamped into the pool, never used)
+  const int pt_raw = a.page_table[(size_t)b * a.maxp + nc];
   uint4 qraw[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) qraw[g] = load16(q + ((size_t)b * Hq + j * G + g) * D + c0);
-  const int nc = min(n, a.maxp - 1);  // from the row width only: no wait for seq_lens
   const T* srow = (const T*)a.summ + ((size_t)list * a.maxp + nc) * 2 * D + c0;
   const uint4 lo_raw = load16(srow), hi_raw = load16(srow + D);
-  // entries past the sequence may hold anything and are clamped into the pool (never used)
-  const int pt_raw = a.page_table[(size_t)b * a.maxp + nc];
   __builtin_amdgcn_sched_barrier(0);
   const int L = a.seq_lens[b];
   const int p = min(max(pt_raw, 0), a.Npp - 1);
