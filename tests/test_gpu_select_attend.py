@@ -114,6 +114,76 @@ def test_tail_refresh_and_workspace_reuse(K):
     assert_selection_equal(fused[0], fused[1], ref_sel, ref_cnt)
 
 
+def _refresh_case(K, w, prep, k, label, stale=True):
+    """select_attend with the tail refresh against the separate calls and the oracle, after
+    `prep(k_pool)` rewrote keys on the host: with `stale` the summaries were built before (prep
+    may then change only the tail pages, whose summaries the refresh rebuilds), else after."""
+    kv = kv_of(K, w)
+    pool = w.k_pool.clone()
+    if stale:
+        summ_a = K.build_summaries(kv)
+    prep(pool)
+    kv.k_pool.copy_(pool.cuda())
+    if not stale:
+        summ_a = K.build_summaries(kv)
+    summ_b = summ_a.clone()
+    q = w.q.cuda()
+    say(f"select_attend tail merge: {label}")
+    fused = K.select_attend(kv, summ_a, q, k, refresh_tail=True)
+    sep = separate_calls(K, kv, summ_b, q, k, refresh_tail=True)
+    torch.cuda.synchronize()
+    assert_same(fused, sep)
+    for b in range(w.B):
+        assert torch.equal(summ_a[b, :, :w.n_pages(b)], summ_b[b, :, :w.n_pages(b)])
+    ref_summ = O.page_summaries(pool, w.page_table, w.seq_lens, w.P)
+    sc = O.page_scores(w.q, ref_summ, w.page_table, w.seq_lens, w.P)
+    ref_sel, ref_cnt = O.top_pages(sc, w.seq_lens, w.P, k)
+    assert_selection_equal(fused[0], fused[1], ref_sel, ref_cnt)
+    return fused, ref_sel
+
+
+def test_tail_merge_cases(K):
+    """The fused form selects over all pages but the tail and merges the refreshed tail page in:
+    a tail that ties the weakest chosen page stays out (the lower index wins), a tail above it
+    displaces it, and lists of at most k pages (or a single page) take the tail as one more."""
+    # every page's keys equal: all scores tie, so the first k pages are chosen, never the tail
+    w = W.custom(341, B=2, Hq=32, Hkv=8, D=128, P=32, k=8, lens=[32 * 40 - 7, 32 * 25],
+                 dtype="bf16")
+    tile = w.k_pool[0].clone()
+
+    def all_equal(pool):
+        pool[:] = tile
+
+    fused, ref_sel = _refresh_case(K, w, all_equal, w.k, "all scores tie", stale=False)
+    assert (ref_sel[:, :, : w.k] == np.arange(w.k)).all()
+    # the tail page's keys far above every other page's for the group's queries: it must enter
+
+    def planted(pool):
+        for b in range(w.B):
+            p = int(w.page_table[b, w.n_pages(b) - 1])
+            qg = w.q[b].float().reshape(w.Hkv, -1, w.D).sum(dim=1)  # [Hkv][D]
+            pool[p] = (12.0 * torch.sign(qg)[:, None, :]).expand(w.Hkv, w.P, w.D).to(pool.dtype)
+
+    fused, ref_sel = _refresh_case(K, w, planted, w.k, "planted tail")
+    for b in range(w.B):
+        assert (ref_sel[b, :, w.k - 1] == w.n_pages(b) - 1).all()
+    # lists of at most k pages, a one-page sequence and an empty one
+    w2 = W.custom(342, B=4, Hq=8, Hkv=2, D=64, P=16, k=12, lens=[16 * 12, 16 * 7 + 3, 5, 0],
+                  dtype="bf16")
+    _refresh_case(K, w2, lambda pool: None, w2.k, "N <= k, one page, empty")
+    # fp32 with many splits
+    w3 = W.custom(343, B=2, Hq=16, Hkv=4, D=128, P=32, k=40, lens=[32 * 300 - 1, 32 * 130 + 9],
+                  dtype="f32")
+    gen = torch.Generator().manual_seed(343)
+
+    def fresh_tails(pool):
+        for b in range(w3.B):
+            p = int(w3.page_table[b, w3.n_pages(b) - 1])
+            pool[p] = 3.0 * torch.randn(pool[p].shape, generator=gen)
+
+    _refresh_case(K, w3, fresh_tails, w3.k, "fp32, fresh tails")
+
+
 def test_fallback_paths_match(K):
     # k above 1024 needs splits larger than the fused launch's, and a 1500-page table is wider
     # than the fused form is taken for: the separate launches run inside the same call
