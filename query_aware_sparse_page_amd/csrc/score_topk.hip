@@ -24,6 +24,8 @@ constexpr int SEL_THREADS = 256;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
 constexpr int SEL_LDS_KEYS = 8192;
 constexpr int TOPK_BATCH = 8;  // independent score loads in flight per thread
+constexpr int TOPK_WIDE_THREADS = 1024;  // top-k block for tables wider than TOPK_SMALL_PAGES
+constexpr int TOPK_SMALL_PAGES = 4 * SEL_THREADS;
 
 // Radix-select state plus an LDS copy of the keys (block_topk, which reads scores from memory).
 template <int NT>
@@ -218,11 +220,11 @@ __device__ void select_outputs(const SelectArgs& a, int list, int N, int correct
   }
 }
 
-// Top-k of one list with C keys per thread in registers (C * SEL_THREADS >= row width). The score
+// Top-k of one list with C keys per thread in registers (C * NT >= row width). The score
 // loads depend on the row width only, so they go out before the sequence length is known.
-template <typename T, int D, int G, int C>
-__device__ void topk_regs(const SelectArgs& a, int list, int b, int j, TopkSmem<SEL_THREADS>& sm,
-                          int* s_corr) {
+template <typename T, int D, int G, int NT, int C>
+__device__ __forceinline__ void topk_regs(const SelectArgs& a, int list, int b, int j,
+                                          TopkSmem<NT>& sm, int* s_corr) {
   const int tid = threadIdx.x;
   const float* sc = a.scores + (size_t)list * a.maxp;
   float v[C];
@@ -235,37 +237,43 @@ __device__ void topk_regs(const SelectArgs& a, int list, int b, int j, TopkSmem<
   uint32_t key[C];
 #pragma unroll
   for (int u = 0; u < C; ++u) key[u] = score_key(v[u]);
-  select_outputs<SEL_THREADS>(a, list, N, corrected, reuse_on, [&](int32_t* out, int32_t* used) {
-    topk_to_list<SEL_THREADS, C>(key, N, a.k, out, used, sm);
+  select_outputs<NT>(a, list, N, corrected, reuse_on, [&](int32_t* out, int32_t* used) {
+    topk_to_list<NT, C>(key, N, a.k, out, used, sm);
   });
 }
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(SEL_THREADS) void topk_kernel(SelectArgs a) {
-  __shared__ TopkSmem<SEL_THREADS> sm;
+// One block of NT threads per list: NT = 256 for tables of at most TOPK_SMALL_PAGES pages (up to 4
+// keys per thread), 1024 for wider ones, so a 4096-page list is 4 keys per thread rather than 16
+// (measured at 128K: 9.0 us per launch with 256 threads).
+template <typename T, int D, int G, int NT>
+__global__ __launch_bounds__(NT) void topk_kernel(SelectArgs a) {
+  __shared__ TopkSmem<NT> sm;
   __shared__ int s_corr;
   const int tid = threadIdx.x;
   const int j = blockIdx.x, b = blockIdx.y;  // grid (Hkv, B)
   const int list = b * a.Hkv + j;
-  const int cpt = (a.maxp + SEL_THREADS - 1) / SEL_THREADS;  // keys per thread
-  if (cpt <= 1) return topk_regs<T, D, G, 1>(a, list, b, j, sm, &s_corr);
-  if (cpt <= 2) return topk_regs<T, D, G, 2>(a, list, b, j, sm, &s_corr);
-  if (cpt <= 4) return topk_regs<T, D, G, 4>(a, list, b, j, sm, &s_corr);
-  if (cpt <= 8) return topk_regs<T, D, G, 8>(a, list, b, j, sm, &s_corr);
-  if (cpt <= 16) return topk_regs<T, D, G, 16>(a, list, b, j, sm, &s_corr);
-  if (cpt <= 32) return topk_regs<T, D, G, 32>(a, list, b, j, sm, &s_corr);
-  // wider rows: scores re-read from memory by block_topk
-  const float* sc = a.scores + (size_t)list * a.maxp;
-  float first[TOPK_BATCH];
+  const int cpt = (a.maxp + NT - 1) / NT;  // keys per thread
+  if constexpr (NT == SEL_THREADS) {  // the host sends tables of <= 4 * NT pages here
+    if (cpt <= 1) return topk_regs<T, D, G, NT, 1>(a, list, b, j, sm, &s_corr);
+    if (cpt <= 2) return topk_regs<T, D, G, NT, 2>(a, list, b, j, sm, &s_corr);
+    return topk_regs<T, D, G, NT, 4>(a, list, b, j, sm, &s_corr);
+  } else {
+    if (cpt <= 2) return topk_regs<T, D, G, NT, 2>(a, list, b, j, sm, &s_corr);
+    if (cpt <= 4) return topk_regs<T, D, G, NT, 4>(a, list, b, j, sm, &s_corr);
+    if (cpt <= 8) return topk_regs<T, D, G, NT, 8>(a, list, b, j, sm, &s_corr);
+    // wider rows: scores re-read from memory by block_topk
+    const float* sc = a.scores + (size_t)list * a.maxp;
+    float first[TOPK_BATCH];
 #pragma unroll
-  for (int u = 0; u < TOPK_BATCH; ++u) first[u] = sc[min(tid + u * SEL_THREADS, a.maxp - 1)];
-  const int L = a.seq_lens[b];
-  const int N = L > 0 ? min((L + a.P - 1) / a.P, a.maxp) : 0;
-  const bool reuse_on = a.reuse.q_prev != nullptr;
-  const int corrected = reuse_on ? reuse_decision<T, D, G>(a, list, b, j, &s_corr) : 1;
-  select_outputs<SEL_THREADS>(a, list, N, corrected, reuse_on, [&](int32_t* out, int32_t* used) {
-    block_topk<SEL_THREADS>(sc, first, N, a.k, out, used, sm);
-  });
+    for (int u = 0; u < TOPK_BATCH; ++u) first[u] = sc[min(tid + u * NT, a.maxp - 1)];
+    const int L = a.seq_lens[b];
+    const int N = L > 0 ? min((L + a.P - 1) / a.P, a.maxp) : 0;
+    const bool reuse_on = a.reuse.q_prev != nullptr;
+    const int corrected = reuse_on ? reuse_decision<T, D, G>(a, list, b, j, &s_corr) : 1;
+    select_outputs<NT>(a, list, N, corrected, reuse_on, [&](int32_t* out, int32_t* used) {
+      block_topk<NT>(sc, first, N, a.k, out, used, sm);
+    });
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -409,8 +417,12 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.scores_only) return hipSuccess;
-  hipLaunchKernelGGL((topk_kernel<T, D, G>), dim3(a.Hkv, a.nlists / a.Hkv), dim3(SEL_THREADS), 0,
-                     stream, a);
+  if (a.maxp <= TOPK_SMALL_PAGES)
+    hipLaunchKernelGGL((topk_kernel<T, D, G, SEL_THREADS>), dim3(a.Hkv, a.nlists / a.Hkv),
+                       dim3(SEL_THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((topk_kernel<T, D, G, TOPK_WIDE_THREADS>), dim3(a.Hkv, a.nlists / a.Hkv),
+                       dim3(TOPK_WIDE_THREADS), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -213,10 +213,23 @@ def test_workspace_reuse_across_calls(K):
         assert torch.equal(sel, sel2) and torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
-@pytest.mark.parametrize("case", ["five_patterns", "all_equal", "uncached_9000_pages"])
+@pytest.mark.parametrize("case", ["five_patterns", "all_equal", "uncached_9000_pages",
+                                  "wide_1500_pages", "wide_6000_pages", "wide_ties_3000_pages"])
 def test_topk_ties_and_long_lists(K, case):
+    # tables wider than 1024 pages take the 1024-thread top-k block (2, 4 or 8 keys per thread,
+    # beyond 8192 pages the memory-resident select)
     if case == "uncached_9000_pages":
         w = W.custom(181, B=1, Hq=2, Hkv=1, D=64, P=16, k=300, lens=[16 * 9000 - 3], dtype="bf16")
+    elif case == "wide_1500_pages":
+        w = W.custom(183, B=2, Hq=8, Hkv=2, D=64, P=16, k=40, lens=[16 * 1500 - 1, 16 * 1100],
+                     dtype="bf16")
+    elif case == "wide_6000_pages":
+        w = W.custom(184, B=1, Hq=4, Hkv=2, D=64, P=16, k=130, lens=[16 * 6000 - 9], dtype="f32")
+    elif case == "wide_ties_3000_pages":
+        w = W.custom(185, B=1, Hq=4, Hkv=2, D=64, P=16, k=77, lens=[16 * 3000], dtype="bf16",
+                     permute=False)
+        for p in range(w.num_phys_pages):
+            w.k_pool[p] = w.k_pool[p % 3]  # exact copies: scores tie exactly
     else:
         w = W.custom(182, B=2, Hq=4, Hkv=2, D=64, P=16, k=17, lens=[16 * 200, 16 * 50 - 7],
                      dtype="bf16", permute=False)
