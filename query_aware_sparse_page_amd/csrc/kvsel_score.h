@@ -74,58 +74,71 @@ __device__ __forceinline__ void tile_minmax(const T* tile, int valid, int P, int
   }
 }
 
-// Scores of chunk `chunk` (WAVES * 64 / LPR consecutive pages) of list (sequence b, KV head j),
-// by one block of WAVES waves: LPR lanes read a page's lo and hi rows as 16-byte slices
-// (sequence-major summaries: one contiguous run per block), multiply by the group's query slice
-// in fp64 (a bf16 x bf16 or fp32 x fp32 product is exact in fp64), take q*hi for q >= 0 and
-// q*lo otherwise, and fold the LPR lanes; one fp64 -> fp32 rounding per score. With the tail
-// refresh on, the wave holding the sequence's last page first rebuilds that page's summary from
-// the key pool, writes it, and scores it from the fresh values.
-template <typename T, int D, int G, int WAVES>
+// Scores of chunk `chunk` (WAVES * U * 64 / LPR consecutive pages) of list (sequence b, KV head
+// j), by one block of WAVES waves: LPR lanes read a page's lo and hi rows as 16-byte slices
+// (sequence-major summaries: one contiguous run per wave and unroll step), multiply by the group's
+// query slice in fp64 (a bf16 x bf16 or fp32 x fp32 product is exact in fp64), take q*hi for
+// q >= 0 and q*lo otherwise, and fold the LPR lanes; one fp64 -> fp32 rounding per score. Each
+// lane group scores U pages (U > 1 for wide tables: fewer blocks, more loads in flight per lane).
+// With the tail refresh on, the wave holding the sequence's last page first rebuilds that page's
+// summary from the key pool, writes it, and scores it from the fresh values.
+template <typename T, int D, int G, int WAVES, int U = 1>
 __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, int chunk) {
   using M = row_map<T, D>;
   constexpr int VEC = M::VEC, LPR = M::LPR;
-  constexpr int PPW = 64 / LPR;          // pages per wave
-  constexpr int PPB = WAVES * PPW;       // pages per block
+  constexpr int PPW = 64 / LPR;          // pages per wave and unroll step
+  constexpr int PPB = WAVES * PPW * U;   // pages per block
 
   const int list = b * a.Hkv + j;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = a.P;
-  const int n0 = chunk * PPB;
+  const int wn0 = chunk * PPB + w * PPW * U;  // first page of this wave
   const int Hq = a.Hkv * G;
   const T* q = (const T*)a.q;
   const int c0 = (lane % LPR) * VEC;
-  const int n = n0 + w * PPW + lane / LPR;
+  const int rgl = lane / LPR;  // the lane's row group: page wn0 + u * PPW + rgl at step u
 
-  // ---- loads first (unconditional, clamped addresses), all in one round: the page id (used
+  // ---- loads first (unconditional, clamped addresses), all in one round: the page ids (used
   // only for the tail refresh), q slice, summary rows (sequence-major, so no page-table hop) and
   // the sequence length ----
-  const int nc = min(n, a.maxp - 1);  // from the row width only: no wait for seq_lens
-  // the page id first: the wave that refreshes the tail page waits for it alone (loads complete
-  // in issue order) and sends its key-tile loads while the summary rows are still in flight
+  // the page ids first: the wave that refreshes the tail page waits for them alone (loads
+  // complete in issue order) and sends its key-tile loads while the summary rows are in flight
   // (entries past the sequence may hold anything and are clamped into the pool, never used)
-  const int pt_raw = a.page_table[(size_t)b * a.maxp + nc];
+  int pt_raw[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)  // indices from the row width only: no wait for seq_lens
+    pt_raw[u] = a.page_table[(size_t)b * a.maxp + min(wn0 + u * PPW + rgl, a.maxp - 1)];
   uint4 qraw[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) qraw[g] = load16(q + ((size_t)b * Hq + j * G + g) * D + c0);
-  const T* srow = (const T*)a.summ + ((size_t)list * a.maxp + nc) * 2 * D + c0;
-  const uint4 lo_raw = load16(srow), hi_raw = load16(srow + D);
+  uint4 lo_raw[U], hi_raw[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int nc = min(wn0 + u * PPW + rgl, a.maxp - 1);
+    const T* srow = (const T*)a.summ + ((size_t)list * a.maxp + nc) * 2 * D + c0;
+    lo_raw[u] = load16(srow);
+    hi_raw[u] = load16(srow + D);
+  }
   __builtin_amdgcn_sched_barrier(0);
   const int L = a.seq_lens[b];
-  const int p = min(max(pt_raw, 0), a.Npp - 1);
   const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;  // never past the table row
-  const bool active = n < N;
 
   // ---- decode-time refresh of the tail page's summary, by the wave that scores that page: the
   // page id is already in its lanes, so the key tile loads go out one hop after the page table,
   // alongside the summary loads, and no other wave waits ----
-  float lo[VEC], hi[VEC];
   const int nt = N - 1;
-  const int wn0 = n0 + w * PPW;  // first page of this wave
-  if (a.refresh_tail && N > 0 && nt >= wn0 && nt < wn0 + PPW) {  // wave-uniform
-    const int rg = nt - wn0;                                   // the tail page's row group
-    const int pt = __builtin_amdgcn_readlane(p, rg * LPR);
-    float flo[VEC], fhi[VEC];
+  const bool tail = a.refresh_tail && N > 0 && nt >= wn0 && nt < wn0 + PPW * U;  // wave-uniform
+  const int t_off = nt - wn0;
+  const int ut = tail ? t_off / PPW : -1, rg = t_off % PPW;  // its unroll step and row group
+  float flo[VEC], fhi[VEC];
+  if (tail) {
+    int pt = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // scalar selects (a uniform index into pt_raw would spill it)
+      const int x = __builtin_amdgcn_readlane(pt_raw[u], rg * LPR);
+      pt = u == ut ? x : pt;
+    }
+    pt = min(max(pt, 0), a.Npp - 1);
     tile_minmax<T, D>((const T*)a.k_pool + ((size_t)pt * a.Hkv + j) * P * D, L - nt * P, P, lane,
                       pt, a.rope, flo, fhi);
     if (lane < LPR) {
@@ -133,21 +146,9 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
       store16(out + c0, pack<T>(flo));
       store16(out + D + c0, pack<T>(fhi));
     }
-    unpack<T>(lo_raw, lo);
-    unpack<T>(hi_raw, hi);
-    if (lane / LPR == rg) {  // the stale rows loaded above are replaced by the fresh ones
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        lo[e] = flo[e];
-        hi[e] = fhi[e];
-      }
-    }
-  } else {
-    unpack<T>(lo_raw, lo);
-    unpack<T>(hi_raw, hi);
   }
 
-  // ---- scores of this block's pages ----
+  // ---- scores of this wave's pages ----
   double qd[G][VEC];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -156,18 +157,36 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
 #pragma unroll
     for (int e = 0; e < VEC; ++e) qd[g][e] = (double)f[e];
   }
-  double acc = 0.0;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int u = 0; u < U; ++u) {
+    float lo[VEC], hi[VEC];
+    unpack<T>(lo_raw[u], lo);
+    unpack<T>(hi_raw[u], hi);
+    if (u == ut && rgl == rg) {  // the stale rows loaded above are replaced by the fresh ones
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const double x = (double)(qd[g][e] >= 0.0 ? hi[e] : lo[e]);
-      acc = fma(qd[g][e], x, acc);
+      for (int e = 0; e < VEC; ++e) {
+        lo[e] = flo[e];
+        hi[e] = fhi[e];
+      }
     }
+    double acc = 0.0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const double x = (double)(qd[g][e] >= 0.0 ? hi[e] : lo[e]);
+        acc = fma(qd[g][e], x, acc);
+      }
+    }
+    acc = seg_sum_f64<LPR>(acc);
+    const int n = wn0 + u * PPW + rgl;
+    if (n < N && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
   }
-  acc = seg_sum_f64<LPR>(acc);
-  if (active && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
 }
+
+// Unroll (pages per lane group) of the score kernel for a table width: wide tables take fewer,
+// fuller blocks.
+inline int score_unroll(int maxp) { return maxp <= 1024 ? 1 : maxp <= 2048 ? 2 : 4; }
 
 // Group-mean cosine similarity of this step's and the previous step's queries for KV head j of
 // sequence b, by one wave, in fp64: for each of the G heads, dot / (|q| |q_prev|) with the

@@ -160,10 +160,10 @@ __device__ void block_topk(const float* __restrict__ sc, const float* first, int
   }
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int U>
 __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   // grid (Hkv, B, chunks): the indices need no division; KV heads vary fastest
-  score_block<T, D, G, SEL_WAVES>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  score_block<T, D, G, SEL_WAVES, U>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // block_topk_regs writing the ascending list to out (and used, when non-null), padded with -1.
@@ -392,10 +392,11 @@ static int pages_per_select_block() {
 }
 
 int select_blocks_per_list(const LaunchKV& kv) {
-  const int ppb = kv.dtype == 0 ? (kv.D == 64 ? pages_per_select_block<float, 64>()
-                                              : pages_per_select_block<float, 128>())
-                                : (kv.D == 64 ? pages_per_select_block<bf16_t, 64>()
-                                              : pages_per_select_block<bf16_t, 128>());
+  const int ppb = (kv.dtype == 0 ? (kv.D == 64 ? pages_per_select_block<float, 64>()
+                                               : pages_per_select_block<float, 128>())
+                                 : (kv.D == 64 ? pages_per_select_block<bf16_t, 64>()
+                                               : pages_per_select_block<bf16_t, 128>())) *
+                  score_unroll(kv.maxp);
   return (kv.maxp + ppb - 1) / ppb;
 }
 
@@ -412,8 +413,12 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t stream) {
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((score_kernel<T, D, G>), dim3(a.Hkv, a.nlists / a.Hkv, a.nchunks), dim3(SEL_THREADS),
-                     0, stream, a);
+  const dim3 sgrid(a.Hkv, a.nlists / a.Hkv, a.nchunks);
+  switch (score_unroll(a.maxp)) {
+    case 1: hipLaunchKernelGGL((score_kernel<T, D, G, 1>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((score_kernel<T, D, G, 2>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
+    default: hipLaunchKernelGGL((score_kernel<T, D, G, 4>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.scores_only) return hipSuccess;

@@ -239,8 +239,15 @@ def test_topk_ties_and_long_lists(K, case):
     say(f"top-k stress {case}: N={[w.n_pages(b) for b in range(w.B)]} k={w.k}")
     kv = kv_of(K, w)
     summ = K.build_summaries(kv)
+    refresh = case.startswith("wide")
+    if refresh:  # new keys in every tail page after the summaries: the refresh must rebuild them
+        gen = torch.Generator().manual_seed(7)
+        for b in range(w.B):
+            p = int(w.page_table[b, w.n_pages(b) - 1])
+            w.k_pool[p] = (4.0 * torch.randn(w.k_pool[p].shape, generator=gen)).to(w.k_pool.dtype)
+            kv.k_pool[p] = w.k_pool[p].cuda()
     sc = torch.full((w.B, w.Hkv, w.max_pages), float("nan"), device="cuda")
-    sel, cnt = K.score_topk(kv, summ, w.q.cuda(), w.k, scores=sc)
+    sel, cnt = K.score_topk(kv, summ, w.q.cuda(), w.k, scores=sc, refresh_tail=refresh)
     torch.cuda.synchronize()
     ref_summ = O.page_summaries(w.k_pool, w.page_table, w.seq_lens, w.P)
     ref_sc = O.page_scores(w.q, ref_summ, w.page_table, w.seq_lens, w.P)
