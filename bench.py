@@ -494,7 +494,9 @@ def main():
             "two_call_us_per_step": round(s["us_two_calls"], 3), "attn_us": round(s["attn_us"], 3),
             "attn_GBps": round(sach, 1), "attn_frac": round(sach / HBM_PEAK_GBPS, 4),
             "select_us": round(s["select_us"], 3), "attn_bytes": s["attn_bytes"],
-            "layers_rotated": n_layers}
+            "layers_rotated": n_layers,
+            "gather_probe": {"avg_us": round(s["probe_us"], 3),
+                             "GBps": round(s["probe_bytes"] / (s["probe_us"] * 1e-6) / 1e9, 1)}}
         progress(f"{name}: step {s['us_step']:.3f} us, attention call {s['attn_us']:.3f} us")
         del s
         torch.cuda.empty_cache()
