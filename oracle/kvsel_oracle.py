@@ -46,6 +46,7 @@ __all__ = [
     "as_f64",
     "n_pages",
     "page_summaries",
+    "append_tokens",
     "page_scores",
     "top_pages",
     "selection_margin_ulps",
@@ -121,6 +122,39 @@ def page_summaries(k_pool, page_table, seq_lens, page_size: int) -> np.ndarray:
             summ[p, :, 0, :] = toks.min(axis=1)
             summ[p, :, 1, :] = toks.max(axis=1)
     return summ
+
+
+def append_tokens(k_pool, v_pool, page_table, seq_lens, k_new, v_new, page_size: int):
+    """One decode step's append of a token's key and value to every sequence.
+
+    [KV-Cache wiki] "Synthesized Content": a decode step stores the new token's key and value and
+    keeps every earlier one. In the paged layout ("Contradictions & Updates", PagedAttention) the
+    token at position L = seq_lens[b] lives in slot L % P of logical page L // P, i.e. physical
+    page page_table[b][L // P] (reading: the caller's page allocator has set that table entry
+    when the token opens a new page). A sequence whose table has no room (L == width * P) is left
+    unchanged and reported.
+
+    k_new, v_new: ``[B][Hkv][D]``. Pools in the oracle layout ``[Npp][Hkv][P][D]`` (both K and V).
+    Returns (k_pool, v_pool, seq_lens, rejected) as new arrays; ``rejected[b]`` is True where
+    nothing was written.
+    """
+    K = np.array(k_pool, copy=True)
+    V = np.array(v_pool, copy=True)
+    table = _ints(page_table)
+    lens = _ints(seq_lens).copy()
+    kn, vn = np.asarray(k_new), np.asarray(v_new)
+    width = table.shape[1]
+    rejected = np.zeros(len(lens), dtype=bool)
+    for b in range(len(lens)):
+        L = int(lens[b])
+        if L < 0 or L >= width * page_size:
+            rejected[b] = True
+            continue
+        p = int(table[b, L // page_size])
+        K[p, :, L % page_size, :] = kn[b]
+        V[p, :, L % page_size, :] = vn[b]
+        lens[b] = L + 1
+    return K, V, lens, rejected
 
 
 # ----------------------------------------------------------------------------------------------

@@ -81,6 +81,85 @@ def test_planted_summary_mistakes_are_caught(mistake):
 
 
 # ----------------------------------------------------------------------------------------------
+# decode-time append
+# ----------------------------------------------------------------------------------------------
+
+def check_append(fn, lens):
+    """A cache filled one token at a time from empty equals the cache built at once: every valid
+    slot holds the reference key and value, nothing else is written, the lengths match, and a
+    full table refuses the next token."""
+    w = W.custom(17, B=len(lens), Hq=4, Hkv=2, D=8, P=4, k=2, lens=lens, dtype="f32")
+    Kref, Vref = w.k_pool.double().numpy(), w.v_pool.double().numpy()
+    table = w.page_table.numpy()
+    K = np.full_like(Kref, np.nan)
+    V = np.full_like(Vref, np.nan)
+    cur = np.zeros(w.B, dtype=np.int64)
+    Lmax = int(max(lens))
+    for t in range(Lmax):
+        kn = np.zeros((w.B, w.Hkv, w.D))
+        vn = np.zeros((w.B, w.Hkv, w.D))
+        for b in range(w.B):
+            if t < lens[b]:  # the reference token at position t
+                p, sl = int(table[b, t // w.P]), t % w.P
+                kn[b], vn[b] = Kref[p, :, sl, :], Vref[p, :, sl, :]
+        K2, V2, cur2, rej = fn(K, V, table, cur, kn, vn, w.P)
+        for b in range(w.B):  # sequences already complete keep their state
+            if t >= lens[b]:
+                K2, V2 = K2.copy(), V2.copy()
+                if not rej[b]:
+                    p, sl = int(table[b, int(cur[b]) // w.P]), int(cur[b]) % w.P
+                    K2[p, :, sl, :], V2[p, :, sl, :] = K[p, :, sl, :], V[p, :, sl, :]
+                cur2[b] = cur[b]
+        K, V, cur = K2, V2, cur2
+    if list(cur) != list(lens):
+        return False
+    for b in range(w.B):
+        for t in range(Lmax):
+            p, sl = int(table[b, t // w.P]), t % w.P
+            if t < lens[b]:
+                if not (np.array_equal(K[p, :, sl], Kref[p, :, sl])
+                        and np.array_equal(V[p, :, sl], Vref[p, :, sl])):
+                    return False
+            elif t // w.P < -(-lens[b] // w.P) and not np.isnan(K[p, :, sl]).all():
+                return False  # a slot past the length was written
+    # a full table takes no further token
+    full = np.array([table.shape[1] * w.P] * w.B)
+    _, _, cur3, rej = fn(K, V, table, full, np.ones((w.B, w.Hkv, w.D)), np.ones((w.B, w.Hkv, w.D)),
+                         w.P)
+    return bool(rej.all()) and list(cur3) == list(full)
+
+
+@pytest.mark.parametrize("lens", [[21, 21], [9, 16, 3], [1, 4, 5]])
+def test_append_builds_the_cache_token_by_token(lens):
+    assert check_append(O.append_tokens, lens)
+
+
+@pytest.mark.parametrize("mistake", ["next_slot", "slot_as_page", "keeps_length", "no_bound"])
+def test_planted_append_mistakes_are_caught(mistake):
+    def broken(k_pool, v_pool, page_table, seq_lens, k_new, v_new, P):
+        lens = np.asarray(seq_lens)
+        if mistake == "next_slot":  # writes one position too far
+            return O.append_tokens(k_pool, v_pool, page_table, lens + 1, k_new, v_new, P)[:2] + \
+                O.append_tokens(k_pool, v_pool, page_table, lens, k_new, v_new, P)[2:]
+        if mistake == "slot_as_page":  # logical page from the slot instead of the position
+            K, V = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+            out = lens.copy()
+            for b in range(len(lens)):
+                L = int(lens[b])
+                p = int(np.asarray(page_table)[b, L % P])
+                K[p, :, L % P], V[p, :, L % P] = k_new[b], v_new[b]
+                out[b] = L + 1
+            return K, V, out, np.zeros(len(lens), dtype=bool)
+        if mistake == "keeps_length":
+            K, V, _, rej = O.append_tokens(k_pool, v_pool, page_table, lens, k_new, v_new, P)
+            return K, V, lens.copy(), rej
+        K, V, out, rej = O.append_tokens(k_pool, v_pool, page_table, lens, k_new, v_new, P)
+        return K, V, np.where(rej, lens + 1, out), np.zeros_like(rej)  # full tables accepted
+
+    assert not all(check_append(broken, lens) for lens in ([21, 21], [9, 16, 3]))
+
+
+# ----------------------------------------------------------------------------------------------
 # a2 scores
 # ----------------------------------------------------------------------------------------------
 
