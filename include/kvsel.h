@@ -244,6 +244,26 @@ kvsel_status kvsel_speculative_step(const kvsel_paged_kv* kv, const kvsel_rope* 
                                     void* out, float* lse, void* ws, size_t ws_bytes,
                                     void* stream);
 
+/* Decode-time append ([KV wiki]: a decode step stores the new token's key and value and keeps
+ * every earlier one). For every sequence b with L = seq_lens[b] in [0, max_pages_per_seq * P):
+ * writes k_new[b][j][:] into slot L % P of logical page L / P (physical page
+ * page_table[b][L / P]) of the key pool and v_new[b][j][:] into the same slot of the value pool,
+ * for every KV head j; when summ is non-NULL, keeps that page's summary current: a token that
+ * opens a page (L % P == 0) sets lo = hi = its key, any other takes lo = min(lo, key),
+ * hi = max(hi, key) -- equal to kvsel_build_summaries' rebuild of the page when the summary was
+ * current before the call; then writes seq_lens_out[b] = L + 1.
+ * A sequence with no room (L == max_pages_per_seq * P) or L < 0 is left unchanged and, when flags
+ * is non-NULL, KVSEL_CHECK_SEQ_LEN is ORed into *flags (device uint32).
+ * The table entry of a page the token opens is the caller's page allocator's to set before the
+ * call (an entry outside the pool is clamped into it, as by every reader). kv->k_pool and
+ * kv->v_pool are written despite the descriptor's const qualifiers. Keys are stored as given: with
+ * a rotary gather, store keys already at their positions, on pages whose page_row is -1.
+ * k_new, v_new: [B][Hkv][D] element type. seq_lens_out: int32 [B], may equal kv->seq_lens (in
+ * place). summ: [B][Hkv][max_pages_per_seq][2][D] as kvsel_build_summaries writes it, or NULL.
+ * One launch of one block per sequence. */
+kvsel_status kvsel_append_kv(const kvsel_paged_kv* kv, const void* k_new, const void* v_new,
+                             void* summ, int32_t* seq_lens_out, uint32_t* flags, void* stream);
+
 /* Device-side check of the contents every other entry point takes on trust (the host cannot
  * read device memory before enqueuing): ORs into *flags (device uint32, sticky: bits are set,
  * never cleared by the library)

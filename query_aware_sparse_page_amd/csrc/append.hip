@@ -1,0 +1,129 @@
+// Decode-time append: each sequence's new token key and value go into the tail page of the paged
+// cache, and that page's summary is kept current without re-reading the page.
+//
+// One block per sequence, one wave per KV head in turn: LPR lanes carry the head's D channels as
+// 16-byte slices. The key row is one 16-byte store per lane (token-major K pages); the value is a
+// column of the channel-major V page (one element per channel, at stride P), written element by
+// element as raw bits. The summary of a page that the token opens is the key itself (lo = hi);
+// otherwise lo = min(lo, key), hi = max(hi, key) over the stored row -- exactly the rebuild of
+// the page's valid keys when the stored summary covered the earlier ones (min and max are exact).
+// The sequence length is read by every thread first and written once after a barrier, so the
+// output may be the length array itself.
+#include "kvsel_device.h"
+#include "kvsel_internal.h"
+
+namespace kvsel {
+
+constexpr int APPEND_THREADS = 256;
+
+struct AppendArgs {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int32_t* seq_lens_out;
+  const void* k_new;  // [B][Hkv][D]
+  const void* v_new;  // [B][Hkv][D]
+  void* summ;         // [B][Hkv][maxp][2][D], may be null
+  uint32_t* flags;    // may be null
+  int Hkv, P, maxp, Npp;
+};
+
+// The raw element bits of one 16-byte slice, one element at a time.
+template <typename T>
+__device__ __forceinline__ void store_slice_column(T* base, size_t stride, const uint4& v);
+template <>
+__device__ __forceinline__ void store_slice_column<float>(float* base, size_t stride, const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) reinterpret_cast<uint32_t*>(base)[e * stride] = w[e];
+}
+template <>
+__device__ __forceinline__ void store_slice_column<bf16_t>(bf16_t* base, size_t stride,
+                                                           const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    reinterpret_cast<uint16_t*>(base)[e * stride] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendArgs a) {
+  using M = row_map<T, D>;
+  constexpr int VEC = M::VEC, LPR = M::LPR;
+  constexpr int NW = APPEND_THREADS / 64;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int L = a.seq_lens[b];
+  const bool ok = L >= 0 && (long)L < (long)a.maxp * a.P;  // room for one more token
+  if (ok) {
+    const int n = L / a.P, slot = L - n * a.P;
+    // the caller's allocator set this entry when the token opens a page; clamp like every reader
+    const int p = min(max(a.page_table[(size_t)b * a.maxp + n], 0), a.Npp - 1);
+    const int c0 = lane * VEC;
+    for (int j = w; j < a.Hkv; j += NW) {
+      if (lane < LPR) {
+        const size_t in = ((size_t)b * a.Hkv + j) * D + c0;
+        const uint4 kv = load16((const T*)a.k_new + in);
+        const uint4 vv = load16((const T*)a.v_new + in);
+        store16((T*)a.k_pool + (((size_t)p * a.Hkv + j) * a.P + slot) * D + c0, kv);
+        store_slice_column<T>((T*)a.v_pool + (((size_t)p * a.Hkv + j) * D + c0) * a.P + slot,
+                              (size_t)a.P, vv);
+        if (a.summ) {
+          T* row = (T*)a.summ + (((size_t)b * a.Hkv + j) * a.maxp + n) * 2 * D + c0;
+          uint4 lo = kv, hi = kv;
+          if (slot > 0) {
+            float k[VEC], l0[VEC], h0[VEC];
+            unpack<T>(kv, k);
+            unpack<T>(load16(row), l0);
+            unpack<T>(load16(row + D), h0);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+              l0[e] = fminf(l0[e], k[e]);
+              h0[e] = fmaxf(h0[e], k[e]);
+            }
+            lo = pack<T>(l0);
+            hi = pack<T>(h0);
+          }
+          store16(row, lo);
+          store16(row + D, hi);
+        }
+      }
+    }
+  } else if (a.flags && tid == 0) {
+    atomicOr(a.flags, 1u);  // KVSEL_CHECK_SEQ_LEN
+  }
+  __syncthreads();  // every thread has read the length before it changes
+  if (ok && tid == 0) a.seq_lens_out[b] = L + 1;
+}
+
+template <typename T>
+static void launch_append_t(int D, const AppendArgs& a, int B, hipStream_t stream) {
+  if (D == 64)
+    hipLaunchKernelGGL((append_kernel<T, 64>), dim3(B), dim3(APPEND_THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((append_kernel<T, 128>), dim3(B), dim3(APPEND_THREADS), 0, stream, a);
+}
+
+hipError_t launch_append(const LaunchKV& kv, const void* k_new, const void* v_new, void* summ,
+                         int32_t* seq_lens_out, uint32_t* flags, hipStream_t stream) {
+  AppendArgs a;
+  a.k_pool = const_cast<void*>(kv.k_pool);
+  a.v_pool = const_cast<void*>(kv.v_pool);
+  a.page_table = kv.page_table;
+  a.seq_lens = kv.seq_lens;
+  a.seq_lens_out = seq_lens_out;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.summ = summ;
+  a.flags = flags;
+  a.Hkv = kv.Hkv;
+  a.P = kv.P;
+  a.maxp = kv.maxp;
+  a.Npp = kv.Npp;
+  if (kv.dtype == 0) launch_append_t<float>(kv.D, a, kv.B, stream);
+  else launch_append_t<bf16_t>(kv.D, a, kv.B, stream);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

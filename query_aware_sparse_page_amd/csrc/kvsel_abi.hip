@@ -251,6 +251,17 @@ kvsel_status kvsel_check_inputs(const kvsel_paged_kv* kv, const int32_t* sel_idx
   return launch_status(launch_check_inputs(f, sel_idx, sel_cnt, k, flags, (hipStream_t)stream));
 }
 
+kvsel_status kvsel_append_kv(const kvsel_paged_kv* kv, const void* k_new, const void* v_new,
+                             void* summ, int32_t* seq_lens_out, uint32_t* flags, void* stream) {
+  LaunchKV f;
+  kvsel_status st = flatten(kv, 3, &f);
+  if (st != KVSEL_OK) return st;
+  if (!k_new || !v_new || !seq_lens_out) return KVSEL_ERR_INVALID_ARGUMENT;
+  if ((st = check_device()) != KVSEL_OK) return st;
+  return launch_status(launch_append(f, k_new, v_new, summ, seq_lens_out, flags,
+                                     (hipStream_t)stream));
+}
+
 kvsel_status kvsel_gather_probe(const uint64_t* chunk_addr, int32_t n_chunks, int32_t chunk_bytes,
                                 uint32_t* sink, void* stream) {
   if (!chunk_addr || !sink || n_chunks < 1 || n_chunks > (1 << 26)) return KVSEL_ERR_INVALID_ARGUMENT;

@@ -80,6 +80,7 @@ EXPORTS = {
                                        c_vp, c_i32, c_i32, ctypes.c_float,
                                        ctypes.POINTER(ReuseDesc), c_vp, c_vp, c_vp, c_vp, c_vp,
                                        ctypes.c_size_t, c_vp]),
+    "kvsel_append_kv": (c_i32, [ctypes.POINTER(PagedKVDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "kvsel_check_inputs": (c_i32, [ctypes.POINTER(PagedKVDesc), c_vp, c_vp, c_i32, c_vp, c_vp]),
     "kvsel_gather_probe": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp]),
     "kvsel_rope_table": (c_i32, [ctypes.c_double, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
@@ -420,6 +421,33 @@ def tile_addresses(kv: PagedKV, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
                 addrs.append(kb + off)
                 addrs.append(vb + off)
     return torch.tensor(addrs, dtype=torch.int64).to(kv.device)
+
+
+def append_kv(kv: PagedKV, k_new: torch.Tensor, v_new: torch.Tensor,
+              summ: Optional[torch.Tensor] = None, seq_lens_out: Optional[torch.Tensor] = None,
+              flags: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode-time append of one token per sequence (k_new, v_new [B][Hkv][D]) into the pools,
+    with the tail page's summary kept current when ``summ`` is given. Writes the new lengths to
+    ``seq_lens_out`` (default: kv.seq_lens, in place) and returns it. The page-table entry of a
+    page a token opens must be set by the caller first."""
+    d = kv.desc()
+    dev = kv.device
+    if kv.v_pool is None:
+        raise ValueError("append_kv needs the value pool")
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, name, kv.k_pool.dtype)
+        if tuple(t.shape) != (kv.batch, kv.num_kv_heads, kv.head_dim):
+            raise ValueError(f"{name} must be [B][Hkv][D]")
+    if summ is not None:
+        _check_summ(kv, summ)
+    if seq_lens_out is None:
+        seq_lens_out = kv.seq_lens
+    _dev(seq_lens_out, "seq_lens_out", torch.int32)
+    if flags is not None:
+        _dev(flags, "flags", torch.int32)
+    _check(lib().kvsel_append_kv(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(summ),
+                                 _ptr(seq_lens_out), _ptr(flags), _stream(dev)))
+    return seq_lens_out
 
 
 def check_inputs(kv: PagedKV, sel_idx: Optional[torch.Tensor] = None,

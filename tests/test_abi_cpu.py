@@ -144,3 +144,17 @@ def test_check_inputs_validation(K):
     assert lib.kvsel_check_inputs(ctypes.byref(d), p, p, 0, p, None) == 1            # k < 1
     dn = _desc(K, page_table=None)
     assert lib.kvsel_check_inputs(ctypes.byref(dn), None, None, 0, p, None) == 1
+
+
+def test_append_validation(K):
+    lib = K.lib()
+    d = _desc(K)
+    p = ctypes.c_void_p(0x5000)
+    assert lib.kvsel_append_kv(ctypes.byref(d), None, p, p, p, None, None) == 1      # no k_new
+    assert lib.kvsel_append_kv(ctypes.byref(d), p, None, p, p, None, None) == 1      # no v_new
+    assert lib.kvsel_append_kv(ctypes.byref(d), p, p, None, None, None, None) == 1   # no lengths out
+    dv = _desc(K, v_pool=None)
+    assert lib.kvsel_append_kv(ctypes.byref(dv), p, p, None, p, None, None) == 1     # no V pool
+    dn = _desc(K, page_table=None)
+    assert lib.kvsel_append_kv(ctypes.byref(dn), p, p, None, p, None, None) == 1
+    assert lib.kvsel_append_kv(ctypes.byref(_desc(K, head_dim=96)), p, p, None, p, None, None) == 2

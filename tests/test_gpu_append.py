@@ -1,0 +1,104 @@
+"""kvsel_append_kv against the oracle's append, bit for bit: the pools, the lengths, and the tail
+summaries it keeps current without a rebuild (checked after every step against the oracle's
+summaries of the grown cache); the full-table refusal; and a decode step on the grown cache
+against the oracle."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_common import (assert_attention_close, assert_selection_equal, assert_summaries_equal,
+                        kv_of, oracle_path, say, scale_of)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from query_aware_sparse_page_amd import kvsel as K
+    K.lib()  # raises if libkvsel.so is missing: no fallback
+    return K
+
+
+def grown_case(seed, dtype, D, P, lens, T, Hq=8, Hkv=2, k=8):
+    """A cache with room for T more tokens per sequence: the table is widened and every page the
+    appends will open is given a spare physical page up front (the caller's allocator)."""
+    extra = sum(-(-(L + T) // P) - -(-L // P) for L in lens)
+    w = W.custom(seed, B=len(lens), Hq=Hq, Hkv=Hkv, D=D, P=P, k=k, lens=lens, dtype=dtype,
+                 spare_pages=extra)
+    width = max(-(-(L + T) // P) for L in lens)
+    table = torch.zeros((w.B, width), dtype=torch.int32)
+    table[:, : w.max_pages] = w.page_table
+    used = {int(w.page_table[b, n]) for b in range(w.B) for n in range(w.n_pages(b))}
+    spare = [p for p in range(w.num_phys_pages) if p not in used]
+    for b, L in enumerate(lens):
+        for n in range(-(-L // P), -(-(L + T) // P)):
+            table[b, n] = spare.pop()
+    return dataclasses.replace(w, page_table=table)
+
+
+CASES = [("bf16", 128, 32), ("bf16", 64, 16), ("f32", 128, 16), ("f32", 64, 32)]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_append_matches_oracle(K, case):
+    dtype, D, P = case
+    lens = [2 * P + 8, P - 1, 0, P, 1]
+    T = P + 5  # crosses a page boundary in every sequence
+    w = grown_case(711, dtype, D, P, lens, T)
+    say(f"append {case}: lens {lens}, {T} steps")
+    kv = kv_of(K, w)
+    summ = K.build_summaries(kv)
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Kc, Vc = w.k_pool.double().numpy(), w.v_pool.double().numpy()
+    cur = w.seq_lens.numpy().astype(np.int64)
+    gen = torch.Generator().manual_seed(712)
+    tdt = w.k_pool.dtype
+    for t in range(T):
+        kn = torch.randn((w.B, w.Hkv, D), generator=gen).to(tdt)
+        vn = torch.randn((w.B, w.Hkv, D), generator=gen).to(tdt)
+        K.append_kv(kv, kn.cuda(), vn.cuda(), summ=summ, flags=flags)
+        Kc, Vc, cur, rej = O.append_tokens(Kc, Vc, w.page_table, cur, kn.double().numpy(),
+                                           vn.double().numpy(), P)
+        assert not rej.any()
+        torch.cuda.synchronize()
+        assert list(kv.seq_lens.cpu().numpy()) == list(cur), f"lengths after step {t}"
+        wt = dataclasses.replace(w, seq_lens=torch.from_numpy(cur.astype(np.int32)))
+        assert_summaries_equal(summ, O.page_summaries(Kc, w.page_table, wt.seq_lens, P), wt)
+    assert int(flags.item()) == 0
+    assert np.array_equal(kv.k_pool.double().cpu().numpy(), Kc)
+    assert np.array_equal(kv.v_pool.permute(0, 1, 3, 2).double().cpu().numpy(), Vc)
+    # a decode step on the grown cache (summaries current: no refresh)
+    wg = dataclasses.replace(w, seq_lens=torch.from_numpy(cur.astype(np.int32)),
+                             k_pool=torch.from_numpy(Kc).to(tdt), v_pool=torch.from_numpy(Vc).to(tdt))
+    ref = oracle_path(wg, scale_of(D))
+    sel, cnt, out, lse = K.select_attend(kv, summ, w.q.cuda(), w.k)
+    torch.cuda.synchronize()
+    assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["margins"])
+    assert_attention_close(out, lse, ref["out"], ref["lse"], dtype)
+
+
+def test_append_refuses_a_full_table(K):
+    w = W.custom(713, B=2, Hq=8, Hkv=2, D=64, P=16, k=4, lens=[32, 10], dtype="bf16")
+    say("append: full table")
+    kv = kv_of(K, w)
+    summ = K.build_summaries(kv)
+    before_k = kv.k_pool.clone()
+    before_s = summ.clone()
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kn = torch.ones((2, 2, 64), dtype=torch.bfloat16, device="cuda")
+    out_lens = torch.empty(2, dtype=torch.int32, device="cuda")
+    out_lens.copy_(kv.seq_lens)
+    K.append_kv(kv, kn, kn, summ=summ, seq_lens_out=out_lens, flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) & 1
+    assert out_lens.tolist() == [32, 11] and kv.seq_lens.tolist() == [32, 10]
+    p0 = [int(x) for x in w.page_table[0, :2]]
+    assert torch.equal(kv.k_pool[p0], before_k[p0])  # the full sequence's pages untouched
+    assert torch.equal(summ[0], before_s[0])
+    p1 = int(w.page_table[1, 0])
+    assert torch.equal(kv.k_pool[p1, :, 10], kn[1])  # the other sequence took its token
