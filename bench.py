@@ -337,6 +337,105 @@ def speculative(dev, reps=3):
                     "kvsel_sparse_decode_attn over the used pages"}
 
 
+def speculative_growing(dev, reps=3):
+    """The speculative workload as a growing-context decode loop: each of the 64 steps appends the
+    new token's key and value (kvsel_append_kv, which keeps the tail page's summary current, so no
+    refresh is needed), then runs the speculative step over the grown cache (32768 -> 32832
+    tokens; the table and pool have two more pages for them; the new keys are stored as given,
+    without a rotary shift). The graph of 64 steps starts by resetting the length, so every replay
+    grows the same cache. Reports µs per step (append + speculative step) against the serial
+    calls (append + kvsel_score_topk with reuse + kvsel_sparse_decode_attn)."""
+    w = W.speculative_rope()
+    bt = w.extra["block_tokens"]
+    blocks = bt // w.P
+    npg = w.num_phys_pages
+    qs = w.extra["q_steps"].to(dev)
+    T, tau = qs.shape[0], w.extra["tau"]
+    extra = -(-T // w.P)
+    cos, sin = K.rope_table(w.extra["theta"], w.D, 0, 8 * bt, dev)
+    kv_raw = K.PagedKV(w.k_pool.to(dev), K.device_v_layout(w.v_pool.to(dev)),
+                       w.page_table.to(dev), w.seq_lens.to(dev), w.Hq)
+    enc_row = torch.from_numpy(((np.arange(npg) % blocks) * w.P).astype(np.int32)).to(dev)
+    enc = K.rope_shift(kv_raw, K.Rope(cos, sin, enc_row, 1))  # the precomputed blocks
+    k_pool = torch.cat([enc, torch.zeros((extra,) + tuple(enc.shape[1:]), dtype=enc.dtype,
+                                         device=dev)])
+    v_pool = torch.cat([kv_raw.v_pool, torch.zeros((extra,) + tuple(kv_raw.v_pool.shape[1:]),
+                                                   dtype=enc.dtype, device=dev)])
+    table = torch.zeros((w.B, w.max_pages + extra), dtype=torch.int32)
+    table[:, : w.max_pages] = w.page_table
+    table[0, w.max_pages:] = torch.arange(npg, npg + extra, dtype=torch.int32)
+    lens0 = w.seq_lens.to(dev)
+    lens = lens0.clone()
+    kv = K.PagedKV(k_pool, v_pool, table.to(dev), lens, w.Hq,
+                   max_seq_len=int(w.seq_lens.max()) + T)  # the longest length the loop reaches
+    shift_row = torch.full((npg + extra,), -1, dtype=torch.int32)
+    shift_row[:npg] = torch.from_numpy(((np.arange(npg) // blocks) * bt).astype(np.int32))
+    shift = K.Rope(cos, sin, shift_row.to(dev), 0)
+    summ = K.build_summaries(kv, rope=shift)
+    ks, vs = W.appended_tokens(w, T, seed=2005)
+    ks, vs = ks.to(dev), vs.to(dev)
+    B, Hkv, k = w.B, w.Hkv, w.k
+    sel = torch.zeros((T, B, Hkv, k), dtype=torch.int32, device=dev)
+    cnt = torch.zeros((T, B, Hkv), dtype=torch.int32, device=dev)
+    out = torch.empty((T,) + tuple(w.q.shape), dtype=qs.dtype, device=dev)
+    lse = torch.empty((T, B, w.Hq), dtype=torch.float32, device=dev)
+    ws_s = K.new_workspace(kv, k, K.KVSEL_OP_SCORE_TOPK)
+    ws_a = K.new_workspace(kv, k, K.KVSEL_OP_ATTENTION)
+    ws_f = K.new_workspace(kv, k, K.KVSEL_OP_SPECULATIVE_STEP)
+
+    def reuse(t):
+        return K.Reuse(qs[t - 1] if t else qs[t], sel[t - 1] if t else sel[t],
+                       cnt[t - 1] if t else cnt[t], tau, first_step=(t == 0))
+
+    def loop_serial():
+        lens.copy_(lens0)
+        for t in range(T):
+            K.append_kv(kv, ks[t], vs[t], summ=summ)
+            r = K.score_topk(kv, summ, qs[t], k, sel_idx=sel[t], sel_cnt=cnt[t], workspace=ws_s,
+                             reuse=reuse(t))
+            K.sparse_decode_attn(kv, qs[t], r[2], r[3], k, rope=shift, out=out[t], lse=lse[t],
+                                 workspace=ws_a)
+
+    def loop_speculative():
+        lens.copy_(lens0)
+        for t in range(T):
+            K.append_kv(kv, ks[t], vs[t], summ=summ)
+            K.speculative_step(kv, summ, qs[t], k, reuse(t), rope=shift, sel_idx=sel[t],
+                               sel_cnt=cnt[t], out=out[t], lse=lse[t], workspace=ws_f)
+
+    def timed(loop):
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            loop()
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            loop()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / (reps * T)
+
+    us_serial = timed(loop_serial)
+    out_serial = out.clone()
+    us = timed(loop_speculative)
+    torch.cuda.synchronize()
+    return {"us_per_step": round(us, 3), "serial_us_per_step": round(us_serial, 3),
+            "speculative_equals_serial": bool(torch.equal(out, out_serial)),
+            "final_len": int(lens.item()), "steps": T,
+            "step": "kvsel_append_kv, then kvsel_speculative_step over the grown cache (warm); "
+                    "serial: kvsel_append_kv, kvsel_score_topk with reuse, "
+                    "kvsel_sparse_decode_attn"}
+
+
 def cpu_baseline(w, lay, budget_s=12.0):
     """The oracle's decode step (tail summary + scores + top-k + attention) on the host, for a
     bounded number of repetitions of the same workload; also checks the GPU's step output."""
@@ -503,6 +602,9 @@ def main():
     if not args.no_secondary:
         result.setdefault("secondary", {})["speculative_rope_64_steps"] = speculative(dev)
         progress("speculative workload done")
+        torch.cuda.empty_cache()
+        result["secondary"]["speculative_growing_64_steps"] = speculative_growing(dev)
+        progress("growing speculative workload done")
         torch.cuda.empty_cache()
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, keep)

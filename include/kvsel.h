@@ -34,8 +34,9 @@
  *  - `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues work and returns
  *    without synchronizing; outputs are ready when the stream reaches that point.
  *  - Errors: arguments are validated on the host BEFORE anything is enqueued, so a failing call
- *    has no effect. Device-side contents (page ids in range, seq_lens <= max_pages_per_seq * P,
- *    selected ids < N_b) are the caller's contract and are not checked.
+ *    has no effect. Device-side contents (page ids in range, seq_lens <= the live bound, i.e.
+ *    max_seq_len if set, else max_pages_per_seq * P; selected ids < N_b) are the caller's
+ *    contract and are not checked.
  */
 #ifndef KVSEL_H
 #define KVSEL_H
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KVSEL_ABI_VERSION 1
+#define KVSEL_ABI_VERSION 2
 
 typedef int32_t kvsel_status;
 #define KVSEL_OK 0
@@ -87,7 +88,18 @@ typedef struct kvsel_paged_kv {
   const void* v_pool;        /* [num_phys_pages][Hkv][D][P] (may be NULL where unused) */
   const int32_t* page_table; /* [B][max_pages_per_seq]                               */
   const int32_t* seq_lens;   /* [B]                                                  */
+  int32_t max_seq_len;       /* 0, or the caller's bound on every seq_lens[b] (host)  */
 } kvsel_paged_kv;
+
+/* max_seq_len: page tables are usually allocated for the longest context a sequence may reach,
+ * while the lengths live on the device. A non-zero max_seq_len tells the library how many pages
+ * are live at most, ceil(max_seq_len / page_size) (capped at max_pages_per_seq), so launch grids
+ * and per-thread key counts follow the live length, not the table width; strides (page table,
+ * summaries, score rows) stay max_pages_per_seq. Logical pages at or past that bound are never
+ * summarized, scored or selected: a longer sequence is selected over as if it held its first
+ * max_seq_len tokens, and kvsel_check_inputs reports it (KVSEL_CHECK_SEQ_LEN). Attention over a
+ * caller-given list reads every listed page the table holds. kvsel_append_kv ignores the bound
+ * (it needs room in the table only). 0 means max_pages_per_seq * page_size. */
 
 /* Host struct: rotary re-positioning of keys ([KV Packet] section 1). Rotate-half convention:
  * channel pair (i, i + D/2) with c = cos[row][i], s = sin[row][i] becomes
@@ -267,7 +279,8 @@ kvsel_status kvsel_append_kv(const kvsel_paged_kv* kv, const void* k_new, const 
 /* Device-side check of the contents every other entry point takes on trust (the host cannot
  * read device memory before enqueuing): ORs into *flags (device uint32, sticky: bits are set,
  * never cleared by the library)
- *   KVSEL_CHECK_SEQ_LEN   if some seq_lens[b] < 0 or > max_pages_per_seq * page_size;
+ *   KVSEL_CHECK_SEQ_LEN   if some seq_lens[b] < 0 or > the live bound (max_seq_len if non-zero,
+ *                         else max_pages_per_seq * page_size);
  *   KVSEL_CHECK_PAGE_ID   if some page_table[b][n], n < N_b, is outside [0, num_phys_pages);
  *   KVSEL_CHECK_SELECTION (only when sel_idx != NULL; sel_cnt and k then required) if some
  *     sel_cnt[b][j] is outside [0, min(k, N_b)] or the first sel_cnt[b][j] entries of

@@ -192,6 +192,7 @@ AttnArgs attn_args(const LaunchKV& kv, const RopeArgs& rope, const void* q, cons
   a.P = kv.P;
   a.log2P = kv.log2P;
   a.maxp = kv.maxp;
+  a.maxn = kv.maxn;
   a.Npp = kv.Npp;
   a.k = k;
   a.pps = pps;

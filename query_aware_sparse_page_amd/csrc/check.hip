@@ -12,13 +12,13 @@ constexpr int CHECK_THREADS = 256;
 
 __global__ __launch_bounds__(CHECK_THREADS) void check_inputs_kernel(
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int Hkv, int P,
-    int maxp, int Npp, const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
+    int maxp, int maxn, int Npp, const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
     int k, uint32_t* flags) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int L = seq_lens[b];
   uint32_t bad = 0;
-  if (L < 0 || (long)L > (long)maxp * P) bad |= 1u;  // KVSEL_CHECK_SEQ_LEN
+  if (L < 0 || (long)L > (long)maxn * P) bad |= 1u;  // KVSEL_CHECK_SEQ_LEN (maxn <= maxp)
   const int N = L > 0 ? (int)min(((long)L + P - 1) / P, (long)maxp) : 0;
   for (int n = tid; n < N; n += CHECK_THREADS) {
     const int p = page_table[(size_t)b * maxp + n];
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(CHECK_THREADS) void check_inputs_kernel(
 hipError_t launch_check_inputs(const LaunchKV& kv, const int32_t* sel_idx, const int32_t* sel_cnt,
                                int k, uint32_t* flags, hipStream_t stream) {
   hipLaunchKernelGGL(check_inputs_kernel, dim3((unsigned)kv.B), dim3(CHECK_THREADS), 0, stream,
-                     kv.page_table, kv.seq_lens, kv.Hkv, kv.P, kv.maxp, kv.Npp, sel_idx, sel_cnt,
+                     kv.page_table, kv.seq_lens, kv.Hkv, kv.P, kv.maxp, kv.maxn, kv.Npp, sel_idx, sel_cnt,
                      k, flags);
   return hipGetLastError();
 }

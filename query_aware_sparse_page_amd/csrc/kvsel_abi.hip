@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "../../include/kvsel.h"
@@ -52,6 +53,7 @@ kvsel_status flatten(const kvsel_paged_kv* kv, int need, LaunchKV* out) {
   // grid limits: sequences and page-range chunks index the second and third grid dimensions
   if (kv->batch > KVSEL_MAX_BATCH || kv->max_pages_per_seq > KVSEL_MAX_PAGES_PER_SEQ)
     return KVSEL_ERR_UNSUPPORTED;
+  if (kv->max_seq_len < 0) return KVSEL_ERR_INVALID_ARGUMENT;
   out->dtype = kv->dtype == KVSEL_F32 ? 0 : 1;
   out->B = kv->batch;
   out->Hq = kv->num_q_heads;
@@ -62,6 +64,10 @@ kvsel_status flatten(const kvsel_paged_kv* kv, int need, LaunchKV* out) {
   out->log2P = ilog2_exact(kv->page_size);
   out->Npp = kv->num_phys_pages;
   out->maxp = kv->max_pages_per_seq;
+  out->maxn = kv->max_seq_len > 0
+                  ? (int)std::min<long>(((long)kv->max_seq_len + kv->page_size - 1) / kv->page_size,
+                                        (long)kv->max_pages_per_seq)
+                  : kv->max_pages_per_seq;
   out->k_pool = kv->k_pool;
   out->v_pool = kv->v_pool;
   out->page_table = kv->page_table;

@@ -54,6 +54,7 @@ struct AttnArgs {
   const int32_t* sel_idx;
   const int32_t* sel_cnt;
   int Hkv, P, log2P, maxp, Npp, k, pps, nsplit, nlists;
+  int maxn;  // live pages at most (<= maxp, the row stride)
   float scale;
   RopeArgs rope;
   float* part_acc;   // [nlists][nsplit][G][D]
@@ -148,14 +149,14 @@ __device__ __forceinline__ bool select_tiles(const AttnArgs& a, int list, int b,
   float v[C];
   int pt[C];
 #pragma unroll
-  for (int u = 0; u < C; ++u) {  // indices from the row width only: no wait for seq_lens
-    const int i = min(tid * C + u, a.maxp - 1);
+  for (int u = 0; u < C; ++u) {  // indices from the live bound only: no wait for seq_lens
+    const int i = min(tid * C + u, a.maxn - 1);
     v[u] = sc[i];
     pt[u] = row[i];
   }
   const int L = a.seq_lens[b];
   if (!corr && split != 0) return false;  // block-uniform
-  const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;
+  const int N = L > 0 ? min((L + P - 1) / P, a.maxn) : 0;
   if (tid < a.pps) {
     ss.page[tid] = 0;
     ss.valid[tid] = 0;

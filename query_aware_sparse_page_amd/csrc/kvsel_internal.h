@@ -10,7 +10,9 @@ namespace kvsel {
 // Flattened, validated copy of a kvsel_paged_kv descriptor.
 struct LaunchKV {
   int dtype;  // 0 = f32, 1 = bf16
-  int B, Hq, Hkv, G, D, P, log2P, Npp, maxp;
+  int B, Hq, Hkv, G, D, P, log2P, Npp;
+  int maxp;  // page-table row width: the stride of the table, summaries and score rows
+  int maxn;  // live pages at most (<= maxp): grids, key counts and the page bound of a sequence
   const void* k_pool;
   const void* v_pool;
   const int32_t* page_table;

@@ -16,6 +16,7 @@ struct SelectArgs {
   const int32_t* page_table;
   const int32_t* seq_lens;
   int Hkv, P, maxp, Npp, k, nlists, nchunks, refresh_tail, write_scores;
+  int maxn;  // live pages at most (<= maxp, the row stride)
   int scores_only;  // launch the score kernel alone (the fused selection + attention call)
   RopeArgs rope;
   float* scores;
@@ -24,13 +25,14 @@ struct SelectArgs {
   ReuseArgs reuse;
 };
 
-// Min / max of the valid rows (1 <= valid) of one (page, KV head) tile of physical page pt,
-// computed by one wave. On return every lane holds lo / hi of its channels [c0, c0 + VEC). The
-// row loads are unconditional (rows past `valid` re-read the last valid row and are ignored), so
-// they all go out at once; the page's rotary row is read after them.
+// Min / max of the valid rows (1 <= valid; more than P means the whole page) of one (page, KV
+// head) tile of physical page pt, computed by one wave. On return every lane holds lo / hi of its
+// channels [c0, c0 + VEC). The row loads are unconditional (rows past `valid` re-read the last
+// valid row and are ignored), so they all go out at once; the page's rotary row is read after them.
 template <typename T, int D>
 __device__ __forceinline__ void tile_minmax(const T* tile, int valid, int P, int lane, int pt,
                                             const RopeArgs& rope, float* lo, float* hi) {
+  valid = min(valid, P);  // a length past the page bound: every row of the last page counted
   using M = row_map<T, D>;
   constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
   constexpr int MAX_LOADS = 32 / RPW;
@@ -107,21 +109,21 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
   int pt_raw[U];
 #pragma unroll
   for (int u = 0; u < U; ++u)  // indices from the row width only: no wait for seq_lens
-    pt_raw[u] = a.page_table[(size_t)b * a.maxp + min(wn0 + u * PPW + rgl, a.maxp - 1)];
+    pt_raw[u] = a.page_table[(size_t)b * a.maxp + min(wn0 + u * PPW + rgl, a.maxn - 1)];
   uint4 qraw[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) qraw[g] = load16(q + ((size_t)b * Hq + j * G + g) * D + c0);
   uint4 lo_raw[U], hi_raw[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int nc = min(wn0 + u * PPW + rgl, a.maxp - 1);
+    const int nc = min(wn0 + u * PPW + rgl, a.maxn - 1);
     const T* srow = (const T*)a.summ + ((size_t)list * a.maxp + nc) * 2 * D + c0;
     lo_raw[u] = load16(srow);
     hi_raw[u] = load16(srow + D);
   }
   __builtin_amdgcn_sched_barrier(0);
   const int L = a.seq_lens[b];
-  const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;  // never past the table row
+  const int N = L > 0 ? min((L + P - 1) / P, a.maxn) : 0;  // never past the live bound
 
   // ---- decode-time refresh of the tail page's summary, by the wave that scores that page: the
   // page id is already in its lanes, so the key tile loads go out one hop after the page table,
@@ -184,9 +186,9 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
   }
 }
 
-// Unroll (pages per lane group) of the score kernel for a table width: wide tables take fewer,
+// Unroll (pages per lane group) of the score kernel for a live page bound: long lists take fewer,
 // fuller blocks.
-inline int score_unroll(int maxp) { return maxp <= 1024 ? 1 : maxp <= 2048 ? 2 : 4; }
+inline int score_unroll(int maxn) { return maxn <= 1024 ? 1 : maxn <= 2048 ? 2 : 4; }
 
 // Group-mean cosine similarity of this step's and the previous step's queries for KV head j of
 // sequence b, by one wave, in fp64: for each of the G heads, dot / (|q| |q_prev|) with the

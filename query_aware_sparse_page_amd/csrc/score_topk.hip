@@ -229,9 +229,9 @@ __device__ __forceinline__ void topk_regs(const SelectArgs& a, int list, int b, 
   const float* sc = a.scores + (size_t)list * a.maxp;
   float v[C];
 #pragma unroll
-  for (int u = 0; u < C; ++u) v[u] = sc[min(tid * C + u, a.maxp - 1)];
+  for (int u = 0; u < C; ++u) v[u] = sc[min(tid * C + u, a.maxn - 1)];
   const int L = a.seq_lens[b];
-  const int N = L > 0 ? min((L + a.P - 1) / a.P, a.maxp) : 0;
+  const int N = L > 0 ? min((L + a.P - 1) / a.P, a.maxn) : 0;
   const bool reuse_on = a.reuse.q_prev != nullptr;
   const int corrected = reuse_on ? reuse_decision<T, D, G>(a, list, b, j, s_corr) : 1;
   uint32_t key[C];
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectArgs a) {
   const int tid = threadIdx.x;
   const int j = blockIdx.x, b = blockIdx.y;  // grid (Hkv, B)
   const int list = b * a.Hkv + j;
-  const int cpt = (a.maxp + NT - 1) / NT;  // keys per thread
+  const int cpt = (a.maxn + NT - 1) / NT;  // keys per thread
   if constexpr (NT == SEL_THREADS) {  // the host sends tables of <= 4 * NT pages here
     if (cpt <= 1) return topk_regs<T, D, G, NT, 1>(a, list, b, j, sm, &s_corr);
     if (cpt <= 2) return topk_regs<T, D, G, NT, 2>(a, list, b, j, sm, &s_corr);
@@ -265,9 +265,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectArgs a) {
     const float* sc = a.scores + (size_t)list * a.maxp;
     float first[TOPK_BATCH];
 #pragma unroll
-    for (int u = 0; u < TOPK_BATCH; ++u) first[u] = sc[min(tid + u * NT, a.maxp - 1)];
+    for (int u = 0; u < TOPK_BATCH; ++u) first[u] = sc[min(tid + u * NT, a.maxn - 1)];
     const int L = a.seq_lens[b];
-    const int N = L > 0 ? min((L + a.P - 1) / a.P, a.maxp) : 0;
+    const int N = L > 0 ? min((L + a.P - 1) / a.P, a.maxn) : 0;
     const bool reuse_on = a.reuse.q_prev != nullptr;
     const int corrected = reuse_on ? reuse_decision<T, D, G>(a, list, b, j, &s_corr) : 1;
     select_outputs<NT>(a, list, N, corrected, reuse_on, [&](int32_t* out, int32_t* used) {
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = a.P;
   const int L = a.seq_lens[b];
-  const int N = L > 0 ? min((L + P - 1) / P, a.maxp) : 0;  // never past the table row
+  const int N = L > 0 ? min((L + P - 1) / P, a.maxn) : 0;  // never past the live bound
   const int Hq = a.Hkv * G;
   const int c0 = (lane % LPR) * VEC;
   const bool refresh = a.refresh_tail && N > 0;
@@ -396,8 +396,8 @@ int select_blocks_per_list(const LaunchKV& kv) {
                                                : pages_per_select_block<float, 128>())
                                  : (kv.D == 64 ? pages_per_select_block<bf16_t, 64>()
                                                : pages_per_select_block<bf16_t, 128>())) *
-                  score_unroll(kv.maxp);
-  return (kv.maxp + ppb - 1) / ppb;
+                  score_unroll(kv.maxn);
+  return (kv.maxn + ppb - 1) / ppb;
 }
 
 template <typename T, int D, int G>
@@ -407,14 +407,14 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t stream) {
   // 8 lists of 1024 pages take 24.7 us in one launch against 10.2 us in two; 128 lists of up
   // to 1024 pages take 15.8 us against 18.6 us).
   if constexpr (G <= 4) {  // larger groups would spill at 1024 threads
-    if (!a.scores_only && a.nlists >= SELECT_ONE_LAUNCH_MIN_LISTS && a.maxp <= FUSED_MAX_PAGES) {
+    if (!a.scores_only && a.nlists >= SELECT_ONE_LAUNCH_MIN_LISTS && a.maxn <= FUSED_MAX_PAGES) {
       hipLaunchKernelGGL((select_fused_kernel<T, D, G>), dim3(a.Hkv, a.nlists / a.Hkv),
                          dim3(FUSED_THREADS), 0, stream, a);
       return hipGetLastError();
     }
   }
   const dim3 sgrid(a.Hkv, a.nlists / a.Hkv, a.nchunks);
-  switch (score_unroll(a.maxp)) {
+  switch (score_unroll(a.maxn)) {
     case 1: hipLaunchKernelGGL((score_kernel<T, D, G, 1>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((score_kernel<T, D, G, 2>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
     default: hipLaunchKernelGGL((score_kernel<T, D, G, 4>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
@@ -422,7 +422,7 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.scores_only) return hipSuccess;
-  if (a.maxp <= TOPK_SMALL_PAGES)
+  if (a.maxn <= TOPK_SMALL_PAGES)
     hipLaunchKernelGGL((topk_kernel<T, D, G, SEL_THREADS>), dim3(a.Hkv, a.nlists / a.Hkv),
                        dim3(SEL_THREADS), 0, stream, a);
   else
@@ -462,6 +462,7 @@ SelectArgs select_args(const LaunchKV& kv, const RopeArgs& rope, void* summ, con
   a.Hkv = kv.Hkv;
   a.P = kv.P;
   a.maxp = kv.maxp;
+  a.maxn = kv.maxn;
   a.Npp = kv.Npp;
   a.k = k;
   a.nlists = kv.B * kv.Hkv;

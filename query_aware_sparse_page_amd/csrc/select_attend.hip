@@ -21,8 +21,8 @@ __global__ __launch_bounds__(WAVES * 64) void fused_f32_kernel(AttnArgs a, int G
 // Score keys per thread of the fused select (the block holds the whole table row in registers).
 static int fused_keys_per_thread(const LaunchKV& kv) {
   const int nt = (kv.dtype == 1 && kv.P == 16) ? 128 : 256;
-  const int c = (kv.maxp + nt - 1) / nt;
-  return c <= 1 ? 1 : c <= 4 ? 4 : c <= 16 ? 16 : c <= 32 ? 32 : 0;
+  const int c = (kv.maxn + nt - 1) / nt;
+  return c <= 1 ? 1 : c <= 4 ? 4 : c <= 8 ? 8 : c <= 16 ? 16 : c <= 32 ? 32 : 0;
 }
 
 bool fused_select_supported(const LaunchKV& kv, int k) {
@@ -55,6 +55,7 @@ static void launch_fused_r(int c, const AttnArgs& a, int G, hipStream_t stream) 
   switch (c) {
     case 1: launch_fused_c<T, D, P, ROPE, 1>(a, G, stream); break;
     case 4: launch_fused_c<T, D, P, ROPE, 4>(a, G, stream); break;
+    case 8: launch_fused_c<T, D, P, ROPE, 8>(a, G, stream); break;
     case 16: launch_fused_c<T, D, P, ROPE, 16>(a, G, stream); break;
     default: launch_fused_c<T, D, P, ROPE, 32>(a, G, stream); break;
   }

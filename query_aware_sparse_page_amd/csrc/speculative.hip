@@ -56,7 +56,7 @@ static hipError_t launch_co_r(const AttnArgs& a, SelectArgs s, int G, int prev_s
                               hipStream_t stream) {
   using S = FusedShape<T, P>;
   constexpr int PPB = S::WAVES * (64 / row_map<T, D>::LPR);  // pages per score block
-  s.nchunks = (s.maxp + PPB - 1) / PPB;
+  s.nchunks = (s.maxn + PPB - 1) / PPB;
   const dim3 grid(a.Hkv, a.nlists / a.Hkv, s.nchunks + 1 + prev_splits);
   const dim3 block(S::WAVES * 64);
   switch (G) {

@@ -16,7 +16,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_pool,
                                                         const int32_t* __restrict__ page_table,
                                                         const int32_t* __restrict__ seq_lens, int B,
-                                                        int Hkv, int P, int maxp, int tail_only,
+                                                        int Hkv, int P, int maxp, int maxn,
+                                                        int tail_only,
                                                         RopeArgs rope, T* __restrict__ summ) {
   using M = row_map<T, D>;
   constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
@@ -31,11 +32,11 @@ __global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_
     j = (int)(unit % Hkv);
     const int L = seq_lens[b];
     if (L <= 0) return;
-    n = (L - 1) / P;
+    n = min((L - 1) / P, maxn - 1);  // a longer sequence: its last live page (all P rows)
   } else {
-    if (unit >= (long)B * maxp * Hkv) return;
-    b = (int)(unit / ((long)maxp * Hkv));
-    const int rem = (int)(unit % ((long)maxp * Hkv));
+    if (unit >= (long)B * maxn * Hkv) return;  // live pages only; maxp is the row stride
+    b = (int)(unit / ((long)maxn * Hkv));
+    const int rem = (int)(unit % ((long)maxn * Hkv));
     n = rem / Hkv;
     j = rem % Hkv;
     if (n * P >= seq_lens[b]) return;
@@ -97,12 +98,12 @@ __global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_
 template <typename T, int D>
 static hipError_t launch_summaries_t(const LaunchKV& kv, const RopeArgs& rope, int tail_only,
                                      void* summ, hipStream_t stream) {
-  const long units = tail_only ? (long)kv.B * kv.Hkv : (long)kv.B * kv.maxp * kv.Hkv;
+  const long units = tail_only ? (long)kv.B * kv.Hkv : (long)kv.B * kv.maxn * kv.Hkv;
   const long blocks = (units + 3) / 4;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((summaries_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const T*)kv.k_pool, kv.page_table, kv.seq_lens, kv.B, kv.Hkv, kv.P, kv.maxp,
-                     tail_only, rope, (T*)summ);
+                     kv.maxn, tail_only, rope, (T*)summ);
   return hipGetLastError();
 }
 

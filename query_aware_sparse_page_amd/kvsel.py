@@ -44,7 +44,7 @@ class PagedKVDesc(ctypes.Structure):
         ("dtype", c_i32), ("batch", c_i32), ("num_q_heads", c_i32), ("num_kv_heads", c_i32),
         ("head_dim", c_i32), ("page_size", c_i32), ("num_phys_pages", c_i32),
         ("max_pages_per_seq", c_i32), ("k_pool", c_vp), ("v_pool", c_vp), ("page_table", c_vp),
-        ("seq_lens", c_vp),
+        ("seq_lens", c_vp), ("max_seq_len", c_i32),
     ]
 
 
@@ -90,6 +90,9 @@ EXPORTS = {
 _lib = None
 
 
+ABI_VERSION = 2  # KVSEL_ABI_VERSION of include/kvsel.h
+
+
 def lib() -> ctypes.CDLL:
     """Load libkvsel.so (once) and declare its signatures."""
     global _lib
@@ -102,6 +105,9 @@ def lib() -> ctypes.CDLL:
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args
+        if handle.kvsel_abi_version() != ABI_VERSION:  # the descriptor layouts above
+            raise KvselError(-1, f"{LIB_PATH} has ABI {handle.kvsel_abi_version()}, this binding "
+                                 f"{ABI_VERSION}; rebuild it")
         _lib = handle
     return _lib
 
@@ -158,13 +164,15 @@ def device_v_layout(v_pool: torch.Tensor) -> torch.Tensor:
 class PagedKV:
     """Device tensors of one paged KV cache: k_pool [Npp][Hkv][P][D] (token-major pages),
     v_pool [Npp][Hkv][D][P] (channel-major pages, see ``device_v_layout``), page_table int32
-    [B][max_pages], seq_lens int32 [B]."""
+    [B][max_pages], seq_lens int32 [B]. ``max_seq_len`` (host int, 0 = the table width) bounds every
+    length so that launches follow the live pages rather than the table width."""
 
     k_pool: torch.Tensor
     v_pool: Optional[torch.Tensor]
     page_table: torch.Tensor
     seq_lens: torch.Tensor
     num_q_heads: int
+    max_seq_len: int = 0
 
     def desc(self) -> PagedKVDesc:
         _dev(self.k_pool, "k_pool")
@@ -181,7 +189,8 @@ class PagedKV:
         return PagedKVDesc(_elem_code(self.k_pool.dtype), B, self.num_q_heads, Hkv, D, P, Npp, maxp,
                            self.k_pool.data_ptr(),
                            self.v_pool.data_ptr() if self.v_pool is not None else None,
-                           self.page_table.data_ptr(), self.seq_lens.data_ptr())
+                           self.page_table.data_ptr(), self.seq_lens.data_ptr(),
+                           int(self.max_seq_len))
 
     @property
     def batch(self) -> int:

@@ -9,7 +9,11 @@ import oracle as O
 
 BF16_OUT_TOL = 2e-2   # absolute, bf16 attention outputs
 F32_OUT_TOL = 1e-5    # absolute, fp32 attention outputs
-BF16_LSE_TOL = 1e-3
+# bf16 lse: the kernel rounds each probability exp(z - m) to bf16 (round to nearest even, unit
+# roundoff 2^-8) before the P x V product and sums the rounded values, so the sum is off by a
+# relative 2^-8 at most and ln of it by -ln(1 - 2^-8) < 3.92e-3; the logits (exact bf16 products,
+# fp32 sums) and the fp32 exp / log add well under 1e-4.
+BF16_LSE_TOL = 4e-3
 F32_LSE_TOL = 1e-5
 
 

@@ -102,3 +102,47 @@ def test_append_refuses_a_full_table(K):
     assert torch.equal(summ[0], before_s[0])
     p1 = int(w.page_table[1, 0])
     assert torch.equal(kv.k_pool[p1, :, 10], kn[1])  # the other sequence took its token
+
+
+def test_growing_speculative_loop(K):
+    """Appends interleaved with speculative steps (the summaries kept current by the appends, no
+    refresh): each step's outputs equal the serial calls' bit for bit, and the last step's
+    attention over the pages it used matches the oracle on the grown cache."""
+    T, k = 12, 6
+    lens = [5 * 16 + 3, 2 * 16, 16 - 2]
+    w = grown_case(721, "bf16", 128, 16, lens, T, Hq=16, Hkv=4, k=k)
+    say(f"growing speculative loop: lens {lens}, {T} steps")
+    kv_a, kv_b = kv_of(K, w), kv_of(K, w)
+    summ_a, summ_b = K.build_summaries(kv_a), K.build_summaries(kv_b)
+    gen = torch.Generator().manual_seed(722)
+    q = w.q.float()
+    sel_prev = cnt_prev = None
+    Kc, Vc = w.k_pool.double().numpy(), w.v_pool.double().numpy()
+    cur = w.seq_lens.numpy().astype(np.int64)
+    for t in range(T):
+        kn = torch.randn((w.B, w.Hkv, 128), generator=gen).to(torch.bfloat16)
+        vn = torch.randn((w.B, w.Hkv, 128), generator=gen).to(torch.bfloat16)
+        q_prev = q
+        q = 0.9 * q + 0.45 * torch.randn(q.shape, generator=gen)
+        qt, qp = q.to(torch.bfloat16).cuda(), q_prev.to(torch.bfloat16).cuda()
+        for kv, summ in ((kv_a, summ_a), (kv_b, summ_b)):
+            K.append_kv(kv, kn.cuda(), vn.cuda(), summ=summ)
+        Kc, Vc, cur, _ = O.append_tokens(Kc, Vc, w.page_table, cur, kn.double().numpy(),
+                                         vn.double().numpy(), 16)
+        first = t == 0
+        prev_i = sel_prev if not first else torch.zeros((w.B, w.Hkv, k), dtype=torch.int32, device="cuda")
+        prev_c = cnt_prev if not first else torch.zeros((w.B, w.Hkv), dtype=torch.int32, device="cuda")
+        reuse = K.Reuse(qp, prev_i, prev_c, 0.8, first_step=first)
+        spec = K.speculative_step(kv_a, summ_a, qt, k, reuse)
+        sel, cnt, used, ucnt, corr, sim = K.score_topk(kv_b, summ_b, qt, k, reuse=reuse)
+        out, lse = K.sparse_decode_attn(kv_b, qt, used, ucnt, k)
+        torch.cuda.synchronize()
+        for x, y, name in zip(spec, (sel, cnt, used, ucnt, corr, sim, out, lse),
+                              ("sel", "cnt", "used", "ucnt", "corrected", "similarity", "out", "lse")):
+            assert torch.equal(x, y), f"step {t}: {name} differs"
+        sel_prev, cnt_prev = spec[0].clone(), spec[1].clone()
+    assert list(kv_a.seq_lens.cpu().numpy()) == list(cur)
+    o_out, o_lse = O.sparse_decode_attention(qt.cpu(), Kc, Vc, w.page_table, cur,
+                                             spec[2].cpu().numpy(), spec[3].cpu().numpy(), 16,
+                                             scale_of(128))
+    assert_attention_close(spec[6], spec[7], o_out, o_lse, "bf16")

@@ -273,6 +273,21 @@ def speculative_rope(seed: int = 1005, steps: int = 64, rho: float = 0.85, tau: 
     )
 
 
+def appended_tokens(w: Workload, steps: int, seed: int):
+    """Keys and values of `steps` decode tokens per sequence, appended one per step to `w`'s cache
+    (a growing-context decode loop): drawn like the cache's own (N(0,1); keys scaled x8 on the
+    workload's outlier channels when it has them). Returns (k_steps, v_steps), each
+    [steps][B][Hkv][D] in the workload's element type."""
+    rng = _rng(seed)
+    K = _normal(rng, (steps, w.B, w.Hkv, w.D))
+    V = _normal(rng, (steps, w.B, w.Hkv, w.D))
+    chans = w.extra.get("outlier_channels")
+    if chans is not None:
+        for j, cs in enumerate(chans):
+            K[:, :, j, cs] *= 8.0
+    return _to(K, w.dtype), _to(V, w.dtype)
+
+
 def custom(seed: int, B: int, Hq: int, Hkv: int, D: int, P: int, k: int, lens, dtype: str = "bf16",
            permute: bool = True, spare_pages: int = 0) -> Workload:
     """Small seeded case with arbitrary shapes (for edge-case tests): q, K, V ~ N(0,1).
