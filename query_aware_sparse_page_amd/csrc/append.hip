@@ -1,20 +1,20 @@
 // Decode-time append: each sequence's new token key and value go into the tail page of the paged
 // cache, and that page's summary is kept current without re-reading the page.
 //
-// One block per sequence, one wave per KV head in turn: LPR lanes carry the head's D channels as
-// 16-byte slices. The key row is one 16-byte store per lane (token-major K pages); the value is a
-// column of the channel-major V page (one element per channel, at stride P), written element by
-// element as raw bits. The summary of a page that the token opens is the key itself (lo = hi);
-// otherwise lo = min(lo, key), hi = max(hi, key) over the stored row -- exactly the rebuild of
-// the page's valid keys when the stored summary covered the earlier ones (min and max are exact).
-// The sequence length is read by every thread first and written once after a barrier, so the
-// output may be the length array itself.
+// One block per sequence, one wave per KV head (up to 16 waves; more heads in turn): LPR lanes
+// carry the head's D channels as 16-byte slices. The key row is one 16-byte store per lane
+// (token-major K pages); the value is a column of the channel-major V page (one element per
+// channel, at stride P), written element by element as raw bits. The summary of a page that the
+// token opens is the key itself (lo = hi); otherwise lo = min(lo, key), hi = max(hi, key) over
+// the stored row -- exactly the rebuild of the page's valid keys when the stored summary covered
+// the earlier ones (min and max are exact). The sequence length is read by every thread first
+// and written once after a barrier, so the output may be the length array itself.
 #include "kvsel_device.h"
 #include "kvsel_internal.h"
 
 namespace kvsel {
 
-constexpr int APPEND_THREADS = 256;
+constexpr int APPEND_MAX_WAVES = 16;
 
 struct AppendArgs {
   void* k_pool;
@@ -47,47 +47,60 @@ __device__ __forceinline__ void store_slice_column<bf16_t>(bf16_t* base, size_t 
     reinterpret_cast<uint16_t*>(base)[e * stride] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
 }
 
+// Block of min(Hkv, APPEND_MAX_WAVES) waves: wave w takes KV heads w, w + waves, ... The first
+// head's new rows are requested before the length (their addresses do not depend on it), and
+// the page-table entry and stored summary rows together right after it, so one memory round trip
+// follows the length's.
 template <typename T, int D>
-__global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendArgs a) {
+__global__ __launch_bounds__(APPEND_MAX_WAVES * 64) void append_kernel(AppendArgs a) {
   using M = row_map<T, D>;
   constexpr int VEC = M::VEC, LPR = M::LPR;
-  constexpr int NW = APPEND_THREADS / 64;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int NW = blockDim.x >> 6;
+  const int c0 = lane * VEC;
+  const bool row_lane = lane < LPR;
+  uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
+  if (row_lane && w < a.Hkv) {
+    const size_t in = ((size_t)b * a.Hkv + w) * D + c0;
+    kv = load16((const T*)a.k_new + in);
+    vv = load16((const T*)a.v_new + in);
+  }
   const int L = a.seq_lens[b];
   const bool ok = L >= 0 && (long)L < (long)a.maxp * a.P;  // room for one more token
   if (ok) {
     const int n = L / a.P, slot = L - n * a.P;
     // the caller's allocator set this entry when the token opens a page; clamp like every reader
     const int p = min(max(a.page_table[(size_t)b * a.maxp + n], 0), a.Npp - 1);
-    const int c0 = lane * VEC;
     for (int j = w; j < a.Hkv; j += NW) {
-      if (lane < LPR) {
+      if (!row_lane) continue;
+      if (j != w) {
         const size_t in = ((size_t)b * a.Hkv + j) * D + c0;
-        const uint4 kv = load16((const T*)a.k_new + in);
-        const uint4 vv = load16((const T*)a.v_new + in);
-        store16((T*)a.k_pool + (((size_t)p * a.Hkv + j) * a.P + slot) * D + c0, kv);
-        store_slice_column<T>((T*)a.v_pool + (((size_t)p * a.Hkv + j) * D + c0) * a.P + slot,
-                              (size_t)a.P, vv);
-        if (a.summ) {
-          T* row = (T*)a.summ + (((size_t)b * a.Hkv + j) * a.maxp + n) * 2 * D + c0;
-          uint4 lo = kv, hi = kv;
-          if (slot > 0) {
-            float k[VEC], l0[VEC], h0[VEC];
-            unpack<T>(kv, k);
-            unpack<T>(load16(row), l0);
-            unpack<T>(load16(row + D), h0);
+        kv = load16((const T*)a.k_new + in);
+        vv = load16((const T*)a.v_new + in);
+      }
+      T* row = a.summ ? (T*)a.summ + (((size_t)b * a.Hkv + j) * a.maxp + n) * 2 * D + c0 : nullptr;
+      uint4 lo = kv, hi = kv;
+      if (row && slot > 0) {
+        float k[VEC], l0[VEC], h0[VEC];
+        const uint4 lraw = load16(row), hraw = load16(row + D);
+        unpack<T>(kv, k);
+        unpack<T>(lraw, l0);
+        unpack<T>(hraw, h0);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-              l0[e] = fminf(l0[e], k[e]);
-              h0[e] = fmaxf(h0[e], k[e]);
-            }
-            lo = pack<T>(l0);
-            hi = pack<T>(h0);
-          }
-          store16(row, lo);
-          store16(row + D, hi);
+        for (int e = 0; e < VEC; ++e) {
+          l0[e] = fminf(l0[e], k[e]);
+          h0[e] = fmaxf(h0[e], k[e]);
         }
+        lo = pack<T>(l0);
+        hi = pack<T>(h0);
+      }
+      store16((T*)a.k_pool + (((size_t)p * a.Hkv + j) * a.P + slot) * D + c0, kv);
+      store_slice_column<T>((T*)a.v_pool + (((size_t)p * a.Hkv + j) * D + c0) * a.P + slot,
+                            (size_t)a.P, vv);
+      if (row) {
+        store16(row, lo);
+        store16(row + D, hi);
       }
     }
   } else if (a.flags && tid == 0) {
@@ -99,10 +112,11 @@ __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendArgs a) {
 
 template <typename T>
 static void launch_append_t(int D, const AppendArgs& a, int B, hipStream_t stream) {
+  const dim3 block(64 * (a.Hkv < APPEND_MAX_WAVES ? a.Hkv : APPEND_MAX_WAVES));
   if (D == 64)
-    hipLaunchKernelGGL((append_kernel<T, 64>), dim3(B), dim3(APPEND_THREADS), 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<T, 64>), dim3(B), block, 0, stream, a);
   else
-    hipLaunchKernelGGL((append_kernel<T, 128>), dim3(B), dim3(APPEND_THREADS), 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<T, 128>), dim3(B), block, 0, stream, a);
 }
 
 hipError_t launch_append(const LaunchKV& kv, const void* k_new, const void* v_new, void* summ,

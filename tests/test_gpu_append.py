@@ -82,6 +82,31 @@ def test_append_matches_oracle(K, case):
     assert_attention_close(out, lse, ref["out"], ref["lse"], dtype)
 
 
+def test_append_more_heads_than_waves(K):
+    """20 KV heads: the block's 16 waves take heads 16..19 on a second pass."""
+    P, T = 16, 20
+    lens = [3 * P + 1, P - 1, 0]
+    w = grown_case(715, "bf16", 64, P, lens, T, Hq=20, Hkv=20, k=4)
+    say(f"append: 20 KV heads, lens {lens}, {T} steps")
+    kv = kv_of(K, w)
+    summ = K.build_summaries(kv)
+    Kc, Vc = w.k_pool.double().numpy(), w.v_pool.double().numpy()
+    cur = w.seq_lens.numpy().astype(np.int64)
+    gen = torch.Generator().manual_seed(716)
+    for t in range(T):
+        kn = torch.randn((w.B, w.Hkv, 64), generator=gen).to(torch.bfloat16)
+        vn = torch.randn((w.B, w.Hkv, 64), generator=gen).to(torch.bfloat16)
+        K.append_kv(kv, kn.cuda(), vn.cuda(), summ=summ)
+        Kc, Vc, cur, _ = O.append_tokens(Kc, Vc, w.page_table, cur, kn.double().numpy(),
+                                         vn.double().numpy(), P)
+    torch.cuda.synchronize()
+    assert list(kv.seq_lens.cpu().numpy()) == list(cur)
+    wt = dataclasses.replace(w, seq_lens=torch.from_numpy(cur.astype(np.int32)))
+    assert_summaries_equal(summ, O.page_summaries(Kc, w.page_table, wt.seq_lens, P), wt)
+    assert np.array_equal(kv.k_pool.double().cpu().numpy(), Kc)
+    assert np.array_equal(kv.v_pool.permute(0, 1, 3, 2).double().cpu().numpy(), Vc)
+
+
 def test_append_refuses_a_full_table(K):
     w = W.custom(713, B=2, Hq=8, Hkv=2, D=64, P=16, k=4, lens=[32, 10], dtype="bf16")
     say("append: full table")
