@@ -341,9 +341,10 @@ def speculative_growing(dev, reps=3):
     """The speculative workload as a growing-context decode loop: each of the 64 steps appends the
     new token's key and value (kvsel_append_kv, which keeps the tail page's summary current, so no
     refresh is needed), then runs the speculative step over the grown cache (32768 -> 32832
-    tokens; the table and pool have two more pages for them; the new keys are stored as given,
-    without a rotary shift). The graph of 64 steps starts by resetting the length, so every replay
-    grows the same cache. Reports µs per step (append + speculative step) against the serial
+    tokens; the pool has two more pages for them, which the appends take from a device-side
+    free-page list into the table; the new keys are stored as given, without a rotary shift). The
+    graph of 64 steps starts by resetting the length and the free count, so every replay grows the
+    same cache. Reports µs per step (append + speculative step) against the serial
     calls (append + kvsel_score_topk with reuse + kvsel_sparse_decode_attn)."""
     w = W.speculative_rope()
     bt = w.extra["block_tokens"]
@@ -363,7 +364,10 @@ def speculative_growing(dev, reps=3):
                                                    dtype=enc.dtype, device=dev)])
     table = torch.zeros((w.B, w.max_pages + extra), dtype=torch.int32)
     table[:, : w.max_pages] = w.page_table
-    table[0, w.max_pages:] = torch.arange(npg, npg + extra, dtype=torch.int32)
+    table[0, w.max_pages:] = -1  # set by the appends from the free list
+    free_ids = torch.arange(npg + extra - 1, npg - 1, -1, dtype=torch.int32, device=dev)
+    free_n0 = torch.tensor([extra], dtype=torch.int32, device=dev)
+    free = K.FreePages(free_ids, free_n0.clone())
     lens0 = w.seq_lens.to(dev)
     lens = lens0.clone()
     kv = K.PagedKV(k_pool, v_pool, table.to(dev), lens, w.Hq,
@@ -389,8 +393,9 @@ def speculative_growing(dev, reps=3):
 
     def loop_serial():
         lens.copy_(lens0)
+        free.count.copy_(free_n0)
         for t in range(T):
-            K.append_kv(kv, ks[t], vs[t], summ=summ)
+            K.append_kv(kv, ks[t], vs[t], summ=summ, free_pages=free)
             r = K.score_topk(kv, summ, qs[t], k, sel_idx=sel[t], sel_cnt=cnt[t], workspace=ws_s,
                              reuse=reuse(t))
             K.sparse_decode_attn(kv, qs[t], r[2], r[3], k, rope=shift, out=out[t], lse=lse[t],
@@ -398,8 +403,9 @@ def speculative_growing(dev, reps=3):
 
     def loop_speculative():
         lens.copy_(lens0)
+        free.count.copy_(free_n0)
         for t in range(T):
-            K.append_kv(kv, ks[t], vs[t], summ=summ)
+            K.append_kv(kv, ks[t], vs[t], summ=summ, free_pages=free)
             K.speculative_step(kv, summ, qs[t], k, reuse(t), rope=shift, sel_idx=sel[t],
                                sel_cnt=cnt[t], out=out[t], lse=lse[t], workspace=ws_f)
 
@@ -430,8 +436,9 @@ def speculative_growing(dev, reps=3):
     torch.cuda.synchronize()
     return {"us_per_step": round(us, 3), "serial_us_per_step": round(us_serial, 3),
             "speculative_equals_serial": bool(torch.equal(out, out_serial)),
-            "final_len": int(lens.item()), "steps": T,
-            "step": "kvsel_append_kv, then kvsel_speculative_step over the grown cache (warm); "
+            "final_len": int(lens.item()), "free_pages_left": int(free.count.item()), "steps": T,
+            "step": "kvsel_append_kv (pages from a device-side free list), then "
+                    "kvsel_speculative_step over the grown cache (warm); "
                     "serial: kvsel_append_kv, kvsel_score_topk with reuse, "
                     "kvsel_sparse_decode_attn"}
 

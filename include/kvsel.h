@@ -256,6 +256,17 @@ kvsel_status kvsel_speculative_step(const kvsel_paged_kv* kv, const kvsel_rope* 
                                     void* out, float* lse, void* ws, size_t ws_bytes,
                                     void* stream);
 
+/* Device-side free-page list for kvsel_append_kv (the caller's page pool, kept on the device so
+ * that a captured decode loop needs no host step to grow a sequence): ids[0 .. *count) are free
+ * physical page ids; a token that opens a page takes the top one, ids[*count - 1], and
+ * decrements *count. The library never pushes ids back: refill the list and set *count between
+ * calls. */
+typedef struct kvsel_free_pages {
+  int32_t* ids;      /* device int32 [capacity] */
+  int32_t* count;    /* device int32 [1], 0 <= *count <= capacity */
+  int32_t capacity;  /* host: entries of ids (>= 1) */
+} kvsel_free_pages;
+
 /* Decode-time append ([KV wiki]: a decode step stores the new token's key and value and keeps
  * every earlier one). For every sequence b with L = seq_lens[b] in [0, max_pages_per_seq * P):
  * writes k_new[b][j][:] into slot L % P of logical page L / P (physical page
@@ -266,15 +277,22 @@ kvsel_status kvsel_speculative_step(const kvsel_paged_kv* kv, const kvsel_rope* 
  * current before the call; then writes seq_lens_out[b] = L + 1.
  * A sequence with no room (L == max_pages_per_seq * P) or L < 0 is left unchanged and, when flags
  * is non-NULL, KVSEL_CHECK_SEQ_LEN is ORed into *flags (device uint32).
- * The table entry of a page the token opens is the caller's page allocator's to set before the
- * call (an entry outside the pool is clamped into it, as by every reader). kv->k_pool and
- * kv->v_pool are written despite the descriptor's const qualifiers. Keys are stored as given: with
- * a rotary gather, store keys already at their positions, on pages whose page_row is -1.
+ * The page a token opens: with free_pages NULL, the table entry is the caller's allocator's to set
+ * before the call (an entry outside the pool is clamped into it, as by every reader). With a
+ * free-page list, the token takes a page from it and page_table[b][L / P] is set to that page;
+ * which sequence gets which of the taken ids is unspecified when several open a page in one call.
+ * If the list is empty the sequence is left unchanged and KVSEL_CHECK_NO_FREE_PAGE is ORed into
+ * *flags; an id outside [0, num_phys_pages) (or *count > capacity) is consumed, the sequence left
+ * unchanged and KVSEL_CHECK_PAGE_ID ORed in.
+ * kv->k_pool, kv->v_pool (and, with a free list, kv->page_table) are written despite the
+ * descriptor's const qualifiers. Keys are stored as given: with a rotary gather, store keys
+ * already at their positions, on pages whose page_row is -1.
  * k_new, v_new: [B][Hkv][D] element type. seq_lens_out: int32 [B], may equal kv->seq_lens (in
  * place). summ: [B][Hkv][max_pages_per_seq][2][D] as kvsel_build_summaries writes it, or NULL.
  * One launch of one block per sequence. */
 kvsel_status kvsel_append_kv(const kvsel_paged_kv* kv, const void* k_new, const void* v_new,
-                             void* summ, int32_t* seq_lens_out, uint32_t* flags, void* stream);
+                             void* summ, int32_t* seq_lens_out,
+                             const kvsel_free_pages* free_pages, uint32_t* flags, void* stream);
 
 /* Device-side check of the contents every other entry point takes on trust (the host cannot
  * read device memory before enqueuing): ORs into *flags (device uint32, sticky: bits are set,
@@ -291,6 +309,7 @@ kvsel_status kvsel_append_kv(const kvsel_paged_kv* kv, const void* k_new, const 
 #define KVSEL_CHECK_SEQ_LEN 1u
 #define KVSEL_CHECK_PAGE_ID 2u
 #define KVSEL_CHECK_SELECTION 4u
+#define KVSEL_CHECK_NO_FREE_PAGE 8u /* kvsel_append_kv only: the free-page list was empty */
 kvsel_status kvsel_check_inputs(const kvsel_paged_kv* kv, const int32_t* sel_idx,
                                 const int32_t* sel_cnt, int32_t k, uint32_t* flags, void* stream);
 

@@ -26,8 +26,28 @@ struct AppendArgs {
   const void* v_new;  // [B][Hkv][D]
   void* summ;         // [B][Hkv][maxp][2][D], may be null
   uint32_t* flags;    // may be null
+  int32_t* table_w;   // the page table, written when a page is taken from the free list
+  FreePages free;     // free.ids == nullptr: the caller set the table entries
   int Hkv, P, maxp, Npp;
 };
+
+// Pop one page id off the free list for sequence b's logical page n (one thread): returns the
+// page, or -1 with the reason ORed into the flags (an empty list is left as it was).
+__device__ __forceinline__ int take_free_page(const AppendArgs& a, int b, int n) {
+  const int top = atomicSub(a.free.count, 1);
+  if (top <= 0) {
+    atomicAdd(a.free.count, 1);  // the list was empty: give the count back
+    if (a.flags) atomicOr(a.flags, 8u);  // KVSEL_CHECK_NO_FREE_PAGE
+    return -1;
+  }
+  const int id = top <= a.free.capacity ? a.free.ids[top - 1] : -1;
+  if (id < 0 || id >= a.Npp) {
+    if (a.flags) atomicOr(a.flags, 2u);  // KVSEL_CHECK_PAGE_ID
+    return -1;
+  }
+  a.table_w[(size_t)b * a.maxp + n] = id;
+  return id;
+}
 
 // The raw element bits of one 16-byte slice, one element at a time.
 template <typename T>
@@ -67,12 +87,22 @@ __global__ __launch_bounds__(APPEND_MAX_WAVES * 64) void append_kernel(AppendArg
     vv = load16((const T*)a.v_new + in);
   }
   const int L = a.seq_lens[b];
-  const bool ok = L >= 0 && (long)L < (long)a.maxp * a.P;  // room for one more token
+  bool ok = L >= 0 && (long)L < (long)a.maxp * a.P;  // room for one more token
+  if (!ok && a.flags && tid == 0) atomicOr(a.flags, 1u);  // KVSEL_CHECK_SEQ_LEN
   if (ok) {
     const int n = L / a.P, slot = L - n * a.P;
-    // the caller's allocator set this entry when the token opens a page; clamp like every reader
-    const int p = min(max(a.page_table[(size_t)b * a.maxp + n], 0), a.Npp - 1);
-    for (int j = w; j < a.Hkv; j += NW) {
+    int p;
+    if (slot == 0 && a.free.ids) {  // block-uniform: the token opens a page from the free list
+      __shared__ int s_page;
+      if (tid == 0) s_page = take_free_page(a, b, n);
+      __syncthreads();
+      p = s_page;
+      ok = p >= 0;
+    } else {
+      // the caller's allocator set this entry; clamp like every reader
+      p = min(max(a.page_table[(size_t)b * a.maxp + n], 0), a.Npp - 1);
+    }
+    for (int j = w; ok && j < a.Hkv; j += NW) {
       if (!row_lane) continue;
       if (j != w) {
         const size_t in = ((size_t)b * a.Hkv + j) * D + c0;
@@ -103,8 +133,6 @@ __global__ __launch_bounds__(APPEND_MAX_WAVES * 64) void append_kernel(AppendArg
         store16(row + D, hi);
       }
     }
-  } else if (a.flags && tid == 0) {
-    atomicOr(a.flags, 1u);  // KVSEL_CHECK_SEQ_LEN
   }
   __syncthreads();  // every thread has read the length before it changes
   if (ok && tid == 0) a.seq_lens_out[b] = L + 1;
@@ -120,7 +148,8 @@ static void launch_append_t(int D, const AppendArgs& a, int B, hipStream_t strea
 }
 
 hipError_t launch_append(const LaunchKV& kv, const void* k_new, const void* v_new, void* summ,
-                         int32_t* seq_lens_out, uint32_t* flags, hipStream_t stream) {
+                         int32_t* seq_lens_out, const FreePages& free_pages, uint32_t* flags,
+                         hipStream_t stream) {
   AppendArgs a;
   a.k_pool = const_cast<void*>(kv.k_pool);
   a.v_pool = const_cast<void*>(kv.v_pool);
@@ -131,6 +160,8 @@ hipError_t launch_append(const LaunchKV& kv, const void* k_new, const void* v_ne
   a.v_new = v_new;
   a.summ = summ;
   a.flags = flags;
+  a.table_w = const_cast<int32_t*>(kv.page_table);
+  a.free = free_pages;
   a.Hkv = kv.Hkv;
   a.P = kv.P;
   a.maxp = kv.maxp;

@@ -258,13 +258,20 @@ kvsel_status kvsel_check_inputs(const kvsel_paged_kv* kv, const int32_t* sel_idx
 }
 
 kvsel_status kvsel_append_kv(const kvsel_paged_kv* kv, const void* k_new, const void* v_new,
-                             void* summ, int32_t* seq_lens_out, uint32_t* flags, void* stream) {
+                             void* summ, int32_t* seq_lens_out,
+                             const kvsel_free_pages* free_pages, uint32_t* flags, void* stream) {
   LaunchKV f;
   kvsel_status st = flatten(kv, 3, &f);
   if (st != KVSEL_OK) return st;
   if (!k_new || !v_new || !seq_lens_out) return KVSEL_ERR_INVALID_ARGUMENT;
+  FreePages fp{nullptr, nullptr, 0};
+  if (free_pages) {
+    if (!free_pages->ids || !free_pages->count || free_pages->capacity < 1)
+      return KVSEL_ERR_INVALID_ARGUMENT;
+    fp = FreePages{free_pages->ids, free_pages->count, free_pages->capacity};
+  }
   if ((st = check_device()) != KVSEL_OK) return st;
-  return launch_status(launch_append(f, k_new, v_new, summ, seq_lens_out, flags,
+  return launch_status(launch_append(f, k_new, v_new, summ, seq_lens_out, fp, flags,
                                      (hipStream_t)stream));
 }
 

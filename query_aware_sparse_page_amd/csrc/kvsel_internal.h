@@ -93,10 +93,18 @@ hipError_t launch_attention(const LaunchKV& kv, const RopeArgs& rope, const void
                             int pages_per_split, void* out, float* lse, void* ws,
                             hipStream_t stream);
 
+// Device-side free-page list of the append (ids == nullptr: the caller set the table entries).
+struct FreePages {
+  int32_t* ids;
+  int32_t* count;
+  int capacity;
+};
+
 // Decode-time append of one token per sequence (k_new / v_new [B][Hkv][D]), with the tail page's
 // summary kept current when summ is non-null; writes seq_lens_out[b] = seq_lens[b] + 1.
 hipError_t launch_append(const LaunchKV& kv, const void* k_new, const void* v_new, void* summ,
-                         int32_t* seq_lens_out, uint32_t* flags, hipStream_t stream);
+                         int32_t* seq_lens_out, const FreePages& free_pages, uint32_t* flags,
+                         hipStream_t stream);
 
 // Device-side contract check; ORs KVSEL_CHECK_* bits into *flags.
 hipError_t launch_check_inputs(const LaunchKV& kv, const int32_t* sel_idx, const int32_t* sel_cnt,

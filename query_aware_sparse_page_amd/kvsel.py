@@ -28,6 +28,7 @@ KVSEL_SCORE_REFRESH_TAIL = 1
 KVSEL_CHECK_SEQ_LEN = 1
 KVSEL_CHECK_PAGE_ID = 2
 KVSEL_CHECK_SELECTION = 4
+KVSEL_CHECK_NO_FREE_PAGE = 8
 
 c_i32 = ctypes.c_int32
 c_vp = ctypes.c_void_p
@@ -46,6 +47,10 @@ class PagedKVDesc(ctypes.Structure):
         ("max_pages_per_seq", c_i32), ("k_pool", c_vp), ("v_pool", c_vp), ("page_table", c_vp),
         ("seq_lens", c_vp), ("max_seq_len", c_i32),
     ]
+
+
+class FreePagesDesc(ctypes.Structure):
+    _fields_ = [("ids", c_vp), ("count", c_vp), ("capacity", c_i32)]
 
 
 class RopeDesc(ctypes.Structure):
@@ -80,7 +85,8 @@ EXPORTS = {
                                        c_vp, c_i32, c_i32, ctypes.c_float,
                                        ctypes.POINTER(ReuseDesc), c_vp, c_vp, c_vp, c_vp, c_vp,
                                        ctypes.c_size_t, c_vp]),
-    "kvsel_append_kv": (c_i32, [ctypes.POINTER(PagedKVDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "kvsel_append_kv": (c_i32, [ctypes.POINTER(PagedKVDesc), c_vp, c_vp, c_vp, c_vp,
+                                ctypes.POINTER(FreePagesDesc), c_vp, c_vp]),
     "kvsel_check_inputs": (c_i32, [ctypes.POINTER(PagedKVDesc), c_vp, c_vp, c_i32, c_vp, c_vp]),
     "kvsel_gather_probe": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp]),
     "kvsel_rope_table": (c_i32, [ctypes.c_double, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
@@ -265,6 +271,15 @@ def build_summaries(kv: PagedKV, rope: Optional[Rope] = None, tail_only: bool = 
 
 
 @dataclass
+class FreePages:
+    """Device-side free-page list of append_kv: ids int32 [capacity]; ids[:count] are free and the
+    top one is taken first; count int32 [1]."""
+
+    ids: torch.Tensor
+    count: torch.Tensor
+
+
+@dataclass
 class Reuse:
     """Inputs of the speculative-reuse decision (previous query and previous fresh selection)."""
 
@@ -434,11 +449,13 @@ def tile_addresses(kv: PagedKV, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
 
 def append_kv(kv: PagedKV, k_new: torch.Tensor, v_new: torch.Tensor,
               summ: Optional[torch.Tensor] = None, seq_lens_out: Optional[torch.Tensor] = None,
-              flags: Optional[torch.Tensor] = None) -> torch.Tensor:
+              flags: Optional[torch.Tensor] = None,
+              free_pages: Optional["FreePages"] = None) -> torch.Tensor:
     """Decode-time append of one token per sequence (k_new, v_new [B][Hkv][D]) into the pools,
     with the tail page's summary kept current when ``summ`` is given. Writes the new lengths to
-    ``seq_lens_out`` (default: kv.seq_lens, in place) and returns it. The page-table entry of a
-    page a token opens must be set by the caller first."""
+    ``seq_lens_out`` (default: kv.seq_lens, in place) and returns it. The page a token opens is
+    taken from ``free_pages`` (and written into the page table) when given; otherwise its
+    page-table entry must be set by the caller first."""
     d = kv.desc()
     dev = kv.device
     if kv.v_pool is None:
@@ -454,8 +471,16 @@ def append_kv(kv: PagedKV, k_new: torch.Tensor, v_new: torch.Tensor,
     _dev(seq_lens_out, "seq_lens_out", torch.int32)
     if flags is not None:
         _dev(flags, "flags", torch.int32)
+    fp = None
+    if free_pages is not None:
+        _dev(free_pages.ids, "free_pages.ids", torch.int32)
+        _dev(free_pages.count, "free_pages.count", torch.int32)
+        if free_pages.ids.dim() != 1 or free_pages.count.numel() != 1:
+            raise ValueError("free_pages: ids [capacity], count [1]")
+        fp = ctypes.byref(FreePagesDesc(free_pages.ids.data_ptr(), free_pages.count.data_ptr(),
+                                        int(free_pages.ids.numel())))
     _check(lib().kvsel_append_kv(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(summ),
-                                 _ptr(seq_lens_out), _ptr(flags), _stream(dev)))
+                                 _ptr(seq_lens_out), fp, _ptr(flags), _stream(dev)))
     return seq_lens_out
 
 

@@ -152,11 +152,16 @@ def test_append_validation(K):
     lib = K.lib()
     d = _desc(K)
     p = ctypes.c_void_p(0x5000)
-    assert lib.kvsel_append_kv(ctypes.byref(d), None, p, p, p, None, None) == 1      # no k_new
-    assert lib.kvsel_append_kv(ctypes.byref(d), p, None, p, p, None, None) == 1      # no v_new
-    assert lib.kvsel_append_kv(ctypes.byref(d), p, p, None, None, None, None) == 1   # no lengths out
+    ap = lib.kvsel_append_kv
+    assert ap(ctypes.byref(d), None, p, p, p, None, None, None) == 1      # no k_new
+    assert ap(ctypes.byref(d), p, None, p, p, None, None, None) == 1      # no v_new
+    assert ap(ctypes.byref(d), p, p, None, None, None, None, None) == 1   # no lengths out
     dv = _desc(K, v_pool=None)
-    assert lib.kvsel_append_kv(ctypes.byref(dv), p, p, None, p, None, None) == 1     # no V pool
+    assert ap(ctypes.byref(dv), p, p, None, p, None, None, None) == 1     # no V pool
     dn = _desc(K, page_table=None)
-    assert lib.kvsel_append_kv(ctypes.byref(dn), p, p, None, p, None, None) == 1
-    assert lib.kvsel_append_kv(ctypes.byref(_desc(K, head_dim=96)), p, p, None, p, None, None) == 2
+    assert ap(ctypes.byref(dn), p, p, None, p, None, None, None) == 1
+    assert ap(ctypes.byref(_desc(K, head_dim=96)), p, p, None, p, None, None, None) == 2
+    # free-page list: ids, count and a positive capacity required
+    for fp in (K.FreePagesDesc(None, 0x6000, 4), K.FreePagesDesc(0x6000, None, 4),
+               K.FreePagesDesc(0x6000, 0x7000, 0)):
+        assert ap(ctypes.byref(d), p, p, None, p, ctypes.byref(fp), None, None) == 1

@@ -171,3 +171,106 @@ def test_growing_speculative_loop(K):
                                              spec[2].cpu().numpy(), spec[3].cpu().numpy(), 16,
                                              scale_of(128))
     assert_attention_close(spec[6], spec[7], o_out, o_lse, "bf16")
+
+
+def free_list_case(seed, lens, T, P=16, D=64, Hkv=2, extra_free=3):
+    """A cache whose table rows hold junk (-7) past each sequence's pages, and a shuffled free list
+    of the spare physical pages: one for every page the T appends will open, plus extra_free."""
+    opened = sum(-(-(L + T) // P) - -(-L // P) for L in lens)
+    w = W.custom(seed, B=len(lens), Hq=2 * Hkv, Hkv=Hkv, D=D, P=P, k=4, lens=lens, dtype="bf16",
+                 spare_pages=opened + extra_free)
+    width = max(-(-(L + T) // P) for L in lens)
+    table = np.full((w.B, width), -7, np.int32)
+    used = set()
+    for b in range(w.B):
+        n = w.n_pages(b)
+        table[b, :n] = w.page_table[b, :n].numpy()
+        used.update(int(x) for x in table[b, :n])
+    spare = np.array([p for p in range(w.num_phys_pages) if p not in used], np.int32)
+    np.random.default_rng(seed).shuffle(spare)
+    return dataclasses.replace(w, page_table=torch.from_numpy(table)), spare, opened
+
+
+def test_append_takes_pages_from_the_free_list(K):
+    """Pages opened by the appends come off the top of the free list into the table (which
+    sequence gets which of them is unspecified: checked as a set); the pools and summaries then
+    equal the oracle's append on the table the appends produced."""
+    P, T = 16, 16 + 5
+    lens = [2 * P - 1, P, 0, 3 * P + 4, P - 2]
+    w, spare, opened = free_list_case(731, lens, T, P=P)
+    say(f"append from a free list: lens {lens}, {T} steps, {opened} pages to open")
+    kv = kv_of(K, w)
+    summ = K.build_summaries(kv)
+    fp = K.FreePages(torch.from_numpy(spare).cuda(), torch.tensor([len(spare)], dtype=torch.int32,
+                                                                  device="cuda"))
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gen = torch.Generator().manual_seed(732)
+    steps = []
+    for t in range(T):
+        kn = torch.randn((w.B, w.Hkv, 64), generator=gen).to(torch.bfloat16)
+        vn = torch.randn((w.B, w.Hkv, 64), generator=gen).to(torch.bfloat16)
+        K.append_kv(kv, kn.cuda(), vn.cuda(), summ=summ, flags=flags, free_pages=fp)
+        steps.append((kn, vn))
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    assert int(fp.count.item()) == len(spare) - opened
+    table = kv.page_table.cpu().numpy()
+    before = w.page_table.numpy()
+    taken = []
+    for b, L in enumerate(lens):
+        n0, n1 = -(-L // P), -(-(L + T) // P)
+        assert (table[b, :n0] == before[b, :n0]).all()
+        assert (table[b, n1:] == -7).all()
+        taken.extend(int(x) for x in table[b, n0:n1])
+    assert sorted(taken) == sorted(int(x) for x in spare[len(spare) - opened:])
+    Kc, Vc = w.k_pool.double().numpy(), w.v_pool.double().numpy()
+    cur = np.asarray(lens, np.int64)
+    for kn, vn in steps:
+        Kc, Vc, cur, rej = O.append_tokens(Kc, Vc, table, cur, kn.double().numpy(),
+                                           vn.double().numpy(), P)
+        assert not rej.any()
+    assert list(kv.seq_lens.cpu().numpy()) == list(cur)
+    assert np.array_equal(kv.k_pool.double().cpu().numpy(), Kc)
+    assert np.array_equal(kv.v_pool.permute(0, 1, 3, 2).double().cpu().numpy(), Vc)
+    wt = dataclasses.replace(w, page_table=torch.from_numpy(table),
+                             seq_lens=torch.from_numpy(cur.astype(np.int32)))
+    assert_summaries_equal(summ, O.page_summaries(Kc, table, wt.seq_lens, P), wt)
+
+
+def test_free_list_runs_out(K):
+    """Two sequences open a page with one id on the list: one takes it, the other is left as it
+    was (KVSEL_CHECK_NO_FREE_PAGE) and the count stays 0; a sequence that does not open a page is
+    unaffected. Then an id outside the pool is consumed and the sequence again left as it was
+    (KVSEL_CHECK_PAGE_ID)."""
+    P = 16
+    lens = [P, 2 * P, P - 1]
+    w, spare, _ = free_list_case(741, lens, 1, P=P, extra_free=0)
+    say("append: free list runs out")
+    kv = kv_of(K, w)
+    summ = K.build_summaries(kv)
+    fp = K.FreePages(torch.from_numpy(spare).cuda(), torch.ones(1, dtype=torch.int32, device="cuda"))
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kn = torch.ones((w.B, w.Hkv, 64), dtype=torch.bfloat16, device="cuda")
+    K.append_kv(kv, kn, kn, summ=summ, flags=flags, free_pages=fp)
+    torch.cuda.synchronize()
+    got = kv.seq_lens.cpu().tolist()
+    assert int(flags.item()) == K.KVSEL_CHECK_NO_FREE_PAGE and int(fp.count.item()) == 0
+    assert got[2] == P and sorted(got[:2]) == sorted([P + 1, 2 * P]) or \
+        sorted(got[:2]) == sorted([P, 2 * P + 1]) and got[2] == P
+    won = 0 if got[0] == P + 1 else 1
+    lost = 1 - won
+    table = kv.page_table.cpu().numpy()
+    assert table[won, lens[won] // P] == spare[0] and table[lost, lens[lost] // P] == -7
+    # an id outside the pool: consumed, the sequence left as it was
+    flags.zero_()
+    fp.ids[0] = w.num_phys_pages + 5
+    fp.count.fill_(1)
+    before = kv.seq_lens.clone()
+    only = torch.zeros((w.B, w.Hkv, 64), dtype=torch.bfloat16, device="cuda")
+    K.append_kv(kv, only, only, summ=summ, flags=flags, free_pages=fp)
+    torch.cuda.synchronize()
+    assert int(flags.item()) & K.KVSEL_CHECK_PAGE_ID
+    assert int(fp.count.item()) == 0
+    after = kv.seq_lens.cpu().tolist()
+    assert after[lost] == before[lost].item()
+    assert kv.page_table[lost, lens[lost] // P].item() == -7
