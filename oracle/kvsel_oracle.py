@@ -33,6 +33,12 @@ Readings taken where the pages are silent (each restated at its function):
 * R9  Rotary convention: rotate-half pairs (i, i + D/2), inverse frequency theta^(-2i/D); the
       cos/sin table is fp64 libm values rounded to fp32; the rotation itself is fp32 with every
       product and sum rounded on its own (no fused multiply-add), then rounded to the cache dtype.
+* R11 A quantized cache stores OCP FP8 E4M3 codes, rounded to nearest (ties to even mantissa),
+      saturating at 448.
+* R12 One fp32 scale per (physical page, KV head) tile of K and of V: amax / 448; a code stands
+      for decode(code) * scale, and attention runs over those values.
+* R13 Summaries of an fp8 page are bf16, rounded outward (lo down, hi up) from the extremes of
+      the dequantized keys, so the page score stays an upper bound.
 """
 from __future__ import annotations
 
@@ -59,6 +65,14 @@ __all__ = [
     "rope_rotate",
     "round_to_dtype",
     "decode_step",
+    "FP8_E4M3_MAX",
+    "fp8_e4m3_decode",
+    "fp8_e4m3_encode",
+    "quantize_pages",
+    "dequantize_pages",
+    "bf16_round_down",
+    "bf16_round_up",
+    "page_summaries_fp8",
 ]
 
 
@@ -430,6 +444,100 @@ def rope_rotate(k_pool, cos, sin, page_row, row_step: int, dtype: str) -> np.nda
         y2 = np.add(np.multiply(x2, c, dtype=np.float32), np.multiply(x1, s, dtype=np.float32),
                     dtype=np.float32)
         out[p] = round_to_dtype(np.concatenate([y1, y2], axis=-1), dtype)
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# fp8 pages: a quantized cache ([KV-Cache wiki] "Contradictions & Updates": a quantized cache
+# holds longer contexts at a small accuracy cost; [KV Packet] section 3: compatible with KV
+# compression). The pages fix no format; readings R11-R13 below.
+# ----------------------------------------------------------------------------------------------
+
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Values of 8-bit codes in the E4M3 format of the Open Compute Project 8-bit floating point
+    specification (OFP8): a sign bit, 4 exponent bits with bias 7 and 3 mantissa bits; exponent
+    field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; there are no infinities, and the largest
+    finite magnitude is 1.75 * 2^8 = 448. Returns float64 (every value is exact)."""
+    c = _ints(codes) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (c & 0x7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def fp8_e4m3_encode(x) -> np.ndarray:
+    """Reading R11: round each value to the nearest E4M3 value, ties to the code with an even
+    mantissa (last bit 0), magnitudes beyond 448 saturate to 448; the sign bit is kept (so -0.0
+    is 0x80). Plainly: the nearest of the 127 non-negative finite values, by search. Returns
+    uint8 codes."""
+    x = np.asarray(x, dtype=np.float64)
+    assert not np.isnan(x).any()
+    table = fp8_e4m3_decode(np.arange(127))  # codes 0x00..0x7E, increasing values
+    a = np.minimum(np.abs(x), FP8_E4M3_MAX)
+    hi = np.searchsorted(table, a, side="left")  # first value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - table[lo]
+    d_hi = table[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(table[hi] == a, hi, np.where(pick_hi, hi, lo))
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_pages(pool) -> Tuple[np.ndarray, np.ndarray]:
+    """Reading R12: one fp32 scale per (physical page, KV head) tile, amax / 448 (fp32 division;
+    1 for an all-zero tile), and every element coded as encode(fp32(x / scale)) with x the cache
+    value (bf16 and fp32 values are exact in fp32; the division is fp32, correctly rounded).
+    The layout of a tile's elements does not matter (amax and the coding are per element).
+
+    Returns (codes uint8, same shape as pool; scales float32 [Npp][Hkv])."""
+    X = as_f64(pool).astype(np.float32)  # exact: the cache values are fp32 or bf16
+    amax = np.abs(X).reshape(X.shape[0], X.shape[1], -1).max(axis=2)
+    scale = np.where(amax > 0, amax / np.float32(FP8_E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (X / scale[:, :, None, None]).astype(np.float32)
+    return fp8_e4m3_encode(y), scale
+
+
+def dequantize_pages(codes, scales) -> np.ndarray:
+    """The value each code stands for: decode(code) * its tile's scale, exact in float64."""
+    return fp8_e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[:, :, None, None]
+
+
+def bf16_round_down(x) -> np.ndarray:
+    """Largest bf16 value <= x (8 significant bits), for x zero or of magnitude >= 2^-126."""
+    return _bf16_directed(x, np.floor)
+
+
+def bf16_round_up(x) -> np.ndarray:
+    """Smallest bf16 value >= x (8 significant bits), for x zero or of magnitude >= 2^-126."""
+    return _bf16_directed(x, np.ceil)
+
+
+def _bf16_directed(x, step) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float64)
+    nz = x[x != 0]
+    assert (np.abs(nz) >= 2.0 ** -126).all(), "bf16 subnormal range"
+    m, e = np.frexp(x)  # x = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(step(m * 256.0), e - 8)  # m * 2^8 has 8 integer bits; scaling is exact
+
+
+def page_summaries_fp8(k_codes, k_scale, page_table, seq_lens, page_size: int) -> np.ndarray:
+    """Reading R13: the summary of an fp8 page is bf16, the outward rounding of the extremes of
+    its dequantized keys: lo = the largest bf16 <= min, hi = the smallest bf16 >= max (products of
+    a code's value and the fp32 scale are exact in float64). The outward rounding keeps every
+    page score an upper bound of q.k over the page's keys. Valid slots only, as page_summaries.
+
+    Returns summ[Npp][Hkv][2][D] float64 (bf16 values); unreferenced pages stay NaN."""
+    summ = page_summaries(dequantize_pages(k_codes, k_scale), page_table, seq_lens, page_size)
+    out = np.full_like(summ, np.nan)
+    done = ~np.isnan(summ[:, 0, 0, 0])
+    out[done, :, 0, :] = bf16_round_down(summ[done, :, 0, :])
+    out[done, :, 1, :] = bf16_round_up(summ[done, :, 1, :])
     return out
 
 
