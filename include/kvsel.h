@@ -18,7 +18,11 @@
  *  - Shapes: B sequences, Hq query heads, Hkv KV heads (G = Hq / Hkv; query head h reads KV head
  *    h / G), head dim D in {64, 128}, page size P in {16, 32}, G in {1, 2, 4, 8}.
  *  - Element type (kvsel_paged_kv.dtype): KVSEL_F32 (float) or KVSEL_BF16 (bfloat16 bits in
- *    uint16). K, V, q, summaries and attention outputs all use it.
+ *    uint16). K, V, q, summaries and attention outputs all use it. KVSEL_FP8_E4M3: K and V
+ *    pools hold 8-bit codes with one fp32 scale per (physical page, KV head) tile (k_scale,
+ *    v_scale; see kvsel_quantize_pages); q, summaries and outputs are then bfloat16 ("the element
+ *    type" below means bfloat16 for them). Calls on an fp8 cache take no rotary argument, and
+ *    kvsel_append_kv and kvsel_rope_shift do not take an fp8 cache (KVSEL_ERR_UNSUPPORTED).
  *  - Pools: k_pool is [num_phys_pages][Hkv][P][D] (token-major pages: key of physical page p,
  *    KV head j, slot s starts at element ((p * Hkv + j) * P + s) * D). v_pool is
  *    [num_phys_pages][Hkv][D][P] (channel-major pages: channel d of the values of page p, head j
@@ -48,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVSEL_ABI_VERSION 2
+#define KVSEL_ABI_VERSION 3
 
 typedef int32_t kvsel_status;
 #define KVSEL_OK 0
@@ -64,6 +68,7 @@ typedef int32_t kvsel_status;
 
 #define KVSEL_F32 0
 #define KVSEL_BF16 1
+#define KVSEL_FP8_E4M3 2 /* pools only: OCP FP8 E4M3 codes + per-tile fp32 scales */
 
 /* Workspace kinds for kvsel_workspace_bytes. */
 #define KVSEL_OP_SCORE_TOPK 1
@@ -76,7 +81,7 @@ typedef int32_t kvsel_status;
 
 /* Host struct describing one paged KV cache (device pointers inside). */
 typedef struct kvsel_paged_kv {
-  int32_t dtype;             /* KVSEL_F32 or KVSEL_BF16                              */
+  int32_t dtype;             /* KVSEL_F32, KVSEL_BF16 or KVSEL_FP8_E4M3               */
   int32_t batch;             /* B                                                    */
   int32_t num_q_heads;       /* Hq                                                   */
   int32_t num_kv_heads;      /* Hkv                                                  */
@@ -89,6 +94,8 @@ typedef struct kvsel_paged_kv {
   const int32_t* page_table; /* [B][max_pages_per_seq]                               */
   const int32_t* seq_lens;   /* [B]                                                  */
   int32_t max_seq_len;       /* 0, or the caller's bound on every seq_lens[b] (host)  */
+  const float* k_scale;      /* fp8 only: [num_phys_pages][Hkv] fp32 (else ignored)   */
+  const float* v_scale;      /* fp8 only: [num_phys_pages][Hkv] fp32, with v_pool     */
 } kvsel_paged_kv;
 
 /* max_seq_len: page tables are usually allocated for the longest context a sequence may reach,
@@ -154,6 +161,9 @@ size_t kvsel_workspace_bytes(const kvsel_paged_kv* kv, int32_t k, int32_t op,
  * tail_only != 0 rebuilds only each sequence's last logical page (the page a decode step appends
  * to). rope != NULL applies the rotary rotation to each key before the reduction (bit-identical
  * to rotating the pool first with kvsel_rope_shift).
+ * fp8 cache: the extremes of the dequantized keys (code value * the tile's k_scale, exact),
+ * rounded outward to bfloat16 (lo toward -inf, hi toward +inf), so the page score below still
+ * bounds q.k over the page's keys; kvsel_score_topk's tail refresh does the same.
  * [FreeKV] section 2.1 chooses KV pages with the query; the min/max page summary is this
  * library's rule for it (the pages do not define one). */
 kvsel_status kvsel_build_summaries(const kvsel_paged_kv* kv, const kvsel_rope* rope,
@@ -192,6 +202,9 @@ kvsel_status kvsel_score_topk(const kvsel_paged_kv* kv, const kvsel_rope* rope, 
  * (0 = the library's choice; a request is rounded to a supported size, and raised so that a list
  * has at most 256 splits) and the splits are merged by log-sum-exp in a second launch.
  * rope != NULL rotates each key on the fly (bit-identical to a pool rotated by kvsel_rope_shift).
+ * fp8 cache: k_t and v_t are the dequantized values (code * the page's k_scale / v_scale); the
+ * logits take the key scale as scale * k_scale in fp32, and each probability enters the value
+ * product as bfloat16(p * v_scale) while the softmax sum adds bfloat16(p).
  * ws / ws_bytes: workspace of kvsel_workspace_bytes(kv, k, KVSEL_OP_ATTENTION, pages_per_split)
  * bytes for the split partials (0 bytes, and ws may be NULL, when there is a single split).
  * [FreeKV] section 2.1 (attention over the retrieved pages), [KV wiki] (decode attention, GQA). */
@@ -255,6 +268,21 @@ kvsel_status kvsel_speculative_step(const kvsel_paged_kv* kv, const kvsel_rope* 
                                     const kvsel_reuse* reuse, int32_t* sel_idx, int32_t* sel_cnt,
                                     void* out, float* lse, void* ws, size_t ws_bytes,
                                     void* stream);
+
+/* Quantize a cache's pages to fp8 (the pages name a quantized cache only as a trade-off of
+ * capacity against a little accuracy -- [KV wiki], Contradictions & Updates entry -- and fix no
+ * format; this library's rule): for every physical page p and KV head j, of K and of V
+ * separately, scale[p][j] = amax / 448 in fp32 (amax = the largest magnitude of the tile's P * D
+ * values; 1 when it is 0), and every value x becomes the OCP FP8 E4M3 code of fp32(x / scale)
+ * (fp32 division, correctly rounded), rounded to nearest with ties to an even mantissa and
+ * magnitudes from 448 up saturating to 448; the sign bit is kept.
+ * src: a KVSEL_F32 or KVSEL_BF16 cache; its page table and lengths are not used. k_codes:
+ * [num_phys_pages][Hkv][P][D] uint8 and k_scale [num_phys_pages][Hkv] fp32 out; v_codes
+ * ([num_phys_pages][Hkv][D][P], the device value layout) and v_scale likewise from src->v_pool,
+ * both NULL to quantize K only. The outputs make an fp8 descriptor with the same page table.
+ * One launch; one wave per tile. */
+kvsel_status kvsel_quantize_pages(const kvsel_paged_kv* src, uint8_t* k_codes, float* k_scale,
+                                  uint8_t* v_codes, float* v_scale, void* stream);
 
 /* Device-side free-page list for kvsel_append_kv (the caller's page pool, kept on the device so
  * that a captured decode loop needs no host step to grow a sequence): ids[0 .. *count) are free

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libkvsel.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["summaries.hip", "score_topk.hip", "attention.hip", "select_attend.hip", "speculative.hip",
-           "append.hip", "rope.hip", "probe.hip", "check.hip", "kvsel_abi.hip"]
+           "append.hip", "quantize.hip", "rope.hip", "probe.hip", "check.hip", "kvsel_abi.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -2,6 +2,8 @@
 // (KV head, sequence, split), body attn_bf16_block / attn_f32_block) and the log-sum-exp merge
 // of the splits in a second launch. The kernel design (tiles, MFMA layouts, softmax, partials)
 // is described in kvsel_attn.h.
+#include <type_traits>
+
 #include "kvsel_attn.h"
 
 namespace kvsel {
@@ -10,6 +12,12 @@ template <int D, int P, int WAVES, int TPW, bool ROPE>
 __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a, int G) {
   // grid (Hkv, B, splits)
   attn_bf16_block<D, P, WAVES, TPW, ROPE>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// fp8 pools (E4M3 codes, per-tile scales), decoded to bf16 in registers; no rotary gather.
+template <int D, int P, int WAVES, int TPW>
+__global__ __launch_bounds__(WAVES * 64) void attn_fp8_kernel(AttnArgs a, int G) {
+  attn_bf16_block<D, P, WAVES, TPW, false, 0, true>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 template <int D, int P, int WAVES, int TPW, bool ROPE>
@@ -130,7 +138,9 @@ template <typename T, int D, int P, int WAVES, int TPW>
 static void launch_split(const AttnArgs& a, int G, bool rope, hipStream_t stream) {
   const dim3 grid(a.Hkv, a.nlists / a.Hkv, a.nsplit);
   const dim3 block(WAVES * 64);
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 1) {
+    hipLaunchKernelGGL((attn_fp8_kernel<D, P, WAVES, TPW>), grid, block, 0, stream, a, G);
+  } else if constexpr (sizeof(T) == 2) {
     if (rope) hipLaunchKernelGGL((attn_bf16_kernel<D, P, WAVES, TPW, true>), grid, block, 0, stream, a, G);
     else hipLaunchKernelGGL((attn_bf16_kernel<D, P, WAVES, TPW, false>), grid, block, 0, stream, a, G);
   } else {
@@ -154,7 +164,8 @@ static hipError_t launch_tiles(int tiles, const AttnArgs& a, int G, bool rope, i
     if (e != hipSuccess) return e;
   }
   if (!(parts & 2) || a.nsplit == 1) return hipSuccess;
-  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(a.Hkv, G, a.nlists / a.Hkv), dim3(D), 0, stream,
+  using OT = std::conditional_t<sizeof(T) == 1, bf16_t, T>;  // fp8 pools: bf16 outputs
+  hipLaunchKernelGGL((attn_merge_kernel<OT, D>), dim3(a.Hkv, G, a.nlists / a.Hkv), dim3(D), 0, stream,
                      a, G);
   return hipGetLastError();
 }
@@ -169,6 +180,10 @@ static hipError_t launch_p(int P, int tiles, const AttnArgs& a, int G, bool rope
 static hipError_t launch_parts(const LaunchKV& kv, const AttnArgs& a, bool rope, int parts,
                                hipStream_t stream) {
   const int tiles = tiles_for(kv, a.pps);
+  if (kv.dtype == 2) {
+    if (kv.D == 64) return launch_p<fp8_t, 64>(kv.P, tiles, a, kv.G, rope, parts, stream);
+    return launch_p<fp8_t, 128>(kv.P, tiles, a, kv.G, rope, parts, stream);
+  }
   if (kv.dtype == 0) {
     if (kv.D == 64) return launch_p<float, 64>(kv.P, tiles, a, kv.G, rope, parts, stream);
     return launch_p<float, 128>(kv.P, tiles, a, kv.G, rope, parts, stream);
@@ -199,6 +214,8 @@ AttnArgs attn_args(const LaunchKV& kv, const RopeArgs& rope, const void* q, cons
   a.nsplit = (k + pps - 1) / pps;
   a.nlists = kv.B * kv.Hkv;
   a.scale = scale;
+  a.k_scale = kv.k_scale;
+  a.v_scale = kv.v_scale;
   a.rope = rope;
   a.part_acc = nullptr;
   a.part_ml = nullptr;

@@ -45,7 +45,10 @@ kvsel_status flatten(const kvsel_paged_kv* kv, int need, LaunchKV* out) {
   if (!kv->k_pool) return KVSEL_ERR_INVALID_ARGUMENT;
   if ((need & 1) && !kv->v_pool) return KVSEL_ERR_INVALID_ARGUMENT;
   if ((need & 2) && (!kv->page_table || !kv->seq_lens)) return KVSEL_ERR_INVALID_ARGUMENT;
-  if (kv->dtype != KVSEL_F32 && kv->dtype != KVSEL_BF16) return KVSEL_ERR_UNSUPPORTED;
+  if (kv->dtype != KVSEL_F32 && kv->dtype != KVSEL_BF16 && kv->dtype != KVSEL_FP8_E4M3)
+    return KVSEL_ERR_UNSUPPORTED;
+  if (kv->dtype == KVSEL_FP8_E4M3 && (!kv->k_scale || ((need & 1) && !kv->v_scale)))
+    return KVSEL_ERR_INVALID_ARGUMENT;
   const int G = kv->num_q_heads / kv->num_kv_heads;
   if (kv->head_dim != 64 && kv->head_dim != 128) return KVSEL_ERR_UNSUPPORTED;
   if (kv->page_size != 16 && kv->page_size != 32) return KVSEL_ERR_UNSUPPORTED;
@@ -54,7 +57,7 @@ kvsel_status flatten(const kvsel_paged_kv* kv, int need, LaunchKV* out) {
   if (kv->batch > KVSEL_MAX_BATCH || kv->max_pages_per_seq > KVSEL_MAX_PAGES_PER_SEQ)
     return KVSEL_ERR_UNSUPPORTED;
   if (kv->max_seq_len < 0) return KVSEL_ERR_INVALID_ARGUMENT;
-  out->dtype = kv->dtype == KVSEL_F32 ? 0 : 1;
+  out->dtype = kv->dtype == KVSEL_F32 ? 0 : kv->dtype == KVSEL_BF16 ? 1 : 2;
   out->B = kv->batch;
   out->Hq = kv->num_q_heads;
   out->Hkv = kv->num_kv_heads;
@@ -72,15 +75,19 @@ kvsel_status flatten(const kvsel_paged_kv* kv, int need, LaunchKV* out) {
   out->v_pool = kv->v_pool;
   out->page_table = kv->page_table;
   out->seq_lens = kv->seq_lens;
+  out->k_scale = out->dtype == 2 ? kv->k_scale : nullptr;
+  out->v_scale = out->dtype == 2 ? kv->v_scale : nullptr;
   return KVSEL_OK;
 }
 
-kvsel_status flatten_rope(const kvsel_rope* rope, RopeArgs* out) {
+// A rotary argument of a call on cache f (fp8 caches take none).
+kvsel_status flatten_rope(const kvsel_rope* rope, const LaunchKV& f, RopeArgs* out) {
   out->cos = nullptr;
   out->sin = nullptr;
   out->page_row = nullptr;
   out->row_step = 0;
   if (!rope) return KVSEL_OK;
+  if (f.dtype == 2) return KVSEL_ERR_UNSUPPORTED;
   if (!rope->cos || !rope->sin || !rope->page_row || rope->n_rows < 1) return KVSEL_ERR_INVALID_ARGUMENT;
   if (rope->row_step != 0 && rope->row_step != 1) return KVSEL_ERR_INVALID_ARGUMENT;
   out->cos = rope->cos;
@@ -135,7 +142,7 @@ kvsel_status kvsel_build_summaries(const kvsel_paged_kv* kv, const kvsel_rope* r
   kvsel_status st = flatten(kv, 2, &f);
   if (st != KVSEL_OK) return st;
   if (!summ) return KVSEL_ERR_INVALID_ARGUMENT;
-  if ((st = flatten_rope(rope, &r)) != KVSEL_OK) return st;
+  if ((st = flatten_rope(rope, f, &r)) != KVSEL_OK) return st;
   if ((st = check_device()) != KVSEL_OK) return st;
   return launch_status(launch_summaries(f, r, tail_only ? 1 : 0, summ, (hipStream_t)stream));
 }
@@ -150,7 +157,7 @@ kvsel_status kvsel_score_topk(const kvsel_paged_kv* kv, const kvsel_rope* rope, 
   if (st != KVSEL_OK) return st;
   if (!summ || !q || !sel_idx || !sel_cnt || k < 1) return KVSEL_ERR_INVALID_ARGUMENT;
   if (flags & ~KVSEL_SCORE_REFRESH_TAIL) return KVSEL_ERR_INVALID_ARGUMENT;
-  if ((st = flatten_rope(rope, &r)) != KVSEL_OK) return st;
+  if ((st = flatten_rope(rope, f, &r)) != KVSEL_OK) return st;
   ReuseArgs ra;
   memset(&ra, 0, sizeof(ra));
   if (reuse) {
@@ -188,7 +195,7 @@ kvsel_status kvsel_sparse_decode_attn(const kvsel_paged_kv* kv, const kvsel_rope
   if (st != KVSEL_OK) return st;
   if (!q || !sel_idx || !sel_cnt || !out || k < 1 || pages_per_split < 0)
     return KVSEL_ERR_INVALID_ARGUMENT;
-  if ((st = flatten_rope(rope, &r)) != KVSEL_OK) return st;
+  if ((st = flatten_rope(rope, f, &r)) != KVSEL_OK) return st;
   if (attention_pages_per_split(f, k, pages_per_split) <= 0) return KVSEL_ERR_UNSUPPORTED;
   const size_t need = attention_workspace(f, k, pages_per_split);
   if (need > 0 && (!ws || ws_bytes < need)) return KVSEL_ERR_WORKSPACE;
@@ -207,7 +214,7 @@ kvsel_status kvsel_select_attend(const kvsel_paged_kv* kv, const kvsel_rope* rop
   if (st != KVSEL_OK) return st;
   if (!summ || !q || !sel_idx || !sel_cnt || !out || k < 1) return KVSEL_ERR_INVALID_ARGUMENT;
   if (flags & ~KVSEL_SCORE_REFRESH_TAIL) return KVSEL_ERR_INVALID_ARGUMENT;
-  if ((st = flatten_rope(rope, &r)) != KVSEL_OK) return st;
+  if ((st = flatten_rope(rope, f, &r)) != KVSEL_OK) return st;
   if (attention_pages_per_split(f, k, 0) <= 0) return KVSEL_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < select_attend_workspace(f, k)) return KVSEL_ERR_WORKSPACE;
   if ((st = check_device()) != KVSEL_OK) return st;
@@ -228,7 +235,7 @@ kvsel_status kvsel_speculative_step(const kvsel_paged_kv* kv, const kvsel_rope* 
       !reuse->used_cnt || !reuse->corrected)
     return KVSEL_ERR_INVALID_ARGUMENT;
   if (flags & ~KVSEL_SCORE_REFRESH_TAIL) return KVSEL_ERR_INVALID_ARGUMENT;
-  if ((st = flatten_rope(rope, &r)) != KVSEL_OK) return st;
+  if ((st = flatten_rope(rope, f, &r)) != KVSEL_OK) return st;
   if (attention_pages_per_split(f, k, 0) <= 0) return KVSEL_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < select_attend_workspace(f, k)) return KVSEL_ERR_WORKSPACE;
   ReuseArgs ra;
@@ -263,6 +270,7 @@ kvsel_status kvsel_append_kv(const kvsel_paged_kv* kv, const void* k_new, const 
   LaunchKV f;
   kvsel_status st = flatten(kv, 3, &f);
   if (st != KVSEL_OK) return st;
+  if (f.dtype == 2) return KVSEL_ERR_UNSUPPORTED;  // an fp8 page's scale is fixed at quantization
   if (!k_new || !v_new || !seq_lens_out) return KVSEL_ERR_INVALID_ARGUMENT;
   FreePages fp{nullptr, nullptr, 0};
   if (free_pages) {
@@ -273,6 +281,19 @@ kvsel_status kvsel_append_kv(const kvsel_paged_kv* kv, const void* k_new, const 
   if ((st = check_device()) != KVSEL_OK) return st;
   return launch_status(launch_append(f, k_new, v_new, summ, seq_lens_out, fp, flags,
                                      (hipStream_t)stream));
+}
+
+kvsel_status kvsel_quantize_pages(const kvsel_paged_kv* src, uint8_t* k_codes, float* k_scale,
+                                  uint8_t* v_codes, float* v_scale, void* stream) {
+  LaunchKV f;
+  const bool with_v = v_codes || v_scale;
+  kvsel_status st = flatten(src, with_v ? 1 : 0, &f);
+  if (st != KVSEL_OK) return st;
+  if (f.dtype == 2) return KVSEL_ERR_UNSUPPORTED;  // the source is an f32 or bf16 cache
+  if (!k_codes || !k_scale || (with_v && (!v_codes || !v_scale))) return KVSEL_ERR_INVALID_ARGUMENT;
+  if ((st = check_device()) != KVSEL_OK) return st;
+  return launch_status(
+      launch_quantize(f, k_codes, k_scale, v_codes, v_scale, (hipStream_t)stream));
 }
 
 kvsel_status kvsel_gather_probe(const uint64_t* chunk_addr, int32_t n_chunks, int32_t chunk_bytes,
@@ -303,7 +324,7 @@ kvsel_status kvsel_rope_shift(const kvsel_paged_kv* kv, const kvsel_rope* rope, 
   kvsel_status st = flatten(kv, 0, &f);
   if (st != KVSEL_OK) return st;
   if (!rope || !k_out) return KVSEL_ERR_INVALID_ARGUMENT;
-  if ((st = flatten_rope(rope, &r)) != KVSEL_OK) return st;
+  if ((st = flatten_rope(rope, f, &r)) != KVSEL_OK) return st;
   if ((st = check_device()) != KVSEL_OK) return st;
   return launch_status(launch_rope_shift(f, r, k_out, (hipStream_t)stream));
 }

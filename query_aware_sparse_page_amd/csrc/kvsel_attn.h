@@ -35,6 +35,7 @@
 #include <math.h>
 
 #include "kvsel_device.h"
+#include "kvsel_fp8.h"
 #include "kvsel_internal.h"
 #include "kvsel_topk.h"
 
@@ -56,6 +57,8 @@ struct AttnArgs {
   int Hkv, P, log2P, maxp, Npp, k, pps, nsplit, nlists;
   int maxn;  // live pages at most (<= maxp, the row stride)
   float scale;
+  const float* k_scale;  // fp8 pools: [Npp][Hkv] tile scales of K and V (else null)
+  const float* v_scale;
   RopeArgs rope;
   float* part_acc;   // [nlists][nsplit][G][D]
   float2* part_ml;   // [nlists][nsplit][G]
@@ -285,8 +288,14 @@ __device__ __forceinline__ void finish_block(const AttnArgs& a, int G, int list,
 // bf16
 // ------------------------------------------------------------------------------------------
 // SEL_C > 0: fused selection with SEL_C score keys per thread (select_tiles).
-template <int D, int P, int WAVES, int TPW, bool ROPE, int SEL_C = 0>
+// FP8: the pools hold E4M3 codes with per-tile scales. A lane's K and V loads are then 8 bytes
+// (8 codes) where bf16 loads 16, decoded to bf16 exactly after every load has been issued, so the
+// MFMA layouts are unchanged. A lane's 8 tokens of a tile lie in one page, so one (k_scale,
+// v_scale) pair per lane and tile: the logits take scale * k_scale, and each probability enters
+// P V as bf16(p * v_scale) while l adds bf16(p).
+template <int D, int P, int WAVES, int TPW, bool ROPE, int SEL_C = 0, bool FP8 = false>
 __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j, int b, int split) {
+  static_assert(!(FP8 && (ROPE || SEL_C > 0)), "fp8 pools take the plain split launch");
   constexpr int TT = 32;       // tokens per tile
   constexpr int CB = D / 32;   // 32-channel blocks of q K^T
   constexpr int VB = D / 16;   // 16-channel blocks of P V
@@ -326,6 +335,8 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
 
   // ---- every K / V load of this wave's tiles ----
   uint4 kraw[TPW][2][CB], vraw[TPW][VB];
+  [[maybe_unused]] uint2 k8[TPW][2][CB], v8[TPW][VB];  // fp8 codes (FP8 only)
+  [[maybe_unused]] float ksc[TPW], vsc[TPW];  // the lane's page's tile scales (FP8 only)
   int vmask[TPW];  // bit e set: token 8*q4 + e of the tile is valid
   int krow[TPW][2];
 #pragma unroll
@@ -337,9 +348,16 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
       const int pg = tp.page_of(t, u);
       // an invalid token's row of S^T is masked to -inf below (rows of an MFMA are
       // independent), so its K needs no zeroing
-      const bf16_t* row = kp + (((size_t)pg * a.Hkv + j) * P + slot) * D + 8 * q4;
+      const size_t krow_off = (((size_t)pg * a.Hkv + j) * P + slot) * D + 8 * q4;
+      if constexpr (FP8) {
+        const uint8_t* row = (const uint8_t*)a.k_pool + krow_off;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) kraw[t][h][cb] = load16(row + 32 * cb);
+        for (int cb = 0; cb < CB; ++cb) k8[t][h][cb] = load8(row + 32 * cb);
+      } else {
+        const bf16_t* row = kp + krow_off;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) kraw[t][h][cb] = load16(row + 32 * cb);
+      }
       if (ROPE) {
         const int pr = a.rope.page_row[pg];
         krow[t][h] = pr < 0 ? -1 : pr + a.rope.row_step * slot;
@@ -352,11 +370,31 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
 #pragma unroll
     for (int e = 0; e < 8; ++e) m |= (slot + e < tp.valid_of(t, u)) ? (1 << e) : 0;
     vmask[t] = m;
-    const bf16_t* vt = vp + ((size_t)pg * a.Hkv + j) * D * P + slot + (size_t)r16 * P;
+    const size_t vt_off = ((size_t)pg * a.Hkv + j) * D * P + slot + (size_t)r16 * P;
+    if constexpr (FP8) {
+      const uint8_t* vt = (const uint8_t*)a.v_pool + vt_off;
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = load16(vt + (size_t)(16 * vb) * P);
+      for (int vb = 0; vb < VB; ++vb) v8[t][vb] = load8(vt + (size_t)(16 * vb) * P);
+      ksc[t] = a.k_scale[(size_t)pg * a.Hkv + j];
+      vsc[t] = a.v_scale[(size_t)pg * a.Hkv + j];
+    } else {
+      const bf16_t* vt = vp + vt_off;
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = load16(vt + (size_t)(16 * vb) * P);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use
+  if constexpr (FP8) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) kraw[t][h][cb] = fp8x8_to_bf16x8(k8[t][h][cb]);
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = fp8x8_to_bf16x8(v8[t][vb]);
+    }
+  }
 
   // ---- S^T = K q^T ----
   f32x4_t s[TPW][2];
@@ -400,13 +438,15 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
   float z[TPW][8];
   float m = NEG_INF;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t)
+  for (int t = 0; t < TPW; ++t) {
+    const float sc = FP8 ? a.scale * ksc[t] : a.scale;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = s[t][e >> 2][e & 3] * a.scale;
+      const float v = s[t][e >> 2][e & 3] * sc;
       z[t][e] = ((vmask[t] >> e) & 1) && r16 < G ? v : NEG_INF;
       m = fmaxf(m, z[t][e]);
     }
+  }
   m = fmaxf(m, xor16_f32(m));
   m = fmaxf(m, xor32_f32(m));
   float l = 0.0f;
@@ -418,10 +458,16 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
     float p[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      // P enters the MFMA as bf16: normalize by the sum of the rounded values, so the weights
-      // applied to V sum to one exactly
-      p[e] = z[t][e] == NEG_INF ? 0.0f : round_to_elem<bf16_t>(__expf(z[t][e] - m));
-      l += p[e];
+      if constexpr (FP8) {
+        const float pf = z[t][e] == NEG_INF ? 0.0f : __expf(z[t][e] - m);
+        l += round_to_elem<bf16_t>(pf);
+        p[e] = round_to_elem<bf16_t>(pf * vsc[t]);
+      } else {
+        // P enters the MFMA as bf16: normalize by the sum of the rounded values, so the weights
+        // applied to V sum to one exactly
+        p[e] = z[t][e] == NEG_INF ? 0.0f : round_to_elem<bf16_t>(__expf(z[t][e] - m));
+        l += p[e];
+      }
     }
     const bf16x8_t pa = as_bf16x8(pack_bf16x8(p));
     const bool partial = vmask[t] != 0xff;  // zero invalid slots (0 * NaN poison is NaN)

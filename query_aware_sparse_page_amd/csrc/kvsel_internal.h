@@ -9,7 +9,7 @@ namespace kvsel {
 
 // Flattened, validated copy of a kvsel_paged_kv descriptor.
 struct LaunchKV {
-  int dtype;  // 0 = f32, 1 = bf16
+  int dtype;  // 0 = f32, 1 = bf16, 2 = fp8 E4M3 pools (q, summaries and outputs bf16)
   int B, Hq, Hkv, G, D, P, log2P, Npp;
   int maxp;  // page-table row width: the stride of the table, summaries and score rows
   int maxn;  // live pages at most (<= maxp): grids, key counts and the page bound of a sequence
@@ -17,6 +17,8 @@ struct LaunchKV {
   const void* v_pool;
   const int32_t* page_table;
   const int32_t* seq_lens;
+  const float* k_scale;  // fp8 pools: [Npp][Hkv] per-tile scales (else null)
+  const float* v_scale;
 };
 
 // Rotary table arguments passed to kernels by value; page_row == nullptr means "no rotation".
@@ -105,6 +107,10 @@ struct FreePages {
 hipError_t launch_append(const LaunchKV& kv, const void* k_new, const void* v_new, void* summ,
                          int32_t* seq_lens_out, const FreePages& free_pages, uint32_t* flags,
                          hipStream_t stream);
+
+// fp8 quantization of every (physical page, KV head) tile of K (and of V when v_codes != null).
+hipError_t launch_quantize(const LaunchKV& src, uint8_t* k_codes, float* k_scale, uint8_t* v_codes,
+                           float* v_scale, hipStream_t stream);
 
 // Device-side contract check; ORs KVSEL_CHECK_* bits into *flags.
 hipError_t launch_check_inputs(const LaunchKV& kv, const int32_t* sel_idx, const int32_t* sel_cnt,

@@ -5,6 +5,7 @@
 #pragma once
 
 #include "kvsel_device.h"
+#include "kvsel_fp8.h"
 #include "kvsel_internal.h"
 
 namespace kvsel {
@@ -23,6 +24,7 @@ struct SelectArgs {
   int32_t* sel_idx;
   int32_t* sel_cnt;
   ReuseArgs reuse;
+  const float* k_scale;  // fp8 pools: [Npp][Hkv] tile scales (the tail refresh)
 };
 
 // Min / max of the valid rows (1 <= valid; more than P means the whole page) of one (page, KV
@@ -76,6 +78,20 @@ __device__ __forceinline__ void tile_minmax(const T* tile, int valid, int P, int
   }
 }
 
+// The tail refresh's rebuild of the (physical page pt, KV head j) tile's summary by one wave: the
+// min / max of its valid rows, rotated first when the rotary gather is on (f32 / bf16 pools), or
+// scaled and rounded outward to bf16 (fp8 pools).
+template <typename T, int D, bool FP8>
+__device__ __forceinline__ void refresh_tile(const SelectArgs& a, int pt, int j, int valid,
+                                             int lane, float* lo, float* hi) {
+  const size_t t = (size_t)pt * a.Hkv + j;
+  if constexpr (FP8)
+    tile_minmax_fp8<D>((const uint8_t*)a.k_pool + t * a.P * D, valid, a.P, lane, a.k_scale[t], lo,
+                       hi);
+  else
+    tile_minmax<T, D>((const T*)a.k_pool + t * a.P * D, valid, a.P, lane, pt, a.rope, lo, hi);
+}
+
 // Scores of chunk `chunk` (WAVES * U * 64 / LPR consecutive pages) of list (sequence b, KV head
 // j), by one block of WAVES waves: LPR lanes read a page's lo and hi rows as 16-byte slices
 // (sequence-major summaries: one contiguous run per wave and unroll step), multiply by the group's
@@ -84,7 +100,7 @@ __device__ __forceinline__ void tile_minmax(const T* tile, int valid, int P, int
 // lane group scores U pages (U > 1 for wide tables: fewer blocks, more loads in flight per lane).
 // With the tail refresh on, the wave holding the sequence's last page first rebuilds that page's
 // summary from the key pool, writes it, and scores it from the fresh values.
-template <typename T, int D, int G, int WAVES, int U = 1>
+template <typename T, int D, int G, int WAVES, int U = 1, bool FP8 = false>
 __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, int chunk) {
   using M = row_map<T, D>;
   constexpr int VEC = M::VEC, LPR = M::LPR;
@@ -141,8 +157,7 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
       pt = u == ut ? x : pt;
     }
     pt = min(max(pt, 0), a.Npp - 1);
-    tile_minmax<T, D>((const T*)a.k_pool + ((size_t)pt * a.Hkv + j) * P * D, L - nt * P, P, lane,
-                      pt, a.rope, flo, fhi);
+    refresh_tile<T, D, FP8>(a, pt, j, L - nt * P, lane, flo, fhi);
     if (lane < LPR) {
       T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;
       store16(out + c0, pack<T>(flo));

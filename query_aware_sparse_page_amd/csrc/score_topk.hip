@@ -160,10 +160,10 @@ __device__ void block_topk(const float* __restrict__ sc, const float* first, int
   }
 }
 
-template <typename T, int D, int G, int U>
+template <typename T, int D, int G, int U, bool FP8>
 __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
   // grid (Hkv, B, chunks): the indices need no division; KV heads vary fastest
-  score_block<T, D, G, SEL_WAVES, U>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  score_block<T, D, G, SEL_WAVES, U, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // block_topk_regs writing the ascending list to out (and used, when non-null), padded with -1.
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectArgs a) {
 constexpr int FUSED_THREADS = 1024;
 constexpr int FUSED_MAX_PAGES = 2048;
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool FP8>
 __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs a) {
   using M = row_map<T, D>;
   constexpr int VEC = M::VEC, LPR = M::LPR;
@@ -316,8 +316,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
     const int nt = N - 1;
     const int pt = min(max(a.page_table[(size_t)b * a.maxp + nt], 0), a.Npp - 1);
     float lo[VEC], hi[VEC];
-    tile_minmax<T, D>((const T*)a.k_pool + ((size_t)pt * a.Hkv + j) * P * D, L - nt * P, P, lane,
-                      pt, a.rope, lo, hi);
+    refresh_tile<T, D, FP8>(a, pt, j, L - nt * P, lane, lo, hi);
     if (lane < LPR) {
       T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;
       store16(out + c0, pack<T>(lo));
@@ -400,7 +399,7 @@ int select_blocks_per_list(const LaunchKV& kv) {
   return (kv.maxn + ppb - 1) / ppb;
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool FP8>
 static hipError_t launch_select_t(const SelectArgs& a, hipStream_t stream) {
   // One block per list reads a whole list's summaries through one CU, so the one-launch form
   // pays only when there are enough lists to spread over the chip (measured on the bf16 path:
@@ -408,16 +407,16 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t stream) {
   // to 1024 pages take 15.8 us against 18.6 us).
   if constexpr (G <= 4) {  // larger groups would spill at 1024 threads
     if (!a.scores_only && a.nlists >= SELECT_ONE_LAUNCH_MIN_LISTS && a.maxn <= FUSED_MAX_PAGES) {
-      hipLaunchKernelGGL((select_fused_kernel<T, D, G>), dim3(a.Hkv, a.nlists / a.Hkv),
+      hipLaunchKernelGGL((select_fused_kernel<T, D, G, FP8>), dim3(a.Hkv, a.nlists / a.Hkv),
                          dim3(FUSED_THREADS), 0, stream, a);
       return hipGetLastError();
     }
   }
   const dim3 sgrid(a.Hkv, a.nlists / a.Hkv, a.nchunks);
   switch (score_unroll(a.maxn)) {
-    case 1: hipLaunchKernelGGL((score_kernel<T, D, G, 1>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((score_kernel<T, D, G, 2>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
-    default: hipLaunchKernelGGL((score_kernel<T, D, G, 4>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((score_kernel<T, D, G, 1, FP8>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((score_kernel<T, D, G, 2, FP8>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
+    default: hipLaunchKernelGGL((score_kernel<T, D, G, 4, FP8>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -431,17 +430,22 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FP8 = false>
 static hipError_t launch_select_g(int G, const SelectArgs& a, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_select_t<T, D, 1>(a, stream);
-    case 2: return launch_select_t<T, D, 2>(a, stream);
-    case 4: return launch_select_t<T, D, 4>(a, stream);
-    default: return launch_select_t<T, D, 8>(a, stream);
+    case 1: return launch_select_t<T, D, 1, FP8>(a, stream);
+    case 2: return launch_select_t<T, D, 2, FP8>(a, stream);
+    case 4: return launch_select_t<T, D, 4, FP8>(a, stream);
+    default: return launch_select_t<T, D, 8, FP8>(a, stream);
   }
 }
 
+// fp8 pools score bf16 summaries with a bf16 query; only the tail refresh reads the codes.
 static hipError_t launch_select(const SelectArgs& a, const LaunchKV& kv, hipStream_t stream) {
+  if (kv.dtype == 2) {
+    if (kv.D == 64) return launch_select_g<bf16_t, 64, true>(kv.G, a, stream);
+    return launch_select_g<bf16_t, 128, true>(kv.G, a, stream);
+  }
   if (kv.dtype == 0) {
     if (kv.D == 64) return launch_select_g<float, 64>(kv.G, a, stream);
     return launch_select_g<float, 128>(kv.G, a, stream);
@@ -475,6 +479,7 @@ SelectArgs select_args(const LaunchKV& kv, const RopeArgs& rope, void* summ, con
   a.sel_cnt = sel_cnt;
   a.reuse = reuse;
   a.scores_only = 0;
+  a.k_scale = kv.k_scale;
   return a;
 }
 

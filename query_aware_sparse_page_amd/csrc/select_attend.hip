@@ -26,6 +26,7 @@ static int fused_keys_per_thread(const LaunchKV& kv) {
 }
 
 bool fused_select_supported(const LaunchKV& kv, int k) {
+  if (kv.dtype == 2) return false;  // fp8 pools: the separate launches
   return fused_keys_per_thread(kv) > 0 && attention_pages_per_split(kv, k, 0) == FUSED_PPS;
 }
 

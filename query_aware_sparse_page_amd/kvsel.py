@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libkvsel.so")
 
 KVSEL_F32 = 0
 KVSEL_BF16 = 1
+KVSEL_FP8_E4M3 = 2
 KVSEL_OP_SCORE_TOPK = 1
 KVSEL_OP_ATTENTION = 2
 KVSEL_OP_SELECT_ATTEND = 3
@@ -45,7 +46,7 @@ class PagedKVDesc(ctypes.Structure):
         ("dtype", c_i32), ("batch", c_i32), ("num_q_heads", c_i32), ("num_kv_heads", c_i32),
         ("head_dim", c_i32), ("page_size", c_i32), ("num_phys_pages", c_i32),
         ("max_pages_per_seq", c_i32), ("k_pool", c_vp), ("v_pool", c_vp), ("page_table", c_vp),
-        ("seq_lens", c_vp), ("max_seq_len", c_i32),
+        ("seq_lens", c_vp), ("max_seq_len", c_i32), ("k_scale", c_vp), ("v_scale", c_vp),
     ]
 
 
@@ -85,6 +86,7 @@ EXPORTS = {
                                        c_vp, c_i32, c_i32, ctypes.c_float,
                                        ctypes.POINTER(ReuseDesc), c_vp, c_vp, c_vp, c_vp, c_vp,
                                        ctypes.c_size_t, c_vp]),
+    "kvsel_quantize_pages": (c_i32, [ctypes.POINTER(PagedKVDesc), c_vp, c_vp, c_vp, c_vp, c_vp]),
     "kvsel_append_kv": (c_i32, [ctypes.POINTER(PagedKVDesc), c_vp, c_vp, c_vp, c_vp,
                                 ctypes.POINTER(FreePagesDesc), c_vp, c_vp]),
     "kvsel_check_inputs": (c_i32, [ctypes.POINTER(PagedKVDesc), c_vp, c_vp, c_i32, c_vp, c_vp]),
@@ -96,7 +98,7 @@ EXPORTS = {
 _lib = None
 
 
-ABI_VERSION = 2  # KVSEL_ABI_VERSION of include/kvsel.h
+ABI_VERSION = 3  # KVSEL_ABI_VERSION of include/kvsel.h
 
 
 def lib() -> ctypes.CDLL:
@@ -146,7 +148,7 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
 
 
 def _check_summ(kv: "PagedKV", summ: torch.Tensor) -> None:
-    _dev(summ, "summ", kv.k_pool.dtype)
+    _dev(summ, "summ", kv.act_dtype)
     shape = (kv.batch, kv.num_kv_heads, int(kv.page_table.shape[1]), 2, kv.head_dim)
     if tuple(summ.shape) != shape:
         raise ValueError(f"summ must be {shape} (sequence-major), got {tuple(summ.shape)}")
@@ -157,6 +159,8 @@ def _elem_code(dtype: torch.dtype) -> int:
         return KVSEL_F32
     if dtype == torch.bfloat16:
         return KVSEL_BF16
+    if dtype == torch.uint8:
+        return KVSEL_FP8_E4M3
     raise ValueError(f"unsupported element type {dtype}")
 
 
@@ -179,11 +183,24 @@ class PagedKV:
     seq_lens: torch.Tensor
     num_q_heads: int
     max_seq_len: int = 0
+    k_scale: Optional[torch.Tensor] = None  # fp8 pools (uint8 codes): [Npp][Hkv] fp32
+    v_scale: Optional[torch.Tensor] = None
+
+    @property
+    def is_fp8(self) -> bool:
+        return self.k_pool.dtype == torch.uint8
+
+    @property
+    def act_dtype(self) -> torch.dtype:
+        """Element type of queries, summaries and outputs (bf16 for an fp8 cache)."""
+        return torch.bfloat16 if self.is_fp8 else self.k_pool.dtype
 
     def desc(self) -> PagedKVDesc:
         _dev(self.k_pool, "k_pool")
         if self.v_pool is not None:
             _dev(self.v_pool, "v_pool", self.k_pool.dtype)
+            if self.is_fp8 and self.v_scale is None:
+                raise ValueError("an fp8 value pool needs v_scale")
             Npp, Hkv, P, D = self.k_pool.shape
             if tuple(self.v_pool.shape) != (Npp, Hkv, D, P):
                 raise ValueError(f"v_pool must be [Npp][Hkv][D][P] = {(Npp, Hkv, D, P)}, got "
@@ -191,12 +208,23 @@ class PagedKV:
         _dev(self.page_table, "page_table", torch.int32)
         _dev(self.seq_lens, "seq_lens", torch.int32)
         Npp, Hkv, P, D = self.k_pool.shape
+        scales = [None, None]
+        if self.is_fp8:
+            for i, (t, name) in enumerate(((self.k_scale, "k_scale"), (self.v_scale, "v_scale"))):
+                if t is None:
+                    continue
+                _dev(t, name, torch.float32)
+                if tuple(t.shape) != (Npp, Hkv):
+                    raise ValueError(f"{name} must be [Npp][Hkv] = {(Npp, Hkv)}")
+                scales[i] = t.data_ptr()
+            if scales[0] is None:
+                raise ValueError("an fp8 key pool needs k_scale")
         B, maxp = self.page_table.shape
         return PagedKVDesc(_elem_code(self.k_pool.dtype), B, self.num_q_heads, Hkv, D, P, Npp, maxp,
                            self.k_pool.data_ptr(),
                            self.v_pool.data_ptr() if self.v_pool is not None else None,
                            self.page_table.data_ptr(), self.seq_lens.data_ptr(),
-                           int(self.max_seq_len))
+                           int(self.max_seq_len), scales[0], scales[1])
 
     @property
     def batch(self) -> int:
@@ -261,8 +289,8 @@ def build_summaries(kv: PagedKV, rope: Optional[Rope] = None, tail_only: bool = 
     _, Hkv, _, D = kv.k_pool.shape
     shape = (kv.batch, Hkv, int(kv.page_table.shape[1]), 2, D)
     if out is None:
-        out = torch.empty(shape, dtype=kv.k_pool.dtype, device=kv.device)
-    _dev(out, "summ", kv.k_pool.dtype)
+        out = torch.empty(shape, dtype=kv.act_dtype, device=kv.device)
+    _dev(out, "summ", kv.act_dtype)
     if tuple(out.shape) != shape:
         raise ValueError(f"summ must be {shape}, got {tuple(out.shape)}")
     _check(lib().kvsel_build_summaries(ctypes.byref(d), _rope_ptr(rope), int(bool(tail_only)),
@@ -302,7 +330,7 @@ def score_topk(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, *,
     B, Hkv = kv.batch, kv.num_kv_heads
     dev = kv.device
     _check_summ(kv, summ)
-    _dev(q, "q", kv.k_pool.dtype)
+    _dev(q, "q", kv.act_dtype)
     if sel_idx is None:
         sel_idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
     if sel_cnt is None:
@@ -316,7 +344,7 @@ def score_topk(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, *,
         used_cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
         corrected = torch.empty((B, Hkv), dtype=torch.uint8, device=dev)
         sim = torch.empty((B, Hkv), dtype=torch.float64, device=dev)
-        _dev(reuse.q_prev, "q_prev", kv.k_pool.dtype)
+        _dev(reuse.q_prev, "q_prev", kv.act_dtype)
         _dev(reuse.prev_idx, "prev_idx", torch.int32)
         _dev(reuse.prev_cnt, "prev_cnt", torch.int32)
         rd = ReuseDesc(reuse.q_prev.data_ptr(), reuse.prev_idx.data_ptr(), reuse.prev_cnt.data_ptr(),
@@ -346,7 +374,7 @@ def sparse_decode_attn(kv: PagedKV, q: torch.Tensor, sel_idx: torch.Tensor, sel_
     """Decode attention over the selected pages. Returns (out [B][Hq][D], lse fp32 [B][Hq])."""
     d = kv.desc()
     dev = kv.device
-    _dev(q, "q", kv.k_pool.dtype)
+    _dev(q, "q", kv.act_dtype)
     _dev(sel_idx, "sel_idx", torch.int32)
     _dev(sel_cnt, "sel_cnt", torch.int32)
     k = int(sel_idx.shape[-1]) if k is None else k
@@ -376,7 +404,7 @@ def select_attend(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, *,
     B, Hkv = kv.batch, kv.num_kv_heads
     dev = kv.device
     _check_summ(kv, summ)
-    _dev(q, "q", kv.k_pool.dtype)
+    _dev(q, "q", kv.act_dtype)
     if sel_idx is None:
         sel_idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
     if sel_cnt is None:
@@ -484,6 +512,26 @@ def append_kv(kv: PagedKV, k_new: torch.Tensor, v_new: torch.Tensor,
     return seq_lens_out
 
 
+def quantize_pages(kv: PagedKV, values: bool = True) -> PagedKV:
+    """The cache with its pages quantized to fp8 (uint8 E4M3 codes, one fp32 scale per (physical
+    page, KV head) tile of K and of V), sharing kv's page table and lengths."""
+    d = kv.desc()
+    if kv.is_fp8:
+        raise ValueError("the cache is already fp8")
+    dev = kv.device
+    Npp, Hkv = kv.k_pool.shape[:2]
+    k_codes = torch.empty(kv.k_pool.shape, dtype=torch.uint8, device=dev)
+    k_scale = torch.empty((Npp, Hkv), dtype=torch.float32, device=dev)
+    v_codes = v_scale = None
+    if values and kv.v_pool is not None:
+        v_codes = torch.empty(kv.v_pool.shape, dtype=torch.uint8, device=dev)
+        v_scale = torch.empty((Npp, Hkv), dtype=torch.float32, device=dev)
+    _check(lib().kvsel_quantize_pages(ctypes.byref(d), _ptr(k_codes), _ptr(k_scale), _ptr(v_codes),
+                                      _ptr(v_scale), _stream(dev)))
+    return PagedKV(k_codes, v_codes, kv.page_table, kv.seq_lens, kv.num_q_heads, kv.max_seq_len,
+                   k_scale, v_scale)
+
+
 def check_inputs(kv: PagedKV, sel_idx: Optional[torch.Tensor] = None,
                  sel_cnt: Optional[torch.Tensor] = None, k: Optional[int] = None,
                  flags: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -515,8 +563,8 @@ def speculative_step(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, r
     B, Hkv = kv.batch, kv.num_kv_heads
     dev = kv.device
     _check_summ(kv, summ)
-    _dev(q, "q", kv.k_pool.dtype)
-    _dev(reuse.q_prev, "q_prev", kv.k_pool.dtype)
+    _dev(q, "q", kv.act_dtype)
+    _dev(reuse.q_prev, "q_prev", kv.act_dtype)
     _dev(reuse.prev_idx, "prev_idx", torch.int32)
     _dev(reuse.prev_cnt, "prev_cnt", torch.int32)
     if sel_idx is None:

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(K):
 
 def test_version_and_status_strings(K):
     lib = K.lib()
-    assert lib.kvsel_abi_version() == K.ABI_VERSION == 2
+    assert lib.kvsel_abi_version() == K.ABI_VERSION == 3
     for code, tag in [(0, "KVSEL_OK"), (1, "INVALID_ARGUMENT"), (2, "UNSUPPORTED"),
                       (3, "WORKSPACE"), (4, "DEVICE"), (5, "LAUNCH"), (99, "UNKNOWN")]:
         assert tag in lib.kvsel_status_str(code).decode()
@@ -52,7 +52,7 @@ def _desc(K, **kw):
     base = dict(dtype=K.KVSEL_BF16, batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128,
                 page_size=32, num_phys_pages=1024, max_pages_per_seq=1024,
                 k_pool=0x1000, v_pool=0x2000, page_table=0x3000, seq_lens=0x4000,
-                max_seq_len=0)
+                max_seq_len=0, k_scale=None, v_scale=None)
     base.update(kw)
     return K.PagedKVDesc(*[base[f] for f, _ in K.PagedKVDesc._fields_])
 
@@ -84,6 +84,7 @@ def test_workspace_sizes(K):
     ("batch", 65536, 2),             # beyond the launch-grid limits
     ("max_pages_per_seq", (1 << 20) + 1, 2),
     ("max_seq_len", -1, 1),
+    ("dtype", 2, 1),                 # fp8 without k_scale
 ])
 def test_descriptor_validation(K, field, value, status):
     lib = K.lib()
@@ -165,3 +166,24 @@ def test_append_validation(K):
     for fp in (K.FreePagesDesc(None, 0x6000, 4), K.FreePagesDesc(0x6000, None, 4),
                K.FreePagesDesc(0x6000, 0x7000, 0)):
         assert ap(ctypes.byref(d), p, p, None, p, ctypes.byref(fp), None, None) == 1
+
+
+def test_fp8_validation(K):
+    """fp8 caches: scales required, no rotary argument, no append or rotary shift; the quantizer
+    takes an f32 / bf16 source and needs its outputs."""
+    lib = K.lib()
+    p = ctypes.c_void_p(0x5000)
+    f8 = _desc(K, dtype=K.KVSEL_FP8_E4M3, k_scale=0x8000, v_scale=0x9000)
+    no_v = _desc(K, dtype=K.KVSEL_FP8_E4M3, k_scale=0x8000)
+    rope = K.RopeDesc(0x10, 0x20, 0x30, 4, 0)
+    # attention needs the value scales
+    assert lib.kvsel_sparse_decode_attn(ctypes.byref(no_v), None, p, p, p, 64, 0.1, 0, p, None, p,
+                                        1 << 30, None) == 1
+    assert lib.kvsel_build_summaries(ctypes.byref(f8), ctypes.byref(rope), 0, p, None) == 2
+    assert lib.kvsel_rope_shift(ctypes.byref(f8), ctypes.byref(rope), p, None) == 2
+    assert lib.kvsel_append_kv(ctypes.byref(f8), p, p, None, p, None, None, None) == 2
+    q = lib.kvsel_quantize_pages
+    assert q(ctypes.byref(f8), p, p, p, p, None) == 2          # source already fp8
+    assert q(ctypes.byref(_desc(K)), None, p, None, None, None) == 1
+    assert q(ctypes.byref(_desc(K)), p, p, p, None, None) == 1  # v codes without v scales
+    assert q(ctypes.byref(_desc(K, v_pool=None)), p, p, p, p, None) == 1
