@@ -47,8 +47,10 @@ METRIC = "sparse decode-attn µs/step and achieved HBM GB/s (% of peak) at 32K/1
 class Layer:
     """One copy of the cache (its own HBM addresses) with preallocated outputs/workspaces."""
 
-    def __init__(self, w, dev, k_pool, v_pool, page_table, seq_lens):
+    def __init__(self, w, dev, k_pool, v_pool, page_table, seq_lens, fp8=False):
         self.kv = K.PagedKV(k_pool, v_pool, page_table, seq_lens, w.Hq)
+        if fp8:  # E4M3 pages with per-tile scales, quantized on the device
+            self.kv = K.quantize_pages(self.kv)
         self.q = w.q.to(dev)
         self.k = w.k
         self.summ = K.build_summaries(self.kv)
@@ -85,16 +87,16 @@ class Layer:
         self.attend()
 
 
-def make_layers(w, dev, n):
+def make_layers(w, dev, n, fp8=False):
     """n copies of the cache at distinct HBM addresses, used in turn like a model's layers: each
     has its own K / V pools, summaries, query and outputs; the page table and sequence lengths
     are shared by all, as a serving engine's block table is shared by every layer."""
     k0 = w.k_pool.to(dev)
     v0 = K.device_v_layout(w.v_pool.to(dev))
     table, lens = w.page_table.to(dev), w.seq_lens.to(dev)
-    layers = [Layer(w, dev, k0, v0, table, lens)]
+    layers = [Layer(w, dev, k0, v0, table, lens, fp8)]
     for _ in range(n - 1):
-        layers.append(Layer(w, dev, k0.clone(), v0.clone(), table, lens))
+        layers.append(Layer(w, dev, k0.clone(), v0.clone(), table, lens, fp8))
     torch.cuda.synchronize()
     return layers
 
@@ -161,8 +163,12 @@ def time_calls(layers, fn, launches):
 
 
 def attention_bytes(w, lay):
+    """K+V bytes of the selected pages' valid tokens; fp8 pages add their two 4-byte scales."""
     sel = lay.sel.cpu().numpy()
     cnt = lay.cnt.cpu().numpy()
+    if lay.kv.is_fp8:
+        return selected_kv_bytes(w.seq_lens.tolist(), sel, cnt, w.Hkv, w.P, w.D, 1) + \
+            8 * int(cnt.sum())
     esize = 4 if w.dtype == "f32" else 2
     return selected_kv_bytes(w.seq_lens.tolist(), sel, cnt, w.Hkv, w.P, w.D, esize)
 
@@ -172,15 +178,15 @@ def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def measure(name, dev, steps, warmup, n_layers):
+def measure(name, dev, steps, warmup, n_layers, fp8=False):
     w = W.make(name)
-    layers = make_layers(w, dev, n_layers)
+    layers = make_layers(w, dev, n_layers, fp8)
     us_step, n = time_graph(layers, steps, warmup)
     us_two, _ = time_graph(layers, steps, warmup, Layer.step_two_calls)
     n_calls = max(len(layers), min(steps, 512) // len(layers) * len(layers))
     attn_mean = time_calls(layers, Layer.attend, n_calls)
     sel_mean = time_calls(layers, Layer.select, n_calls)
-    esize = 4 if w.dtype == "f32" else 2
+    esize = 1 if fp8 else 4 if w.dtype == "f32" else 2
     for lay in layers:  # the tiles each layer's selection names, at that layer's addresses
         lay.probe_addr = K.tile_addresses(lay.kv, lay.sel, lay.cnt, w.page_table)
         lay.probe_chunk = w.P * w.D * esize
@@ -188,7 +194,7 @@ def measure(name, dev, steps, warmup, n_layers):
     probe_us = time_calls(layers, Layer.probe, n_calls)
     probe_bytes = int(layers[0].probe_addr.numel()) * w.P * w.D * esize
     abytes = attention_bytes(w, layers[0])
-    sbytes = summary_bytes(w.seq_lens.tolist(), w.Hkv, w.P, w.D, esize)
+    sbytes = summary_bytes(w.seq_lens.tolist(), w.Hkv, w.P, w.D, 2 if fp8 else esize)
     return dict(w=w, layers=layers, us_step=us_step, us_two_calls=us_two, steps=n, attn_us=attn_mean,
                 select_us=sel_mean, attn_bytes=abytes, summary_bytes=sbytes, probe_us=probe_us,
                 probe_bytes=probe_bytes, calls_timed=n_calls)
@@ -589,13 +595,17 @@ def main():
     progress(f"{w.name}: step {result['value']} us, attention call {m['attn_us']:.3f} us")
     # the 128K case of the metric, and the batched case whose 64 MiB per step is where bandwidth
     # rather than latency sets the time
-    for name, n_layers in (("qwen4b_128k", max(2, args.layers // 2)),
-                           ("ragged_batch", max(2, args.layers // 4))):
-        if args.no_secondary or name == args.workload:
+    # and both again with fp8 (E4M3) pages: half the bytes of the selected K/V
+    for name, n_layers, fp8 in (("qwen4b_128k", max(2, args.layers // 2), False),
+                                ("ragged_batch", max(2, args.layers // 4), False),
+                                (args.workload, args.layers, True),
+                                ("ragged_batch", max(2, args.layers // 4), True)):
+        if args.no_secondary or (name == args.workload and not fp8):
             continue
-        s = measure(name, dev, args.steps, args.warmup, n_layers)
+        s = measure(name, dev, args.steps, args.warmup, n_layers, fp8)
         sach = s["attn_bytes"] / (s["attn_us"] * 1e-6) / 1e9
-        result.setdefault("secondary", {})[name] = {
+        key = name + ("_fp8" if fp8 else "")
+        result.setdefault("secondary", {})[key] = {
             "us_per_step": round(s["us_step"], 3),
             "two_call_us_per_step": round(s["us_two_calls"], 3), "attn_us": round(s["attn_us"], 3),
             "attn_GBps": round(sach, 1), "attn_frac": round(sach / HBM_PEAK_GBPS, 4),
@@ -603,7 +613,9 @@ def main():
             "layers_rotated": n_layers,
             "gather_probe": {"avg_us": round(s["probe_us"], 3),
                              "GBps": round(s["probe_bytes"] / (s["probe_us"] * 1e-6) / 1e9, 1)}}
-        progress(f"{name}: step {s['us_step']:.3f} us, attention call {s['attn_us']:.3f} us")
+        if fp8:
+            result["secondary"][key]["pages"] = "fp8 E4M3 K/V, per-tile fp32 scales, bf16 summaries"
+        progress(f"{key}: step {s['us_step']:.3f} us, attention call {s['attn_us']:.3f} us")
         del s
         torch.cuda.empty_cache()
     if not args.no_secondary:

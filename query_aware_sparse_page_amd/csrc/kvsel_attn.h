@@ -295,7 +295,7 @@ __device__ __forceinline__ void finish_block(const AttnArgs& a, int G, int list,
 // P V as bf16(p * v_scale) while l adds bf16(p).
 template <int D, int P, int WAVES, int TPW, bool ROPE, int SEL_C = 0, bool FP8 = false>
 __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j, int b, int split) {
-  static_assert(!(FP8 && (ROPE || SEL_C > 0)), "fp8 pools take the plain split launch");
+  static_assert(!(FP8 && ROPE), "fp8 pools take no rotary gather");
   constexpr int TT = 32;       // tokens per tile
   constexpr int CB = D / 32;   // 32-channel blocks of q K^T
   constexpr int VB = D / 16;   // 16-channel blocks of P V
@@ -663,8 +663,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int FUSED_PPS = 4;
 
 template <typename T, int P>
-struct FusedShape {
-  static constexpr int WAVES = (sizeof(T) == 2 && P == 16) ? 2 : 4;
+struct FusedShape {  // T = fp8_t: the bf16 shape (fp8 pages are decoded into the bf16 body)
+  static constexpr int WAVES = (sizeof(T) <= 2 && P == 16) ? 2 : 4;
   static constexpr int TPW = (sizeof(T) == 4 && P == 32) ? 2 : 1;
 };
 

@@ -13,6 +13,11 @@ __global__ __launch_bounds__(WAVES * 64) void fused_bf16_kernel(AttnArgs a, int 
   attn_bf16_block<D, P, WAVES, TPW, ROPE, C>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
+template <int D, int P, int WAVES, int TPW, int C>
+__global__ __launch_bounds__(WAVES * 64) void fused_fp8_kernel(AttnArgs a, int G) {
+  attn_bf16_block<D, P, WAVES, TPW, false, C, true>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
 template <int D, int P, int WAVES, int TPW, bool ROPE, int C>
 __global__ __launch_bounds__(WAVES * 64) void fused_f32_kernel(AttnArgs a, int G) {
   attn_f32_block<D, P, WAVES, TPW, ROPE, C>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
@@ -20,13 +25,12 @@ __global__ __launch_bounds__(WAVES * 64) void fused_f32_kernel(AttnArgs a, int G
 
 // Score keys per thread of the fused select (the block holds the whole table row in registers).
 static int fused_keys_per_thread(const LaunchKV& kv) {
-  const int nt = (kv.dtype == 1 && kv.P == 16) ? 128 : 256;
+  const int nt = (kv.dtype != 0 && kv.P == 16) ? 128 : 256;  // FusedShape's threads
   const int c = (kv.maxn + nt - 1) / nt;
   return c <= 1 ? 1 : c <= 4 ? 4 : c <= 8 ? 8 : c <= 16 ? 16 : c <= 32 ? 32 : 0;
 }
 
 bool fused_select_supported(const LaunchKV& kv, int k) {
-  if (kv.dtype == 2) return false;  // fp8 pools: the separate launches
   return fused_keys_per_thread(kv) > 0 && attention_pages_per_split(kv, k, 0) == FUSED_PPS;
 }
 
@@ -45,7 +49,9 @@ static void launch_fused_c(const AttnArgs& a, int G, hipStream_t stream) {
   using S = FusedShape<T, P>;
   const dim3 grid(a.Hkv, a.nlists / a.Hkv, a.nsplit);
   const dim3 block(S::WAVES * 64);
-  if constexpr (sizeof(T) == 2)
+  if constexpr (sizeof(T) == 1)
+    hipLaunchKernelGGL((fused_fp8_kernel<D, P, S::WAVES, S::TPW, C>), grid, block, 0, stream, a, G);
+  else if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((fused_bf16_kernel<D, P, S::WAVES, S::TPW, ROPE, C>), grid, block, 0, stream, a, G);
   else
     hipLaunchKernelGGL((fused_f32_kernel<D, P, S::WAVES, S::TPW, ROPE, C>), grid, block, 0, stream, a, G);
@@ -64,6 +70,11 @@ static void launch_fused_r(int c, const AttnArgs& a, int G, hipStream_t stream) 
 
 template <typename T, int D>
 static void launch_fused_p(int P, int c, const AttnArgs& a, int G, bool rope, hipStream_t stream) {
+  if constexpr (sizeof(T) == 1) {  // fp8: no rotary gather
+    if (P == 16) launch_fused_r<T, D, 16, false>(c, a, G, stream);
+    else launch_fused_r<T, D, 32, false>(c, a, G, stream);
+    return;
+  }
   if (P == 16) {
     if (rope) launch_fused_r<T, D, 16, true>(c, a, G, stream);
     else launch_fused_r<T, D, 16, false>(c, a, G, stream);
@@ -76,7 +87,10 @@ static void launch_fused_p(int P, int c, const AttnArgs& a, int G, bool rope, hi
 hipError_t launch_fused_select(const LaunchKV& kv, const AttnArgs& a, bool rope,
                                hipStream_t stream) {
   const int c = fused_keys_per_thread(kv);
-  if (kv.dtype == 0) {
+  if (kv.dtype == 2) {
+    if (kv.D == 64) launch_fused_p<fp8_t, 64>(kv.P, c, a, kv.G, false, stream);
+    else launch_fused_p<fp8_t, 128>(kv.P, c, a, kv.G, false, stream);
+  } else if (kv.dtype == 0) {
     if (kv.D == 64) launch_fused_p<float, 64>(kv.P, c, a, kv.G, rope, stream);
     else launch_fused_p<float, 128>(kv.P, c, a, kv.G, rope, stream);
   } else {

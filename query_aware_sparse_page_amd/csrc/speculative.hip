@@ -26,12 +26,13 @@
 
 namespace kvsel {
 
-template <typename T, int D, int P, bool ROPE, int G, int WAVES = FusedShape<T, P>::WAVES>
+// T: the query / summary type (bf16 for fp8 pools, FP8 set).
+template <typename T, int D, int P, bool ROPE, int G, bool FP8, int WAVES = FusedShape<T, P>::WAVES>
 __global__ __launch_bounds__(WAVES * 64) void spec_co_kernel(AttnArgs a, SelectArgs s) {
   using S = FusedShape<T, P>;
   const int j = blockIdx.x, b = blockIdx.y, z = blockIdx.z;  // grid (Hkv, B, chunks + 1 + splits)
   if (z < s.nchunks) {
-    score_block<T, D, G, S::WAVES>(s, j, b, z);
+    score_block<T, D, G, S::WAVES, 1, FP8>(s, j, b, z);
     return;
   }
   if (z == s.nchunks) {  // the list's reuse decision
@@ -46,12 +47,12 @@ __global__ __launch_bounds__(WAVES * 64) void spec_co_kernel(AttnArgs a, SelectA
     return;
   }
   if constexpr (sizeof(T) == 2)
-    attn_bf16_block<D, P, S::WAVES, S::TPW, ROPE>(a, G, j, b, z - s.nchunks - 1);
+    attn_bf16_block<D, P, S::WAVES, S::TPW, ROPE, 0, FP8>(a, G, j, b, z - s.nchunks - 1);
   else
     attn_f32_block<D, P, S::WAVES, S::TPW, ROPE>(a, G, j, b, z - s.nchunks - 1);
 }
 
-template <typename T, int D, int P, bool ROPE>
+template <typename T, int D, int P, bool ROPE, bool FP8>
 static hipError_t launch_co_r(const AttnArgs& a, SelectArgs s, int G, int prev_splits,
                               hipStream_t stream) {
   using S = FusedShape<T, P>;
@@ -60,21 +61,25 @@ static hipError_t launch_co_r(const AttnArgs& a, SelectArgs s, int G, int prev_s
   const dim3 grid(a.Hkv, a.nlists / a.Hkv, s.nchunks + 1 + prev_splits);
   const dim3 block(S::WAVES * 64);
   switch (G) {
-    case 1: hipLaunchKernelGGL((spec_co_kernel<T, D, P, ROPE, 1>), grid, block, 0, stream, a, s); break;
-    case 2: hipLaunchKernelGGL((spec_co_kernel<T, D, P, ROPE, 2>), grid, block, 0, stream, a, s); break;
-    case 4: hipLaunchKernelGGL((spec_co_kernel<T, D, P, ROPE, 4>), grid, block, 0, stream, a, s); break;
-    default: hipLaunchKernelGGL((spec_co_kernel<T, D, P, ROPE, 8>), grid, block, 0, stream, a, s); break;
+    case 1: hipLaunchKernelGGL((spec_co_kernel<T, D, P, ROPE, 1, FP8>), grid, block, 0, stream, a, s); break;
+    case 2: hipLaunchKernelGGL((spec_co_kernel<T, D, P, ROPE, 2, FP8>), grid, block, 0, stream, a, s); break;
+    case 4: hipLaunchKernelGGL((spec_co_kernel<T, D, P, ROPE, 4, FP8>), grid, block, 0, stream, a, s); break;
+    default: hipLaunchKernelGGL((spec_co_kernel<T, D, P, ROPE, 8, FP8>), grid, block, 0, stream, a, s); break;
   }
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FP8 = false>
 static hipError_t launch_co(int P, bool rope, const AttnArgs& a, const SelectArgs& s, int G,
                             int prev_splits, hipStream_t stream) {
-  if (P == 16) return rope ? launch_co_r<T, D, 16, true>(a, s, G, prev_splits, stream)
-                           : launch_co_r<T, D, 16, false>(a, s, G, prev_splits, stream);
-  return rope ? launch_co_r<T, D, 32, true>(a, s, G, prev_splits, stream)
-              : launch_co_r<T, D, 32, false>(a, s, G, prev_splits, stream);
+  if constexpr (FP8) {  // no rotary gather on fp8 pools
+    return P == 16 ? launch_co_r<T, D, 16, false, true>(a, s, G, prev_splits, stream)
+                   : launch_co_r<T, D, 32, false, true>(a, s, G, prev_splits, stream);
+  }
+  if (P == 16) return rope ? launch_co_r<T, D, 16, true, false>(a, s, G, prev_splits, stream)
+                           : launch_co_r<T, D, 16, false, false>(a, s, G, prev_splits, stream);
+  return rope ? launch_co_r<T, D, 32, true, false>(a, s, G, prev_splits, stream)
+              : launch_co_r<T, D, 32, false, false>(a, s, G, prev_splits, stream);
 }
 
 hipError_t launch_speculative_step(const LaunchKV& kv, const RopeArgs& rope, void* summ,
@@ -96,7 +101,10 @@ hipError_t launch_speculative_step(const LaunchKV& kv, const RopeArgs& rope, voi
                                   out, lse, attn_ws);
   const int prev_splits = reuse.first_step ? 0 : prev.nsplit;
   hipError_t e;
-  if (kv.dtype == 0)
+  if (kv.dtype == 2)
+    e = kv.D == 64 ? launch_co<bf16_t, 64, true>(kv.P, r, prev, s, kv.G, prev_splits, stream)
+                   : launch_co<bf16_t, 128, true>(kv.P, r, prev, s, kv.G, prev_splits, stream);
+  else if (kv.dtype == 0)
     e = kv.D == 64 ? launch_co<float, 64>(kv.P, r, prev, s, kv.G, prev_splits, stream)
                    : launch_co<float, 128>(kv.P, r, prev, s, kv.G, prev_splits, stream);
   else

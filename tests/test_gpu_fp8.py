@@ -73,7 +73,8 @@ def test_fp8_path_matches_oracle(K, case):
     assert_scores_close(scores, ref["scores"], w, exact=False)
     assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["margins"])
     err = assert_attention_close(out, lse, ref["out"], ref["lse"], "bf16")
-    # the one-call forms on an fp8 cache run the separate launches: identical outputs
+    # the one-call forms (the top-k fused into the attention launch, the speculative
+    # co-launch) give the separate calls' outputs bit for bit
     s2, c2, o2, l2 = K.select_attend(kv8, summ, q, w.k, scale=scale)
     zi = torch.zeros((w.B, w.Hkv, w.k), dtype=torch.int32, device="cuda")
     zc = torch.zeros((w.B, w.Hkv), dtype=torch.int32, device="cuda")
@@ -84,7 +85,20 @@ def test_fp8_path_matches_oracle(K, case):
                         (spec[0], sel, "spec sel"), (spec[6], out, "spec out"),
                         (spec[7], lse, "spec lse")):
         assert torch.equal(a, b_), f"{name} differs from the separate calls"
-    say(f"fp8 {case['seed']}: max abs attention error {err:.3g}")
+    # a second speculative step reusing the first's pages where the queries agree (the attention
+    # over the previous pages runs in the scoring launch) equals the serial calls bit for bit
+    gen = torch.Generator().manual_seed(case["seed"] + 50)
+    q2 = (ref["q"].float() + 0.3 * torch.randn(ref["q"].shape, generator=gen)).to(torch.bfloat16).cuda()
+    reuse = K.Reuse(q, spec[0].clone(), spec[1].clone(), 0.95)
+    s2 = K.speculative_step(kv8, summ, q2, w.k, reuse, scale=scale)
+    r2 = K.score_topk(kv8, summ, q2, w.k, reuse=reuse)
+    o2, l2 = K.sparse_decode_attn(kv8, q2, r2[2], r2[3], w.k, scale=scale)
+    torch.cuda.synchronize()
+    for a, b_, name in zip(s2, tuple(r2) + (o2, l2),
+                           ("sel", "cnt", "used", "ucnt", "corrected", "similarity", "out", "lse")):
+        assert torch.equal(a, b_), f"second speculative step: {name} differs"
+    say(f"fp8 {case['seed']}: max abs attention error {err:.3g}, "
+        f"{int((~s2[4].bool()).sum())} lists kept on their previous pages")
 
 
 def test_fp8_tail_refresh(K):
