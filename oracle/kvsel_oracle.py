@@ -33,11 +33,11 @@ Readings taken where the pages are silent (each restated at its function):
 * R9  Rotary convention: rotate-half pairs (i, i + D/2), inverse frequency theta^(-2i/D); the
       cos/sin table is fp64 libm values rounded to fp32; the rotation itself is fp32 with every
       product and sum rounded on its own (no fused multiply-add), then rounded to the cache dtype.
-* R11 A quantized cache stores OCP FP8 E4M3 codes, rounded to nearest (ties to even mantissa),
+* R12 A quantized cache stores OCP FP8 E4M3 codes, rounded to nearest (ties to even mantissa),
       saturating at 448.
-* R12 One fp32 scale per (physical page, KV head) tile of K and of V: amax / 448; a code stands
+* R13 One fp32 scale per (physical page, KV head) tile of K and of V: amax / 448; a code stands
       for decode(code) * scale, and attention runs over those values.
-* R13 Summaries of an fp8 page are bf16, rounded outward (lo down, hi up) from the extremes of
+* R14 Summaries of an fp8 page are bf16, rounded outward (lo down, hi up) from the extremes of
       the dequantized keys, so the page score stays an upper bound.
 """
 from __future__ import annotations
@@ -450,7 +450,7 @@ def rope_rotate(k_pool, cos, sin, page_row, row_step: int, dtype: str) -> np.nda
 # ----------------------------------------------------------------------------------------------
 # fp8 pages: a quantized cache ([KV-Cache wiki] "Contradictions & Updates": a quantized cache
 # holds longer contexts at a small accuracy cost; [KV Packet] section 3: compatible with KV
-# compression). The pages fix no format; readings R11-R13 below.
+# compression). The pages fix no format; readings R12-R14 below.
 # ----------------------------------------------------------------------------------------------
 
 FP8_E4M3_MAX = 448.0
@@ -471,7 +471,7 @@ def fp8_e4m3_decode(codes) -> np.ndarray:
 
 
 def fp8_e4m3_encode(x) -> np.ndarray:
-    """Reading R11: round each value to the nearest E4M3 value, ties to the code with an even
+    """Reading R12: round each value to the nearest E4M3 value, ties to the code with an even
     mantissa (last bit 0), magnitudes beyond 448 saturate to 448; the sign bit is kept (so -0.0
     is 0x80). Plainly: the nearest of the 127 non-negative finite values, by search. Returns
     uint8 codes."""
@@ -490,7 +490,7 @@ def fp8_e4m3_encode(x) -> np.ndarray:
 
 
 def quantize_pages(pool) -> Tuple[np.ndarray, np.ndarray]:
-    """Reading R12: one fp32 scale per (physical page, KV head) tile, amax / 448 (fp32 division;
+    """Reading R13: one fp32 scale per (physical page, KV head) tile, amax / 448 (fp32 division;
     1 for an all-zero tile), and every element coded as encode(fp32(x / scale)) with x the cache
     value (bf16 and fp32 values are exact in fp32; the division is fp32, correctly rounded).
     The layout of a tile's elements does not matter (amax and the coding are per element).
@@ -527,7 +527,7 @@ def _bf16_directed(x, step) -> np.ndarray:
 
 
 def page_summaries_fp8(k_codes, k_scale, page_table, seq_lens, page_size: int) -> np.ndarray:
-    """Reading R13: the summary of an fp8 page is bf16, the outward rounding of the extremes of
+    """Reading R14: the summary of an fp8 page is bf16, the outward rounding of the extremes of
     its dequantized keys: lo = the largest bf16 <= min, hi = the smallest bf16 >= max (products of
     a code's value and the fp32 scale are exact in float64). The outward rounding keeps every
     page score an upper bound of q.k over the page's keys. Valid slots only, as page_summaries.

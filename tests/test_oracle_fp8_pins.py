@@ -1,4 +1,4 @@
-"""Pins of the oracle's fp8-page functions (readings R11-R13) against things other than
+"""Pins of the oracle's fp8-page functions (readings R12-R14) against things other than
 themselves: the OCP E4M3 definition's closed forms, torch's own float8_e4m3fn conversions (an
 independent library routine), round trips, half-ulp error bounds, and the upper-bound invariant
 of the page score. Each check also gets a broken copy of the oracle function (a planted mistake)
@@ -50,7 +50,7 @@ def test_planted_decode_mistakes_are_caught(mistake):
 
 
 # ----------------------------------------------------------------------------------------------
-# encoding (R11)
+# encoding (R12)
 # ----------------------------------------------------------------------------------------------
 
 
@@ -98,7 +98,7 @@ def test_planted_encode_mistakes_are_caught(mistake):
 
 
 # ----------------------------------------------------------------------------------------------
-# page quantization (R12)
+# page quantization (R13)
 # ----------------------------------------------------------------------------------------------
 
 
@@ -153,7 +153,7 @@ def test_planted_quantize_mistakes_are_caught(mistake):
 
 
 # ----------------------------------------------------------------------------------------------
-# outward bf16 rounding and fp8 summaries (R13)
+# outward bf16 rounding and fp8 summaries (R14)
 # ----------------------------------------------------------------------------------------------
 
 
