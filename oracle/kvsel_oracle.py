@@ -39,6 +39,10 @@ Readings taken where the pages are silent (each restated at its function):
       for decode(code) * scale, and attention runs over those values.
 * R14 Summaries of an fp8 page are bf16, rounded outward (lo down, hi up) from the extremes of
       the dequantized keys, so the page score stays an upper bound.
+* R15 Composition ([KV Packet] sections 1 and 3: independently cached documents reused at new
+      positions without recomputation): a sequence may chain the pages of several documents in
+      any order; a page may hold fewer valid slots than P (a document's last page), given per
+      physical page as page_fill; positions come from the rotary page rows.
 """
 from __future__ import annotations
 
@@ -51,6 +55,7 @@ import torch
 __all__ = [
     "as_f64",
     "n_pages",
+    "valid_slots",
     "page_summaries",
     "append_tokens",
     "page_scores",
@@ -98,6 +103,16 @@ def n_pages(seq_len: int, page_size: int) -> int:
     return -(-int(seq_len) // int(page_size))
 
 
+def valid_slots(seq_len: int, n: int, page_size: int, phys_page: int, page_fill=None) -> int:
+    """Valid slots of logical page n (physical page ``phys_page``) of a sequence of ``seq_len``
+    slots: reading R5 (a partial last page) and, with ``page_fill``, reading R15 (a page of a
+    composed sequence may end early: slot s is valid only below page_fill[phys_page])."""
+    v = min(int(page_size), int(seq_len) - int(n) * int(page_size))
+    if page_fill is not None:
+        v = min(v, int(_ints(page_fill)[phys_page]))
+    return v
+
+
 def round_to_dtype(x32: np.ndarray, dtype: str) -> np.ndarray:
     """Round fp32 values to the cache dtype ("f32" or "bf16", round-to-nearest-even) and return
     them widened back to fp32 NumPy. Uses torch's conversion as a library primitive."""
@@ -111,12 +126,12 @@ def round_to_dtype(x32: np.ndarray, dtype: str) -> np.ndarray:
 # a1: per-page key summaries
 # ----------------------------------------------------------------------------------------------
 
-def page_summaries(k_pool, page_table, seq_lens, page_size: int) -> np.ndarray:
+def page_summaries(k_pool, page_table, seq_lens, page_size: int, page_fill=None) -> np.ndarray:
     """Channel-wise min and max of the keys of every referenced page, per KV head.
 
     [FreeKV] section 2.1 chooses whole KV pages with the query; the pages do not say what a page
     keeps about its keys. Reading R1/R5: keep lo = min and hi = max over the page's valid tokens,
-    for each KV head and channel.
+    for each KV head and channel (valid slots per valid_slots, with ``page_fill`` if given).
 
     Returns ``summ[Npp][Hkv][2][D]`` (index 0 = lo, 1 = hi) in float64; pages no sequence
     references stay NaN.
@@ -131,7 +146,8 @@ def page_summaries(k_pool, page_table, seq_lens, page_size: int) -> np.ndarray:
         L = int(lens[b])
         for n in range(n_pages(L, P)):
             p = int(table[b, n])
-            valid = min(P, L - n * P)
+            valid = valid_slots(L, n, P, p, page_fill)
+            assert valid >= 1, "a page holds at least one valid slot"
             toks = K[p, :, :valid, :]  # [Hkv][valid][D]
             summ[p, :, 0, :] = toks.min(axis=1)
             summ[p, :, 1, :] = toks.max(axis=1)
@@ -316,17 +332,18 @@ def speculative_choice(fresh_idx, fresh_cnt, prev_idx, prev_cnt, C, tau: float,
 # a5 + a6: attention over the selected pages
 # ----------------------------------------------------------------------------------------------
 
-def gather_tokens(pool, page_table, seq_len: int, b: int, j: int, pages, page_size: int):
+def gather_tokens(pool, page_table, seq_len: int, b: int, j: int, pages, page_size: int,
+                  page_fill=None):
     """Rows [T][D] (float64) of KV head j for the valid tokens of logical pages ``pages`` of
     sequence b, in the order given (reading R5: a partial last page contributes its valid
-    slots only)."""
+    slots only; R15: so does a page that ``page_fill`` ends early)."""
     X = pool if isinstance(pool, np.ndarray) and pool.dtype == np.float64 else as_f64(pool)
     table = _ints(page_table)
     rows = []
     for n in pages:
         n = int(n)
         p = int(table[b, n])
-        valid = min(page_size, int(seq_len) - n * page_size)
+        valid = valid_slots(seq_len, n, page_size, p, page_fill)
         rows.append(X[p, j, :valid, :])
     if not rows:
         return np.zeros((0, X.shape[-1]))
@@ -342,7 +359,7 @@ def _softmax_attend(qv: np.ndarray, Kr: np.ndarray, Vr: np.ndarray, scale: float
 
 
 def sparse_decode_attention(q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt,
-                            page_size: int, scale: float):
+                            page_size: int, scale: float, page_fill=None):
     """Decode attention of every query head over the tokens of its KV head's chosen pages.
 
     [FreeKV] section 2.1: attention runs over the retrieved pages only; [KV-Cache wiki]: one
@@ -367,8 +384,8 @@ def sparse_decode_attention(q, k_pool, v_pool, page_table, seq_lens, sel_idx, se
     for b in range(B):
         for j in range(Hkv):
             pages = sel[b, j, :cnt[b, j]]
-            Kr = gather_tokens(K, page_table, lens[b], b, j, pages, page_size)
-            Vr = gather_tokens(V, page_table, lens[b], b, j, pages, page_size)
+            Kr = gather_tokens(K, page_table, lens[b], b, j, pages, page_size, page_fill)
+            Vr = gather_tokens(V, page_table, lens[b], b, j, pages, page_size, page_fill)
             if Kr.shape[0] == 0:
                 continue
             for h in range(j * G, (j + 1) * G):
@@ -526,14 +543,16 @@ def _bf16_directed(x, step) -> np.ndarray:
     return np.ldexp(step(m * 256.0), e - 8)  # m * 2^8 has 8 integer bits; scaling is exact
 
 
-def page_summaries_fp8(k_codes, k_scale, page_table, seq_lens, page_size: int) -> np.ndarray:
+def page_summaries_fp8(k_codes, k_scale, page_table, seq_lens, page_size: int,
+                       page_fill=None) -> np.ndarray:
     """Reading R14: the summary of an fp8 page is bf16, the outward rounding of the extremes of
     its dequantized keys: lo = the largest bf16 <= min, hi = the smallest bf16 >= max (products of
     a code's value and the fp32 scale are exact in float64). The outward rounding keeps every
     page score an upper bound of q.k over the page's keys. Valid slots only, as page_summaries.
 
     Returns summ[Npp][Hkv][2][D] float64 (bf16 values); unreferenced pages stay NaN."""
-    summ = page_summaries(dequantize_pages(k_codes, k_scale), page_table, seq_lens, page_size)
+    summ = page_summaries(dequantize_pages(k_codes, k_scale), page_table, seq_lens, page_size,
+                          page_fill)
     out = np.full_like(summ, np.nan)
     done = ~np.isnan(summ[:, 0, 0, 0])
     out[done, :, 0, :] = bf16_round_down(summ[done, :, 0, :])

@@ -35,6 +35,7 @@ __all__ = [
     "ragged_batch",
     "qwen4b_128k",
     "speculative_rope",
+    "composed",
     "custom",
 ]
 
@@ -318,12 +319,76 @@ def custom(seed: int, B: int, Hq: int, Hkv: int, D: int, P: int, k: int, lens, d
     )
 
 
+def composed(seed: int = 1006, doc_lens=(3000, 517, 4099, 1, 2222, 700, 5120, 31), order=None,
+             B: int = 1, Hq: int = 32, Hkv: int = 8, D: int = 128, P: int = 32, k: int = 48,
+             dtype: str = "bf16", lead: int = 0, theta: float = 500000.0) -> Workload:
+    """Contexts composed of independently cached documents (the positional half of RAG reuse).
+
+    Document i holds doc_lens[i] tokens in pages of its own; its last page holds
+    doc_lens[i] % P valid slots when that is not 0 (``page_fill`` gives every physical page's
+    valid slots). Sequence b chains the documents' pages in ``order[b]`` (default: document order
+    for b = 0, rotated by b for later sequences, so sequences share documents in different
+    orders); its length counts slots, holes included. In sequence b the document at chain
+    position c starts at position lead + the tokens of the documents before it. Keys, values and
+    the query are N(0,1) with the usual outlier key channels; physical pages are shuffled.
+
+    extra: page_fill int32 [Npp]; page_in_doc int32 [Npp] (index of the page within its
+    document); doc_of_page int32 [Npp]; doc_start int32 [B][n_docs] (position of each document in
+    sequence b); theta (the rotary base of the positional tests).
+    """
+    rng = _rng(seed)
+    n_docs = len(doc_lens)
+    if order is None:
+        order = [[(c + b) % n_docs for c in range(n_docs)] for b in range(B)]
+    pages_of = [-(-int(L) // P) for L in doc_lens]
+    Npp = int(sum(pages_of))
+    perm = rng.permutation(Npp)
+    doc_pages, off = [], 0
+    page_fill = np.full(Npp, P, dtype=np.int32)
+    page_in_doc = np.zeros(Npp, dtype=np.int32)
+    doc_of_page = np.zeros(Npp, dtype=np.int32)
+    for i, L in enumerate(doc_lens):
+        pg = perm[off:off + pages_of[i]]
+        off += pages_of[i]
+        doc_pages.append(pg)
+        page_in_doc[pg] = np.arange(len(pg), dtype=np.int32)
+        doc_of_page[pg] = i
+        if L % P:
+            page_fill[pg[-1]] = L % P
+    width = max(sum(pages_of[i] for i in o) for o in order)
+    table = np.zeros((B, width), dtype=np.int32)
+    lens = np.zeros(B, dtype=np.int64)
+    doc_start = np.zeros((B, n_docs), dtype=np.int32)
+    for b, o in enumerate(order):
+        chain = np.concatenate([doc_pages[i] for i in o])
+        table[b, :len(chain)] = chain
+        lens[b] = (len(chain) - 1) * P + int(page_fill[chain[-1]])
+        pos = lead
+        for i in o:
+            doc_start[b, i] = pos
+            pos += int(doc_lens[i])
+    chans = _outlier_channels(rng, Hkv, D)
+    K = _normal(rng, (Npp, Hkv, P, D))
+    _apply_outliers(K, chans)
+    V = _normal(rng, (Npp, Hkv, P, D))
+    q = _normal(rng, (B, Hq, D))
+    return Workload(
+        "composed", dtype, B, Hq, Hkv, D, P, k,
+        seq_lens=torch.tensor(lens, dtype=torch.int32), page_table=torch.from_numpy(table),
+        k_pool=_to(K, dtype), v_pool=_to(V, dtype), q=_to(q, dtype),
+        extra={"page_fill": torch.from_numpy(page_fill), "page_in_doc": torch.from_numpy(page_in_doc),
+               "doc_of_page": torch.from_numpy(doc_of_page), "doc_start": torch.from_numpy(doc_start),
+               "doc_lens": list(doc_lens), "order": order, "theta": theta},
+    )
+
+
 WORKLOADS = {
     "tiny_fp32": tiny_fp32,
     "llama8b_32k": llama8b_32k,
     "ragged_batch": ragged_batch,
     "qwen4b_128k": qwen4b_128k,
     "speculative_rope": speculative_rope,
+    "composed": composed,
 }
 
 
