@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVSEL_ABI_VERSION 3
+#define KVSEL_ABI_VERSION 4
 
 typedef int32_t kvsel_status;
 #define KVSEL_OK 0
@@ -96,7 +96,17 @@ typedef struct kvsel_paged_kv {
   int32_t max_seq_len;       /* 0, or the caller's bound on every seq_lens[b] (host)  */
   const float* k_scale;      /* fp8 only: [num_phys_pages][Hkv] fp32 (else ignored)   */
   const float* v_scale;      /* fp8 only: [num_phys_pages][Hkv] fp32, with v_pool     */
+  const int32_t* page_fill;  /* [num_phys_pages] valid slots per page (1..P), or NULL  */
 } kvsel_paged_kv;
+
+/* page_fill: a sequence may chain pages that end early -- the pages of independently cached
+ * documents composed into one context ([KV Packet] sections 1 and 3: cached documents reused at
+ * new positions without recomputation; the positions come from the rotary page rows). Slot s of
+ * logical page n (physical page p) of sequence b is valid iff n * P + s < seq_lens[b] and
+ * s < page_fill[p]; seq_lens[b] counts slots, holes included. Summaries, the tail refresh and
+ * attention skip the other slots; kvsel_check_inputs reports an entry outside [1, P]
+ * (KVSEL_CHECK_PAGE_FILL). kvsel_append_kv ignores page_fill: the page it writes, a sequence's
+ * last, must be full-capacity (page_fill P). NULL: every page holds P valid slots. */
 
 /* max_seq_len: page tables are usually allocated for the longest context a sequence may reach,
  * while the lengths live on the device. A non-zero max_seq_len tells the library how many pages
@@ -328,6 +338,7 @@ kvsel_status kvsel_append_kv(const kvsel_paged_kv* kv, const void* k_new, const 
  *   KVSEL_CHECK_SEQ_LEN   if some seq_lens[b] < 0 or > the live bound (max_seq_len if non-zero,
  *                         else max_pages_per_seq * page_size);
  *   KVSEL_CHECK_PAGE_ID   if some page_table[b][n], n < N_b, is outside [0, num_phys_pages);
+ *   KVSEL_CHECK_PAGE_FILL with page_fill, if such a page's page_fill is outside [1, P];
  *   KVSEL_CHECK_SELECTION (only when sel_idx != NULL; sel_cnt and k then required) if some
  *     sel_cnt[b][j] is outside [0, min(k, N_b)] or the first sel_cnt[b][j] entries of
  *     sel_idx[b][j] are not strictly ascending page ids in [0, N_b).
@@ -338,6 +349,7 @@ kvsel_status kvsel_append_kv(const kvsel_paged_kv* kv, const void* k_new, const 
 #define KVSEL_CHECK_PAGE_ID 2u
 #define KVSEL_CHECK_SELECTION 4u
 #define KVSEL_CHECK_NO_FREE_PAGE 8u /* kvsel_append_kv only: the free-page list was empty */
+#define KVSEL_CHECK_PAGE_FILL 16u   /* some page_fill[p], p referenced, outside [1, P] */
 kvsel_status kvsel_check_inputs(const kvsel_paged_kv* kv, const int32_t* sel_idx,
                                 const int32_t* sel_cnt, int32_t k, uint32_t* flags, void* stream);
 

@@ -216,6 +216,7 @@ AttnArgs attn_args(const LaunchKV& kv, const RopeArgs& rope, const void* q, cons
   a.scale = scale;
   a.k_scale = kv.k_scale;
   a.v_scale = kv.v_scale;
+  a.page_fill = kv.page_fill;
   a.rope = rope;
   a.part_acc = nullptr;
   a.part_ml = nullptr;

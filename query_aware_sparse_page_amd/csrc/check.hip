@@ -12,7 +12,8 @@ constexpr int CHECK_THREADS = 256;
 
 __global__ __launch_bounds__(CHECK_THREADS) void check_inputs_kernel(
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int Hkv, int P,
-    int maxp, int maxn, int Npp, const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
+    int maxp, int maxn, int Npp, const int32_t* __restrict__ page_fill,
+    const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
     int k, uint32_t* flags) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -22,7 +23,11 @@ __global__ __launch_bounds__(CHECK_THREADS) void check_inputs_kernel(
   const int N = L > 0 ? (int)min(((long)L + P - 1) / P, (long)maxp) : 0;
   for (int n = tid; n < N; n += CHECK_THREADS) {
     const int p = page_table[(size_t)b * maxp + n];
-    if (p < 0 || p >= Npp) bad |= 2u;  // KVSEL_CHECK_PAGE_ID
+    if (p < 0 || p >= Npp) {
+      bad |= 2u;  // KVSEL_CHECK_PAGE_ID
+    } else if (page_fill && (page_fill[p] < 1 || page_fill[p] > P)) {
+      bad |= 16u;  // KVSEL_CHECK_PAGE_FILL
+    }
   }
   if (sel_idx) {
     const int lim = min(k, N);
@@ -43,7 +48,7 @@ __global__ __launch_bounds__(CHECK_THREADS) void check_inputs_kernel(
 hipError_t launch_check_inputs(const LaunchKV& kv, const int32_t* sel_idx, const int32_t* sel_cnt,
                                int k, uint32_t* flags, hipStream_t stream) {
   hipLaunchKernelGGL(check_inputs_kernel, dim3((unsigned)kv.B), dim3(CHECK_THREADS), 0, stream,
-                     kv.page_table, kv.seq_lens, kv.Hkv, kv.P, kv.maxp, kv.maxn, kv.Npp, sel_idx, sel_cnt,
+                     kv.page_table, kv.seq_lens, kv.Hkv, kv.P, kv.maxp, kv.maxn, kv.Npp, kv.page_fill, sel_idx, sel_cnt,
                      k, flags);
   return hipGetLastError();
 }

@@ -77,6 +77,7 @@ kvsel_status flatten(const kvsel_paged_kv* kv, int need, LaunchKV* out) {
   out->seq_lens = kv->seq_lens;
   out->k_scale = out->dtype == 2 ? kv->k_scale : nullptr;
   out->v_scale = out->dtype == 2 ? kv->v_scale : nullptr;
+  out->page_fill = kv->page_fill;
   return KVSEL_OK;
 }
 

@@ -59,6 +59,7 @@ struct AttnArgs {
   float scale;
   const float* k_scale;  // fp8 pools: [Npp][Hkv] tile scales of K and V (else null)
   const float* v_scale;
+  const int32_t* page_fill;  // [Npp] valid slots per physical page, or null (every page full)
   RopeArgs rope;
   float* part_acc;   // [nlists][nsplit][G][D]
   float2* part_ml;   // [nlists][nsplit][G]
@@ -333,6 +334,18 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
     lookup_tiles<P, TT, TPW>(a, list, b, split, w * TPW, tp);
   }
 
+  // valid slots of the tiles' pages in a composed sequence (page_fill): scalar loads beside the
+  // K / V loads, applied to the masks after every load has been issued
+  const bool filled = a.page_fill != nullptr;
+  [[maybe_unused]] int fillp[TPW][TP::NPT];
+  if (filled) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int u = 0; u < TP::NPT; ++u)
+        fillp[t][u] = __builtin_amdgcn_readfirstlane(a.page_fill[tp.page[t][u]]);
+  }
+
   // ---- every K / V load of this wave's tiles ----
   uint4 kraw[TPW][2][CB], vraw[TPW][VB];
   [[maybe_unused]] uint2 k8[TPW][2][CB], v8[TPW][VB];  // fp8 codes (FP8 only)
@@ -384,6 +397,18 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use
+  if (filled) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int xv = 8 * q4, u = xv / P, slot = xv % P;
+      const int f = TP::NPT == 1 ? fillp[t][0]
+                                 : fillp[t][0] + u * (fillp[t][TP::NPT - 1] - fillp[t][0]);
+      int m = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m |= (slot + e < f) ? (1 << e) : 0;
+      vmask[t] &= m;
+    }
+  }
   if constexpr (FP8) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
@@ -540,6 +565,13 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs& a, int G, int j, 
     lookup_tiles<P, TT, TPW>(a, list, b, split, w * TPW, tp);
   }
 
+  const bool filled = a.page_fill != nullptr;  // composed sequences: see attn_bf16_block
+  [[maybe_unused]] int fillp[TPW];
+  if (filled) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      fillp[t] = __builtin_amdgcn_readfirstlane(a.page_fill[tp.page[t][0]]);
+  }
   uint4 kraw[TPW][KL], vraw[TPW][VB];
   int vmask[TPW];
   int krow[TPW];
@@ -566,6 +598,16 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs& a, int G, int j, 
     for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = load16(vt + (size_t)(16 * vb) * P);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use
+  if (filled) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int vslot = (w * TPW + t) * TT % P + 4 * q4;
+      int mk = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mk |= (vslot + e < fillp[t]) ? (1 << e) : 0;
+      vmask[t] &= mk;
+    }
+  }
 
   f32x4_t s[TPW];
 #pragma unroll

@@ -83,13 +83,14 @@ __device__ __forceinline__ uint32_t f64_to_bf16_directed(double x) {
   return b;
 }
 
-// Min / max of the valid rows (1 <= valid; more than P means the whole page) of one fp8 (page,
-// KV head) tile, times the tile's scale, rounded outward to bf16, by one wave. The lane layout is
+// Min / max of the valid rows (1 <= valid; more than P means the whole page; rows from `fill` on
+// are excluded too, without changing the loads) of one fp8 (page, KV head) tile, times the
+// tile's scale, rounded outward to bf16, by one wave. The lane layout is
 // bf16's (row_map<bf16_t, D>: 8 channels per lane); each lane loads 8 codes per row. On return
 // every lane holds lo / hi of its channels [c0, c0 + 8) as bf16 values in fp32.
 template <int D>
-__device__ __forceinline__ void tile_minmax_fp8(const uint8_t* tile, int valid, int P, int lane,
-                                                float scale, float* lo, float* hi) {
+__device__ __forceinline__ void tile_minmax_fp8(const uint8_t* tile, int valid, int fill, int P,
+                                                int lane, float scale, float* lo, float* hi) {
   using M = row_map<bf16_t, D>;
   constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
   constexpr int MAX_LOADS = 32 / RPW;
@@ -113,7 +114,7 @@ __device__ __forceinline__ void tile_minmax_fp8(const uint8_t* tile, int valid, 
     if (i * RPW >= P) break;
     float x[VEC];
     fp8x8_to_f32(raw[i], x);
-    if (s < valid) {
+    if (s < valid && s < fill) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         lo[e] = fminf(lo[e], x[e]);

@@ -19,6 +19,7 @@ struct LaunchKV {
   const int32_t* seq_lens;
   const float* k_scale;  // fp8 pools: [Npp][Hkv] per-tile scales (else null)
   const float* v_scale;
+  const int32_t* page_fill;  // [Npp] valid slots of each physical page (composed sequences), or null
 };
 
 // Rotary table arguments passed to kernels by value; page_row == nullptr means "no rotation".

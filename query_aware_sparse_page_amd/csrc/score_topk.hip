@@ -480,6 +480,7 @@ SelectArgs select_args(const LaunchKV& kv, const RopeArgs& rope, void* summ, con
   a.reuse = reuse;
   a.scores_only = 0;
   a.k_scale = kv.k_scale;
+  a.page_fill = kv.page_fill;
   return a;
 }
 

@@ -18,7 +18,9 @@ namespace kvsel {
 __device__ __forceinline__ bool summary_unit(long unit, const int32_t* __restrict__ page_table,
                                              const int32_t* __restrict__ seq_lens, int B, int Hkv,
                                              int P, int maxp, int maxn, int Npp, int tail_only,
-                                             int& b, int& n, int& j, int& p, int& valid) {
+                                             const int32_t* __restrict__ page_fill,
+                                             int& b, int& n, int& j, int& p, int& valid,
+                                             int& fill) {
   if (tail_only) {
     if (unit >= (long)B * Hkv) return false;
     b = (int)(unit / Hkv);
@@ -37,6 +39,7 @@ __device__ __forceinline__ bool summary_unit(long unit, const int32_t* __restric
   const int L = seq_lens[b];
   p = min(max(page_table[(size_t)b * maxp + n], 0), Npp - 1);  // clamp like every reader
   valid = min(P, L - n * P);
+  fill = page_fill ? page_fill[p] : P;  // a composed sequence's page may end early (masks only)
   return true;
 }
 
@@ -46,6 +49,7 @@ __global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_
                                                         const int32_t* __restrict__ seq_lens, int B,
                                                         int Hkv, int P, int maxp, int maxn, int Npp,
                                                         int tail_only,
+                                                        const int32_t* __restrict__ page_fill,
                                                         RopeArgs rope, T* __restrict__ summ) {
   using M = row_map<T, D>;
   constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
@@ -53,9 +57,9 @@ __global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_
 
   const int lane = threadIdx.x & 63;
   const long unit = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  int b, n, j, p, valid;
-  if (!summary_unit(unit, page_table, seq_lens, B, Hkv, P, maxp, maxn, Npp, tail_only, b, n, j, p,
-                    valid))
+  int b, n, j, p, valid, fill;
+  if (!summary_unit(unit, page_table, seq_lens, B, Hkv, P, maxp, maxn, Npp, tail_only, page_fill,
+                    b, n, j, p, valid, fill))
     return;
   const int rg = lane / LPR;
   const int c0 = (lane % LPR) * VEC;
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_
     unpack<T>(raw[i], x);
     if (rope.page_row)  // all lanes take part in the partner exchange
       rope_rotate_slice<T, D>(x, c0, prow < 0 ? -1 : prow + rope.row_step * s, rope.cos, rope.sin);
-    if (s < valid) {
+    if (s < valid && s < fill) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         lo[e] = fminf(lo[e], x[e]);
@@ -116,16 +120,17 @@ __global__ __launch_bounds__(256) void summaries_fp8_kernel(const uint8_t* __res
                                                             const int32_t* __restrict__ seq_lens,
                                                             int B, int Hkv, int P, int maxp,
                                                             int maxn, int Npp, int tail_only,
+                                                            const int32_t* __restrict__ page_fill,
                                                             bf16_t* __restrict__ summ) {
   using M = row_map<bf16_t, D>;
   const int lane = threadIdx.x & 63;
   const long unit = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  int b, n, j, p, valid;
-  if (!summary_unit(unit, page_table, seq_lens, B, Hkv, P, maxp, maxn, Npp, tail_only, b, n, j, p,
-                    valid))
+  int b, n, j, p, valid, fill;
+  if (!summary_unit(unit, page_table, seq_lens, B, Hkv, P, maxp, maxn, Npp, tail_only, page_fill,
+                    b, n, j, p, valid, fill))
     return;
   float lo[M::VEC], hi[M::VEC];
-  tile_minmax_fp8<D>(k_pool + ((size_t)p * Hkv + j) * P * D, valid, P, lane,
+  tile_minmax_fp8<D>(k_pool + ((size_t)p * Hkv + j) * P * D, valid, fill, P, lane,
                      k_scale[(size_t)p * Hkv + j], lo, hi);
   if (lane < M::LPR) {
     bf16_t* out = summ + (((size_t)b * Hkv + j) * maxp + n) * 2 * D + lane * M::VEC;
@@ -142,7 +147,7 @@ static hipError_t launch_summaries_t(const LaunchKV& kv, const RopeArgs& rope, i
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((summaries_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const T*)kv.k_pool, kv.page_table, kv.seq_lens, kv.B, kv.Hkv, kv.P, kv.maxp,
-                     kv.maxn, kv.Npp, tail_only, rope, (T*)summ);
+                     kv.maxn, kv.Npp, tail_only, kv.page_fill, rope, (T*)summ);
   return hipGetLastError();
 }
 
@@ -154,7 +159,8 @@ static hipError_t launch_summaries_fp8(const LaunchKV& kv, int tail_only, void* 
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((summaries_fp8_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const uint8_t*)kv.k_pool, kv.k_scale, kv.page_table, kv.seq_lens, kv.B,
-                     kv.Hkv, kv.P, kv.maxp, kv.maxn, kv.Npp, tail_only, (bf16_t*)summ);
+                     kv.Hkv, kv.P, kv.maxp, kv.maxn, kv.Npp, tail_only, kv.page_fill,
+                     (bf16_t*)summ);
   return hipGetLastError();
 }
 

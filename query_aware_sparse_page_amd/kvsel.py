@@ -30,6 +30,7 @@ KVSEL_CHECK_SEQ_LEN = 1
 KVSEL_CHECK_PAGE_ID = 2
 KVSEL_CHECK_SELECTION = 4
 KVSEL_CHECK_NO_FREE_PAGE = 8
+KVSEL_CHECK_PAGE_FILL = 16
 
 c_i32 = ctypes.c_int32
 c_vp = ctypes.c_void_p
@@ -47,6 +48,7 @@ class PagedKVDesc(ctypes.Structure):
         ("head_dim", c_i32), ("page_size", c_i32), ("num_phys_pages", c_i32),
         ("max_pages_per_seq", c_i32), ("k_pool", c_vp), ("v_pool", c_vp), ("page_table", c_vp),
         ("seq_lens", c_vp), ("max_seq_len", c_i32), ("k_scale", c_vp), ("v_scale", c_vp),
+        ("page_fill", c_vp),
     ]
 
 
@@ -98,7 +100,7 @@ EXPORTS = {
 _lib = None
 
 
-ABI_VERSION = 3  # KVSEL_ABI_VERSION of include/kvsel.h
+ABI_VERSION = 4  # KVSEL_ABI_VERSION of include/kvsel.h
 
 
 def lib() -> ctypes.CDLL:
@@ -185,6 +187,7 @@ class PagedKV:
     max_seq_len: int = 0
     k_scale: Optional[torch.Tensor] = None  # fp8 pools (uint8 codes): [Npp][Hkv] fp32
     v_scale: Optional[torch.Tensor] = None
+    page_fill: Optional[torch.Tensor] = None  # int32 [Npp] valid slots per page (composition)
 
     @property
     def is_fp8(self) -> bool:
@@ -219,12 +222,18 @@ class PagedKV:
                 scales[i] = t.data_ptr()
             if scales[0] is None:
                 raise ValueError("an fp8 key pool needs k_scale")
+        fill = None
+        if self.page_fill is not None:
+            _dev(self.page_fill, "page_fill", torch.int32)
+            if tuple(self.page_fill.shape) != (Npp,):
+                raise ValueError(f"page_fill must be int32 [Npp] = [{Npp}]")
+            fill = self.page_fill.data_ptr()
         B, maxp = self.page_table.shape
         return PagedKVDesc(_elem_code(self.k_pool.dtype), B, self.num_q_heads, Hkv, D, P, Npp, maxp,
                            self.k_pool.data_ptr(),
                            self.v_pool.data_ptr() if self.v_pool is not None else None,
                            self.page_table.data_ptr(), self.seq_lens.data_ptr(),
-                           int(self.max_seq_len), scales[0], scales[1])
+                           int(self.max_seq_len), scales[0], scales[1], fill)
 
     @property
     def batch(self) -> int:
@@ -529,7 +538,7 @@ def quantize_pages(kv: PagedKV, values: bool = True) -> PagedKV:
     _check(lib().kvsel_quantize_pages(ctypes.byref(d), _ptr(k_codes), _ptr(k_scale), _ptr(v_codes),
                                       _ptr(v_scale), _stream(dev)))
     return PagedKV(k_codes, v_codes, kv.page_table, kv.seq_lens, kv.num_q_heads, kv.max_seq_len,
-                   k_scale, v_scale)
+                   k_scale, v_scale, kv.page_fill)
 
 
 def check_inputs(kv: PagedKV, sel_idx: Optional[torch.Tensor] = None,

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(K):
 
 def test_version_and_status_strings(K):
     lib = K.lib()
-    assert lib.kvsel_abi_version() == K.ABI_VERSION == 3
+    assert lib.kvsel_abi_version() == K.ABI_VERSION == 4
     for code, tag in [(0, "KVSEL_OK"), (1, "INVALID_ARGUMENT"), (2, "UNSUPPORTED"),
                       (3, "WORKSPACE"), (4, "DEVICE"), (5, "LAUNCH"), (99, "UNKNOWN")]:
         assert tag in lib.kvsel_status_str(code).decode()
@@ -52,7 +52,7 @@ def _desc(K, **kw):
     base = dict(dtype=K.KVSEL_BF16, batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128,
                 page_size=32, num_phys_pages=1024, max_pages_per_seq=1024,
                 k_pool=0x1000, v_pool=0x2000, page_table=0x3000, seq_lens=0x4000,
-                max_seq_len=0, k_scale=None, v_scale=None)
+                max_seq_len=0, k_scale=None, v_scale=None, page_fill=None)
     base.update(kw)
     return K.PagedKVDesc(*[base[f] for f, _ in K.PagedKVDesc._fields_])
 
