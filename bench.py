@@ -47,13 +47,15 @@ METRIC = "sparse decode-attn µs/step and achieved HBM GB/s (% of peak) at 32K/1
 class Layer:
     """One copy of the cache (its own HBM addresses) with preallocated outputs/workspaces."""
 
-    def __init__(self, w, dev, k_pool, v_pool, page_table, seq_lens, fp8=False):
-        self.kv = K.PagedKV(k_pool, v_pool, page_table, seq_lens, w.Hq)
+    def __init__(self, w, dev, k_pool, v_pool, page_table, seq_lens, fp8=False, rope=None,
+                 page_fill=None):
+        self.kv = K.PagedKV(k_pool, v_pool, page_table, seq_lens, w.Hq, page_fill=page_fill)
         if fp8:  # E4M3 pages with per-tile scales, quantized on the device
             self.kv = K.quantize_pages(self.kv)
+        self.rope = rope  # rotary re-positioning fused into the key gathers, or None
         self.q = w.q.to(dev)
         self.k = w.k
-        self.summ = K.build_summaries(self.kv)
+        self.summ = K.build_summaries(self.kv, rope=rope)
         self.sel = torch.empty((w.B, w.Hkv, w.k), dtype=torch.int32, device=dev)
         self.cnt = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=dev)
         self.out = torch.empty_like(self.q)
@@ -63,14 +65,15 @@ class Layer:
         self.ws_fused = K.new_workspace(self.kv, w.k, K.KVSEL_OP_SELECT_ATTEND)
 
     def select(self):
-        K.score_topk(self.kv, self.summ, self.q, self.k, refresh_tail=True, sel_idx=self.sel,
-                     sel_cnt=self.cnt, workspace=self.ws_score)
+        K.score_topk(self.kv, self.summ, self.q, self.k, refresh_tail=True, rope=self.rope,
+                     sel_idx=self.sel, sel_cnt=self.cnt, workspace=self.ws_score)
 
     pps = 0  # pages per split: 0 = the library's choice
 
     def attend(self):
-        K.sparse_decode_attn(self.kv, self.q, self.sel, self.cnt, self.k, out=self.out,
-                             lse=self.lse, pages_per_split=self.pps, workspace=self.ws_attn)
+        K.sparse_decode_attn(self.kv, self.q, self.sel, self.cnt, self.k, rope=self.rope,
+                             out=self.out, lse=self.lse, pages_per_split=self.pps,
+                             workspace=self.ws_attn)
 
     def probe(self):
         """Plain gather of the K/V tiles the selection names (measurement context)."""
@@ -78,8 +81,9 @@ class Layer:
 
     def step(self):
         """The decode step as one kvsel_select_attend call (top-k fused into the attention)."""
-        K.select_attend(self.kv, self.summ, self.q, self.k, refresh_tail=True, sel_idx=self.sel,
-                        sel_cnt=self.cnt, out=self.out, lse=self.lse, workspace=self.ws_fused)
+        K.select_attend(self.kv, self.summ, self.q, self.k, refresh_tail=True, rope=self.rope,
+                        sel_idx=self.sel, sel_cnt=self.cnt, out=self.out, lse=self.lse,
+                        workspace=self.ws_fused)
 
     def step_two_calls(self):
         """The same step as kvsel_score_topk + kvsel_sparse_decode_attn."""
@@ -170,6 +174,15 @@ def attention_bytes(w, lay):
         return selected_kv_bytes(w.seq_lens.tolist(), sel, cnt, w.Hkv, w.P, w.D, 1) + \
             8 * int(cnt.sum())
     esize = 4 if w.dtype == "f32" else 2
+    if lay.kv.page_fill is not None:  # a composed context: pages that end early hold fewer tokens
+        fill = lay.kv.page_fill.cpu().numpy()
+        toks = 0
+        for b, L in enumerate(w.seq_lens.tolist()):
+            for j in range(w.Hkv):
+                for n in sel[b, j, :cnt[b, j]]:
+                    p = int(w.page_table[b, int(n)])
+                    toks += min(w.P, int(L) - int(n) * w.P, int(fill[p]))
+        return 2 * toks * w.D * esize
     return selected_kv_bytes(w.seq_lens.tolist(), sel, cnt, w.Hkv, w.P, w.D, esize)
 
 
@@ -449,6 +462,44 @@ def speculative_growing(dev, reps=3):
                     "kvsel_sparse_decode_attn"}
 
 
+COMPOSED_DOCS = (4000, 3100, 517, 2900, 6000, 1, 3333, 2048, 4500, 1234, 777, 3600)
+
+
+def composed_context(dev, steps, warmup, n_layers=48):
+    """A 32K-token context composed of 12 independently cached documents of ragged lengths
+    (the positional half of RAG reuse): each document's keys encoded at its own positions
+    [0, len), its pages chained in the context with the last page of each document ending early
+    (page_fill), and every page moved to its composed position by a rotary shift fused into the
+    key gathers. Same step and timing as the headline (one kvsel_select_attend call per layer
+    copy, 48 copies rotated)."""
+    w = W.composed(1007, doc_lens=COMPOSED_DOCS, B=1, k=64)
+    page_in_doc = w.extra["page_in_doc"].numpy()
+    doc_of_page = w.extra["doc_of_page"].numpy()
+    start = w.extra["doc_start"].numpy()[0]
+    cos, sin = K.rope_table(w.extra["theta"], w.D, 0, int(start.max()) + max(COMPOSED_DOCS) + w.P,
+                            dev)
+    table, lens = w.page_table.to(dev), w.seq_lens.to(dev)
+    fill = w.extra["page_fill"].to(dev)
+    v0 = K.device_v_layout(w.v_pool.to(dev))
+    raw = K.PagedKV(w.k_pool.to(dev), v0, table, lens, w.Hq, page_fill=fill)
+    enc_row = torch.from_numpy((page_in_doc * w.P).astype(np.int32)).to(dev)
+    k0 = K.rope_shift(raw, K.Rope(cos, sin, enc_row, 1))  # the documents as cached
+    shift = K.Rope(cos, sin, torch.from_numpy(start[doc_of_page].astype(np.int32)).to(dev), 0)
+    layers = [Layer(w, dev, k0 if i == 0 else k0.clone(), v0 if i == 0 else v0.clone(), table,
+                    lens, rope=shift, page_fill=fill) for i in range(n_layers)]
+    torch.cuda.synchronize()
+    us_step, _ = time_graph(layers, steps, warmup)
+    n_calls = max(len(layers), min(steps, 512) // len(layers) * len(layers))
+    attn_us = time_calls(layers, Layer.attend, n_calls)
+    abytes = attention_bytes(w, layers[0])
+    return {"us_per_step": round(us_step, 3), "attn_us": round(attn_us, 3),
+            "attn_GBps": round(abytes / (attn_us * 1e-6) / 1e9, 1), "attn_bytes": abytes,
+            "context_slots": int(w.seq_lens[0]), "documents": len(COMPOSED_DOCS),
+            "tokens": int(sum(COMPOSED_DOCS)), "layers_rotated": n_layers,
+            "step": "kvsel_select_attend over the composed context: tail refresh, scores, top-k "
+                    "and attention, every key gather rotating its page by its document's offset"}
+
+
 def cpu_baseline(w, lay, budget_s=12.0):
     """The oracle's decode step (tail summary + scores + top-k + attention) on the host, for a
     bounded number of repetitions of the same workload; also checks the GPU's step output."""
@@ -624,6 +675,10 @@ def main():
         torch.cuda.empty_cache()
         result["secondary"]["speculative_growing_64_steps"] = speculative_growing(dev)
         progress("growing speculative workload done")
+        torch.cuda.empty_cache()
+        result["secondary"]["composed_32k_12_documents"] = composed_context(dev, args.steps,
+                                                                           args.warmup)
+        progress("composed-context workload done")
         torch.cuda.empty_cache()
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, keep)

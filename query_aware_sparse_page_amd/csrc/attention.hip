@@ -8,21 +8,22 @@
 
 namespace kvsel {
 
-template <int D, int P, int WAVES, int TPW, bool ROPE>
+// FILL: pages that end early (page_fill set), a separate instantiation.
+template <int D, int P, int WAVES, int TPW, bool ROPE, bool FILL = false>
 __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a, int G) {
   // grid (Hkv, B, splits)
-  attn_bf16_block<D, P, WAVES, TPW, ROPE>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
+  attn_bf16_block<D, P, WAVES, TPW, ROPE, 0, false, FILL>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // fp8 pools (E4M3 codes, per-tile scales), decoded to bf16 in registers; no rotary gather.
-template <int D, int P, int WAVES, int TPW>
+template <int D, int P, int WAVES, int TPW, bool FILL = false>
 __global__ __launch_bounds__(WAVES * 64) void attn_fp8_kernel(AttnArgs a, int G) {
-  attn_bf16_block<D, P, WAVES, TPW, false, 0, true>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
+  attn_bf16_block<D, P, WAVES, TPW, false, 0, true, FILL>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-template <int D, int P, int WAVES, int TPW, bool ROPE>
+template <int D, int P, int WAVES, int TPW, bool ROPE, bool FILL = false>
 __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(AttnArgs a, int G) {
-  attn_f32_block<D, P, WAVES, TPW, ROPE>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
+  attn_f32_block<D, P, WAVES, TPW, ROPE, 0, FILL>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -134,19 +135,25 @@ size_t attention_workspace(const LaunchKV& kv, int k, int pages_per_split) {
   return align256(parts * kv.D * sizeof(float)) + parts * sizeof(float2);
 }
 
-template <typename T, int D, int P, int WAVES, int TPW>
-static void launch_split(const AttnArgs& a, int G, bool rope, hipStream_t stream) {
+template <typename T, int D, int P, int WAVES, int TPW, bool FILL>
+static void launch_split_f(const AttnArgs& a, int G, bool rope, hipStream_t stream) {
   const dim3 grid(a.Hkv, a.nlists / a.Hkv, a.nsplit);
   const dim3 block(WAVES * 64);
   if constexpr (sizeof(T) == 1) {
-    hipLaunchKernelGGL((attn_fp8_kernel<D, P, WAVES, TPW>), grid, block, 0, stream, a, G);
+    hipLaunchKernelGGL((attn_fp8_kernel<D, P, WAVES, TPW, FILL>), grid, block, 0, stream, a, G);
   } else if constexpr (sizeof(T) == 2) {
-    if (rope) hipLaunchKernelGGL((attn_bf16_kernel<D, P, WAVES, TPW, true>), grid, block, 0, stream, a, G);
-    else hipLaunchKernelGGL((attn_bf16_kernel<D, P, WAVES, TPW, false>), grid, block, 0, stream, a, G);
+    if (rope) hipLaunchKernelGGL((attn_bf16_kernel<D, P, WAVES, TPW, true, FILL>), grid, block, 0, stream, a, G);
+    else hipLaunchKernelGGL((attn_bf16_kernel<D, P, WAVES, TPW, false, FILL>), grid, block, 0, stream, a, G);
   } else {
-    if (rope) hipLaunchKernelGGL((attn_f32_kernel<D, P, WAVES, TPW, true>), grid, block, 0, stream, a, G);
-    else hipLaunchKernelGGL((attn_f32_kernel<D, P, WAVES, TPW, false>), grid, block, 0, stream, a, G);
+    if (rope) hipLaunchKernelGGL((attn_f32_kernel<D, P, WAVES, TPW, true, FILL>), grid, block, 0, stream, a, G);
+    else hipLaunchKernelGGL((attn_f32_kernel<D, P, WAVES, TPW, false, FILL>), grid, block, 0, stream, a, G);
   }
+}
+
+template <typename T, int D, int P, int WAVES, int TPW>
+static void launch_split(const AttnArgs& a, int G, bool rope, hipStream_t stream) {
+  if (a.page_fill) launch_split_f<T, D, P, WAVES, TPW, true>(a, G, rope, stream);
+  else launch_split_f<T, D, P, WAVES, TPW, false>(a, G, rope, stream);
 }
 
 // parts: 1 = the split launch, 2 = the merge launch (when there is more than one split)

@@ -294,9 +294,13 @@ __device__ __forceinline__ void finish_block(const AttnArgs& a, int G, int list,
 // MFMA layouts are unchanged. A lane's 8 tokens of a tile lie in one page, so one (k_scale,
 // v_scale) pair per lane and tile: the logits take scale * k_scale, and each probability enters
 // P V as bf16(p * v_scale) while l adds bf16(p).
-template <int D, int P, int WAVES, int TPW, bool ROPE, int SEL_C = 0, bool FP8 = false>
+// FILL: the pages may end early (page_fill, composed sequences); a separate instantiation, so
+// the common case carries none of its registers.
+template <int D, int P, int WAVES, int TPW, bool ROPE, int SEL_C = 0, bool FP8 = false,
+          bool FILL = false>
 __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j, int b, int split) {
   static_assert(!(FP8 && ROPE), "fp8 pools take no rotary gather");
+  static_assert(!(FILL && SEL_C > 0), "composed sequences take the separate selection");
   constexpr int TT = 32;       // tokens per tile
   constexpr int CB = D / 32;   // 32-channel blocks of q K^T
   constexpr int VB = D / 16;   // 16-channel blocks of P V
@@ -332,18 +336,6 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
       return;
   } else {
     lookup_tiles<P, TT, TPW>(a, list, b, split, w * TPW, tp);
-  }
-
-  // valid slots of the tiles' pages in a composed sequence (page_fill): scalar loads beside the
-  // K / V loads, applied to the masks after every load has been issued
-  const bool filled = a.page_fill != nullptr;
-  [[maybe_unused]] int fillp[TPW][TP::NPT];
-  if (filled) {
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int u = 0; u < TP::NPT; ++u)
-        fillp[t][u] = __builtin_amdgcn_readfirstlane(a.page_fill[tp.page[t][u]]);
   }
 
   // ---- every K / V load of this wave's tiles ----
@@ -396,8 +388,18 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
       for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = load16(vt + (size_t)(16 * vb) * P);
     }
   }
+  // valid slots of the tiles' pages in a composed sequence (page_fill): scalar loads after the
+  // K / V loads, applied to the masks
+  [[maybe_unused]] int fillp[TPW][TP::NPT];
+  if constexpr (FILL) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int u = 0; u < TP::NPT; ++u)
+        fillp[t][u] = __builtin_amdgcn_readfirstlane(a.page_fill[tp.page[t][u]]);
+  }
   __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use
-  if (filled) {
+  if constexpr (FILL) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const int xv = 8 * q4, u = xv / P, slot = xv % P;
@@ -524,8 +526,9 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
 // ------------------------------------------------------------------------------------------
 // fp32
 // ------------------------------------------------------------------------------------------
-template <int D, int P, int WAVES, int TPW, bool ROPE, int SEL_C = 0>
+template <int D, int P, int WAVES, int TPW, bool ROPE, int SEL_C = 0, bool FILL = false>
 __device__ __forceinline__ void attn_f32_block(const AttnArgs& a, int G, int j, int b, int split) {
+  static_assert(!(FILL && SEL_C > 0), "composed sequences take the separate selection");
   constexpr int TT = 16;       // tokens per tile
   constexpr int KC = D / 4;    // channels per lane in q K^T (4 lane groups)
   constexpr int KL = KC / 4;   // 16-byte loads per lane per token
@@ -565,13 +568,6 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs& a, int G, int j, 
     lookup_tiles<P, TT, TPW>(a, list, b, split, w * TPW, tp);
   }
 
-  const bool filled = a.page_fill != nullptr;  // composed sequences: see attn_bf16_block
-  [[maybe_unused]] int fillp[TPW];
-  if (filled) {
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-      fillp[t] = __builtin_amdgcn_readfirstlane(a.page_fill[tp.page[t][0]]);
-  }
   uint4 kraw[TPW][KL], vraw[TPW][VB];
   int vmask[TPW];
   int krow[TPW];
@@ -597,8 +593,14 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs& a, int G, int j, 
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = load16(vt + (size_t)(16 * vb) * P);
   }
+  [[maybe_unused]] int fillp[TPW];  // composed sequences: see attn_bf16_block
+  if constexpr (FILL) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      fillp[t] = __builtin_amdgcn_readfirstlane(a.page_fill[tp.page[t][0]]);
+  }
   __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use
-  if (filled) {
+  if constexpr (FILL) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const int vslot = (w * TPW + t) * TT % P + 4 * q4;

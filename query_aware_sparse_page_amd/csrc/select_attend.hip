@@ -31,6 +31,7 @@ static int fused_keys_per_thread(const LaunchKV& kv) {
 }
 
 bool fused_select_supported(const LaunchKV& kv, int k) {
+  if (kv.page_fill) return false;  // composed sequences: the separate launches
   return fused_keys_per_thread(kv) > 0 && attention_pages_per_split(kv, k, 0) == FUSED_PPS;
 }
 

@@ -18,9 +18,7 @@ namespace kvsel {
 __device__ __forceinline__ bool summary_unit(long unit, const int32_t* __restrict__ page_table,
                                              const int32_t* __restrict__ seq_lens, int B, int Hkv,
                                              int P, int maxp, int maxn, int Npp, int tail_only,
-                                             const int32_t* __restrict__ page_fill,
-                                             int& b, int& n, int& j, int& p, int& valid,
-                                             int& fill) {
+                                             int& b, int& n, int& j, int& p, int& valid) {
   if (tail_only) {
     if (unit >= (long)B * Hkv) return false;
     b = (int)(unit / Hkv);
@@ -39,7 +37,6 @@ __device__ __forceinline__ bool summary_unit(long unit, const int32_t* __restric
   const int L = seq_lens[b];
   p = min(max(page_table[(size_t)b * maxp + n], 0), Npp - 1);  // clamp like every reader
   valid = min(P, L - n * P);
-  fill = page_fill ? page_fill[p] : P;  // a composed sequence's page may end early (masks only)
   return true;
 }
 
@@ -57,9 +54,9 @@ __global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_
 
   const int lane = threadIdx.x & 63;
   const long unit = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  int b, n, j, p, valid, fill;
-  if (!summary_unit(unit, page_table, seq_lens, B, Hkv, P, maxp, maxn, Npp, tail_only, page_fill,
-                    b, n, j, p, valid, fill))
+  int b, n, j, p, valid;
+  if (!summary_unit(unit, page_table, seq_lens, B, Hkv, P, maxp, maxn, Npp, tail_only, b, n, j, p,
+                    valid))
     return;
   const int rg = lane / LPR;
   const int c0 = (lane % LPR) * VEC;
@@ -74,6 +71,8 @@ __global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_
     raw[i] = load16(tile + (size_t)min(s, valid - 1) * D + c0);
   }
 
+  // a composed sequence's page may end early: masks only, read after the row loads
+  const int fill = page_fill ? page_fill[p] : P;
   float lo[VEC], hi[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
@@ -125,12 +124,12 @@ __global__ __launch_bounds__(256) void summaries_fp8_kernel(const uint8_t* __res
   using M = row_map<bf16_t, D>;
   const int lane = threadIdx.x & 63;
   const long unit = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  int b, n, j, p, valid, fill;
-  if (!summary_unit(unit, page_table, seq_lens, B, Hkv, P, maxp, maxn, Npp, tail_only, page_fill,
-                    b, n, j, p, valid, fill))
+  int b, n, j, p, valid;
+  if (!summary_unit(unit, page_table, seq_lens, B, Hkv, P, maxp, maxn, Npp, tail_only, b, n, j, p,
+                    valid))
     return;
   float lo[M::VEC], hi[M::VEC];
-  tile_minmax_fp8<D>(k_pool + ((size_t)p * Hkv + j) * P * D, valid, fill, P, lane,
+  tile_minmax_fp8<D>(k_pool + ((size_t)p * Hkv + j) * P * D, valid, page_fill, p, P, lane,
                      k_scale[(size_t)p * Hkv + j], lo, hi);
   if (lane < M::LPR) {
     bf16_t* out = summ + (((size_t)b * Hkv + j) * maxp + n) * 2 * D + lane * M::VEC;
