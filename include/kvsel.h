@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVSEL_ABI_VERSION 4
+#define KVSEL_ABI_VERSION 5
 
 typedef int32_t kvsel_status;
 #define KVSEL_OK 0
@@ -123,13 +123,19 @@ typedef struct kvsel_paged_kv {
  * (x_i*c - x_{i+D/2}*s, x_{i+D/2}*c + x_i*s), each product and sum rounded to fp32 separately
  * (no fused multiply-add), then rounded to the element type (round-to-nearest-even).
  * Slot s of physical page p uses table row page_row[p] + row_step * s; page_row[p] < 0 leaves
- * the page as it is. row_step 1 encodes per-token positions; row_step 0 shifts a whole page. */
+ * the page as it is. row_step 1 encodes per-token positions; row_step 0 shifts a whole page.
+ * per_sequence != 0: page_row is [B][max_pages_per_seq] and logical page n of sequence b uses
+ * page_row[b][n] instead, so sequences that share a document's pages can place it at different
+ * positions (composed contexts); kvsel_rope_shift, which rewrites physical pages, rejects it
+ * (KVSEL_ERR_UNSUPPORTED). */
 typedef struct kvsel_rope {
   const float* cos;        /* [n_rows][D/2] fp32                                       */
   const float* sin;        /* [n_rows][D/2] fp32                                       */
-  const int32_t* page_row; /* [num_phys_pages]; every used row must be < n_rows         */
+  const int32_t* page_row; /* [num_phys_pages], or [B][max_pages_per_seq] (per_sequence);
+                              every used row must be < n_rows                           */
   int32_t n_rows;
   int32_t row_step;        /* 0 or 1                                                    */
+  int32_t per_sequence;    /* 0: rows by physical page; 1: by (sequence, logical page)  */
 } kvsel_rope;
 
 /* Host struct: speculative reuse with correction ([FreeKV] section 2.1). For every (b, j):

@@ -87,6 +87,8 @@ kvsel_status flatten_rope(const kvsel_rope* rope, const LaunchKV& f, RopeArgs* o
   out->sin = nullptr;
   out->page_row = nullptr;
   out->row_step = 0;
+  out->per_seq = 0;
+  out->stride = f.maxp;
   if (!rope) return KVSEL_OK;
   if (f.dtype == 2) return KVSEL_ERR_UNSUPPORTED;
   if (!rope->cos || !rope->sin || !rope->page_row || rope->n_rows < 1) return KVSEL_ERR_INVALID_ARGUMENT;
@@ -95,6 +97,7 @@ kvsel_status flatten_rope(const kvsel_rope* rope, const LaunchKV& f, RopeArgs* o
   out->sin = rope->sin;
   out->page_row = rope->page_row;
   out->row_step = rope->row_step;
+  out->per_seq = rope->per_sequence ? 1 : 0;
   return KVSEL_OK;
 }
 
@@ -326,6 +329,7 @@ kvsel_status kvsel_rope_shift(const kvsel_paged_kv* kv, const kvsel_rope* rope, 
   if (st != KVSEL_OK) return st;
   if (!rope || !k_out) return KVSEL_ERR_INVALID_ARGUMENT;
   if ((st = flatten_rope(rope, f, &r)) != KVSEL_OK) return st;
+  if (r.per_seq) return KVSEL_ERR_UNSUPPORTED;  // a shared physical page has one rotation
   if ((st = check_device()) != KVSEL_OK) return st;
   return launch_status(launch_rope_shift(f, r, k_out, (hipStream_t)stream));
 }

@@ -87,10 +87,14 @@ struct TilePages {
   static_assert(NPT <= 2, "a tile spans at most two pages");
   int page[TPW][NPT];   // physical page to address (always a valid page)
   int valid[TPW][NPT];  // valid slots of that page; 0 when the slot range is not in the list
+  int lpage[TPW][NPT];  // its logical page in the sequence (the per-sequence rotary rows)
   // Entry u (lane-dependent, 0 or 1) of tile t, by arithmetic: a register array indexed by a
   // per-lane value (which a select of two entries can be folded into) lands in private memory.
   __device__ __forceinline__ int page_of(int t, int u) const {
     return NPT == 1 ? page[t][0] : page[t][0] + u * (page[t][NPT - 1] - page[t][0]);
+  }
+  __device__ __forceinline__ int lpage_of(int t, int u) const {
+    return NPT == 1 ? lpage[t][0] : lpage[t][0] + u * (lpage[t][NPT - 1] - lpage[t][0]);
   }
   __device__ __forceinline__ int valid_of(int t, int u) const {
     return NPT == 1 ? valid[t][0] : valid[t][0] + u * (valid[t][NPT - 1] - valid[t][0]);
@@ -120,6 +124,7 @@ __device__ __forceinline__ void lookup_tiles(const AttnArgs& a, int list, int b,
       // an entry outside the list may hold anything: clamp it into the pool before addressing
       const int pg = __builtin_amdgcn_readfirstlane(a.page_table[(size_t)b * a.maxp + (in_range ? nn : 0)]);
       tp.page[t][u] = min(max(pg, 0), a.Npp - 1);
+      tp.lpage[t][u] = in_range ? nn : 0;
       const int sp = split * a.pps + ((first_tile + t) * TT) / P + u;
       tp.valid[t][u] = (in_range && sp < cnt) ? min(P, L - nn * P) : 0;
     }
@@ -140,6 +145,7 @@ struct SplitSelectSmem {
   RadixSmem<NT> r;
   int page[ATT_MAX_PPS];   // physical page at each of the split's positions
   int valid[ATT_MAX_PPS];  // its valid slots (0: nothing selected at that position)
+  int lpage[ATT_MAX_PPS];  // its logical page
 };
 
 template <int P, int TT, int TPW, int NT, int C>
@@ -164,6 +170,7 @@ __device__ __forceinline__ bool select_tiles(const AttnArgs& a, int list, int b,
   if (tid < a.pps) {
     ss.page[tid] = 0;
     ss.valid[tid] = 0;
+    ss.lpage[tid] = 0;
   }
   uint32_t key[C];
 #pragma unroll
@@ -183,6 +190,7 @@ __device__ __forceinline__ bool select_tiles(const AttnArgs& a, int list, int b,
     if (sp >= 0 && sp < a.pps) {
       ss.page[sp] = min(max(pt[u], 0), a.Npp - 1);  // any table value stays inside the pool
       ss.valid[sp] = min(P, L - i * P);
+      ss.lpage[sp] = i;
     }
   });
   if (writer) {
@@ -208,6 +216,7 @@ __device__ __forceinline__ bool select_tiles(const AttnArgs& a, int list, int b,
       const int sp = ((first_tile + t) * TT) / P + u;
       tp.page[t][u] = __builtin_amdgcn_readfirstlane(ss.page[sp]);
       tp.valid[t][u] = __builtin_amdgcn_readfirstlane(ss.valid[sp]);
+      tp.lpage[t][u] = __builtin_amdgcn_readfirstlane(ss.lpage[sp]);
     }
   return true;
 }
@@ -364,7 +373,7 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
         for (int cb = 0; cb < CB; ++cb) kraw[t][h][cb] = load16(row + 32 * cb);
       }
       if (ROPE) {
-        const int pr = a.rope.page_row[pg];
+        const int pr = a.rope.page_row[rope_row_index(a.rope, b, tp.lpage_of(t, u), pg)];
         krow[t][h] = pr < 0 ? -1 : pr + a.rope.row_step * slot;
       }
     }
@@ -581,7 +590,7 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs& a, int G, int j, 
 #pragma unroll
     for (int u = 0; u < KL; ++u) kraw[t][u] = load16(row + 4 * u);
     if (ROPE) {
-      const int pr = a.rope.page_row[pg];
+      const int pr = a.rope.page_row[rope_row_index(a.rope, b, tp.lpage[t][0], pg)];
       krow[t] = pr < 0 ? -1 : pr + a.rope.row_step * slot;
     }
     const int vslot = base + 4 * q4;

@@ -28,7 +28,14 @@ struct RopeArgs {
   const float* sin;
   const int32_t* page_row;
   int row_step;
+  int per_seq;  // page_row by (sequence, logical page), row stride `stride`; else by physical page
+  int stride;
 };
+
+// The page_row entry of logical page n (physical page p) of sequence b.
+__host__ __device__ inline int rope_row_index(const RopeArgs& r, int b, int n, int p) {
+  return r.per_seq ? b * r.stride + n : p;
+}
 
 // Per-pair inverse rotary frequencies theta^(-2i/D), i < D/2 <= 64 (kernel argument by value).
 struct InvFreq {

@@ -30,13 +30,13 @@ struct SelectArgs {
 
 // Min / max of the valid rows (1 <= valid; more than P means the whole page; with page_fill, rows
 // from page_fill[pt] on are excluded too, read after the row loads are issued) of one (page, KV
-// head) tile of physical page pt, computed by one wave. On return every lane holds lo / hi of its
+// head) tile of physical page pt, computed by one wave; rope_idx is its rotary page_row entry. On return every lane holds lo / hi of its
 // channels [c0, c0 + VEC). The row loads are unconditional (rows past `valid` re-read the last
 // valid row and are ignored), so they all go out at once; the page's rotary row is read after them.
 template <typename T, int D>
 __device__ __forceinline__ void tile_minmax(const T* tile, int valid, const int32_t* page_fill,
-                                            int P, int lane, int pt, const RopeArgs& rope,
-                                            float* lo, float* hi) {
+                                            int P, int lane, int pt, int rope_idx,
+                                            const RopeArgs& rope, float* lo, float* hi) {
   valid = min(valid, P);  // a length past the page bound: every row of the last page counted
   using M = row_map<T, D>;
   constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
@@ -50,7 +50,7 @@ __device__ __forceinline__ void tile_minmax(const T* tile, int valid, const int3
     raw[i] = load16(tile + (size_t)min(s, valid - 1) * D + c0);
   }
   const int fill = page_fill ? page_fill[pt] : P;
-  const int prow = rope.page_row ? rope.page_row[pt] : -1;
+  const int prow = rope.page_row ? rope.page_row[rope_idx] : -1;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     lo[e] = __int_as_float(0x7f800000);
@@ -86,15 +86,15 @@ __device__ __forceinline__ void tile_minmax(const T* tile, int valid, const int3
 // min / max of its valid rows, rotated first when the rotary gather is on (f32 / bf16 pools), or
 // scaled and rounded outward to bf16 (fp8 pools).
 template <typename T, int D, bool FP8>
-__device__ __forceinline__ void refresh_tile(const SelectArgs& a, int pt, int j, int valid,
-                                             int lane, float* lo, float* hi) {
+__device__ __forceinline__ void refresh_tile(const SelectArgs& a, int b, int n, int pt, int j,
+                                             int valid, int lane, float* lo, float* hi) {
   const size_t t = (size_t)pt * a.Hkv + j;
   if constexpr (FP8)
     tile_minmax_fp8<D>((const uint8_t*)a.k_pool + t * a.P * D, valid, a.page_fill, pt, a.P, lane,
                        a.k_scale[t], lo, hi);
   else
-    tile_minmax<T, D>((const T*)a.k_pool + t * a.P * D, valid, a.page_fill, a.P, lane, pt, a.rope,
-                      lo, hi);
+    tile_minmax<T, D>((const T*)a.k_pool + t * a.P * D, valid, a.page_fill, a.P, lane, pt,
+                      rope_row_index(a.rope, b, n, pt), a.rope, lo, hi);
 }
 
 // Scores of chunk `chunk` (WAVES * U * 64 / LPR consecutive pages) of list (sequence b, KV head
@@ -162,7 +162,7 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
       pt = u == ut ? x : pt;
     }
     pt = min(max(pt, 0), a.Npp - 1);
-    refresh_tile<T, D, FP8>(a, pt, j, L - nt * P, lane, flo, fhi);
+    refresh_tile<T, D, FP8>(a, b, nt, pt, j, L - nt * P, lane, flo, fhi);
     if (lane < LPR) {
       T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;
       store16(out + c0, pack<T>(flo));

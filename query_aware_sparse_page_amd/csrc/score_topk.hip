@@ -316,7 +316,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
     const int nt = N - 1;
     const int pt = min(max(a.page_table[(size_t)b * a.maxp + nt], 0), a.Npp - 1);
     float lo[VEC], hi[VEC];
-    refresh_tile<T, D, FP8>(a, pt, j, L - nt * P, lane, lo, hi);
+    refresh_tile<T, D, FP8>(a, b, nt, pt, j, L - nt * P, lane, lo, hi);
     if (lane < LPR) {
       T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;
       store16(out + c0, pack<T>(lo));

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_
     lo[e] = __int_as_float(0x7f800000);   // +inf
     hi[e] = __int_as_float(0xff800000);   // -inf
   }
-  const int prow = rope.page_row ? rope.page_row[p] : -1;
+  const int prow = rope.page_row ? rope.page_row[rope_row_index(rope, b, n, p)] : -1;
 #pragma unroll
   for (int i = 0; i < MAX_LOADS; ++i) {
     const int s = rg + i * RPW;

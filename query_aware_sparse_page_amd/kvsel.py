@@ -58,7 +58,7 @@ class FreePagesDesc(ctypes.Structure):
 
 class RopeDesc(ctypes.Structure):
     _fields_ = [("cos", c_vp), ("sin", c_vp), ("page_row", c_vp), ("n_rows", c_i32),
-                ("row_step", c_i32)]
+                ("row_step", c_i32), ("per_sequence", c_i32)]
 
 
 class ReuseDesc(ctypes.Structure):
@@ -100,7 +100,7 @@ EXPORTS = {
 _lib = None
 
 
-ABI_VERSION = 4  # KVSEL_ABI_VERSION of include/kvsel.h
+ABI_VERSION = 5  # KVSEL_ABI_VERSION of include/kvsel.h
 
 
 def lib() -> ctypes.CDLL:
@@ -254,19 +254,22 @@ class PagedKV:
 
 @dataclass
 class Rope:
-    """Rotary table (fp32 [n_rows][D/2] cos and sin) and per-physical-page row (int32 [Npp])."""
+    """Rotary table (fp32 [n_rows][D/2] cos and sin) and the first table row of each page: int32
+    [Npp] by physical page, or, with ``per_sequence``, int32 [B][max_pages] by (sequence, logical
+    page), so that sequences sharing pages can place them at different positions."""
 
     cos: torch.Tensor
     sin: torch.Tensor
     page_row: torch.Tensor
     row_step: int = 0
+    per_sequence: bool = False
 
     def desc(self) -> RopeDesc:
         _dev(self.cos, "cos", torch.float32)
         _dev(self.sin, "sin", torch.float32)
         _dev(self.page_row, "page_row", torch.int32)
         return RopeDesc(self.cos.data_ptr(), self.sin.data_ptr(), self.page_row.data_ptr(),
-                        int(self.cos.shape[0]), int(self.row_step))
+                        int(self.cos.shape[0]), int(self.row_step), int(bool(self.per_sequence)))
 
 
 def _rope_ptr(rope: Optional[Rope]):

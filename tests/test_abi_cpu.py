@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(K):
 
 def test_version_and_status_strings(K):
     lib = K.lib()
-    assert lib.kvsel_abi_version() == K.ABI_VERSION == 4
+    assert lib.kvsel_abi_version() == K.ABI_VERSION == 5
     for code, tag in [(0, "KVSEL_OK"), (1, "INVALID_ARGUMENT"), (2, "UNSUPPORTED"),
                       (3, "WORKSPACE"), (4, "DEVICE"), (5, "LAUNCH"), (99, "UNKNOWN")]:
         assert tag in lib.kvsel_status_str(code).decode()
@@ -123,6 +123,9 @@ def test_call_argument_validation(K):
     # rope descriptors
     bad_rope = K.RopeDesc(0x10, 0x20, 0x30, 4, 2)
     assert lib.kvsel_rope_shift(ctypes.byref(d), ctypes.byref(bad_rope), p, None) == 1
+    # per-sequence rows cannot be materialized into shared physical pages
+    per_seq = K.RopeDesc(0x10, 0x20, 0x30, 4, 0, 1)
+    assert lib.kvsel_rope_shift(ctypes.byref(d), ctypes.byref(per_seq), p, None) == 2
     assert lib.kvsel_rope_shift(ctypes.byref(d), None, p, None) == 1
     assert lib.kvsel_rope_table(500000.0, 127, 0, 4, p, p, None) == 1
     assert lib.kvsel_rope_table(-1.0, 128, 0, 4, p, p, None) == 1

@@ -135,3 +135,42 @@ def test_composed_rotary_gather_equals_materialized(K):
     assert torch.equal(s_f, s_m)
     for a, b_, name in zip(fused, mat, ("sel", "cnt", "out", "lse")):
         assert torch.equal(a, b_), f"{name}: fused rotary gather differs from materialized keys"
+
+
+def test_shared_documents_at_different_offsets(K):
+    """Two sequences chain the same documents in different orders, so a shared page sits at a
+    different position in each; rows by (sequence, logical page) place it per sequence. Each
+    sequence's summaries and step outputs equal those of that sequence alone with rows by
+    physical page, bit for bit."""
+    w = W.composed(1231, B=2)
+    say(f"shared documents, per-sequence rotary rows: lens {w.seq_lens.tolist()}")
+    page_in_doc = w.extra["page_in_doc"].numpy()
+    doc_of_page = w.extra["doc_of_page"].numpy()
+    start = w.extra["doc_start"].numpy()  # [B][documents]
+    n_rows = int(start.max()) + max(w.extra["doc_lens"]) + w.P
+    cos, sin = K.rope_table(w.extra["theta"], w.D, 0, n_rows, torch.device("cuda"))
+    kv_raw = composed_kv(K, w)
+    enc = K.rope_shift(kv_raw, K.Rope(cos, sin, torch.from_numpy((page_in_doc * w.P).astype(np.int32)).cuda(), 1))
+    kv = K.PagedKV(enc, kv_raw.v_pool, kv_raw.page_table, kv_raw.seq_lens, w.Hq,
+                   page_fill=kv_raw.page_fill)
+    table = w.page_table.numpy()
+    rows = np.zeros(table.shape, dtype=np.int32)
+    for b in range(w.B):
+        for n in range(w.n_pages(b)):
+            rows[b, n] = start[b, doc_of_page[table[b, n]]]
+    per_seq = K.Rope(cos, sin, torch.from_numpy(rows).cuda(), 0, per_sequence=True)
+    q = w.q.cuda()
+    summ = K.build_summaries(kv, rope=per_seq)
+    both = K.select_attend(kv, summ, q, w.k, rope=per_seq)
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        phys = K.Rope(cos, sin, torch.from_numpy(start[b][doc_of_page].astype(np.int32)).cuda(), 0)
+        one = K.PagedKV(enc, kv_raw.v_pool, kv_raw.page_table[b:b + 1].contiguous(),
+                        kv_raw.seq_lens[b:b + 1].contiguous(), w.Hq, page_fill=kv_raw.page_fill)
+        s1 = K.build_summaries(one, rope=phys)
+        alone = K.select_attend(one, s1, q[b:b + 1].contiguous(), w.k, rope=phys)
+        torch.cuda.synchronize()
+        assert torch.equal(summ[b], s1[0]), f"sequence {b}: summaries"
+        for x, y, name in zip(both, alone, ("sel", "cnt", "out", "lse")):
+            assert torch.equal(x[b], y[0]), f"sequence {b}: {name}"
+    assert not torch.equal(both[2][0], both[2][1])  # the two placements differ
