@@ -162,8 +162,10 @@ __device__ void block_topk(const float* __restrict__ sc, const float* first, int
 
 template <typename T, int D, int G, int U, bool FP8>
 __global__ __launch_bounds__(SEL_THREADS) void score_kernel(SelectArgs a) {
-  // grid (Hkv, B, chunks): the indices need no division; KV heads vary fastest
-  score_block<T, D, G, SEL_WAVES, U, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  // grid (Hkv, B, chunks): the indices need no division; KV heads vary fastest. Chunks run in
+  // reverse order of z, so the blocks holding the sequences' last pages (the tail refresh, the
+  // longest chain) are dispatched first.
+  score_block<T, D, G, SEL_WAVES, U, FP8>(a, blockIdx.x, blockIdx.y, a.nchunks - 1 - blockIdx.z);
 }
 
 // block_topk_regs writing the ascending list to out (and used, when non-null), padded with -1.

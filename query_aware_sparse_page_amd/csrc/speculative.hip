@@ -31,8 +31,8 @@ template <typename T, int D, int P, bool ROPE, int G, bool FP8, int WAVES = Fuse
 __global__ __launch_bounds__(WAVES * 64) void spec_co_kernel(AttnArgs a, SelectArgs s) {
   using S = FusedShape<T, P>;
   const int j = blockIdx.x, b = blockIdx.y, z = blockIdx.z;  // grid (Hkv, B, chunks + 1 + splits)
-  if (z < s.nchunks) {
-    score_block<T, D, G, S::WAVES, 1, FP8>(s, j, b, z);
+  if (z < s.nchunks) {  // chunks in reverse order: the tail refresh's blocks are dispatched first
+    score_block<T, D, G, S::WAVES, 1, FP8>(s, j, b, s.nchunks - 1 - z);
     return;
   }
   if (z == s.nchunks) {  // the list's reuse decision
