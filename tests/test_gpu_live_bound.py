@@ -117,3 +117,39 @@ def test_length_past_the_bound(K):
     flags = K.check_inputs(kv)
     torch.cuda.synchronize()
     assert int(flags.item()) == 1  # KVSEL_CHECK_SEQ_LEN only
+
+
+def test_live_bound_fp8(K):
+    """fp8 pages with 1500 live pages in a 4096-page table: the fused selection with 8 keys per
+    thread and the fp8 co-launch, against the oracle over the dequantized cache."""
+    import oracle as O
+    c = dict(seed=821, B=2, Hq=32, Hkv=8, D=128, P=32, k=64, lens=[1500 * 32 - 3, 700 * 32 + 9],
+             dtype="bf16")
+    w = widened(W.custom(**c), 4096, 822)
+    say(f"live bound, fp8: lens {c['lens']}, table 4096")
+    scale = scale_of(w.D)
+    kc, ks = O.quantize_pages(w.k_pool)
+    vc, vs = O.quantize_pages(w.v_pool)
+    summ_ref = O.page_summaries_fp8(kc, ks, w.page_table, w.seq_lens, w.P)
+    sc = O.page_scores(w.q, summ_ref, w.page_table, w.seq_lens, w.P)
+    sel_ref, cnt_ref = O.top_pages(sc, w.seq_lens, w.P, w.k)
+    margins = O.selection_margin_ulps(sc, w.seq_lens, w.P, w.k)
+    out_ref, lse_ref = O.sparse_decode_attention(w.q, O.dequantize_pages(kc, ks),
+                                                 O.dequantize_pages(vc, vs), w.page_table,
+                                                 w.seq_lens, sel_ref, cnt_ref, w.P, scale)
+    kv = kv_of(K, w)
+    kv.max_seq_len = max(c["lens"])
+    kv8 = K.quantize_pages(kv)
+    q = w.q.cuda()
+    summ = K.build_summaries(kv8)
+    sel, cnt, out, lse = K.select_attend(kv8, summ, q, w.k, refresh_tail=True, scale=scale)
+    zi = torch.zeros((w.B, w.Hkv, w.k), dtype=torch.int32, device="cuda")
+    zc = torch.zeros((w.B, w.Hkv), dtype=torch.int32, device="cuda")
+    spec = K.speculative_step(kv8, summ, q, w.k, K.Reuse(q, zi, zc, 0.8, first_step=True),
+                              scale=scale)
+    torch.cuda.synchronize()
+    assert_summaries_equal(summ, summ_ref, w)
+    assert_selection_equal(sel, cnt, sel_ref, cnt_ref, margins)
+    assert_attention_close(out, lse, out_ref, lse_ref, "bf16")
+    for a, b_, name in ((spec[0], sel, "sel"), (spec[6], out, "out"), (spec[7], lse, "lse")):
+        assert torch.equal(a, b_), f"speculative step: {name} differs from kvsel_select_attend"
