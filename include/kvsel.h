@@ -271,8 +271,8 @@ kvsel_status kvsel_rope_shift(const kvsel_paged_kv* kv, const kvsel_rope* rope, 
  * scoring and the reuse decision; the next launch selects, and re-attends only the lists the
  * decision corrected, over their fresh pages; a last launch merges the splits. With
  * reuse->first_step every list is corrected and no attention runs over the previous pages.
- * Page tables wider than 8192 entries (4096 for bf16 with P 16) and k above 1024 run the two
- * calls serially instead, with the same outputs. One stream; capturable in a HIP graph.
+ * Page tables wider than 8192 entries (4096 for bf16 with P 16), k above 1024 and composed
+ * sequences (page_fill set) run the two calls serially instead, with the same outputs. One stream; capturable in a HIP graph.
  * sel_idx / sel_cnt and reuse->used_idx / used_cnt must not alias reuse->prev_idx / prev_cnt.
  * ws / ws_bytes: kvsel_workspace_bytes(kv, k, KVSEL_OP_SPECULATIVE_STEP, 0). Other arguments as
  * kvsel_score_topk and kvsel_sparse_decode_attn.

@@ -309,7 +309,6 @@ template <int D, int P, int WAVES, int TPW, bool ROPE, int SEL_C = 0, bool FP8 =
           bool FILL = false>
 __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j, int b, int split) {
   static_assert(!(FP8 && ROPE), "fp8 pools take no rotary gather");
-  static_assert(!(FILL && SEL_C > 0), "composed sequences take the separate selection");
   constexpr int TT = 32;       // tokens per tile
   constexpr int CB = D / 32;   // 32-channel blocks of q K^T
   constexpr int VB = D / 16;   // 16-channel blocks of P V
@@ -537,7 +536,6 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
 // ------------------------------------------------------------------------------------------
 template <int D, int P, int WAVES, int TPW, bool ROPE, int SEL_C = 0, bool FILL = false>
 __device__ __forceinline__ void attn_f32_block(const AttnArgs& a, int G, int j, int b, int split) {
-  static_assert(!(FILL && SEL_C > 0), "composed sequences take the separate selection");
   constexpr int TT = 16;       // tokens per tile
   constexpr int KC = D / 4;    // channels per lane in q K^T (4 lane groups)
   constexpr int KL = KC / 4;   // 16-byte loads per lane per token

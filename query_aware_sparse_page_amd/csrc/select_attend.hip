@@ -1,26 +1,27 @@
 // kvsel_select_attend: the scores (score kernel), then the attention launch with the selection
 // fused in (select_tiles: every block re-derives its list's top-k from the scores and keeps the
 // pages of its own split), then the merge. The fused launch uses the default split of FUSED_PPS
-// pages (block shapes in kvsel_attn.h). Other cases (many lists, a wide table, a k that needs
+// pages (block shapes in kvsel_attn.h); with pages that end early (page_fill) it is a separate
+// instantiation (FILL), taken at <= 4 keys per thread only. Other cases (many lists, a wide table, a k that needs
 // larger splits; select_attend_fused) run the two separate calls' launches instead.
 #include "kvsel_attn.h"
 
 namespace kvsel {
 
-template <int D, int P, int WAVES, int TPW, bool ROPE, int C>
+template <int D, int P, int WAVES, int TPW, bool ROPE, int C, bool FILL>
 __global__ __launch_bounds__(WAVES * 64) void fused_bf16_kernel(AttnArgs a, int G) {
   // grid (Hkv, B, splits)
-  attn_bf16_block<D, P, WAVES, TPW, ROPE, C>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
+  attn_bf16_block<D, P, WAVES, TPW, ROPE, C, false, FILL>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-template <int D, int P, int WAVES, int TPW, int C>
+template <int D, int P, int WAVES, int TPW, int C, bool FILL>
 __global__ __launch_bounds__(WAVES * 64) void fused_fp8_kernel(AttnArgs a, int G) {
-  attn_bf16_block<D, P, WAVES, TPW, false, C, true>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
+  attn_bf16_block<D, P, WAVES, TPW, false, C, true, FILL>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-template <int D, int P, int WAVES, int TPW, bool ROPE, int C>
+template <int D, int P, int WAVES, int TPW, bool ROPE, int C, bool FILL>
 __global__ __launch_bounds__(WAVES * 64) void fused_f32_kernel(AttnArgs a, int G) {
-  attn_f32_block<D, P, WAVES, TPW, ROPE, C>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
+  attn_f32_block<D, P, WAVES, TPW, ROPE, C, FILL>(a, G, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Score keys per thread of the fused select (the block holds the whole table row in registers).
@@ -30,9 +31,12 @@ static int fused_keys_per_thread(const LaunchKV& kv) {
   return c <= 1 ? 1 : c <= 4 ? 4 : c <= 8 ? 8 : c <= 16 ? 16 : c <= 32 ? 32 : 0;
 }
 
-bool fused_select_supported(const LaunchKV& kv, int k) {
-  if (kv.page_fill) return false;  // composed sequences: the separate launches
+static bool fused_shape(const LaunchKV& kv, int k) {
   return fused_keys_per_thread(kv) > 0 && attention_pages_per_split(kv, k, 0) == FUSED_PPS;
+}
+
+bool fused_select_supported(const LaunchKV& kv, int k) {
+  return !kv.page_fill && fused_shape(kv, k);  // composed sequences: kvsel_select_attend only
 }
 
 // Every block of a list repeats the list's select, so the fused form pays where that select is
@@ -41,31 +45,36 @@ bool fused_select_supported(const LaunchKV& kv, int k) {
 // 8 lists of 1024 pages 18.8 us against 20.2 us for the separate launches; 8 lists of 4096 pages
 // 30.6 against 30.5; 128 lists of <= 512 pages 37.5 against 36.5.
 bool select_attend_fused(const LaunchKV& kv, const RopeArgs&, int k) {
-  return fused_select_supported(kv, k) && fused_keys_per_thread(kv) <= 4 &&
+  return fused_shape(kv, k) && fused_keys_per_thread(kv) <= 4 &&
          kv.B * kv.Hkv < SELECT_ONE_LAUNCH_MIN_LISTS;
 }
 
-template <typename T, int D, int P, bool ROPE, int C>
+template <typename T, int D, int P, bool ROPE, int C, bool FILL>
 static void launch_fused_c(const AttnArgs& a, int G, hipStream_t stream) {
   using S = FusedShape<T, P>;
   const dim3 grid(a.Hkv, a.nlists / a.Hkv, a.nsplit);
   const dim3 block(S::WAVES * 64);
   if constexpr (sizeof(T) == 1)
-    hipLaunchKernelGGL((fused_fp8_kernel<D, P, S::WAVES, S::TPW, C>), grid, block, 0, stream, a, G);
+    hipLaunchKernelGGL((fused_fp8_kernel<D, P, S::WAVES, S::TPW, C, FILL>), grid, block, 0, stream, a, G);
   else if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((fused_bf16_kernel<D, P, S::WAVES, S::TPW, ROPE, C>), grid, block, 0, stream, a, G);
+    hipLaunchKernelGGL((fused_bf16_kernel<D, P, S::WAVES, S::TPW, ROPE, C, FILL>), grid, block, 0, stream, a, G);
   else
-    hipLaunchKernelGGL((fused_f32_kernel<D, P, S::WAVES, S::TPW, ROPE, C>), grid, block, 0, stream, a, G);
+    hipLaunchKernelGGL((fused_f32_kernel<D, P, S::WAVES, S::TPW, ROPE, C, FILL>), grid, block, 0, stream, a, G);
 }
 
 template <typename T, int D, int P, bool ROPE>
 static void launch_fused_r(int c, const AttnArgs& a, int G, hipStream_t stream) {
+  if (a.page_fill) {  // c <= 4 (launch_fused_select checks)
+    if (c == 1) launch_fused_c<T, D, P, ROPE, 1, true>(a, G, stream);
+    else launch_fused_c<T, D, P, ROPE, 4, true>(a, G, stream);
+    return;
+  }
   switch (c) {
-    case 1: launch_fused_c<T, D, P, ROPE, 1>(a, G, stream); break;
-    case 4: launch_fused_c<T, D, P, ROPE, 4>(a, G, stream); break;
-    case 8: launch_fused_c<T, D, P, ROPE, 8>(a, G, stream); break;
-    case 16: launch_fused_c<T, D, P, ROPE, 16>(a, G, stream); break;
-    default: launch_fused_c<T, D, P, ROPE, 32>(a, G, stream); break;
+    case 1: launch_fused_c<T, D, P, ROPE, 1, false>(a, G, stream); break;
+    case 4: launch_fused_c<T, D, P, ROPE, 4, false>(a, G, stream); break;
+    case 8: launch_fused_c<T, D, P, ROPE, 8, false>(a, G, stream); break;
+    case 16: launch_fused_c<T, D, P, ROPE, 16, false>(a, G, stream); break;
+    default: launch_fused_c<T, D, P, ROPE, 32, false>(a, G, stream); break;
   }
 }
 
@@ -88,6 +97,7 @@ static void launch_fused_p(int P, int c, const AttnArgs& a, int G, bool rope, hi
 hipError_t launch_fused_select(const LaunchKV& kv, const AttnArgs& a, bool rope,
                                hipStream_t stream) {
   const int c = fused_keys_per_thread(kv);
+  if (a.page_fill && c > 4) return hipErrorInvalidValue;  // no such instantiation
   if (kv.dtype == 2) {
     if (kv.D == 64) launch_fused_p<fp8_t, 64>(kv.P, c, a, kv.G, false, stream);
     else launch_fused_p<fp8_t, 128>(kv.P, c, a, kv.G, false, stream);
