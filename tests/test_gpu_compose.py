@@ -56,6 +56,12 @@ CASES = [
     dict(name="bf16-P16-G8-B1", kw=dict(seed=1203, doc_lens=(1000, 17, 333, 5, 64), P=16, B=1,
                                         Hq=16, Hkv=2, D=128, k=24), fp8=False),
     dict(name="fp8-P32-B2", kw=dict(seed=1204, B=2), fp8=True),
+    # wider tables: the fused selection's fill variants at 4 keys per thread for fp32 and for bf16
+    # with P 16 (356 and 174 pages)
+    dict(name="f32-P16-D64-wide", kw=dict(seed=1205, doc_lens=(3000, 517, 1400, 33, 700), P=16,
+                                          B=1, Hq=8, Hkv=4, D=64, k=24, dtype="f32"), fp8=False),
+    dict(name="bf16-P16-G8-wide", kw=dict(seed=1206, doc_lens=(1500, 17, 900, 333), P=16, B=2,
+                                          Hq=16, Hkv=2, D=128, k=24), fp8=False),
 ]
 
 
