@@ -231,6 +231,28 @@ __device__ __forceinline__ void rope_pair(float& x1, float& x2, float c, float s
   x2 = round_to_elem<T>(y2);
 }
 
+// The rotation of rope_pair without its rounding (the gather packs the results once, below).
+__device__ __forceinline__ void rope_pair_f32(float& x1, float& x2, float c, float s) {
+  const float y1 = rot_sub(rot_mul(x1, c), rot_mul(x2, s));
+  const float y2 = rot_add(rot_mul(x2, c), rot_mul(x1, s));
+  x1 = y1;
+  x2 = y2;
+}
+
+// 8 fp32 values to 8 bf16 by gfx950's packed conversion (round to nearest even: for every finite
+// value the bits of round_to_elem<bf16_t>, one instruction per pair instead of the integer
+// sequence).
+__device__ __forceinline__ uint4 pack_bf16x8_rne(const float* f) {
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2_v v = {(__bf16)f[2 * i], (__bf16)f[2 * i + 1]};
+    __builtin_memcpy(&w[i], &v, 4);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
   bf16x8_t r;
   __builtin_memcpy(&r, &v, 16);
@@ -454,9 +476,9 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
             unpack<float>(load16(sr), sv);
             unpack<float>(load16(sr + 4), sv + 4);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) rope_pair<bf16_t>(x1[e], x2[e], cv[e], sv[e]);
-            kraw[t][h][cb] = pack_bf16x8(x1);
-            kraw[t][h][cb + CB / 2] = pack_bf16x8(x2);
+            for (int e = 0; e < 8; ++e) rope_pair_f32(x1[e], x2[e], cv[e], sv[e]);
+            kraw[t][h][cb] = pack_bf16x8_rne(x1);
+            kraw[t][h][cb + CB / 2] = pack_bf16x8_rne(x2);
           }
         }
       }
@@ -490,21 +512,30 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
   for (int vb = 0; vb < VB; ++vb) o[vb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    float p[8];
+    // P enters the MFMA as bf16: normalize by the sum of the rounded values, so the weights
+    // applied to V sum to one exactly (fp8: l sums bf16(p), the MFMA takes bf16(p * v_scale))
+    float pf[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (FP8) {
-        const float pf = z[t][e] == NEG_INF ? 0.0f : __expf(z[t][e] - m);
-        l += round_to_elem<bf16_t>(pf);
-        p[e] = round_to_elem<bf16_t>(pf * vsc[t]);
-      } else {
-        // P enters the MFMA as bf16: normalize by the sum of the rounded values, so the weights
-        // applied to V sum to one exactly
-        p[e] = z[t][e] == NEG_INF ? 0.0f : round_to_elem<bf16_t>(__expf(z[t][e] - m));
-        l += p[e];
+    for (int e = 0; e < 8; ++e) pf[e] = z[t][e] == NEG_INF ? 0.0f : __expf(z[t][e] - m);
+    uint4 pb;
+    if constexpr (FP8) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = pf[e] * vsc[t];
+      pb = pack_bf16x8_rne(pv);
+    } else {
+      pb = pack_bf16x8_rne(pf);
+    }
+    {
+      const uint4 lb = FP8 ? pack_bf16x8_rne(pf) : pb;
+      const uint32_t lw[4] = {lb.x, lb.y, lb.z, lb.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        l += __uint_as_float(lw[i] << 16);
+        l += __uint_as_float(lw[i] & 0xffff0000u);
       }
     }
-    const bf16x8_t pa = as_bf16x8(pack_bf16x8(p));
+    const bf16x8_t pa = as_bf16x8(pb);
     const bool partial = vmask[t] != 0xff;  // zero invalid slots (0 * NaN poison is NaN)
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb) {
