@@ -50,7 +50,9 @@ template <>
 __device__ __forceinline__ float round_to_elem<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ float round_to_elem<bf16_t>(float x) {
-  return bf16_to_f32(f32_to_bf16_bits(x));
+  // gfx950's v_cvt_pk_bf16_f32: round to nearest even, the bits of f32_to_bf16_bits for every
+  // finite value, in one instruction
+  return (float)(__bf16)x;
 }
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
