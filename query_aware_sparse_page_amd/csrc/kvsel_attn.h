@@ -661,7 +661,7 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs& a, int G, int j, 
       const int row = krow[t];
       float pv[KC];
 #pragma unroll
-      for (int e = 0; e < KC; ++e) pv[e] = __shfl_xor(kv[e], 32);
+      for (int e = 0; e < KC; ++e) pv[e] = lane_xor_f32(kv[e], 32);
       if (row >= 0) {
         const bool first = q4 < 2;
         const int i0 = first ? KC * q4 : KC * q4 - D / 2;

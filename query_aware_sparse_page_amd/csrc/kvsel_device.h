@@ -136,6 +136,8 @@ __device__ __forceinline__ float rot_add(float a, float b) {
   return a + b;
 }
 
+__device__ __forceinline__ float lane_xor_f32(float v, int m);  // defined below
+
 template <typename T, int D>
 __device__ __forceinline__ void rope_rotate_slice(float* x, int c0, int row, const float* __restrict__ cos_t,
                                                   const float* __restrict__ sin_t) {
@@ -144,7 +146,7 @@ __device__ __forceinline__ void rope_rotate_slice(float* x, int c0, int row, con
   constexpr int HALF = D / 2;
   float partner[VEC];
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) partner[e] = __shfl_xor(x[e], LPR / 2);
+  for (int e = 0; e < VEC; ++e) partner[e] = lane_xor_f32(x[e], LPR / 2);
   if (row < 0) return;
   const bool first = c0 < HALF;
   const int i0 = first ? c0 : c0 - HALF;
@@ -212,6 +214,13 @@ __device__ __forceinline__ uint32_t xor32_u32(uint32_t v) {
 }
 __device__ __forceinline__ float xor16_f32(float v) { return __uint_as_float(xor16_u32(__float_as_uint(v))); }
 __device__ __forceinline__ float xor32_f32(float v) { return __uint_as_float(xor32_u32(__float_as_uint(v))); }
+// The value of lane (lane ^ m), m a power of two fixed at compile time after unrolling: the lane
+// swaps above for m = 16 and 32, DPP row_ror:8 for m = 8 (a rotation by 8 inside a row of 16
+// lanes is lane ^ 8), ds_bpermute otherwise.
+__device__ __forceinline__ float lane_xor_f32(float v, int m) {
+  if (m == 8) return __uint_as_float(dpp_u32<0x128>(0u, __float_as_uint(v)));
+  return m == 16 ? xor16_f32(v) : m == 32 ? xor32_f32(v) : __shfl_xor(v, m);
+}
 
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {

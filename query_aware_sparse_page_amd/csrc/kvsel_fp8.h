@@ -129,8 +129,8 @@ __device__ __forceinline__ void tile_minmax_fp8(const uint8_t* tile, int valid,
   for (int m = LPR; m < 64; m <<= 1) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      lo[e] = fminf(lo[e], __shfl_xor(lo[e], m));
-      hi[e] = fmaxf(hi[e], __shfl_xor(hi[e], m));
+      lo[e] = fminf(lo[e], lane_xor_f32(lo[e], m));
+      hi[e] = fmaxf(hi[e], lane_xor_f32(hi[e], m));
     }
   }
   const double sd = (double)scale;

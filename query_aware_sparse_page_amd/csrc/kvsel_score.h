@@ -76,8 +76,8 @@ __device__ __forceinline__ void tile_minmax(const T* tile, int valid, const int3
   for (int m = LPR; m < 64; m <<= 1) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      lo[e] = fminf(lo[e], __shfl_xor(lo[e], m));
-      hi[e] = fmaxf(hi[e], __shfl_xor(hi[e], m));
+      lo[e] = fminf(lo[e], lane_xor_f32(lo[e], m));
+      hi[e] = fmaxf(hi[e], lane_xor_f32(hi[e], m));
     }
   }
 }

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(QUANT_WAVES * 64) void quantize_kernel(const T* __r
     for (int e = 0; e < VEC; ++e) amax = fmaxf(amax, fabsf(x[e]));
   }
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, lane_xor_f32(amax, m));
   const float s = amax > 0.0f ? __fdiv_rn(amax, FP8_MAX) : 1.0f;
   if (lane == 0) scale[tile] = s;
   uint8_t* out = codes + tile * N;

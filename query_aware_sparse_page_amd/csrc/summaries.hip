@@ -100,8 +100,8 @@ __global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_
   for (int m = LPR; m < 64; m <<= 1) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      lo[e] = fminf(lo[e], __shfl_xor(lo[e], m));
-      hi[e] = fmaxf(hi[e], __shfl_xor(hi[e], m));
+      lo[e] = fminf(lo[e], lane_xor_f32(lo[e], m));
+      hi[e] = fmaxf(hi[e], lane_xor_f32(hi[e], m));
     }
   }
   if (rg == 0) {
