@@ -354,6 +354,112 @@ def test_planted_topk_mistakes_are_caught(mistake):
     assert not check_topk(broken, _topk_cases())
 
 
+# The k-boundary margin (selection_margin_ulps) decides which fp32 lists the parity tests compare
+# by a band check instead of bit for bit, so it is pinned on its own: the distance between the
+# k-th and (k+1)-th best score is counted as np.nextafter steps (an fp32 walk that knows nothing
+# of the oracle's integer mapping), with +0 and -0 one value.
+
+def _steps_between(lo, hi):
+    """nextafter steps from fp32 lo up to fp32 hi (lo <= hi), -0 and +0 counted as one value."""
+    lo, hi = np.float32(lo), np.float32(hi)
+    n = 0
+    x = lo
+    while x != hi:  # -0 == +0 compares equal, so the two zeros are one value
+        x = np.nextafter(x, np.float32(np.inf))
+        n += 1
+        assert n < 10_000
+    return n
+
+
+def brute_margin(scores, k):
+    """Steps between the k-th and (k+1)-th largest of a list; None when it has <= k entries."""
+    vals = sorted((np.float32(v) for v in scores), key=float, reverse=True)
+    if len(vals) <= k:
+        return None
+    return _steps_between(vals[k], vals[k - 1])
+
+
+def _margin_cases():
+    f = np.float32
+
+    def up(x, n):  # n nextafter steps up from fp32 x
+        x = f(x)
+        for _ in range(n):
+            x = np.nextafter(x, f(np.inf))
+        return x
+
+    tiny = np.nextafter(f(0), f(1))  # smallest positive subnormal
+    cases = [
+        ([1.0, 2.0, 2.0, 0.5], 1),                           # exact tie at the boundary -> 0
+        ([f(1.0), up(f(1.0), 1), f(0.0)], 1),               # adjacent floats -> 1
+        ([f(3.0), up(f(3.0), 2), f(-1.0)], 1),              # two ulps -> 2
+        ([f(-0.0), f(0.0), f(5.0)], 2),                     # -0 against +0 -> a tie
+        ([tiny, -tiny, f(9.0)], 2),                         # across zero: -tiny, 0, tiny -> 2
+        ([up(f(7.0), 1), up(f(7.0), 6), f(7.0), up(f(7.0), 7), f(1.0)], 2),  # 5 between k and k+1
+        ([f(1.0), f(2.0)], 2),                              # N == k: no boundary
+        ([f(1.0)], 3),                                      # N < k
+    ]
+    rng = np.random.Generator(np.random.PCG64(17))
+    for _ in range(40):  # random lists a few ulps apart around random bases, either sign
+        base = f(rng.standard_normal() * 10.0 ** int(rng.integers(-3, 4)))
+        N = int(rng.integers(2, 12))
+        vals = [up(base, int(s)) for s in rng.integers(0, 12, size=N)]
+        cases.append((vals, int(rng.integers(1, N + 2))))
+    return cases
+
+
+def check_margin(fn):
+    for vals, k in _margin_cases():
+        sc = np.asarray(vals, dtype=np.float32)[None, None, :]
+        got = int(fn(sc, torch.tensor([len(vals)]), 1, k)[0, 0])
+        want = brute_margin(vals, k)
+        if want is None:
+            if got < (1 << 40):
+                return False
+        elif got != want:
+            return False
+    return True
+
+
+def test_selection_margin_matches_nextafter_walk():
+    assert check_margin(O.selection_margin_ulps)
+    # the hand-built cases alone, by name
+    m = lambda vals, k: int(O.selection_margin_ulps(  # noqa: E731
+        np.asarray(vals, np.float32)[None, None], torch.tensor([len(vals)]), 1, k)[0, 0])
+    assert m([1.0, 2.0, 2.0, 0.5], 1) == 0
+    assert m([1.0, float(np.nextafter(np.float32(1), np.float32(2))), 0.0], 1) == 1
+    assert m([-0.0, 0.0, 5.0], 2) == 0
+    assert m([1.0, 2.0], 2) >= 1 << 40
+
+
+@pytest.mark.parametrize("mistake", ["k_plus_1", "k_minus_1", "always_0", "raw_bits",
+                                     "no_sentinel"])
+def test_planted_margin_mistakes_are_caught(mistake):
+    def broken(scores, seq_lens, P, k):
+        sc = np.asarray(scores, dtype=np.float32)
+        N = sc.shape[2]
+        out = np.full((1, 1), 1 << 40, dtype=np.int64)
+        if N <= k:
+            if mistake == "no_sentinel":
+                out[0, 0] = 0
+            return out
+        u = np.where(sc[0, 0] == 0, np.float32(0), sc[0, 0]).view(np.int32).astype(np.int64)
+        if mistake != "raw_bits":  # raw_bits: two's-complement order, wrong below zero
+            u = np.where(u < 0, -(u & 0x7FFFFFFF), u)
+        o = np.sort(u)[::-1]
+        if mistake == "k_plus_1":
+            out[0, 0] = o[k] - o[k + 1] if k + 1 < N else o[k]
+        elif mistake == "k_minus_1":
+            out[0, 0] = o[k - 2] - o[k - 1] if k >= 2 else o[0]
+        elif mistake == "always_0":
+            out[0, 0] = 0
+        else:
+            out[0, 0] = o[k - 1] - o[k]
+        return out
+
+    assert not check_margin(broken)
+
+
 # ----------------------------------------------------------------------------------------------
 # a4 reuse / correction
 # ----------------------------------------------------------------------------------------------
