@@ -27,30 +27,71 @@ __global__ __launch_bounds__(WAVES * 64) void attn_f32_kernel(AttnArgs a, int G)
 }
 
 // ------------------------------------------------------------------------------------------
-// merge: one block per (list, query head of the group), one thread per channel. The partial
-// accumulators of up to MERGE_CHUNK splits and every (m, l) pair are loaded in one round, so the
-// merge costs one memory round trip for up to MERGE_CHUNK splits.
+// merge: one block per (list, query head of the group), one thread per channel.
+//
+// attn_merge_kernel (up to 64 splits): every thread loads its channel's accumulator of each split
+// (MC >= nsplit loads, clamped indices, block-uniform row bases) and lane s of every wave loads
+// split s's (m, l, lu), all in one memory round trip. Each wave then forms the split weights
+// lane-parallel: M = max m_s and the sums of l_s and lu_s weighted by e^(m_s - M) are wave-wide
+// reductions on DPP and the lane swaps, and the weights reach the wave's lanes through LDS, so no
+// block barrier is needed. Splits are combined in split order, as in the wide form.
+// attn_merge_wide_kernel (more splits): the (m, l, lu) of every split through LDS, accumulators in
+// rounds of MERGE_CHUNK splits.
 // ------------------------------------------------------------------------------------------
 constexpr int MERGE_CHUNK = 32;
 
-template <typename T, int D>
+template <typename T, int D, int MC>
 __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int G) {
+  static_assert(MC <= 64, "one split per lane");
   const float NEG_INF = __int_as_float(0xff800000);
   // grid (Hkv, G, B): KV heads vary fastest, as in the attention grid, so a list's merge blocks
   // are dispatched to the XCD that ran its splits (round-robin placement)
   const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int list = b * a.Hkv + j;
+  const int d = threadIdx.x, lane = d & 63, w = d >> 6;
+  const int Hq = a.Hkv * G;
+  const int ns = a.nsplit;
+  const float4* ml = a.part_ml + (size_t)list * ns * G + g;
+  const float* pa = a.part_acc + ((size_t)list * ns * G + g) * D;  // block-uniform base
+  const int GD = G * D;
+  const float4 mv = ml[(size_t)min(lane, ns - 1) * G];
+  float v[MC];
+#pragma unroll
+  for (int u = 0; u < MC; ++u) v[u] = (pa + min(u, ns - 1) * GD)[d];
+  __builtin_amdgcn_sched_barrier(0);
+  const bool ok = lane < ns && mv.x != NEG_INF;  // a split with no valid token has m = -inf
+  const float M = wave_allreduce_f32(ok ? mv.x : NEG_INF, [](float x, float y) { return fmaxf(x, y); });
+  const float f = ok ? __expf(mv.x - M) : 0.0f;
+  const float L = wave_allreduce_f32(ok ? mv.y * f : 0.0f, [](float x, float y) { return x + y; });
+  const float LU = wave_allreduce_f32(ok ? mv.z * f : 0.0f, [](float x, float y) { return x + y; });
+  __shared__ float s_f[D / 64][64];  // this wave's split weights (lane s: split s)
+  s_f[w][lane] = f;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float A = 0.0f;
+#pragma unroll
+  for (int u = 0; u < MC; ++u) A = fmaf(v[u], s_f[w][u], A);  // weight 0 past the last split
+  const size_t o = ((size_t)b * Hq + j * G + g) * D + d;
+  store_elem<T>((T*)a.out, o, M == NEG_INF ? 0.0f : A / L);
+  if (d == 0 && a.lse) a.lse[(size_t)b * Hq + j * G + g] = M == NEG_INF ? NEG_INF : M + logf(LU);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(D) void attn_merge_wide_kernel(AttnArgs a, int G) {
+  const float NEG_INF = __int_as_float(0xff800000);
+  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;  // grid (Hkv, G, B)
+  const int list = b * a.Hkv + j;
   const int d = threadIdx.x;
   const int Hq = a.Hkv * G;
   const int ns = a.nsplit;
-  __shared__ float s_m[ATT_MAX_SPLITS], s_l[ATT_MAX_SPLITS];
-  const float2* ml = a.part_ml + (size_t)list * ns * G + g;
+  __shared__ float s_m[ATT_MAX_SPLITS], s_l[ATT_MAX_SPLITS], s_lu[ATT_MAX_SPLITS];
+  const float4* ml = a.part_ml + (size_t)list * ns * G + g;
   const float* pa = a.part_acc + ((size_t)list * ns * G + g) * D;  // block-uniform base
   const int GD = G * D;
   // one round of unconditional loads with clamped indices (a conditional load would make the
-  // compiler wait for each one before the next); each split's row address is block-uniform, so
-  // a load is a scalar base plus this thread's channel offset
-  const float2 mv = ml[min(d, ns - 1) * G];
+  // compiler wait for each one before the next)
+  const float4 mv = ml[min(d, ns - 1) * G];
   float v[MERGE_CHUNK];
 #pragma unroll
   for (int u = 0; u < MERGE_CHUNK; ++u) v[u] = (pa + min(u, ns - 1) * GD)[d];
@@ -58,11 +99,13 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int G) {
   if (d < ns) {
     s_m[d] = mv.x;
     s_l[d] = mv.y;
+    s_lu[d] = mv.z;
   }
   for (int s = d + D; s < ns; s += D) {  // more splits than threads
-    const float2 x = ml[(size_t)s * G];
+    const float4 x = ml[(size_t)s * G];
     s_m[s] = x.x;
     s_l[s] = x.y;
+    s_lu[s] = x.z;
   }
   __syncthreads();
   float M = NEG_INF;
@@ -73,7 +116,7 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int G) {
     if (d == 0 && a.lse) a.lse[(size_t)b * Hq + j * G + g] = NEG_INF;
     return;
   }
-  float L = 0.0f, A = 0.0f;
+  float L = 0.0f, LU = 0.0f, A = 0.0f;
   for (int s0 = 0; s0 < ns; s0 += MERGE_CHUNK) {
     if (s0 > 0) {
 #pragma unroll
@@ -85,12 +128,13 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int G) {
       if (s < ns && s_m[s] != NEG_INF) {
         const float f = __expf(s_m[s] - M);
         L = fmaf(s_l[s], f, L);
+        LU = fmaf(s_lu[s], f, LU);
         A = fmaf(v[u], f, A);
       }
     }
   }
   store_elem<T>((T*)a.out, o, A / L);
-  if (d == 0 && a.lse) a.lse[(size_t)b * Hq + j * G + g] = M + logf(L);
+  if (d == 0 && a.lse) a.lse[(size_t)b * Hq + j * G + g] = M + logf(LU);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -132,7 +176,7 @@ size_t attention_workspace(const LaunchKV& kv, int k, int pages_per_split) {
   const size_t nsplit = (size_t)((k + pps - 1) / pps);
   if (nsplit <= 1) return 0;
   const size_t parts = (size_t)kv.B * kv.Hkv * nsplit * kv.G;
-  return align256(parts * kv.D * sizeof(float)) + parts * sizeof(float2);
+  return align256(parts * kv.D * sizeof(float)) + parts * sizeof(float4);
 }
 
 template <typename T, int D, int P, int WAVES, int TPW, bool FILL>
@@ -172,8 +216,17 @@ static hipError_t launch_tiles(int tiles, const AttnArgs& a, int G, bool rope, i
   }
   if (!(parts & 2) || a.nsplit == 1) return hipSuccess;
   using OT = std::conditional_t<sizeof(T) == 1, bf16_t, T>;  // fp8 pools: bf16 outputs
-  hipLaunchKernelGGL((attn_merge_kernel<OT, D>), dim3(a.Hkv, G, a.nlists / a.Hkv), dim3(D), 0, stream,
-                     a, G);
+  const dim3 grid(a.Hkv, G, a.nlists / a.Hkv);
+  if (a.nsplit <= 8)
+    hipLaunchKernelGGL((attn_merge_kernel<OT, D, 8>), grid, dim3(D), 0, stream, a, G);
+  else if (a.nsplit <= 16)
+    hipLaunchKernelGGL((attn_merge_kernel<OT, D, 16>), grid, dim3(D), 0, stream, a, G);
+  else if (a.nsplit <= 32)
+    hipLaunchKernelGGL((attn_merge_kernel<OT, D, 32>), grid, dim3(D), 0, stream, a, G);
+  else if (a.nsplit <= 64)
+    hipLaunchKernelGGL((attn_merge_kernel<OT, D, 64>), grid, dim3(D), 0, stream, a, G);
+  else
+    hipLaunchKernelGGL((attn_merge_wide_kernel<OT, D>), grid, dim3(D), 0, stream, a, G);
   return hipGetLastError();
 }
 
@@ -230,7 +283,7 @@ AttnArgs attn_args(const LaunchKV& kv, const RopeArgs& rope, const void* q, cons
   if (a.nsplit > 1) {
     const size_t parts = (size_t)a.nlists * a.nsplit * kv.G;
     a.part_acc = (float*)ws;
-    a.part_ml = (float2*)((char*)ws + align256(parts * kv.D * sizeof(float)));
+    a.part_ml = (float4*)((char*)ws + align256(parts * kv.D * sizeof(float)));
   }
   a.out = out;
   a.lse = lse;

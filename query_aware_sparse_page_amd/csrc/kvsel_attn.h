@@ -24,10 +24,13 @@
 //   4*q4 + s (a lane's 16-byte V load covers its tokens).
 //
 // Softmax: per wave a two-pass max / exp over its tiles (the max needs 2 cross-lane steps),
-// l accumulated per lane, O accumulated in the MFMA accumulators; the waves of a block merge
-// through LDS. One split: the block writes out / lse directly. Otherwise it writes its
-// (acc[G][D], m, l) partial and attn_merge_kernel (one block per list) combines the partials in
-// split order: M = max m_s, out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
+// two row sums accumulated per lane -- l of the probabilities as they enter P V (bf16-rounded
+// in the bf16 body, so the weights applied to V sum to one exactly) and lu of the unrounded fp32
+// probabilities, which gives lse -- and O accumulated in the MFMA accumulators; the waves of a
+// block merge through LDS. One split: the block writes out / lse directly. Otherwise it writes
+// its (acc[G][D], m, l, lu) partial and attn_merge_kernel (one block per list) combines the
+// partials in split order: M = max m_s, out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s,
+// lse = M + ln sum_s e^(m_s - M) lu_s.
 // Invalid token slots (past a sequence's end, or past the list's count) load as zeros and get
 // probability 0, so poisoned padding never reaches the accumulators.
 #pragma once
@@ -62,7 +65,7 @@ struct AttnArgs {
   const int32_t* page_fill;  // [Npp] valid slots per physical page, or null (every page full)
   RopeArgs rope;
   float* part_acc;   // [nlists][nsplit][G][D]
-  float2* part_ml;   // [nlists][nsplit][G]
+  float4* part_ml;   // [nlists][nsplit][G]: (m, l, lu, unused)
   void* out;
   float* lse;
   // fused selection only: the scores, and the selection outputs written by split 0
@@ -167,7 +170,10 @@ __device__ __forceinline__ bool select_tiles(const AttnArgs& a, int list, int b,
   const int L = a.seq_lens[b];
   if (!corr && split != 0) return false;  // block-uniform
   const int N = L > 0 ? min((L + P - 1) / P, a.maxn) : 0;
-  if (tid < a.pps) {
+  const int first = split * a.pps;
+  // positions of this split past the selection's length are never filled: clear those (the
+  // others are written exactly once by the select, so no barrier is needed before it)
+  if (tid < a.pps && first + tid >= min(N, a.k)) {
     ss.page[tid] = 0;
     ss.valid[tid] = 0;
     ss.lpage[tid] = 0;
@@ -175,8 +181,6 @@ __device__ __forceinline__ bool select_tiles(const AttnArgs& a, int list, int b,
   uint32_t key[C];
 #pragma unroll
   for (int u = 0; u < C; ++u) key[u] = score_key(v[u]);
-  __syncthreads();  // positions cleared before any is filled
-  const int first = split * a.pps;
   const bool writer = split == 0 && a.sel_out != nullptr;
   const bool spec = a.reuse.q_prev != nullptr;
   int32_t* out = a.sel_out + (size_t)list * a.k;
@@ -278,40 +282,51 @@ __device__ __forceinline__ uint4 mask_f32x4(const uint4& v, int keep) {
 
 constexpr int ATT_MAX_G = 8;
 
-// Block-level merge of the waves' (m, l, O) and the write of the block's result.
+// Block-level merge of the waves' (m, l, lu, O) and the write of the block's result. The weight
+// e^(m_v - M) of each (wave, head) is computed once, by G threads, before the channels combine.
+// A wave without a valid token has m = -inf and O = 0, and gets weight 0.
 template <typename T, int D, int WAVES>
 __device__ __forceinline__ void finish_block(const AttnArgs& a, int G, int list, int split, int b,
                                              int j, float (*s_m)[ATT_MAX_G],
-                                             float (*s_l)[ATT_MAX_G],
+                                             float (*s_l)[ATT_MAX_G], float (*s_lu)[ATT_MAX_G],
                                              float (*s_o)[ATT_MAX_G][D]) {
   const float NEG_INF = __int_as_float(0xff800000);
   const int Hq = a.Hkv * G;
+  __shared__ float s_w[WAVES][ATT_MAX_G], s_blk[3][ATT_MAX_G];  // weights; the block's M, l, lu
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += WAVES * 64) {
-    const int g = idx / D, d = idx % D;
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
     float Mx = s_m[0][g];
 #pragma unroll
     for (int v = 1; v < WAVES; ++v) Mx = fmaxf(Mx, s_m[v][g]);
-    float Ls = 0.0f, A = 0.0f;
-    if (Mx != NEG_INF) {
+    float Ls = 0.0f, Lu = 0.0f;
 #pragma unroll
-      for (int v = 0; v < WAVES; ++v) {
-        if (s_m[v][g] != NEG_INF) {
-          const float f = __expf(s_m[v][g] - Mx);
-          Ls = fmaf(s_l[v][g], f, Ls);
-          A = fmaf(s_o[v][g][d], f, A);
-        }
-      }
+    for (int v = 0; v < WAVES; ++v) {
+      const float f = (Mx != NEG_INF && s_m[v][g] != NEG_INF) ? __expf(s_m[v][g] - Mx) : 0.0f;
+      s_w[v][g] = f;
+      Ls = fmaf(s_l[v][g], f, Ls);
+      Lu = fmaf(s_lu[v][g], f, Lu);
     }
+    s_blk[0][g] = Mx;
+    s_blk[1][g] = Ls;
+    s_blk[2][g] = Lu;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += WAVES * 64) {
+    const int g = idx / D, d = idx % D;
+    float A = 0.0f;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) A = fmaf(s_o[v][g][d], s_w[v][g], A);
+    const float Mx = s_blk[0][g], Ls = s_blk[1][g], Lu = s_blk[2][g];
     if (a.nsplit == 1) {
       const size_t o = ((size_t)b * Hq + j * G + g) * D + d;
       store_elem<T>((T*)a.out, o, Mx == NEG_INF ? 0.0f : A / Ls);
       if (d == 0 && a.lse)
-        a.lse[(size_t)b * Hq + j * G + g] = Mx == NEG_INF ? NEG_INF : Mx + logf(Ls);
+        a.lse[(size_t)b * Hq + j * G + g] = Mx == NEG_INF ? NEG_INF : Mx + logf(Lu);
     } else {
       const size_t ps = ((size_t)list * a.nsplit + split) * G + g;
       a.part_acc[ps * D + d] = A;
-      if (d == 0) a.part_ml[ps] = make_float2(Mx, Ls);
+      if (d == 0) a.part_ml[ps] = make_float4(Mx, Ls, Lu, 0.0f);
     }
   }
 }
@@ -506,17 +521,21 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
   }
   m = fmaxf(m, xor16_f32(m));
   m = fmaxf(m, xor32_f32(m));
-  float l = 0.0f;
+  float l = 0.0f, lu = 0.0f;
   f32x4_t o[VB];
 #pragma unroll
   for (int vb = 0; vb < VB; ++vb) o[vb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     // P enters the MFMA as bf16: normalize by the sum of the rounded values, so the weights
-    // applied to V sum to one exactly (fp8: l sums bf16(p), the MFMA takes bf16(p * v_scale))
+    // applied to V sum to one exactly (fp8: l sums bf16(p), the MFMA takes bf16(p * v_scale));
+    // lse takes the sum of the unrounded values
     float pf[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pf[e] = z[t][e] == NEG_INF ? 0.0f : __expf(z[t][e] - m);
+    for (int e = 0; e < 8; ++e) {
+      pf[e] = z[t][e] == NEG_INF ? 0.0f : __expf(z[t][e] - m);
+      lu += pf[e];
+    }
     uint4 pb;
     if constexpr (FP8) {
       float pv[8];
@@ -545,13 +564,16 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
   }
   l += xor16_f32(l);
   l += xor32_f32(l);
+  lu += xor16_f32(lu);
+  lu += xor32_f32(lu);
 
   // ---- merge the block's waves through LDS ----
-  __shared__ float s_m[WAVES][ATT_MAX_G], s_l[WAVES][ATT_MAX_G];
+  __shared__ float s_m[WAVES][ATT_MAX_G], s_l[WAVES][ATT_MAX_G], s_lu[WAVES][ATT_MAX_G];
   __shared__ float s_o[WAVES][ATT_MAX_G][D];
   if (q4 == 0 && r16 < G) {
     s_m[w][r16] = m;
     s_l[w][r16] = l;
+    s_lu[w][r16] = lu;
   }
   if (4 * q4 < G) {  // lanes holding rows (heads) 4*q4 .. 4*q4+3
 #pragma unroll
@@ -559,7 +581,7 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_o[w][4 * q4 + i][16 * vb + r16] = o[vb][i];
   }
-  finish_block<bf16_t, D, WAVES>(a, G, list, split, b, j, s_m, s_l, s_o);
+  finish_block<bf16_t, D, WAVES>(a, G, list, split, b, j, s_m, s_l, s_lu, s_o);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -717,6 +739,7 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs& a, int G, int j, 
   l += xor16_f32(l);
   l += xor32_f32(l);
 
+  // the probabilities enter the fp32 MFMA unrounded: l is both sums
   __shared__ float s_m[WAVES][ATT_MAX_G], s_l[WAVES][ATT_MAX_G];
   __shared__ float s_o[WAVES][ATT_MAX_G][D];
   if (q4 == 0 && r16 < G) {
@@ -729,7 +752,7 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs& a, int G, int j, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_o[w][4 * q4 + i][16 * vb + r16] = o[vb][i];
   }
-  finish_block<float, D, WAVES>(a, G, list, split, b, j, s_m, s_l, s_o);
+  finish_block<float, D, WAVES>(a, G, list, split, b, j, s_m, s_l, s_l, s_o);
 }
 
 

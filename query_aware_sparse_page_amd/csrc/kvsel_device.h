@@ -222,6 +222,19 @@ __device__ __forceinline__ float lane_xor_f32(float v, int m) {
   return m == 16 ? xor16_f32(v) : m == 32 ? xor32_f32(v) : __shfl_xor(v, m);
 }
 
+// op over the whole wave, in every lane (butterfly: quad xor 1 and 2, half-row and row mirrors on
+// DPP, then the lane ^ 16 and lane ^ 32 swaps).
+template <class Op>
+__device__ __forceinline__ float wave_allreduce_f32(float x, Op op) {
+  x = op(x, __uint_as_float(dpp_u32<DPP_QUAD_XOR1>(0u, __float_as_uint(x))));
+  x = op(x, __uint_as_float(dpp_u32<DPP_QUAD_XOR2>(0u, __float_as_uint(x))));
+  x = op(x, __uint_as_float(dpp_u32<DPP_ROW_HALF_MIRROR>(0u, __float_as_uint(x))));
+  x = op(x, __uint_as_float(dpp_u32<DPP_ROW_MIRROR>(0u, __float_as_uint(x))));
+  x = op(x, xor16_f32(x));
+  x = op(x, xor32_f32(x));
+  return x;
+}
+
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
   const uint64_t u = __double_as_longlong(x);

@@ -10,7 +10,9 @@ namespace kvsel {
 template <int NT>
 struct RadixSmem {
   static constexpr int NW = NT / 64;
-  static constexpr int HC = NW < 4 ? NW : 4;  // histogram copies: wave w counts into copy w % HC
+  // histogram copies: wave w counts into copy w % HC (one copy for up to 4 waves, where reading
+  // and summing copies measured slower than the atomics they spread; 4 for larger blocks)
+  static constexpr int HC = NW <= 4 ? 1 : 4;
   // three rotating sets of HC 256-bin histograms, as 64 uint4 (lane l reads bins 4l .. 4l+3)
   uint4 hist[3][HC][64];
   uint32_t wave_a[NW], wave_b[NW];      // scan totals

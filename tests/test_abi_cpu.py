@@ -62,11 +62,12 @@ def test_workspace_sizes(K):
     d = _desc(K)
     ws = lib.kvsel_workspace_bytes(ctypes.byref(d), 64, K.KVSEL_OP_SCORE_TOPK, 0)
     assert ws == 1 * 8 * 1024 * 4  # room for the scores
-    # 64 pages in splits of 2 -> 32 partials per (b, KV head, query head of the group)
+    # 64 pages in splits of 2 -> 32 partials per (b, KV head, query head of the group): the
+    # accumulator rows, then (m, l, lu, unused) as 4 floats
     parts = 1 * 8 * 32 * 4
     acc = parts * 128 * 4
     assert lib.kvsel_workspace_bytes(ctypes.byref(d), 64, K.KVSEL_OP_ATTENTION, 2) == \
-        ((acc + 255) // 256) * 256 + parts * 8
+        ((acc + 255) // 256) * 256 + parts * 16
     # one split needs no workspace
     assert lib.kvsel_workspace_bytes(ctypes.byref(d), 2, K.KVSEL_OP_ATTENTION, 2) == 0
     assert lib.kvsel_workspace_bytes(None, 64, K.KVSEL_OP_SCORE_TOPK, 0) == 0

@@ -78,7 +78,7 @@ def test_append_matches_oracle(K, case):
     ref = oracle_path(wg, scale_of(D))
     sel, cnt, out, lse = K.select_attend(kv, summ, w.q.cuda(), w.k)
     torch.cuda.synchronize()
-    assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["margins"])
+    assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["fp32"])
     assert_attention_close(out, lse, ref["out"], ref["lse"], dtype)
 
 

@@ -11,6 +11,7 @@ import torch
 import oracle as O
 import workloads as W
 from gpu_common import (assert_attention_close, assert_selection_equal, assert_summaries_equal,
+                        fp32_boundary,
                         kv_of, say, scale_of)
 
 pytestmark = pytest.mark.gpu
@@ -43,10 +44,10 @@ def oracle_composed(w, scale, fp8=False):
         summ = O.page_summaries(w.k_pool, w.page_table, w.seq_lens, w.P, fill)
     sc = O.page_scores(q, summ, w.page_table, w.seq_lens, w.P)
     sel, cnt = O.top_pages(sc, w.seq_lens, w.P, w.k)
-    margins = O.selection_margin_ulps(sc, w.seq_lens, w.P, w.k)
+    fp32 = None if fp8 else fp32_boundary(w.dtype, sc, w.seq_lens, w.P, w.k)
     out, lse = O.sparse_decode_attention(q, keys, values, w.page_table, w.seq_lens, sel, cnt, w.P,
                                          scale, fill)
-    return dict(q=q, summ=summ, sel=sel, cnt=cnt, margins=margins, out=out, lse=lse)
+    return dict(q=q, summ=summ, sel=sel, cnt=cnt, fp32=fp32, out=out, lse=lse)
 
 
 CASES = [
@@ -85,7 +86,7 @@ def test_composed_matches_oracle(K, case):
     dtype = "bf16" if case["fp8"] else w.dtype
     assert_summaries_equal(summ, ref["summ"], w)
     assert_summaries_equal(stale, ref["summ"], w)
-    assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["margins"])
+    assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["fp32"])
     assert_attention_close(out, lse, ref["out"], ref["lse"], dtype)
     s2, c2 = K.score_topk(kv, summ, q, w.k)
     o2, l2 = K.sparse_decode_attn(kv, q, s2, c2, w.k, scale=scale)

@@ -30,11 +30,10 @@ def fp8_reference(w, scale):
     summ = O.page_summaries_fp8(kc, ks, w.page_table, w.seq_lens, w.P)
     sc = O.page_scores(q, summ, w.page_table, w.seq_lens, w.P)
     sel, cnt = O.top_pages(sc, w.seq_lens, w.P, w.k)
-    margins = O.selection_margin_ulps(sc, w.seq_lens, w.P, w.k)
     out, lse = O.sparse_decode_attention(q, O.dequantize_pages(kc, ks), O.dequantize_pages(vc, vs),
                                          w.page_table, w.seq_lens, sel, cnt, w.P, scale)
     return dict(kc=kc, ks=ks, vc=vc, vs=vs, q=q, summ=summ, scores=sc, sel=sel, cnt=cnt,
-                margins=margins, out=out, lse=lse)
+                fp32=None, out=out, lse=lse)
 
 
 def check_quantized(kv8, ref):
@@ -71,7 +70,7 @@ def test_fp8_path_matches_oracle(K, case):
     out, lse = K.sparse_decode_attn(kv8, q, sel, cnt, w.k, scale=scale)
     torch.cuda.synchronize()
     assert_scores_close(scores, ref["scores"], w, exact=False)
-    assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["margins"])
+    assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["fp32"])
     err = assert_attention_close(out, lse, ref["out"], ref["lse"], "bf16")
     # the one-call forms (the top-k fused into the attention launch, the speculative
     # co-launch) give the separate calls' outputs bit for bit
@@ -116,7 +115,7 @@ def test_fp8_tail_refresh(K):
     sel, cnt = K.score_topk(kv8, summ, ref["q"].cuda(), w.k, refresh_tail=True)
     torch.cuda.synchronize()
     assert_summaries_equal(summ, ref["summ"], w)
-    assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["margins"])
+    assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["fp32"])
 
 
 def test_every_code_decodes(K):
@@ -200,6 +199,6 @@ def test_fp8_full_workloads(K, name, seqs):
         check_quantized(sub, ref)
         rows = list(seqs)
     assert_summaries_equal(summ[rows], ref["summ"], ws)
-    assert_selection_equal(sel[rows], cnt[rows], ref["sel"], ref["cnt"], ref["margins"])
+    assert_selection_equal(sel[rows], cnt[rows], ref["sel"], ref["cnt"], ref["fp32"])
     err = assert_attention_close(out[rows], lse[rows], ref["out"], ref["lse"], "bf16")
     say(f"fp8 {name}: max abs attention error {err:.3g}")

@@ -65,11 +65,11 @@ def test_live_bound_matches_oracle(K, case):
     sel, cnt = K.score_topk(kv, summ, q, w.k, refresh_tail=True)
     out, lse = K.sparse_decode_attn(kv, q, sel, cnt, w.k)
     torch.cuda.synchronize()
-    assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["margins"])
+    assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["fp32"])
     assert_attention_close(out, lse, ref["out"], ref["lse"], w.dtype)
     fs, fc, fo, fl = K.select_attend(kv, summ, q, w.k, refresh_tail=True)
     torch.cuda.synchronize()
-    assert_selection_equal(fs, fc, ref["sel"], ref["cnt"], ref["margins"])
+    assert_selection_equal(fs, fc, ref["sel"], ref["cnt"], ref["fp32"])
     assert_attention_close(fo, fl, ref["out"], ref["lse"], w.dtype)
     # speculative step: the first step takes the fresh selection; the second reuses it where the
     # queries agree and must equal the serial calls bit for bit
@@ -77,7 +77,7 @@ def test_live_bound_matches_oracle(K, case):
     zc = torch.zeros((w.B, w.Hkv), dtype=torch.int32, device="cuda")
     s1 = K.speculative_step(kv, summ, q, w.k, K.Reuse(q, zi, zc, 0.8, first_step=True))
     torch.cuda.synchronize()
-    assert_selection_equal(s1[0], s1[1], ref["sel"], ref["cnt"], ref["margins"])
+    assert_selection_equal(s1[0], s1[1], ref["sel"], ref["cnt"], ref["fp32"])
     assert_attention_close(s1[6], s1[7], ref["out"], ref["lse"], w.dtype)
     gen = torch.Generator().manual_seed(c["seed"] + 2)
     q2 = (w.q.float() + 0.3 * torch.randn(w.q.shape, generator=gen)).to(w.q.dtype).cuda()
@@ -112,7 +112,7 @@ def test_length_past_the_bound(K):
     sel, cnt, out, lse = K.select_attend(kv, summ, q, w.k, refresh_tail=True)
     torch.cuda.synchronize()
     assert_summaries_equal(summ, ref["summ"], cut)
-    assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["margins"])
+    assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["fp32"])
     assert_attention_close(out, lse, ref["out"], ref["lse"], w.dtype)
     flags = K.check_inputs(kv)
     torch.cuda.synchronize()
@@ -133,7 +133,6 @@ def test_live_bound_fp8(K):
     summ_ref = O.page_summaries_fp8(kc, ks, w.page_table, w.seq_lens, w.P)
     sc = O.page_scores(w.q, summ_ref, w.page_table, w.seq_lens, w.P)
     sel_ref, cnt_ref = O.top_pages(sc, w.seq_lens, w.P, w.k)
-    margins = O.selection_margin_ulps(sc, w.seq_lens, w.P, w.k)
     out_ref, lse_ref = O.sparse_decode_attention(w.q, O.dequantize_pages(kc, ks),
                                                  O.dequantize_pages(vc, vs), w.page_table,
                                                  w.seq_lens, sel_ref, cnt_ref, w.P, scale)
@@ -149,7 +148,7 @@ def test_live_bound_fp8(K):
                               scale=scale)
     torch.cuda.synchronize()
     assert_summaries_equal(summ, summ_ref, w)
-    assert_selection_equal(sel, cnt, sel_ref, cnt_ref, margins)
+    assert_selection_equal(sel, cnt, sel_ref, cnt_ref)
     assert_attention_close(out, lse, out_ref, lse_ref, "bf16")
     for a, b_, name in ((spec[0], sel, "sel"), (spec[6], out, "out"), (spec[7], lse, "lse")):
         assert torch.equal(a, b_), f"speculative step: {name} differs from kvsel_select_attend"

@@ -171,8 +171,7 @@ def test_speculative_decode_loop_matches_oracle(K, spec):
             o_prev = (f_sel, f_cnt)
         u_sel, u_cnt, o_corr = O.speculative_choice(f_sel, f_cnt, o_prev[0], o_prev[1], C, tau,
                                                     first_step=(t == 0))
-        margins = O.selection_margin_ulps(sc, w.seq_lens, w.P, w.k)
-        assert_selection_equal(sel, cnt, f_sel, f_cnt, margins)
+        assert_selection_equal(sel, cnt, f_sel, f_cnt)
         assert np.abs(sim.cpu().numpy() - C).max() < 1e-12
         assert np.abs(C - tau).min() > 1e-9, "a correction decision sits on the rounding edge"
         np.testing.assert_array_equal(corr.cpu().numpy(), o_corr)

@@ -43,7 +43,7 @@ def test_full_workloads(K, name):
     torch.cuda.synchronize()
     assert_same(fused, sep)
     ref = oracle_path(w, scale_of(w.D))
-    assert_selection_equal(fused[0], fused[1], ref["sel"], ref["cnt"], ref["margins"])
+    assert_selection_equal(fused[0], fused[1], ref["sel"], ref["cnt"], ref["fp32"])
     err = assert_attention_close(fused[2], fused[3], ref["out"], ref["lse"], w.dtype)
     say(f"{name}: max abs err {err:.3g}")
 
@@ -85,7 +85,7 @@ def test_edge_cases(K, case):
     torch.cuda.synchronize()
     assert_same(fused, sep)
     ref = oracle_path(w, scale_of(w.D))
-    assert_selection_equal(fused[0], fused[1], ref["sel"], ref["cnt"], ref["margins"])
+    assert_selection_equal(fused[0], fused[1], ref["sel"], ref["cnt"], ref["fp32"])
     assert_attention_close(fused[2], fused[3], ref["out"], ref["lse"], w.dtype)
 
 
