@@ -11,7 +11,8 @@ The step is timed over R copies of the cache at distinct HBM addresses (default 
 turn like the layers of a model: the selected K/V of all copies (48 x 8 MiB at 32K) exceeds the
 256 MB Infinity Cache, so a copy's pages have been evicted by the time it is visited again (the
 situation of a real decode, where every layer runs between two visits of one layer's cache).
-The R steps are captured once in a HIP graph and replayed.
+Exactly --warmup untimed steps run first; exactly --steps timed steps (step i on copy i mod R)
+are captured in one HIP graph and replayed once between two HIP events.
 
 Prints ONE JSON line: µs/step of the whole path (the headline value), the roofline of the
 dominant kernel (the attention call: its time per call from a graph of back-to-back calls between
@@ -106,32 +107,28 @@ def make_layers(w, dev, n, fp8=False):
 
 
 def time_graph(layers, steps, warmup, step=Layer.step):
-    """µs per step of the whole path, replaying a graph of one step per layer."""
+    """µs per step of the whole path: exactly ``warmup`` untimed steps (eager), then exactly
+    ``steps`` timed steps captured in one HIP graph and replayed once between two HIP events. Step
+    i runs on cache copy i mod R, so a timed step reads a copy that R - 1 other copies were used
+    after it (cold for R = 48 at 32K: 48 x 8 MiB of selected K/V exceeds the Infinity Cache)."""
+    R = len(layers)
+    for i in range(warmup):
+        step(layers[i % R])
+    torch.cuda.synchronize()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for lay in layers:  # eager warm-up before capture
-            step(lay)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for lay in layers:
-            step(lay)
-    reps_w = max(1, warmup // len(layers))
-    reps = max(1, steps // len(layers))
-    for _ in range(reps_w):
-        g.replay()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(warmup, warmup + steps):
+            step(layers[i % R])
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(reps):
-        g.replay()
+    g.replay()
     e1.record()
     torch.cuda.synchronize()
-    n = reps * len(layers)
-    return e0.elapsed_time(e1) * 1000.0 / n, n
+    return e0.elapsed_time(e1) * 1000.0 / steps, steps
 
 
 def time_calls(layers, fn, launches):
@@ -255,7 +252,7 @@ def sweep_pps(name, dev, n_layers, launches=256):
     print(json.dumps({"sweep_pps": name, "attn_us_by_pages_per_split": out}), flush=True)
 
 
-def speculative(dev, reps=3):
+def speculative(dev, reps=3, tau=None):
     """The speculative workload: a 32K cache built from eight rotary-encoded 4096-token blocks,
     re-positioned on the fly (fused rotary gather), then 64 decode steps with AR(1) queries where
     step t attends over step t-1's pages unless the group-mean query similarity is below tau.
@@ -270,12 +267,13 @@ def speculative(dev, reps=3):
                        w.page_table.to(dev), w.seq_lens.to(dev), w.Hq)
     enc_row = torch.from_numpy(((np.arange(npg) % blocks) * w.P).astype(np.int32)).to(dev)
     shift_row = torch.from_numpy(((np.arange(npg) // blocks) * bt).astype(np.int32)).to(dev)
+    tau = w.extra["tau"] if tau is None else tau
     enc = K.rope_shift(kv_raw, K.Rope(cos, sin, enc_row, 1))  # the precomputed blocks
     kv = K.PagedKV(enc, kv_raw.v_pool, kv_raw.page_table, kv_raw.seq_lens, w.Hq)
     shift = K.Rope(cos, sin, shift_row, 0)
     summ = K.build_summaries(kv, rope=shift)
     qs = w.extra["q_steps"].to(dev)
-    T, tau = qs.shape[0], w.extra["tau"]
+    T = qs.shape[0]
     B, Hkv, k = w.B, w.Hkv, w.k
     sel = torch.zeros((T, B, Hkv, k), dtype=torch.int32, device=dev)
     cnt = torch.zeros((T, B, Hkv), dtype=torch.int32, device=dev)
@@ -672,6 +670,11 @@ def main():
     if not args.no_secondary:
         result.setdefault("secondary", {})["speculative_rope_64_steps"] = speculative(dev)
         progress("speculative workload done")
+        torch.cuda.empty_cache()
+        # the same loop at tau 0.85, where about half the decisions correct (re-select and
+        # re-attend inside the speculative step)
+        result["secondary"]["speculative_rope_64_steps_tau0.85"] = speculative(dev, tau=0.85)
+        progress("speculative workload (tau 0.85) done")
         torch.cuda.empty_cache()
         result["secondary"]["speculative_growing_64_steps"] = speculative_growing(dev)
         progress("growing speculative workload done")

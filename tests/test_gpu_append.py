@@ -131,8 +131,9 @@ def test_append_refuses_a_full_table(K):
 
 def test_growing_speculative_loop(K):
     """Appends interleaved with speculative steps (the summaries kept current by the appends, no
-    refresh): each step's outputs equal the serial calls' bit for bit, and the last step's
-    attention over the pages it used matches the oracle on the grown cache."""
+    refresh): each step's outputs equal the serial calls' bit for bit, and every step's fresh
+    selection, similarity, decision and used lists match the oracle on the grown cache, with the
+    attention against the oracle's over its own used lists."""
     T, k = 12, 6
     lens = [5 * 16 + 3, 2 * 16, 16 - 2]
     w = grown_case(721, "bf16", 128, 16, lens, T, Hq=16, Hkv=4, k=k)
@@ -142,6 +143,7 @@ def test_growing_speculative_loop(K):
     gen = torch.Generator().manual_seed(722)
     q = w.q.float()
     sel_prev = cnt_prev = None
+    o_prev = None
     Kc, Vc = w.k_pool.double().numpy(), w.v_pool.double().numpy()
     cur = w.seq_lens.numpy().astype(np.int64)
     for t in range(T):
@@ -166,11 +168,24 @@ def test_growing_speculative_loop(K):
                               ("sel", "cnt", "used", "ucnt", "corrected", "similarity", "out", "lse")):
             assert torch.equal(x, y), f"step {t}: {name} differs"
         sel_prev, cnt_prev = spec[0].clone(), spec[1].clone()
+        # the oracle on the grown cache
+        o_summ = O.page_summaries(Kc, w.page_table, cur, 16)
+        sc = O.page_scores(qt.cpu(), o_summ, w.page_table, cur, 16)
+        f_sel, f_cnt = O.top_pages(sc, cur, 16, k)
+        C = O.query_similarity(qt.cpu(), qp.cpu(), w.Hkv)
+        if first:
+            o_prev = (f_sel, f_cnt)
+        u_sel, u_cnt, o_corr = O.speculative_choice(f_sel, f_cnt, o_prev[0], o_prev[1], C, 0.8,
+                                                    first)
+        assert_selection_equal(spec[0], spec[1], f_sel, f_cnt)
+        assert np.abs(spec[5].cpu().numpy() - C).max() < 1e-12
+        np.testing.assert_array_equal(spec[4].cpu().numpy(), o_corr)
+        assert_selection_equal(spec[2], spec[3], u_sel, u_cnt)
+        o_out, o_lse = O.sparse_decode_attention(qt.cpu(), Kc, Vc, w.page_table, cur, u_sel, u_cnt,
+                                                 16, scale_of(128))
+        assert_attention_close(spec[6], spec[7], o_out, o_lse, "bf16")
+        o_prev = (f_sel, f_cnt)
     assert list(kv_a.seq_lens.cpu().numpy()) == list(cur)
-    o_out, o_lse = O.sparse_decode_attention(qt.cpu(), Kc, Vc, w.page_table, cur,
-                                             spec[2].cpu().numpy(), spec[3].cpu().numpy(), 16,
-                                             scale_of(128))
-    assert_attention_close(spec[6], spec[7], o_out, o_lse, "bf16")
 
 
 def free_list_case(seed, lens, T, P=16, D=64, Hkv=2, extra_free=3):

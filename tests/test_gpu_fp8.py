@@ -174,12 +174,22 @@ def restricted(w, seqs):
                       w.q[list(seqs)].clone()), pages
 
 
-@pytest.mark.parametrize("name,seqs", [("llama8b_32k", None), ("ragged_batch", (0, 7, 15))])
+_full = {}
+
+
+@pytest.mark.parametrize("name,seqs", [("llama8b_32k", None), ("ragged_batch", (0, 1, 2, 3)),
+                                       ("ragged_batch", (4, 5, 6, 7)),
+                                       ("ragged_batch", (8, 9, 10, 11)),
+                                       ("ragged_batch", (12, 13, 14, 15))])
 def test_fp8_full_workloads(K, name, seqs):
     """The full-size workloads quantized on the GPU and run in the bench's launch configuration
     (one kvsel_select_attend call, the default split): quantizer, summaries and selection exact,
-    attention within tolerance. For the ragged batch the oracle checks three sampled sequences."""
-    w = W.make(name)
+    attention within tolerance. The ragged batch runs whole on the GPU; the oracle checks its 16
+    sequences four at a time (one case each, to bound the oracle's time per test)."""
+    if name not in _full:
+        _full.clear()
+        _full[name] = W.make(name)
+    w = _full[name]
     say(f"fp8 full workload {name}, oracle on sequences {seqs or 'all'}")
     scale = scale_of(w.D)
     kv8 = K.quantize_pages(kv_of(K, w))

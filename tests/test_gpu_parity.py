@@ -65,12 +65,19 @@ def test_full_workload_parity(K, name):
 
 
 def test_structure_is_found(K):
-    # planted tokens (tiny) and needle pages (128K) end up in every KV head's selection
+    """The planted tokens of the 1K fp32 case and the 16 needle pages of the 128K case are in
+    every KV head's selection (the stand-in for needle retrieval)."""
     w = W.tiny_fp32()
     g = run_gpu_path(K, w)
     s = g["sel"].cpu().numpy()
     for j in range(w.Hkv):
         assert set(w.extra["planted_pages"]) <= set(s[0, j].tolist())
+    w = W.qwen4b_128k()
+    g = run_gpu_path(K, w, scores=False)
+    s = g["sel"].cpu().numpy()
+    for j in range(w.Hkv):
+        missing = set(w.extra["needle_pages"]) - set(s[0, j].tolist())
+        assert not missing, f"KV head {j}: needle pages {sorted(missing)} not selected"
 
 
 @pytest.mark.parametrize("case", [

@@ -76,7 +76,10 @@ def test_rope_shift_matches_oracle(K, dtype, D, P, row_step, in_place):
 
 @pytest.fixture(scope="module")
 def spec(K):
-    """The speculative workload rotated on both sides."""
+    """The speculative workload rotated on both sides. The library encodes and shifts the blocks
+    twice: with its own rotary table (kvsel_rope_table), and with the oracle's table handed to it
+    as data (so both sides rotate with identical cos / sin bits and the rotated keys must agree
+    bit for bit)."""
     w = W.speculative_rope()
     blocks = w.extra["block_tokens"] // w.P  # pages per block
     npg = w.num_phys_pages
@@ -94,13 +97,23 @@ def spec(K):
     same = table_agreement(gc, gs, oc, os_)
     o_enc = O.rope_rotate(w.k_pool, oc, os_, enc_row, 1, "bf16")
     o_abs = O.rope_rotate(torch.from_numpy(o_enc).to(torch.bfloat16), oc, os_, shift_row, 0, "bf16")
+    # the oracle's table as the library's input data
+    dc, ds = torch.from_numpy(oc).cuda(), torch.from_numpy(os_).cuda()
+    enc_d = K.rope_shift(kv_raw, K.Rope(dc, ds, torch.from_numpy(enc_row).cuda(), 1))
+    kv_enc_d = K.PagedKV(enc_d, kv_raw.v_pool, kv_raw.page_table, kv_raw.seq_lens, w.Hq)
+    absk_d = K.rope_shift(kv_enc_d, K.Rope(dc, ds, torch.from_numpy(shift_row).cuda(), 0))
+    torch.cuda.synchronize()
     return dict(w=w, kv_enc=kv_enc, shift=shift, absk=absk, o_enc=o_enc, o_abs=o_abs,
                 table_same=bool(same.all()), same=same, enc_row=enc_row, shift_row=shift_row,
-                enc_gpu=enc)
+                enc_gpu=enc, enc_d=enc_d, absk_d=absk_d)
 
 
 def test_speculative_rope_blocks_match_oracle(spec):
     w = spec["w"]
+    # with the oracle's table as data: bit for bit, unconditionally
+    np.testing.assert_array_equal(spec["enc_d"].float().cpu().numpy(), spec["o_enc"])
+    np.testing.assert_array_equal(spec["absk_d"].float().cpu().numpy(), spec["o_abs"])
+    # with the library's own table
     g_enc = spec["enc_gpu"].float().cpu().numpy()
     g_abs = spec["absk"].float().cpu().numpy()
     if spec["table_same"]:
@@ -135,15 +148,20 @@ def test_fused_rope_is_bit_identical_to_materialized(K, spec):
     assert torch.equal(o_mat, o_fused) and torch.equal(l_mat, l_fused)
 
 
-def test_speculative_decode_loop_matches_oracle(K, spec):
+@pytest.mark.parametrize("tau", [None, 0.85], ids=["tau0.8", "tau0.85"])
+def test_speculative_decode_loop_matches_oracle(K, spec, tau):
+    """64 decode steps, each run as the serial calls (kvsel_score_topk with reuse, then
+    kvsel_sparse_decode_attn over the used pages) and as one kvsel_speculative_step, both against
+    the oracle's fresh selection, similarity, decision, used lists and attention over its own used
+    lists. tau 0.8 is the workload's (no correction fires); at tau 0.85 about half the decisions
+    correct."""
     w = spec["w"]
-    tau = w.extra["tau"]
+    tau = w.extra["tau"] if tau is None else tau
     qs = w.extra["q_steps"]
     o_pool = torch.from_numpy(spec["o_abs"]).to(torch.bfloat16)
-    # identical tables: the GPU's own rotated keys (end to end); otherwise the oracle's keys, so
-    # the selection / reuse / attention comparison stays bit-exact
-    keys = spec["absk"] if spec["table_same"] else o_pool.cuda()
-    kv = K.PagedKV(keys, spec["kv_enc"].v_pool, spec["kv_enc"].page_table,
+    # the keys the library encoded and shifted itself (kvsel_rope_shift with the oracle's table as
+    # data), end to end through summaries, selection, reuse and attention
+    kv = K.PagedKV(spec["absk_d"], spec["kv_enc"].v_pool, spec["kv_enc"].page_table,
                    spec["kv_enc"].seq_lens, w.Hq)
     say("speculative loop: summaries")
     summ = K.build_summaries(kv)
@@ -153,15 +171,18 @@ def test_speculative_decode_loop_matches_oracle(K, spec):
     scale = scale_of(w.D)
     prev = (torch.zeros((w.B, w.Hkv, w.k), dtype=torch.int32, device="cuda"),
             torch.zeros((w.B, w.Hkv), dtype=torch.int32, device="cuda"))
+    sprev = prev
     o_prev = None
     fires = 0
     for t in range(qs.shape[0]):
-        say(f"speculative step {t}")
+        say(f"speculative step {t} (tau {tau})")
         q = qs[t].cuda()
         q_prev = qs[t - 1].cuda() if t > 0 else q
         sel, cnt, used, ucnt, corr, sim = K.score_topk(
             kv, summ, q, w.k, reuse=K.Reuse(q_prev, prev[0], prev[1], tau, first_step=(t == 0)))
         out, lse = K.sparse_decode_attn(kv, q, used, ucnt, w.k)
+        sp = K.speculative_step(kv, summ, q, w.k,
+                                K.Reuse(q_prev, sprev[0], sprev[1], tau, first_step=(t == 0)))
         torch.cuda.synchronize()
         # oracle step
         sc = O.page_scores(qs[t], o_summ, w.page_table, w.seq_lens, w.P)
@@ -179,7 +200,16 @@ def test_speculative_decode_loop_matches_oracle(K, spec):
         o_out, o_lse = O.sparse_decode_attention(qs[t], o_pool, w.v_pool, w.page_table, w.seq_lens,
                                                  u_sel, u_cnt, w.P, scale)
         assert_attention_close(out, lse, o_out, o_lse, "bf16")
+        # the speculative step against the same oracle results
+        assert_selection_equal(sp[0], sp[1], f_sel, f_cnt)
+        assert np.abs(sp[5].cpu().numpy() - C).max() < 1e-12
+        np.testing.assert_array_equal(sp[4].cpu().numpy(), o_corr)
+        assert_selection_equal(sp[2], sp[3], u_sel, u_cnt)
+        assert_attention_close(sp[6], sp[7], o_out, o_lse, "bf16")
         fires += int(o_corr.sum()) if t > 0 else 0
         prev = (sel, cnt)
+        sprev = (sp[0], sp[1])
         o_prev = (f_sel, f_cnt)
-    say(f"speculative loop: corrections {fires}/{(qs.shape[0] - 1) * w.Hkv}")
+    say(f"speculative loop (tau {tau}): corrections {fires}/{(qs.shape[0] - 1) * w.Hkv}")
+    if tau > 0.84:
+        assert fires > 0, "no correction fired"

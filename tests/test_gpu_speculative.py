@@ -8,7 +8,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_common import assert_attention_close, kv_of, say, scale_of
+from gpu_common import (assert_attention_close, assert_selection_equal, fp32_boundary, kv_of, say,
+                        scale_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +57,7 @@ def assert_same(a, b):
         assert torch.equal(x, y), f"{n} differs between the speculative step and the serial calls"
 
 
-def check_both_outcomes(K, kv, summ, q, q_prev, prev_idx, prev_cnt, k, rope=None):
+def check_both_outcomes(K, kv, summ, q, q_prev, prev_idx, prev_cnt, k, rope=None, specs=None):
     Hkv = kv.num_kv_heads
     for first in (False, True):
         reuse = K.Reuse(q_prev, prev_idx, prev_cnt, 0.8, first_step=first)
@@ -69,7 +70,33 @@ def check_both_outcomes(K, kv, summ, q, q_prev, prev_idx, prev_cnt, k, rope=None
             assert corr.all()
         else:  # both outcomes occur
             assert corr[:, Hkv // 2:].all() and not corr[:, :Hkv // 2].any()
+        if specs is not None:
+            specs[first] = spec
     return spec
+
+
+def check_against_oracle(w, q, q_prev, k, tau, first, spec):
+    """The step's fresh selection, similarity, decision and used lists against the oracle's (its
+    previous selection being the oracle's top-k for q_prev), and the attention against the oracle
+    over the oracle's own used lists."""
+    summ = O.page_summaries(w.k_pool, w.page_table, w.seq_lens, w.P)
+    qc, pc = q.cpu(), q_prev.cpu()
+    sc = O.page_scores(qc, summ, w.page_table, w.seq_lens, w.P)
+    f_sel, f_cnt = O.top_pages(sc, w.seq_lens, w.P, k)
+    psc = O.page_scores(pc, summ, w.page_table, w.seq_lens, w.P)
+    p_sel, p_cnt = O.top_pages(psc, w.seq_lens, w.P, k)
+    C = O.query_similarity(qc, pc, w.Hkv)
+    u_sel, u_cnt, corr = O.speculative_choice(f_sel, f_cnt, p_sel, p_cnt, C, tau, first)
+    assert_selection_equal(spec[0], spec[1], f_sel, f_cnt,
+                           fp32_boundary(w.dtype, sc, w.seq_lens, w.P, k))
+    assert np.abs(spec[5].cpu().numpy() - C).max() < 1e-12
+    np.testing.assert_array_equal(spec[4].cpu().numpy(), corr)
+    used_sc = np.where(corr[:, :, None].astype(bool), sc, psc)
+    assert_selection_equal(spec[2], spec[3], u_sel, u_cnt,
+                           fp32_boundary(w.dtype, used_sc, w.seq_lens, w.P, k))
+    o_out, o_lse = O.sparse_decode_attention(qc, w.k_pool, w.v_pool, w.page_table, w.seq_lens,
+                                             u_sel, u_cnt, w.P, scale_of(w.D))
+    assert_attention_close(spec[6], spec[7], o_out, o_lse, w.dtype)
 
 
 # (dtype, P, D, Hq, Hkv, k): every block shape of the co-scheduled launch (bf16 P 32: 4 waves;
@@ -91,13 +118,10 @@ def test_speculative_step_matches_serial(K, shape):
     say(f"speculative step {shape}")
     w, kv, summ, q, q_prev, prev_idx, prev_cnt = setup_case(K, k, dtype=dtype, Hq=Hq, Hkv=Hkv,
                                                               D=D, P=P)
-    spec = check_both_outcomes(K, kv, summ, q, q_prev, prev_idx, prev_cnt, k)
-    # the used pages' attention against the oracle
-    out, lse = spec[6], spec[7]
-    o_out, o_lse = O.sparse_decode_attention(q.cpu(), w.k_pool, w.v_pool, w.page_table, w.seq_lens,
-                                             spec[2].cpu().numpy(), spec[3].cpu().numpy(), w.P,
-                                             scale_of(w.D))
-    assert_attention_close(out, lse, o_out, o_lse, dtype)
+    specs = {}
+    check_both_outcomes(K, kv, summ, q, q_prev, prev_idx, prev_cnt, k, specs=specs)
+    for first, spec in specs.items():  # both decision outcomes, and the first step
+        check_against_oracle(w, q, q_prev, k, 0.8, first, spec)
 
 
 def test_speculative_step_empty_and_short_sequences(K):
