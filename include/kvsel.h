@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVSEL_ABI_VERSION 5
+#define KVSEL_ABI_VERSION 6
 
 typedef int32_t kvsel_status;
 #define KVSEL_OK 0
@@ -61,6 +61,10 @@ typedef int32_t kvsel_status;
 #define KVSEL_ERR_WORKSPACE 3        /* workspace NULL or smaller than kvsel_workspace_bytes */
 #define KVSEL_ERR_DEVICE 4           /* current device is not gfx950, or no device           */
 #define KVSEL_ERR_LAUNCH 5           /* the HIP runtime rejected a launch                    */
+#define KVSEL_ERR_SCRATCH 6          /* the call needs more than KVSEL_STATIC_SCRATCH_BYTES    */
+
+/* Size of the library's device-resident scratch array (kvsel_select_attend_static). */
+#define KVSEL_STATIC_SCRATCH_BYTES (8u << 20)
 
 /* Largest supported batch and page-table width (launch-grid limits). */
 #define KVSEL_MAX_BATCH 65535
@@ -246,6 +250,23 @@ kvsel_status kvsel_select_attend(const kvsel_paged_kv* kv, const kvsel_rope* rop
                                  const void* q, int32_t k, int32_t flags, float scale,
                                  int32_t* sel_idx, int32_t* sel_cnt, void* out, float* lse,
                                  void* ws, size_t ws_bytes, void* stream);
+
+/* kvsel_select_attend without a workspace argument, for callers that cannot allocate device
+ * memory (code being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation): the scores and split partials live in a device array of the library
+ * (KVSEL_STATIC_SCRATCH_BYTES, one per GPU, held until the process ends). Same outputs as
+ * kvsel_select_attend, bit for bit; the call allocates and frees nothing. A call that needs more
+ * than KVSEL_STATIC_SCRATCH_BYTES (kvsel_workspace_bytes(kv, k, KVSEL_OP_SELECT_ATTEND, 0))
+ * returns KVSEL_ERR_SCRATCH before anything is enqueued. Nothing in the array needs to start at
+ * zero (every byte read is written earlier in the same call). Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (several streams, or several threads) race and must
+ * be serialized by the caller. The first call on a device looks up the array's device address
+ * (hipGetSymbolAddress, with that device current), so it should not be the first call made
+ * inside a stream capture. */
+kvsel_status kvsel_select_attend_static(const kvsel_paged_kv* kv, const kvsel_rope* rope,
+                                        void* summ, const void* q, int32_t k, int32_t flags,
+                                        float scale, int32_t* sel_idx, int32_t* sel_cnt, void* out,
+                                        float* lse, void* stream);
 
 /* Rotary table: cos[r][i], sin[r][i] (fp32 [n_rows][D/2]) of the angle
  * (first_position + r) * theta^(-2i/D), evaluated in fp64 and rounded to fp32. head_dim is even

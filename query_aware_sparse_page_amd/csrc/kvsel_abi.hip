@@ -5,11 +5,17 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "../../include/kvsel.h"
 #include "kvsel_internal.h"
 
 using namespace kvsel;
+
+// Scratch of kvsel_select_attend_static (scores and split partials): one copy per GPU, at its own
+// address there. Host code never passes this name to a kernel (on the host it is a stand-in, not
+// a device address); it uses the address looked up per device by static_scratch below.
+static __device__ __align__(256) unsigned char scratch[KVSEL_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -103,6 +109,27 @@ kvsel_status flatten_rope(const kvsel_rope* rope, const LaunchKV& f, RopeArgs* o
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Device address of `scratch` on the current device, looked up once per device with that device
+// current (hipGetSymbolAddress) and kept.
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+kvsel_status static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVSEL_ERR_DEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVSEL_ERR_DEVICE;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return KVSEL_OK;
+}
+
 // Room for the scores when the caller does not provide a score buffer.
 size_t score_workspace(const LaunchKV& kv, bool with_scores) {
   return with_scores ? align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float)) : 0;
@@ -124,6 +151,9 @@ const char* kvsel_status_str(kvsel_status status) {
     case KVSEL_ERR_WORKSPACE: return "KVSEL_ERR_WORKSPACE: workspace missing or too small";
     case KVSEL_ERR_DEVICE: return "KVSEL_ERR_DEVICE: current device is not gfx950";
     case KVSEL_ERR_LAUNCH: return "KVSEL_ERR_LAUNCH: kernel launch failed";
+    case KVSEL_ERR_SCRATCH:
+      return "KVSEL_ERR_SCRATCH: the call needs more than the library's static scratch "
+             "(KVSEL_STATIC_SCRATCH_BYTES); use the entry point that takes a workspace";
     default: return "KVSEL_ERR_UNKNOWN: unknown status code";
   }
 }
@@ -222,6 +252,26 @@ kvsel_status kvsel_select_attend(const kvsel_paged_kv* kv, const kvsel_rope* rop
   if (attention_pages_per_split(f, k, 0) <= 0) return KVSEL_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < select_attend_workspace(f, k)) return KVSEL_ERR_WORKSPACE;
   if ((st = check_device()) != KVSEL_OK) return st;
+  return launch_status(launch_select_attend(f, r, summ, q, k, flags, scale, sel_idx, sel_cnt, out,
+                                            lse, ws, (hipStream_t)stream));
+}
+
+kvsel_status kvsel_select_attend_static(const kvsel_paged_kv* kv, const kvsel_rope* rope,
+                                        void* summ, const void* q, int32_t k, int32_t flags,
+                                        float scale, int32_t* sel_idx, int32_t* sel_cnt, void* out,
+                                        float* lse, void* stream) {
+  LaunchKV f;
+  RopeArgs r;
+  kvsel_status st = flatten(kv, 3, &f);
+  if (st != KVSEL_OK) return st;
+  if (!summ || !q || !sel_idx || !sel_cnt || !out || k < 1) return KVSEL_ERR_INVALID_ARGUMENT;
+  if (flags & ~KVSEL_SCORE_REFRESH_TAIL) return KVSEL_ERR_INVALID_ARGUMENT;
+  if ((st = flatten_rope(rope, f, &r)) != KVSEL_OK) return st;
+  if (attention_pages_per_split(f, k, 0) <= 0) return KVSEL_ERR_UNSUPPORTED;
+  if (select_attend_workspace(f, k) > (size_t)KVSEL_STATIC_SCRATCH_BYTES) return KVSEL_ERR_SCRATCH;
+  if ((st = check_device()) != KVSEL_OK) return st;
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws)) != KVSEL_OK) return st;
   return launch_status(launch_select_attend(f, r, summ, q, k, flags, scale, sel_idx, sel_cnt, out,
                                             lse, ws, (hipStream_t)stream));
 }

@@ -31,6 +31,8 @@ KVSEL_CHECK_PAGE_ID = 2
 KVSEL_CHECK_SELECTION = 4
 KVSEL_CHECK_NO_FREE_PAGE = 8
 KVSEL_CHECK_PAGE_FILL = 16
+KVSEL_ERR_SCRATCH = 6
+KVSEL_STATIC_SCRATCH_BYTES = 8 << 20  # the library's per-GPU scratch (kvsel_select_attend_static)
 
 c_i32 = ctypes.c_int32
 c_vp = ctypes.c_void_p
@@ -84,6 +86,9 @@ EXPORTS = {
     "kvsel_select_attend": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp, c_vp,
                                     c_i32, c_i32, ctypes.c_float, c_vp, c_vp, c_vp, c_vp, c_vp,
                                     ctypes.c_size_t, c_vp]),
+    "kvsel_select_attend_static": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc),
+                                           c_vp, c_vp, c_i32, c_i32, ctypes.c_float, c_vp, c_vp,
+                                           c_vp, c_vp, c_vp]),
     "kvsel_speculative_step": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp,
                                        c_vp, c_i32, c_i32, ctypes.c_float,
                                        ctypes.POINTER(ReuseDesc), c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -100,7 +105,7 @@ EXPORTS = {
 _lib = None
 
 
-ABI_VERSION = 5  # KVSEL_ABI_VERSION of include/kvsel.h
+ABI_VERSION = 6  # KVSEL_ABI_VERSION of include/kvsel.h
 
 
 def lib() -> ctypes.CDLL:
@@ -432,6 +437,31 @@ def select_attend(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, *,
     _check(lib().kvsel_select_attend(ctypes.byref(d), _rope_ptr(rope), _ptr(summ), _ptr(q), k, flags,
                                      scale, _ptr(sel_idx), _ptr(sel_cnt), _ptr(out), _ptr(lse),
                                      _ptr(ws), ws_bytes, _stream(dev)))
+    return sel_idx, sel_cnt, out, lse
+
+
+def select_attend_static(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, *,
+                         sel_idx: torch.Tensor, sel_cnt: torch.Tensor, out: torch.Tensor,
+                         lse: Optional[torch.Tensor] = None, refresh_tail: bool = False,
+                         rope: Optional[Rope] = None, scale: Optional[float] = None):
+    """kvsel_select_attend_static: select_attend with its scores and split partials in the
+    library's per-GPU device array instead of a workspace. Every output is the caller's (this
+    wrapper allocates nothing either). Returns (sel_idx, sel_cnt, out, lse)."""
+    d = kv.desc()
+    dev = kv.device
+    _check_summ(kv, summ)
+    _dev(q, "q", kv.act_dtype)
+    _dev(sel_idx, "sel_idx", torch.int32)
+    _dev(sel_cnt, "sel_cnt", torch.int32)
+    _dev(out, "out", q.dtype)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    if scale is None:
+        scale = default_scale(kv.head_dim)
+    flags = KVSEL_SCORE_REFRESH_TAIL if refresh_tail else 0
+    _check(lib().kvsel_select_attend_static(ctypes.byref(d), _rope_ptr(rope), _ptr(summ), _ptr(q),
+                                            k, flags, scale, _ptr(sel_idx), _ptr(sel_cnt),
+                                            _ptr(out), _ptr(lse), _stream(dev)))
     return sel_idx, sel_cnt, out, lse
 
 

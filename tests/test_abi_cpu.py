@@ -42,9 +42,10 @@ def test_every_declared_symbol_is_exported(K):
 
 def test_version_and_status_strings(K):
     lib = K.lib()
-    assert lib.kvsel_abi_version() == K.ABI_VERSION == 5
+    assert lib.kvsel_abi_version() == K.ABI_VERSION == 6
     for code, tag in [(0, "KVSEL_OK"), (1, "INVALID_ARGUMENT"), (2, "UNSUPPORTED"),
-                      (3, "WORKSPACE"), (4, "DEVICE"), (5, "LAUNCH"), (99, "UNKNOWN")]:
+                      (3, "WORKSPACE"), (4, "DEVICE"), (5, "LAUNCH"), (6, "SCRATCH"),
+                      (99, "UNKNOWN")]:
         assert tag in lib.kvsel_status_str(code).decode()
 
 
@@ -130,6 +131,25 @@ def test_call_argument_validation(K):
     assert lib.kvsel_rope_shift(ctypes.byref(d), None, p, None) == 1
     assert lib.kvsel_rope_table(500000.0, 127, 0, 4, p, p, None) == 1
     assert lib.kvsel_rope_table(-1.0, 128, 0, 4, p, p, None) == 1
+
+
+def test_select_attend_static_validation(K):
+    """The entry point without a workspace rejects a call whose scores and partials exceed the
+    library's static scratch before touching any device, and checks its arguments."""
+    lib = K.lib()
+    p = ctypes.c_void_p(0x5000)
+    fn = lib.kvsel_select_attend_static
+    big = _desc(K, batch=64, num_phys_pages=64 * 4096, max_pages_per_seq=4096)
+    need = lib.kvsel_workspace_bytes(ctypes.byref(big), 64, K.KVSEL_OP_SELECT_ATTEND, 0)
+    assert need > K.KVSEL_STATIC_SCRATCH_BYTES
+    assert fn(ctypes.byref(big), None, p, p, 64, 0, 0.1, p, p, p, p, None) == K.KVSEL_ERR_SCRATCH
+    d = _desc(K)
+    assert lib.kvsel_workspace_bytes(ctypes.byref(d), 64, K.KVSEL_OP_SELECT_ATTEND, 0) <= \
+        K.KVSEL_STATIC_SCRATCH_BYTES
+    assert fn(ctypes.byref(d), None, None, p, 64, 0, 0.1, p, p, p, p, None) == 1  # no summaries
+    assert fn(ctypes.byref(d), None, p, p, 0, 0, 0.1, p, p, p, p, None) == 1      # k < 1
+    assert fn(ctypes.byref(d), None, p, p, 64, 4, 0.1, p, p, p, p, None) == 1     # unknown flag
+    assert fn(ctypes.byref(d), None, p, p, 64, 0, 0.1, p, p, None, p, None) == 1  # no output
 
 
 def test_gather_probe_validation(K):
