@@ -108,16 +108,29 @@ template <int P, int TT, int TPW>
 __device__ __forceinline__ void lookup_tiles(const AttnArgs& a, int list, int b, int split,
                                              int first_tile, TilePages<P, TT, TPW>& tp) {
   constexpr int NPT = TilePages<P, TT, TPW>::NPT;
+  // the ids, the list count and the length are issued unconditionally from clamped indices and
+  // held in front by a scheduling barrier, so they share one memory round trip (left to itself
+  // the compiler issued the length after waiting for the ids)
+  int n_raw[TPW][NPT];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int sp = split * a.pps + ((first_tile + t) * TT) / P + u;
+      n_raw[t][u] = __builtin_amdgcn_readfirstlane(a.sel_idx[(size_t)list * a.k + min(sp, a.k - 1)]);
+    }
+  const int cnt_raw = __builtin_amdgcn_readfirstlane(a.sel_cnt[list]);
+  const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+  __builtin_amdgcn_sched_barrier(0);
+  const int cnt = min(cnt_raw, a.k);
   int n[TPW][NPT];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int u = 0; u < NPT; ++u) {
       const int sp = split * a.pps + ((first_tile + t) * TT) / P + u;
-      n[t][u] = sp < a.k ? __builtin_amdgcn_readfirstlane(a.sel_idx[(size_t)list * a.k + sp]) : -1;
+      n[t][u] = sp < a.k ? n_raw[t][u] : -1;
     }
-  const int cnt = __builtin_amdgcn_readfirstlane(min(a.sel_cnt[list], a.k));
-  const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
