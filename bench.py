@@ -542,9 +542,10 @@ def cpu_baseline(w, lay, budget_s=12.0):
                 parity=dict(selection_bit_exact=ok_sel, attention_max_abs_err=err))
 
 
-def counter_pass(name, dev, n_layers):
-    """Eager steps over the rotated layers, then a plain device copy of exactly 64 MiB: its
-    FETCH_SIZE / WRITE_SIZE per dispatch calibrate the counters against known bytes."""
+def counter_pass(name, dev, n_layers, split_sizes=()):
+    """Eager steps over the rotated layers (and attention calls at the given split sizes), then a
+    plain device copy of exactly 64 MiB: its FETCH_SIZE / WRITE_SIZE per dispatch calibrate the
+    counters against known bytes."""
     w = W.make(name)
     layers = make_layers(w, dev, n_layers)
     for _ in range(2):
@@ -553,6 +554,15 @@ def counter_pass(name, dev, n_layers):
         for lay in layers:
             lay.step_two_calls()  # kvsel_score_topk + kvsel_sparse_decode_attn
     torch.cuda.synchronize()
+    if split_sizes:  # the attention call at other split sizes (dispatches differ in grid size)
+        for pps in split_sizes:
+            for lay in layers:
+                lay.pps = pps
+                lay.ws_attn = K.new_workspace(lay.kv, w.k, K.KVSEL_OP_ATTENTION, pps)
+            for _ in range(2):
+                for lay in layers:
+                    lay.attend()
+            torch.cuda.synchronize()
     src = torch.empty(64 << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -580,6 +590,9 @@ def main():
     ap.add_argument("--counter-pass", action="store_true",
                     help="only run a few eager steps plus a 64 MiB calibration copy (for rocprofv3 "
                          "--pmc FETCH_SIZE / WRITE_SIZE runs) and exit")
+    ap.add_argument("--counter-splits", default="",
+                    help="with --counter-pass: comma-separated split sizes (pages per split) at "
+                         "which the attention call also runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -589,7 +602,8 @@ def main():
     dev = torch.device("cuda:0")
     K.lib()
     if args.counter_pass:
-        counter_pass(args.workload, dev, args.layers)
+        counter_pass(args.workload, dev, args.layers,
+                     [int(x) for x in args.counter_splits.split(",") if x])
         return
     if args.sweep_pps:
         for name in (args.workload, "qwen4b_128k", "ragged_batch"):
