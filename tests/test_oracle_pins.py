@@ -576,6 +576,78 @@ def test_planted_attention_mistakes_are_caught(mistake):
     assert not check_all_pages_is_sdpa(broken, w, scale)
 
 
+def check_dense_is_sdpa(dense_fn, w, scale):
+    """dense_decode_attention over a sequence's tokens against torch's CPU
+    scaled_dot_product_attention (float64), one sequence at a time (lengths differ)."""
+    Ks, Vs = _dense_tokens(w)
+    for b in range(w.B):
+        out, lse = dense_fn(w.q[b:b + 1], Ks[b][None], Vs[b][None], scale)
+        q = w.q[b].double()[None, :, None, :]
+        k = torch.from_numpy(Ks[b]).repeat_interleave(w.G, dim=0)[None]
+        v = torch.from_numpy(Vs[b]).repeat_interleave(w.G, dim=0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale)[0, :, 0]
+        if not np.allclose(out[0], ref.numpy(), rtol=0, atol=1e-12):
+            return False
+        z = scale * torch.einsum("hd,htd->ht", w.q[b].double(), k[0])
+        if not np.allclose(lse[0], torch.logsumexp(z, dim=-1).numpy(), rtol=0, atol=1e-12):
+            return False
+    return True
+
+
+def test_dense_attention_equals_sdpa():
+    w = W.custom(32, B=3, Hq=8, Hkv=2, D=32, P=16, k=4, lens=[50, 16, 1], dtype="bf16")
+    scale = float(np.float32(1.0 / math.sqrt(w.D)))
+    assert check_dense_is_sdpa(O.dense_decode_attention, w, scale)
+
+
+@pytest.mark.parametrize("mistake", ["no_scale", "wrong_head_map"])
+def test_planted_dense_attention_mistakes_are_caught(mistake):
+    w = W.custom(32, B=3, Hq=8, Hkv=2, D=32, P=16, k=4, lens=[50, 16, 1], dtype="bf16")
+    scale = float(np.float32(1.0 / math.sqrt(w.D)))
+
+    def broken(q, keys, values, sc):
+        if mistake == "no_scale":
+            return O.dense_decode_attention(q, keys, values, 1.0)
+        Hq, Hkv = q.shape[1], keys.shape[1]
+        G = Hq // Hkv
+        perm = [(h % Hkv) * G + h // Hkv for h in range(Hq)]  # interleaved groups
+        return O.dense_decode_attention(q[:, perm], keys, values, sc)
+
+    assert not check_dense_is_sdpa(broken, w, scale)
+
+
+def check_decode_step_all_pages(step_fn, w, scale):
+    """The one-step composition (scores, top-k, attention) with k at least every sequence's page
+    count attends over every token: it must equal dense attention on the CPU (torch SDPA)."""
+    summ = O.page_summaries(w.k_pool, w.page_table, w.seq_lens, w.P)
+    kk = max(-(-int(L) // w.P) for L in w.seq_lens)
+    sel, cnt, out, lse = step_fn(w.q, summ, w.k_pool, w.v_pool, w.page_table, w.seq_lens, w.P,
+                                 kk, scale)
+    Ks, Vs = _dense_tokens(w)
+    for b in range(w.B):
+        n = -(-int(w.seq_lens[b]) // w.P)
+        if not (np.asarray(cnt)[b] == n).all():
+            return False
+        q = w.q[b].double()[None, :, None, :]
+        k = torch.from_numpy(Ks[b]).repeat_interleave(w.G, dim=0)[None]
+        v = torch.from_numpy(Vs[b]).repeat_interleave(w.G, dim=0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale)[0, :, 0]
+        if not np.allclose(out[b], ref.numpy(), rtol=0, atol=1e-12):
+            return False
+    return True
+
+
+def test_decode_step_with_every_page_is_dense_attention():
+    w = W.custom(33, B=3, Hq=8, Hkv=2, D=32, P=16, k=4, lens=[70, 33, 5], dtype="bf16")
+    scale = float(np.float32(1.0 / math.sqrt(w.D)))
+    assert check_decode_step_all_pages(O.decode_step, w, scale)
+
+    def broken(q, summ, kp, vp, table, lens, P, k, sc):  # attends over one page too few
+        return O.decode_step(q, summ, kp, vp, table, lens, P, k - 1, sc)
+
+    assert not check_decode_step_all_pages(broken, w, scale)
+
+
 def test_attention_weights_sum_to_one_and_closed_forms():
     w = W.custom(41, B=2, Hq=4, Hkv=2, D=16, P=8, k=3, lens=[29, 9], dtype="bf16")
     sel = np.array([[[0, 2, 3], [1, 3, -1]], [[1, -1, -1], [0, 1, -1]]], dtype=np.int32)
