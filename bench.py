@@ -91,6 +91,13 @@ class Layer:
         self.select()
         self.attend()
 
+    def step_current(self):
+        """The step over summaries that are already current (as kvsel_append_kv keeps them): no
+        tail refresh, so scores + top-k + attention + merge only."""
+        K.select_attend(self.kv, self.summ, self.q, self.k, refresh_tail=False, rope=self.rope,
+                        sel_idx=self.sel, sel_cnt=self.cnt, out=self.out, lse=self.lse,
+                        workspace=self.ws_fused)
+
 
 def make_layers(w, dev, n, fp8=False):
     """n copies of the cache at distinct HBM addresses, used in turn like a model's layers: each
@@ -193,6 +200,7 @@ def measure(name, dev, steps, warmup, n_layers, fp8=False):
     layers = make_layers(w, dev, n_layers, fp8)
     us_step, n = time_graph(layers, steps, warmup)
     us_two, _ = time_graph(layers, steps, warmup, Layer.step_two_calls)
+    us_current, _ = time_graph(layers, steps, warmup, Layer.step_current)
     n_calls = max(len(layers), min(steps, 512) // len(layers) * len(layers))
     attn_mean = time_calls(layers, Layer.attend, n_calls)
     sel_mean = time_calls(layers, Layer.select, n_calls)
@@ -205,7 +213,8 @@ def measure(name, dev, steps, warmup, n_layers, fp8=False):
     probe_bytes = int(layers[0].probe_addr.numel()) * w.P * w.D * esize
     abytes = attention_bytes(w, layers[0])
     sbytes = summary_bytes(w.seq_lens.tolist(), w.Hkv, w.P, w.D, 2 if fp8 else esize)
-    return dict(w=w, layers=layers, us_step=us_step, us_two_calls=us_two, steps=n, attn_us=attn_mean,
+    return dict(w=w, layers=layers, us_step=us_step, us_two_calls=us_two, us_current=us_current,
+                steps=n, attn_us=attn_mean,
                 select_us=sel_mean, attn_bytes=abytes, summary_bytes=sbytes, probe_us=probe_us,
                 probe_bytes=probe_bytes, calls_timed=n_calls)
 
@@ -651,6 +660,9 @@ def main():
         },
         "select_us": round(m["select_us"], 3),
         "two_call_us_per_step": round(m["us_two_calls"], 3),
+        # the same step over summaries already current (no tail refresh): scores + top-k +
+        # attention + merge, the decode step after kvsel_append_kv has updated the tail summary
+        "step_current_summaries_us": round(m["us_current"], 3),
     }
     keep = m["layers"][0]  # its last step's outputs are checked against the CPU oracle
     del m["layers"]
@@ -670,7 +682,8 @@ def main():
         key = name + ("_fp8" if fp8 else "")
         result.setdefault("secondary", {})[key] = {
             "us_per_step": round(s["us_step"], 3),
-            "two_call_us_per_step": round(s["us_two_calls"], 3), "attn_us": round(s["attn_us"], 3),
+            "two_call_us_per_step": round(s["us_two_calls"], 3),
+            "step_current_summaries_us": round(s["us_current"], 3), "attn_us": round(s["attn_us"], 3),
             "attn_GBps": round(sach, 1), "attn_frac": round(sach / HBM_PEAK_GBPS, 4),
             "select_us": round(s["select_us"], 3), "attn_bytes": s["attn_bytes"],
             "layers_rotated": n_layers,
