@@ -5,6 +5,8 @@ rotary-encoded at positions 0..4095 and re-rotated to its absolute offset, then 
 with AR(1)-correlated queries; step t attends over the pages chosen at step t-1 unless the
 group-mean query similarity is below tau.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -40,8 +42,17 @@ def test_rope_table_matches_oracle(K):
     same = table_agreement(gc, gs, oc, os_)
     say(f"rope table: {int(same.sum())}/{same.size} entries bit-identical")
     # both sides round the same fp64 angle's cos/sin; two libms can differ only when the value
-    # sits within an fp64 ulp of an fp32 rounding boundary
+    # sits within an fp64 ulp of an fp32 rounding boundary: every differing entry must be one
     assert same.size - int(same.sum()) <= 4
+    gcn, gsn = gc.cpu().numpy(), gs.cpu().numpy()
+    for r, i in zip(*np.nonzero(~same)):
+        ang = float(r) * math.pow(500000.0, -(2.0 * i) / 128)
+        for v64, got, ref in ((math.cos(ang), gcn[r, i], oc[r, i]), (math.sin(ang), gsn[r, i], os_[r, i])):
+            if got == ref:
+                continue
+            lo, hi = sorted((float(got), float(ref)))  # adjacent fp32 values around the fp64 value
+            mid = 0.5 * (lo + hi)
+            assert abs(v64 - mid) <= 4.0 * np.spacing(abs(v64)), (r, i, v64, got, ref)
 
 
 @pytest.mark.parametrize("dtype,D,P,row_step,in_place", [
