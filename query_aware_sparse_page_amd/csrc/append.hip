@@ -119,8 +119,8 @@ __global__ __launch_bounds__(APPEND_MAX_WAVES * 64) void append_kernel(AppendArg
         unpack<T>(hraw, h0);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          l0[e] = fminf(l0[e], k[e]);
-          h0[e] = fmaxf(h0[e], k[e]);
+          l0[e] = tmin(l0[e], k[e]);
+          h0[e] = tmax(h0[e], k[e]);
         }
         lo = pack<T>(l0);
         hi = pack<T>(h0);

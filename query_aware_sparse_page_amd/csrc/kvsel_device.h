@@ -55,6 +55,13 @@ __device__ __forceinline__ float round_to_elem<bf16_t>(float x) {
   return (float)(__bf16)x;
 }
 
+// Min / max of summary extremes (page summaries, their tail refresh and the append's running
+// update): IEEE 754-2019 minimum / maximum, so a NaN key propagates and -0 < +0; gfx950 has them as
+// native three-operand instructions (v_minimum3_f32 / v_maximum3_f32), where fminf / fmaxf also
+// need a quieting step per operand.
+__device__ __forceinline__ float tmin(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+__device__ __forceinline__ float tmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 

@@ -83,62 +83,4 @@ __device__ __forceinline__ uint32_t f64_to_bf16_directed(double x) {
   return b;
 }
 
-// Min / max of the valid rows (1 <= valid; more than P means the whole page; with page_fill, rows
-// from page_fill[pt] on are excluded too, read after the row loads are issued) of one fp8
-// (page, KV head) tile of physical page pt, times the tile's scale, rounded outward to bf16, by
-// one wave. The lane layout is
-// bf16's (row_map<bf16_t, D>: 8 channels per lane); each lane loads 8 codes per row. On return
-// every lane holds lo / hi of its channels [c0, c0 + 8) as bf16 values in fp32.
-template <int D>
-__device__ __forceinline__ void tile_minmax_fp8(const uint8_t* tile, int valid,
-                                                const int32_t* page_fill, int pt, int P, int lane,
-                                                float scale, float* lo, float* hi) {
-  using M = row_map<bf16_t, D>;
-  constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
-  constexpr int MAX_LOADS = 32 / RPW;
-  valid = min(valid, P);
-  const int rg = lane / LPR;
-  const int c0 = (lane % LPR) * VEC;
-  uint2 raw[MAX_LOADS];
-#pragma unroll
-  for (int i = 0; i < MAX_LOADS; ++i) {
-    const int s = rg + i * RPW;
-    raw[i] = load8(tile + (size_t)min(s, valid - 1) * D + c0);
-  }
-  const int fill = page_fill ? page_fill[pt] : P;
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    lo[e] = __int_as_float(0x7f800000);
-    hi[e] = __int_as_float(0xff800000);
-  }
-#pragma unroll
-  for (int i = 0; i < MAX_LOADS; ++i) {
-    const int s = rg + i * RPW;
-    if (i * RPW >= P) break;
-    float x[VEC];
-    fp8x8_to_f32(raw[i], x);
-    if (s < valid && s < fill) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        lo[e] = fminf(lo[e], x[e]);
-        hi[e] = fmaxf(hi[e], x[e]);
-      }
-    }
-  }
-#pragma unroll
-  for (int m = LPR; m < 64; m <<= 1) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      lo[e] = fminf(lo[e], lane_xor_f32(lo[e], m));
-      hi[e] = fmaxf(hi[e], lane_xor_f32(hi[e], m));
-    }
-  }
-  const double sd = (double)scale;
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) {  // a code's value times an fp32 scale is exact in fp64
-    lo[e] = __uint_as_float(f64_to_bf16_directed<false>((double)lo[e] * sd) << 16);
-    hi[e] = __uint_as_float(f64_to_bf16_directed<true>((double)hi[e] * sd) << 16);
-  }
-}
-
 }  // namespace kvsel

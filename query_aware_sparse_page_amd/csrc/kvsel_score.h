@@ -4,6 +4,8 @@
 // the group-mean query similarity of the speculative-reuse decision.
 #pragma once
 
+#include <type_traits>
+
 #include "kvsel_device.h"
 #include "kvsel_fp8.h"
 #include "kvsel_internal.h"
@@ -28,58 +30,216 @@ struct SelectArgs {
   const int32_t* page_fill;  // [Npp] valid slots per physical page, or null (the tail refresh)
 };
 
-// Min / max of the valid rows (1 <= valid; more than P means the whole page; with page_fill, rows
-// from page_fill[pt] on are excluded too, read after the row loads are issued) of one (page, KV
-// head) tile of physical page pt, computed by one wave; rope_idx is its rotary page_row entry. On return every lane holds lo / hi of its
-// channels [c0, c0 + VEC). The row loads are unconditional (rows past `valid` re-read the last
-// valid row and are ignored), so they all go out at once; the page's rotary row is read after them.
-template <typename T, int D>
-__device__ __forceinline__ void tile_minmax(const T* tile, int valid, const int32_t* page_fill,
-                                            int P, int lane, int pt, int rope_idx,
-                                            const RopeArgs& rope, float* lo, float* hi) {
-  valid = min(valid, P);  // a length past the page bound: every row of the last page counted
+// ---- min / max of one key tile (the summary build and its tail refresh) ----
+
+// One wave's share of the rows of one (page, KV head) tile: wave wv of the NW waves that share the
+// tile takes rows wv * RPW + rg + i * NW * RPW (rg the lane's row group). Row indices at or past
+// `valid` (1 <= valid <= P) are clamped to valid - 1, so every load reads -- and, with the rotary
+// gather, rotates -- a valid row and a fold over all of them needs no guard; loads past the page
+// (P = 16) repeat the wave's first row. fp8 pools (FP8): 8 codes per lane and row (bf16's layout).
+template <typename T, int D, int NW, bool FP8>
+struct TileRows {
   using M = row_map<T, D>;
-  constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
-  constexpr int MAX_LOADS = 32 / RPW;
-  const int rg = lane / LPR;
-  const int c0 = (lane % LPR) * VEC;
-  uint4 raw[MAX_LOADS];
-#pragma unroll
-  for (int i = 0; i < MAX_LOADS; ++i) {
-    const int s = rg + i * RPW;
-    raw[i] = load16(tile + (size_t)min(s, valid - 1) * D + c0);
+  static constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
+  static constexpr int STRIDE = NW * RPW;                 // rows between a lane's loads
+  static constexpr int NL = (32 + STRIDE - 1) / STRIDE;   // loads per lane: a page has <= 32 rows
+  using Raw = std::conditional_t<FP8, uint2, uint4>;
+  Raw raw[NL];
+  int first, last, P;  // the lane's first row, the last valid row, the page size
+
+  // Row of load i (recomputed where needed: the kernels that hold a whole block's work in
+  // registers cannot spare one per load).
+  __device__ __forceinline__ int row(int i) const {
+    return min(i * STRIDE < P ? first + i * STRIDE : first, last);
   }
-  const int fill = page_fill ? page_fill[pt] : P;
-  const int prow = rope.page_row ? rope.page_row[rope_idx] : -1;
+
+  __device__ __forceinline__ void load(const void* tile, int valid, int P_, int lane, int wv) {
+    first = wv * RPW + lane / LPR;
+    last = valid - 1;
+    P = P_;
+    const int c0 = (lane % LPR) * VEC;
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    lo[e] = __int_as_float(0x7f800000);
-    hi[e] = __int_as_float(0xff800000);
+    for (int i = 0; i < NL; ++i) {
+      if constexpr (FP8)
+        raw[i] = load8((const uint8_t*)tile + (size_t)row(i) * D + c0);
+      else
+        raw[i] = load16((const T*)tile + (size_t)row(i) * D + c0);
+    }
   }
+
+  // Row i's slice as fp32 (unpacked; fp8 codes decoded, unscaled).
+  __device__ __forceinline__ void decode(int i, float* x) const {
+    if constexpr (FP8)
+      fp8x8_to_f32(raw[i], x);
+    else
+      unpack<T>(raw[i], x);
+  }
+
+  // Min / max over the lane's rows. Without a guard or rotation every row folds in, starting from
+  // the first, so the compiler may pair rows into three-operand min / max. With page_fill (GUARD)
+  // or the rotary gather (ROPE), lo / hi start at +inf / -inf and take one row at a time, rows at
+  // or past `valid` or `fill` skipped: a rotated row uses its own position (prow: the page's first
+  // rotary row, -1 for none), and each row's cos / sin loads stay live for that row only.
+  template <bool ROPE, bool GUARD>
+  __device__ __forceinline__ void fold(int c0, int valid, int fill, int prow,
+                                       const RopeArgs& rope, float* lo, float* hi) const {
+    if constexpr (!ROPE && !GUARD) {
 #pragma unroll
-  for (int i = 0; i < MAX_LOADS; ++i) {
-    const int s = rg + i * RPW;
-    if (i * RPW >= P) break;
-    float x[VEC];
-    unpack<T>(raw[i], x);
-    if (rope.page_row)
-      rope_rotate_slice<T, D>(x, c0, prow < 0 ? -1 : prow + rope.row_step * s, rope.cos, rope.sin);
-    if (s < valid && s < fill) {
+      for (int i = 0; i < NL; ++i) {
+        float x[VEC];
+        decode(i, x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          lo[e] = i == 0 ? x[e] : tmin(lo[e], x[e]);
+          hi[e] = i == 0 ? x[e] : tmax(hi[e], x[e]);
+        }
+      }
+    } else {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        lo[e] = fminf(lo[e], x[e]);
-        hi[e] = fmaxf(hi[e], x[e]);
+        lo[e] = __int_as_float(0x7f800000);
+        hi[e] = __int_as_float(0xff800000);
+      }
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        if (i * STRIDE >= P) break;
+        const int s = first + i * STRIDE;  // the row itself (loads past `valid` were clamped)
+        float x[VEC];
+        decode(i, x);
+        if constexpr (ROPE)  // every lane takes part in the partner exchange
+          rope_rotate_slice<T, D>(x, c0, prow < 0 ? -1 : prow + rope.row_step * s, rope.cos,
+                                  rope.sin);
+        if (s < valid && s < fill) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            lo[e] = tmin(lo[e], x[e]);
+            hi[e] = tmax(hi[e], x[e]);
+          }
+        }
       }
     }
   }
+};
+
+// Min / max of lane's channels [c0, c0 + VEC) over its rows of wave wv's share (of NW) of the
+// valid rows of one tile of physical page pt (1 <= valid; more than P means the whole page; with
+// page_fill, rows from page_fill[pt] on are excluded too, read after the row loads are issued);
+// rope_idx is the page's rotary page_row entry (f32 / bf16 pools). Not folded across lanes.
+template <typename T, int D, int NW, bool FP8>
+__device__ __forceinline__ void tile_rows_minmax(const void* tile, int valid,
+                                                 const int32_t* page_fill, int P, int lane, int wv,
+                                                 int pt, int rope_idx, const RopeArgs& rope,
+                                                 float* lo, float* hi) {
+  TileRows<T, D, NW, FP8> r;
+  valid = min(valid, P);
+  r.load(tile, valid, P, lane, wv);
+  const int c0 = (lane % row_map<T, D>::LPR) * row_map<T, D>::VEC;
+  const bool rot = !FP8 && rope.page_row != nullptr;
+  const int prow = rot ? rope.page_row[rope_idx] : -1;
+  const int fill = page_fill ? page_fill[pt] : P;
+  if (rot)
+    r.template fold<!FP8, true>(c0, valid, fill, prow, rope, lo, hi);
+  else if (page_fill)
+    r.template fold<false, true>(c0, valid, fill, prow, rope, lo, hi);
+  else
+    r.template fold<false, false>(c0, valid, fill, prow, rope, lo, hi);
+}
+
+// lo / hi folded over the lanes that share a channel slice (lane ^ LPR, ..., lane ^ 32): every
+// lane ends with the min / max of its channels.
+template <int LPR, int VEC>
+__device__ __forceinline__ void fold_lanes(float* lo, float* hi) {
 #pragma unroll
   for (int m = LPR; m < 64; m <<= 1) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      lo[e] = fminf(lo[e], lane_xor_f32(lo[e], m));
-      hi[e] = fmaxf(hi[e], lane_xor_f32(hi[e], m));
+      lo[e] = tmin(lo[e], lane_xor_f32(lo[e], m));
+      hi[e] = tmax(hi[e], lane_xor_f32(hi[e], m));
     }
   }
+}
+
+// Values a lane keeps after fold_lanes_scatter: one halving per lane swap (m = 16 and m = 32).
+template <int LPR, int VEC>
+constexpr int scatter_kept() { return LPR <= 16 ? VEC / 4 : VEC / 2; }
+
+// The fold of fold_lanes as a reduce-scatter: at m = 16 and m = 32 one lane swap (gfx950 permlane16 /
+// permlane32 swap of lo[i] and lo[i + h]) moves two values at once, and the min of the swapped pair
+// leaves lo[i]'s result in one half of the lanes and lo[i + h]'s in the other; each step halves
+// what a lane holds, at one swap and one min / max per pair. A smaller xor (8 lanes per row) folds
+// in full first. On return lo / hi[0, K) (K = scatter_kept) are the results for channels
+// c0 + off + [0, K); the return value is off.
+template <int LPR, int VEC>
+__device__ __forceinline__ int fold_lanes_scatter(float* lo, float* hi) {
+  static_assert(LPR >= 8 && LPR <= 32, "lanes per row");
+#pragma unroll
+  for (int m = LPR; m < 16; m <<= 1) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      lo[e] = tmin(lo[e], lane_xor_f32(lo[e], m));
+      hi[e] = tmax(hi[e], lane_xor_f32(hi[e], m));
+    }
+  }
+  const int lane = threadIdx.x & 63;
+  int n = VEC, off = 0;
+  if constexpr (LPR <= 16) {  // rows of 16 lanes: odd rows take lo[i + h]
+    const int h = n / 2;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      auto rl = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo[i]), __float_as_uint(lo[i + h]), false, false);
+      auto rh = __builtin_amdgcn_permlane16_swap(__float_as_uint(hi[i]), __float_as_uint(hi[i + h]), false, false);
+      lo[i] = tmin(__uint_as_float(rl[0]), __uint_as_float(rl[1]));
+      hi[i] = tmax(__uint_as_float(rh[0]), __uint_as_float(rh[1]));
+    }
+    off += (lane & 16) ? h : 0;
+    n = h;
+  }
+  {  // halves of 32 lanes: the upper half takes lo[i + h]
+    const int h = n / 2;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      auto rl = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo[i]), __float_as_uint(lo[i + h]), false, false);
+      auto rh = __builtin_amdgcn_permlane32_swap(__float_as_uint(hi[i]), __float_as_uint(hi[i + h]), false, false);
+      lo[i] = tmin(__uint_as_float(rl[0]), __uint_as_float(rl[1]));
+      hi[i] = tmax(__uint_as_float(rh[0]), __uint_as_float(rh[1]));
+    }
+    off += (lane & 32) ? h : 0;
+  }
+  return off;
+}
+
+// fp8 tile extremes (codes' values) times the tile's scale, rounded outward to bf16; a code's
+// value times an fp32 scale is exact in fp64.
+template <int VEC>
+__device__ __forceinline__ void fp8_scale_outward(float scale, float* lo, float* hi) {
+  const double sd = (double)scale;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    lo[e] = __uint_as_float(f64_to_bf16_directed<false>((double)lo[e] * sd) << 16);
+    hi[e] = __uint_as_float(f64_to_bf16_directed<true>((double)hi[e] * sd) << 16);
+  }
+}
+
+// Min / max of the valid rows of one (page, KV head) tile, computed by one wave: on return every
+// lane holds lo / hi of its channels [c0, c0 + VEC), rotated first when the rotary gather is on.
+template <typename T, int D>
+__device__ __forceinline__ void tile_minmax(const T* tile, int valid, const int32_t* page_fill,
+                                            int P, int lane, int pt, int rope_idx,
+                                            const RopeArgs& rope, float* lo, float* hi) {
+  tile_rows_minmax<T, D, 1, false>(tile, valid, page_fill, P, lane, 0, pt, rope_idx, rope, lo, hi);
+  fold_lanes<row_map<T, D>::LPR, row_map<T, D>::VEC>(lo, hi);
+}
+
+// The same for an fp8 tile (bf16's lane layout, 8 channels per lane), times the tile's scale and
+// rounded outward to bf16: every lane holds bf16 values in fp32.
+template <int D>
+__device__ __forceinline__ void tile_minmax_fp8(const uint8_t* tile, int valid,
+                                                const int32_t* page_fill, int pt, int P, int lane,
+                                                float scale, float* lo, float* hi) {
+  tile_rows_minmax<bf16_t, D, 1, true>(tile, valid, page_fill, P, lane, 0, pt, 0, RopeArgs{}, lo,
+                                       hi);
+  fold_lanes<row_map<bf16_t, D>::LPR, row_map<bf16_t, D>::VEC>(lo, hi);
+  fp8_scale_outward<row_map<bf16_t, D>::VEC>(scale, lo, hi);
 }
 
 // The tail refresh's rebuild of the (physical page pt, KV head j) tile's summary by one wave: the
@@ -103,34 +263,37 @@ __device__ __forceinline__ void refresh_tile(const SelectArgs& a, int b, int n, 
 // query slice in fp64 (a bf16 x bf16 or fp32 x fp32 product is exact in fp64), take q*hi for
 // q >= 0 and q*lo otherwise, and fold the LPR lanes; one fp64 -> fp32 rounding per score. Each
 // lane group scores U pages (U > 1 for wide tables: fewer blocks, more loads in flight per lane).
-// With the tail refresh on, the wave holding the sequence's last page first rebuilds that page's
-// summary from the key pool, writes it, and scores it from the fresh values.
+// With the tail refresh on, the block holding the sequence's last page first rebuilds that page's
+// summary from the key pool -- every wave folds a share of the tile's rows, the waves meet in LDS
+// -- and the wave that scores the page writes the summary and scores it from the fresh values.
 template <typename T, int D, int G, int WAVES, int U = 1, bool FP8 = false>
 __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, int chunk) {
   using M = row_map<T, D>;
   constexpr int VEC = M::VEC, LPR = M::LPR;
   constexpr int PPW = 64 / LPR;          // pages per wave and unroll step
   constexpr int PPB = WAVES * PPW * U;   // pages per block
+  constexpr int NPT = (PPB + 63) / 64;   // page-id loads per lane (the block's pages)
 
   const int list = b * a.Hkv + j;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = a.P;
-  const int wn0 = chunk * PPB + w * PPW * U;  // first page of this wave
+  const int pb0 = chunk * PPB;            // first page of this block
+  const int wn0 = pb0 + w * PPW * U;      // first page of this wave
   const int Hq = a.Hkv * G;
   const T* q = (const T*)a.q;
   const int c0 = (lane % LPR) * VEC;
   const int rgl = lane / LPR;  // the lane's row group: page wn0 + u * PPW + rgl at step u
 
-  // ---- loads first (unconditional, clamped addresses), all in one round: the page ids (used
-  // only for the tail refresh), q slice, summary rows (sequence-major, so no page-table hop) and
-  // the sequence length ----
-  // the page ids first: the wave that refreshes the tail page waits for them alone (loads
+  // ---- loads first (unconditional, clamped addresses), all in one round: the block's page ids
+  // (used only for the tail refresh), q slice, summary rows (sequence-major, so no page-table hop)
+  // and the sequence length ----
+  // the page ids first: the block that refreshes the tail page waits for them alone (loads
   // complete in issue order) and sends its key-tile loads while the summary rows are in flight
   // (entries past the sequence may hold anything and are clamped into the pool, never used)
-  int pt_raw[U];
+  int pt_raw[NPT];
 #pragma unroll
-  for (int u = 0; u < U; ++u)  // indices from the row width only: no wait for seq_lens
-    pt_raw[u] = a.page_table[(size_t)b * a.maxp + min(wn0 + u * PPW + rgl, a.maxn - 1)];
+  for (int k = 0; k < NPT; ++k)  // indices from the row width only: no wait for seq_lens
+    pt_raw[k] = a.page_table[(size_t)b * a.maxp + min(pb0 + k * 64 + lane, a.maxn - 1)];
   uint4 qraw[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) qraw[g] = load16(q + ((size_t)b * Hq + j * G + g) * D + c0);
@@ -146,27 +309,70 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
   const int L = a.seq_lens[b];
   const int N = L > 0 ? min((L + P - 1) / P, a.maxn) : 0;  // never past the live bound
 
-  // ---- decode-time refresh of the tail page's summary, by the wave that scores that page: the
-  // page id is already in its lanes, so the key tile loads go out one hop after the page table,
-  // alongside the summary loads, and no other wave waits ----
+  // ---- decode-time refresh of the tail page's summary by the block that holds the page: its id
+  // is already in the lanes, so the key-tile loads go out one hop after the page table, alongside
+  // the summary loads; each wave folds its share of the tile's rows, the partial extremes meet in
+  // LDS, and the wave that scores the page combines them ----
   const int nt = N - 1;
-  const bool tail = a.refresh_tail && N > 0 && nt >= wn0 && nt < wn0 + PPW * U;  // wave-uniform
+  const int to = nt - pb0;  // the tail page's place in the block
+  const bool btail = a.refresh_tail && N > 0 && to >= 0 && to < PPB;  // block-uniform
+  const bool tail = btail && nt >= wn0 && nt < wn0 + PPW * U;         // wave-uniform
   const int t_off = nt - wn0;
   const int ut = tail ? t_off / PPW : -1, rg = t_off % PPW;  // its unroll step and row group
   float flo[VEC], fhi[VEC];
-  if (tail) {
+  if (btail) {
     int pt = 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {  // scalar selects (a uniform index into pt_raw would spill it)
-      const int x = __builtin_amdgcn_readlane(pt_raw[u], rg * LPR);
-      pt = u == ut ? x : pt;
+    for (int k = 0; k < NPT; ++k) {  // scalar selects (a uniform index into pt_raw would spill it)
+      const int x = __builtin_amdgcn_readlane(pt_raw[k], to & 63);
+      pt = k == (to >> 6) ? x : pt;
     }
     pt = min(max(pt, 0), a.Npp - 1);
-    refresh_tile<T, D, FP8>(a, b, nt, pt, j, L - nt * P, lane, flo, fhi);
-    if (lane < LPR) {
-      T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;
-      store16(out + c0, pack<T>(flo));
-      store16(out + D + c0, pack<T>(fhi));
+    const size_t t = (size_t)pt * a.Hkv + j;
+    float ksc = 1.0f;
+    if constexpr (FP8) ksc = a.k_scale[t];  // in flight with the tile
+    float plo[VEC], phi[VEC];
+    if constexpr (FP8)
+      tile_rows_minmax<T, D, WAVES, true>((const uint8_t*)a.k_pool + t * P * D, L - nt * P,
+                                          a.page_fill, P, lane, w, pt, 0, a.rope, plo, phi);
+    else
+      tile_rows_minmax<T, D, WAVES, false>((const T*)a.k_pool + t * P * D, L - nt * P,
+                                           a.page_fill, P, lane, w, pt,
+                                           rope_row_index(a.rope, b, nt, pt), a.rope, plo, phi);
+    const int off = fold_lanes_scatter<LPR, VEC>(plo, phi);
+    __shared__ __align__(16) float s_fold[WAVES][2][D];  // each wave's extremes of the tile
+#pragma unroll
+    for (int i = 0; i < scatter_kept<LPR, VEC>(); ++i) {
+      s_fold[w][0][c0 + off + i] = plo[i];
+      s_fold[w][1][c0 + off + i] = phi[i];
+    }
+    __syncthreads();
+    if (tail) {
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) {
+        const float4 l0 = *(const float4*)&s_fold[0][0][c0 + e];
+        const float4 h0 = *(const float4*)&s_fold[0][1][c0 + e];
+        flo[e] = l0.x, flo[e + 1] = l0.y, flo[e + 2] = l0.z, flo[e + 3] = l0.w;
+        fhi[e] = h0.x, fhi[e + 1] = h0.y, fhi[e + 2] = h0.z, fhi[e + 3] = h0.w;
+      }
+#pragma unroll
+      for (int v = 1; v < WAVES; ++v) {
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+          const float4 l = *(const float4*)&s_fold[v][0][c0 + e];
+          const float4 h = *(const float4*)&s_fold[v][1][c0 + e];
+          flo[e] = tmin(flo[e], l.x), flo[e + 1] = tmin(flo[e + 1], l.y);
+          flo[e + 2] = tmin(flo[e + 2], l.z), flo[e + 3] = tmin(flo[e + 3], l.w);
+          fhi[e] = tmax(fhi[e], h.x), fhi[e + 1] = tmax(fhi[e + 1], h.y);
+          fhi[e + 2] = tmax(fhi[e + 2], h.z), fhi[e + 3] = tmax(fhi[e + 3], h.w);
+        }
+      }
+      if constexpr (FP8) fp8_scale_outward<VEC>(ksc, flo, fhi);
+      if (lane < LPR) {
+        T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;
+        store16(out + c0, pack<T>(flo));
+        store16(out + D + c0, pack<T>(fhi));
+      }
     }
   }
 

@@ -10,6 +10,7 @@
 #include "kvsel_device.h"
 #include "kvsel_fp8.h"
 #include "kvsel_internal.h"
+#include "kvsel_score.h"
 
 namespace kvsel {
 
@@ -49,61 +50,17 @@ __global__ __launch_bounds__(256) void summaries_kernel(const T* __restrict__ k_
                                                         const int32_t* __restrict__ page_fill,
                                                         RopeArgs rope, T* __restrict__ summ) {
   using M = row_map<T, D>;
-  constexpr int VEC = M::VEC, LPR = M::LPR, RPW = M::RPW;
-  constexpr int MAX_LOADS = 32 / RPW;  // P <= 32
-
   const int lane = threadIdx.x & 63;
   const long unit = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   int b, n, j, p, valid;
   if (!summary_unit(unit, page_table, seq_lens, B, Hkv, P, maxp, maxn, Npp, tail_only, b, n, j, p,
                     valid))
     return;
-  const int rg = lane / LPR;
-  const int c0 = (lane % LPR) * VEC;
-
-  const T* tile = k_pool + ((size_t)p * Hkv + j) * P * D;
-  uint4 raw[MAX_LOADS];
-#pragma unroll
-  for (int i = 0; i < MAX_LOADS; ++i) {
-    const int s = rg + i * RPW;
-    // unconditional (rows past `valid` >= 1 re-read the last valid row and are ignored below),
-    // so every load goes out before the first wait
-    raw[i] = load16(tile + (size_t)min(s, valid - 1) * D + c0);
-  }
-
-  // a composed sequence's page may end early: masks only, read after the row loads
-  const int fill = page_fill ? page_fill[p] : P;
-  float lo[VEC], hi[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    lo[e] = __int_as_float(0x7f800000);   // +inf
-    hi[e] = __int_as_float(0xff800000);   // -inf
-  }
-  const int prow = rope.page_row ? rope.page_row[rope_row_index(rope, b, n, p)] : -1;
-#pragma unroll
-  for (int i = 0; i < MAX_LOADS; ++i) {
-    const int s = rg + i * RPW;
-    if (i * RPW >= P) break;
-    float x[VEC];
-    unpack<T>(raw[i], x);
-    if (rope.page_row)  // all lanes take part in the partner exchange
-      rope_rotate_slice<T, D>(x, c0, prow < 0 ? -1 : prow + rope.row_step * s, rope.cos, rope.sin);
-    if (s < valid && s < fill) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        lo[e] = fminf(lo[e], x[e]);
-        hi[e] = fmaxf(hi[e], x[e]);
-      }
-    }
-  }
-#pragma unroll
-  for (int m = LPR; m < 64; m <<= 1) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      lo[e] = fminf(lo[e], lane_xor_f32(lo[e], m));
-      hi[e] = fmaxf(hi[e], lane_xor_f32(hi[e], m));
-    }
-  }
+  const int rg = lane / M::LPR;
+  const int c0 = (lane % M::LPR) * M::VEC;
+  float lo[M::VEC], hi[M::VEC];
+  tile_minmax<T, D>(k_pool + ((size_t)p * Hkv + j) * P * D, valid, page_fill, P, lane, p,
+                    rope_row_index(rope, b, n, p), rope, lo, hi);
   if (rg == 0) {
     T* out = summ + (((size_t)b * Hkv + j) * maxp + n) * 2 * D;
     store16(out + c0, pack<T>(lo));
