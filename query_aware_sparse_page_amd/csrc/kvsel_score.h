@@ -125,24 +125,43 @@ struct TileRows {
 // valid rows of one tile of physical page pt (1 <= valid; more than P means the whole page; with
 // page_fill, rows from page_fill[pt] on are excluded too, read after the row loads are issued);
 // rope_idx is the page's rotary page_row entry (f32 / bf16 pools). Not folded across lanes.
+// start() issues every load, finish() folds: work that needs none of the tile can run between.
+template <typename T, int D, int NW, bool FP8>
+struct TileMinMax {
+  TileRows<T, D, NW, FP8> r;
+  int c0, valid, fill, prow;
+  bool rot, guard;
+
+  __device__ __forceinline__ void start(const void* tile, int valid_, const int32_t* page_fill,
+                                        int P, int lane, int wv, int pt, int rope_idx,
+                                        const RopeArgs& rope) {
+    valid = min(valid_, P);
+    r.load(tile, valid, P, lane, wv);
+    c0 = (lane % row_map<T, D>::LPR) * row_map<T, D>::VEC;
+    rot = !FP8 && rope.page_row != nullptr;
+    prow = rot ? rope.page_row[rope_idx] : -1;
+    guard = page_fill != nullptr;
+    fill = guard ? page_fill[pt] : P;
+  }
+
+  __device__ __forceinline__ void finish(const RopeArgs& rope, float* lo, float* hi) const {
+    if (rot)
+      r.template fold<!FP8, true>(c0, valid, fill, prow, rope, lo, hi);
+    else if (guard)
+      r.template fold<false, true>(c0, valid, fill, prow, rope, lo, hi);
+    else
+      r.template fold<false, false>(c0, valid, fill, prow, rope, lo, hi);
+  }
+};
+
 template <typename T, int D, int NW, bool FP8>
 __device__ __forceinline__ void tile_rows_minmax(const void* tile, int valid,
                                                  const int32_t* page_fill, int P, int lane, int wv,
                                                  int pt, int rope_idx, const RopeArgs& rope,
                                                  float* lo, float* hi) {
-  TileRows<T, D, NW, FP8> r;
-  valid = min(valid, P);
-  r.load(tile, valid, P, lane, wv);
-  const int c0 = (lane % row_map<T, D>::LPR) * row_map<T, D>::VEC;
-  const bool rot = !FP8 && rope.page_row != nullptr;
-  const int prow = rot ? rope.page_row[rope_idx] : -1;
-  const int fill = page_fill ? page_fill[pt] : P;
-  if (rot)
-    r.template fold<!FP8, true>(c0, valid, fill, prow, rope, lo, hi);
-  else if (page_fill)
-    r.template fold<false, true>(c0, valid, fill, prow, rope, lo, hi);
-  else
-    r.template fold<false, false>(c0, valid, fill, prow, rope, lo, hi);
+  TileMinMax<T, D, NW, FP8> m;
+  m.start(tile, valid, page_fill, P, lane, wv, pt, rope_idx, rope);
+  m.finish(rope, lo, hi);
 }
 
 // lo / hi folded over the lanes that share a channel slice (lane ^ LPR, ..., lane ^ 32): every
@@ -257,6 +276,24 @@ __device__ __forceinline__ void refresh_tile(const SelectArgs& a, int b, int n, 
                       rope_row_index(a.rope, b, n, pt), a.rope, lo, hi);
 }
 
+// Score of one page from its lo / hi slices, by the LPR lanes that hold the page (every lane
+// returns the group's sum): sum over the group's heads and the channels of q*hi for q >= 0 and
+// q*lo otherwise, each product exact in fp64, folded over the LPR lanes.
+template <int G, int VEC, int LPR>
+__device__ __forceinline__ double page_score(const double (&qd)[G][VEC], const float* lo,
+                                             const float* hi) {
+  double acc = 0.0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const double x = (double)(qd[g][e] >= 0.0 ? hi[e] : lo[e]);
+      acc = fma(qd[g][e], x, acc);
+    }
+  }
+  return seg_sum_f64<LPR>(acc);
+}
+
 // Scores of chunk `chunk` (WAVES * U * 64 / LPR consecutive pages) of list (sequence b, KV head
 // j), by one block of WAVES waves: LPR lanes read a page's lo and hi rows as 16-byte slices
 // (sequence-major summaries: one contiguous run per wave and unroll step), multiply by the group's
@@ -309,18 +346,141 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
   const int L = a.seq_lens[b];
   const int N = L > 0 ? min((L + P - 1) / P, a.maxn) : 0;  // never past the live bound
 
-  // ---- decode-time refresh of the tail page's summary by the block that holds the page: its id
-  // is already in the lanes, so the key-tile loads go out one hop after the page table, alongside
-  // the summary loads; each wave folds its share of the tile's rows, the partial extremes meet in
-  // LDS, and the wave that scores the page combines them ----
+  // ---- the decode-time refresh: the sequence's last page, the block and the wave holding it ----
   const int nt = N - 1;
   const int to = nt - pb0;  // the tail page's place in the block
   const bool btail = a.refresh_tail && N > 0 && to >= 0 && to < PPB;  // block-uniform
   const bool tail = btail && nt >= wn0 && nt < wn0 + PPW * U;         // wave-uniform
-  const int t_off = nt - wn0;
-  const int ut = tail ? t_off / PPW : -1, rg = t_off % PPW;  // its unroll step and row group
-  float flo[VEC], fhi[VEC];
-  if (btail) {
+
+  if constexpr (U == 1) {
+    const int t_off = nt - wn0;
+    const int ut = tail ? t_off / PPW : -1, rg = t_off % PPW;  // its unroll step and row group
+    float flo[VEC], fhi[VEC];
+    if (btail) {
+      int pt = 0;
+#pragma unroll
+      for (int k = 0; k < NPT; ++k) {  // scalar selects (a uniform index into pt_raw would spill it)
+        const int x = __builtin_amdgcn_readlane(pt_raw[k], to & 63);
+        pt = k == (to >> 6) ? x : pt;
+      }
+      pt = min(max(pt, 0), a.Npp - 1);
+      const size_t t = (size_t)pt * a.Hkv + j;
+      float ksc = 1.0f;
+      if constexpr (FP8) ksc = a.k_scale[t];  // in flight with the tile
+      float plo[VEC], phi[VEC];
+      if constexpr (FP8)
+        tile_rows_minmax<T, D, WAVES, true>((const uint8_t*)a.k_pool + t * P * D, L - nt * P,
+                                            a.page_fill, P, lane, w, pt, 0, a.rope, plo, phi);
+      else
+        tile_rows_minmax<T, D, WAVES, false>((const T*)a.k_pool + t * P * D, L - nt * P,
+                                             a.page_fill, P, lane, w, pt,
+                                             rope_row_index(a.rope, b, nt, pt), a.rope, plo, phi);
+      const int off = fold_lanes_scatter<LPR, VEC>(plo, phi);
+      __shared__ __align__(16) float s_fold[WAVES][2][D];  // each wave's extremes of the tile
+#pragma unroll
+      for (int i = 0; i < scatter_kept<LPR, VEC>(); ++i) {
+        s_fold[w][0][c0 + off + i] = plo[i];
+        s_fold[w][1][c0 + off + i] = phi[i];
+      }
+      __syncthreads();
+      if (tail) {
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+          const float4 l0 = *(const float4*)&s_fold[0][0][c0 + e];
+          const float4 h0 = *(const float4*)&s_fold[0][1][c0 + e];
+          flo[e] = l0.x, flo[e + 1] = l0.y, flo[e + 2] = l0.z, flo[e + 3] = l0.w;
+          fhi[e] = h0.x, fhi[e + 1] = h0.y, fhi[e + 2] = h0.z, fhi[e + 3] = h0.w;
+        }
+#pragma unroll
+        for (int v = 1; v < WAVES; ++v) {
+#pragma unroll
+          for (int e = 0; e < VEC; e += 4) {
+            const float4 l = *(const float4*)&s_fold[v][0][c0 + e];
+            const float4 h = *(const float4*)&s_fold[v][1][c0 + e];
+            flo[e] = tmin(flo[e], l.x), flo[e + 1] = tmin(flo[e + 1], l.y);
+            flo[e + 2] = tmin(flo[e + 2], l.z), flo[e + 3] = tmin(flo[e + 3], l.w);
+            fhi[e] = tmax(fhi[e], h.x), fhi[e + 1] = tmax(fhi[e + 1], h.y);
+            fhi[e + 2] = tmax(fhi[e + 2], h.z), fhi[e + 3] = tmax(fhi[e + 3], h.w);
+          }
+        }
+        if constexpr (FP8) fp8_scale_outward<VEC>(ksc, flo, fhi);
+        if (lane < LPR) {
+          T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;
+          store16(out + c0, pack<T>(flo));
+          store16(out + D + c0, pack<T>(fhi));
+        }
+      }
+    }
+
+    // ---- scores of this wave's pages ----
+    double qd[G][VEC];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float f[VEC];
+      unpack<T>(qraw[g], f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) qd[g][e] = (double)f[e];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float lo[VEC], hi[VEC];
+      unpack<T>(lo_raw[u], lo);
+      unpack<T>(hi_raw[u], hi);
+      if (u == ut && rgl == rg) {  // the stale rows loaded above are replaced by the fresh ones
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          lo[e] = flo[e];
+          hi[e] = fhi[e];
+        }
+      }
+      double acc = 0.0;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const double x = (double)(qd[g][e] >= 0.0 ? hi[e] : lo[e]);
+          acc = fma(qd[g][e], x, acc);
+        }
+      }
+      acc = seg_sum_f64<LPR>(acc);
+      const int n = wn0 + u * PPW + rgl;
+      if (n < N && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
+    }
+  } else {
+    // ---- scores of this wave's pages from the stored summary rows (the refreshed tail page's is
+    // written from its fresh summary) ----
+    auto q_f64 = [&](double (&qd)[G][VEC]) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float f[VEC];
+        unpack<T>(qraw[g], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) qd[g][e] = (double)f[e];
+      }
+    };
+    auto score_pages = [&](const double (&qd)[G][VEC], int skip) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float lo[VEC], hi[VEC];
+        unpack<T>(lo_raw[u], lo);
+        unpack<T>(hi_raw[u], hi);
+        const double acc = page_score<G, VEC, LPR>(qd, lo, hi);
+        const int n = wn0 + u * PPW + rgl;
+        if (n < N && n != skip && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
+      }
+    };
+    if (!btail) {
+      double qd[G][VEC];
+      q_f64(qd);
+      score_pages(qd, -1);
+      return;
+    }
+
+    // ---- the block holding the tail page: its key tile's loads go out first (the page id is in
+    // the lanes already); every wave folds its share of the tile's rows, the shares meet in LDS, and
+    // the wave that scores the tail page combines them, scores the page and writes its summary.
+    // With several pages per lane group (U > 1) the waves score their pages while the tile is in
+    // flight; with one, the tile tends to land before the summary rows, and the fold goes first ----
     int pt = 0;
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {  // scalar selects (a uniform index into pt_raw would spill it)
@@ -331,14 +491,30 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
     const size_t t = (size_t)pt * a.Hkv + j;
     float ksc = 1.0f;
     if constexpr (FP8) ksc = a.k_scale[t];  // in flight with the tile
-    float plo[VEC], phi[VEC];
+    TileMinMax<T, D, WAVES, FP8> tm;
     if constexpr (FP8)
-      tile_rows_minmax<T, D, WAVES, true>((const uint8_t*)a.k_pool + t * P * D, L - nt * P,
-                                          a.page_fill, P, lane, w, pt, 0, a.rope, plo, phi);
+      tm.start((const uint8_t*)a.k_pool + t * P * D, L - nt * P, a.page_fill, P, lane, w, pt, 0,
+               a.rope);
     else
-      tile_rows_minmax<T, D, WAVES, false>((const T*)a.k_pool + t * P * D, L - nt * P,
-                                           a.page_fill, P, lane, w, pt,
-                                           rope_row_index(a.rope, b, nt, pt), a.rope, plo, phi);
+      tm.start((const T*)a.k_pool + t * P * D, L - nt * P, a.page_fill, P, lane, w, pt,
+               rope_row_index(a.rope, b, nt, pt), a.rope);
+    if constexpr (U > 1) {
+      // the scoring must stay behind the tile loads: these registers, renamed here, keep the
+      // compiler from hoisting its (identical) start above the branch
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        asm volatile("" : "+v"(qraw[g].x), "+v"(qraw[g].y), "+v"(qraw[g].z), "+v"(qraw[g].w));
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        asm volatile("" : "+v"(lo_raw[u].x), "+v"(lo_raw[u].y), "+v"(lo_raw[u].z), "+v"(lo_raw[u].w));
+        asm volatile("" : "+v"(hi_raw[u].x), "+v"(hi_raw[u].y), "+v"(hi_raw[u].z), "+v"(hi_raw[u].w));
+      }
+      double qd[G][VEC];
+      q_f64(qd);
+      score_pages(qd, nt);
+    }
+    float plo[VEC], phi[VEC];
+    tm.finish(a.rope, plo, phi);
     const int off = fold_lanes_scatter<LPR, VEC>(plo, phi);
     __shared__ __align__(16) float s_fold[WAVES][2][D];  // each wave's extremes of the tile
 #pragma unroll
@@ -347,68 +523,45 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
       s_fold[w][1][c0 + off + i] = phi[i];
     }
     __syncthreads();
-    if (tail) {
+    if (!tail) {
+      if constexpr (U == 1) {
+        double qd[G][VEC];
+        q_f64(qd);
+        score_pages(qd, -1);
+      }
+      return;
+    }
+    float flo[VEC], fhi[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4) {
+      const float4 l0 = *(const float4*)&s_fold[0][0][c0 + e];
+      const float4 h0 = *(const float4*)&s_fold[0][1][c0 + e];
+      flo[e] = l0.x, flo[e + 1] = l0.y, flo[e + 2] = l0.z, flo[e + 3] = l0.w;
+      fhi[e] = h0.x, fhi[e + 1] = h0.y, fhi[e + 2] = h0.z, fhi[e + 3] = h0.w;
+    }
+#pragma unroll
+    for (int v = 1; v < WAVES; ++v) {
 #pragma unroll
       for (int e = 0; e < VEC; e += 4) {
-        const float4 l0 = *(const float4*)&s_fold[0][0][c0 + e];
-        const float4 h0 = *(const float4*)&s_fold[0][1][c0 + e];
-        flo[e] = l0.x, flo[e + 1] = l0.y, flo[e + 2] = l0.z, flo[e + 3] = l0.w;
-        fhi[e] = h0.x, fhi[e + 1] = h0.y, fhi[e + 2] = h0.z, fhi[e + 3] = h0.w;
-      }
-#pragma unroll
-      for (int v = 1; v < WAVES; ++v) {
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4) {
-          const float4 l = *(const float4*)&s_fold[v][0][c0 + e];
-          const float4 h = *(const float4*)&s_fold[v][1][c0 + e];
-          flo[e] = tmin(flo[e], l.x), flo[e + 1] = tmin(flo[e + 1], l.y);
-          flo[e + 2] = tmin(flo[e + 2], l.z), flo[e + 3] = tmin(flo[e + 3], l.w);
-          fhi[e] = tmax(fhi[e], h.x), fhi[e + 1] = tmax(fhi[e + 1], h.y);
-          fhi[e + 2] = tmax(fhi[e + 2], h.z), fhi[e + 3] = tmax(fhi[e + 3], h.w);
-        }
-      }
-      if constexpr (FP8) fp8_scale_outward<VEC>(ksc, flo, fhi);
-      if (lane < LPR) {
-        T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;
-        store16(out + c0, pack<T>(flo));
-        store16(out + D + c0, pack<T>(fhi));
+        const float4 l = *(const float4*)&s_fold[v][0][c0 + e];
+        const float4 h = *(const float4*)&s_fold[v][1][c0 + e];
+        flo[e] = tmin(flo[e], l.x), flo[e + 1] = tmin(flo[e + 1], l.y);
+        flo[e + 2] = tmin(flo[e + 2], l.z), flo[e + 3] = tmin(flo[e + 3], l.w);
+        fhi[e] = tmax(fhi[e], h.x), fhi[e + 1] = tmax(fhi[e + 1], h.y);
+        fhi[e + 2] = tmax(fhi[e + 2], h.z), fhi[e + 3] = tmax(fhi[e + 3], h.w);
       }
     }
-  }
-
-  // ---- scores of this wave's pages ----
-  double qd[G][VEC];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float f[VEC];
-    unpack<T>(qraw[g], f);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) qd[g][e] = (double)f[e];
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    float lo[VEC], hi[VEC];
-    unpack<T>(lo_raw[u], lo);
-    unpack<T>(hi_raw[u], hi);
-    if (u == ut && rgl == rg) {  // the stale rows loaded above are replaced by the fresh ones
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        lo[e] = flo[e];
-        hi[e] = fhi[e];
-      }
+    if constexpr (FP8) fp8_scale_outward<VEC>(ksc, flo, fhi);
+    double qd[G][VEC];
+    q_f64(qd);
+    if constexpr (U == 1) score_pages(qd, nt);
+    const double acc = page_score<G, VEC, LPR>(qd, flo, fhi);  // every row group: the same page
+    if (lane == 0) a.scores[(size_t)list * a.maxp + nt] = (float)acc;
+    if (lane < LPR) {
+      T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;
+      store16(out + c0, pack<T>(flo));
+      store16(out + D + c0, pack<T>(fhi));
     }
-    double acc = 0.0;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const double x = (double)(qd[g][e] >= 0.0 ? hi[e] : lo[e]);
-        acc = fma(qd[g][e], x, acc);
-      }
-    }
-    acc = seg_sum_f64<LPR>(acc);
-    const int n = wn0 + u * PPW + rgl;
-    if (n < N && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
   }
 }
 

@@ -4,7 +4,8 @@ folds a share of the tile's rows; the shares meet in LDS). After a call with the
 live summary must equal a fresh summary build of the same keys (and, without the rotary gather,
 the oracle's), and the selection must equal the selection over the fresh build. Shapes: 8, 16
 and 32 lanes per key row (bf16 D 64, bf16 D 128 / f32 D 64, f32 D 128), pages of 16 and 32 rows,
-blocks of up to 128 pages (the tail's page id in a lane's second page-id load), fp8 pools, the
+blocks of up to 128 pages (the tail's page id in a lane's second page-id load), one, two and four
+pages per lane group (where the tail block scores its pages before the fold), fp8 pools, the
 rotary gather, full, one-row and empty tails; the same through kvsel_select_attend and through
 the speculative step's shared launch (2- and 4-wave blocks) against its serial calls."""
 import numpy as np
@@ -33,6 +34,8 @@ CASES = [
     ("f32-D128-P32", "f32", 128, 32, 16, 4, 9, [32 * 250 + 7, 40, 32], None),
     ("f32-D64-P16", "f32", 64, 16, 8, 4, 7, [16 * 100 + 3, 17, 0], None),
     ("bf16-D128-P16", "bf16", 128, 16, 16, 2, 10, [16 * 300 + 1, 32, 5], None),
+    ("bf16-D128-P16-U2", "bf16", 128, 16, 16, 4, 10, [16 * 1500 + 7, 900], None),
+    ("f32-D64-P32-U2", "f32", 64, 32, 8, 4, 8, [32 * 1300 + 1, 64], None),
     ("fp8-D128-P32", "bf16", 128, 32, 32, 8, 6, [40 * 32 - 3, 9 * 32 + 1, 1], "fp8"),
     ("fp8-D64-P16-wide", "bf16", 64, 16, 8, 2, 12, [16 * 2147 + 9, 16 * 3], "fp8"),
 ]
