@@ -152,8 +152,10 @@ static int tiles_for(const LaunchKV& kv, int pps) {
 }
 
 int attention_pages_per_split(const LaunchKV& kv, int k, int requested) {
-  // default 4 pages per split: measured best at 32K, 128K and the ragged batch of 16
-  const int want = requested > 0 ? requested : 4;
+  // default: 4 pages per split below 64 lists, where a call is latency-bound (measured best for
+  // one sequence at 32K and 128K); 8 from 64 lists on, where it is bandwidth-bound and halving
+  // the partials and the merge's loads pays
+  const int want = requested > 0 ? requested : (kv.B * kv.Hkv >= 64 ? 8 : 4);
   int pps = 0;
   // largest supported split not above the request, else the smallest supported one
   for (int p = want; p >= 1 && !pps; --p)

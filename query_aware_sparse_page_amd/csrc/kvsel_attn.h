@@ -415,11 +415,11 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
       if constexpr (FP8) {
         const uint8_t* row = (const uint8_t*)a.k_pool + krow_off;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) k8[t][h][cb] = load8(row + 32 * cb);
+        for (int cb = 0; cb < CB; ++cb) k8[t][h][cb] = load8_nt(row + 32 * cb);
       } else {
         const bf16_t* row = kp + krow_off;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) kraw[t][h][cb] = load16(row + 32 * cb);
+        for (int cb = 0; cb < CB; ++cb) kraw[t][h][cb] = load16_nt(row + 32 * cb);
       }
       if (ROPE) {
         const int pr = a.rope.page_row[rope_row_index(a.rope, b, tp.lpage_of(t, u), pg)];
@@ -437,13 +437,13 @@ __device__ __forceinline__ void attn_bf16_block(const AttnArgs& a, int G, int j,
     if constexpr (FP8) {
       const uint8_t* vt = (const uint8_t*)a.v_pool + vt_off;
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb) v8[t][vb] = load8(vt + (size_t)(16 * vb) * P);
+      for (int vb = 0; vb < VB; ++vb) v8[t][vb] = load8_nt(vt + (size_t)(16 * vb) * P);
       ksc[t] = a.k_scale[(size_t)pg * a.Hkv + j];
       vsc[t] = a.v_scale[(size_t)pg * a.Hkv + j];
     } else {
       const bf16_t* vt = vp + vt_off;
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = load16(vt + (size_t)(16 * vb) * P);
+      for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = load16_nt(vt + (size_t)(16 * vb) * P);
     }
   }
   // valid slots of the tiles' pages in a composed sequence (page_fill): scalar loads after the
@@ -652,7 +652,7 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs& a, int G, int j, 
     const int slot = base + r16;
     const float* row = kp + (((size_t)pg * a.Hkv + j) * P + slot) * D + KC * q4;
 #pragma unroll
-    for (int u = 0; u < KL; ++u) kraw[t][u] = load16(row + 4 * u);
+    for (int u = 0; u < KL; ++u) kraw[t][u] = load16_nt(row + 4 * u);
     if (ROPE) {
       const int pr = a.rope.page_row[rope_row_index(a.rope, b, tp.lpage[t][0], pg)];
       krow[t] = pr < 0 ? -1 : pr + a.rope.row_step * slot;
@@ -664,7 +664,7 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs& a, int G, int j, 
     vmask[t] = mk;
     const float* vt = vp + ((size_t)pg * a.Hkv + j) * D * P + vslot + (size_t)r16 * P;
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = load16(vt + (size_t)(16 * vb) * P);
+    for (int vb = 0; vb < VB; ++vb) vraw[t][vb] = load16_nt(vt + (size_t)(16 * vb) * P);
   }
   [[maybe_unused]] int fillp[TPW];  // composed sequences: see attn_bf16_block
   if constexpr (FILL) {

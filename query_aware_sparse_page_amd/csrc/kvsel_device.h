@@ -63,6 +63,11 @@ __device__ __forceinline__ float tmin(float a, float b) { return __builtin_eleme
 __device__ __forceinline__ float tmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+typedef unsigned int u32x4_nt_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+  const u32x4_nt_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // Unpack one 16-byte vector into VEC floats.

@@ -22,6 +22,11 @@ struct fp8_t {
 };
 
 __device__ __forceinline__ uint2 load8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+typedef unsigned int u32x2_nt_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 load8_nt(const void* p) {
+  const u32x2_nt_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt_t*>(p));
+  return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ void store8(void* p, const uint2& v) { *reinterpret_cast<uint2*>(p) = v; }
 
 // Codes 4i .. 4i+3 of one 32-bit word as fp32 (exact).

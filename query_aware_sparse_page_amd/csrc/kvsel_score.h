@@ -61,9 +61,9 @@ struct TileRows {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       if constexpr (FP8)
-        raw[i] = load8((const uint8_t*)tile + (size_t)row(i) * D + c0);
+        raw[i] = load8_nt((const uint8_t*)tile + (size_t)row(i) * D + c0);
       else
-        raw[i] = load16((const T*)tile + (size_t)row(i) * D + c0);
+        raw[i] = load16_nt((const T*)tile + (size_t)row(i) * D + c0);
     }
   }
 
@@ -339,8 +339,8 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
   for (int u = 0; u < U; ++u) {
     const int nc = min(wn0 + u * PPW + rgl, a.maxn - 1);
     const T* srow = (const T*)a.summ + ((size_t)list * a.maxp + nc) * 2 * D + c0;
-    lo_raw[u] = load16(srow);
-    hi_raw[u] = load16(srow + D);
+    lo_raw[u] = load16_nt(srow);
+    hi_raw[u] = load16_nt(srow + D);
   }
   __builtin_amdgcn_sched_barrier(0);
   const int L = a.seq_lens[b];

@@ -5,6 +5,7 @@
 // K and V tiles a sparse attention call reads, it gives the time of moving exactly those bytes
 // with no index chain, no arithmetic and no merge: the floor the attention kernel is compared
 // against.
+#include "kvsel_device.h"
 #include "kvsel_internal.h"
 
 namespace kvsel {
@@ -18,7 +19,7 @@ __global__ __launch_bounds__(256) void gather_probe_kernel(const uint64_t* __res
   const uint4* p = reinterpret_cast<const uint4*>(addr[c]) + lane;
   uint4 v[LPL];
 #pragma unroll
-  for (int i = 0; i < LPL; ++i) v[i] = p[i * 64];
+  for (int i = 0; i < LPL; ++i) v[i] = load16_nt(p + i * 64);
   uint32_t x = 0;
 #pragma unroll
   for (int i = 0; i < LPL; ++i) x ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;

@@ -346,8 +346,8 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
     for (int u = 0; u < UNROLL; ++u) {
       const int n = (it0 + u) * PPI + w * PPW + lane / LPR;
       const T* srow = (const T*)a.summ + ((size_t)list * a.maxp + min(n, n_end - 1)) * 2 * D + c0;
-      lo_raw[u] = load16(srow);
-      hi_raw[u] = load16(srow + D);
+      lo_raw[u] = load16_nt(srow);
+      hi_raw[u] = load16_nt(srow + D);
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {

@@ -4,6 +4,8 @@
 // pages (block shapes in kvsel_attn.h); with pages that end early (page_fill) it is a separate
 // instantiation (FILL), taken at <= 4 keys per thread only. Other cases (many lists, a wide table, a k that needs
 // larger splits; select_attend_fused) run the two separate calls' launches instead.
+#include <algorithm>
+
 #include "kvsel_attn.h"
 
 namespace kvsel {
@@ -113,8 +115,12 @@ hipError_t launch_fused_select(const LaunchKV& kv, const AttnArgs& a, bool rope,
   return launch_merge(kv, a, stream);
 }
 
+// The scores, then the partials of the larger of the two splits a call may run: the default
+// split (the separate launches) and the fused launches' FUSED_PPS pages (the fused selection and
+// the speculative step).
 size_t select_attend_workspace(const LaunchKV& kv, int k) {
-  return align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float)) + attention_workspace(kv, k, 0);
+  return align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float)) +
+         std::max(attention_workspace(kv, k, 0), attention_workspace(kv, k, FUSED_PPS));
 }
 
 hipError_t launch_select_attend(const LaunchKV& kv, const RopeArgs& rope, void* summ,
