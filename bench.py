@@ -113,6 +113,22 @@ def make_layers(w, dev, n, fp8=False):
     return layers
 
 
+def batched_layers(name, dev, n):
+    """n independently drawn batches of the same shape (seeds 1006, 1007, ...), each with its own
+    pools and page table, drawn on the device, used in turn like layers."""
+    layers, first = [], None
+    for c in range(n):
+        w = W.batched_device(name, dev, seed=1006 + c)
+        v = K.device_v_layout(w.v_pool)
+        w.v_pool = None  # only the channel-major copy is kept
+        lay = Layer(w, dev, w.k_pool, v, w.page_table, w.seq_lens)
+        lay.table_cpu = w.page_table.cpu()
+        layers.append(lay)
+        first = first or w
+    torch.cuda.synchronize()
+    return first, layers
+
+
 def time_graph(layers, steps, warmup, step=Layer.step):
     """µs per step of the whole path: exactly ``warmup`` untimed steps (eager), then exactly
     ``steps`` timed steps captured in one HIP graph and replayed once between two HIP events. Step
@@ -196,8 +212,11 @@ def progress(msg):
 
 
 def measure(name, dev, steps, warmup, n_layers, fp8=False):
-    w = W.make(name)
-    layers = make_layers(w, dev, n_layers, fp8)
+    if name in W.BATCHED:
+        w, layers = batched_layers(name, dev, n_layers)
+    else:
+        w = W.make(name)
+        layers = make_layers(w, dev, n_layers, fp8)
     us_step, n = time_graph(layers, steps, warmup)
     us_two, _ = time_graph(layers, steps, warmup, Layer.step_two_calls)
     us_current, _ = time_graph(layers, steps, warmup, Layer.step_current)
@@ -206,7 +225,8 @@ def measure(name, dev, steps, warmup, n_layers, fp8=False):
     sel_mean = time_calls(layers, Layer.select, n_calls)
     esize = 1 if fp8 else 4 if w.dtype == "f32" else 2
     for lay in layers:  # the tiles each layer's selection names, at that layer's addresses
-        lay.probe_addr = K.tile_addresses(lay.kv, lay.sel, lay.cnt, w.page_table)
+        lay.probe_addr = K.tile_addresses(lay.kv, lay.sel, lay.cnt,
+                                          getattr(lay, "table_cpu", w.page_table))
         lay.probe_chunk = w.P * w.D * esize
         lay.probe_sink = torch.zeros(1, dtype=torch.int32, device=dev)
     probe_us = time_calls(layers, Layer.probe, n_calls)
@@ -671,10 +691,14 @@ def main():
     # the 128K case of the metric, and the batched case whose 64 MiB per step is where bandwidth
     # rather than latency sets the time
     # and both again with fp8 (E4M3) pages: half the bytes of the selected K/V
+    # and batches of the 32K and 128K shapes (256 MiB of selected K/V per step, two independently
+    # drawn batches rotated), where the attention call is bandwidth-bound
     for name, n_layers, fp8 in (("qwen4b_128k", max(2, args.layers // 2), False),
                                 ("ragged_batch", max(2, args.layers // 4), False),
                                 (args.workload, args.layers, True),
-                                ("ragged_batch", max(2, args.layers // 4), True)):
+                                ("ragged_batch", max(2, args.layers // 4), True),
+                                ("llama8b_32k_batch32", 2, False),
+                                ("qwen4b_128k_batch16", 2, False)):
         if args.no_secondary or (name == args.workload and not fp8):
             continue
         s = measure(name, dev, args.steps, args.warmup, n_layers, fp8)
@@ -691,6 +715,10 @@ def main():
                              "GBps": round(s["probe_bytes"] / (s["probe_us"] * 1e-6) / 1e9, 1)}}
         if fp8:
             result["secondary"][key]["pages"] = "fp8 E4M3 K/V, per-tile fp32 scales, bf16 summaries"
+        if name in W.BATCHED:
+            result["secondary"][key].update(
+                batch=s["w"].B, context=int(s["w"].seq_lens.max()), topk_pages=s["w"].k,
+                data="drawn on the device (workloads.batched_device)")
         progress(f"{key}: step {s['us_step']:.3f} us, attention call {s['attn_us']:.3f} us")
         del s
         torch.cuda.empty_cache()

@@ -53,3 +53,24 @@ def test_speculative_queries_are_correlated():
     cos = torch.nn.functional.cosine_similarity(qs[1:], qs[:-1], dim=-1)
     assert 0.75 < cos.mean().item() < 0.92
     assert torch.equal(w.q, w.extra["q_steps"][0])
+
+
+def test_batched_device_structure(monkeypatch):
+    """The device-drawn batch generator (run here on the CPU at a small size): shapes, one
+    permutation of the pool over all sequences, the outlier channels, determinism per seed."""
+    monkeypatch.setitem(W.BATCHED, "small_batch", (3, 4096, 512))
+    w = W.batched_device("small_batch", "cpu")
+    assert w.k_pool.shape == (384, 8, 32, 128) and w.v_pool.shape == w.k_pool.shape
+    assert w.page_table.shape == (3, 128) and w.k == 16 and w.B == 3
+    assert w.seq_lens.tolist() == [4096] * 3 and w.q.dtype == torch.bfloat16
+    assert torch.equal(torch.sort(w.page_table.flatten().long())[0], torch.arange(384))
+    k = w.k_pool.float()
+    for j, chans in enumerate(w.extra["outlier_channels"]):
+        std = k[:, j].std(dim=(0, 1))
+        others = torch.ones(128, dtype=torch.bool)
+        others[chans] = False
+        assert std[chans].min() > 6.0 and std[others].max() < 1.5
+    w2 = W.batched_device("small_batch", "cpu")
+    assert torch.equal(w.k_pool, w2.k_pool) and torch.equal(w.page_table, w2.page_table)
+    w3 = W.batched_device("small_batch", "cpu", seed=7)
+    assert not torch.equal(w.q, w3.q)

@@ -12,7 +12,8 @@ The shapes follow the pages' workloads:
   * strongly correlated queries of adjacent decode steps (FreeKV summary, section 2.1: cosine of
     about 0.84 or more between neighbouring steps' queries).
 
-Every tensor is a CPU torch tensor; callers move it to the device. bf16 values are produced by
+Every tensor is a CPU torch tensor; callers move it to the device (except ``batched_device``,
+whose batches of long contexts are drawn on the device: several GiB per pool). bf16 values are produced by
 round-to-nearest-even of fp32/fp64 draws (torch's conversion).
 
 Seeds: workload ``i`` (1-based) draws from ``numpy.random.Generator(PCG64(1000 + i))`` unless a
@@ -37,6 +38,8 @@ __all__ = [
     "speculative_rope",
     "composed",
     "custom",
+    "BATCHED",
+    "batched_device",
 ]
 
 
@@ -381,6 +384,54 @@ def composed(seed: int = 1006, doc_lens=(3000, 517, 4099, 1, 2222, 700, 5120, 31
                "doc_lens": list(doc_lens), "order": order, "theta": theta},
     )
 
+
+
+# Batches of the 32K and 128K decode shapes, for the bandwidth-bound regime of the attention:
+# name -> (batch, context tokens, token budget).
+BATCHED = {
+    "llama8b_32k_batch32": (32, 32768, 2048),
+    "qwen4b_128k_batch16": (16, 131072, 4096),
+}
+
+
+def batched_device(name: str, device, seed: int = 1006) -> Workload:
+    """B sequences of the 32K or 128K decode shape (``BATCHED``), every one at the full context:
+    32 / 8 heads, D 128, bf16, P 32, k = budget / P. q, V ~ N(0,1); K ~ N(0,1) with 4 outlier
+    channels per KV head scaled by 8 (the 32K recipe; no needles). One random permutation of the
+    pool's pages is laid out over all (sequence, logical page) pairs in order.
+
+    Drawn on ``device`` from ``torch.Generator(device)`` seeded with ``seed``, in the order q, page
+    permutation, outlier channels, then K and V in chunks of 2048 pages (fp32 draws rounded to
+    bf16); the tensors stay on the device.
+    """
+    B, context, budget = BATCHED[name]
+    Hq, Hkv, D, P = 32, 8, 128, 32
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    q = torch.randn((B, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+    npg = context // P
+    Npp = B * npg
+    perm = torch.randperm(Npp, generator=g, device=dev).to(torch.int32)
+    chans = torch.stack([torch.randperm(D, generator=g, device=dev)[:4] for _ in range(Hkv)])
+    k_pool = torch.empty((Npp, Hkv, P, D), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.empty((Npp, Hkv, P, D), dtype=torch.bfloat16, device=dev)
+    step = 2048
+    for p0 in range(0, Npp, step):
+        n = min(step, Npp - p0)
+        kc = torch.randn((n, Hkv, P, D), generator=g, device=dev)
+        for j in range(Hkv):
+            kc[:, j, :, chans[j]] *= 8.0
+        k_pool[p0:p0 + n] = kc.to(torch.bfloat16)
+        v_pool[p0:p0 + n] = torch.randn((n, Hkv, P, D), generator=g, device=dev).to(torch.bfloat16)
+        del kc
+    return Workload(
+        name, "bf16", B, Hq, Hkv, D, P, budget // P,
+        seq_lens=torch.full((B,), context, dtype=torch.int32, device=dev),
+        page_table=perm.reshape(B, npg).contiguous(),
+        k_pool=k_pool, v_pool=v_pool, q=q,
+        extra={"outlier_channels": chans.cpu().tolist(), "device": True},
+    )
 
 WORKLOADS = {
     "tiny_fp32": tiny_fp32,
