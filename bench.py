@@ -575,8 +575,11 @@ def counter_pass(name, dev, n_layers, split_sizes=()):
     """Eager steps over the rotated layers (and attention calls at the given split sizes), then a
     plain device copy of exactly 64 MiB: its FETCH_SIZE / WRITE_SIZE per dispatch calibrate the
     counters against known bytes."""
-    w = W.make(name)
-    layers = make_layers(w, dev, n_layers)
+    if name in W.BATCHED:
+        w, layers = batched_layers(name, dev, n_layers)
+    else:
+        w = W.make(name)
+        layers = make_layers(w, dev, n_layers)
     for _ in range(2):
         for lay in layers:
             lay.step()  # kvsel_select_attend
