@@ -565,9 +565,16 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
   }
 }
 
-// Unroll (pages per lane group) of the score kernel for a live page bound: long lists take fewer,
-// fuller blocks.
-inline int score_unroll(int maxn) { return maxn <= 1024 ? 1 : maxn <= 2048 ? 2 : 4; }
+// Unroll (pages per lane group) of the score kernel for a live page bound and a list count: long
+// lists take fewer, fuller blocks. Measured with non-temporal summary reads:
+// - at 1024 pages, U = 1 / 2 / 4 gave the 32K step in 14.15 / 14.54 / 15.21 us;
+// - at 4096 pages and 8 lists, U = 2 / 4 gave the 128K selection call in 12.85 / 13.13 us;
+// - at 128 lists of 4096 pages, U = 2 / 4 gave it in 68.0 / 55.3 us.
+inline int score_unroll(int maxn, int nlists) {
+  if (maxn <= 1024) return 1;
+  if (maxn <= 2048 || (maxn <= 8192 && nlists < 64)) return 2;
+  return 4;
+}
 
 // Group-mean cosine similarity of this step's and the previous step's queries for KV head j of
 // sequence b, by one wave, in fp64: for each of the G heads, dot / (|q| |q_prev|) with the

@@ -397,7 +397,7 @@ int select_blocks_per_list(const LaunchKV& kv) {
                                                : pages_per_select_block<float, 128>())
                                  : (kv.D == 64 ? pages_per_select_block<bf16_t, 64>()
                                                : pages_per_select_block<bf16_t, 128>())) *
-                  score_unroll(kv.maxn);
+                  score_unroll(kv.maxn, kv.B * kv.Hkv);
   return (kv.maxn + ppb - 1) / ppb;
 }
 
@@ -415,7 +415,7 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t stream) {
     }
   }
   const dim3 sgrid(a.Hkv, a.nlists / a.Hkv, a.nchunks);
-  switch (score_unroll(a.maxn)) {
+  switch (score_unroll(a.maxn, a.nlists)) {
     case 1: hipLaunchKernelGGL((score_kernel<T, D, G, 1, FP8>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((score_kernel<T, D, G, 2, FP8>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
     default: hipLaunchKernelGGL((score_kernel<T, D, G, 4, FP8>), sgrid, dim3(SEL_THREADS), 0, stream, a); break;
