@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVSEL_ABI_VERSION 6
+#define KVSEL_ABI_VERSION 7
 
 typedef int32_t kvsel_status;
 #define KVSEL_OK 0
@@ -173,6 +173,14 @@ const char* kvsel_status_str(kvsel_status status);
 size_t kvsel_workspace_bytes(const kvsel_paged_kv* kv, int32_t k, int32_t op,
                              int32_t pages_per_split);
 
+/* Pages per split of the attention that kvsel_select_attend, kvsel_select_attend_static and
+ * kvsel_speculative_step run: 4 (the split their fused launches are built for) below 64
+ * (sequence, KV head) lists, the default split of kvsel_sparse_decode_attn from 64 lists on; as
+ * kvsel_sparse_decode_attn resolves a request, so possibly larger when k needs it. Those calls
+ * equal kvsel_sparse_decode_attn at this pages_per_split bit for bit. Returns 0 for invalid input.
+ * Pure host arithmetic: touches no device. */
+int32_t kvsel_step_pages_per_split(const kvsel_paged_kv* kv, int32_t k);
+
 /* Page-summary build. For every logical page n < N_b of every sequence b and every KV head j,
  * writes summ[b][j][n][0][:] = channel-wise minimum and summ[b][j][n][1][:] = channel-wise
  * maximum of the valid slots' keys of physical page page_table[b][n]. summ is
@@ -219,8 +227,10 @@ kvsel_status kvsel_score_topk(const kvsel_paged_kv* kv, const kvsel_rope* rope, 
  * with fp32 arithmetic (K/V read in the element type). out is [B][Hq][D] in the element type;
  * lse is fp32 [B][Hq] and may be NULL. A (b, h) with nothing selected gets out = 0 and
  * lse = -inf. The work is split over groups of pages_per_split consecutive selected pages
- * (0 = the library's choice; a request is rounded to a supported size, and raised so that a list
- * has at most 256 splits) and the splits are merged by log-sum-exp in a second launch.
+ * (0 = the library's choice: 8 from 64 lists on; below that 2 when lists x ceil(k / 2) <= 256,
+ * about one block per compute unit, else 4; a request is rounded to a supported size, and raised
+ * so that a list has at most 256 splits) and the splits are merged by log-sum-exp in a second
+ * launch.
  * rope != NULL rotates each key on the fly (bit-identical to a pool rotated by kvsel_rope_shift).
  * fp8 cache: k_t and v_t are the dequantized values (code * the page's k_scale / v_scale); the
  * logits take the key scale as scale * k_scale in fp32, and each probability enters the value
@@ -235,8 +245,8 @@ kvsel_status kvsel_sparse_decode_attn(const kvsel_paged_kv* kv, const kvsel_rope
                                       size_t ws_bytes, void* stream);
 
 /* Selection and attention in one call: the outputs of kvsel_score_topk (without reuse, scores
- * kept in the workspace) followed by kvsel_sparse_decode_attn with the library's default split,
- * bit for bit. The top-k is re-derived inside the attention launch by every block of a list from
+ * kept in the workspace) followed by kvsel_sparse_decode_attn with pages_per_split =
+ * kvsel_step_pages_per_split(kv, k), bit for bit. The top-k is re-derived inside the attention launch by every block of a list from
  * the page scores (each block keeps the pages of its own split), so the K / V reads follow one
  * memory round trip after the scores instead of the selection-ids -> page-table chain, and no
  * separate top-k launch runs. The fused form is taken where it measured faster than the
@@ -286,8 +296,8 @@ kvsel_status kvsel_rope_shift(const kvsel_paged_kv* kv, const kvsel_rope* rope, 
                               void* stream);
 
 /* Speculative decode step: the outputs of kvsel_score_topk with `reuse` (required) followed by
- * kvsel_sparse_decode_attn over the used pages (reuse->used_idx / used_cnt) with the library's
- * default split, bit for bit. The attention over the previous step's pages (reuse->prev_idx /
+ * kvsel_sparse_decode_attn over the used pages (reuse->used_idx / used_cnt) with pages_per_split
+ * = kvsel_step_pages_per_split(kv, k), bit for bit. The attention over the previous step's pages (reuse->prev_idx /
  * prev_cnt), which does not depend on this step's selection, runs in the same launch as the page
  * scoring and the reuse decision; the next launch selects, and re-attends only the lists the
  * decision corrected, over their fresh pages; a last launch merges the splits. With

@@ -152,10 +152,13 @@ static int tiles_for(const LaunchKV& kv, int pps) {
 }
 
 int attention_pages_per_split(const LaunchKV& kv, int k, int requested) {
-  // default: 4 pages per split below 64 lists, where a call is latency-bound (measured best for
-  // one sequence at 32K and 128K); 8 from 64 lists on, where it is bandwidth-bound and halving
-  // the partials and the merge's loads pays
-  const int want = requested > 0 ? requested : (kv.B * kv.Hkv >= 64 ? 8 : 4);
+  // default: below 64 lists a call is latency-bound, and the split that puts about one block on
+  // each of the 256 CUs measured best (2 pages when lists x k/2 <= 256: one 32K sequence at k 64,
+  // 6.82 against 7.80 us for 4 pages with cold caches; else 4: one 128K sequence at k 128, 8.60
+  // against 9.21 us for 2 pages); from 64 lists on the call is bandwidth-bound, and 8 pages halve
+  // the partials and the merge's loads
+  const int nl = kv.B * kv.Hkv;
+  const int want = requested > 0 ? requested : nl >= 64 ? 8 : (nl * ((k + 1) / 2) <= 256 ? 2 : 4);
   int pps = 0;
   // largest supported split not above the request, else the smallest supported one
   for (int p = want; p >= 1 && !pps; --p)

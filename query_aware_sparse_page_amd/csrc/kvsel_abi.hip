@@ -169,6 +169,12 @@ size_t kvsel_workspace_bytes(const kvsel_paged_kv* kv, int32_t k, int32_t op,
   return 0;
 }
 
+int32_t kvsel_step_pages_per_split(const kvsel_paged_kv* kv, int32_t k) {
+  LaunchKV f;
+  if (k < 1 || flatten(kv, 0, &f) != KVSEL_OK) return 0;
+  return step_pages_per_split(f, k);
+}
+
 kvsel_status kvsel_build_summaries(const kvsel_paged_kv* kv, const kvsel_rope* rope,
                                    int32_t tail_only, void* summ, void* stream) {
   LaunchKV f;
@@ -249,7 +255,7 @@ kvsel_status kvsel_select_attend(const kvsel_paged_kv* kv, const kvsel_rope* rop
   if (!summ || !q || !sel_idx || !sel_cnt || !out || k < 1) return KVSEL_ERR_INVALID_ARGUMENT;
   if (flags & ~KVSEL_SCORE_REFRESH_TAIL) return KVSEL_ERR_INVALID_ARGUMENT;
   if ((st = flatten_rope(rope, f, &r)) != KVSEL_OK) return st;
-  if (attention_pages_per_split(f, k, 0) <= 0) return KVSEL_ERR_UNSUPPORTED;
+  if (step_pages_per_split(f, k) <= 0) return KVSEL_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < select_attend_workspace(f, k)) return KVSEL_ERR_WORKSPACE;
   if ((st = check_device()) != KVSEL_OK) return st;
   return launch_status(launch_select_attend(f, r, summ, q, k, flags, scale, sel_idx, sel_cnt, out,
@@ -267,7 +273,7 @@ kvsel_status kvsel_select_attend_static(const kvsel_paged_kv* kv, const kvsel_ro
   if (!summ || !q || !sel_idx || !sel_cnt || !out || k < 1) return KVSEL_ERR_INVALID_ARGUMENT;
   if (flags & ~KVSEL_SCORE_REFRESH_TAIL) return KVSEL_ERR_INVALID_ARGUMENT;
   if ((st = flatten_rope(rope, f, &r)) != KVSEL_OK) return st;
-  if (attention_pages_per_split(f, k, 0) <= 0) return KVSEL_ERR_UNSUPPORTED;
+  if (step_pages_per_split(f, k) <= 0) return KVSEL_ERR_UNSUPPORTED;
   if (select_attend_workspace(f, k) > (size_t)KVSEL_STATIC_SCRATCH_BYTES) return KVSEL_ERR_SCRATCH;
   if ((st = check_device()) != KVSEL_OK) return st;
   void* ws = nullptr;
@@ -290,7 +296,7 @@ kvsel_status kvsel_speculative_step(const kvsel_paged_kv* kv, const kvsel_rope* 
     return KVSEL_ERR_INVALID_ARGUMENT;
   if (flags & ~KVSEL_SCORE_REFRESH_TAIL) return KVSEL_ERR_INVALID_ARGUMENT;
   if ((st = flatten_rope(rope, f, &r)) != KVSEL_OK) return st;
-  if (attention_pages_per_split(f, k, 0) <= 0) return KVSEL_ERR_UNSUPPORTED;
+  if (step_pages_per_split(f, k) <= 0) return KVSEL_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < select_attend_workspace(f, k)) return KVSEL_ERR_WORKSPACE;
   ReuseArgs ra;
   memset(&ra, 0, sizeof(ra));

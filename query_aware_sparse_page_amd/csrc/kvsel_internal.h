@@ -79,6 +79,9 @@ constexpr int SELECT_ONE_LAUNCH_MIN_LISTS = 64;
 // fused_select_supported: the fused launch exists for this shape (register-resident select of
 // the table row, the default split); select_attend_fused: kvsel_select_attend also takes it.
 bool fused_select_supported(const LaunchKV& kv, int k);
+// Pages per split of the attention in kvsel_select_attend and kvsel_speculative_step: the fused
+// launches' split below 64 lists, the default split from 64 lists on.
+int step_pages_per_split(const LaunchKV& kv, int k);
 bool select_attend_fused(const LaunchKV& kv, const RopeArgs& rope, int k);
 size_t select_attend_workspace(const LaunchKV& kv, int k);
 hipError_t launch_select_attend(const LaunchKV& kv, const RopeArgs& rope, void* summ,

@@ -1,11 +1,10 @@
 // kvsel_select_attend: the scores (score kernel), then the attention launch with the selection
 // fused in (select_tiles: every block re-derives its list's top-k from the scores and keeps the
-// pages of its own split), then the merge. The fused launch uses the default split of FUSED_PPS
-// pages (block shapes in kvsel_attn.h); with pages that end early (page_fill) it is a separate
-// instantiation (FILL), taken at <= 4 keys per thread only. Other cases (many lists, a wide table, a k that needs
-// larger splits; select_attend_fused) run the two separate calls' launches instead.
-#include <algorithm>
-
+// pages of its own split), then the merge. The fused launch uses splits of FUSED_PPS pages (block
+// shapes in kvsel_attn.h), the step's split below 64 lists (step_pages_per_split); with pages that
+// end early (page_fill) it is a separate instantiation (FILL), taken at <= 4 keys per thread only.
+// Other cases (many lists, a wide table, a k that needs larger splits; select_attend_fused) run
+// the two separate calls' launches at the step's split instead.
 #include "kvsel_attn.h"
 
 namespace kvsel {
@@ -33,8 +32,12 @@ static int fused_keys_per_thread(const LaunchKV& kv) {
   return c <= 1 ? 1 : c <= 4 ? 4 : c <= 8 ? 8 : c <= 16 ? 16 : c <= 32 ? 32 : 0;
 }
 
+int step_pages_per_split(const LaunchKV& kv, int k) {
+  return attention_pages_per_split(kv, k, kv.B * kv.Hkv < SELECT_ONE_LAUNCH_MIN_LISTS ? FUSED_PPS : 0);
+}
+
 static bool fused_shape(const LaunchKV& kv, int k) {
-  return fused_keys_per_thread(kv) > 0 && attention_pages_per_split(kv, k, 0) == FUSED_PPS;
+  return fused_keys_per_thread(kv) > 0 && step_pages_per_split(kv, k) == FUSED_PPS;
 }
 
 bool fused_select_supported(const LaunchKV& kv, int k) {
@@ -115,12 +118,10 @@ hipError_t launch_fused_select(const LaunchKV& kv, const AttnArgs& a, bool rope,
   return launch_merge(kv, a, stream);
 }
 
-// The scores, then the partials of the larger of the two splits a call may run: the default
-// split (the separate launches) and the fused launches' FUSED_PPS pages (the fused selection and
-// the speculative step).
+// The scores, then the partials of the step's split.
 size_t select_attend_workspace(const LaunchKV& kv, int k) {
   return align256((size_t)kv.B * kv.Hkv * kv.maxp * sizeof(float)) +
-         std::max(attention_workspace(kv, k, 0), attention_workspace(kv, k, FUSED_PPS));
+         attention_workspace(kv, k, step_pages_per_split(kv, k));
 }
 
 hipError_t launch_select_attend(const LaunchKV& kv, const RopeArgs& rope, void* summ,
@@ -133,7 +134,8 @@ hipError_t launch_select_attend(const LaunchKV& kv, const RopeArgs& rope, void* 
     hipError_t e = launch_score_topk(kv, rope, summ, q, k, flags, sel_idx, sel_cnt, scores, false,
                                      ReuseArgs{}, stream);
     if (e != hipSuccess) return e;
-    return launch_attention(kv, rope, q, sel_idx, sel_cnt, k, scale, 0, out, lse, attn_ws, stream);
+    return launch_attention(kv, rope, q, sel_idx, sel_cnt, k, scale, step_pages_per_split(kv, k),
+                            out, lse, attn_ws, stream);
   }
   hipError_t e = launch_scores(kv, rope, summ, q, flags, scores, stream);
   if (e != hipSuccess) return e;

@@ -92,7 +92,8 @@ hipError_t launch_speculative_step(const LaunchKV& kv, const RopeArgs& rope, voi
     hipError_t e = launch_score_topk(kv, rope, summ, q, k, flags, sel_idx, sel_cnt, scores, false,
                                      reuse, stream);
     if (e != hipSuccess) return e;
-    return launch_attention(kv, rope, q, reuse.used_idx, reuse.used_cnt, k, scale, 0, out, lse,
+    return launch_attention(kv, rope, q, reuse.used_idx, reuse.used_cnt, k, scale,
+                            step_pages_per_split(kv, k), out, lse,
                             attn_ws, stream);
   }
   const bool r = rope.page_row != nullptr;

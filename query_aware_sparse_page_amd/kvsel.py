@@ -75,6 +75,7 @@ EXPORTS = {
     "kvsel_abi_version": (c_i32, []),
     "kvsel_status_str": (ctypes.c_char_p, [c_i32]),
     "kvsel_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PagedKVDesc), c_i32, c_i32, c_i32]),
+    "kvsel_step_pages_per_split": (c_i32, [ctypes.POINTER(PagedKVDesc), c_i32]),
     "kvsel_build_summaries": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_i32,
                                       c_vp, c_vp]),
     "kvsel_score_topk": (c_i32, [ctypes.POINTER(PagedKVDesc), ctypes.POINTER(RopeDesc), c_vp, c_vp,
@@ -105,7 +106,7 @@ EXPORTS = {
 _lib = None
 
 
-ABI_VERSION = 6  # KVSEL_ABI_VERSION of include/kvsel.h
+ABI_VERSION = 7  # KVSEL_ABI_VERSION of include/kvsel.h
 
 
 def lib() -> ctypes.CDLL:
@@ -283,6 +284,16 @@ def _rope_ptr(rope: Optional[Rope]):
 
 def workspace_bytes(kv: PagedKV, k: int, op: int, pages_per_split: int = 0) -> int:
     return int(lib().kvsel_workspace_bytes(ctypes.byref(kv.desc()), k, op, pages_per_split))
+
+
+def step_pages_per_split(kv: PagedKV, k: int) -> int:
+    """Pages per split at which select_attend, select_attend_static and speculative_step run their
+    attention (they equal sparse_decode_attn at this pages_per_split, bit for bit)."""
+    d = kv.desc()
+    n = lib().kvsel_step_pages_per_split(ctypes.byref(d), int(k))
+    if n <= 0:
+        raise KvselError(-1, "no attention split for this descriptor and k")
+    return int(n)
 
 
 def new_workspace(kv: PagedKV, k: int, op: int, pages_per_split: int = 0) -> torch.Tensor:

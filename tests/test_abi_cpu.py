@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(K):
 
 def test_version_and_status_strings(K):
     lib = K.lib()
-    assert lib.kvsel_abi_version() == K.ABI_VERSION == 6
+    assert lib.kvsel_abi_version() == K.ABI_VERSION == 7
     for code, tag in [(0, "KVSEL_OK"), (1, "INVALID_ARGUMENT"), (2, "UNSUPPORTED"),
                       (3, "WORKSPACE"), (4, "DEVICE"), (5, "LAUNCH"), (6, "SCRATCH"),
                       (99, "UNKNOWN")]:
@@ -73,6 +73,37 @@ def test_workspace_sizes(K):
     assert lib.kvsel_workspace_bytes(ctypes.byref(d), 2, K.KVSEL_OP_ATTENTION, 2) == 0
     assert lib.kvsel_workspace_bytes(None, 64, K.KVSEL_OP_SCORE_TOPK, 0) == 0
     assert lib.kvsel_workspace_bytes(ctypes.byref(d), 0, K.KVSEL_OP_SCORE_TOPK, 0) == 0
+
+
+def _attn_ws(lib, d, k, pps):
+    return lib.kvsel_workspace_bytes(ctypes.byref(d), k, 2, pps)  # KVSEL_OP_ATTENTION
+
+
+def test_default_and_step_splits(K):
+    """The library's split choices, read through the workspace sizes and the step-split query:
+    below 64 lists 2 pages when lists x ceil(k / 2) <= 256, else 4; 8 from 64 lists on. The
+    select-attend and speculative calls run 4-page splits below 64 lists (their fused launches'),
+    the default from 64 lists on."""
+    lib = K.lib()
+    one = _desc(K)  # 8 lists of 1024 pages
+    assert _attn_ws(lib, one, 64, 0) == _attn_ws(lib, one, 64, 2)  # 8 x 32 = 256 blocks
+    assert _attn_ws(lib, one, 128, 0) == _attn_ws(lib, one, 128, 4)  # 8 x 64 > 256
+    assert lib.kvsel_step_pages_per_split(ctypes.byref(one), 64) == 4
+    assert lib.kvsel_step_pages_per_split(ctypes.byref(one), 128) == 4
+    scores = 8 * 1024 * 4
+    assert lib.kvsel_workspace_bytes(ctypes.byref(one), 64, K.KVSEL_OP_SELECT_ATTEND, 0) == \
+        scores + _attn_ws(lib, one, 64, 4)
+    two = _desc(K, batch=2, num_phys_pages=2048)  # 16 lists: 16 x 32 > 256
+    assert _attn_ws(lib, two, 64, 0) == _attn_ws(lib, two, 64, 4)
+    many = _desc(K, batch=8, num_phys_pages=8192)  # 64 lists
+    assert _attn_ws(lib, many, 64, 0) == _attn_ws(lib, many, 64, 8)
+    assert lib.kvsel_step_pages_per_split(ctypes.byref(many), 64) == 8
+    assert lib.kvsel_workspace_bytes(ctypes.byref(many), 64, K.KVSEL_OP_SPECULATIVE_STEP, 0) == \
+        8 * 8 * 1024 * 4 + _attn_ws(lib, many, 64, 8)
+    # a k that needs more than 256 splits of 4 raises the split
+    assert lib.kvsel_step_pages_per_split(ctypes.byref(one), 1024) == 4
+    assert lib.kvsel_step_pages_per_split(ctypes.byref(one), 0) == 0
+    assert lib.kvsel_step_pages_per_split(None, 64) == 0
 
 
 @pytest.mark.parametrize("field,value,status", [

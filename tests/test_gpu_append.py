@@ -162,7 +162,8 @@ def test_growing_speculative_loop(K):
         reuse = K.Reuse(qp, prev_i, prev_c, 0.8, first_step=first)
         spec = K.speculative_step(kv_a, summ_a, qt, k, reuse)
         sel, cnt, used, ucnt, corr, sim = K.score_topk(kv_b, summ_b, qt, k, reuse=reuse)
-        out, lse = K.sparse_decode_attn(kv_b, qt, used, ucnt, k)
+        out, lse = K.sparse_decode_attn(kv_b, qt, used, ucnt, k,
+                                        pages_per_split=K.step_pages_per_split(kv_b, k))
         torch.cuda.synchronize()
         for x, y, name in zip(spec, (sel, cnt, used, ucnt, corr, sim, out, lse),
                               ("sel", "cnt", "used", "ucnt", "corrected", "similarity", "out", "lse")):

@@ -89,7 +89,8 @@ def test_composed_matches_oracle(K, case):
     assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["fp32"])
     assert_attention_close(out, lse, ref["out"], ref["lse"], dtype)
     s2, c2 = K.score_topk(kv, summ, q, w.k)
-    o2, l2 = K.sparse_decode_attn(kv, q, s2, c2, w.k, scale=scale)
+    o2, l2 = K.sparse_decode_attn(kv, q, s2, c2, w.k, scale=scale,
+                                  pages_per_split=K.step_pages_per_split(kv, w.k))
     zi = torch.zeros((w.B, w.Hkv, w.k), dtype=torch.int32, device="cuda")
     zc = torch.zeros((w.B, w.Hkv), dtype=torch.int32, device="cuda")
     spec = K.speculative_step(kv, summ, q, w.k, K.Reuse(q, zi, zc, 0.8, first_step=True), scale=scale)

@@ -67,7 +67,8 @@ def test_fp8_path_matches_oracle(K, case):
     assert_summaries_equal(summ, ref["summ"], w)
     scores = torch.empty((w.B, w.Hkv, w.max_pages), dtype=torch.float32, device="cuda")
     sel, cnt = K.score_topk(kv8, summ, q, w.k, scores=scores)
-    out, lse = K.sparse_decode_attn(kv8, q, sel, cnt, w.k, scale=scale)
+    out, lse = K.sparse_decode_attn(kv8, q, sel, cnt, w.k, scale=scale,
+                                    pages_per_split=K.step_pages_per_split(kv8, w.k))
     torch.cuda.synchronize()
     assert_scores_close(scores, ref["scores"], w, exact=False)
     assert_selection_equal(sel, cnt, ref["sel"], ref["cnt"], ref["fp32"])
@@ -91,7 +92,8 @@ def test_fp8_path_matches_oracle(K, case):
     reuse = K.Reuse(q, spec[0].clone(), spec[1].clone(), 0.95)
     s2 = K.speculative_step(kv8, summ, q2, w.k, reuse, scale=scale)
     r2 = K.score_topk(kv8, summ, q2, w.k, reuse=reuse)
-    o2, l2 = K.sparse_decode_attn(kv8, q2, r2[2], r2[3], w.k, scale=scale)
+    o2, l2 = K.sparse_decode_attn(kv8, q2, r2[2], r2[3], w.k, scale=scale,
+                                  pages_per_split=K.step_pages_per_split(kv8, w.k))
     torch.cuda.synchronize()
     for a, b_, name in zip(s2, tuple(r2) + (o2, l2),
                            ("sel", "cnt", "used", "ucnt", "corrected", "similarity", "out", "lse")):

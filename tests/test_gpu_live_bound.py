@@ -84,7 +84,8 @@ def test_live_bound_matches_oracle(K, case):
     reuse = K.Reuse(q, s1[0].clone(), s1[1].clone(), 0.95)
     s2 = K.speculative_step(kv, summ, q2, w.k, reuse)
     r2 = K.score_topk(kv, summ, q2, w.k, reuse=reuse)
-    o2, l2 = K.sparse_decode_attn(kv, q2, r2[2], r2[3], w.k)
+    o2, l2 = K.sparse_decode_attn(kv, q2, r2[2], r2[3], w.k,
+                                  pages_per_split=K.step_pages_per_split(kv, w.k))
     torch.cuda.synchronize()
     for x, y, name in zip(s2, tuple(r2) + (o2, l2),
                           ("sel", "cnt", "used", "ucnt", "corrected", "similarity", "out", "lse")):

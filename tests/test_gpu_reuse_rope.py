@@ -191,7 +191,8 @@ def test_speculative_decode_loop_matches_oracle(K, spec, tau):
         q_prev = qs[t - 1].cuda() if t > 0 else q
         sel, cnt, used, ucnt, corr, sim = K.score_topk(
             kv, summ, q, w.k, reuse=K.Reuse(q_prev, prev[0], prev[1], tau, first_step=(t == 0)))
-        out, lse = K.sparse_decode_attn(kv, q, used, ucnt, w.k)
+        out, lse = K.sparse_decode_attn(kv, q, used, ucnt, w.k,
+                                        pages_per_split=K.step_pages_per_split(kv, w.k))
         sp = K.speculative_step(kv, summ, q, w.k,
                                 K.Reuse(q_prev, sprev[0], sprev[1], tau, first_step=(t == 0)))
         torch.cuda.synchronize()

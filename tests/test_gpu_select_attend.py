@@ -22,7 +22,7 @@ def K():
 
 def separate_calls(K, kv, summ, q, k, refresh_tail=False):
     sel, cnt = K.score_topk(kv, summ, q, k, refresh_tail=refresh_tail)
-    out, lse = K.sparse_decode_attn(kv, q, sel, cnt, k)
+    out, lse = K.sparse_decode_attn(kv, q, sel, cnt, k, pages_per_split=K.step_pages_per_split(kv, k))
     return sel, cnt, out, lse
 
 
@@ -220,6 +220,7 @@ def test_rotary_gather_fused(K):
         summ_r = K.build_summaries(kv, rope=rope)
         fused = K.select_attend(kv, summ_r, q, w.k, rope=rope)
         sel, cnt = K.score_topk(kv, summ_r, q, w.k)
-        out, lse = K.sparse_decode_attn(kv, q, sel, cnt, w.k, rope=rope)
+        out, lse = K.sparse_decode_attn(kv, q, sel, cnt, w.k, rope=rope,
+                                        pages_per_split=K.step_pages_per_split(kv, w.k))
         torch.cuda.synchronize()
         assert_same(fused, (sel, cnt, out, lse))

@@ -45,7 +45,8 @@ def setup_case(K, k, seed=601, dtype="bf16", Hq=32, Hkv=8, D=128, P=32,
 
 def serial(K, kv, summ, q, k, reuse, rope=None):
     sel, cnt, used, ucnt, corr, sim = K.score_topk(kv, summ, q, k, reuse=reuse)
-    out, lse = K.sparse_decode_attn(kv, q, used, ucnt, k, rope=rope)
+    out, lse = K.sparse_decode_attn(kv, q, used, ucnt, k, rope=rope,
+                                    pages_per_split=K.step_pages_per_split(kv, k))
     return sel, cnt, used, ucnt, corr, sim, out, lse
 
 

@@ -142,7 +142,8 @@ def test_speculative_step_refresh_matches_serial(K, shape):
         sb = poison_tails(fresh.clone(), w)
         spec = K.speculative_step(kv, sa, q, k, reuse, refresh_tail=True)
         sel, cnt, used, ucnt, corr, sim = K.score_topk(kv, sb, q, k, reuse=reuse, refresh_tail=True)
-        out, lse = K.sparse_decode_attn(kv, q, used, ucnt, k)
+        out, lse = K.sparse_decode_attn(kv, q, used, ucnt, k,
+                                        pages_per_split=K.step_pages_per_split(kv, k))
         torch.cuda.synchronize()
         assert_live_equal(sa, fresh, w)
         assert_live_equal(sb, fresh, w)
