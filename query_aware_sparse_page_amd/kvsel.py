@@ -426,7 +426,7 @@ def select_attend(kv: PagedKV, summ: torch.Tensor, q: torch.Tensor, k: int, *,
                   sel_cnt: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                   lse: Optional[torch.Tensor] = None, want_lse: bool = True,
                   workspace: Optional[torch.Tensor] = None):
-    """score_topk + sparse_decode_attn (default split) in one call, with the top-k fused into the
+    """score_topk + sparse_decode_attn (at step_pages_per_split) in one call, with the top-k fused into the
     attention launch. Returns (sel_idx, sel_cnt, out, lse)."""
     d = kv.desc()
     B, Hkv = kv.batch, kv.num_kv_heads
