@@ -230,7 +230,9 @@ kvsel_status kvsel_score_topk(const kvsel_paged_kv* kv, const kvsel_rope* rope, 
  * (0 = the library's choice: 8 from 64 lists on; below that 2 when lists x ceil(k / 2) <= 256,
  * about one block per compute unit, else 4; a request is rounded to a supported size, and raised
  * so that a list has at most 256 splits) and the splits are merged by log-sum-exp in a second
- * launch.
+ * launch. The default depends on the list count, and the split fixes the order in which the
+ * partial sums are combined, so a sequence's outputs may differ in the last bits between batches;
+ * a caller that needs batch-independent bits passes pages_per_split.
  * rope != NULL rotates each key on the fly (bit-identical to a pool rotated by kvsel_rope_shift).
  * fp8 cache: k_t and v_t are the dequantized values (code * the page's k_scale / v_scale); the
  * logits take the key scale as scale * k_scale in fp32, and each probability enters the value
