@@ -1,7 +1,7 @@
 """The batched 32K and 128K workloads (B sequences of the full context, drawn on the device) in
 the bench's launch configuration: one kvsel_select_attend call with the tail refresh, at the
-default split of a call with this many lists (8 pages per split). Sampled sequences -- the first
-and the last of the batch -- are checked against the CPU oracle on their own pages: summaries and
+default split of a call with this many lists (8 pages per split). Sampled sequences -- the first,
+the last and two in between -- are checked against the CPU oracle on their own pages: summaries and
 selection bit-exact, attention within the bf16 tolerance."""
 import numpy as np
 import pytest
@@ -39,7 +39,7 @@ def test_batched_workload_sampled_sequences(K, name):
     summ = K.build_summaries(kv)
     sel, cnt, out, lse = K.select_attend(kv, summ, w.q, w.k, refresh_tail=True, scale=scale)
     torch.cuda.synchronize()
-    for b in (0, w.B - 1):
+    for b in sorted({0, w.B // 3, (2 * w.B) // 3, w.B - 1}):
         ws = sequence_on_host(w, b)
         ref = oracle_path(ws, scale)
         s = summ[b:b + 1].float().cpu().numpy()
