@@ -253,9 +253,8 @@ kvsel_status kvsel_sparse_decode_attn(const kvsel_paged_kv* kv, const kvsel_rope
  * memory round trip after the scores instead of the selection-ids -> page-table chain, and no
  * separate top-k launch runs. The fused form is taken where it measured faster than the
  * separate launches: fewer than 64 (sequence, KV head) lists, tables of at most 1024 entries
- * (512 for bf16 with P 16) and k up to 1024; or, from 64 lists on, bf16 / fp8 pages of 32 slots
- * with at most 512 live pages per sequence (blocks of 8 pages at the default split). Other cases
- * run the two calls' launches inside this call. The outputs are the same either way.
+ * (512 for bf16 with P 16) and k up to 1024; other cases run the two calls' launches inside this
+ * call. The outputs are the same either way.
  * sel_idx / sel_cnt: as kvsel_score_topk. out / lse: as kvsel_sparse_decode_attn. flags: as
  * kvsel_score_topk. ws / ws_bytes: kvsel_workspace_bytes(kv, k, KVSEL_OP_SELECT_ATTEND, 0).
  * [FreeKV] sections 1 and 2.1. */

@@ -276,19 +276,65 @@ __device__ __forceinline__ void refresh_tile(const SelectArgs& a, int b, int n, 
                       rope_row_index(a.rope, b, n, pt), a.rope, lo, hi);
 }
 
+// The group's query slices of one lane folded per channel, in fp64: qp[e] sums the G heads'
+// non-negative values of channel e and qn[e] the negative ones (exact for bf16 queries, and for
+// fp32 queries whose G values span at most 29 binary orders). Then sum over the group of q*hi
+// for q >= 0 and q*lo otherwise is, per channel, qp*hi + qn*lo: the same sum with two products
+// per channel instead of 2G selects and G products, and no per-page work on the query.
+template <int VEC>
+struct QSums {
+  double qp[VEC], qn[VEC];
+};
+
+template <typename T, int G, int VEC>
+__device__ __forceinline__ QSums<VEC> q_sums(const uint4 (&qraw)[G]) {
+  QSums<VEC> s;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s.qp[e] = 0.0, s.qn[e] = 0.0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float f[VEC];
+    unpack<T>(qraw[g], f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const double x = (double)f[e];
+      s.qp[e] += x >= 0.0 ? x : 0.0;
+      s.qn[e] += x >= 0.0 ? 0.0 : x;
+    }
+  }
+  return s;
+}
+
 // Score of one page from its lo / hi slices, by the LPR lanes that hold the page (every lane
-// returns the group's sum): sum over the group's heads and the channels of q*hi for q >= 0 and
-// q*lo otherwise, each product exact in fp64, folded over the LPR lanes.
-template <int G, int VEC, int LPR>
-__device__ __forceinline__ double page_score(const double (&qd)[G][VEC], const float* lo,
+// returns the group's sum): the channel terms qp*hi + qn*lo (each product exact inside the fp64
+// fma), folded over the LPR lanes.
+template <int VEC, int LPR>
+__device__ __forceinline__ double page_score(const QSums<VEC>& qs, const float* lo,
                                              const float* hi) {
   double acc = 0.0;
 #pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    acc = fma(qs.qp[e], (double)hi[e], acc);
+    acc = fma(qs.qn[e], (double)lo[e], acc);
+  }
+  return seg_sum_f64<LPR>(acc);
+}
+
+// The same score in the per-head form (q*hi for q >= 0, q*lo otherwise, G products per channel),
+// for the kernel that scores one page per lane group: there the channel sums would be formed for
+// a single page and would hold 4 * VEC more registers (fewer resident waves).
+template <typename T, int G, int VEC, int LPR>
+__device__ __forceinline__ double page_score_heads(const uint4 (&qraw)[G], const float* lo,
+                                                   const float* hi) {
+  double acc = 0.0;
+#pragma unroll
   for (int g = 0; g < G; ++g) {
+    float f[VEC];
+    unpack<T>(qraw[g], f);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      const double x = (double)(qd[g][e] >= 0.0 ? hi[e] : lo[e]);
-      acc = fma(qd[g][e], x, acc);
+      const double qd = (double)f[e];
+      acc = fma(qd, (double)(qd >= 0.0 ? hi[e] : lo[e]), acc);
     }
   }
   return seg_sum_f64<LPR>(acc);
@@ -413,14 +459,6 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
     }
 
     // ---- scores of this wave's pages ----
-    double qd[G][VEC];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float f[VEC];
-      unpack<T>(qraw[g], f);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) qd[g][e] = (double)f[e];
-    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float lo[VEC], hi[VEC];
@@ -433,54 +471,34 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
           hi[e] = fhi[e];
         }
       }
-      double acc = 0.0;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const double x = (double)(qd[g][e] >= 0.0 ? hi[e] : lo[e]);
-          acc = fma(qd[g][e], x, acc);
-        }
-      }
-      acc = seg_sum_f64<LPR>(acc);
+      const double acc = page_score_heads<T, G, VEC, LPR>(qraw, lo, hi);
       const int n = wn0 + u * PPW + rgl;
       if (n < N && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
     }
   } else {
     // ---- scores of this wave's pages from the stored summary rows (the refreshed tail page's is
     // written from its fresh summary) ----
-    auto q_f64 = [&](double (&qd)[G][VEC]) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float f[VEC];
-        unpack<T>(qraw[g], f);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) qd[g][e] = (double)f[e];
-      }
-    };
-    auto score_pages = [&](const double (&qd)[G][VEC], int skip) {
+    auto score_pages = [&](const QSums<VEC>& qs, int skip) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float lo[VEC], hi[VEC];
         unpack<T>(lo_raw[u], lo);
         unpack<T>(hi_raw[u], hi);
-        const double acc = page_score<G, VEC, LPR>(qd, lo, hi);
+        const double acc = page_score<VEC, LPR>(qs, lo, hi);
         const int n = wn0 + u * PPW + rgl;
         if (n < N && n != skip && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
       }
     };
     if (!btail) {
-      double qd[G][VEC];
-      q_f64(qd);
-      score_pages(qd, -1);
+      const QSums<VEC> qs = q_sums<T, G, VEC>(qraw);
+      score_pages(qs, -1);
       return;
     }
 
     // ---- the block holding the tail page: its key tile's loads go out first (the page id is in
     // the lanes already); every wave folds its share of the tile's rows, the shares meet in LDS, and
     // the wave that scores the tail page combines them, scores the page and writes its summary.
-    // With several pages per lane group (U > 1) the waves score their pages while the tile is in
-    // flight; with one, the tile tends to land before the summary rows, and the fold goes first ----
+    // The waves score their other pages while the tile is in flight ----
     int pt = 0;
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {  // scalar selects (a uniform index into pt_raw would spill it)
@@ -498,7 +516,7 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
     else
       tm.start((const T*)a.k_pool + t * P * D, L - nt * P, a.page_fill, P, lane, w, pt,
                rope_row_index(a.rope, b, nt, pt), a.rope);
-    if constexpr (U > 1) {
+    {
       // the scoring must stay behind the tile loads: these registers, renamed here, keep the
       // compiler from hoisting its (identical) start above the branch
 #pragma unroll
@@ -509,9 +527,8 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
         asm volatile("" : "+v"(lo_raw[u].x), "+v"(lo_raw[u].y), "+v"(lo_raw[u].z), "+v"(lo_raw[u].w));
         asm volatile("" : "+v"(hi_raw[u].x), "+v"(hi_raw[u].y), "+v"(hi_raw[u].z), "+v"(hi_raw[u].w));
       }
-      double qd[G][VEC];
-      q_f64(qd);
-      score_pages(qd, nt);
+      const QSums<VEC> qs = q_sums<T, G, VEC>(qraw);
+      score_pages(qs, nt);
     }
     float plo[VEC], phi[VEC];
     tm.finish(a.rope, plo, phi);
@@ -523,14 +540,7 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
       s_fold[w][1][c0 + off + i] = phi[i];
     }
     __syncthreads();
-    if (!tail) {
-      if constexpr (U == 1) {
-        double qd[G][VEC];
-        q_f64(qd);
-        score_pages(qd, -1);
-      }
-      return;
-    }
+    if (!tail) return;
     float flo[VEC], fhi[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; e += 4) {
@@ -552,10 +562,8 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
       }
     }
     if constexpr (FP8) fp8_scale_outward<VEC>(ksc, flo, fhi);
-    double qd[G][VEC];
-    q_f64(qd);
-    if constexpr (U == 1) score_pages(qd, nt);
-    const double acc = page_score<G, VEC, LPR>(qd, flo, fhi);  // every row group: the same page
+    const QSums<VEC> qs = q_sums<T, G, VEC>(qraw);
+    const double acc = page_score<VEC, LPR>(qs, flo, fhi);  // every row group: the same page
     if (lane == 0) a.scores[(size_t)list * a.maxp + nt] = (float)acc;
     if (lane < LPR) {
       T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;

@@ -49,24 +49,9 @@ bool fused_select_supported(const LaunchKV& kv, int k) {
 // with P 16) and fewer lists than the one-launch selection takes. Measured with cold caches:
 // 8 lists of 1024 pages 18.8 us against 20.2 us for the separate launches; 8 lists of 4096 pages
 // 30.6 against 30.5; 128 lists of <= 512 pages 37.5 against 36.5.
-// From 64 lists on (the 8-page default split), lists of at most 512 pages of 32 slots (bf16 or
-// fp8) take a wide form of the fused launch: blocks of 4 waves x 2 tiles, so a list's select runs
-// once per 8 pages. Measured (cold, the ragged batch of 16: 128 lists of <= 512 pages): step 31.45
-// -> 31.14 us, with fp8 pages 30.26 -> 28.76 us against the one-launch selection and the split
-// launch. Longer lists keep the one-launch selection: 32 x 32K (256 lists of 1024 pages) went
-// from 81.5 to 104.3 us in this form (the score launch over 128 MiB of summaries, and 8 selects of
-// 1024 keys per list).
-static bool fused_wide(const LaunchKV& kv, int k) {
-  return kv.B * kv.Hkv >= SELECT_ONE_LAUNCH_MIN_LISTS && kv.maxn <= 512 && kv.dtype != 0 &&
-         kv.P == 32 &&
-         !kv.page_fill && fused_keys_per_thread(kv) > 0 && fused_keys_per_thread(kv) <= 4 &&
-         step_pages_per_split(kv, k) == 2 * FUSED_PPS;
-}
-
 bool select_attend_fused(const LaunchKV& kv, const RopeArgs&, int k) {
-  return (fused_shape(kv, k) && fused_keys_per_thread(kv) <= 4 &&
-          kv.B * kv.Hkv < SELECT_ONE_LAUNCH_MIN_LISTS) ||
-         fused_wide(kv, k);
+  return fused_shape(kv, k) && fused_keys_per_thread(kv) <= 4 &&
+         kv.B * kv.Hkv < SELECT_ONE_LAUNCH_MIN_LISTS;
 }
 
 template <typename T, int D, int P, bool ROPE, int C, bool FILL>
@@ -82,24 +67,8 @@ static void launch_fused_c(const AttnArgs& a, int G, hipStream_t stream) {
     hipLaunchKernelGGL((fused_f32_kernel<D, P, S::WAVES, S::TPW, ROPE, C, FILL>), grid, block, 0, stream, a, G);
 }
 
-template <typename T, int D, int P, bool ROPE, int C>
-static void launch_fused_wide(const AttnArgs& a, int G, hipStream_t stream) {
-  const dim3 grid(a.Hkv, a.nlists / a.Hkv, a.nsplit);
-  if constexpr (sizeof(T) == 1)
-    hipLaunchKernelGGL((fused_fp8_kernel<D, P, 4, 2, C, false>), grid, dim3(256), 0, stream, a, G);
-  else if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((fused_bf16_kernel<D, P, 4, 2, ROPE, C, false>), grid, dim3(256), 0, stream, a, G);
-}
-
 template <typename T, int D, int P, bool ROPE>
 static void launch_fused_r(int c, const AttnArgs& a, int G, hipStream_t stream) {
-  if constexpr (sizeof(T) <= 2 && P == 32) {
-    if (a.pps == 2 * FUSED_PPS) {  // the wide form (fused_wide): c <= 4, no page_fill
-      if (c == 1) launch_fused_wide<T, D, P, ROPE, 1>(a, G, stream);
-      else launch_fused_wide<T, D, P, ROPE, 4>(a, G, stream);
-      return;
-    }
-  }
   if (a.page_fill) {  // c <= 4 (launch_fused_select checks)
     if (c == 1) launch_fused_c<T, D, P, ROPE, 1, true>(a, G, stream);
     else launch_fused_c<T, D, P, ROPE, 4, true>(a, G, stream);
@@ -170,8 +139,7 @@ hipError_t launch_select_attend(const LaunchKV& kv, const RopeArgs& rope, void* 
   }
   hipError_t e = launch_scores(kv, rope, summ, q, flags, scores, stream);
   if (e != hipSuccess) return e;
-  AttnArgs a = attn_args(kv, rope, q, nullptr, nullptr, k, scale, step_pages_per_split(kv, k), out,
-                         lse, attn_ws);
+  AttnArgs a = attn_args(kv, rope, q, nullptr, nullptr, k, scale, FUSED_PPS, out, lse, attn_ws);
   a.scores = scores;
   a.sel_out = sel_idx;
   a.cnt_out = sel_cnt;
