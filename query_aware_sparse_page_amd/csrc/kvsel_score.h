@@ -276,33 +276,55 @@ __device__ __forceinline__ void refresh_tile(const SelectArgs& a, int b, int n, 
                       rope_row_index(a.rope, b, n, pt), a.rope, lo, hi);
 }
 
-// The group's query slices of one lane folded per channel, in fp64: qp[e] sums the G heads'
-// non-negative values of channel e and qn[e] the negative ones (exact for bf16 queries, and for
-// fp32 queries whose G values span at most 29 binary orders). Then sum over the group of q*hi
-// for q >= 0 and q*lo otherwise is, per channel, qp*hi + qn*lo: the same sum with two products
-// per channel instead of 2G selects and G products, and no per-page work on the query.
+// The group's query folded per channel, in fp64: qp[e] sums the G heads' non-negative values of
+// channel e and qn[e] the negative ones (exact for bf16 queries, and for fp32 queries whose G
+// values span at most 29 binary orders). Then the sum over the group of q*hi for q >= 0 and q*lo
+// otherwise is, per channel, qp*hi + qn*lo: the same sum with two products per channel and page
+// instead of 2G selects and G products, and no per-page work on the query. A lane holds the sums
+// of its VEC channels.
 template <int VEC>
 struct QSums {
   double qp[VEC], qn[VEC];
 };
 
-template <typename T, int G, int VEC>
-__device__ __forceinline__ QSums<VEC> q_sums(const uint4 (&qraw)[G]) {
-  QSums<VEC> s;
+// The channel sums are formed once per block: thread d < D loads channel d of the G heads with the
+// block's first loads (q_channel_load), folds it in head order into LDS, and after one barrier
+// every lane reads the sums of its VEC channels (q_sums_shared; block-uniform, blocks of at least
+// D threads). q_sums_read re-reads them later from the same LDS.
+template <typename T, int D, int G>
+__device__ __forceinline__ void q_channel_load(const T* qrow, float (&qc)[G]) {
+  const int d = min((int)threadIdx.x, D - 1);
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) s.qp[e] = 0.0, s.qn[e] = 0.0;
+  for (int g = 0; g < G; ++g) qc[g] = load_elem<T>(qrow, (size_t)g * D + d);
+}
+
+template <int D, int VEC>
+__device__ __forceinline__ QSums<VEC> q_sums_read(const double (&s_q)[2][D], int c0) {
+  QSums<VEC> r;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float f[VEC];
-    unpack<T>(qraw[g], f);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const double x = (double)f[e];
-      s.qp[e] += x >= 0.0 ? x : 0.0;
-      s.qn[e] += x >= 0.0 ? 0.0 : x;
-    }
+  for (int e = 0; e < VEC; ++e) {
+    r.qp[e] = s_q[0][c0 + e];
+    r.qn[e] = s_q[1][c0 + e];
   }
-  return s;
+  return r;
+}
+
+template <int D, int G, int VEC>
+__device__ __forceinline__ QSums<VEC> q_sums_shared(const float (&qc)[G], double (&s_q)[2][D],
+                                                    int c0) {
+  if (threadIdx.x < D) {
+    double p = 0.0, n = 0.0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const double x = (double)qc[g];
+      p += x >= 0.0 ? x : 0.0;
+      n += x >= 0.0 ? 0.0 : x;
+    }
+    s_q[0][threadIdx.x] = p;
+    s_q[1][threadIdx.x] = n;
+  }
+  __syncthreads();
+  return q_sums_read<D, VEC>(s_q, c0);
 }
 
 // Score of one page from its lo / hi slices, by the LPR lanes that hold the page (every lane
@@ -320,31 +342,11 @@ __device__ __forceinline__ double page_score(const QSums<VEC>& qs, const float* 
   return seg_sum_f64<LPR>(acc);
 }
 
-// The same score in the per-head form (q*hi for q >= 0, q*lo otherwise, G products per channel),
-// for the kernel that scores one page per lane group: there the channel sums would be formed for
-// a single page and would hold 4 * VEC more registers (fewer resident waves).
-template <typename T, int G, int VEC, int LPR>
-__device__ __forceinline__ double page_score_heads(const uint4 (&qraw)[G], const float* lo,
-                                                   const float* hi) {
-  double acc = 0.0;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float f[VEC];
-    unpack<T>(qraw[g], f);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const double qd = (double)f[e];
-      acc = fma(qd, (double)(qd >= 0.0 ? hi[e] : lo[e]), acc);
-    }
-  }
-  return seg_sum_f64<LPR>(acc);
-}
-
 // Scores of chunk `chunk` (WAVES * U * 64 / LPR consecutive pages) of list (sequence b, KV head
 // j), by one block of WAVES waves: LPR lanes read a page's lo and hi rows as 16-byte slices
-// (sequence-major summaries: one contiguous run per wave and unroll step), multiply by the group's
-// query slice in fp64 (a bf16 x bf16 or fp32 x fp32 product is exact in fp64), take q*hi for
-// q >= 0 and q*lo otherwise, and fold the LPR lanes; one fp64 -> fp32 rounding per score. Each
+// (sequence-major summaries: one contiguous run per wave and unroll step), take qp*hi + qn*lo per
+// channel with the block's channel sums of the query (QSums) in fp64 fmas, and fold the LPR
+// lanes; one fp64 -> fp32 rounding per score. Each
 // lane group scores U pages (U > 1 for wide tables: fewer blocks, more loads in flight per lane).
 // With the tail refresh on, the block holding the sequence's last page first rebuilds that page's
 // summary from the key pool -- every wave folds a share of the tile's rows, the waves meet in LDS
@@ -368,7 +370,7 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
   const int rgl = lane / LPR;  // the lane's row group: page wn0 + u * PPW + rgl at step u
 
   // ---- loads first (unconditional, clamped addresses), all in one round: the block's page ids
-  // (used only for the tail refresh), q slice, summary rows (sequence-major, so no page-table hop)
+  // (used only for the tail refresh), query channels, summary rows (sequence-major, so no page-table hop)
   // and the sequence length ----
   // the page ids first: the block that refreshes the tail page waits for them alone (loads
   // complete in issue order) and sends its key-tile loads while the summary rows are in flight
@@ -377,9 +379,10 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
 #pragma unroll
   for (int k = 0; k < NPT; ++k)  // indices from the row width only: no wait for seq_lens
     pt_raw[k] = a.page_table[(size_t)b * a.maxp + min(pb0 + k * 64 + lane, a.maxn - 1)];
-  uint4 qraw[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) qraw[g] = load16(q + ((size_t)b * Hq + j * G + g) * D + c0);
+  // the query, one channel per thread, for the block's channel sums
+  static_assert(WAVES * 64 >= D, "one thread per channel");
+  float qc[G];
+  q_channel_load<T, D, G>(q + ((size_t)b * Hq + j * G) * D, qc);
   uint4 lo_raw[U], hi_raw[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -459,6 +462,8 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
     }
 
     // ---- scores of this wave's pages ----
+    __shared__ double s_q[2][D];  // the block's channel sums
+    const QSums<VEC> qs = q_sums_shared<D, G, VEC>(qc, s_q, c0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float lo[VEC], hi[VEC];
@@ -471,13 +476,14 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
           hi[e] = fhi[e];
         }
       }
-      const double acc = page_score_heads<T, G, VEC, LPR>(qraw, lo, hi);
+      const double acc = page_score<VEC, LPR>(qs, lo, hi);
       const int n = wn0 + u * PPW + rgl;
       if (n < N && (lane % LPR) == 0) a.scores[(size_t)list * a.maxp + n] = (float)acc;
     }
   } else {
     // ---- scores of this wave's pages from the stored summary rows (the refreshed tail page's is
     // written from its fresh summary) ----
+    __shared__ double s_q[2][D];  // the block's channel sums
     auto score_pages = [&](const QSums<VEC>& qs, int skip) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -490,8 +496,7 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
       }
     };
     if (!btail) {
-      const QSums<VEC> qs = q_sums<T, G, VEC>(qraw);
-      score_pages(qs, -1);
+      score_pages(q_sums_shared<D, G, VEC>(qc, s_q, c0), -1);
       return;
     }
 
@@ -520,15 +525,13 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
       // the scoring must stay behind the tile loads: these registers, renamed here, keep the
       // compiler from hoisting its (identical) start above the branch
 #pragma unroll
-      for (int g = 0; g < G; ++g)
-        asm volatile("" : "+v"(qraw[g].x), "+v"(qraw[g].y), "+v"(qraw[g].z), "+v"(qraw[g].w));
+      for (int g = 0; g < G; ++g) asm volatile("" : "+v"(qc[g]));
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         asm volatile("" : "+v"(lo_raw[u].x), "+v"(lo_raw[u].y), "+v"(lo_raw[u].z), "+v"(lo_raw[u].w));
         asm volatile("" : "+v"(hi_raw[u].x), "+v"(hi_raw[u].y), "+v"(hi_raw[u].z), "+v"(hi_raw[u].w));
       }
-      const QSums<VEC> qs = q_sums<T, G, VEC>(qraw);
-      score_pages(qs, nt);
+      score_pages(q_sums_shared<D, G, VEC>(qc, s_q, c0), nt);
     }
     float plo[VEC], phi[VEC];
     tm.finish(a.rope, plo, phi);
@@ -562,8 +565,7 @@ __device__ __forceinline__ void score_block(const SelectArgs& a, int j, int b, i
       }
     }
     if constexpr (FP8) fp8_scale_outward<VEC>(ksc, flo, fhi);
-    const QSums<VEC> qs = q_sums<T, G, VEC>(qraw);
-    const double acc = page_score<VEC, LPR>(qs, flo, fhi);  // every row group: the same page
+    const double acc = page_score<VEC, LPR>(q_sums_read<D, VEC>(s_q, c0), flo, fhi);  // every row group: the same page
     if (lane == 0) a.scores[(size_t)list * a.maxp + nt] = (float)acc;
     if (lane < LPR) {
       T* out = (T*)a.summ + ((size_t)list * a.maxp + nt) * 2 * D;

@@ -311,10 +311,11 @@ __global__ __launch_bounds__(FUSED_THREADS) void select_fused_kernel(SelectArgs 
   const bool refresh = a.refresh_tail && N > 0;
   const int n_end = refresh ? N - 1 : N;  // pages scored from stored summaries
 
-  uint4 qraw[G];  // packed query slices (half the registers of unpacked bf16)
-#pragma unroll
-  for (int g = 0; g < G; ++g) qraw[g] = load16((const T*)a.q + ((size_t)b * Hq + j * G + g) * D + c0);
-  const QSums<VEC> qs = q_sums<T, G, VEC>(qraw);
+  static_assert(FUSED_THREADS >= D, "one thread per channel");
+  float qc[G];
+  q_channel_load<T, D, G>((const T*)a.q + ((size_t)b * Hq + j * G) * D, qc);
+  __shared__ double s_q[2][D];
+  const QSums<VEC> qs = q_sums_shared<D, G, VEC>(qc, s_q, c0);
 
   // ---- wave 0: decode-time refresh of the tail page, scored from registers ----
   if (refresh && w == 0) {
