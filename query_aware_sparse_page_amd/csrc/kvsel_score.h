@@ -298,13 +298,23 @@ __device__ __forceinline__ void q_channel_load(const T* qrow, float (&qc)[G]) {
   for (int g = 0; g < G; ++g) qc[g] = load_elem<T>(qrow, (size_t)g * D + d);
 }
 
+// LDS slot of channel c's sum: channel pairs (2i, 2i + 1) of the D / VEC lane slices side by side,
+// so the lanes of a row group read their pair i from consecutive 16-byte slots (a lane's VEC
+// channels in one run would put the lanes 8 * VEC bytes apart, on the same banks).
+template <int D, int VEC>
+__device__ __forceinline__ int q_sum_slot(int c) {
+  static_assert(VEC % 2 == 0, "channel pairs");
+  constexpr int LPR = D / VEC;
+  return (((c % VEC) >> 1) * LPR + c / VEC) * 2 + (c & 1);
+}
+
 template <int D, int VEC>
 __device__ __forceinline__ QSums<VEC> q_sums_read(const double (&s_q)[2][D], int c0) {
   QSums<VEC> r;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    r.qp[e] = s_q[0][c0 + e];
-    r.qn[e] = s_q[1][c0 + e];
+    r.qp[e] = s_q[0][q_sum_slot<D, VEC>(c0 + e)];
+    r.qn[e] = s_q[1][q_sum_slot<D, VEC>(c0 + e)];
   }
   return r;
 }
@@ -320,8 +330,8 @@ __device__ __forceinline__ QSums<VEC> q_sums_shared(const float (&qc)[G], double
       p += x >= 0.0 ? x : 0.0;
       n += x >= 0.0 ? 0.0 : x;
     }
-    s_q[0][threadIdx.x] = p;
-    s_q[1][threadIdx.x] = n;
+    s_q[0][q_sum_slot<D, VEC>(threadIdx.x)] = p;
+    s_q[1][q_sum_slot<D, VEC>(threadIdx.x)] = n;
   }
   __syncthreads();
   return q_sums_read<D, VEC>(s_q, c0);
